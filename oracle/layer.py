@@ -1,0 +1,82 @@
+"""The routed-expert MoE layer in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Statement of the layer (page "Step 5 Preview: 92 narrow layers, and a sparse
+indexer that scores blocks of 8", "The shape: narrow and deep"; page
+"Step-5-Preview-Spark", "At a glance"): each MoE layer has 352 routed experts
+of which 8 are chosen per token by a sigmoid router, plus one shared expert;
+every expert is a SwiGLU of width 1536 on the hidden size 4096, built from
+gate, up and down projections (page "NeuroSenko/Step-5-Preview-Int4-g128",
+"Tensor layout"). The residual stream is kept in fp32 (page "Step 5
+Preview: ...", the paragraph on training the deep stack:
+fp32_residual_connection).
+
+Per slot s = (t, k) routed to expert e:
+    g = Wg_e x_t,  u = Wu_e x_t,  h = silu(g) * u = g u / (1 + exp(-g)),
+    y_s = Wd_e h
+and   out_t = sum_k w[t, k] y_(t,k)  (k ascending)
+            [+ shared SwiGLU(x_t)] [+ residual_t].
+
+Everything is float64 with no intermediate rounding; the weights are the
+exact dequantized values and x is the 16-bit activation widened exactly.
+
+Readings: silu applies to the gate and multiplies the up projection; there is
+no clamp (the NVFP4 page names a "SwiGLU limit" but gives neither formula nor
+value); the shared expert's output is added unweighted; in the chained stack
+there is no norm between layers, each layer's input is the fp32 residual
+rounded to the activation dtype, and its output is added to the residual.
+"""
+import numpy as np
+
+
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_ffn(x, Wg, Wu, Wd):
+    """x [m, H] -> [m, H] for one expert with float64 weights Wg, Wu [F, H]
+    and Wd [H, F]."""
+    g = x @ Wg.T
+    u = x @ Wu.T
+    return (silu(g) * u) @ Wd.T
+
+
+def routed_outputs(x, ids, expert_weights):
+    """y [T, K, H]: the output of the chosen expert for every slot.
+
+    expert_weights(e) -> (Wg, Wu, Wd) float64. Slots routed to the same
+    expert are evaluated together (one matrix product per expert); each
+    slot's value depends only on its own token and expert.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    y = np.zeros((T, K, x.shape[1]))
+    for e in np.unique(ids):
+        t_idx, k_idx = np.nonzero(ids == e)
+        Wg, Wu, Wd = expert_weights(int(e))
+        y[t_idx, k_idx] = swiglu_ffn(x[t_idx], Wg, Wu, Wd)
+    return y
+
+
+def combine(y, w, shared=None, residual=None):
+    """out[t] = sum over k ascending of w[t, k] * y[t, k]  (+ shared) (+ residual)."""
+    T, K, H = y.shape
+    out = np.zeros((T, H))
+    for k in range(K):
+        out += w[:, k:k + 1] * y[:, k, :]
+    if shared is not None:
+        out = out + shared
+    if residual is not None:
+        out = out + residual
+    return out
+
+
+def moe_layer(x, ids, w, expert_weights, shared_weights=None, residual=None):
+    """One layer: routed experts + optional shared expert + optional residual."""
+    y = routed_outputs(x, ids, expert_weights)
+    sh = None
+    if shared_weights is not None:
+        sh = swiglu_ffn(np.asarray(x, dtype=np.float64), *shared_weights)
+    return combine(y, w, sh, residual)

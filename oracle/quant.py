@@ -1,0 +1,178 @@
+"""Weight formats of the routed experts: quantizers, packing, dequantization.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+int4-g128 (page "NeuroSenko/Step-5-Preview-Int4-g128", sections "Recipe" and
+"Tensor layout"): symmetric int4, one scale per 128 input channels, the scale
+stored in bf16 and chosen per group among 17 clip ratios in [0.60, 1.00] to
+minimise the rounding MSE, the search done in the scale's own precision so
+that quantizing and dequantizing agree exactly. Routed experts only; the
+fused source tensors are [experts, out, in].
+
+NVFP4 (page "Step-5-Preview-NVFP4-Local", "Modifications" item 2 and
+"Format"): weight U8 [E, R, K/2] holding E2M1 pairs, one F8_E4M3 block scale
+per 16 weights [E, R, K/16], one F32 weight_scale_2 per expert [E]; a weight
+dequantizes as E2M1 value x E4M3 block scale x weight_scale_2. Layers that
+were BF16 at the source were "quantized here the same way".
+
+Readings where the pages are silent (each also listed in the design notes):
+* int4 scale = clip_ratio * max|w| / 7 (divisor 7), q = clamp(rne(w/s), -8, 7).
+  The divisor is not printed; 7 is the one that reproduces the page's error
+  table (max-abs 11.74 %, clip search 10.11 %) on Gaussian weights.
+* the 17 ratios are 1.00, 0.975, ..., 0.60 (evenly spaced, step 0.025); the
+  candidate scale is bf16(fl64((40 - i) * a / 280)), rounded once to bf16;
+  the MSE of a candidate is accumulated in float64 in ascending input order;
+  the first minimum in ratio order wins (ties go to the larger ratio).
+* nibble j of int32 word w along K holds input 8w+j (low nibble first, as the
+  NVFP4 page's scale codes are stored), as a two's-complement 4-bit integer.
+* NVFP4 global scale = fp32(max|W| / (6 * 448)) per expert matrix (1 for an
+  all-zero matrix); block scale = E4M3(max|block| / (6 * gs)), saturating,
+  ties to even; element code = E2M1(w / (bs * gs)), saturating, ties to
+  even, a value that rounds to zero gets code 0 (+0). Within a byte the low
+  nibble is the even input index.
+"""
+import numpy as np
+
+from .formats import (E2M1, E4M3, bf16_from_bits, round_to_format, to_bf16,
+                      to_fp32, e2m1_decode, e2m1_encode, e4m3_decode,
+                      e4m3_encode_nonneg)
+
+INT4_GROUP = 128
+NVFP4_GROUP = 16
+N_CLIP = 17
+
+
+# ------------------------------------------------------------------ int4 ---
+def int4_candidate_scale(a, i):
+    """Scale of clip ratio i (ratio (40 - i)/40) for a group with max|w| = a."""
+    return to_bf16(((40 - i) * np.asarray(a, dtype=np.float64)) / 280.0)
+
+
+def quantize_int4(W, clip_search=True, group=INT4_GROUP):
+    """Quantize W [n, k] (bf16-representable values, float64 array).
+
+    Returns q [n, k] int8 in [-8, 7] and s [n, k/group] float64 (bf16 values).
+    With clip_search=False only ratio 1.00 is tried (the max-abs comparator).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    n, k = W.shape
+    assert k % group == 0
+    Wg = W.reshape(n, k // group, group)
+    a = np.max(np.abs(Wg), axis=-1)
+    best_mse = np.full(a.shape, np.inf)
+    best_s = np.zeros(a.shape)
+    best_q = np.zeros(Wg.shape, dtype=np.int8)
+    for i in range(N_CLIP if clip_search else 1):
+        s = int4_candidate_scale(a, i)
+        sg = s[..., None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.where(sg > 0, np.clip(np.rint(Wg / sg), -8, 7), 0.0)
+        err = q * sg - Wg
+        mse = np.cumsum(err * err, axis=-1)[..., -1]    # ascending k, fp64
+        better = mse < best_mse                          # first minimum wins
+        best_mse = np.where(better, mse, best_mse)
+        best_s = np.where(better, s, best_s)
+        best_q = np.where(better[..., None], q.astype(np.int8), best_q)
+    return best_q.reshape(n, k), best_s
+
+
+def pack_int4(q):
+    """q [n, k] int in [-8, 7] -> int32 words [n, k/8]; nibble j of word w is
+    input 8w+j, stored as its two's-complement low 4 bits."""
+    q = np.asarray(q, dtype=np.int64)
+    n, k = q.shape
+    assert k % 8 == 0 and q.min(initial=0) >= -8 and q.max(initial=0) <= 7
+    nib = (q & 0xF).astype(np.uint64).reshape(n, k // 8, 8)
+    shifts = (4 * np.arange(8)).astype(np.uint64)
+    words = np.bitwise_or.reduce(nib << shifts, axis=-1).astype(np.uint32)
+    return words.view(np.int32)
+
+
+def unpack_int4(words):
+    """int32 words [n, k/8] -> q [n, k] int8."""
+    w = np.asarray(words).view(np.uint32).astype(np.int64)
+    n, kw = w.shape
+    nib = (w[..., None] >> (4 * np.arange(8))) & 0xF
+    q = nib - 16 * (nib >= 8)
+    return q.reshape(n, kw * 8).astype(np.int8)
+
+
+def dequant_int4(words, scales_bf16_bits, group=INT4_GROUP):
+    """Exact dequantized values q * s (float64) from packed words [n, k/8]
+    and bf16 scale bit patterns [n, k/group] (uint16)."""
+    q = unpack_int4(words).astype(np.float64)
+    s = bf16_from_bits(scales_bf16_bits)
+    return q * np.repeat(s, group, axis=1)
+
+
+def rel_error(W, Wq, X):
+    """||(Wq - W) X|| / ||W X|| (Frobenius norm over the columns of X), the
+    error measure of the int4 page's table."""
+    return np.linalg.norm((Wq - W) @ X) / np.linalg.norm(W @ X)
+
+
+# ----------------------------------------------------------------- NVFP4 ---
+def nvfp4_global_scale(W):
+    A = float(np.max(np.abs(W))) if np.size(W) else 0.0
+    if A == 0.0:
+        return 1.0
+    return float(to_fp32(A / (6.0 * 448.0)))
+
+
+def quantize_nvfp4(W, group=NVFP4_GROUP):
+    """Quantize one expert matrix W [n, k] (float64, bf16-representable).
+
+    Returns codes [n, k] uint8 (E2M1 codes), block-scale values bs [n, k/16]
+    (float64, E4M3-representable, >= 0) and the global scale gs (float,
+    fp32-representable).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    n, k = W.shape
+    assert k % group == 0
+    gs = nvfp4_global_scale(W)
+    Wb = W.reshape(n, k // group, group)
+    amax = np.max(np.abs(Wb), axis=-1)
+    bs = round_to_format(amax / (6.0 * gs), E4M3, saturate=True)
+    denom = (bs * gs)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(denom > 0, Wb / denom, 0.0)
+    vq = round_to_format(v, E2M1, saturate=True)
+    codes = e2m1_encode(vq.reshape(n, k))
+    return codes, bs, gs
+
+
+def pack_nvfp4(codes):
+    """codes [n, k] -> bytes [n, k/2]; the low nibble is the even input."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] & 0xF) | ((c[:, 1::2] & 0xF) << 4)
+
+
+def unpack_nvfp4(packed):
+    p = np.asarray(packed, dtype=np.uint8)
+    n, kh = p.shape
+    out = np.empty((n, 2 * kh), dtype=np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def e4m3_bytes(bs):
+    return e4m3_encode_nonneg(bs)
+
+
+def dequant_nvfp4(packed, scale_bytes, gs, group=NVFP4_GROUP):
+    """E2M1 value x E4M3 block scale x global scale, exact in float64."""
+    v = e2m1_decode(unpack_nvfp4(packed))
+    b = e4m3_decode(scale_bytes)
+    return v * np.repeat(b, group, axis=1) * float(gs)
+
+
+def dequant_nvfp4_fp32(packed, scale_bytes, gs, group=NVFP4_GROUP):
+    """The dequantized weight rounded once to float32 (the exact float64
+    product has at most 2 + 4 + 24 significant bits)."""
+    return to_fp32(dequant_nvfp4(packed, scale_bytes, gs, group))
+
+
+def nmse(W, Wq):
+    """Weight normalised MSE ||Wq - W||^2 / ||W||^2."""
+    return float(np.sum((Wq - W) ** 2) / np.sum(W ** 2))

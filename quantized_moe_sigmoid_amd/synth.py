@@ -1,0 +1,97 @@
+"""Seeded synthetic inputs for the MoE layer workloads.
+
+This module only draws random numbers and casts them to storage types; it
+holds none of the layer's arithmetic (no routing, quantization, dequant or
+FFN). Both the test oracle and the HIP library are fed from here.
+
+Every stream is numpy's PCG64 seeded by SeedSequence([root, layer, tensor,
+expert]), so one tensor never depends on the shapes or draw order of another.
+Tensor ids: 0 activations, 1 router weight, 2 router logits, 3 Zipf
+permutation, 10/11/12 gate/up/down expert weights, 20/21/22 shared expert.
+
+Distributions (the layer's shapes are those of page "Step 5 Preview: 92
+narrow layers, and a sparse indexer that scores blocks of 8", "The shape:
+narrow and deep": hidden 4096, 352 experts, top-8, SwiGLU width 1536):
+* activations N(0, 1), rounded to fp16 or bf16;
+* expert weights N(0, 0.02), rounded to bf16 (the source checkpoints are
+  BF16: page "NeuroSenko/Step-5-Preview-Int4-g128", first paragraph);
+* router weight N(0, 0.02) float32; given router logits N(0, 1) float32;
+* skewed routing: bias_e = -s * ln(rank_e) with s = 1.1 and rank a seeded
+  permutation of 1..E (a Zipf(s) popularity on the sigmoid's logit scale).
+
+Large weight banks for the benchmark are drawn on the GPU by torch's own
+generator (see `device_normal`), chunk by chunk, since 6.6 G numpy draws
+would take minutes.
+"""
+import numpy as np
+
+T_X, T_WR, T_LOGITS, T_ZIPF = 0, 1, 2, 3
+T_GATE, T_UP, T_DOWN = 10, 11, 12
+T_SH_GATE, T_SH_UP, T_SH_DOWN = 20, 21, 22
+
+# Workloads: the tiny layer, decode, prefill, NVFP4 and the chained stack.
+CONFIGS = {
+    "tiny": dict(T=(8,), H=256, E=16, K=2, F=128, act="f16", fmt="int4",
+                 router="weights", root=0),
+    "decode": dict(T=(1, 8, 64), H=4096, E=352, K=8, F=1536, act="f16",
+                   fmt="int4", router="logits", root=2),
+    "prefill": dict(T=(2048,), H=4096, E=352, K=8, F=1536, act="bf16",
+                    fmt="int4", router="weights", root=3),
+    "nvfp4": dict(T=(1, 256), H=4096, E=352, K=8, F=1536, act="bf16",
+                  fmt="nvfp4", router="logits", root=4),
+    "stack": dict(T=(32, 4096), H=4096, E=352, K=8, F=1536, act="bf16",
+                  fmt="int4", router="weights+zipf", root=5, layers=8,
+                  shared=True),
+}
+
+
+def rng(root, layer, tensor, expert=0):
+    return np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([int(root), int(layer), int(tensor), int(expert)])))
+
+
+def normal(shape, std, root, layer, tensor, expert=0):
+    """float32 N(0, std^2)."""
+    return (rng(root, layer, tensor, expert).standard_normal(shape, dtype=np.float32)
+            * np.float32(std)).astype(np.float32)
+
+
+def cast16(a, dtype):
+    """Round float32 values to fp16 / bf16 (round to nearest even) with torch
+    and return the torch CPU tensor."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.float16 if dtype == "f16" else torch.bfloat16)
+
+
+def activations(T, H, dtype, root, layer=0):
+    return cast16(normal((T, H), 1.0, root, layer, T_X), dtype)
+
+
+def router_weight_T(H, E, root, layer=0):
+    """Router weight stored transposed, [H, E] float32, N(0, 0.02)."""
+    return np.ascontiguousarray(normal((E, H), 0.02, root, layer, T_WR).T)
+
+
+def router_logits(T, E, root, layer=0):
+    return normal((T, E), 1.0, root, layer, T_LOGITS)
+
+
+def zipf_bias(E, root, layer=0, s=1.1):
+    rank = rng(root, layer, T_ZIPF).permutation(E) + 1
+    return (-s * np.log(rank.astype(np.float64))).astype(np.float32)
+
+
+def expert_weight_bf16(n, k, root, layer, tensor, expert):
+    """One expert matrix [n, k]: N(0, 0.02) rounded to bf16 (torch tensor)."""
+    return cast16(normal((n, k), 0.02, root, layer, tensor, expert), "bf16")
+
+
+def device_normal(shape, std, seed, device, dtype=None):
+    """N(0, std^2) drawn on `device` by torch's generator for that device,
+    seeded with `seed`; optionally cast to `dtype` (torch dtype)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+    return x if dtype is None else x.to(dtype)

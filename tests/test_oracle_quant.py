@@ -1,0 +1,197 @@
+"""Pins of the oracle's int4-g128 and NVFP4 quantizers, packing and dequant.
+
+Pinned against the pages' printed figures (tests/golden/page_figures.json),
+exhaustive enumeration, exactly-representable special cases and invariants.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import quant as Q
+from quantized_moe_sigmoid_amd import synth
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def _gauss_bf16(n, k, seed):
+    return synth.expert_weight_bf16(n, k, 100 + seed, 0, 10, 0).float().numpy().astype(np.float64)
+
+
+# ------------------------------------------------------------- packing ---
+def test_int4_pack_exhaustive_single_nibbles():
+    for pos in range(8):
+        for v in range(-8, 8):
+            q = np.zeros((1, 8), dtype=np.int64)
+            q[0, pos] = v
+            w = Q.pack_int4(q)
+            assert int(w.view(np.uint32)[0, 0]) == ((v & 0xF) << (4 * pos))
+            assert np.array_equal(Q.unpack_int4(w), q)
+
+
+@pytest.mark.parametrize("word", [0, 0x88888888, 0x77777777, 0xFFFFFFFF, 0x01234567, 0xFEDCBA98])
+def test_int4_special_words_roundtrip(word):
+    w = np.array([[word]], dtype=np.uint32).view(np.int32)
+    q = Q.unpack_int4(w)
+    assert np.array_equal(Q.pack_int4(q).view(np.uint32), w.view(np.uint32))
+    nib = [(word >> (4 * i)) & 0xF for i in range(8)]
+    assert list(q[0]) == [n - 16 if n >= 8 else n for n in nib]
+
+
+def test_int4_random_words_roundtrip():
+    r = np.random.default_rng(0)
+    w = r.integers(0, 2 ** 32, size=(1000, 125), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    assert np.array_equal(Q.pack_int4(Q.unpack_int4(w)), w)
+
+
+def test_nvfp4_pack_roundtrip_low_nibble_even():
+    codes = np.arange(32, dtype=np.uint8).reshape(1, 32) % 16
+    p = Q.pack_nvfp4(codes)
+    assert p[0, 0] == (0 | (1 << 4)) and p[0, 7] == (14 | (15 << 4))
+    assert np.array_equal(Q.unpack_nvfp4(p), codes)
+
+
+# ---------------------------------------------------- int4 quantizer ---
+def test_int4_error_table_matches_page():
+    """Max-abs and clip-search errors of the page's table on Gaussian weights
+    and inputs. A wrong divisor (7.5 or 8 give 11.1 % / 10.5 % for max-abs),
+    ratio grid, rounding or group size moves these well outside the band."""
+    g = GOLD["int4_g128_relative_error"]
+    W = _gauss_bf16(512, 4096, 0)
+    X = synth.rng(7, 0, 0).standard_normal((4096, 64))
+    q0, s0 = Q.quantize_int4(W, clip_search=False)
+    q1, s1 = Q.quantize_int4(W, clip_search=True)
+    e0 = Q.rel_error(W, q0 * np.repeat(s0, 128, 1), X)
+    e1 = Q.rel_error(W, q1 * np.repeat(s1, 128, 1), X)
+    assert abs(e0 - g["maxabs"]) < 0.0025, e0
+    assert abs(e1 - g["clip_search"]) < 0.003, e1
+    # Gaussian x: E||E x||^2 = ||E||_F^2, so the Frobenius ratio agrees.
+    f1 = np.linalg.norm(q1 * np.repeat(s1, 128, 1) - W) / np.linalg.norm(W)
+    assert abs(f1 - e1) < 0.004
+
+
+def test_int4_clip_never_worse_than_maxabs_per_group():
+    W = _gauss_bf16(64, 1024, 1)
+    q0, s0 = Q.quantize_int4(W, clip_search=False)
+    q1, s1 = Q.quantize_int4(W, clip_search=True)
+    e0 = ((q0 * np.repeat(s0, 128, 1) - W) ** 2).reshape(64, 8, 128).sum(-1)
+    e1 = ((q1 * np.repeat(s1, 128, 1) - W) ** 2).reshape(64, 8, 128).sum(-1)
+    assert np.all(e1 <= e0 * (1 + 1e-12))
+    assert np.mean(e1 < e0) > 0.9
+
+
+def test_int4_scale_is_one_of_the_17_bf16_candidates():
+    W = _gauss_bf16(16, 512, 2)
+    q, s = Q.quantize_int4(W)
+    a = np.abs(W).reshape(16, 4, 128).max(-1)
+    for i in range(16):
+        for g in range(4):
+            cands = [float(F.to_bf16((1.0 - 0.025 * r) * a[i, g] / 7.0)) for r in range(17)]
+            assert s[i, g] in cands
+            assert float(F.to_bf16(s[i, g])) == s[i, g]
+    assert q.min() >= -8 and q.max() <= 7
+
+
+def test_int4_exactly_representable_groups_have_zero_error():
+    """A group made of integer multiples q0 * s0 with max |q0| = 7 and s0 a
+    bf16 value equal to max|w|/7 is reproduced exactly (ratio 1.00)."""
+    r = np.random.default_rng(3)
+    s0 = np.array([2.0 ** -8 * 1.5, 2.0 ** -6 * 1.25, 2.0 ** -10 * 1.875])
+    W = np.empty((3, 256))
+    for i in range(3):
+        q0 = r.integers(-7, 8, 256)
+        q0[5] = 7
+        W[i] = q0 * s0[i]
+    q, s = Q.quantize_int4(W)
+    assert np.array_equal(q * np.repeat(s, 128, 1), W)
+
+
+def test_int4_zero_group():
+    W = np.zeros((2, 256))
+    W[1, 128:] = 0.01
+    q, s = Q.quantize_int4(W)
+    assert s[0, 0] == 0 and s[0, 1] == 0 and s[1, 0] == 0 and np.all(q[0] == 0)
+    assert s[1, 1] > 0
+
+
+def test_int4_dequant_exact_and_requantizes():
+    W = _gauss_bf16(8, 256, 4)
+    q, s = Q.quantize_int4(W)
+    words = Q.pack_int4(q)
+    sb = F.bf16_bits(s)
+    Wd = Q.dequant_int4(words, sb)
+    assert np.array_equal(Wd, q * np.repeat(s, 128, 1))
+    # float32 holds q*s exactly (<= 4 + 8 significant bits)
+    assert np.array_equal(Wd.astype(np.float32).astype(np.float64), Wd)
+    assert np.array_equal(np.rint(Wd / np.repeat(s, 128, 1)), q)
+
+
+# --------------------------------------------------------------- NVFP4 ---
+def test_nvfp4_nmse_matches_page():
+    g = GOLD["nvfp4_weight_nmse"]
+    W = _gauss_bf16(512, 4096, 5)
+    codes, bs, gs = Q.quantize_nvfp4(W)
+    Wd = Q.dequant_nvfp4(Q.pack_nvfp4(codes), Q.e4m3_bytes(bs), gs)
+    assert abs(Q.nmse(W, Wd) - g["layers_88_90"]) < 0.0005
+
+
+def test_nvfp4_decodes_exactly_to_quantizer_output():
+    W = _gauss_bf16(64, 512, 6)
+    codes, bs, gs = Q.quantize_nvfp4(W)
+    packed = Q.pack_nvfp4(codes)
+    sb = Q.e4m3_bytes(bs)
+    assert np.array_equal(F.e4m3_decode(sb), bs)
+    Wd = Q.dequant_nvfp4(packed, sb, gs)
+    want = F.e2m1_decode(codes) * np.repeat(bs, 16, 1) * gs
+    assert np.array_equal(Wd, want)
+    # exact in float64; one rounding to float32
+    assert np.array_equal(Q.dequant_nvfp4_fp32(packed, sb, gs), F.to_fp32(want))
+
+
+def test_nvfp4_representable_block_roundtrip():
+    """Weights that are exactly e2m1 * bs * gs quantize back to the same codes."""
+    W = np.zeros((2, 32))
+    vals = F.E2M1_TABLE[[7, 1, 2, 3, 4, 5, 6, 15, 9, 10, 11, 12, 13, 14, 0, 6]]
+    gs = float(F.to_fp32(6.0 / (6 * 448)))
+    W[0, :16] = vals * 448.0 * gs
+    W[1, 16:] = vals * 448.0 * gs
+    codes, bs, gs2 = Q.quantize_nvfp4(W)
+    assert gs2 == gs
+    assert bs[0, 0] == 448.0 and bs[0, 1] == 0.0 and bs[1, 1] == 448.0
+    assert np.array_equal(F.e2m1_decode(codes[0, :16]), vals)
+
+
+def test_nvfp4_global_and_block_scale_rule():
+    W = _gauss_bf16(32, 256, 7)
+    codes, bs, gs = Q.quantize_nvfp4(W)
+    A = np.abs(W).max()
+    assert gs == float(np.float32(A / 2688.0))
+    amax = np.abs(W).reshape(32, 16, 16).max(-1)
+    # the block's largest magnitude lands at most one E2M1 step from 6
+    top = np.abs(F.e2m1_decode(codes)).reshape(32, 16, 16).max(-1)
+    assert np.all((top >= 4.0) | (amax == 0))
+    assert np.all(bs <= 448.0)
+
+
+def test_nvfp4_layout_sizes_match_page():
+    s = GOLD["nvfp4_sizes_bytes"]
+    E, H, Fw = 352, 4096, 1536
+    per_layer_w = 0
+    per_layer_s = 0
+    for (R, K) in ((Fw, H), (Fw, H), (H, Fw)):
+        per_layer_w += E * R * (K // 2)
+        per_layer_s += E * R * (K // 16)
+    assert 3 * per_layer_w == s["layers_88_90_nvfp4_weights"]
+    assert 85 * per_layer_s == s["layers_3_87_raw_e4m3_scales"]
+    assert 3 * E * 3 * Fw * H * 2 == s["layers_88_90_bf16_experts"]
+    assert H // 16 == s["gate_up_C"] and Fw // 16 == s["down_C"]
+
+
+def test_expert_parameter_count_matches_page():
+    g = GOLD["per_expert_params_millions"]
+    shp = GOLD["layer_shape"]
+    per = 3 * shp["hidden"] * shp["expert_width"]
+    assert round(per / 1e6, 2) == g["value"]
+    assert round(shp["moe_layers"] * shp["top_k"] * per / 1e9, 2) == g["active_routed_billions"]
