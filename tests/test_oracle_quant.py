@@ -195,3 +195,26 @@ def test_expert_parameter_count_matches_page():
     per = 3 * shp["hidden"] * shp["expert_width"]
     assert round(per / 1e6, 2) == g["value"]
     assert round(shp["moe_layers"] * shp["top_k"] * per / 1e9, 2) == g["active_routed_billions"]
+
+
+@pytest.mark.parametrize("a_hex,b_hex", [("0x1.14p-6", "-0x1.0ep-6"), ("0x1.78p-4", "-0x1.6ep-4"),
+                                         ("0x1.a2p-6", "0x1.2p-6")])
+def test_int4_exact_mse_tie_goes_to_larger_ratio(a_hex, b_hex):
+    """Groups whose rounding MSE ties exactly between ratios 1.00 and 0.975
+    (verified with exact rational arithmetic): the first minimum in ratio
+    order, i.e. the larger ratio, is kept."""
+    from fractions import Fraction
+    a, b = float.fromhex(a_hex), float.fromhex(b_hex)
+    W = np.zeros((1, 128))
+    W[0, 0], W[0, 77] = a, b
+    exact = []
+    for i in range(17):
+        s = float(F.to_bf16(((40 - i) * a) / 280.0))
+        qs = [max(-8, min(7, round(Fraction(w) / Fraction(s)))) for w in (a, b)]
+        exact.append((sum((Fraction(q) * Fraction(s) - Fraction(w)) ** 2
+                          for q, w in zip(qs, (a, b))), s))
+    best = min(m for m, _ in exact)
+    winners = [i for i, (m, _) in enumerate(exact) if m == best]
+    assert winners[:2] == [0, 1] and exact[0][1] != exact[1][1]
+    q, s = Q.quantize_int4(W)
+    assert s[0, 0] == exact[0][1]
