@@ -1,0 +1,212 @@
+/*
+ * moe_w4a16.h -- C ABI of the W4A16 routed-expert MoE layer for AMD MI355X
+ * (CDNA4, gfx950).
+ *
+ * The layer (page "Step 5 Preview: 92 narrow layers, and a sparse indexer
+ * that scores blocks of 8", section "The shape: narrow and deep"; page
+ * "Step-5-Preview-Spark", "At a glance"): hidden size 4096, 352 routed
+ * experts of which a sigmoid router picks 8 per token, plus one shared
+ * expert; every expert is a SwiGLU of width 1536 made of gate, up and down
+ * projections. Routed-expert weights are 4-bit and dequantized inside the
+ * kernels; activations stay 16-bit (W4A16).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer unless its comment says
+ *   "host". The caller owns all memory, workspaces included; the library
+ *   allocates nothing and keeps no mutable global state.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Every call only enqueues work on it and returns; nothing synchronises.
+ * - Arguments are validated on the host before anything is launched; an
+ *   invalid call returns an error and enqueues nothing. A failed launch
+ *   returns MOE_ERR_HIP. Faults inside kernels surface at the caller's next
+ *   synchronisation.
+ * - Inputs are assumed finite; NaN or Inf gives unspecified routing.
+ * - Matrices are row-major. Slot s = t*K + k is the k-th expert choice of
+ *   token t.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,         /* null pointer, bad size or stride   */
+    MOE_ERR_UNSUPPORTED = 2,         /* valid but not implemented shape    */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_HIP = 4                  /* a HIP launch or API call failed    */
+} moe_status_t;
+
+typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
+
+/* Weight formats of one bank of expert matrices.
+ *
+ * MOE_W_INT4_G128 -- page "NeuroSenko/Step-5-Preview-Int4-g128", "Recipe"
+ *   and "Tensor layout": symmetric int4, one bf16 scale per 128 input
+ *   channels, routed experts fused as [experts, out, in].
+ *   qweight: int32 [E][n][k/8]; nibble j (bits 4j..4j+3) of word w holds
+ *            input 8w+j as a two's-complement value q in [-8, 7].
+ *   scale:   bf16 [E][n][k/128].   weight = q * scale.
+ *
+ * MOE_W_NVFP4_G16 -- page "Step-5-Preview-NVFP4-Local", "Modifications"
+ *   item 2 and "Format": weight U8 [E, R, K/2] of E2M1 pairs, F8_E4M3 block
+ *   scale [E, R, K/16], F32 weight_scale_2 [E]; the W4A16 variant keeps
+ *   activations in BF16.
+ *   qweight: uint8 [E][n][k/2]; the low nibble is the even input index.
+ *   scale:   uint8 E4M3FN [E][n][k/16].
+ *   global_scale: float [E].   weight = e2m1 * e4m3 * global_scale.
+ *
+ * MOE_W_BF16 -- an unquantized bank (the shared expert stays BF16: page
+ *   "NeuroSenko/Step-5-Preview-Int4-g128", "What stays in BF16").
+ *   qweight: bf16 [E][n][k]; scale and global_scale NULL.
+ */
+typedef enum { MOE_W_INT4_G128 = 1, MOE_W_NVFP4_G16 = 2, MOE_W_BF16 = 3 } moe_wfmt_t;
+
+/* One bank of E matrices, each [n out][k in]. Strides are in bytes; the
+ * row strides must be multiples of 16 and the base pointers 16-byte
+ * aligned (the kernels load 128 bits at a time). Per-expert tensors stored
+ * at a constant distance are described by the expert stride. */
+typedef struct {
+    int32_t fmt;                 /* moe_wfmt_t                                  */
+    int32_t num_experts, n, k;
+    const void  *qweight;
+    const void  *scale;          /* NULL for MOE_W_BF16                          */
+    const float *global_scale;   /* NVFP4 only, else NULL                        */
+    int64_t qweight_expert_stride, qweight_row_stride;
+    int64_t scale_expert_stride, scale_row_stride;
+} moe_weight_desc_t;
+
+/* The three projections of a SwiGLU bank: gate and up are [F][H], down is
+ * [H][F]; all three share one format and expert count. */
+typedef struct { moe_weight_desc_t gate, up, down; } moe_ffn_desc_t;
+
+/* Output of moe_permute (every pointer a device array the caller sized
+ * with moe_permute_sizes). Definition:
+ *   counts[e]            slots routed to expert e                     [E]
+ *   expert_offsets[e]    exclusive prefix sum of counts               [E+1]
+ *   padded_offsets[e]    exclusive prefix sum of counts rounded up to
+ *                        a multiple of tile_m                         [E+1]
+ *   sorted_slots[r]      row r of the expert-sorted order: each expert's
+ *                        slots in ascending slot order, its segment
+ *                        padded with -1 to its padded length; rows at and
+ *                        beyond padded_offsets[E] are not written     [max_rows]
+ *   slot_to_row[s]       row of slot s in sorted_slots                [T*K]
+ *   tile_expert[i]       expert owning rows [i*tile_m, (i+1)*tile_m)  [max_tiles]
+ *   num_tiles[0]         padded_offsets[E] / tile_m                   [1]
+ *   active_experts[j]    experts with counts > 0, ascending           [E]
+ *   num_active[0]        how many there are                           [1]
+ */
+typedef struct {
+    int32_t *counts, *expert_offsets, *padded_offsets, *sorted_slots,
+            *slot_to_row, *tile_expert, *num_tiles, *active_experts,
+            *num_active;
+    int32_t tile_m;
+} moe_perm_t;
+
+/* Human-readable name of a status code (host, static storage). */
+const char *moe_status_string(int status);
+
+/* ABI version of this header: 1. */
+int moe_abi_version(void);
+
+/*
+ * moe_route_topk -- sigmoid top-K router (page "Step-5-Preview-Spark",
+ * "At a glance": top-8 of 352 experts by a sigmoid router; tie rule as the
+ * sparse indexer's region top-k on page "Step 5 Preview: ...", "Sparse GQA,
+ * read from the kernels", step 3).
+ *
+ * Logits come from exactly one of:
+ *   router_wT [H][E] float: logit[t][e] = the float32 chain
+ *       acc = 0; for k = 0..H-1: acc = fma(float(x[t][k]), router_wT[k][e], acc)
+ *     (this fixed order makes the selected indices reproducible bit for
+ *     bit; page "Step-5-Preview-Spark", "Quality", shows top-8 routing
+ *     flipping under a changed summation order);  x [T][H] in x_dtype
+ *     (MOE_F16 or MOE_BF16);
+ *   logits_in [T][E] float: given logits (x and router_wT unused, may be
+ *     NULL).
+ * If bias [E] float is non-NULL, logit = logit + bias[e] in float32.
+ * topk_ids [T][K] int32: the K largest logits by (logit descending, expert
+ * index ascending), -0 equal to +0. topk_w [T][K] float: sigmoid of those
+ * logits, divided by their sum over the K when renormalize != 0.
+ * Limits: 1 <= K <= min(E, 16), E <= 512, H % 8 == 0 when router_wT is used.
+ * T == 0 is a no-op.
+ */
+moe_status_t moe_route_topk(const void *x, int x_dtype, const float *router_wT,
+                            const float *logits_in, const float *bias,
+                            int T, int H, int E, int K, int renormalize,
+                            int32_t *topk_ids, float *topk_w, void *stream);
+
+/* Sizes (host outputs, in elements) of the moe_permute arrays for T tokens,
+ * K choices, E experts and tile_m rows per tile:
+ *   max_rows  = T*K + min(E, T*K)*(tile_m - 1)  (sorted_slots)
+ *   max_tiles = max_rows / tile_m               (tile_expert)          */
+moe_status_t moe_permute_sizes(int T, int K, int E, int tile_m,
+                               int64_t *max_rows, int64_t *max_tiles);
+
+/*
+ * moe_permute -- expert histogram and stable expert-sorted permutation of
+ * the T*K slots (see moe_perm_t). The pages do not describe this step; it
+ * exists so that each touched expert's weights stream from HBM once
+ * (routed experts are 96.7 % of the weight bytes: page
+ * "NeuroSenko/Step-5-Preview-Int4-g128", "Recipe").
+ * topk_ids [T][K] int32 with values in [0, E). tile_m in [1, 256].
+ * Deterministic: no atomics decide any order.
+ */
+moe_status_t moe_permute(const int32_t *topk_ids, int T, int K, int E,
+                         const moe_perm_t *perm, void *stream);
+
+/* The tile_m the forward pass needs for T tokens (host output), and the
+ * workspace bytes it needs (host output). Pass that tile_m to moe_permute. */
+moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts,
+                              const moe_ffn_desc_t *shared, int T, int K,
+                              int act_dtype, int *tile_m, size_t *ws_bytes);
+
+/*
+ * moe_w4a16_forward -- the routed experts, the optional shared expert and
+ * the weighted combine (page "Step 5 Preview: ...", "The shape: narrow and
+ * deep": 8 routed experts per token plus one shared expert, each a SwiGLU of
+ * width 1536; the residual stream is fp32 per the same page's paragraph on
+ * fp32_residual_connection):
+ *
+ *   for each slot s = (t, k) routed to expert e:
+ *     h_s = silu(Wg_e x_t) * (Wu_e x_t),   y_s = Wd_e h_s
+ *   out_t = sum_{k ascending} topk_w[t][k] * y_(t,k)
+ *           [+ Wd_sh (silu(Wg_sh x_t) * (Wu_sh x_t))]  [+ residual_t]
+ *
+ * x [T][H] in act_dtype (MOE_F16 or MOE_BF16); experts: int4-g128 or NVFP4
+ * bank with gate/up [F][H] and down [H][F]; shared: NULL or a MOE_W_BF16
+ * bank with num_experts == 1 (act_dtype must then be MOE_BF16);
+ * topk_w [T][K] float; perm: moe_permute output for this routing with the
+ * tile_m from moe_forward_plan; residual: NULL or [T][H] float;
+ * out [T][H] in out_dtype (MOE_F32, MOE_F16 or MOE_BF16); ws: device
+ * workspace of at least moe_forward_plan's ws_bytes, 256-byte aligned.
+ * Accumulation is float32; h is rounded to act_dtype before the down
+ * projection. Limits: H % 128 == 0, F % 128 == 0 (int4) or % 16 (NVFP4),
+ * H and F <= 16384, E <= 512.
+ */
+moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts,
+                               const moe_ffn_desc_t *shared,
+                               const void *x, int act_dtype, int T, int K,
+                               const float *topk_w, const moe_perm_t *perm,
+                               const float *residual, void *out, int out_dtype,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_dequant -- the exact dequantized matrix of one expert, as float32
+ * [n][k] (int4: q * scale; NVFP4: (e2m1 * e4m3) * global_scale with one
+ * float32 rounding). Uses the same in-kernel decode as the forward pass.
+ */
+moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

@@ -1,0 +1,221 @@
+"""Thin Python binding of libmoe_w4a16.so (ctypes).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the layer runs in the library's HIP kernels. The
+function names are the C entry points' names. If the library is missing
+the calls raise: there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_w4a16.so")
+_lib = None
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+MOE_F16, MOE_BF16, MOE_F32 = 1, 2, 3
+MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16 = 1, 2, 3
+
+EXPORTS = ("moe_status_string", "moe_abi_version", "moe_route_topk", "moe_permute_sizes",
+           "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_dequant")
+
+_DT = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
+_TD = {v: k for k, v in _DT.items()}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_string(status)))
+
+
+class WeightDesc(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("qweight", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p),
+                ("qweight_expert_stride", ctypes.c_int64), ("qweight_row_stride", ctypes.c_int64),
+                ("scale_expert_stride", ctypes.c_int64), ("scale_row_stride", ctypes.c_int64)]
+
+
+class FfnDesc(ctypes.Structure):
+    _fields_ = [("gate", WeightDesc), ("up", WeightDesc), ("down", WeightDesc)]
+
+
+class PermDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("counts", "expert_offsets", "padded_offsets", "sorted_slots", "slot_to_row",
+                 "tile_expert", "num_tiles", "active_experts", "num_active")] + \
+               [("tile_m", ctypes.c_int32)]
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libmoe_w4a16.so is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        P = ctypes.POINTER
+        L.moe_status_string.argtypes = [i32]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_abi_version.restype = i32
+        L.moe_route_topk.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.moe_permute_sizes.argtypes = [i32, i32, i32, i32, P(i64), P(i64)]
+        L.moe_permute.argtypes = [vp, i32, i32, i32, P(PermDesc), vp]
+        L.moe_forward_plan.argtypes = [P(FfnDesc), P(FfnDesc), i32, i32, i32, P(i32), P(sz)]
+        L.moe_w4a16_forward.argtypes = [P(FfnDesc), P(FfnDesc), vp, i32, i32, i32, vp,
+                                        P(PermDesc), vp, vp, i32, vp, sz, vp]
+        L.moe_dequant.argtypes = [P(WeightDesc), i32, vp, vp]
+        for name in ("moe_route_topk", "moe_permute_sizes", "moe_permute", "moe_forward_plan",
+                     "moe_w4a16_forward", "moe_dequant"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(st):
+    return lib().moe_status_string(int(st)).decode()
+
+
+def _check(st, where):
+    if st != MOE_OK:
+        raise MoeError(st, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# ------------------------------------------------------------ descriptors ---
+def bank_int4(qweight, scale):
+    """qweight int32 [E, n, k/8], scale bf16 [E, n, k/128] (device)."""
+    E, n, kw = qweight.shape
+    d = WeightDesc(MOE_W_INT4_G128, E, n, kw * 8, qweight.data_ptr(), scale.data_ptr(), None,
+                   qweight.stride(0) * 4, qweight.stride(1) * 4,
+                   scale.stride(0) * 2, scale.stride(1) * 2)
+    d._keep = (qweight, scale)
+    return d
+
+
+def bank_nvfp4(qweight, scale, global_scale):
+    """qweight uint8 [E, n, k/2], scale uint8 (E4M3) [E, n, k/16], global_scale float [E]."""
+    E, n, kh = qweight.shape
+    d = WeightDesc(MOE_W_NVFP4_G16, E, n, kh * 2, qweight.data_ptr(), scale.data_ptr(),
+                   global_scale.data_ptr(), qweight.stride(0), qweight.stride(1),
+                   scale.stride(0), scale.stride(1))
+    d._keep = (qweight, scale, global_scale)
+    return d
+
+
+def ffn(gate, up, down):
+    f = FfnDesc(gate, up, down)
+    f._keep = (gate, up, down)
+    return f
+
+
+# ----------------------------------------------------------------- calls ---
+def moe_route_topk(K, x=None, router_wT=None, logits=None, bias=None, renormalize=True,
+                   ids=None, w=None):
+    """Returns (topk_ids int32 [T, K], topk_w float32 [T, K])."""
+    src = logits if logits is not None else x
+    T = src.shape[0]
+    E = logits.shape[1] if logits is not None else router_wT.shape[1]
+    H = x.shape[1] if x is not None else 0
+    dev = src.device
+    if ids is None:
+        ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    xd = _DT.get(x.dtype, 0) if x is not None else 0
+    st = lib().moe_route_topk(_ptr(x), xd, _ptr(router_wT), _ptr(logits), _ptr(bias), T, H, E,
+                              K, int(bool(renormalize)), _ptr(ids), _ptr(w), _stream(dev))
+    _check(st, "moe_route_topk")
+    return ids, w
+
+
+def moe_permute_sizes(T, K, E, tile_m):
+    mr, mt = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().moe_permute_sizes(T, K, E, tile_m, ctypes.byref(mr), ctypes.byref(mt)),
+           "moe_permute_sizes")
+    return mr.value, mt.value
+
+
+class Perm:
+    """Device arrays of one permutation (see moe_perm_t)."""
+
+    FIELDS = ("counts", "expert_offsets", "padded_offsets", "sorted_slots", "slot_to_row",
+              "tile_expert", "num_tiles", "active_experts", "num_active")
+
+    def __init__(self, T, K, E, tile_m, device):
+        mr, mt = moe_permute_sizes(T, K, E, tile_m)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.tile_m, self.E = tile_m, E
+        self.counts = torch.zeros(E, **i32)
+        self.expert_offsets = torch.zeros(E + 1, **i32)
+        self.padded_offsets = torch.zeros(E + 1, **i32)
+        self.sorted_slots = torch.full((max(mr, 1),), -2, **i32)
+        self.slot_to_row = torch.zeros(max(T * K, 1), **i32)
+        self.tile_expert = torch.full((max(mt, 1),), -2, **i32)
+        self.num_tiles = torch.zeros(1, **i32)
+        self.active_experts = torch.full((E,), -2, **i32)
+        self.num_active = torch.zeros(1, **i32)
+
+    def desc(self):
+        d = PermDesc(*[getattr(self, f).data_ptr() for f in self.FIELDS], self.tile_m)
+        return d
+
+
+def moe_permute(topk_ids, E, tile_m, perm=None):
+    T, K = topk_ids.shape
+    if perm is None:
+        perm = Perm(T, K, E, tile_m, topk_ids.device)
+    d = perm.desc()
+    _check(lib().moe_permute(_ptr(topk_ids), T, K, E, ctypes.byref(d), _stream(topk_ids.device)),
+           "moe_permute")
+    return perm
+
+
+def moe_forward_plan(experts, T, K, act_dtype, shared=None):
+    tm, ws = ctypes.c_int(), ctypes.c_size_t()
+    st = lib().moe_forward_plan(ctypes.byref(experts), ctypes.byref(shared) if shared else None,
+                                T, K, _DT[act_dtype], ctypes.byref(tm), ctypes.byref(ws))
+    _check(st, "moe_forward_plan")
+    return tm.value, ws.value
+
+
+def moe_w4a16_forward(experts, x, topk_w, perm, residual=None, out_dtype=torch.float32,
+                      shared=None, out=None, ws=None):
+    T, H = x.shape
+    K = topk_w.shape[1]
+    dev = x.device
+    _, need = moe_forward_plan(experts, T, K, x.dtype, shared)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    pd = perm.desc()
+    st = lib().moe_w4a16_forward(ctypes.byref(experts), ctypes.byref(shared) if shared else None,
+                                 _ptr(x), _DT[x.dtype], T, K, _ptr(topk_w), ctypes.byref(pd),
+                                 _ptr(residual), _ptr(out), _DT[out.dtype], _ptr(ws),
+                                 ws.numel(), _stream(dev))
+    _check(st, "moe_w4a16_forward")
+    return out
+
+
+def moe_dequant(desc, expert, out=None, device=None):
+    if out is None:
+        out = torch.empty((desc.n, desc.k), dtype=torch.float32, device=device or "cuda")
+    _check(lib().moe_dequant(ctypes.byref(desc), expert, _ptr(out), _stream(out.device)),
+           "moe_dequant")
+    return out

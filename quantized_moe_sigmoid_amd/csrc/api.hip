@@ -1,0 +1,215 @@
+// C ABI of the MoE library: host-side validation, workspace planning and
+// dispatch to the kernels. Every check runs before the first launch, so an
+// invalid call enqueues nothing.
+#include <string.h>
+
+#include "common.h"
+
+namespace moe {
+moe_status_t launch_route(const void *x, int x_dtype, const float *wT, const float *logits,
+                          const float *bias, int T, int H, int E, int K, int renorm,
+                          int32_t *ids, float *wts, hipStream_t s);
+moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_perm_t &p,
+                            hipStream_t s);
+moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out, hipStream_t s);
+moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
+                                 const moe_perm_t &p, int max_tiles, void *h, float *y,
+                                 hipStream_t s);
+moe_status_t launch_combine(const float *y, const int32_t *slot_to_row, const float *w, int T,
+                            int K, int H, const float *shared, const float *residual, void *out,
+                            int out_dtype, hipStream_t s);
+int gemv_tile_m();
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxDim = 16384;
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t perm_max_rows(int T, int K, int E, int tile_m) {
+    const int64_t n = (int64_t)T * K;
+    return n + (n < E ? n : E) * (int64_t)(tile_m - 1);
+}
+
+// A quantized bank of E matrices [n][k]: format rules and alignment.
+moe_status_t check_bank(const moe_weight_desc_t &d, int E, int n, int k) {
+    if (d.num_experts != E || d.n != n || d.k != k) return MOE_ERR_INVALID_ARG;
+    if (!d.qweight || !d.scale) return MOE_ERR_INVALID_ARG;
+    if (n <= 0 || k <= 0 || n > kMaxDim || k > kMaxDim) return MOE_ERR_INVALID_ARG;
+    if (!aligned(d.qweight, 16) || d.qweight_row_stride % 16 || d.qweight_expert_stride % 16)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(d.scale, 2) || d.scale_row_stride % 2 || d.scale_expert_stride % 2)
+        return MOE_ERR_INVALID_ARG;
+    if (d.fmt == MOE_W_INT4_G128) {
+        if (k % 128) return MOE_ERR_INVALID_ARG;
+        if (d.qweight_row_stride < k / 2 || d.scale_row_stride < (k / 128) * 2)
+            return MOE_ERR_INVALID_ARG;
+    } else if (d.fmt == MOE_W_NVFP4_G16) {
+        if (k % 16) return MOE_ERR_INVALID_ARG;
+        if (k % 32) return MOE_ERR_UNSUPPORTED;     // kernels read 32 inputs per 16 bytes
+        if (!d.global_scale || !aligned(d.global_scale, 4)) return MOE_ERR_INVALID_ARG;
+        if (d.qweight_row_stride < k / 2 || d.scale_row_stride < k / 16)
+            return MOE_ERR_INVALID_ARG;
+    } else {
+        return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+moe_status_t check_experts(const moe_ffn_desc_t *ex, int *E, int *H, int *F) {
+    if (!ex) return MOE_ERR_INVALID_ARG;
+    const int e = ex->gate.num_experts, f = ex->gate.n, h = ex->gate.k;
+    if (e < 1 || e > kMaxExperts) return MOE_ERR_INVALID_ARG;
+    if (ex->up.fmt != ex->gate.fmt || ex->down.fmt != ex->gate.fmt) return MOE_ERR_INVALID_ARG;
+    moe_status_t st;
+    if ((st = check_bank(ex->gate, e, f, h)) != MOE_OK) return st;
+    if ((st = check_bank(ex->up, e, f, h)) != MOE_OK) return st;
+    if ((st = check_bank(ex->down, e, h, f)) != MOE_OK) return st;
+    *E = e; *H = h; *F = f;
+    return MOE_OK;
+}
+
+bool is_act(int d) { return d == MOE_F16 || d == MOE_BF16; }
+
+moe_status_t check_perm(const moe_perm_t *p) {
+    if (!p || !p->counts || !p->expert_offsets || !p->padded_offsets || !p->sorted_slots ||
+        !p->slot_to_row || !p->tile_expert || !p->num_tiles || !p->active_experts ||
+        !p->num_active)
+        return MOE_ERR_INVALID_ARG;
+    if (p->tile_m < 1 || p->tile_m > 256) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+struct FwdPlan {
+    int tile_m;
+    int64_t max_rows, max_tiles;
+    size_t off_h, off_y, total;
+};
+
+FwdPlan plan_forward(int T, int K, int E, int H, int F, int act) {
+    (void)act;
+    FwdPlan p;
+    p.tile_m = gemv_tile_m();
+    p.max_rows = perm_max_rows(T, K, E, p.tile_m);
+    p.max_tiles = p.max_rows / p.tile_m;
+    p.off_h = 0;
+    p.off_y = align256((size_t)p.max_rows * F * 2);
+    p.total = p.off_y + align256((size_t)p.max_rows * H * 4);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+int moe_abi_version(void) { return 1; }
+
+moe_status_t moe_route_topk(const void *x, int x_dtype, const float *router_wT,
+                            const float *logits_in, const float *bias, int T, int H, int E,
+                            int K, int renormalize, int32_t *topk_ids, float *topk_w,
+                            void *stream) {
+    if (T < 0 || E < 1 || E > kMaxExperts || K < 1 || K > E || K > kMaxTopK)
+        return MOE_ERR_INVALID_ARG;
+    if (!topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if ((router_wT == nullptr) == (logits_in == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (router_wT) {
+        if (!x || !is_act(x_dtype) || H < 1 || H % 8) return MOE_ERR_INVALID_ARG;
+    }
+    if (T == 0) return MOE_OK;
+    return launch_route(x, x_dtype, router_wT, logits_in, bias, T, H, E, K, renormalize,
+                        topk_ids, topk_w, (hipStream_t)stream);
+}
+
+moe_status_t moe_permute_sizes(int T, int K, int E, int tile_m, int64_t *max_rows,
+                               int64_t *max_tiles) {
+    if (T < 0 || K < 1 || E < 1 || E > kMaxExperts || tile_m < 1 || tile_m > 256 ||
+        !max_rows || !max_tiles)
+        return MOE_ERR_INVALID_ARG;
+    *max_rows = perm_max_rows(T, K, E, tile_m);
+    *max_tiles = *max_rows / tile_m;
+    return MOE_OK;
+}
+
+moe_status_t moe_permute(const int32_t *topk_ids, int T, int K, int E, const moe_perm_t *perm,
+                         void *stream) {
+    if (T < 0 || K < 1 || E < 1 || E > kMaxExperts) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)T * K > (1 << 24)) return MOE_ERR_UNSUPPORTED;
+    if (T > 0 && !topk_ids) return MOE_ERR_INVALID_ARG;
+    moe_status_t st = check_perm(perm);
+    if (st != MOE_OK) return st;
+    return launch_permute(topk_ids, T, K, E, *perm, (hipStream_t)stream);
+}
+
+moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts, const moe_ffn_desc_t *shared,
+                              int T, int K, int act_dtype, int *tile_m, size_t *ws_bytes) {
+    int E, H, F;
+    moe_status_t st = check_experts(experts, &E, &H, &F);
+    if (st != MOE_OK) return st;
+    if (T < 0 || K < 1 || K > E || !is_act(act_dtype) || !tile_m || !ws_bytes)
+        return MOE_ERR_INVALID_ARG;
+    if (shared) return MOE_ERR_UNSUPPORTED;
+    const FwdPlan p = plan_forward(T, K, E, H, F, act_dtype);
+    *tile_m = p.tile_m;
+    *ws_bytes = p.total;
+    return MOE_OK;
+}
+
+moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts, const moe_ffn_desc_t *shared,
+                               const void *x, int act_dtype, int T, int K, const float *topk_w,
+                               const moe_perm_t *perm, const float *residual, void *out,
+                               int out_dtype, void *ws, size_t ws_bytes, void *stream) {
+    int E, H, F;
+    moe_status_t st = check_experts(experts, &E, &H, &F);
+    if (st != MOE_OK) return st;
+    if (T < 0 || K < 1 || K > E || !is_act(act_dtype)) return MOE_ERR_INVALID_ARG;
+    if (out_dtype != MOE_F32 && !is_act(out_dtype)) return MOE_ERR_INVALID_ARG;
+    if ((st = check_perm(perm)) != MOE_OK) return st;
+    if (shared) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_w || !out || !ws) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256) ||
+        (residual && !aligned(residual, 16)))
+        return MOE_ERR_INVALID_ARG;
+    const FwdPlan p = plan_forward(T, K, E, H, F, act_dtype);
+    if (perm->tile_m != p.tile_m) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (p.max_tiles > 65535) return MOE_ERR_UNSUPPORTED;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    void *h = w + p.off_h;
+    float *y = (float *)(w + p.off_y);
+    st = launch_gemv_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s);
+    if (st != MOE_OK) return st;
+    return launch_combine(y, perm->slot_to_row, topk_w, T, K, H, nullptr, residual, out,
+                          out_dtype, s);
+}
+
+moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out, void *stream) {
+    if (!w || !out) return MOE_ERR_INVALID_ARG;
+    const int E = w->num_experts;
+    if (E < 1 || E > kMaxExperts || expert < 0 || expert >= E) return MOE_ERR_INVALID_ARG;
+    moe_status_t st = check_bank(*w, E, w->n, w->k);
+    if (st != MOE_OK) return st;
+    if (!aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+    return launch_dequant(*w, expert, out, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Decoding of the 4-bit weight formats, shared by the dequant export and the
+// forward kernels.
+//
+// int4-g128 (page "NeuroSenko/Step-5-Preview-Int4-g128", "Recipe", "Tensor
+// layout"): int32 words along K, nibble j of a word = input 8w+j, a
+// two's-complement value in [-8, 7]; one bf16 scale per 128 inputs.
+//
+// NVFP4 (page "Step-5-Preview-NVFP4-Local", "Modifications" item 2,
+// "Format"): bytes of two E2M1 codes (low nibble = even input), one E4M3
+// block scale per 16 inputs, one float32 global scale per expert; value =
+// E2M1 x E4M3 x global scale.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// ---- int4 -------------------------------------------------------------------
+__device__ __forceinline__ int int4_q(uint32_t w, int j) {
+    return ((int32_t)(w << (28 - 4 * j))) >> 28;          // sign-extend nibble j
+}
+
+// The four 16-bit pairs of a word, each pair = inputs (8w+i, 8w+i+4), as the
+// exact 16-bit value BIAS + q: XOR 0x8 turns the two's-complement nibble
+// into q + 8 in [0, 15]; OR-ing that into the mantissa of 1024 (fp16, ulp 1)
+// or 128 (bf16, ulp 1) gives 1032 + q or 136 + q without any rounding.
+template <int ACT>
+struct Int4Bias;
+template <>
+struct Int4Bias<MOE_F16> {
+    static constexpr uint32_t kMagic = 0x64006400u;   // fp16 1024.0 in each half
+    static constexpr float kBias = 1032.0f;
+};
+template <>
+struct Int4Bias<MOE_BF16> {
+    static constexpr uint32_t kMagic = 0x43004300u;   // bf16 128.0 in each half
+    static constexpr float kBias = 136.0f;
+};
+
+template <int ACT>
+__device__ __forceinline__ void int4_biased_pairs(uint32_t w, uint32_t out[4]) {
+    const uint32_t u = w ^ 0x88888888u;
+    out[0] = (u & 0x000F000Fu) | Int4Bias<ACT>::kMagic;
+    out[1] = ((u >> 4) & 0x000F000Fu) | Int4Bias<ACT>::kMagic;
+    out[2] = ((u >> 8) & 0x000F000Fu) | Int4Bias<ACT>::kMagic;
+    out[3] = ((u >> 12) & 0x000F000Fu) | Int4Bias<ACT>::kMagic;
+}
+
+// ---- NVFP4 ------------------------------------------------------------------
+// E4M3FN byte -> float32 (exact): exponent bias 7, subnormals m * 2^-9.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 0xF, m = b & 7;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
+                        : (float)m * 0.001953125f;
+    return (b & 0x80) ? -mag : mag;
+}
+
+// E2M1 code -> float32 (exact): {0, .5, 1, 1.5, 2, 3, 4, 6}, sign bit 3.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 1) & 3, m = c & 1;
+    const float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
+    return (c & 8) ? -mag : mag;
+}
+
+// Two E2M1 codes of byte `SEL` of `w` as a 16-bit pair (element 0 = low
+// nibble = even input), exact, via the CDNA4 scaled FP4 conversion with a
+// unit scale.
+template <int ACT, int SEL>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w) {
+    if constexpr (ACT == MOE_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
+}
+
+// ---- 16-bit pair dot products with float32 accumulation --------------------
+template <int ACT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (ACT == MOE_BF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                               __builtin_bit_cast(bf162_t, b), c, false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a),
+                                      __builtin_bit_cast(half2_t, b), c, false);
+}
+
+}  // namespace moe

@@ -1,0 +1,74 @@
+// Export of one expert's dequantized matrix as float32 [n][k].
+//
+// It runs the forward kernels' own decoders: int4 words go through the
+// biased fp16 pairs (1032 + q, then the bias is removed exactly) and the
+// scale is applied as one exact float32 product; NVFP4 bytes go through the
+// hardware E2M1 pair conversion, the E4M3 scale multiplies exactly, and the
+// global scale is the single float32 rounding.
+#include "decode.h"
+
+namespace moe {
+
+__global__ void __launch_bounds__(256) dequant_int4_kernel(
+    const uint8_t *__restrict__ qw, int64_t qrow, const uint8_t *__restrict__ sc, int64_t srow,
+    int n, int k, float *__restrict__ out) {
+    const int words = k / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)n * words) return;
+    const int r = (int)(idx / words), j = (int)(idx % words);
+    const uint32_t w = *(const uint32_t *)(qw + r * qrow + 4 * (int64_t)j);
+    const uint16_t sb = *(const uint16_t *)(sc + r * srow + 2 * (int64_t)((8 * j) / 128));
+    const float s = bf16_bits_to_f32(sb);
+    uint32_t p[4];
+    int4_biased_pairs<MOE_F16>(w, p);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = (f16_bits_to_f32(p[i] & 0xFFFF) - Int4Bias<MOE_F16>::kBias) * s;
+        v[i + 4] = (f16_bits_to_f32(p[i] >> 16) - Int4Bias<MOE_F16>::kBias) * s;
+    }
+    float4 *o = (float4 *)(out + (int64_t)r * k + 8 * (int64_t)j);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+__global__ void __launch_bounds__(256) dequant_nvfp4_kernel(
+    const uint8_t *__restrict__ qw, int64_t qrow, const uint8_t *__restrict__ sc, int64_t srow,
+    const float *__restrict__ gsp, int n, int k, float *__restrict__ out) {
+    const float gs = *gsp;
+    const int dwords = k / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)n * dwords) return;
+    const int r = (int)(idx / dwords), j = (int)(idx % dwords);
+    const uint32_t w = *(const uint32_t *)(qw + r * qrow + 4 * (int64_t)j);
+    const float bs = e4m3_to_f32(sc[r * srow + (8 * j) / 16]);
+    const uint32_t p[4] = {fp4_pair<MOE_BF16, 0>(w), fp4_pair<MOE_BF16, 1>(w),
+                           fp4_pair<MOE_BF16, 2>(w), fp4_pair<MOE_BF16, 3>(w)};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = (bf16_bits_to_f32(p[i] & 0xFFFF) * bs) * gs;
+        v[2 * i + 1] = (bf16_bits_to_f32(p[i] >> 16) * bs) * gs;
+    }
+    float4 *o = (float4 *)(out + (int64_t)r * k + 8 * (int64_t)j);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out,
+                            hipStream_t s) {
+    const uint8_t *qw = (const uint8_t *)d.qweight + (int64_t)e * d.qweight_expert_stride;
+    const uint8_t *sc = (const uint8_t *)d.scale + (int64_t)e * d.scale_expert_stride;
+    const int64_t items = (int64_t)d.n * (d.k / 8);
+    const dim3 grid((unsigned)((items + 255) / 256));
+    if (d.fmt == MOE_W_INT4_G128)
+        hipLaunchKernelGGL(dequant_int4_kernel, grid, dim3(256), 0, s, qw, d.qweight_row_stride,
+                           sc, d.scale_row_stride, d.n, d.k, out);
+    else
+        hipLaunchKernelGGL(dequant_nvfp4_kernel, grid, dim3(256), 0, s, qw, d.qweight_row_stride,
+                           sc, d.scale_row_stride, d.global_scale + e, d.n, d.k, out);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+}  // namespace moe

@@ -95,3 +95,31 @@ def device_normal(shape, std, seed, device, dtype=None):
     g.manual_seed(int(seed))
     x = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
     return x if dtype is None else x.to(dtype)
+
+
+def packed_int4_random(E, n, k, seed, device, scale_mean=0.0043):
+    """Random int4-g128 bank drawn directly in packed form: uniform 32-bit
+    words (every nibble uniform over the 16 codes) and bf16 scales
+    scale_mean * (1 + 0.1 N(0, 1)), so the weights have a standard
+    deviation near 0.02. For full-size tests and benchmarks where drawing
+    and quantizing 6.6 G Gaussian weights on the host would take minutes."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    q = torch.randint(-2 ** 31, 2 ** 31 - 1, (E, n, k // 8), generator=g, device=device,
+                      dtype=torch.int32)
+    s = (torch.randn((E, n, k // 128), generator=g, device=device) * 0.1 + 1.0) * scale_mean
+    return q, s.to(torch.bfloat16)
+
+
+def packed_nvfp4_random(E, n, k, seed, device, gs_mean=2.0e-5):
+    """Random NVFP4 bank in packed form: uniform bytes (two uniform E2M1
+    codes each), E4M3 block-scale bytes uniform in [0x70, 0x7E] (128 .. 448)
+    and float32 global scales gs_mean * (1 + 0.1 N(0, 1))."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    q = torch.randint(0, 256, (E, n, k // 2), generator=g, device=device, dtype=torch.uint8)
+    s = torch.randint(0x70, 0x7F, (E, n, k // 16), generator=g, device=device, dtype=torch.uint8)
+    gs = (torch.randn((E,), generator=g, device=device) * 0.1 + 1.0) * gs_mean
+    return q, s, gs.float()

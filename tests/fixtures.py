@@ -1,0 +1,76 @@
+"""Shared helpers of the test suite: seeded inputs quantized by the oracle,
+conversion to device tensors, oracle references and the tolerance rule."""
+import numpy as np
+import torch
+
+from oracle import formats as OF
+from oracle import layer as OL
+from oracle import quant as OQ
+from quantized_moe_sigmoid_amd import synth
+
+TENSOR_OF = {"gate": synth.T_GATE, "up": synth.T_UP, "down": synth.T_DOWN}
+
+
+def int4_bank_oracle(E, n, k, root, layer, which):
+    """Gaussian bf16 weights quantized by the oracle's clip search and packed.
+    Returns (words int32 [E, n, k/8], scale bits uint16 [E, n, k/128])."""
+    q = np.empty((E, n, k // 8), dtype=np.int32)
+    s = np.empty((E, n, k // 128), dtype=np.uint16)
+    for e in range(E):
+        W = synth.expert_weight_bf16(n, k, root, layer, TENSOR_OF[which], e)
+        qq, ss = OQ.quantize_int4(W.float().numpy().astype(np.float64))
+        q[e] = OQ.pack_int4(qq)
+        s[e] = OF.bf16_bits(ss)
+    return q, s
+
+
+def nvfp4_bank_oracle(E, n, k, root, layer, which):
+    """Gaussian bf16 weights quantized by the oracle's NVFP4 rule and packed.
+    Returns (bytes uint8 [E, n, k/2], E4M3 bytes uint8 [E, n, k/16], gs float32 [E])."""
+    q = np.empty((E, n, k // 2), dtype=np.uint8)
+    s = np.empty((E, n, k // 16), dtype=np.uint8)
+    gs = np.empty((E,), dtype=np.float32)
+    for e in range(E):
+        W = synth.expert_weight_bf16(n, k, root, layer, TENSOR_OF[which], e)
+        codes, bs, g = OQ.quantize_nvfp4(W.float().numpy().astype(np.float64))
+        q[e] = OQ.pack_nvfp4(codes)
+        s[e] = OQ.e4m3_bytes(bs)
+        gs[e] = g
+    return q, s, gs
+
+
+def int4_to_device(q, s_bits, device="cuda"):
+    qt = torch.from_numpy(np.ascontiguousarray(q)).to(device)
+    st = torch.from_numpy(np.ascontiguousarray(s_bits).view(np.int16)).view(torch.bfloat16).to(device)
+    return qt, st
+
+
+def int4_from_device(qt, st):
+    q = qt.cpu().numpy()
+    s = st.view(torch.int16).cpu().numpy().view(np.uint16)
+    return q, s
+
+
+def oracle_int4_expert(q, s, e):
+    return OQ.dequant_int4(q[e], s[e])
+
+
+def oracle_nvfp4_expert(q, s, gs, e):
+    return OQ.dequant_nvfp4(q[e], s[e], float(gs[e]))
+
+
+def within_tolerance(gpu, ref, rel=1e-2):
+    """|gpu - ref| <= rel * (|ref| + rms(ref)) elementwise, rms over the whole
+    output. Returns (ok, worst ratio)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    bound = rel * (np.abs(ref) + rms)
+    err = np.abs(gpu - ref)
+    ratio = float(np.max(err / np.maximum(bound, 1e-300))) if ref.size else 0.0
+    return bool(np.all(err <= bound)), ratio
+
+
+def oracle_layer(x16, ids, w, experts_fn, shared=None, residual=None):
+    x = x16.float().cpu().numpy().astype(np.float64)
+    return OL.moe_layer(x, ids, np.asarray(w, dtype=np.float64), experts_fn, shared, residual)

@@ -1,0 +1,306 @@
+"""GPU parity of every step of the layer against the CPU oracle, through the
+C ABI: dequant and routing bit for bit, permutation bit for bit, layer
+outputs within |gpu - oracle| <= 1e-2 (|oracle| + rms(oracle))."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import permute as OP
+from oracle import quant as OQ
+from oracle import router as OR
+from quantized_moe_sigmoid_amd import binding as B
+from quantized_moe_sigmoid_amd import synth
+from tests import fixtures as FX
+
+pytestmark = pytest.mark.gpu
+
+H, F, E, K = 4096, 1536, 352, 8
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    return torch.device("cuda:0")
+
+
+def _bits_equal(a, b):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------------ dequant ---
+def test_dequant_int4_bitwise_tiny(dev):
+    cfg = synth.CONFIGS["tiny"]
+    for which, (n, k) in (("gate", (cfg["F"], cfg["H"])), ("down", (cfg["H"], cfg["F"]))):
+        q, s = FX.int4_bank_oracle(cfg["E"], n, k, 0, 0, which)
+        qt, st = FX.int4_to_device(q, s, dev)
+        d = B.bank_int4(qt, st)
+        for e in range(cfg["E"]):
+            got = B.moe_dequant(d, e, device=dev).cpu().numpy()
+            assert _bits_equal(got, FX.oracle_int4_expert(q, s, e)), (which, e)
+
+
+def test_dequant_int4_bitwise_full_shape_sampled(dev):
+    qt, st = synth.packed_int4_random(E, F, H, 11, dev)
+    d = B.bank_int4(qt, st)
+    for e in (0, 177, 351):
+        got = B.moe_dequant(d, e, device=dev).cpu().numpy()
+        q = qt[e].cpu().numpy()
+        sb = st[e].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert _bits_equal(got, OQ.dequant_int4(q, sb)), e
+
+
+def test_dequant_nvfp4_bitwise(dev):
+    q, s, gs = FX.nvfp4_bank_oracle(3, 64, 512, 4, 0, "up")
+    d = B.bank_nvfp4(torch.from_numpy(q).to(dev), torch.from_numpy(s).to(dev),
+                     torch.from_numpy(gs).to(dev))
+    for e in range(3):
+        got = B.moe_dequant(d, e, device=dev).cpu().numpy()
+        want = OQ.dequant_nvfp4_fp32(q[e], s[e], gs[e])
+        assert _bits_equal(got, want), e
+    qt, st, gt = synth.packed_nvfp4_random(E, H, F, 12, dev)
+    d = B.bank_nvfp4(qt, st, gt)
+    for e in (5, 300):
+        got = B.moe_dequant(d, e, device=dev).cpu().numpy()
+        want = OQ.dequant_nvfp4_fp32(qt[e].cpu().numpy(), st[e].cpu().numpy(),
+                                     float(gt[e].cpu()))
+        assert _bits_equal(got, want), e
+
+
+# ------------------------------------------------------------------ routing ---
+def _check_route(ids, w, lg_used, K):
+    want_ids = OR.topk_ids(lg_used, K)
+    assert np.array_equal(ids.cpu().numpy(), want_ids)
+    want_w = OR.routing_weights(lg_used, want_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), want_w, rtol=1e-5, atol=0)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 256, 2048])
+def test_route_given_logits(dev, T):
+    lg = synth.router_logits(T, E, 2)
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    _check_route(ids, w, lg, K)
+    b = synth.zipf_bias(E, 2)
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev),
+                              bias=torch.from_numpy(b).to(dev))
+    _check_route(ids, w, (lg + b).astype(np.float32), K)
+
+
+def test_route_adversarial_ties(dev):
+    T = 6
+    lg = np.zeros((T, E), dtype=np.float32)
+    lg[1, :] = -0.0
+    lg[1, 100:] = 0.0
+    lg[2, [5, 70, 300, 7]] = 1.5                 # four-way tie inside the top-8
+    lg[3, :] = np.repeat(np.arange(44, dtype=np.float32), 8)   # ties across the K boundary
+    lg[4, 351] = 3.0
+    lg[5, :] = -50.0                             # all equal and tiny sigmoid
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    _check_route(ids, w, lg, K)
+    ids, w = B.moe_route_topk(3, logits=torch.from_numpy(lg).to(dev), renormalize=False)
+    got = ids.cpu().numpy()
+    assert np.array_equal(got, OR.topk_ids(lg, 3))
+    np.testing.assert_allclose(w.cpu().numpy(), OR.routing_weights(lg, got, False), rtol=1e-5)
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_route_from_router_weight_tiny(dev, act):
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.activations(8, cfg["H"], act, 0)
+    wT = synth.router_weight_T(cfg["H"], cfg["E"], 0)
+    lg = OR.router_logits(x.float().numpy(), wT)
+    ids, w = B.moe_route_topk(cfg["K"], x=x.to(dev), router_wT=torch.from_numpy(wT).to(dev))
+    _check_route(ids, w, lg, cfg["K"])
+
+
+@pytest.mark.parametrize("T,zipf", [(37, False), (2048, False), (300, True)])
+def test_route_from_router_weight_full(dev, T, zipf):
+    x = synth.activations(T, H, "bf16", 3)
+    wT = synth.router_weight_T(H, E, 3)
+    b = synth.zipf_bias(E, 3) if zipf else None
+    lg = OR.router_logits(x.float().numpy(), wT, b)
+    ids, w = B.moe_route_topk(K, x=x.to(dev), router_wT=torch.from_numpy(wT).to(dev),
+                              bias=None if b is None else torch.from_numpy(b).to(dev))
+    _check_route(ids, w, lg, K)
+
+
+# -------------------------------------------------------------- permutation ---
+@pytest.mark.parametrize("T,Kk,Ee,tm,skew", [(1, 8, 352, 4, False), (64, 8, 352, 4, False),
+                                             (2048, 8, 352, 64, False), (2048, 8, 352, 64, True),
+                                             (4096, 8, 352, 128, True), (8, 2, 16, 4, False),
+                                             (3, 3, 5, 1, False), (0, 8, 352, 4, False)])
+def test_permute_bitwise(dev, T, Kk, Ee, tm, skew):
+    r = np.random.default_rng(T * 7 + Kk)
+    if skew:
+        p = 1.0 / np.arange(1, Ee + 1) ** 1.1
+        p = p / p.sum()
+        ids = np.stack([r.choice(Ee, Kk, replace=False, p=p) for _ in range(T)]) if T else \
+            np.zeros((0, Kk), dtype=np.int64)
+    else:
+        ids = np.stack([r.choice(Ee, Kk, replace=False) for _ in range(T)]) if T else \
+            np.zeros((0, Kk), dtype=np.int64)
+    ids = ids.astype(np.int32)
+    perm = B.moe_permute(torch.from_numpy(ids).reshape(T, Kk).to(dev), Ee, tm)
+    torch.cuda.synchronize()
+    want = OP.permute(ids.reshape(T, Kk), Ee, tm)
+    tot = int(want["padded_offsets"][-1])
+    assert np.array_equal(perm.counts.cpu().numpy(), want["counts"])
+    assert np.array_equal(perm.expert_offsets.cpu().numpy(), want["expert_offsets"])
+    assert np.array_equal(perm.padded_offsets.cpu().numpy(), want["padded_offsets"])
+    assert np.array_equal(perm.sorted_slots.cpu().numpy()[:tot], want["sorted_slots"])
+    if T:
+        assert np.array_equal(perm.slot_to_row.cpu().numpy(), want["slot_to_row"])
+    assert int(perm.num_tiles.cpu()[0]) == want["num_tiles"]
+    assert np.array_equal(perm.tile_expert.cpu().numpy()[:want["num_tiles"]], want["tile_expert"])
+    na = want["num_active"]
+    assert int(perm.num_active.cpu()[0]) == na
+    assert np.array_equal(perm.active_experts.cpu().numpy()[:na], want["active_experts"])
+
+
+# ------------------------------------------------------------------ forward ---
+def _int4_ffn_from_oracle(E_, H_, F_, root, dev):
+    banks, host = [], []
+    for which, (n, k) in (("gate", (F_, H_)), ("up", (F_, H_)), ("down", (H_, F_))):
+        q, s = FX.int4_bank_oracle(E_, n, k, root, 0, which)
+        qt, st = FX.int4_to_device(q, s, dev)
+        banks.append(B.bank_int4(qt, st))
+        host.append((q, s))
+    return B.ffn(*banks), host
+
+
+def _int4_ffn_random(E_, H_, F_, seed, dev):
+    banks, host = [], []
+    for i, (n, k) in enumerate(((F_, H_), (F_, H_), (H_, F_))):
+        qt, st = synth.packed_int4_random(E_, n, k, seed + i, dev)
+        banks.append(B.bank_int4(qt, st))
+        host.append((qt, st))
+    return B.ffn(*banks), host
+
+
+def _experts_fn_int4(host):
+    cache = {}
+
+    def fn(e):
+        if e not in cache:
+            mats = []
+            for (q, s) in host:
+                if isinstance(q, torch.Tensor):
+                    qq = q[e].cpu().numpy()
+                    ss = s[e].view(torch.int16).cpu().numpy().view(np.uint16)
+                else:
+                    qq, ss = q[e], s[e]
+                mats.append(OQ.dequant_int4(qq, ss))
+            cache[e] = tuple(mats)
+        return cache[e]
+    return fn
+
+
+def _run_layer(dev, ffn, x, ids, w, Ee, residual=None, out_dtype=torch.float32):
+    tm, _ = B.moe_forward_plan(ffn, x.shape[0], ids.shape[1], x.dtype)
+    perm = B.moe_permute(ids, Ee, tm)
+    return B.moe_w4a16_forward(ffn, x, w, perm, residual=residual, out_dtype=out_dtype)
+
+
+def test_forward_tiny_end_to_end(dev):
+    """The tiny layer: router from weights, clip-search int4 experts."""
+    cfg = synth.CONFIGS["tiny"]
+    T, Hh, Ee, Kk, Ff = 8, cfg["H"], cfg["E"], cfg["K"], cfg["F"]
+    ffn, host = _int4_ffn_from_oracle(Ee, Hh, Ff, 0, dev)
+    x = synth.activations(T, Hh, "f16", 0)
+    wT = synth.router_weight_T(Hh, Ee, 0)
+    ids, w = B.moe_route_topk(Kk, x=x.to(dev), router_wT=torch.from_numpy(wT).to(dev))
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, Ee).cpu().numpy()
+    lg, oids, ow = OR.route(x=x.float().numpy(), wT=wT, K=Kk)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    ref = FX.oracle_layer(x, oids, ow, _experts_fn_int4(host))
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_forward_decode_full_shape(dev, T):
+    """Decode shape: 352 int4 experts, hidden 4096, width 1536, fp16 x,
+    given logits. Every token for T <= 8, four sampled tokens for T = 64."""
+    ffn, host = _int4_ffn_random(E, H, F, 100 + T, dev)
+    x = synth.activations(T, H, "f16", 2)
+    lg = synth.router_logits(T, E, 2)
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, E).cpu().numpy()
+    toks = list(range(T)) if T <= 8 else [0, 17, 40, 63]
+    oids = OR.topk_ids(lg, K)
+    ow = OR.routing_weights(lg, oids)
+    ref = FX.oracle_layer(x[toks], oids[toks], ow[toks], _experts_fn_int4(host))
+    ok, ratio = FX.within_tolerance(out[toks], ref)
+    assert ok, ratio
+
+
+def test_forward_nvfp4_small(dev):
+    Ee, Hh, Ff, T, Kk = 6, 512, 256, 5, 3
+    banks, host = [], []
+    for which, (n, k) in (("gate", (Ff, Hh)), ("up", (Ff, Hh)), ("down", (Hh, Ff))):
+        q, s, gs = FX.nvfp4_bank_oracle(Ee, n, k, 4, 0, which)
+        banks.append(B.bank_nvfp4(torch.from_numpy(q).to(dev), torch.from_numpy(s).to(dev),
+                                  torch.from_numpy(gs).to(dev)))
+        host.append((q, s, gs))
+    ffn = B.ffn(*banks)
+    x = synth.activations(T, Hh, "bf16", 4)
+    lg = synth.router_logits(T, Ee, 4)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, Ee).cpu().numpy()
+    oids = OR.topk_ids(lg, Kk)
+    ow = OR.routing_weights(lg, oids)
+
+    def efn(e):
+        return tuple(FX.oracle_nvfp4_expert(q, s, gs, e) for (q, s, gs) in host)
+    ref = FX.oracle_layer(x, oids, ow, efn)
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
+def test_forward_nvfp4_decode_full_shape(dev):
+    T = 1
+    banks, host = [], []
+    for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
+        qt, st, gt = synth.packed_nvfp4_random(E, n, k, 40 + i, dev)
+        banks.append(B.bank_nvfp4(qt, st, gt))
+        host.append((qt, st, gt))
+    ffn = B.ffn(*banks)
+    x = synth.activations(T, H, "bf16", 4)
+    lg = synth.router_logits(T, E, 4)
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, E).cpu().numpy()
+    oids = OR.topk_ids(lg, K)
+    ow = OR.routing_weights(lg, oids)
+
+    def efn(e):
+        return tuple(OQ.dequant_nvfp4(q[e].cpu().numpy(), s[e].cpu().numpy(), float(g[e].cpu()))
+                     for (q, s, g) in host)
+    ref = FX.oracle_layer(x, oids, ow, efn)
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
+# --------------------------------------------------------------- properties ---
+def test_forward_properties(dev):
+    """Determinism, zero input, residual pass-through, and exact doubling of
+    the output when every down-projection scale doubles."""
+    Ee, Hh, Ff, T, Kk = 16, 512, 256, 12, 4
+    ffn, host = _int4_ffn_random(Ee, Hh, Ff, 7, dev)
+    x = synth.activations(T, Hh, "bf16", 9).to(dev)
+    lg = torch.from_numpy(synth.router_logits(T, Ee, 9)).to(dev)
+    ids, w = B.moe_route_topk(Kk, logits=lg)
+    a = _run_layer(dev, ffn, x, ids, w, Ee)
+    b = _run_layer(dev, ffn, x, ids, w, Ee)
+    assert torch.equal(a, b)
+    z = _run_layer(dev, ffn, torch.zeros_like(x), ids, w, Ee)
+    assert torch.count_nonzero(z) == 0
+    res = torch.randn(T, Hh, device=dev)
+    r = _run_layer(dev, ffn, torch.zeros_like(x), ids, w, Ee, residual=res)
+    assert torch.equal(r, res)
+    qd, sd = host[2]
+    ffn2 = B.ffn(ffn.gate, ffn.up, B.bank_int4(qd, (sd.float() * 2).to(torch.bfloat16)))
+    c = _run_layer(dev, ffn2, x, ids, w, Ee)
+    assert torch.equal(c, 2 * a)
