@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Throughput of the W4A16 routed-expert MoE layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch: sigmoid top-8
+routing, expert histogram + permutation, the int4 (or NVFP4) SwiGLU experts
+and the weighted combine, all in the HIP library. Inputs are synthetic,
+seeded and resident in HBM before the timed region; weights rotate over
+several copies and every step routes a fresh batch of logits, so the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+Prints one JSON line: tokens/s of the chosen workload, the roofline of its
+dominant kernel (algorithmic bytes or FLOPs per launch over the launch's
+HIP-event duration, against the MI355X peak), the CPU oracle timed on a
+bounded sample, and a sweep over the other layer shapes.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|nvfp4]
+                  [--tokens T] [--no-sweep] [--no-cpu-baseline]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from quantized_moe_sigmoid_amd import binding as B  # noqa: E402
+from quantized_moe_sigmoid_amd import synth  # noqa: E402
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # FLOP/s, dense bf16 / fp16
+H, F, E, K = 4096, 1536, 352, 8
+# Algorithmic bytes of one touched expert (packed weights + scales).
+INT4_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 128) * 2)
+INT4_DOWN_BYTES = H * F // 2 + H * (F // 128) * 2
+NVFP4_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 16))
+NVFP4_DOWN_BYTES = H * F // 2 + H * (F // 16) + 4
+FLOP_PER_SLOT = 3 * 2 * H * F
+
+
+class Hip:
+    """hipEvent_t handles through the HIP runtime (ctypes)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                          ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def int4_banks(copies, dev, seed0):
+    out = []
+    for c in range(copies):
+        mats = []
+        for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
+            q, s = synth.packed_int4_random(E, n, k, seed0 + 10 * c + i, dev)
+            mats.append(B.bank_int4(q, s))
+        out.append(B.ffn(*mats))
+    return out
+
+
+def nvfp4_banks(copies, dev, seed0):
+    out = []
+    for c in range(copies):
+        mats = []
+        for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
+            q, s, g = synth.packed_nvfp4_random(E, n, k, seed0 + 10 * c + i, dev)
+            mats.append(B.bank_nvfp4(q, s, g))
+        out.append(B.ffn(*mats))
+    return out
+
+
+def touched_experts(logits_cpu):
+    return int(torch.unique(torch.topk(logits_cpu, K, dim=1).indices).numel())
+
+
+def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt):
+    """Times `steps` layer passes. route_mode: 'logits' (fresh N(0,1) logits
+    per step) or 'weights' (router weight + fixed batch). Returns a dict."""
+    n_in = steps + warmup
+    x = synth.activations(T, H, act, 3 if route_mode == "weights" else 2).to(dev)
+    if route_mode == "logits":
+        lg_cpu = [torch.from_numpy(synth.router_logits(T, E, 1000 + i)) for i in range(n_in)]
+        logits = [t.to(dev) for t in lg_cpu]
+        wT = None
+    else:
+        lg_cpu = None
+        wT = torch.from_numpy(synth.router_weight_T(H, E, 3)).to(dev)
+    tm, ws_bytes = B.moe_forward_plan(banks[0], T, K, x.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    perm = B.Perm(T, K, E, tm, dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ev = [[hip.event() for _ in range(B.MOE_FORWARD_STAGES + 1)] for _ in range(steps)]
+
+    def step(i, events=None):
+        if route_mode == "logits":
+            B.moe_route_topk(K, logits=logits[i], ids=ids, w=w)
+        else:
+            B.moe_route_topk(K, x=x, router_wT=wT, ids=ids, w=w)
+        B.moe_permute(ids, E, tm, perm=perm)
+        B.moe_w4a16_forward(banks[i % len(banks)], x, w, perm, out=out, ws=ws, events=events)
+
+    for i in range(warmup):
+        step(steps + i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(B.MOE_FORWARD_STAGES)]
+                         for e in ev])
+    for e in ev:
+        for h in e:
+            hip.destroy(h)
+    if route_mode == "logits":
+        U = np.array([touched_experts(lg_cpu[i]) for i in range(steps)], dtype=np.float64)
+    else:
+        U = np.full(steps, float(torch.unique(ids).numel()))
+    gu_bytes, dn_bytes = ((INT4_GATEUP_BYTES, INT4_DOWN_BYTES) if fmt == "int4"
+                          else (NVFP4_GATEUP_BYTES, NVFP4_DOWN_BYTES))
+    ms = wall / steps * 1e3
+    gu_ms = stage_ms[:, 0]
+    r = dict(workload=name, tokens=T, ms_per_step=ms, tok_s=T / (ms * 1e-3),
+             touched_experts=float(U.mean()),
+             layer_GBps=float((U * (gu_bytes + dn_bytes)).mean() / (ms * 1e-3) / 1e9),
+             gateup_ms=float(gu_ms.mean()), down_ms=float(stage_ms[:, 1].mean()),
+             combine_ms=float(stage_ms[:, 2].mean()),
+             gateup_GBps=float(np.mean(U * gu_bytes / (gu_ms * 1e-3)) / 1e9),
+             down_GBps=float(np.mean(U * dn_bytes / (stage_ms[:, 1] * 1e-3)) / 1e9),
+             layer_TFLOPs=float(T * K * FLOP_PER_SLOT / (ms * 1e-3) / 1e12))
+    r["gateup_frac_hbm"] = r["gateup_GBps"] * 1e9 / HBM_PEAK
+    return r
+
+
+def cpu_baseline(dev_banks, n_tok=2):
+    """The oracle, as it stands, on a bounded sample of the decode workload:
+    n_tok tokens of a T=64 batch with their 8 experts each, dequantized from
+    the same packed int4 bytes in float64."""
+    from oracle import layer as OL
+    from oracle import quant as OQ
+    from oracle import router as OR
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    mats = dev_banks[0]._keep              # the gate, up, down descriptors
+    lg = synth.router_logits(64, E, 1000)[:n_tok]
+    x = synth.activations(64, H, "f16", 2)[:n_tok]
+    t0 = time.perf_counter()
+    _, ids, w = OR.route(logits=lg, K=K)
+    cache = {}
+
+    def efn(e):
+        if e not in cache:
+            cache[e] = tuple(OQ.dequant_int4(m._keep[0][e].cpu().numpy(),
+                                             m._keep[1][e].view(torch.int16).cpu().numpy()
+                                             .view(np.uint16)) for m in mats)
+        return cache[e]
+    OL.moe_layer(x.float().numpy().astype(np.float64), ids, w, efn)
+    dt = time.perf_counter() - t0
+    return dict(value=n_tok / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample="%d tokens of the decode T=64 batch (route on given logits, 8 int4 "
+                       "experts per token dequantized to float64, SwiGLU, combine); %.1f s"
+                       % (n_tok, dt))
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_moe_sigmoid_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "nvfp4"])
+    ap.add_argument("--tokens", type=int, default=None)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer has no multi-GPU path in this build "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    B.lib()
+
+    int4 = int4_banks(2, dev, 500)
+    jobs = []
+    main_T = args.tokens or {"decode": 64, "prefill": 2048, "nvfp4": 256}[args.workload]
+    spec = {"decode": ("f16", "logits", "int4"), "prefill": ("bf16", "weights", "int4"),
+            "nvfp4": ("bf16", "logits", "nvfp4")}
+    jobs.append((args.workload, main_T))
+    if not args.no_sweep:
+        for wl, T in (("decode", 1), ("decode", 8), ("decode", 64), ("prefill", 2048),
+                      ("nvfp4", 1), ("nvfp4", 256)):
+            if (wl, T) != (args.workload, main_T):
+                jobs.append((wl, T))
+    nv = None
+    results = []
+    for wl, T in jobs:
+        act, rmode, fmt = spec[wl]
+        if fmt == "nvfp4" and nv is None:
+            nv = nvfp4_banks(2, dev, 900)
+        banks = int4 if fmt == "int4" else nv
+        steps = args.steps if (wl, T) == jobs[0] else max(10, args.steps // 2)
+        results.append(run_layer("%s T=%d" % (wl, T), banks, T, act, rmode, steps, args.warmup,
+                                 hip, dev, fmt))
+        print("# %s" % json.dumps(results[-1]), file=sys.stderr, flush=True)
+
+    head = results[0]
+    act, rmode, fmt = spec[args.workload]
+    kern = "gemv_gateup_%s_%s" % (fmt, act)
+    traffic = traffic_for(kern)
+    roof = dict(bound="hbm", kernel=kern, achieved=round(head["gateup_GBps"], 1),
+                peak=HBM_PEAK / 1e9, unit="GB/s", frac=round(head["gateup_frac_hbm"], 4),
+                traffic=traffic,
+                algorithmic_bytes_per_launch=round(head["touched_experts"] *
+                                                   (INT4_GATEUP_BYTES if fmt == "int4"
+                                                    else NVFP4_GATEUP_BYTES)))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(int4)
+    line = {
+        "metric": "W4A16 MoE layer tok/s; decode HBM GB/s %peak; prefill TFLOP/s %peak",
+        "value": round(head["tok_s"], 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": act, "data": "synthetic",
+        "config": {"workload": "%s T=%d: 352 %s experts, top-8 sigmoid routing, hidden 4096, "
+                               "SwiGLU width 1536, %s activations" % (args.workload, main_T,
+                                                                      fmt, act),
+                   "tokens": main_T, "experts": E, "top_k": K, "hidden": H, "width": F},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "sweep": results,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

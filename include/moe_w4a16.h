@@ -70,7 +70,8 @@ typedef enum { MOE_W_INT4_G128 = 1, MOE_W_NVFP4_G16 = 2, MOE_W_BF16 = 3 } moe_wf
 
 /* One bank of E matrices, each [n out][k in]. Strides are in bytes; the
  * row strides must be multiples of 16 and the base pointers 16-byte
- * aligned (the kernels load 128 bits at a time). Per-expert tensors stored
+ * aligned (the kernels load 128 bits at a time); scale pointers and strides
+ * must be even. Per-expert tensors stored
  * at a constant distance are described by the expert stride. */
 typedef struct {
     int32_t fmt;                 /* moe_wfmt_t                                  */
@@ -197,10 +198,34 @@ moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts,
                                const float *residual, void *out, int out_dtype,
                                void *ws, size_t ws_bytes, void *stream);
 
+/* Number of timed stages of moe_w4a16_forward_profiled. */
+#define MOE_FORWARD_STAGES 3
+
+/*
+ * moe_w4a16_forward_profiled -- moe_w4a16_forward, additionally recording
+ * the caller's HIP events on `stream` at the stage boundaries, so the
+ * caller can time each kernel stage with hipEventElapsedTime:
+ *   events[0] | gate/up + SwiGLU | events[1] | down | events[2] |
+ *   combine | events[3]
+ * events: host array of n_events == MOE_FORWARD_STAGES + 1 hipEvent_t
+ * handles (passed as void*), created by the caller. Same results, same
+ * kernels, same validation as moe_w4a16_forward.
+ */
+moe_status_t moe_w4a16_forward_profiled(const moe_ffn_desc_t *experts,
+                                        const moe_ffn_desc_t *shared,
+                                        const void *x, int act_dtype, int T, int K,
+                                        const float *topk_w, const moe_perm_t *perm,
+                                        const float *residual, void *out, int out_dtype,
+                                        void *ws, size_t ws_bytes, void *stream,
+                                        void *const *events, int n_events);
+
 /*
  * moe_dequant -- the exact dequantized matrix of one expert, as float32
  * [n][k] (int4: q * scale; NVFP4: (e2m1 * e4m3) * global_scale with one
- * float32 rounding). Uses the same in-kernel decode as the forward pass.
+ * float32 rounding). It runs the forward kernels' own nibble decoders
+ * (int4: the biased 16-bit pair decode; NVFP4: the hardware E2M1 pair
+ * conversion), so a bit-exact export checks the format interpretation the
+ * forward pass relies on.
  */
 moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out,
                          void *stream);

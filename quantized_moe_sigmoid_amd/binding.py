@@ -18,7 +18,9 @@ MOE_F16, MOE_BF16, MOE_F32 = 1, 2, 3
 MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16 = 1, 2, 3
 
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_route_topk", "moe_permute_sizes",
-           "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_dequant")
+           "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_w4a16_forward_profiled",
+           "moe_dequant")
+MOE_FORWARD_STAGES = 3
 
 _DT = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
 _TD = {v: k for k, v in _DT.items()}
@@ -72,9 +74,10 @@ def lib():
         L.moe_forward_plan.argtypes = [P(FfnDesc), P(FfnDesc), i32, i32, i32, P(i32), P(sz)]
         L.moe_w4a16_forward.argtypes = [P(FfnDesc), P(FfnDesc), vp, i32, i32, i32, vp,
                                         P(PermDesc), vp, vp, i32, vp, sz, vp]
+        L.moe_w4a16_forward_profiled.argtypes = L.moe_w4a16_forward.argtypes + [P(vp), i32]
         L.moe_dequant.argtypes = [P(WeightDesc), i32, vp, vp]
         for name in ("moe_route_topk", "moe_permute_sizes", "moe_permute", "moe_forward_plan",
-                     "moe_w4a16_forward", "moe_dequant"):
+                     "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_dequant"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -195,7 +198,9 @@ def moe_forward_plan(experts, T, K, act_dtype, shared=None):
 
 
 def moe_w4a16_forward(experts, x, topk_w, perm, residual=None, out_dtype=torch.float32,
-                      shared=None, out=None, ws=None):
+                      shared=None, out=None, ws=None, events=None):
+    """events: None, or a sequence of MOE_FORWARD_STAGES + 1 hipEvent_t
+    handles (ints) recorded at the stage boundaries (the profiled entry)."""
     T, H = x.shape
     K = topk_w.shape[1]
     dev = x.device
@@ -205,11 +210,15 @@ def moe_w4a16_forward(experts, x, topk_w, perm, residual=None, out_dtype=torch.f
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=dev)
     pd = perm.desc()
-    st = lib().moe_w4a16_forward(ctypes.byref(experts), ctypes.byref(shared) if shared else None,
-                                 _ptr(x), _DT[x.dtype], T, K, _ptr(topk_w), ctypes.byref(pd),
-                                 _ptr(residual), _ptr(out), _DT[out.dtype], _ptr(ws),
-                                 ws.numel(), _stream(dev))
-    _check(st, "moe_w4a16_forward")
+    args = [ctypes.byref(experts), ctypes.byref(shared) if shared else None, _ptr(x),
+            _DT[x.dtype], T, K, _ptr(topk_w), ctypes.byref(pd), _ptr(residual), _ptr(out),
+            _DT[out.dtype], _ptr(ws), ws.numel(), _stream(dev)]
+    if events is None:
+        _check(lib().moe_w4a16_forward(*args), "moe_w4a16_forward")
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check(lib().moe_w4a16_forward_profiled(*args, arr, len(events)),
+               "moe_w4a16_forward_profiled")
     return out
 
 

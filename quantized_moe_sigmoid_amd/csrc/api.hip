@@ -3,6 +3,8 @@
 // invalid call enqueues nothing.
 #include <string.h>
 
+#include <functional>
+
 #include "common.h"
 
 namespace moe {
@@ -14,7 +16,7 @@ moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_p
 moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out, hipStream_t s);
 moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
-                                 hipStream_t s);
+                                 hipStream_t s, const std::function<moe_status_t(int)> &mark);
 moe_status_t launch_combine(const float *y, const int32_t *slot_to_row, const float *w, int T,
                             int K, int H, const float *shared, const float *residual, void *out,
                             int out_dtype, hipStream_t s);
@@ -171,10 +173,12 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts, const moe_ffn_desc_
     return MOE_OK;
 }
 
-moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts, const moe_ffn_desc_t *shared,
-                               const void *x, int act_dtype, int T, int K, const float *topk_w,
-                               const moe_perm_t *perm, const float *residual, void *out,
-                               int out_dtype, void *ws, size_t ws_bytes, void *stream) {
+static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_desc_t *shared,
+                                 const void *x, int act_dtype, int T, int K,
+                                 const float *topk_w, const moe_perm_t *perm,
+                                 const float *residual, void *out, int out_dtype, void *ws,
+                                 size_t ws_bytes, void *stream, void *const *events,
+                                 int n_events) {
     int E, H, F;
     moe_status_t st = check_experts(experts, &E, &H, &F);
     if (st != MOE_OK) return st;
@@ -182,6 +186,7 @@ moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts, const moe_ffn_desc
     if (out_dtype != MOE_F32 && !is_act(out_dtype)) return MOE_ERR_INVALID_ARG;
     if ((st = check_perm(perm)) != MOE_OK) return st;
     if (shared) return MOE_ERR_UNSUPPORTED;
+    if (events && n_events != MOE_FORWARD_STAGES + 1) return MOE_ERR_INVALID_ARG;
     if (T == 0) return MOE_OK;
     if (!x || !topk_w || !out || !ws) return MOE_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256) ||
@@ -193,13 +198,42 @@ moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts, const moe_ffn_desc
     if (p.max_tiles > 65535) return MOE_ERR_UNSUPPORTED;
 
     hipStream_t s = (hipStream_t)stream;
+    auto mark = [&](int i) -> moe_status_t {
+        if (events && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess) return MOE_ERR_HIP;
+        return MOE_OK;
+    };
     char *w = (char *)ws;
     void *h = w + p.off_h;
     float *y = (float *)(w + p.off_y);
-    st = launch_gemv_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s);
+    if ((st = mark(0)) != MOE_OK) return st;
+    st = launch_gemv_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s,
+                             events ? [&](int i) { return mark(i); } : std::function<moe_status_t(int)>());
     if (st != MOE_OK) return st;
-    return launch_combine(y, perm->slot_to_row, topk_w, T, K, H, nullptr, residual, out,
-                          out_dtype, s);
+    st = launch_combine(y, perm->slot_to_row, topk_w, T, K, H, nullptr, residual, out,
+                        out_dtype, s);
+    if (st != MOE_OK) return st;
+    return mark(3);
+}
+
+moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts, const moe_ffn_desc_t *shared,
+                               const void *x, int act_dtype, int T, int K, const float *topk_w,
+                               const moe_perm_t *perm, const float *residual, void *out,
+                               int out_dtype, void *ws, size_t ws_bytes, void *stream) {
+    return forward_impl(experts, shared, x, act_dtype, T, K, topk_w, perm, residual, out,
+                        out_dtype, ws, ws_bytes, stream, nullptr, 0);
+}
+
+moe_status_t moe_w4a16_forward_profiled(const moe_ffn_desc_t *experts,
+                                        const moe_ffn_desc_t *shared, const void *x,
+                                        int act_dtype, int T, int K, const float *topk_w,
+                                        const moe_perm_t *perm, const float *residual,
+                                        void *out, int out_dtype, void *ws, size_t ws_bytes,
+                                        void *stream, void *const *events, int n_events) {
+    if (!events) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < n_events; ++i)
+        if (!events[i]) return MOE_ERR_INVALID_ARG;
+    return forward_impl(experts, shared, x, act_dtype, T, K, topk_w, perm, residual, out,
+                        out_dtype, ws, ws_bytes, stream, events, n_events);
 }
 
 moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out, void *stream) {

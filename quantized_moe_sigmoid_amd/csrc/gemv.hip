@@ -19,6 +19,8 @@
 // NVFP4: the hardware pair conversion gives exact E2M1 values; the E4M3
 //   block scale applies per 16 inputs in float32, the global scale once at
 //   the end.
+#include <functional>
+
 #include "decode.h"
 
 namespace moe {
@@ -277,7 +279,7 @@ inline void allow_lds(Kern k, size_t lds) {
 template <int ACT, int FMT>
 moe_status_t gemv_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
                             const moe_perm_t &p, int max_tiles, uint16_t *h, float *y,
-                            hipStream_t s) {
+                            hipStream_t s, const std::function<moe_status_t(int)> &mark) {
     constexpr int LPR = kGemvLPR, TM = kGemvTM;
     const int F = ex.gate.n, H = ex.gate.k;
     const int rows_per_block = kGemvWaves * (kWave / LPR);
@@ -290,6 +292,7 @@ moe_status_t gemv_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
                            p.tile_expert, p.num_tiles, h, nullptr);
         MOE_LAUNCH_CHECK();
     }
+    if (mark && mark(1) != MOE_OK) return MOE_ERR_HIP;
     {
         const size_t lds = gemv_lds_bytes<LPR, TM>(F);
         dim3 grid((H + rows_per_block - 1) / rows_per_block, max_tiles);
@@ -299,6 +302,7 @@ moe_status_t gemv_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
                            p.sorted_slots, p.tile_expert, p.num_tiles, nullptr, y);
         MOE_LAUNCH_CHECK();
     }
+    if (mark && mark(2) != MOE_OK) return MOE_ERR_HIP;
     return MOE_OK;
 }
 
@@ -306,15 +310,15 @@ int gemv_tile_m() { return kGemvTM; }
 
 moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
-                                 hipStream_t s) {
+                                 hipStream_t s, const std::function<moe_status_t(int)> &mark) {
     const uint16_t *xx = (const uint16_t *)x;
     uint16_t *hh = (uint16_t *)h;
     const bool nv = ex.gate.fmt == MOE_W_NVFP4_G16;
     if (act == MOE_BF16)
-        return nv ? gemv_forward_t<MOE_BF16, MOE_W_NVFP4_G16>(ex, xx, K, p, max_tiles, hh, y, s)
-                  : gemv_forward_t<MOE_BF16, MOE_W_INT4_G128>(ex, xx, K, p, max_tiles, hh, y, s);
-    return nv ? gemv_forward_t<MOE_F16, MOE_W_NVFP4_G16>(ex, xx, K, p, max_tiles, hh, y, s)
-              : gemv_forward_t<MOE_F16, MOE_W_INT4_G128>(ex, xx, K, p, max_tiles, hh, y, s);
+        return nv ? gemv_forward_t<MOE_BF16, MOE_W_NVFP4_G16>(ex, xx, K, p, max_tiles, hh, y, s, mark)
+                  : gemv_forward_t<MOE_BF16, MOE_W_INT4_G128>(ex, xx, K, p, max_tiles, hh, y, s, mark);
+    return nv ? gemv_forward_t<MOE_F16, MOE_W_NVFP4_G16>(ex, xx, K, p, max_tiles, hh, y, s, mark)
+              : gemv_forward_t<MOE_F16, MOE_W_INT4_G128>(ex, xx, K, p, max_tiles, hh, y, s, mark);
 }
 
 }  // namespace moe
