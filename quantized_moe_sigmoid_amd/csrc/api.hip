@@ -20,7 +20,12 @@ moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int ac
 moe_status_t launch_combine(const float *y, const int32_t *slot_to_row, const float *w, int T,
                             int K, int H, const float *shared, const float *residual, void *out,
                             int out_dtype, hipStream_t s);
+moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
+                                 const moe_perm_t &p, int max_tiles, void *h, float *y,
+                                 hipStream_t s, const std::function<moe_status_t(int)> &mark);
 int gemv_tile_m();
+int gemm_tile_m();
+int gemm_group();
 }  // namespace moe
 
 using namespace moe;
@@ -89,15 +94,26 @@ moe_status_t check_perm(const moe_perm_t *p) {
 }
 
 struct FwdPlan {
+    bool mfma;
     int tile_m;
     int64_t max_rows, max_tiles;
     size_t off_h, off_y, total;
 };
 
+// Kernel choice by batch shape: with few slots per expert the dequantizing
+// GEMV streams each touched expert once per tile of 4 slots; once the
+// average expert sees several tiles' worth of slots (T*K >= 4*E) the MFMA
+// grouped GEMM, which reads each weight once per tile of 64 slots, takes
+// over. One code path per shape class.
+bool use_mfma(int T, int K, int E, int H, int F) {
+    return (int64_t)T * K >= 4 * (int64_t)E && H % gemm_group() == 0 && F % gemm_group() == 0;
+}
+
 FwdPlan plan_forward(int T, int K, int E, int H, int F, int act) {
     (void)act;
     FwdPlan p;
-    p.tile_m = gemv_tile_m();
+    p.mfma = use_mfma(T, K, E, H, F);
+    p.tile_m = p.mfma ? gemm_tile_m() : gemv_tile_m();
     p.max_rows = perm_max_rows(T, K, E, p.tile_m);
     p.max_tiles = p.max_rows / p.tile_m;
     p.off_h = 0;
@@ -195,7 +211,9 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     const FwdPlan p = plan_forward(T, K, E, H, F, act_dtype);
     if (perm->tile_m != p.tile_m) return MOE_ERR_INVALID_ARG;
     if (ws_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    if (p.max_tiles > 65535) return MOE_ERR_UNSUPPORTED;
+    if (!p.mfma && p.max_tiles > 65535) return MOE_ERR_UNSUPPORTED;
+    if (p.mfma && p.max_tiles * ((H > F ? H : F) / 128 + 1) > (int64_t)1 << 30)
+        return MOE_ERR_UNSUPPORTED;
 
     hipStream_t s = (hipStream_t)stream;
     auto mark = [&](int i) -> moe_status_t {
@@ -206,8 +224,10 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     void *h = w + p.off_h;
     float *y = (float *)(w + p.off_y);
     if ((st = mark(0)) != MOE_OK) return st;
-    st = launch_gemv_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s,
-                             events ? [&](int i) { return mark(i); } : std::function<moe_status_t(int)>());
+    const std::function<moe_status_t(int)> mk =
+        events ? std::function<moe_status_t(int)>(mark) : std::function<moe_status_t(int)>();
+    st = p.mfma ? launch_gemm_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s, mk)
+                : launch_gemv_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s, mk);
     if (st != MOE_OK) return st;
     st = launch_combine(y, perm->slot_to_row, topk_w, T, K, H, nullptr, residual, out,
                         out_dtype, s);

@@ -304,3 +304,107 @@ def test_forward_properties(dev):
     ffn2 = B.ffn(ffn.gate, ffn.up, B.bank_int4(qd, (sd.float() * 2).to(torch.bfloat16)))
     c = _run_layer(dev, ffn2, x, ids, w, Ee)
     assert torch.equal(c, 2 * a)
+
+
+# ------------------------------------------------- prefill (MFMA) forward ---
+def _nvfp4_ffn_from_oracle(E_, H_, F_, root, dev):
+    banks, host = [], []
+    for which, (n, k) in (("gate", (F_, H_)), ("up", (F_, H_)), ("down", (H_, F_))):
+        q, s, gs = FX.nvfp4_bank_oracle(E_, n, k, root, 0, which)
+        banks.append(B.bank_nvfp4(torch.from_numpy(q).to(dev), torch.from_numpy(s).to(dev),
+                                  torch.from_numpy(gs).to(dev)))
+        host.append((q, s, gs))
+    return B.ffn(*banks), host
+
+
+def _efn_nvfp4(host):
+    cache = {}
+
+    def fn(e):
+        if e not in cache:
+            mats = []
+            for (q, s, g) in host:
+                if isinstance(q, torch.Tensor):
+                    mats.append(OQ.dequant_nvfp4(q[e].cpu().numpy(), s[e].cpu().numpy(),
+                                                 float(g[e].cpu())))
+                else:
+                    mats.append(FX.oracle_nvfp4_expert(q, s, g, e))
+            cache[e] = tuple(mats)
+        return cache[e]
+    return fn
+
+
+@pytest.mark.parametrize("act,Ee,Kk,T", [("bf16", 8, 4, 40), ("bf16", 4, 2, 150),
+                                         ("f16", 8, 4, 40), ("f16", 5, 3, 97)])
+def test_forward_mfma_int4_small(dev, act, Ee, Kk, T):
+    """MFMA grouped-GEMM path (T*K >= 4E) on clip-search int4 experts:
+    partial tiles, one and two 32-row blocks, several tiles per expert."""
+    Hh, Ff = 512, 256
+    assert T * Kk >= 4 * Ee
+    ffn, host = _int4_ffn_from_oracle(Ee, Hh, Ff, 6, dev)
+    x = synth.activations(T, Hh, act, 6)
+    lg = synth.router_logits(T, Ee, 6)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    tm, _ = B.moe_forward_plan(ffn, T, Kk, x.dtype)
+    assert tm == 64
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, Ee).cpu().numpy()
+    oids = OR.topk_ids(lg, Kk)
+    ref = FX.oracle_layer(x, oids, OR.routing_weights(lg, oids), _experts_fn_int4(host))
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
+def test_forward_mfma_nvfp4_small(dev):
+    Ee, Hh, Ff, T, Kk = 6, 512, 256, 64, 3
+    ffn, host = _nvfp4_ffn_from_oracle(Ee, Hh, Ff, 8, dev)
+    x = synth.activations(T, Hh, "bf16", 8)
+    lg = synth.router_logits(T, Ee, 8)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, Ee).cpu().numpy()
+    oids = OR.topk_ids(lg, Kk)
+    ref = FX.oracle_layer(x, oids, OR.routing_weights(lg, oids), _efn_nvfp4(host))
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
+@pytest.mark.parametrize("zipf", [False, True])
+def test_forward_prefill_full_shape(dev, zipf):
+    """Prefill shape T=2048, bf16 x, router from a N(0, 0.02) weight (plus
+    Zipf expert biases when skewed), 352 int4 experts; outputs of sampled
+    tokens against the oracle, routing of every token bit for bit."""
+    T = 2048
+    ffn, host = _int4_ffn_random(E, H, F, 300 + int(zipf), dev)
+    x = synth.activations(T, H, "bf16", 3)
+    wT = synth.router_weight_T(H, E, 3)
+    b = synth.zipf_bias(E, 3) if zipf else None
+    ids, w = B.moe_route_topk(K, x=x.to(dev), router_wT=torch.from_numpy(wT).to(dev),
+                              bias=None if b is None else torch.from_numpy(b).to(dev))
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, E).cpu().numpy()
+    lg = OR.router_logits(x.float().numpy(), wT, b)
+    oids = OR.topk_ids(lg, K)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    toks = [0, 1, 1023, 2047]
+    ow = OR.routing_weights(lg, oids)
+    ref = FX.oracle_layer(x[toks], oids[toks], ow[toks], _experts_fn_int4(host))
+    ok, ratio = FX.within_tolerance(out[toks], ref)
+    assert ok, ratio
+
+
+def test_forward_nvfp4_prefill_full_shape(dev):
+    T = 256
+    banks, host = [], []
+    for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
+        qt, st, gt = synth.packed_nvfp4_random(E, n, k, 60 + i, dev)
+        banks.append(B.bank_nvfp4(qt, st, gt))
+        host.append((qt, st, gt))
+    ffn = B.ffn(*banks)
+    x = synth.activations(T, H, "bf16", 4)
+    lg = synth.router_logits(T, E, 4)
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, E).cpu().numpy()
+    oids = OR.topk_ids(lg, K)
+    toks = [0, 100, 255]
+    ref = FX.oracle_layer(x[toks], oids[toks], OR.routing_weights(lg, oids)[toks],
+                          _efn_nvfp4(host))
+    ok, ratio = FX.within_tolerance(out[toks], ref)
+    assert ok, ratio
