@@ -114,13 +114,15 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt):
     w = torch.empty((T, K), dtype=torch.float32, device=dev)
     perm = B.Perm(T, K, E, tm, dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    rws = torch.empty(max(B.moe_route_workspace(T, E, route_mode == "weights"), 256),
+                      dtype=torch.uint8, device=dev)
     ev = [[hip.event() for _ in range(B.MOE_FORWARD_STAGES + 1)] for _ in range(steps)]
 
     def step(i, events=None):
         if route_mode == "logits":
             B.moe_route_topk(K, logits=logits[i], ids=ids, w=w)
         else:
-            B.moe_route_topk(K, x=x, router_wT=wT, ids=ids, w=w)
+            B.moe_route_topk(K, x=x, router_wT=wT, ids=ids, w=w, ws=rws)
         B.moe_permute(ids, E, tm, perm=perm)
         B.moe_w4a16_forward(banks[i % len(banks)], x, w, perm, out=out, ws=ws, events=events)
 

@@ -117,31 +117,48 @@ const char *moe_status_string(int status);
 int moe_abi_version(void);
 
 /*
- * moe_route_topk -- sigmoid top-K router (page "Step-5-Preview-Spark",
- * "At a glance": top-8 of 352 experts by a sigmoid router; tie rule as the
- * sparse indexer's region top-k on page "Step 5 Preview: ...", "Sparse GQA,
- * read from the kernels", step 3).
+ * moe_router_logits -- the router scores of every (token, expert) pair
+ * (page "Step-5-Preview-Spark", "At a glance": a sigmoid router over 352
+ * routed experts), as the float32 chain
+ *     acc = +0; for k = 0 .. H-1: acc = fma(float(x[t][k]), router_wT[k][e], acc)
+ *     logits[t][e] = acc   (+ bias[e], one float32 addition, if bias != NULL)
+ * This fixed order makes routing reproducible bit for bit (page
+ * "Step-5-Preview-Spark", "Quality": top-8 choices flip under a changed
+ * summation order).
+ * x [T][H] in x_dtype (MOE_F16 or MOE_BF16), router_wT [H][E] float (the
+ * router weight transposed, 16-byte aligned), bias [E] float or NULL,
+ * logits [T][E] float. Limits: H % 64 == 0, E % 4 == 0, E <= 512.
+ */
+moe_status_t moe_router_logits(const void *x, int x_dtype, const float *router_wT,
+                               const float *bias, int T, int H, int E, float *logits,
+                               void *stream);
+
+/* Workspace bytes (host output) moe_route_topk needs: T*E*4 when it computes
+ * the logits from a router weight (use_router_weight != 0), else 0. */
+moe_status_t moe_route_workspace(int T, int E, int use_router_weight, size_t *bytes);
+
+/*
+ * moe_route_topk -- sigmoid top-K routing (page "Step-5-Preview-Spark",
+ * "At a glance": top-8 of 352 experts by a sigmoid router; ties go to the
+ * lower index, as in the sparse indexer's region top-k on page "Step 5
+ * Preview: ...", "Sparse GQA, read from the kernels", step 3).
  *
  * Logits come from exactly one of:
- *   router_wT [H][E] float: logit[t][e] = the float32 chain
- *       acc = 0; for k = 0..H-1: acc = fma(float(x[t][k]), router_wT[k][e], acc)
- *     (this fixed order makes the selected indices reproducible bit for
- *     bit; page "Step-5-Preview-Spark", "Quality", shows top-8 routing
- *     flipping under a changed summation order);  x [T][H] in x_dtype
- *     (MOE_F16 or MOE_BF16);
- *   logits_in [T][E] float: given logits (x and router_wT unused, may be
- *     NULL).
+ *   router_wT: the moe_router_logits chain of x (x, x_dtype, H as there),
+ *     written to the workspace `ws` (moe_route_workspace bytes);
+ *   logits_in [T][E] float: given logits (x, router_wT, ws unused).
  * If bias [E] float is non-NULL, logit = logit + bias[e] in float32.
  * topk_ids [T][K] int32: the K largest logits by (logit descending, expert
  * index ascending), -0 equal to +0. topk_w [T][K] float: sigmoid of those
- * logits, divided by their sum over the K when renormalize != 0.
- * Limits: 1 <= K <= min(E, 16), E <= 512, H % 8 == 0 when router_wT is used.
- * T == 0 is a no-op.
+ * logits, divided by their sum over the K (summed in ascending k) when
+ * renormalize != 0. Limits: 1 <= K <= min(E, 16), E <= 512. T == 0 is a
+ * no-op.
  */
 moe_status_t moe_route_topk(const void *x, int x_dtype, const float *router_wT,
                             const float *logits_in, const float *bias,
                             int T, int H, int E, int K, int renormalize,
-                            int32_t *topk_ids, float *topk_w, void *stream);
+                            int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
+                            void *stream);
 
 /* Sizes (host outputs, in elements) of the moe_permute arrays for T tokens,
  * K choices, E experts and tile_m rows per tile:

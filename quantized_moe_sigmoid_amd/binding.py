@@ -17,7 +17,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, M
 MOE_F16, MOE_BF16, MOE_F32 = 1, 2, 3
 MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16 = 1, 2, 3
 
-EXPORTS = ("moe_status_string", "moe_abi_version", "moe_route_topk", "moe_permute_sizes",
+EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_route_workspace",
+           "moe_route_topk", "moe_permute_sizes",
            "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_w4a16_forward_profiled",
            "moe_dequant")
 MOE_FORWARD_STAGES = 3
@@ -68,7 +69,10 @@ def lib():
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
-        L.moe_route_topk.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.moe_router_logits.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp]
+        L.moe_route_workspace.argtypes = [i32, i32, i32, P(sz)]
+        L.moe_route_topk.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, sz,
+                                     vp]
         L.moe_permute_sizes.argtypes = [i32, i32, i32, i32, P(i64), P(i64)]
         L.moe_permute.argtypes = [vp, i32, i32, i32, P(PermDesc), vp]
         L.moe_forward_plan.argtypes = [P(FfnDesc), P(FfnDesc), i32, i32, i32, P(i32), P(sz)]
@@ -76,7 +80,8 @@ def lib():
                                         P(PermDesc), vp, vp, i32, vp, sz, vp]
         L.moe_w4a16_forward_profiled.argtypes = L.moe_w4a16_forward.argtypes + [P(vp), i32]
         L.moe_dequant.argtypes = [P(WeightDesc), i32, vp, vp]
-        for name in ("moe_route_topk", "moe_permute_sizes", "moe_permute", "moe_forward_plan",
+        for name in ("moe_router_logits", "moe_route_workspace", "moe_route_topk",
+                     "moe_permute_sizes", "moe_permute", "moe_forward_plan",
                      "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_dequant"):
             getattr(L, name).restype = i32
         _lib = L
@@ -128,8 +133,26 @@ def ffn(gate, up, down):
 
 
 # ----------------------------------------------------------------- calls ---
+def moe_router_logits(x, router_wT, bias=None, out=None):
+    """Canonical float32 router logits [T, E]."""
+    T, H = x.shape
+    E = router_wT.shape[1]
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib().moe_router_logits(_ptr(x), _DT[x.dtype], _ptr(router_wT), _ptr(bias), T, H, E,
+                                   _ptr(out), _stream(x.device)), "moe_router_logits")
+    return out
+
+
+def moe_route_workspace(T, E, use_router_weight):
+    b = ctypes.c_size_t()
+    _check(lib().moe_route_workspace(T, E, int(bool(use_router_weight)), ctypes.byref(b)),
+           "moe_route_workspace")
+    return b.value
+
+
 def moe_route_topk(K, x=None, router_wT=None, logits=None, bias=None, renormalize=True,
-                   ids=None, w=None):
+                   ids=None, w=None, ws=None):
     """Returns (topk_ids int32 [T, K], topk_w float32 [T, K])."""
     src = logits if logits is not None else x
     T = src.shape[0]
@@ -140,9 +163,13 @@ def moe_route_topk(K, x=None, router_wT=None, logits=None, bias=None, renormaliz
         ids = torch.empty((T, K), dtype=torch.int32, device=dev)
     if w is None:
         w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    need = moe_route_workspace(T, E, router_wT is not None)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     xd = _DT.get(x.dtype, 0) if x is not None else 0
     st = lib().moe_route_topk(_ptr(x), xd, _ptr(router_wT), _ptr(logits), _ptr(bias), T, H, E,
-                              K, int(bool(renormalize)), _ptr(ids), _ptr(w), _stream(dev))
+                              K, int(bool(renormalize)), _ptr(ids), _ptr(w),
+                              _ptr(ws) if need else None, need, _stream(dev))
     _check(st, "moe_route_topk")
     return ids, w
 

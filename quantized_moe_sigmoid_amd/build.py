@@ -22,6 +22,10 @@ FLAGS = [
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
+    # MFMA accumulators in ordinary VGPRs: the GEMM rescales them with VALU
+    # instructions between MFMAs, and AGPR residency would copy them back
+    # and forth every group
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

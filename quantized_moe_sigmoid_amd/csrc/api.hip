@@ -8,9 +8,10 @@
 #include "common.h"
 
 namespace moe {
-moe_status_t launch_route(const void *x, int x_dtype, const float *wT, const float *logits,
-                          const float *bias, int T, int H, int E, int K, int renorm,
-                          int32_t *ids, float *wts, hipStream_t s);
+moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, const float *bias,
+                                  int T, int H, int E, float *logits, hipStream_t s);
+moe_status_t launch_topk(const float *logits, const float *bias, int T, int E, int K, int renorm,
+                         int32_t *ids, float *wts, hipStream_t s);
 moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_perm_t &p,
                             hipStream_t s);
 moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out, hipStream_t s);
@@ -20,9 +21,10 @@ moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int ac
 moe_status_t launch_combine(const float *y, const int32_t *slot_to_row, const float *w, int T,
                             int K, int H, const float *shared, const float *residual, void *out,
                             int out_dtype, hipStream_t s);
-moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
+moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int act, int T, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
-                                 hipStream_t s, const std::function<moe_status_t(int)> &mark);
+                                 void *xperm, float *xsum, float *hsum, hipStream_t s,
+                                 const std::function<moe_status_t(int)> &mark);
 int gemv_tile_m();
 int gemm_tile_m();
 int gemm_group();
@@ -97,7 +99,7 @@ struct FwdPlan {
     bool mfma;
     int tile_m;
     int64_t max_rows, max_tiles;
-    size_t off_h, off_y, total;
+    size_t off_h, off_y, off_xperm, off_xsum, off_hsum, total;
 };
 
 // Kernel choice by batch shape: with few slots per expert the dequantizing
@@ -105,20 +107,39 @@ struct FwdPlan {
 // average expert sees several tiles' worth of slots (T*K >= 4*E) the MFMA
 // grouped GEMM, which reads each weight once per tile of 64 slots, takes
 // over. One code path per shape class.
-bool use_mfma(int T, int K, int E, int H, int F) {
-    return (int64_t)T * K >= 4 * (int64_t)E && H % gemm_group() == 0 && F % gemm_group() == 0;
+bool mfma_layout_ok(const moe_weight_desc_t &d) {
+    // the GEMM loads a step's scales as one 4-byte (int4) or 16-byte (NVFP4) word
+    const int64_t a = d.fmt == MOE_W_INT4_G128 ? 4 : 16;
+    return aligned(d.scale, a) && d.scale_row_stride % a == 0 && d.scale_expert_stride % a == 0;
 }
 
-FwdPlan plan_forward(int T, int K, int E, int H, int F, int act) {
+bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
+    const int E = ex.gate.num_experts, H = ex.gate.k, F = ex.gate.n;
+    // 32-bit buffer offsets must reach every row of an expert matrix
+    const bool fits = (int64_t)F * ex.gate.qweight_row_stride < INT32_MAX &&
+                      (int64_t)F * ex.up.qweight_row_stride < INT32_MAX &&
+                      (int64_t)H * ex.down.qweight_row_stride < INT32_MAX;
+    return (int64_t)T * K >= 4 * (int64_t)E && H % gemm_group() == 0 &&
+           F % gemm_group() == 0 && fits && mfma_layout_ok(ex.gate) && mfma_layout_ok(ex.up) &&
+           mfma_layout_ok(ex.down);
+}
+
+FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F, int act) {
     (void)act;
     FwdPlan p;
-    p.mfma = use_mfma(T, K, E, H, F);
+    p.mfma = use_mfma(ex, T, K);
     p.tile_m = p.mfma ? gemm_tile_m() : gemv_tile_m();
     p.max_rows = perm_max_rows(T, K, E, p.tile_m);
     p.max_tiles = p.max_rows / p.tile_m;
     p.off_h = 0;
     p.off_y = align256((size_t)p.max_rows * F * 2);
-    p.total = p.off_y + align256((size_t)p.max_rows * H * 4);
+    // MFMA path, int4: x in the decoder's pair order, and per-row sums of
+    // each 128-input group of x and of h
+    const bool sums = p.mfma && ex.gate.fmt == MOE_W_INT4_G128;
+    p.off_xperm = p.off_y + align256((size_t)p.max_rows * H * 4);
+    p.off_xsum = p.off_xperm + (sums ? align256((size_t)T * H * 2) : 0);
+    p.off_hsum = p.off_xsum + (sums ? align256((size_t)T * (H / 128) * 4) : 0);
+    p.total = p.off_hsum + (sums ? align256((size_t)p.max_rows * (F / 128) * 4) : 0);
     return p;
 }
 
@@ -139,20 +160,56 @@ const char *moe_status_string(int status) {
 
 int moe_abi_version(void) { return 1; }
 
+static moe_status_t check_router(const void *x, int x_dtype, const float *wT, int T, int H,
+                                 int E) {
+    if (T < 0 || E < 1 || E > kMaxExperts) return MOE_ERR_INVALID_ARG;
+    if (!wT || !is_act(x_dtype) || H < 1) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && !x) return MOE_ERR_INVALID_ARG;
+    if (H % 64 || E % 4) return MOE_ERR_UNSUPPORTED;
+    if (!aligned(wT, 16) || (x && !aligned(x, 16))) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status_t moe_router_logits(const void *x, int x_dtype, const float *router_wT,
+                               const float *bias, int T, int H, int E, float *logits,
+                               void *stream) {
+    moe_status_t st = check_router(x, x_dtype, router_wT, T, H, E);
+    if (st != MOE_OK) return st;
+    if (T > 0 && !logits) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    return launch_router_logits(x, x_dtype, router_wT, bias, T, H, E, logits,
+                                (hipStream_t)stream);
+}
+
+moe_status_t moe_route_workspace(int T, int E, int use_router_weight, size_t *bytes) {
+    if (T < 0 || E < 1 || E > kMaxExperts || !bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = use_router_weight ? (size_t)T * E * 4 : 0;
+    return MOE_OK;
+}
+
 moe_status_t moe_route_topk(const void *x, int x_dtype, const float *router_wT,
                             const float *logits_in, const float *bias, int T, int H, int E,
-                            int K, int renormalize, int32_t *topk_ids, float *topk_w,
-                            void *stream) {
+                            int K, int renormalize, int32_t *topk_ids, float *topk_w, void *ws,
+                            size_t ws_bytes, void *stream) {
     if (T < 0 || E < 1 || E > kMaxExperts || K < 1 || K > E || K > kMaxTopK)
         return MOE_ERR_INVALID_ARG;
     if (!topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
     if ((router_wT == nullptr) == (logits_in == nullptr)) return MOE_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
     if (router_wT) {
-        if (!x || !is_act(x_dtype) || H < 1 || H % 8) return MOE_ERR_INVALID_ARG;
+        moe_status_t st = check_router(x, x_dtype, router_wT, T, H, E);
+        if (st != MOE_OK) return st;
+        if (T > 0 && !ws) return MOE_ERR_INVALID_ARG;
+        if (ws_bytes < (size_t)T * E * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
+        if (ws && !aligned(ws, 16)) return MOE_ERR_INVALID_ARG;
+        if (T == 0) return MOE_OK;
+        float *lg = (float *)ws;
+        st = launch_router_logits(x, x_dtype, router_wT, bias, T, H, E, lg, s);
+        if (st != MOE_OK) return st;
+        return launch_topk(lg, nullptr, T, E, K, renormalize, topk_ids, topk_w, s);
     }
     if (T == 0) return MOE_OK;
-    return launch_route(x, x_dtype, router_wT, logits_in, bias, T, H, E, K, renormalize,
-                        topk_ids, topk_w, (hipStream_t)stream);
+    return launch_topk(logits_in, bias, T, E, K, renormalize, topk_ids, topk_w, s);
 }
 
 moe_status_t moe_permute_sizes(int T, int K, int E, int tile_m, int64_t *max_rows,
@@ -183,7 +240,7 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts, const moe_ffn_desc_
     if (T < 0 || K < 1 || K > E || !is_act(act_dtype) || !tile_m || !ws_bytes)
         return MOE_ERR_INVALID_ARG;
     if (shared) return MOE_ERR_UNSUPPORTED;
-    const FwdPlan p = plan_forward(T, K, E, H, F, act_dtype);
+    const FwdPlan p = plan_forward(*experts, T, K, E, H, F, act_dtype);
     *tile_m = p.tile_m;
     *ws_bytes = p.total;
     return MOE_OK;
@@ -208,7 +265,7 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256) ||
         (residual && !aligned(residual, 16)))
         return MOE_ERR_INVALID_ARG;
-    const FwdPlan p = plan_forward(T, K, E, H, F, act_dtype);
+    const FwdPlan p = plan_forward(*experts, T, K, E, H, F, act_dtype);
     if (perm->tile_m != p.tile_m) return MOE_ERR_INVALID_ARG;
     if (ws_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!p.mfma && p.max_tiles > 65535) return MOE_ERR_UNSUPPORTED;
@@ -226,7 +283,9 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     if ((st = mark(0)) != MOE_OK) return st;
     const std::function<moe_status_t(int)> mk =
         events ? std::function<moe_status_t(int)>(mark) : std::function<moe_status_t(int)>();
-    st = p.mfma ? launch_gemm_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s, mk)
+    st = p.mfma ? launch_gemm_forward(*experts, x, act_dtype, T, K, *perm, (int)p.max_tiles, h, y,
+                                      w + p.off_xperm, (float *)(w + p.off_xsum),
+                                      (float *)(w + p.off_hsum), s, mk)
                 : launch_gemv_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s, mk);
     if (st != MOE_OK) return st;
     st = launch_combine(y, perm->slot_to_row, topk_w, T, K, H, nullptr, residual, out,

@@ -46,6 +46,20 @@ __device__ __forceinline__ void int4_biased_pairs(uint32_t w, uint32_t out[4]) {
     out[3] = ((u >> 12) & 0x000F000Fu) | Int4Bias<ACT>::kMagic;
 }
 
+// The same pairs with a per-group nibble mask: ((w >> 4i) & m) ^ K equals
+// the expression above when m = 0x000F000F (K folds the XOR with 8 into the
+// magic, whose bits are disjoint from the nibbles), and gives BIAS + 0 for
+// every input when m = 0, i.e. q = 0: how a group with a zero scale is
+// dropped. One shift and one three-input bit operation per pair.
+template <int ACT>
+__device__ __forceinline__ void int4_biased_pairs_masked(uint32_t w, uint32_t m, uint32_t out[4]) {
+    constexpr uint32_t K = Int4Bias<ACT>::kMagic | 0x00080008u;
+    out[0] = (w & m) ^ K;
+    out[1] = ((w >> 4) & m) ^ K;
+    out[2] = ((w >> 8) & m) ^ K;
+    out[3] = ((w >> 12) & m) ^ K;
+}
+
 // ---- NVFP4 ------------------------------------------------------------------
 // E4M3FN byte -> float32 (exact): exponent bias 7, subnormals m * 2^-9.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {

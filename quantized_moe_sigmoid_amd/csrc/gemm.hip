@@ -35,17 +35,16 @@ namespace moe {
 constexpr int kGemmThreads = 256;
 constexpr int kGemmTM = 64;          // rows per tile
 constexpr int kGemmBN = 128;         // output columns per block
-constexpr int kGemmKG = 128;         // inputs per staged group
-constexpr int kGemmRowBytes = kGemmKG * 2;
+constexpr int kGemmKS = 256;         // inputs per pipeline step (two int4 groups)
+constexpr int kGemmRowBytes = kGemmKS * 2;
+constexpr int kGemmChunks = kGemmKS / 8;                    // 16-byte chunks per row
+constexpr int kGemmStage = kGemmTM * kGemmChunks / kGemmThreads;   // chunks per thread
 
 struct GemmMat {
     const uint8_t *q, *s;
     const float *gs;
     int64_t qe, qr, se, sr;
 };
-
-template <int ACT>
-using mfma_op_t = typename std::conditional<ACT == MOE_BF16, bf16x8_t, f16x8_t>::type;
 
 template <int ACT>
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
@@ -57,8 +56,7 @@ __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// 16-bit pair of two exact float32 values (their low 16 bits are zero for
-// bf16 targets; fp16 targets convert exactly).
+// 16-bit pair of two float32 values that are exact in the target format.
 template <int ACT>
 __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
     if constexpr (ACT == MOE_BF16)
@@ -69,13 +67,14 @@ __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
 
 // B operand (4 dwords = 8 inputs of one output column) from packed word w.
 template <int ACT, int FMT>
-__device__ __forceinline__ uint4 decode_b(uint32_t w, float bs) {
+__device__ __forceinline__ uint4 decode_b(uint32_t w, float bs, uint32_t qmask) {
     if constexpr (FMT == MOE_W_INT4_G128) {
         uint32_t p[4];
-        int4_biased_pairs<ACT>(w, p);
+        int4_biased_pairs_masked<ACT>(w, qmask, p);
         (void)bs;
         return make_uint4(p[0], p[1], p[2], p[3]);
     } else {
+        (void)qmask;
         uint32_t d[4];
         const uint32_t e[4] = {fp4_pair<MOE_BF16, 0>(w), fp4_pair<MOE_BF16, 1>(w),
                                fp4_pair<MOE_BF16, 2>(w), fp4_pair<MOE_BF16, 3>(w)};
@@ -89,48 +88,6 @@ __device__ __forceinline__ uint4 decode_b(uint32_t w, float bs) {
     }
 }
 
-// Staging of one 128-input group of the 64-row activation tile into LDS.
-// Thread t moves 16-byte chunks q = t + 256 s (s = 0..3): row q/16, chunk
-// q%16; the 16 threads of a row also reduce the row's group sum (int4).
-template <int ACT, int FMT>
-struct Stager {
-    uint4 v[4];
-    __device__ __forceinline__ void load(const uint16_t *const *rows, int g) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int q = threadIdx.x + kGemmThreads * s;
-            const uint16_t *r = rows[q >> 4];
-            v[s] = r ? *(const uint4 *)(r + g * kGemmKG + (q & 15) * 8) : make_uint4(0, 0, 0, 0);
-        }
-    }
-    __device__ __forceinline__ void store(uint8_t *buf, float *xs) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int q = threadIdx.x + kGemmThreads * s;
-            const int row = q >> 4, c = q & 15;
-            uint4 p = v[s];
-            if (FMT == MOE_W_INT4_G128) {          // pairs (i, i+4) of the 8 inputs
-                p.x = (v[s].x & 0xFFFFu) | (v[s].z << 16);
-                p.y = (v[s].x >> 16) | (v[s].z & 0xFFFF0000u);
-                p.z = (v[s].y & 0xFFFFu) | (v[s].w << 16);
-                p.w = (v[s].y >> 16) | (v[s].w & 0xFFFF0000u);
-            }
-            *(uint4 *)(buf + row * kGemmRowBytes + ((c ^ (row & 7)) << 4)) = p;
-            if (FMT == MOE_W_INT4_G128) {
-                const uint32_t one = ACT == MOE_BF16 ? 0x3F803F80u : 0x3C003C00u;
-                float t = 0.0f;
-                t = dot2<ACT>(v[s].x, one, t);
-                t = dot2<ACT>(v[s].y, one, t);
-                t = dot2<ACT>(v[s].z, one, t);
-                t = dot2<ACT>(v[s].w, one, t);
-#pragma unroll
-                for (int m = 8; m >= 1; m >>= 1) t += shfl_xor_f(t, m);
-                if (c == 0) xs[row] = t;
-            }
-        }
-    }
-};
-
 __device__ __forceinline__ int xcd_remap(int b, int nwg) {
     // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
     // contiguous range of logical blocks so blocks sharing a tile (and its
@@ -139,155 +96,330 @@ __device__ __forceinline__ int xcd_remap(int b, int nwg) {
     return xcd * q + min(xcd, r) + b / 8;
 }
 
+// Buffer resource over one expert's matrix: 32-bit offsets, and any offset
+// past `bytes` reads zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0,
+                                             (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
+                                             0x00020000);
+}
+
+// Weights of one pipeline step for one lane: four 16-byte loads per matrix
+// (inputs 64i + 32h .. +31 of the step) and the step's scales.
+template <int FMT>
+struct StepW {
+    uint4 w[4];
+    uint32_t s32;      // int4: the step's two bf16 group scales
+    uint4 s128;        // NVFP4: the step's sixteen E4M3 block scales
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t q, __amdgpu_buffer_rsrc_t s,
+                                         int qoff, int soff, int step, int half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                q, qoff + step * (kGemmKS / 2) + i * 32 + half * 16, 0, 0));
+        if (FMT == MOE_W_INT4_G128)
+            s32 = __builtin_amdgcn_raw_buffer_load_b32(s, soff + step * 4, 0, 0);
+        else
+            s128 = __builtin_bit_cast(uint4,
+                                      __builtin_amdgcn_raw_buffer_load_b128(s, soff + step * 16, 0, 0));
+    }
+};
+
+__device__ __forceinline__ uint32_t byte_of(uint4 v, int i) {
+    const uint32_t d = i < 8 ? (i < 4 ? v.x : v.y) : (i < 12 ? v.z : v.w);
+    return (d >> (8 * (i & 3))) & 0xFF;
+}
+
+// LDS layout of one 256-input step of the 64-row activation tile: eight
+// 1 KB column groups (4 chunks of 16 bytes = 32 inputs each), and inside a
+// group 64 rows of 64 bytes. The chunk slot of a row is XOR-swizzled with
+// bits 1..2 of the row, so the 8 lanes of one 16-byte read phase (8
+// consecutive rows, one chunk) land on 8 different 4-bank groups.
+__device__ __forceinline__ int a_swz(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int a_offset(int row, int chunk) {
+    return ((chunk >> 2) * kGemmTM + row) * 64 + (((chunk & 3) ^ a_swz(row)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One step of the activation tile, global -> LDS by DMA: wave w moves rows
+// 16w .. 16w+15, one 1 KB column group per instruction; lane L carries row
+// 16w + L/4, whose 16-byte chunk slot L%4 holds input chunk (L%4) ^ swz.
+__device__ __forceinline__ void dma_a(uint8_t *buf, const uint16_t *src_row, int step) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = wave * 16 + (lane >> 2);
+    const int kc = (lane & 3) ^ a_swz(row);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        const uint16_t *gp = src_row + step * kGemmKS + (g * 4 + kc) * 8;
+        __builtin_amdgcn_global_load_lds((const void *)gp,
+                                         (lds_void_t *)(buf + (g * kGemmTM + wave * 16) * 64),
+                                         16, 0, 0);
+    }
+}
+
+// The step's two (-BIAS * group sum) values of every row, by DMA (wave 0).
+__device__ __forceinline__ void dma_sums(float *xs_buf, const float *row_sums, int step) {
+    if (threadIdx.x < 64) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+            __builtin_amdgcn_global_load_lds((const void *)(row_sums + 2 * step + gi),
+                                             (lds_void_t *)(xs_buf + gi * kGemmTM), 4, 0, 0);
+    }
+}
+
+template <int ACT, int FMT, bool GATEUP>
+struct GemmCtx {
+    f32x16_t da[2], db[2];
+    float sprev_a, sprev_b;
+    int half, l32;
+    bool two_mb;
+
+    // One 256-input step: MFMAs over the LDS tile `buf` with weights (wa, wb).
+    __device__ __forceinline__ void step(const uint8_t *buf, const float *xs,
+                                         const StepW<FMT> &wa_s, const StepW<FMT> &wb_s) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {            // two 128-input groups per step
+            const uint4 wa0 = wa_s.w[2 * gi], wa1 = wa_s.w[2 * gi + 1];
+            const uint4 wb0 = wb_s.w[2 * gi], wb1 = wb_s.w[2 * gi + 1];
+            uint32_t ma = 0, mbk = 0;
+            if (FMT == MOE_W_INT4_G128) {
+                float sa_g = bf16_bits_to_f32(gi ? wa_s.s32 >> 16 : wa_s.s32 & 0xFFFF);
+                float sb_g = bf16_bits_to_f32(gi ? wb_s.s32 >> 16 : wb_s.s32 & 0xFFFF);
+                // a zero scale drops the group: its nibbles decode as q = 0
+                ma = sa_g == 0.0f ? 0u : 0x000F000Fu;
+                mbk = sb_g == 0.0f ? 0u : 0x000F000Fu;
+                sa_g = sa_g == 0.0f ? 1.0f : sa_g;
+                sb_g = sb_g == 0.0f ? 1.0f : sb_g;
+                const float ra = sprev_a * __builtin_amdgcn_rcpf(sa_g);
+                const float rb = sprev_b * __builtin_amdgcn_rcpf(sb_g);
+                sprev_a = sa_g;
+                sprev_b = sb_g;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    if (mb == 1 && !two_mb) break;
+#pragma unroll
+                    for (int b4 = 0; b4 < 4; ++b4) {
+                        const float4 x4 = *(const float4 *)&xs[gi * kGemmTM + mb * 32 + 8 * b4 + 4 * half];
+                        const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            da[mb][4 * b4 + r] = __builtin_fmaf(da[mb][4 * b4 + r], ra, xv[r]);
+                            db[mb][4 * b4 + r] = __builtin_fmaf(db[mb][4 * b4 + r], rb, xv[r]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+                const uint4 wa = i2 ? wa1 : wa0, wb = i2 ? wb1 : wb0;
+                const uint32_t wav[4] = {wa.x, wa.y, wa.z, wa.w};
+                const uint32_t wbv[4] = {wb.x, wb.y, wb.z, wb.w};
+                const int i = 2 * gi + i2;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float bsa = 0.0f, bsb = 0.0f;
+                    if (FMT == MOE_W_NVFP4_G16) {
+                        const int blk = i * 4 + half * 2 + (j >> 1);
+                        bsa = e4m3_to_f32(byte_of(wa_s.s128, blk));
+                        bsb = e4m3_to_f32(byte_of(wb_s.s128, blk));
+                    }
+                    const uint4 ob = decode_b<ACT, FMT>(wav[j], bsa, ma);
+                    const uint4 obb = decode_b<ACT, FMT>(wbv[j], bsb, mbk);
+                    const int chunk = i * 8 + half * 4 + j;
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb) {
+                        if (mb == 1 && !two_mb) break;
+                        const int row = mb * 32 + l32;
+                        const uint4 av = *(const uint4 *)(buf + a_offset(row, chunk));
+                        da[mb] = mfma32<ACT>(av, ob, da[mb]);
+                        db[mb] = mfma32<ACT>(av, obb, db[mb]);
+                    }
+                }
+            }
+        }
+    }
+};
+
+// vmcnt-only wait (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima).
+#define MOE_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt(0x0F70)
+
+// GATEUP: A = gate, B = up, both for the wave's 32 columns; the epilogue
+// writes h = silu(gate) * up. Otherwise A and B are the same down matrix at
+// columns c and c + 32, so a wave owns 64 output columns and every
+// activation fragment read from LDS feeds two MFMAs in both passes.
 template <int ACT, int FMT, bool GATEUP>
 __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
     GemmMat A, GemmMat Bm, int n_rows, int kin, const uint16_t *__restrict__ xin,
-    int x_from_slots, int topk, const int32_t *__restrict__ sorted_slots,
-    const int32_t *__restrict__ tile_expert, const int32_t *__restrict__ num_tiles,
-    int n_blocks, uint16_t *__restrict__ hout, float *__restrict__ yout) {
+    int x_from_slots, int topk, const float *__restrict__ rowsum_in,
+    const int32_t *__restrict__ sorted_slots, const int32_t *__restrict__ tile_expert,
+    const int32_t *__restrict__ num_tiles, int n_blocks, uint16_t *__restrict__ hout,
+    float *__restrict__ hsum_out, float *__restrict__ yout) {
+    constexpr int BN = GATEUP ? kGemmBN : 2 * kGemmBN;      // output columns per block
     __shared__ __attribute__((aligned(16))) uint8_t abuf[2][kGemmTM * kGemmRowBytes];
-    __shared__ float xsum[2][kGemmTM];
-    __shared__ const uint16_t *rows[kGemmTM];
+    __shared__ __attribute__((aligned(16))) float xsum[2][2 * kGemmTM];
     __shared__ int m_sh;
 
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = lid / n_blocks, nb = lid - tile * n_blocks;
     if (tile >= num_tiles[0]) return;
     const int e = tile_expert[tile];
+    const int groups = kin / 128;
 
-    if (threadIdx.x < kGemmTM) {
-        const int s = sorted_slots[tile * kGemmTM + threadIdx.x];
-        rows[threadIdx.x] = s < 0 ? nullptr
-                            : x_from_slots ? xin + (size_t)(s / topk) * kin
-                                           : xin + (size_t)(tile * kGemmTM + threadIdx.x) * kin;
-        const uint64_t live = __ballot(s >= 0);
+    // this lane's DMA row (padded rows repeat the tile's first, real, row;
+    // their output rows are never stored)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint16_t *src_row;
+    {
+        const int row = wave * 16 + (lane >> 2);
+        int sl = sorted_slots[tile * kGemmTM + row];
+        int prow = row;
+        if (sl < 0) { sl = sorted_slots[tile * kGemmTM]; prow = 0; }
+        src_row = xin + (x_from_slots ? (size_t)(sl / topk) : (size_t)tile * kGemmTM + prow) * kin;
+    }
+    const float *sum_row = nullptr;
+    if (FMT == MOE_W_INT4_G128 && threadIdx.x < kGemmTM) {
+        int sl = sorted_slots[tile * kGemmTM + threadIdx.x];
+        int prow = threadIdx.x;
+        const uint64_t live = __ballot(sl >= 0);
+        if (threadIdx.x == 0) m_sh = __popcll(live);
+        if (sl < 0) { sl = sorted_slots[tile * kGemmTM]; prow = 0; }
+        sum_row = rowsum_in + (x_from_slots ? (size_t)(sl / topk) : (size_t)tile * kGemmTM + prow) * groups;
+    } else if (threadIdx.x < kGemmTM) {
+        const uint64_t live = __ballot(sorted_slots[tile * kGemmTM + threadIdx.x] >= 0);
         if (threadIdx.x == 0) m_sh = __popcll(live);
     }
-    __syncthreads();
-    const int m_valid = m_sh;                    // valid rows come first in a tile
-    const bool two_mb = m_valid > 32;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int half = lane >> 5, l32 = lane & 31;
-    const int col = nb * kGemmBN + wave * 32 + l32;
-    const bool col_ok = col < n_rows;
-    const int colc = col_ok ? col : 0;
-    const uint8_t *qa = A.q + e * A.qe + (int64_t)colc * A.qr;
-    const uint8_t *sa = A.s + e * A.se + (int64_t)colc * A.sr;
-    const uint8_t *qb = GATEUP ? Bm.q + e * Bm.qe + (int64_t)colc * Bm.qr : nullptr;
-    const uint8_t *sb = GATEUP ? Bm.s + e * Bm.se + (int64_t)colc * Bm.sr : nullptr;
+    GemmCtx<ACT, FMT, GATEUP> cx;
+    cx.half = lane >> 5;
+    cx.l32 = lane & 31;
+    const int col_a = nb * BN + wave * (GATEUP ? 32 : 64) + cx.l32;
+    const int col_b = GATEUP ? col_a : col_a + 32;
+    const bool ok_a = col_a < n_rows, ok_b = col_b < n_rows;
+    const __amdgpu_buffer_rsrc_t rqa = make_rsrc(A.q + e * A.qe, (int64_t)n_rows * A.qr);
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(A.s + e * A.se, (int64_t)n_rows * A.sr);
+    const __amdgpu_buffer_rsrc_t rqb = make_rsrc(Bm.q + e * Bm.qe, (int64_t)n_rows * Bm.qr);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(Bm.s + e * Bm.se, (int64_t)n_rows * Bm.sr);
+    const int qoff_a = (ok_a ? col_a : 0) * (int)A.qr, soff_a = (ok_a ? col_a : 0) * (int)A.sr;
+    const int qoff_b = (ok_b ? col_b : 0) * (int)Bm.qr, soff_b = (ok_b ? col_b : 0) * (int)Bm.sr;
 
-    f32x16_t acc_a[2], acc_b[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc_a[mb][v] = acc_b[mb][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) cx.da[mb][v] = cx.db[mb][v] = 0.0f;
+    cx.sprev_a = cx.sprev_b = 1.0f;
 
-    const int ngroups = kin / kGemmKG;
-    Stager<ACT, FMT> st;
-    st.load(rows, 0);
-    st.store(abuf[0], xsum[0]);
+    const int nsteps = kin / kGemmKS;
+    StepW<FMT> w0a, w0b, w1a, w1b;
+    w0a.load(rqa, rsa, qoff_a, soff_a, 0, cx.half);
+    w0b.load(rqb, rsb, qoff_b, soff_b, 0, cx.half);
+    dma_a(abuf[0], src_row, 0);
+    if (FMT == MOE_W_INT4_G128) dma_sums(xsum[0], sum_row, 0);
+    MOE_WAIT_VMCNT0();
     __syncthreads();
+    cx.two_mb = m_sh > 32;
 
-    for (int g = 0; g < ngroups; ++g) {
-        const int cur = g & 1;
-        if (g + 1 < ngroups) st.load(rows, g + 1);
-        // weights of this group: two 16-byte loads per matrix
-        uint4 wa[2], wb[2];
-        float sca = 0.0f, scb = 0.0f;
-        float bsa[2][2], bsb[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t off = (int64_t)g * (kGemmKG / 2) + i * 32 + half * 16;
-            wa[i] = *(const uint4 *)(qa + off);
-            if (GATEUP) wb[i] = *(const uint4 *)(qb + off);
-            if (FMT == MOE_W_NVFP4_G16) {
-                const int blk = g * 8 + i * 4 + half * 2;
-                const uint16_t two = *(const uint16_t *)(sa + blk);
-                bsa[i][0] = e4m3_to_f32(two & 0xFF);
-                bsa[i][1] = e4m3_to_f32(two >> 8);
-                if (GATEUP) {
-                    const uint16_t tb = *(const uint16_t *)(sb + blk);
-                    bsb[i][0] = e4m3_to_f32(tb & 0xFF);
-                    bsb[i][1] = e4m3_to_f32(tb >> 8);
-                }
+    // ping-pong between the two weight register sets: step s computes with
+    // set s&1 while set (s+1)&1 and the next activation step are loading
+    for (int step = 0; step < nsteps; step += 2) {
+        {
+            const bool more = step + 1 < nsteps;
+            if (more) {
+                w1a.load(rqa, rsa, qoff_a, soff_a, step + 1, cx.half);
+                w1b.load(rqb, rsb, qoff_b, soff_b, step + 1, cx.half);
+                dma_a(abuf[1], src_row, step + 1);
+                if (FMT == MOE_W_INT4_G128) dma_sums(xsum[1], sum_row, step + 1);
             }
+            cx.step(abuf[0], xsum[0], w0a, w0b);
+            MOE_WAIT_VMCNT0();
+            __syncthreads();
+            if (!more) break;
         }
-        if (FMT == MOE_W_INT4_G128) {
-            sca = bf16_bits_to_f32(*(const uint16_t *)(sa + 2 * g));
-            if (GATEUP) scb = bf16_bits_to_f32(*(const uint16_t *)(sb + 2 * g));
-        }
-
-        f32x16_t pa[2], pb[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) pa[mb][v] = pb[mb][v] = 0.0f;
-        const uint8_t *buf = abuf[cur];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t wav[4] = {wa[i].x, wa[i].y, wa[i].z, wa[i].w};
-            const uint32_t wbv[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float ba = FMT == MOE_W_NVFP4_G16 ? bsa[i][j >> 1] : 0.0f;
-                const uint4 ob = decode_b<ACT, FMT>(wav[j], ba);
-                uint4 obb = make_uint4(0, 0, 0, 0);
-                if (GATEUP) obb = decode_b<ACT, FMT>(wbv[j], FMT == MOE_W_NVFP4_G16 ? bsb[i][j >> 1] : 0.0f);
-                const int chunk = i * 8 + half * 4 + j;
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    if (mb == 1 && !two_mb) break;
-                    const int row = mb * 32 + l32;
-                    const uint4 av = *(const uint4 *)(buf + row * kGemmRowBytes +
-                                                      ((chunk ^ (row & 7)) << 4));
-                    if (FMT == MOE_W_INT4_G128) {
-                        pa[mb] = mfma32<ACT>(av, ob, pa[mb]);
-                        if (GATEUP) pb[mb] = mfma32<ACT>(av, obb, pb[mb]);
-                    } else {
-                        acc_a[mb] = mfma32<ACT>(av, ob, acc_a[mb]);
-                        if (GATEUP) acc_b[mb] = mfma32<ACT>(av, obb, acc_b[mb]);
-                    }
-                }
+        {
+            const bool more = step + 2 < nsteps;
+            if (more) {
+                w0a.load(rqa, rsa, qoff_a, soff_a, step + 2, cx.half);
+                w0b.load(rqb, rsb, qoff_b, soff_b, step + 2, cx.half);
+                dma_a(abuf[0], src_row, step + 2);
+                if (FMT == MOE_W_INT4_G128) dma_sums(xsum[0], sum_row, step + 2);
             }
+            cx.step(abuf[1], xsum[1], w1a, w1b);
+            MOE_WAIT_VMCNT0();
+            __syncthreads();
         }
-        if (FMT == MOE_W_INT4_G128) {
-            constexpr float bias = Int4Bias<ACT>::kBias;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                if (mb == 1 && !two_mb) break;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                    const float c = bias * xsum[cur][m];
-                    acc_a[mb][v] = __builtin_fmaf(sca, pa[mb][v] - c, acc_a[mb][v]);
-                    if (GATEUP) acc_b[mb][v] = __builtin_fmaf(scb, pb[mb][v] - c, acc_b[mb][v]);
-                }
-            }
-        }
-        if (g + 1 < ngroups) st.store(abuf[cur ^ 1], xsum[cur ^ 1]);
-        __syncthreads();
     }
 
-    if (!col_ok) return;
-    float ga = 1.0f, gb = 1.0f;
-    if (FMT == MOE_W_NVFP4_G16) {
-        ga = A.gs[e];
-        if (GATEUP) gb = Bm.gs[e];
-    }
+    const int m_valid = m_sh;
+    const int half = cx.half;
+    const float ga = FMT == MOE_W_INT4_G128 ? cx.sprev_a : A.gs[e];
+    const float gb = FMT == MOE_W_INT4_G128 ? cx.sprev_b : Bm.gs[e];
+    float *hs = (float *)abuf;                     // [64 rows][128 cols] for the row sums
+    // position of column c inside the pair-permuted layout of its 8-group
+    // (int4 MFMA path only): (c0 c4 c1 c5 c2 c6 c3 c7)
+    const int hcol = FMT == MOE_W_INT4_G128 ? (col_a & ~7) | ((col_a & 3) << 1) | ((col_a >> 2) & 1)
+                                            : col_a;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int m = mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            if (m >= m_valid) continue;
             const size_t r = (size_t)tile * kGemmTM + m;
-            if (GATEUP)
-                hout[r * n_rows + col] = f32_to_act<ACT>(silu_mul(acc_a[mb][v] * ga,
-                                                                  acc_b[mb][v] * gb));
-            else
-                yout[r * n_rows + col] = acc_a[mb][v] * ga;
+            if (GATEUP) {
+                const uint16_t hb = f32_to_act<ACT>(silu_mul(cx.da[mb][v] * ga, cx.db[mb][v] * gb));
+                if (m < m_valid && ok_a) hout[r * n_rows + hcol] = hb;
+                if (FMT == MOE_W_INT4_G128)
+                    hs[m * kGemmBN + wave * 32 + cx.l32] = m < m_valid ? act_to_f32<ACT>(hb) : 0.0f;
+            } else if (m < m_valid) {
+                if (ok_a) yout[r * n_rows + col_a] = cx.da[mb][v] * ga;
+                if (ok_b) yout[r * n_rows + col_b] = cx.db[mb][v] * gb;
+            }
         }
+    }
+    if (GATEUP && FMT == MOE_W_INT4_G128) {
+        // -BIAS * sum of the rounded h over this block's 128 columns: the
+        // down projection's 128-input group nb of row m
+        __syncthreads();
+        const int row = threadIdx.x >> 2, qtr = threadIdx.x & 3;
+        float t = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < 32; ++c) t += hs[row * kGemmBN + qtr * 32 + c];
+        t += shfl_xor_f(t, 1);
+        t += shfl_xor_f(t, 2);
+        if (qtr == 0 && row < m_valid)
+            hsum_out[((size_t)tile * kGemmTM + row) * n_blocks + nb] = -Int4Bias<ACT>::kBias * t;
+    }
+}
+
+// int4 MFMA path, once per token: x with the inputs of every 8-group in
+// the decoder's pair order (x0 x4 x1 x5 x2 x6 x3 x7), and -BIAS times the
+// sum of each 128-input group (float32).
+template <int ACT>
+__global__ void __launch_bounds__(256) prep_x_kernel(const uint16_t *__restrict__ x, int H,
+                                                     uint16_t *__restrict__ xp,
+                                                     float *__restrict__ sums) {
+    const int t = blockIdx.x;
+    const int groups = H / 128;
+    for (int g0 = 0; g0 < groups; g0 += 16) {
+        const int g = g0 + (threadIdx.x >> 4), sub = threadIdx.x & 15;
+        float s = 0.0f;
+        if (g < groups) {
+            const size_t off = (size_t)t * H + g * 128 + sub * 8;
+            const uint4 v = *(const uint4 *)(x + off);
+            uint4 p;
+            p.x = (v.x & 0xFFFFu) | (v.z << 16);
+            p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+            p.z = (v.y & 0xFFFFu) | (v.w << 16);
+            p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+            *(uint4 *)(xp + off) = p;
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s += act_to_f32<ACT>(d[i] & 0xFFFF) + act_to_f32<ACT>(d[i] >> 16);
+        }
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) s += shfl_xor_f(s, m);
+        if (g < groups && sub == 0) sums[(size_t)t * groups + g] = -Int4Bias<ACT>::kBias * s;
     }
 }
 
@@ -298,23 +430,33 @@ inline GemmMat gemm_mat(const moe_weight_desc_t &d) {
 }
 
 template <int ACT, int FMT>
-moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
+moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int T, int K,
                             const moe_perm_t &p, int max_tiles, uint16_t *h, float *y,
-                            hipStream_t s, const std::function<moe_status_t(int)> &mark) {
+                            uint16_t *xperm, float *xsum, float *hsum, hipStream_t s,
+                            const std::function<moe_status_t(int)> &mark) {
     const int F = ex.gate.n, H = ex.gate.k;
+    const uint16_t *xa = x;
+    if (FMT == MOE_W_INT4_G128) {
+        hipLaunchKernelGGL(prep_x_kernel<ACT>, dim3(T), dim3(256), 0, s, x, H, xperm, xsum);
+        MOE_LAUNCH_CHECK();
+        xa = xperm;
+    }
     {
-        const int nbk = (F + kGemmBN - 1) / kGemmBN;
+        const int nbk = F / kGemmBN;
         hipLaunchKernelGGL((gemm_kernel<ACT, FMT, true>), dim3(max_tiles * nbk),
-                           dim3(kGemmThreads), 0, s, gemm_mat(ex.gate), gemm_mat(ex.up), F, H, x,
-                           1, K, p.sorted_slots, p.tile_expert, p.num_tiles, nbk, h, nullptr);
+                           dim3(kGemmThreads), 0, s, gemm_mat(ex.gate), gemm_mat(ex.up), F, H, xa,
+                           1, K, xsum, p.sorted_slots, p.tile_expert, p.num_tiles, nbk, h, hsum,
+                           nullptr);
         MOE_LAUNCH_CHECK();
     }
     if (mark && mark(1) != MOE_OK) return MOE_ERR_HIP;
     {
-        const int nbk = (H + kGemmBN - 1) / kGemmBN;
+        const int nbk = H / (2 * kGemmBN);
+        // A and B are the same down matrix; the kernel offsets B by 32 columns
+        const GemmMat d = gemm_mat(ex.down);
         hipLaunchKernelGGL((gemm_kernel<ACT, FMT, false>), dim3(max_tiles * nbk),
-                           dim3(kGemmThreads), 0, s, gemm_mat(ex.down), gemm_mat(ex.down), H, F,
-                           h, 0, K, p.sorted_slots, p.tile_expert, p.num_tiles, nbk, nullptr, y);
+                           dim3(kGemmThreads), 0, s, d, d, H, F, h, 0, K, hsum, p.sorted_slots,
+                           p.tile_expert, p.num_tiles, nbk, nullptr, nullptr, y);
         MOE_LAUNCH_CHECK();
     }
     if (mark && mark(2) != MOE_OK) return MOE_ERR_HIP;
@@ -322,19 +464,21 @@ moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
 }
 
 int gemm_tile_m() { return kGemmTM; }
-int gemm_group() { return kGemmKG; }
+int gemm_group() { return kGemmKS; }
+int gemm_bn() { return kGemmBN; }
 
-moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
+moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int act, int T, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
-                                 hipStream_t s, const std::function<moe_status_t(int)> &mark) {
+                                 void *xperm, float *xsum, float *hsum, hipStream_t s,
+                                 const std::function<moe_status_t(int)> &mark) {
     const uint16_t *xx = (const uint16_t *)x;
     uint16_t *hh = (uint16_t *)h;
     const bool nv = ex.gate.fmt == MOE_W_NVFP4_G16;
     if (act == MOE_BF16)
-        return nv ? gemm_forward_t<MOE_BF16, MOE_W_NVFP4_G16>(ex, xx, K, p, max_tiles, hh, y, s, mark)
-                  : gemm_forward_t<MOE_BF16, MOE_W_INT4_G128>(ex, xx, K, p, max_tiles, hh, y, s, mark);
-    return nv ? gemm_forward_t<MOE_F16, MOE_W_NVFP4_G16>(ex, xx, K, p, max_tiles, hh, y, s, mark)
-              : gemm_forward_t<MOE_F16, MOE_W_INT4_G128>(ex, xx, K, p, max_tiles, hh, y, s, mark);
+        return nv ? gemm_forward_t<MOE_BF16, MOE_W_NVFP4_G16>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark)
+                  : gemm_forward_t<MOE_BF16, MOE_W_INT4_G128>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark);
+    return nv ? gemm_forward_t<MOE_F16, MOE_W_NVFP4_G16>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark)
+              : gemm_forward_t<MOE_F16, MOE_W_INT4_G128>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark);
 }
 
 }  // namespace moe

@@ -19,8 +19,6 @@
 
 namespace moe {
 
-constexpr int kRouteTok = 8;       // tokens per block in the logit kernel
-constexpr int kRouteKC = 256;      // k-chunk of x staged in LDS
 constexpr int kMaxE = 512;
 constexpr int kMaxK = 16;
 
@@ -95,73 +93,110 @@ __global__ void __launch_bounds__(256) route_given_kernel(
     wave_topk(load, E, K, renorm, ids + (size_t)t * K, wts + (size_t)t * K);
 }
 
-// Logits computed: a block owns kRouteTok tokens and all experts; thread e
-// runs the kRouteTok fma chains of expert e in k order, then waves select.
-template <int ACT>
-__global__ void __launch_bounds__(512) route_logits_kernel(
-    const uint16_t *__restrict__ x, const float *__restrict__ wT,
-    const float *__restrict__ bias, int T, int H, int E, int K, int renorm,
-    int32_t *__restrict__ ids, float *__restrict__ wts) {
-    __shared__ float xs[kRouteKC][kRouteTok];     // token-minor: 2 x b128 reads
-    __shared__ float lg[kRouteTok][kMaxE];
-    const int t0 = blockIdx.x * kRouteTok;
-    const int e = threadIdx.x;
-    const int nthr = blockDim.x;
-    float acc[kRouteTok];
-#pragma unroll
-    for (int i = 0; i < kRouteTok; ++i) acc[i] = 0.0f;
+// Logits computed: a plain fp32 SIMT GEMM, logits[t][e] = x[t] . wT[:, e],
+// in which every output is one fma chain over k in ascending order. Block
+// tile: 64 experts (one per lane) x 32 tokens (8 per wave); k advances in
+// chunks of 64 staged in LDS (double buffered): the 64 x 64 slice of wT
+// read by all four waves, and x widened to float32, token-minor, so a wave
+// reads its 8 tokens' inputs with two broadcast 16-byte LDS reads.
+constexpr int kRtExp = 64, kRtTok = 32, kRtKC = 64;
 
-    for (int k0 = 0; k0 < H; k0 += kRouteKC) {
-        const int kc = min(kRouteKC, H - k0);
-        __syncthreads();
-        for (int i = threadIdx.x; i < kRouteTok * kc; i += nthr) {
-            const int tt = i / kc, kk = i - tt * kc;
-            const int t = t0 + tt;
-            xs[kk][tt] = t < T ? act_to_f32<ACT>(x[(size_t)t * H + k0 + kk]) : 0.0f;
-        }
-        __syncthreads();
-        if (e < E) {
-            const float *w = wT + (size_t)k0 * E + e;
-#pragma unroll 8
-            for (int kk = 0; kk < kc; ++kk) {
-                const float wv = w[(size_t)kk * E];
+template <int ACT>
+__global__ void __launch_bounds__(256) router_logits_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ wT,
+    const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
+    __shared__ __attribute__((aligned(16))) float xs[2][kRtKC][kRtTok];
+    const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    // staging roles: wT rows k = tid/4 (16 experts each, 4 float4 loads),
+    // x: token tid/8, 8 consecutive k (one 16-byte load)
+    const int wk = threadIdx.x >> 2, we = (threadIdx.x & 3) * 16;
+    const int xt = threadIdx.x >> 3, xk = (threadIdx.x & 7) * 8;
+    float4 wreg[4];
+    uint4 xreg;
+    auto load = [&](int k0) {
+        const float *wp = wT + (size_t)(k0 + wk) * E + e0 + we;
 #pragma unroll
-                for (int i = 0; i < kRouteTok; ++i) acc[i] = __builtin_fmaf(xs[kk][i], wv, acc[i]);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int e = e0 + we + 4 * i;
+            wreg[i] = e + 3 < E ? *(const float4 *)(wp + 4 * i)
+                                : make_float4(e < E ? wp[4 * i] : 0.f, e + 1 < E ? wp[4 * i + 1] : 0.f,
+                                              e + 2 < E ? wp[4 * i + 2] : 0.f, 0.f);
         }
-    }
-    if (e < E) {
-        const float b = bias ? bias[e] : 0.0f;
+        const int t = t0 + xt;
+        xreg = t < T ? *(const uint4 *)(x + (size_t)t * H + k0 + xk) : make_uint4(0, 0, 0, 0);
+    };
+    auto store = [&](int b) {
 #pragma unroll
-        for (int i = 0; i < kRouteTok; ++i) lg[i][e] = bias ? acc[i] + b : acc[i];
-    }
+        for (int i = 0; i < 4; ++i) *(float4 *)&ws[b][wk][we + 4 * i] = wreg[i];
+        const uint32_t d[4] = {xreg.x, xreg.y, xreg.z, xreg.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xs[b][xk + 2 * i][xt] = act_to_f32<ACT>(d[i] & 0xFFFF);
+            xs[b][xk + 2 * i + 1][xt] = act_to_f32<ACT>(d[i] >> 16);
+        }
+    };
+
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    const int nch = H / kRtKC;
+    load(0);
+    store(0);
     __syncthreads();
-    const int wave = threadIdx.x >> 6, nwave = nthr >> 6;
-    for (int i = wave; i < kRouteTok; i += nwave) {
-        const int t = t0 + i;
-        if (t >= T) break;
-        auto load = [&](int ee) { return lg[i][ee]; };
-        wave_topk(load, E, K, renorm, ids + (size_t)t * K, wts + (size_t)t * K);
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        if (c + 1 < nch) load((c + 1) * kRtKC);
+#pragma unroll 16
+        for (int k = 0; k < kRtKC; ++k) {
+            const float w = ws[b][k][lane];
+            const float4 xa = *(const float4 *)&xs[b][k][8 * wave];
+            const float4 xb = *(const float4 *)&xs[b][k][8 * wave + 4];
+            acc[0] = __builtin_fmaf(xa.x, w, acc[0]);
+            acc[1] = __builtin_fmaf(xa.y, w, acc[1]);
+            acc[2] = __builtin_fmaf(xa.z, w, acc[2]);
+            acc[3] = __builtin_fmaf(xa.w, w, acc[3]);
+            acc[4] = __builtin_fmaf(xb.x, w, acc[4]);
+            acc[5] = __builtin_fmaf(xb.y, w, acc[5]);
+            acc[6] = __builtin_fmaf(xb.z, w, acc[6]);
+            acc[7] = __builtin_fmaf(xb.w, w, acc[7]);
+        }
+        if (c + 1 < nch) store(b ^ 1);
+        __syncthreads();
+    }
+    const int e = e0 + lane;
+    if (e >= E) return;
+    const float bv = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = t0 + 8 * wave + i;
+        if (t < T) logits[(size_t)t * E + e] = bias ? acc[i] + bv : acc[i];
     }
 }
 
-moe_status_t launch_route(const void *x, int x_dtype, const float *wT, const float *logits,
-                          const float *bias, int T, int H, int E, int K, int renorm,
-                          int32_t *ids, float *wts, hipStream_t s) {
+moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, const float *bias,
+                                  int T, int H, int E, float *logits, hipStream_t s) {
     if (T == 0) return MOE_OK;
-    if (logits) {
-        hipLaunchKernelGGL(route_given_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, bias,
-                           T, E, K, renorm, ids, wts);
-    } else {
-        const int threads = ((E + kWave - 1) / kWave) * kWave;
-        const dim3 grid((T + kRouteTok - 1) / kRouteTok);
-        if (x_dtype == MOE_BF16)
-            hipLaunchKernelGGL(route_logits_kernel<MOE_BF16>, grid, dim3(threads), 0, s,
-                               (const uint16_t *)x, wT, bias, T, H, E, K, renorm, ids, wts);
-        else
-            hipLaunchKernelGGL(route_logits_kernel<MOE_F16>, grid, dim3(threads), 0, s,
-                               (const uint16_t *)x, wT, bias, T, H, E, K, renorm, ids, wts);
-    }
+    const dim3 grid((T + kRtTok - 1) / kRtTok, (E + kRtExp - 1) / kRtExp);
+    if (x_dtype == MOE_BF16)
+        hipLaunchKernelGGL(router_logits_kernel<MOE_BF16>, grid, dim3(256), 0, s,
+                           (const uint16_t *)x, wT, bias, T, H, E, logits);
+    else
+        hipLaunchKernelGGL(router_logits_kernel<MOE_F16>, grid, dim3(256), 0, s,
+                           (const uint16_t *)x, wT, bias, T, H, E, logits);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+// Top-K of logits that are already final (bias, if any, folded in by the
+// caller) or given plus an optional bias.
+moe_status_t launch_topk(const float *logits, const float *bias, int T, int E, int K, int renorm,
+                         int32_t *ids, float *wts, hipStream_t s) {
+    if (T == 0) return MOE_OK;
+    hipLaunchKernelGGL(route_given_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, bias, T, E,
+                       K, renorm, ids, wts);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

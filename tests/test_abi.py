@@ -106,19 +106,38 @@ def test_forward_plan_rejects_bad_sizes(L):
 
 def test_route_topk_validation(L):
     R = L.moe_route_topk
-    ok_ptr = ctypes.c_void_p(FAKE)
-    # K > E, K > 16, E > 512, both or neither logit source, missing x
-    assert R(None, 0, None, ok_ptr, None, 4, 0, 8, 9, 1, ok_ptr, ok_ptr, None) == B.MOE_ERR_INVALID_ARG
-    assert R(None, 0, None, ok_ptr, None, 4, 0, 64, 17, 1, ok_ptr, ok_ptr, None) == B.MOE_ERR_INVALID_ARG
-    assert R(None, 0, None, ok_ptr, None, 4, 0, 513, 8, 1, ok_ptr, ok_ptr, None) == B.MOE_ERR_INVALID_ARG
-    assert R(ok_ptr, 1, ok_ptr, ok_ptr, None, 4, 64, 16, 2, 1, ok_ptr, ok_ptr, None) == B.MOE_ERR_INVALID_ARG
-    assert R(None, 0, None, None, None, 4, 64, 16, 2, 1, ok_ptr, ok_ptr, None) == B.MOE_ERR_INVALID_ARG
-    assert R(None, 1, ok_ptr, None, None, 4, 64, 16, 2, 1, ok_ptr, ok_ptr, None) == B.MOE_ERR_INVALID_ARG
-    assert R(ok_ptr, 1, ok_ptr, None, None, 4, 60, 16, 2, 1, ok_ptr, ok_ptr, None) == B.MOE_ERR_INVALID_ARG
-    assert R(ok_ptr, 3, ok_ptr, None, None, 4, 64, 16, 2, 1, ok_ptr, ok_ptr, None) == B.MOE_ERR_INVALID_ARG
-    assert R(None, 0, None, ok_ptr, None, 4, 0, 16, 2, 1, None, ok_ptr, None) == B.MOE_ERR_INVALID_ARG
+    p = ctypes.c_void_p(FAKE)
+    n = None
+    big = 1 << 30
+    # K > E, K > 16, E > 512, both or neither logit source
+    assert R(n, 0, n, p, n, 4, 0, 8, 9, 1, p, p, n, 0, n) == B.MOE_ERR_INVALID_ARG
+    assert R(n, 0, n, p, n, 4, 0, 64, 17, 1, p, p, n, 0, n) == B.MOE_ERR_INVALID_ARG
+    assert R(n, 0, n, p, n, 4, 0, 513, 8, 1, p, p, n, 0, n) == B.MOE_ERR_INVALID_ARG
+    assert R(p, 1, p, p, n, 4, 64, 16, 2, 1, p, p, p, big, n) == B.MOE_ERR_INVALID_ARG
+    assert R(n, 0, n, n, n, 4, 64, 16, 2, 1, p, p, p, big, n) == B.MOE_ERR_INVALID_ARG
+    # router weight: missing x, bad dtype, H % 64, E % 4, workspace
+    assert R(n, 1, p, n, n, 4, 64, 16, 2, 1, p, p, p, big, n) == B.MOE_ERR_INVALID_ARG
+    assert R(p, 3, p, n, n, 4, 64, 16, 2, 1, p, p, p, big, n) == B.MOE_ERR_INVALID_ARG
+    assert R(p, 1, p, n, n, 4, 96, 16, 2, 1, p, p, p, big, n) == B.MOE_ERR_UNSUPPORTED
+    assert R(p, 1, p, n, n, 4, 64, 18, 2, 1, p, p, p, big, n) == B.MOE_ERR_UNSUPPORTED
+    assert R(p, 1, p, n, n, 4, 64, 16, 2, 1, p, p, n, big, n) == B.MOE_ERR_INVALID_ARG
+    assert R(p, 1, p, n, n, 4, 64, 16, 2, 1, p, p, p, 4 * 16 * 4 - 1, n) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert R(n, 0, n, p, n, 4, 0, 16, 2, 1, n, p, n, 0, n) == B.MOE_ERR_INVALID_ARG
     # T == 0 is a no-op that touches nothing
-    assert R(None, 0, None, ok_ptr, None, 0, 0, 16, 2, 1, ok_ptr, ok_ptr, None) == B.MOE_OK
+    assert R(n, 0, n, p, n, 0, 0, 16, 2, 1, p, p, n, 0, n) == B.MOE_OK
+    assert B.moe_route_workspace(2048, 352, True) == 2048 * 352 * 4
+    assert B.moe_route_workspace(2048, 352, False) == 0
+
+
+def test_router_logits_validation(L):
+    G = L.moe_router_logits
+    p = ctypes.c_void_p(FAKE)
+    assert G(p, 2, None, None, 4, 4096, 352, p, None) == B.MOE_ERR_INVALID_ARG
+    assert G(p, 2, p, None, 4, 4000, 352, p, None) == B.MOE_ERR_UNSUPPORTED
+    assert G(p, 2, ctypes.c_void_p(FAKE + 4), None, 4, 4096, 352, p, None) == B.MOE_ERR_INVALID_ARG
+    assert G(p, 2, p, None, 4, 4096, 352, None, None) == B.MOE_ERR_INVALID_ARG
+    assert G(None, 2, p, None, 0, 4096, 352, None, None) == B.MOE_OK
 
 
 def test_permute_validation(L):

@@ -116,6 +116,21 @@ def test_route_from_router_weight_tiny(dev, act):
     _check_route(ids, w, lg, cfg["K"])
 
 
+@pytest.mark.parametrize("T,Hh,Ee,act", [(37, 4096, 352, "bf16"), (2048, 4096, 352, "bf16"),
+                                         (8, 256, 16, "f16"), (70, 192, 20, "f16")])
+def test_router_logits_bitwise(dev, T, Hh, Ee, act):
+    """The canonical float32 fma chain, bit for bit against the C oracle
+    (partial token and expert tiles included)."""
+    x = synth.activations(T, Hh, act, 5)
+    wT = synth.router_weight_T(Hh, Ee, 5)
+    b = synth.zipf_bias(Ee, 5)
+    for bias in (None, b):
+        got = B.moe_router_logits(x.to(dev), torch.from_numpy(wT).to(dev),
+                                  None if bias is None else torch.from_numpy(bias).to(dev))
+        want = OR.router_logits(x.float().numpy(), wT, bias)
+        assert _bits_equal(got.cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("T,zipf", [(37, False), (2048, False), (300, True)])
 def test_route_from_router_weight_full(dev, T, zipf):
     x = synth.activations(T, H, "bf16", 3)
