@@ -28,6 +28,7 @@ moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int ac
 int gemv_tile_m();
 int gemm_tile_m();
 int gemm_group();
+int gemm_bn();
 }  // namespace moe
 
 using namespace moe;
@@ -119,9 +120,11 @@ bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
     const bool fits = (int64_t)F * ex.gate.qweight_row_stride < INT32_MAX &&
                       (int64_t)F * ex.up.qweight_row_stride < INT32_MAX &&
                       (int64_t)H * ex.down.qweight_row_stride < INT32_MAX;
+    // K steps of gemm_group() inputs; gate/up blocks of gemm_bn() columns,
+    // down blocks of 2 * gemm_bn()
     return (int64_t)T * K >= 4 * (int64_t)E && H % gemm_group() == 0 &&
-           F % gemm_group() == 0 && fits && mfma_layout_ok(ex.gate) && mfma_layout_ok(ex.up) &&
-           mfma_layout_ok(ex.down);
+           F % gemm_group() == 0 && F % gemm_bn() == 0 && H % (2 * gemm_bn()) == 0 && fits &&
+           mfma_layout_ok(ex.gate) && mfma_layout_ok(ex.up) && mfma_layout_ok(ex.down);
 }
 
 FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F, int act) {

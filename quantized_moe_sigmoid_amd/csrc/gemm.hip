@@ -132,40 +132,59 @@ __device__ __forceinline__ uint32_t byte_of(uint4 v, int i) {
 
 // LDS layout of one 256-input step of the 64-row activation tile: eight
 // 1 KB column groups (4 chunks of 16 bytes = 32 inputs each), and inside a
-// group 64 rows of 64 bytes. The chunk slot of a row is XOR-swizzled with
-// bits 1..2 of the row, so the 8 lanes of one 16-byte read phase (8
-// consecutive rows, one chunk) land on 8 different 4-bank groups.
-__device__ __forceinline__ int a_swz(int row) { return (row >> 1) & 3; }
+// group 64 rows of 64 bytes. The chunk slot of a row is XOR-swizzled so
+// that one 16-byte read of a chunk by 16 consecutive rows (the lanes one
+// cycle of a 64-bank LDS serves) touches 16 different 4-bank groups:
+// the group is 4 * (row & 3) + (slot), and the swizzle makes the slot take
+// all four values over rows of equal row & 3 (it also spreads 8 rows over
+// a 32-bank LDS).
+__device__ __forceinline__ int a_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int a_offset(int row, int chunk) {
     return ((chunk >> 2) * kGemmTM + row) * 64 + (((chunk & 3) ^ a_swz(row)) << 4);
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
+// One step of the 64-row activation tile through registers into LDS.
+// Thread t owns row t/4 and chunk slot t%4 of each of the eight column
+// groups; the slot holds input chunk (t%4) ^ swz(row), so the four threads
+// of a row read 64 contiguous bytes per group and a wave writes 1 KB of LDS
+// contiguously. Thread t < 64 also carries row t's two (-BIAS * group sum)
+// values (int4).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// One step of the activation tile, global -> LDS by DMA: wave w moves rows
-// 16w .. 16w+15, one 1 KB column group per instruction; lane L carries row
-// 16w + L/4, whose 16-byte chunk slot L%4 holds input chunk (L%4) ^ swz.
-__device__ __forceinline__ void dma_a(uint8_t *buf, const uint16_t *src_row, int step) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = wave * 16 + (lane >> 2);
-    const int kc = (lane & 3) ^ a_swz(row);
+template <int FMT>
+struct Stager {
+    u32x4_t v[8];      // a native vector type: HIP's uint4 struct copies become
+                       // memcpy through scratch memory
+    float rs0, rs1;
+    __device__ __forceinline__ void load(const uint16_t *src_row, const float *sum_row, int step) {
+        const int row = threadIdx.x >> 2;
+        const int kc = (threadIdx.x & 3) ^ a_swz(row);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-        const uint16_t *gp = src_row + step * kGemmKS + (g * 4 + kc) * 8;
-        __builtin_amdgcn_global_load_lds((const void *)gp,
-                                         (lds_void_t *)(buf + (g * kGemmTM + wave * 16) * 64),
-                                         16, 0, 0);
+        for (int g = 0; g < 8; ++g)
+            v[g] = *(const u32x4_t *)(src_row + step * kGemmKS + (g * 4 + kc) * 8);
+        if (FMT == MOE_W_INT4_G128 && threadIdx.x < kGemmTM) {
+            rs0 = sum_row[2 * step];
+            rs1 = sum_row[2 * step + 1];
+        }
     }
-}
+    __device__ __forceinline__ void store(uint8_t *buf, float *xs) {
+        const int row = threadIdx.x >> 2;
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+            *(u32x4_t *)(buf + (g * kGemmTM + row) * 64 + ((threadIdx.x & 3) << 4)) = v[g];
+        if (FMT == MOE_W_INT4_G128 && threadIdx.x < kGemmTM) {
+            xs[threadIdx.x] = rs0;
+            xs[kGemmTM + threadIdx.x] = rs1;
+        }
+    }
+};
 
-// The step's two (-BIAS * group sum) values of every row, by DMA (wave 0).
-__device__ __forceinline__ void dma_sums(float *xs_buf, const float *row_sums, int step) {
-    if (threadIdx.x < 64) {
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-            __builtin_amdgcn_global_load_lds((const void *)(row_sums + 2 * step + gi),
-                                             (lds_void_t *)(xs_buf + gi * kGemmTM), 4, 0, 0);
-    }
+// Workgroup barrier that orders LDS only: outstanding global loads (the
+// next step's weights) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <int ACT, int FMT, bool GATEUP>
@@ -241,24 +260,28 @@ struct GemmCtx {
     }
 };
 
-// vmcnt-only wait (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14,
-// expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima).
-#define MOE_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt(0x0F70)
-
 // GATEUP: A = gate, B = up, both for the wave's 32 columns; the epilogue
 // writes h = silu(gate) * up. Otherwise A and B are the same down matrix at
 // columns c and c + 32, so a wave owns 64 output columns and every
 // activation fragment read from LDS feeds two MFMAs in both passes.
 template <int ACT, int FMT, bool GATEUP>
 __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
-    GemmMat A, GemmMat Bm, int n_rows, int kin, const uint16_t *__restrict__ xin,
-    int x_from_slots, int topk, const float *__restrict__ rowsum_in,
+    GemmMat A, GemmMat Bm, int n_rows, int kin,
+    // xin and rowsum_in are not __restrict__: as restrict read-only kernel
+    // arguments their loads count as invariant and get sunk below the MFMAs
+    // that should hide their latency
+    const uint16_t *xin, int x_from_slots, int topk, const float *rowsum_in,
     const int32_t *__restrict__ sorted_slots, const int32_t *__restrict__ tile_expert,
     const int32_t *__restrict__ num_tiles, int n_blocks, uint16_t *__restrict__ hout,
     float *__restrict__ hsum_out, float *__restrict__ yout) {
     constexpr int BN = GATEUP ? kGemmBN : 2 * kGemmBN;      // output columns per block
-    __shared__ __attribute__((aligned(16))) uint8_t abuf[2][kGemmTM * kGemmRowBytes];
-    __shared__ __attribute__((aligned(16))) float xsum[2][2 * kGemmTM];
+    // two separate LDS objects per double buffer: the compiler then knows a
+    // DMA into one does not alias reads of the other, and does not make the
+    // reads wait for the DMA
+    __shared__ __attribute__((aligned(16))) uint8_t abuf0[kGemmTM * kGemmRowBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t abuf1[kGemmTM * kGemmRowBytes];
+    __shared__ __attribute__((aligned(16))) float xsum0[2 * kGemmTM];
+    __shared__ __attribute__((aligned(16))) float xsum1[2 * kGemmTM];
     __shared__ int m_sh;
 
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -267,28 +290,27 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
     const int e = tile_expert[tile];
     const int groups = kin / 128;
 
-    // this lane's DMA row (padded rows repeat the tile's first, real, row;
-    // their output rows are never stored)
+    // this thread's staging row (padded rows repeat the tile's first, real,
+    // row; their output rows are never stored)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint16_t *src_row;
     {
-        const int row = wave * 16 + (lane >> 2);
+        const int row = threadIdx.x >> 2;
         int sl = sorted_slots[tile * kGemmTM + row];
         int prow = row;
         if (sl < 0) { sl = sorted_slots[tile * kGemmTM]; prow = 0; }
         src_row = xin + (x_from_slots ? (size_t)(sl / topk) : (size_t)tile * kGemmTM + prow) * kin;
     }
     const float *sum_row = nullptr;
-    if (FMT == MOE_W_INT4_G128 && threadIdx.x < kGemmTM) {
+    if (threadIdx.x < kGemmTM) {
         int sl = sorted_slots[tile * kGemmTM + threadIdx.x];
         int prow = threadIdx.x;
         const uint64_t live = __ballot(sl >= 0);
         if (threadIdx.x == 0) m_sh = __popcll(live);
         if (sl < 0) { sl = sorted_slots[tile * kGemmTM]; prow = 0; }
-        sum_row = rowsum_in + (x_from_slots ? (size_t)(sl / topk) : (size_t)tile * kGemmTM + prow) * groups;
-    } else if (threadIdx.x < kGemmTM) {
-        const uint64_t live = __ballot(sorted_slots[tile * kGemmTM + threadIdx.x] >= 0);
-        if (threadIdx.x == 0) m_sh = __popcll(live);
+        if (FMT == MOE_W_INT4_G128)
+            sum_row = rowsum_in +
+                      (x_from_slots ? (size_t)(sl / topk) : (size_t)tile * kGemmTM + prow) * groups;
     }
 
     GemmCtx<ACT, FMT, GATEUP> cx;
@@ -310,51 +332,51 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
         for (int v = 0; v < 16; ++v) cx.da[mb][v] = cx.db[mb][v] = 0.0f;
     cx.sprev_a = cx.sprev_b = 1.0f;
 
+    // Pipeline: while step s computes, the activations and the weights of
+    // step s+1 load into registers; after the MFMAs the activations go to
+    // the other LDS buffer and an LDS-only barrier closes the step, so the
+    // weight loads stay in flight until their first use.
     const int nsteps = kin / kGemmKS;
-    StepW<FMT> w0a, w0b, w1a, w1b;
-    w0a.load(rqa, rsa, qoff_a, soff_a, 0, cx.half);
-    w0b.load(rqb, rsb, qoff_b, soff_b, 0, cx.half);
-    dma_a(abuf[0], src_row, 0);
-    if (FMT == MOE_W_INT4_G128) dma_sums(xsum[0], sum_row, 0);
-    MOE_WAIT_VMCNT0();
+    Stager<FMT> st;
+    StepW<FMT> wa0, wb0, wa1, wb1;
+    st.load(src_row, sum_row, 0);
+    wa0.load(rqa, rsa, qoff_a, soff_a, 0, cx.half);
+    wb0.load(rqb, rsb, qoff_b, soff_b, 0, cx.half);
+    st.store(abuf0, xsum0);
     __syncthreads();
     cx.two_mb = m_sh > 32;
 
-    // ping-pong between the two weight register sets: step s computes with
-    // set s&1 while set (s+1)&1 and the next activation step are loading
-    for (int step = 0; step < nsteps; step += 2) {
-        {
-            const bool more = step + 1 < nsteps;
-            if (more) {
-                w1a.load(rqa, rsa, qoff_a, soff_a, step + 1, cx.half);
-                w1b.load(rqb, rsb, qoff_b, soff_b, step + 1, cx.half);
-                dma_a(abuf[1], src_row, step + 1);
-                if (FMT == MOE_W_INT4_G128) dma_sums(xsum[1], sum_row, step + 1);
-            }
-            cx.step(abuf[0], xsum[0], w0a, w0b);
-            MOE_WAIT_VMCNT0();
-            __syncthreads();
-            if (!more) break;
-        }
-        {
-            const bool more = step + 2 < nsteps;
-            if (more) {
-                w0a.load(rqa, rsa, qoff_a, soff_a, step + 2, cx.half);
-                w0b.load(rqb, rsb, qoff_b, soff_b, step + 2, cx.half);
-                dma_a(abuf[0], src_row, step + 2);
-                if (FMT == MOE_W_INT4_G128) dma_sums(xsum[0], sum_row, step + 2);
-            }
-            cx.step(abuf[1], xsum[1], w1a, w1b);
-            MOE_WAIT_VMCNT0();
-            __syncthreads();
-        }
+#define MOE_GEMM_STEP(S, BUF, XS, NBUF, NXS, WA, WB, NWA, NWB)                          \
+    {                                                                                  \
+        const int s_ = (S);                                                            \
+        if (s_ >= nsteps) break;                                                       \
+        const bool more = s_ + 1 < nsteps;                                             \
+        /* unconditional (the last step reloads itself): conditional loads */         \
+        /* would merge with the old register values and force early waits */         \
+        const int sn = more ? s_ + 1 : s_;                                             \
+        st.load(src_row, sum_row, sn);                                                 \
+        NWA.load(rqa, rsa, qoff_a, soff_a, sn, cx.half);                               \
+        NWB.load(rqb, rsb, qoff_b, soff_b, sn, cx.half);                               \
+        /* keep the compiler from sinking the prefetch below the MFMAs */             \
+        /* (no memory clobber: it would pin the staging registers to memory) */       \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        cx.step(BUF, XS, WA, WB);                                                      \
+        /* unconditional too, so the loads are not sunk into a branch */              \
+        st.store(NBUF, NXS);                                                           \
+        lds_barrier();                                                                 \
     }
+
+    for (int step = 0; step < nsteps; step += 2) {
+        MOE_GEMM_STEP(step, abuf0, xsum0, abuf1, xsum1, wa0, wb0, wa1, wb1)
+        MOE_GEMM_STEP(step + 1, abuf1, xsum1, abuf0, xsum0, wa1, wb1, wa0, wb0)
+    }
+#undef MOE_GEMM_STEP
 
     const int m_valid = m_sh;
     const int half = cx.half;
     const float ga = FMT == MOE_W_INT4_G128 ? cx.sprev_a : A.gs[e];
     const float gb = FMT == MOE_W_INT4_G128 ? cx.sprev_b : Bm.gs[e];
-    float *hs = (float *)abuf;                     // [64 rows][128 cols] for the row sums
+    float *hs = (float *)abuf0;                    // [64 rows][128 cols] for the row sums
     // position of column c inside the pair-permuted layout of its 8-group
     // (int4 MFMA path only): (c0 c4 c1 c5 c2 c6 c3 c7)
     const int hcol = FMT == MOE_W_INT4_G128 ? (col_a & ~7) | ((col_a & 3) << 1) | ((col_a >> 2) & 1)

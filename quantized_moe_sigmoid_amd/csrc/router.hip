@@ -105,32 +105,36 @@ template <int ACT>
 __global__ void __launch_bounds__(256) router_logits_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wT,
     const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
+    // xs rows padded to 36 floats: the transposing stores of two k rows 8
+    // apart then fall on different bank halves; 36 * 4 bytes keeps every
+    // 8-token group 16-byte aligned for the broadcast reads
     __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
-    __shared__ __attribute__((aligned(16))) float xs[2][kRtKC][kRtTok];
+    __shared__ __attribute__((aligned(16))) float xs[2][kRtKC][kRtTok + 4];
     const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-    // staging roles: wT rows k = tid/4 (16 experts each, 4 float4 loads),
-    // x: token tid/8, 8 consecutive k (one 16-byte load)
-    const int wk = threadIdx.x >> 2, we = (threadIdx.x & 3) * 16;
-    const int xt = threadIdx.x >> 3, xk = (threadIdx.x & 7) * 8;
+    // staging roles: wT float4 column tid%16 of rows tid/16 + 16 i (each
+    // store instruction writes 4 whole 256-byte rows: no bank conflicts);
+    // x: token tid%32, 8 consecutive k starting at 8 * (tid/32)
+    const int wk = threadIdx.x >> 4, we = (threadIdx.x & 15) * 4;
+    const int xt = threadIdx.x & 31, xk = (threadIdx.x >> 5) * 8;
     float4 wreg[4];
     uint4 xreg;
     auto load = [&](int k0) {
-        const float *wp = wT + (size_t)(k0 + wk) * E + e0 + we;
+        const int e = e0 + we;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int e = e0 + we + 4 * i;
-            wreg[i] = e + 3 < E ? *(const float4 *)(wp + 4 * i)
-                                : make_float4(e < E ? wp[4 * i] : 0.f, e + 1 < E ? wp[4 * i + 1] : 0.f,
-                                              e + 2 < E ? wp[4 * i + 2] : 0.f, 0.f);
+            const float *wp = wT + (size_t)(k0 + wk + 16 * i) * E + e;
+            wreg[i] = e + 3 < E ? *(const float4 *)wp
+                                : make_float4(e < E ? wp[0] : 0.f, e + 1 < E ? wp[1] : 0.f,
+                                              e + 2 < E ? wp[2] : 0.f, 0.f);
         }
         const int t = t0 + xt;
         xreg = t < T ? *(const uint4 *)(x + (size_t)t * H + k0 + xk) : make_uint4(0, 0, 0, 0);
     };
     auto store = [&](int b) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(float4 *)&ws[b][wk][we + 4 * i] = wreg[i];
+        for (int i = 0; i < 4; ++i) *(float4 *)&ws[b][wk + 16 * i][we] = wreg[i];
         const uint32_t d[4] = {xreg.x, xreg.y, xreg.z, xreg.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
