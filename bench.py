@@ -151,12 +151,90 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt):
              touched_experts=float(U.mean()),
              layer_GBps=float((U * (gu_bytes + dn_bytes)).mean() / (ms * 1e-3) / 1e9),
              gateup_ms=float(gu_ms.mean()), down_ms=float(stage_ms[:, 1].mean()),
-             combine_ms=float(stage_ms[:, 2].mean()),
+             combine_ms=float(stage_ms[:, 3].mean()),
              gateup_GBps=float(np.mean(U * gu_bytes / (gu_ms * 1e-3)) / 1e9),
              down_GBps=float(np.mean(U * dn_bytes / (stage_ms[:, 1] * 1e-3)) / 1e9),
              layer_TFLOPs=float(T * K * FLOP_PER_SLOT / (ms * 1e-3) / 1e12))
     r["gateup_frac_hbm"] = r["gateup_GBps"] * 1e9 / HBM_PEAK
     return r
+
+
+class StackLayer:
+    """One layer of the stack: 352 random packed int4 experts, a BF16 shared
+    expert N(0, 0.02), a router weight N(0, 0.02) and Zipf expert biases."""
+
+    def __init__(self, l, dev):
+        mats = []
+        for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
+            q, s = synth.packed_int4_random(E, n, k, 7000 + 10 * l + i, dev)
+            mats.append(B.bank_int4(q, s))
+        self.ffn = B.ffn(*mats)
+        sh = [synth.device_normal(shape, 0.02, 7500 + 10 * l + i, dev, torch.bfloat16)
+              for i, shape in enumerate(((F, H), (F, H), (H, F)))]
+        self.shared = B.ffn(*[B.bank_bf16(w) for w in sh])
+        self.wT = torch.from_numpy(synth.router_weight_T(H, E, 5, l)).to(dev)
+        self.bias = torch.from_numpy(synth.zipf_bias(E, 5, l)).to(dev)
+        self.norm_w = torch.from_numpy(synth.norm_weight(H, 5, l)).to(dev)
+
+
+def run_stack(layers, T, steps, warmup, hip, dev):
+    """Times `steps` passes of the 8-layer stack: per layer, the RMSNorm of
+    the fp32 residual rounded to bf16, routing from the router weight plus Zipf bias,
+    permutation, routed + shared experts and the combine with the residual."""
+    r0 = synth.activations(T, H, "bf16", 5).float().to(dev)
+    res = [r0.clone(), torch.empty_like(r0)]
+    a = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    tm, ws_bytes = B.moe_forward_plan(layers[0].ffn, T, K, torch.bfloat16, layers[0].shared)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    perm = B.Perm(T, K, E, tm, dev)
+    rws = torch.empty(B.moe_route_workspace(T, E, True), dtype=torch.uint8, device=dev)
+    NS = B.MOE_FORWARD_STAGES
+    ev = [[[hip.event() for _ in range(NS + 1)] for _ in layers] for _ in range(steps)]
+
+    def step(events=None, keep_ids=None):
+        res[0].copy_(r0)
+        for l, L in enumerate(layers):
+            src, dst = res[l % 2], res[(l + 1) % 2]
+            B.moe_rmsnorm(src, L.norm_w, 1e-5, out=a)
+            B.moe_route_topk(K, x=a, router_wT=L.wT, bias=L.bias, ids=ids, w=w, ws=rws)
+            B.moe_permute(ids, E, tm, perm=perm)
+            B.moe_w4a16_forward(L.ffn, a, w, perm, residual=src, out=dst, ws=ws,
+                                shared=L.shared, events=None if events is None else events[l])
+            if keep_ids is not None:
+                keep_ids.append(int(torch.unique(ids).numel()))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = np.array([[[hip.elapsed_ms(e[j], e[j + 1]) for j in range(NS)] for e in le]
+                   for le in ev])                          # [step, layer, stage]
+    for le in ev:
+        for e in le:
+            for h in e:
+                hip.destroy(h)
+    U = []
+    step(keep_ids=U)
+    torch.cuda.synchronize()
+    ms = wall / steps * 1e3
+    per = st.sum(axis=1).mean(axis=0)                      # stage ms per step, all layers
+    flop = len(layers) * T * (K + 1) * FLOP_PER_SLOT
+    gu_flop = len(layers) * T * K * 2 * 2 * H * F
+    return dict(workload="stack T=%d" % T, tokens=T, layers=len(layers), ms_per_step=ms,
+                tok_s=T / (ms * 1e-3), ms_per_layer=ms / len(layers),
+                touched_experts=float(np.mean(U)),
+                layer_GBps=float(np.sum(U) * (INT4_GATEUP_BYTES + INT4_DOWN_BYTES) /
+                                 (ms * 1e-3) / 1e9),
+                gateup_ms=float(per[0]), down_ms=float(per[1]), shared_ms=float(per[2]),
+                combine_ms=float(per[3]),
+                gateup_TFLOPs=float(gu_flop / (per[0] * 1e-3) / 1e12),
+                layer_TFLOPs=float(flop / (ms * 1e-3) / 1e12))
 
 
 def cpu_baseline(dev_banks, n_tok=2):
@@ -220,7 +298,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "nvfp4"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "nvfp4", "stack"])
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -235,28 +314,39 @@ def main():
 
     int4 = int4_banks(2, dev, 500)
     jobs = []
-    main_T = args.tokens or {"decode": 64, "prefill": 2048, "nvfp4": 256}[args.workload]
+    main_T = args.tokens or {"decode": 64, "prefill": 2048, "nvfp4": 256,
+                             "stack": 4096}[args.workload]
     spec = {"decode": ("f16", "logits", "int4"), "prefill": ("bf16", "weights", "int4"),
-            "nvfp4": ("bf16", "logits", "nvfp4")}
+            "nvfp4": ("bf16", "logits", "nvfp4"), "stack": ("bf16", "weights", "int4")}
     jobs.append((args.workload, main_T))
     if not args.no_sweep:
         for wl, T in (("decode", 1), ("decode", 8), ("decode", 64), ("prefill", 2048),
-                      ("nvfp4", 1), ("nvfp4", 256)):
+                      ("nvfp4", 1), ("nvfp4", 256), ("stack", 32), ("stack", 4096)):
             if (wl, T) != (args.workload, main_T):
                 jobs.append((wl, T))
     nv = None
+    stack = None
     results = []
     for wl, T in jobs:
         act, rmode, fmt = spec[wl]
-        if fmt == "nvfp4" and nv is None:
-            nv = nvfp4_banks(2, dev, 900)
-        banks = int4 if fmt == "int4" else nv
         steps = args.steps if (wl, T) == jobs[0] else max(10, args.steps // 2)
-        results.append(run_layer("%s T=%d" % (wl, T), banks, T, act, rmode, steps, args.warmup,
-                                 hip, dev, fmt))
+        if wl == "stack":
+            if stack is None:
+                stack = [StackLayer(l, dev) for l in range(8)]
+            results.append(run_stack(stack, T, max(5, steps // 4), max(2, args.warmup // 4),
+                                     hip, dev))
+        else:
+            if fmt == "nvfp4" and nv is None:
+                nv = nvfp4_banks(2, dev, 900)
+            banks = int4 if fmt == "int4" else nv
+            results.append(run_layer("%s T=%d" % (wl, T), banks, T, act, rmode, steps,
+                                     args.warmup, hip, dev, fmt))
         print("# %s" % json.dumps(results[-1]), file=sys.stderr, flush=True)
 
     head = results[0]
+    if args.workload == "stack":
+        print(json.dumps({"workload": "stack", "result": head}))
+        return
     act, rmode, fmt = spec[args.workload]
     kern = "gemv_gateup_%s_%s" % (fmt, act)
     traffic = traffic_for(kern)

@@ -180,7 +180,9 @@ moe_status_t moe_permute(const int32_t *topk_ids, int T, int K, int E,
                          const moe_perm_t *perm, void *stream);
 
 /* The tile_m the forward pass needs for T tokens (host output), and the
- * workspace bytes it needs (host output). Pass that tile_m to moe_permute. */
+ * workspace bytes it needs (host output), with or without the shared expert
+ * (same argument rules as moe_w4a16_forward). Pass that tile_m to
+ * moe_permute. */
 moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts,
                               const moe_ffn_desc_t *shared, int T, int K,
                               int act_dtype, int *tile_m, size_t *ws_bytes);
@@ -199,7 +201,10 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts,
  *
  * x [T][H] in act_dtype (MOE_F16 or MOE_BF16); experts: int4-g128 or NVFP4
  * bank with gate/up [F][H] and down [H][F]; shared: NULL or a MOE_W_BF16
- * bank with num_experts == 1 (act_dtype must then be MOE_BF16);
+ * bank with num_experts == 1, gate/up [Fs][H], down [H][Fs] (act_dtype must
+ * then be MOE_BF16; Fs % 128 == 0 and H % 256 == 0, else
+ * MOE_ERR_UNSUPPORTED); the shared expert's h is rounded to bf16 like the
+ * routed experts' h, and its output is added unweighted;
  * topk_w [T][K] float; perm: moe_permute output for this routing with the
  * tile_m from moe_forward_plan; residual: NULL or [T][H] float;
  * out [T][H] in out_dtype (MOE_F32, MOE_F16 or MOE_BF16); ws: device
@@ -216,14 +221,15 @@ moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts,
                                void *ws, size_t ws_bytes, void *stream);
 
 /* Number of timed stages of moe_w4a16_forward_profiled. */
-#define MOE_FORWARD_STAGES 3
+#define MOE_FORWARD_STAGES 4
 
 /*
  * moe_w4a16_forward_profiled -- moe_w4a16_forward, additionally recording
  * the caller's HIP events on `stream` at the stage boundaries, so the
  * caller can time each kernel stage with hipEventElapsedTime:
- *   events[0] | gate/up + SwiGLU | events[1] | down | events[2] |
- *   combine | events[3]
+ *   events[0] | routed gate/up + SwiGLU | events[1] | routed down |
+ *   events[2] | shared expert (empty without one) | events[3] | combine |
+ *   events[4]
  * events: host array of n_events == MOE_FORWARD_STAGES + 1 hipEvent_t
  * handles (passed as void*), created by the caller. Same results, same
  * kernels, same validation as moe_w4a16_forward.
@@ -235,6 +241,31 @@ moe_status_t moe_w4a16_forward_profiled(const moe_ffn_desc_t *experts,
                                         const float *residual, void *out, int out_dtype,
                                         void *ws, size_t ws_bytes, void *stream,
                                         void *const *events, int n_events);
+
+/*
+ * moe_round_activations -- out[i] = in[i] rounded to out_dtype (MOE_F16 or
+ * MOE_BF16) to nearest, ties to even, for 0 <= i < n: the next layer's
+ * 16-bit input from the float32 residual stream when layers are stacked
+ * (page "Step 5 Preview: ...", "The shape: narrow and deep", on
+ * fp32_residual_connection). in float [n] and out [n] 16-byte aligned.
+ * n == 0 is a no-op.
+ */
+moe_status_t moe_round_activations(const float *in, int64_t n, int out_dtype, void *out,
+                                   void *stream);
+
+/*
+ * moe_rmsnorm -- the normalised 16-bit input of a layer from the float32
+ * residual stream (page "Step 5 Preview: ...", the paragraph on training the
+ * deep stack: Step5RMSNorm scales x / rms(x) by the zero-centred gain
+ * (1 + w), computed in fp32; the gain is stored in FP32):
+ *   out[t][h] = x[t][h] / sqrt(mean_h x[t][h]^2 + eps) * (1 + weight[h])
+ * evaluated in float64 and rounded once to out_dtype (MOE_F16 or MOE_BF16),
+ * to nearest, ties to even. x [T][H] float and weight [H] float (NULL = all
+ * zero, a gain of 1) 16-byte aligned; out [T][H] 16-byte aligned.
+ * Limits: H % 4 == 0, 4 <= H <= 16384, 0 <= eps <= 1. T == 0 is a no-op.
+ */
+moe_status_t moe_rmsnorm(const float *x, const float *weight, float eps, int T, int H,
+                         int out_dtype, void *out, void *stream);
 
 /*
  * moe_dequant -- the exact dequantized matrix of one expert, as float32

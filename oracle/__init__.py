@@ -19,8 +19,8 @@ quant     int4-g128 symmetric quantizer with the 17-ratio clip search,
 router    canonical float32 router logits (C), top-K selection, sigmoid
           weights with renormalisation.
 permute   expert histogram, stable expert-sorted permutation, padded tiles.
-layer     SwiGLU expert FFN, weighted combine, shared expert, residual, and
-          the chained-layer stack.
+layer     SwiGLU expert FFN, weighted combine, shared expert, residual.
+norm      the zero-centred-gain RMSNorm that feeds each layer of the stack.
 
 Every function with no independent pin says "parity unpinned" in its
 docstring.

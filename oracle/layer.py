@@ -23,9 +23,9 @@ exact dequantized values and x is the 16-bit activation widened exactly.
 
 Readings: silu applies to the gate and multiplies the up projection; there is
 no clamp (the NVFP4 page names a "SwiGLU limit" but gives neither formula nor
-value); the shared expert's output is added unweighted; in the chained stack
-there is no norm between layers, each layer's input is the fp32 residual
-rounded to the activation dtype, and its output is added to the residual.
+value); the shared expert's output is added unweighted. The chained stack
+(see norm.py) feeds each layer the RMSNorm of the fp32 residual rounded to
+the activation dtype and adds the layer's output back to the residual.
 """
 import numpy as np
 

@@ -20,8 +20,8 @@ MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16 = 1, 2, 3
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_route_workspace",
            "moe_route_topk", "moe_permute_sizes",
            "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_w4a16_forward_profiled",
-           "moe_dequant")
-MOE_FORWARD_STAGES = 3
+           "moe_round_activations", "moe_rmsnorm", "moe_dequant")
+MOE_FORWARD_STAGES = 4
 
 _DT = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
 _TD = {v: k for k, v in _DT.items()}
@@ -79,10 +79,13 @@ def lib():
         L.moe_w4a16_forward.argtypes = [P(FfnDesc), P(FfnDesc), vp, i32, i32, i32, vp,
                                         P(PermDesc), vp, vp, i32, vp, sz, vp]
         L.moe_w4a16_forward_profiled.argtypes = L.moe_w4a16_forward.argtypes + [P(vp), i32]
+        L.moe_round_activations.argtypes = [vp, i64, i32, vp, vp]
+        L.moe_rmsnorm.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, vp]
         L.moe_dequant.argtypes = [P(WeightDesc), i32, vp, vp]
         for name in ("moe_router_logits", "moe_route_workspace", "moe_route_topk",
                      "moe_permute_sizes", "moe_permute", "moe_forward_plan",
-                     "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_dequant"):
+                     "moe_w4a16_forward", "moe_w4a16_forward_profiled",
+                     "moe_round_activations", "moe_rmsnorm", "moe_dequant"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -123,6 +126,16 @@ def bank_nvfp4(qweight, scale, global_scale):
                    global_scale.data_ptr(), qweight.stride(0), qweight.stride(1),
                    scale.stride(0), scale.stride(1))
     d._keep = (qweight, scale, global_scale)
+    return d
+
+
+def bank_bf16(weight):
+    """weight bf16 [n, k] or [E, n, k] (device), rows contiguous."""
+    w = weight if weight.dim() == 3 else weight.unsqueeze(0)
+    E, n, k = w.shape
+    d = WeightDesc(MOE_W_BF16, E, n, k, w.data_ptr(), None, None,
+                   w.stride(0) * 2, w.stride(1) * 2, 0, 0)
+    d._keep = (w,)
     return d
 
 
@@ -218,7 +231,8 @@ def moe_permute(topk_ids, E, tile_m, perm=None):
 
 def moe_forward_plan(experts, T, K, act_dtype, shared=None):
     tm, ws = ctypes.c_int(), ctypes.c_size_t()
-    st = lib().moe_forward_plan(ctypes.byref(experts), ctypes.byref(shared) if shared else None,
+    st = lib().moe_forward_plan(ctypes.byref(experts),
+                                ctypes.byref(shared) if shared is not None else None,
                                 T, K, _DT[act_dtype], ctypes.byref(tm), ctypes.byref(ws))
     _check(st, "moe_forward_plan")
     return tm.value, ws.value
@@ -237,7 +251,7 @@ def moe_w4a16_forward(experts, x, topk_w, perm, residual=None, out_dtype=torch.f
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=dev)
     pd = perm.desc()
-    args = [ctypes.byref(experts), ctypes.byref(shared) if shared else None, _ptr(x),
+    args = [ctypes.byref(experts), ctypes.byref(shared) if shared is not None else None, _ptr(x),
             _DT[x.dtype], T, K, _ptr(topk_w), ctypes.byref(pd), _ptr(residual), _ptr(out),
             _DT[out.dtype], _ptr(ws), ws.numel(), _stream(dev)]
     if events is None:
@@ -246,6 +260,25 @@ def moe_w4a16_forward(experts, x, topk_w, perm, residual=None, out_dtype=torch.f
         arr = (ctypes.c_void_p * len(events))(*events)
         _check(lib().moe_w4a16_forward_profiled(*args, arr, len(events)),
                "moe_w4a16_forward_profiled")
+    return out
+
+
+def moe_round_activations(x, dtype=torch.bfloat16, out=None):
+    """float32 tensor -> `dtype` (float16 / bfloat16), round to nearest even."""
+    if out is None:
+        out = torch.empty(x.shape, dtype=dtype, device=x.device)
+    _check(lib().moe_round_activations(_ptr(x), x.numel(), _DT[out.dtype], _ptr(out),
+                                       _stream(x.device)), "moe_round_activations")
+    return out
+
+
+def moe_rmsnorm(x, weight=None, eps=1e-5, dtype=torch.bfloat16, out=None):
+    """float32 [T, H] -> x / sqrt(mean(x^2) + eps) * (1 + weight) in `dtype`."""
+    T, H = x.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=dtype, device=x.device)
+    _check(lib().moe_rmsnorm(_ptr(x), _ptr(weight), float(eps), T, H, _DT[out.dtype], _ptr(out),
+                             _stream(x.device)), "moe_rmsnorm")
     return out
 
 

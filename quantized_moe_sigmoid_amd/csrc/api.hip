@@ -25,6 +25,13 @@ moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int ac
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
                                  void *xperm, float *xsum, float *hsum, hipStream_t s,
                                  const std::function<moe_status_t(int)> &mark);
+moe_status_t launch_dense_swiglu(const moe_ffn_desc_t &sh, const void *x, int T, void *h,
+                                 float *y, float *part, hipStream_t s);
+moe_status_t launch_round(const float *in, size_t n, int dtype, void *out, hipStream_t s);
+moe_status_t launch_rmsnorm(const float *x, const float *w, float eps, int T, int H, int dtype,
+                            void *out, hipStream_t s);
+DenseSplit dense_plan(int T, int H, int F);
+bool dense_shape_ok(int H, int F);
 int gemv_tile_m();
 int gemm_tile_m();
 int gemm_group();
@@ -87,6 +94,29 @@ moe_status_t check_experts(const moe_ffn_desc_t *ex, int *E, int *H, int *F) {
 
 bool is_act(int d) { return d == MOE_F16 || d == MOE_BF16; }
 
+// The shared expert: one BF16 SwiGLU of any width Fs over the same H.
+moe_status_t check_dense(const moe_weight_desc_t &d, int n, int k) {
+    if (d.fmt != MOE_W_BF16 || d.num_experts != 1 || d.n != n || d.k != k || !d.qweight)
+        return MOE_ERR_INVALID_ARG;
+    if (n <= 0 || k <= 0 || n > kMaxDim || k > kMaxDim) return MOE_ERR_INVALID_ARG;
+    if (!aligned(d.qweight, 16) || d.qweight_row_stride % 16 || d.qweight_row_stride < 2 * k)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status_t check_shared(const moe_ffn_desc_t *sh, int H, int act, int *Fs) {
+    if (!sh) { *Fs = 0; return MOE_OK; }
+    const int f = sh->gate.n;
+    moe_status_t st;
+    if ((st = check_dense(sh->gate, f, H)) != MOE_OK) return st;
+    if ((st = check_dense(sh->up, f, H)) != MOE_OK) return st;
+    if ((st = check_dense(sh->down, H, f)) != MOE_OK) return st;
+    if (act != MOE_BF16) return MOE_ERR_INVALID_ARG;      // bf16 x bf16 MFMA
+    if (!dense_shape_ok(H, f)) return MOE_ERR_UNSUPPORTED;
+    *Fs = f;
+    return MOE_OK;
+}
+
 moe_status_t check_perm(const moe_perm_t *p) {
     if (!p || !p->counts || !p->expert_offsets || !p->padded_offsets || !p->sorted_slots ||
         !p->slot_to_row || !p->tile_expert || !p->num_tiles || !p->active_experts ||
@@ -100,7 +130,8 @@ struct FwdPlan {
     bool mfma;
     int tile_m;
     int64_t max_rows, max_tiles;
-    size_t off_h, off_y, off_xperm, off_xsum, off_hsum, total;
+    size_t off_h, off_y, off_xperm, off_xsum, off_hsum;
+    size_t off_sh_h, off_sh_y, off_sh_part, total;
 };
 
 // Kernel choice by batch shape: with few slots per expert the dequantizing
@@ -127,8 +158,7 @@ bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
            mfma_layout_ok(ex.gate) && mfma_layout_ok(ex.up) && mfma_layout_ok(ex.down);
 }
 
-FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F, int act) {
-    (void)act;
+FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F, int Fs) {
     FwdPlan p;
     p.mfma = use_mfma(ex, T, K);
     p.tile_m = p.mfma ? gemm_tile_m() : gemv_tile_m();
@@ -142,7 +172,12 @@ FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F
     p.off_xperm = p.off_y + align256((size_t)p.max_rows * H * 4);
     p.off_xsum = p.off_xperm + (sums ? align256((size_t)T * H * 2) : 0);
     p.off_hsum = p.off_xsum + (sums ? align256((size_t)T * (H / 128) * 4) : 0);
-    p.total = p.off_hsum + (sums ? align256((size_t)p.max_rows * (F / 128) * 4) : 0);
+    p.off_sh_h = p.off_hsum + (sums ? align256((size_t)p.max_rows * (F / 128) * 4) : 0);
+    // shared expert: h [T][Fs] bf16, y [T][H] float32, split partial sums
+    const size_t part = Fs ? dense_plan(T, H, Fs).part_floats : 0;
+    p.off_sh_y = p.off_sh_h + (Fs ? align256((size_t)T * Fs * 2) : 0);
+    p.off_sh_part = p.off_sh_y + (Fs ? align256((size_t)T * H * 4) : 0);
+    p.total = p.off_sh_part + align256(part * 4);
     return p;
 }
 
@@ -242,8 +277,9 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts, const moe_ffn_desc_
     if (st != MOE_OK) return st;
     if (T < 0 || K < 1 || K > E || !is_act(act_dtype) || !tile_m || !ws_bytes)
         return MOE_ERR_INVALID_ARG;
-    if (shared) return MOE_ERR_UNSUPPORTED;
-    const FwdPlan p = plan_forward(*experts, T, K, E, H, F, act_dtype);
+    int Fs;
+    if ((st = check_shared(shared, H, act_dtype, &Fs)) != MOE_OK) return st;
+    const FwdPlan p = plan_forward(*experts, T, K, E, H, F, Fs);
     *tile_m = p.tile_m;
     *ws_bytes = p.total;
     return MOE_OK;
@@ -261,14 +297,15 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     if (T < 0 || K < 1 || K > E || !is_act(act_dtype)) return MOE_ERR_INVALID_ARG;
     if (out_dtype != MOE_F32 && !is_act(out_dtype)) return MOE_ERR_INVALID_ARG;
     if ((st = check_perm(perm)) != MOE_OK) return st;
-    if (shared) return MOE_ERR_UNSUPPORTED;
+    int Fs;
+    if ((st = check_shared(shared, H, act_dtype, &Fs)) != MOE_OK) return st;
     if (events && n_events != MOE_FORWARD_STAGES + 1) return MOE_ERR_INVALID_ARG;
     if (T == 0) return MOE_OK;
     if (!x || !topk_w || !out || !ws) return MOE_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256) ||
         (residual && !aligned(residual, 16)))
         return MOE_ERR_INVALID_ARG;
-    const FwdPlan p = plan_forward(*experts, T, K, E, H, F, act_dtype);
+    const FwdPlan p = plan_forward(*experts, T, K, E, H, F, Fs);
     if (perm->tile_m != p.tile_m) return MOE_ERR_INVALID_ARG;
     if (ws_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!p.mfma && p.max_tiles > 65535) return MOE_ERR_UNSUPPORTED;
@@ -291,10 +328,16 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
                                       (float *)(w + p.off_hsum), s, mk)
                 : launch_gemv_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s, mk);
     if (st != MOE_OK) return st;
-    st = launch_combine(y, perm->slot_to_row, topk_w, T, K, H, nullptr, residual, out,
-                        out_dtype, s);
+    float *ysh = shared ? (float *)(w + p.off_sh_y) : nullptr;
+    if (shared) {
+        st = launch_dense_swiglu(*shared, x, T, w + p.off_sh_h, ysh, (float *)(w + p.off_sh_part),
+                                 s);
+        if (st != MOE_OK) return st;
+    }
+    if ((st = mark(3)) != MOE_OK) return st;
+    st = launch_combine(y, perm->slot_to_row, topk_w, T, K, H, ysh, residual, out, out_dtype, s);
     if (st != MOE_OK) return st;
-    return mark(3);
+    return mark(4);
 }
 
 moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts, const moe_ffn_desc_t *shared,
@@ -316,6 +359,24 @@ moe_status_t moe_w4a16_forward_profiled(const moe_ffn_desc_t *experts,
         if (!events[i]) return MOE_ERR_INVALID_ARG;
     return forward_impl(experts, shared, x, act_dtype, T, K, topk_w, perm, residual, out,
                         out_dtype, ws, ws_bytes, stream, events, n_events);
+}
+
+moe_status_t moe_round_activations(const float *in, int64_t n, int out_dtype, void *out,
+                                   void *stream) {
+    if (n < 0 || !is_act(out_dtype)) return MOE_ERR_INVALID_ARG;
+    if (n == 0) return MOE_OK;
+    if (!in || !out || !aligned(in, 16) || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+    return launch_round(in, (size_t)n, out_dtype, out, (hipStream_t)stream);
+}
+
+moe_status_t moe_rmsnorm(const float *x, const float *weight, float eps, int T, int H,
+                         int out_dtype, void *out, void *stream) {
+    if (T < 0 || H < 4 || H > kMaxDim || H % 4 || !is_act(out_dtype)) return MOE_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f) || eps > 1.0f) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !out || !aligned(x, 16) || !aligned(out, 16) || (weight && !aligned(weight, 16)))
+        return MOE_ERR_INVALID_ARG;
+    return launch_rmsnorm(x, weight, eps, T, H, out_dtype, out, (hipStream_t)stream);
 }
 
 moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out, void *stream) {

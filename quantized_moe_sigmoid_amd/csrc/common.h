@@ -51,6 +51,14 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + __expf(-g)) * u;
 }
 
+// ---- shared-expert (dense BF16) planning ---------------------------------
+// Input-range splits of the dense gate/up and down launches, and the float32
+// partial-sum buffer they need (0 when neither is split).
+struct DenseSplit {
+    int s_gateup, s_down;
+    size_t part_floats;
+};
+
 // ---- launch helpers --------------------------------------------------------
 #define MOE_LAUNCH_CHECK()                                   \
     do {                                                     \

@@ -25,7 +25,7 @@ would take minutes.
 """
 import numpy as np
 
-T_X, T_WR, T_LOGITS, T_ZIPF = 0, 1, 2, 3
+T_X, T_WR, T_LOGITS, T_ZIPF, T_NORM = 0, 1, 2, 3, 4
 T_GATE, T_UP, T_DOWN = 10, 11, 12
 T_SH_GATE, T_SH_UP, T_SH_DOWN = 20, 21, 22
 
@@ -80,6 +80,12 @@ def router_logits(T, E, root, layer=0):
 def zipf_bias(E, root, layer=0, s=1.1):
     rank = rng(root, layer, T_ZIPF).permutation(E) + 1
     return (-s * np.log(rank.astype(np.float64))).astype(np.float32)
+
+
+def norm_weight(H, root, layer=0, std=0.1):
+    """Zero-centred RMSNorm gain offsets w [H] float32, N(0, std^2): the
+    layer scales by (1 + w)."""
+    return normal((H,), std, root, layer, T_NORM)
 
 
 def expert_weight_bf16(n, k, root, layer, tensor, expert):

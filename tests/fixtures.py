@@ -6,6 +6,7 @@ import torch
 from oracle import formats as OF
 from oracle import layer as OL
 from oracle import quant as OQ
+from quantized_moe_sigmoid_amd import binding as B
 from quantized_moe_sigmoid_amd import synth
 
 TENSOR_OF = {"gate": synth.T_GATE, "up": synth.T_UP, "down": synth.T_DOWN}
@@ -74,3 +75,43 @@ def within_tolerance(gpu, ref, rel=1e-2):
 def oracle_layer(x16, ids, w, experts_fn, shared=None, residual=None):
     x = x16.float().cpu().numpy().astype(np.float64)
     return OL.moe_layer(x, ids, np.asarray(w, dtype=np.float64), experts_fn, shared, residual)
+
+
+def int4_ffn_random(E_, H_, F_, seed, dev):
+    """Random packed int4 gate/up/down banks on `dev` (see
+    synth.packed_int4_random); returns (ffn descriptor, device tensors)."""
+    banks, host = [], []
+    for i, (n, k) in enumerate(((F_, H_), (F_, H_), (H_, F_))):
+        qt, st = synth.packed_int4_random(E_, n, k, seed + i, dev)
+        banks.append(B.bank_int4(qt, st))
+        host.append((qt, st))
+    return B.ffn(*banks), host
+
+
+def experts_fn_int4(host):
+    """expert -> float64 (Wg, Wu, Wd) dequantized by the oracle, cached."""
+    cache = {}
+
+    def fn(e):
+        if e not in cache:
+            mats = []
+            for (q, s) in host:
+                if isinstance(q, torch.Tensor):
+                    qq = q[e].cpu().numpy()
+                    ss = s[e].view(torch.int16).cpu().numpy().view(np.uint16)
+                else:
+                    qq, ss = q[e], s[e]
+                mats.append(OQ.dequant_int4(qq, ss))
+            cache[e] = tuple(mats)
+        return cache[e]
+    return fn
+
+
+def shared_bf16(Fs, H, root, layer, dev):
+    """The BF16 shared expert: N(0, 0.02) weights rounded to bf16. Returns
+    (ffn descriptor on `dev`, float64 (Wg, Wu, Wd) for the oracle)."""
+    mats = (synth.expert_weight_bf16(Fs, H, root, layer, synth.T_SH_GATE, 0),
+            synth.expert_weight_bf16(Fs, H, root, layer, synth.T_SH_UP, 0),
+            synth.expert_weight_bf16(H, Fs, root, layer, synth.T_SH_DOWN, 0))
+    desc = B.ffn(*[B.bank_bf16(W.to(dev)) for W in mats])
+    return desc, tuple(W.float().numpy().astype(np.float64) for W in mats)

@@ -184,3 +184,65 @@ def test_dequant_validation(L):
     assert L.moe_dequant(ctypes.byref(b), -1, out, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_dequant(ctypes.byref(b), 0, None, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_dequant(ctypes.byref(b), 0, ctypes.c_void_p(FAKE + 4), None) == B.MOE_ERR_INVALID_ARG
+
+
+def _dense(n, k, row=None):
+    r = row if row is not None else 2 * k
+    return B.WeightDesc(B.MOE_W_BF16, 1, n, k, FAKE, None, None, r * n, r, 0, 0)
+
+
+def _shared(H=4096, Fs=1536):
+    return B.FfnDesc(_dense(Fs, H), _dense(Fs, H), _dense(H, Fs))
+
+
+def test_shared_expert_plan(L):
+    ex = _ffn()
+    st0, tm0, ws0 = _plan(ex, T=32, act=B.MOE_BF16)
+    st, tm, ws = _plan(ex, T=32, act=B.MOE_BF16, shared=ctypes.byref(_shared()))
+    assert st0 == st == B.MOE_OK and tm == tm0
+    # at least h [T][Fs] bf16 and y [T][H] float32 more
+    assert ws >= ws0 + 32 * 1536 * 2 + 32 * 4096 * 4
+
+
+@pytest.mark.parametrize("mutate,act,want", [
+    (lambda s: None, B.MOE_F16, B.MOE_ERR_INVALID_ARG),                # bf16 activations only
+    (lambda s: setattr(s.gate, "fmt", B.MOE_W_INT4_G128), B.MOE_BF16, B.MOE_ERR_INVALID_ARG),
+    (lambda s: setattr(s.up, "num_experts", 2), B.MOE_BF16, B.MOE_ERR_INVALID_ARG),
+    (lambda s: setattr(s.down, "k", 1024), B.MOE_BF16, B.MOE_ERR_INVALID_ARG),    # Fs mismatch
+    (lambda s: setattr(s.gate, "k", 2048), B.MOE_BF16, B.MOE_ERR_INVALID_ARG),    # H mismatch
+    (lambda s: setattr(s.gate, "qweight_row_stride", 8200), B.MOE_BF16, B.MOE_ERR_INVALID_ARG),
+    (lambda s: setattr(s.gate, "qweight_row_stride", 4096), B.MOE_BF16, B.MOE_ERR_INVALID_ARG),
+    (lambda s: setattr(s.down, "qweight", None), B.MOE_BF16, B.MOE_ERR_INVALID_ARG),
+])
+def test_shared_expert_rejects_bad_descriptors(L, mutate, act, want):
+    s = _shared()
+    mutate(s)
+    assert _plan(_ffn(), act=act, shared=ctypes.byref(s))[0] == want
+
+
+def test_shared_expert_unsupported_width(L):
+    s = _shared(Fs=1600)                      # not a multiple of the 128-column block
+    assert _plan(_ffn(), act=B.MOE_BF16, shared=ctypes.byref(s))[0] == B.MOE_ERR_UNSUPPORTED
+
+
+def test_round_activations_validation(L):
+    R = L.moe_round_activations
+    p = ctypes.c_void_p(FAKE)
+    assert R(p, 16, B.MOE_F32, p, None) == B.MOE_ERR_INVALID_ARG
+    assert R(p, -1, B.MOE_BF16, p, None) == B.MOE_ERR_INVALID_ARG
+    assert R(None, 16, B.MOE_BF16, p, None) == B.MOE_ERR_INVALID_ARG
+    assert R(ctypes.c_void_p(FAKE + 4), 16, B.MOE_BF16, p, None) == B.MOE_ERR_INVALID_ARG
+    assert R(None, 0, B.MOE_BF16, None, None) == B.MOE_OK
+
+
+def test_rmsnorm_validation(L):
+    N = L.moe_rmsnorm
+    p = ctypes.c_void_p(FAKE)
+    assert N(p, None, 1e-5, 4, 4096, B.MOE_F32, p, None) == B.MOE_ERR_INVALID_ARG   # dtype
+    assert N(p, None, 1e-5, 4, 4094, B.MOE_BF16, p, None) == B.MOE_ERR_INVALID_ARG  # H % 4
+    assert N(p, None, -1.0, 4, 4096, B.MOE_BF16, p, None) == B.MOE_ERR_INVALID_ARG  # eps
+    assert N(p, None, float("nan"), 4, 4096, B.MOE_BF16, p, None) == B.MOE_ERR_INVALID_ARG
+    assert N(p, ctypes.c_void_p(FAKE + 4), 1e-5, 4, 4096, B.MOE_BF16, p, None) == \
+        B.MOE_ERR_INVALID_ARG                                                      # alignment
+    assert N(None, None, 1e-5, 4, 4096, B.MOE_BF16, p, None) == B.MOE_ERR_INVALID_ARG
+    assert N(None, None, 1e-5, 0, 4096, B.MOE_BF16, None, None) == B.MOE_OK

@@ -186,31 +186,8 @@ def _int4_ffn_from_oracle(E_, H_, F_, root, dev):
     return B.ffn(*banks), host
 
 
-def _int4_ffn_random(E_, H_, F_, seed, dev):
-    banks, host = [], []
-    for i, (n, k) in enumerate(((F_, H_), (F_, H_), (H_, F_))):
-        qt, st = synth.packed_int4_random(E_, n, k, seed + i, dev)
-        banks.append(B.bank_int4(qt, st))
-        host.append((qt, st))
-    return B.ffn(*banks), host
-
-
-def _experts_fn_int4(host):
-    cache = {}
-
-    def fn(e):
-        if e not in cache:
-            mats = []
-            for (q, s) in host:
-                if isinstance(q, torch.Tensor):
-                    qq = q[e].cpu().numpy()
-                    ss = s[e].view(torch.int16).cpu().numpy().view(np.uint16)
-                else:
-                    qq, ss = q[e], s[e]
-                mats.append(OQ.dequant_int4(qq, ss))
-            cache[e] = tuple(mats)
-        return cache[e]
-    return fn
+_int4_ffn_random = FX.int4_ffn_random
+_experts_fn_int4 = FX.experts_fn_int4
 
 
 def _run_layer(dev, ffn, x, ids, w, Ee, residual=None, out_dtype=torch.float32):

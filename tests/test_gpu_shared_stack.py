@@ -1,0 +1,271 @@
+"""GPU parity of the shared expert, the float32 -> 16-bit rounding, the
+RMSNorm and the stack of eight MoE layers with an fp32 residual stream,
+against the oracle, through the C ABI.
+
+The stack (page "Step 5 Preview: ...", "The shape: narrow and deep": every
+MoE layer has 8 routed experts per token and one shared expert; the
+paragraph on training the deep stack: the residual stream is fp32 and
+Step5RMSNorm scales x / rms(x) by (1 + w)): r_0 = x; per layer l,
+a_l = bf16(rmsnorm_l(r_l)), route a_l with the layer's router weight and
+Zipf expert bias, r_{l+1} = fp32(r_l + MoE_l(a_l)). Without the norm the
+chain diverges: the SwiGLU is quadratic in its input, so the residual's rms
+roughly squares from layer to layer. Tokens never mix inside an MoE layer, so
+the oracle follows a few sampled tokens through all eight layers on its own;
+each GPU layer is then fed the oracle's r_l in those rows and checked against
+the oracle's r_{l+1} there (routing bit for bit, outputs within the
+tolerance). The GPU's own eight-layer chain is run too, and its drift from
+the oracle's is printed, not graded: rounding differences compound with
+depth and may flip near-tied routes.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as OF
+from oracle import layer as OL
+from oracle import norm as ON
+from oracle import router as OR
+from quantized_moe_sigmoid_amd import binding as B
+from quantized_moe_sigmoid_amd import synth
+from tests import fixtures as FX
+
+pytestmark = pytest.mark.gpu
+
+H, F, E, K = 4096, 1536, 352, 8
+LAYERS = 8
+STACK_ROOT = 5
+EPS = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    return torch.device("cuda:0")
+
+
+def _forward(dev, ffn, x, ids, w, Ee, shared=None, residual=None, out_dtype=torch.float32):
+    tm, _ = B.moe_forward_plan(ffn, x.shape[0], ids.shape[1], x.dtype, shared)
+    perm = B.moe_permute(ids, Ee, tm)
+    return B.moe_w4a16_forward(ffn, x, w, perm, residual=residual, out_dtype=out_dtype,
+                               shared=shared)
+
+
+# ------------------------------------------------------------ rounding ---
+@pytest.mark.parametrize("dtype,fmt", [(torch.bfloat16, OF.BF16), (torch.float16, OF.FP16)])
+def test_round_activations_bitwise(dev, dtype, fmt):
+    """moe_round_activations against the oracle's ties-to-even rounding on
+    Gaussian values of several magnitudes, exact ties, both signed zeros,
+    subnormals of the target and values past its largest finite number."""
+    g = synth.rng(9, 0, synth.T_X)
+    vals = [g.standard_normal(5000) * s for s in (1e-6, 1e-3, 1.0, 1e3, 6e4)]
+    fmt_ulp_bits = 16 if dtype == torch.bfloat16 else 13       # dropped fp32 mantissa bits
+    base = g.integers(0x3F800000, 0x40800000, size=2000, dtype=np.uint32)
+    half = np.uint32(1 << (fmt_ulp_bits - 1))
+    ties = ((base >> fmt_ulp_bits) << fmt_ulp_bits) | half      # exactly halfway
+    vals.append(ties.view(np.float32).astype(np.float64))
+    vals.append(np.array([0.0, -0.0, 1e-40, -3e-39, 6e-8, 3e-8, 65504.0, 65520.0, 7e4,
+                          3.3895e38, -3.39e38, 1e-45]))
+    vals.append(np.array([0.5, 1.5, 2.5]))                    # ragged tail: n % 4 == 3
+    x = np.concatenate(vals).astype(np.float32)
+    assert len(x) % 4 == 3
+    out = B.moe_round_activations(torch.from_numpy(x).to(dev), dtype)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = OF.round_to_format(x.astype(np.float64), fmt).astype(np.float32)
+    if dtype == torch.bfloat16:
+        want = (ref.view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        want = ref.astype(np.float16).view(np.uint16)            # exact: ref is an fp16 value
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+# ------------------------------------------------------------- rmsnorm ---
+@pytest.mark.parametrize("dtype,fmt", [(torch.bfloat16, OF.BF16), (torch.float16, OF.FP16)])
+@pytest.mark.parametrize("T,Hh", [(37, 4096), (5, 256), (3, 12)])
+def test_rmsnorm_bitwise(dev, dtype, fmt, T, Hh):
+    """moe_rmsnorm against the oracle's float64 RMSNorm rounded once: Gaussian
+    rows of several scales, a zero row (eps keeps it finite), and a row with
+    one large entry so that the others land in the fp16 subnormal range."""
+    g = synth.rng(10, 0, synth.T_X)
+    x = g.standard_normal((T, Hh)) * np.exp(g.uniform(-8, 8, size=(T, 1)))
+    x[1] = 0.0
+    x[2] = 1e-3 * g.standard_normal(Hh)
+    x[2, 0] = 1000.0
+    x = x.astype(np.float32)
+    w = synth.norm_weight(Hh, 10)
+    for wt in (None, w):
+        out = B.moe_rmsnorm(torch.from_numpy(x).to(dev),
+                            None if wt is None else torch.from_numpy(wt).to(dev), EPS, dtype)
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = OF.round_to_format(ON.rmsnorm(x, wt, EPS), fmt).astype(np.float32)
+        want = ((ref.view(np.uint32) >> 16).astype(np.uint16) if dtype == torch.bfloat16
+                else ref.astype(np.float16).view(np.uint16))
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, [(tuple(i), hex(got[tuple(i)]), hex(want[tuple(i)]))
+                               for i in bad[:5]]
+
+
+# ------------------------------------------------------- shared expert ---
+@pytest.mark.parametrize("T", [1, 8, 37, 100])
+def test_shared_expert_tiny(dev, T):
+    """Tiny layer (H=256, 16 experts, top-2, width 128) plus a shared expert
+    of width 128, bf16 activations, every token against the oracle."""
+    cfg = synth.CONFIGS["tiny"]
+    Hh, Ee, Kk, Ff = cfg["H"], cfg["E"], cfg["K"], cfg["F"]
+    ffn, host = FX.int4_ffn_random(Ee, Hh, Ff, 40 + T, dev)
+    sh, sh_host = FX.shared_bf16(128, Hh, 1, 0, dev)
+    x = synth.activations(T, Hh, "bf16", 1)
+    lg = synth.router_logits(T, Ee, 1)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    out = _forward(dev, ffn, x.to(dev), ids, w, Ee, shared=sh).cpu().numpy()
+    oids = OR.topk_ids(lg, Kk)
+    ref = FX.oracle_layer(x, oids, OR.routing_weights(lg, oids), FX.experts_fn_int4(host),
+                          shared=sh_host)
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
+@pytest.mark.parametrize("T", [1, 32, 77, 300, 2048])
+def test_shared_expert_full_width(dev, T):
+    """A shared expert of the real shape (4096 -> 1536 -> 4096, 37.7 MB of
+    bf16) beside 8 routed int4 experts (top-2), so that both the decode and
+    the prefill routed kernels and every input-range split of the dense
+    kernels run. All tokens up to T=77, then sampled tokens."""
+    Ee, Kk = 8, 2
+    ffn, host = FX.int4_ffn_random(Ee, H, F, 70 + T, dev)
+    sh, sh_host = FX.shared_bf16(F, H, 2, 0, dev)
+    x = synth.activations(T, H, "bf16", 6)
+    lg = synth.router_logits(T, Ee, 6)
+    r = synth.normal((T, H), 1.0, 6, 0, synth.T_LOGITS, 1)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    out = _forward(dev, ffn, x.to(dev), ids, w, Ee, shared=sh,
+                   residual=torch.from_numpy(r).to(dev)).cpu().numpy()
+    toks = list(range(T)) if T <= 77 else sorted({0, 1, T // 3, T // 2, T - 2, T - 1})
+    oids = OR.topk_ids(lg, Kk)
+    ow = OR.routing_weights(lg, oids)
+    ref = FX.oracle_layer(x[toks], oids[toks], ow[toks], FX.experts_fn_int4(host),
+                          shared=sh_host, residual=r[toks].astype(np.float64))
+    ok, ratio = FX.within_tolerance(out[toks], ref)
+    assert ok, ratio
+
+
+def test_shared_expert_bf16_output_and_zero_experts(dev):
+    """Residual-only and shared-only reductions: with every routed weight
+    zero the layer is residual + shared expert; bf16 output is the float32
+    result rounded once."""
+    Ee, Kk, T = 8, 2, 50
+    z = lambda n, k: torch.zeros((Ee, n, k // 8), dtype=torch.int32, device=dev)
+    s = lambda n, k: torch.zeros((Ee, n, k // 128), dtype=torch.bfloat16, device=dev)
+    ffn = B.ffn(B.bank_int4(z(F, H), s(F, H)), B.bank_int4(z(F, H), s(F, H)),
+                B.bank_int4(z(H, F), s(H, F)))
+    sh, sh_host = FX.shared_bf16(F, H, 3, 0, dev)
+    x = synth.activations(T, H, "bf16", 7)
+    lg = synth.router_logits(T, Ee, 7)
+    r = synth.normal((T, H), 1.0, 7, 0, synth.T_LOGITS, 1)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    rd = torch.from_numpy(r).to(dev)
+    o32 = _forward(dev, ffn, x.to(dev), ids, w, Ee, shared=sh, residual=rd)
+    o16 = _forward(dev, ffn, x.to(dev), ids, w, Ee, shared=sh, residual=rd,
+                   out_dtype=torch.bfloat16)
+    ref = OL.swiglu_ffn(x.float().numpy().astype(np.float64), *sh_host) + r
+    ok, ratio = FX.within_tolerance(o32.cpu().numpy(), ref)
+    assert ok, ratio
+    ok, ratio = FX.within_tolerance(o16.float().cpu().numpy(), ref)
+    assert ok, ratio
+    assert torch.equal(o16, o32.to(torch.bfloat16))            # one rounding of the same sum
+
+
+# ----------------------------------------------------------- the stack ---
+class _Layer:
+    def __init__(self, l, dev):
+        self.ffn, self.host = FX.int4_ffn_random(E, H, F, 5000 + 10 * l, dev)
+        self.sh, self.sh_host = FX.shared_bf16(F, H, STACK_ROOT, l, dev)
+        self.wT = synth.router_weight_T(H, E, STACK_ROOT, l)
+        self.bias = synth.zipf_bias(E, STACK_ROOT, l)
+        self.norm_w = synth.norm_weight(H, STACK_ROOT, l)
+        self.norm_w_d = torch.from_numpy(self.norm_w).to(dev)
+        self.wT_d = torch.from_numpy(self.wT).to(dev)
+        self.bias_d = torch.from_numpy(self.bias).to(dev)
+        self.experts = FX.experts_fn_int4(self.host)
+
+    def gpu(self, dev, r):
+        """One GPU layer on the float32 residual r [T, H] (device)."""
+        a = B.moe_rmsnorm(r, self.norm_w_d, EPS, torch.bfloat16)
+        ids, w = B.moe_route_topk(K, x=a, router_wT=self.wT_d, bias=self.bias_d)
+        out = _forward(dev, self.ffn, a, ids, w, E, shared=self.sh, residual=r)
+        return a, ids, w, out
+
+    def oracle(self, r):
+        """One oracle layer on float32 residual rows r [n, H] (numpy)."""
+        a = OF.round_to_format(ON.rmsnorm(r, self.norm_w, EPS), OF.BF16)
+        lg = OR.router_logits(a.astype(np.float32), self.wT, self.bias)
+        ids = OR.topk_ids(lg, K)
+        w = OR.routing_weights(lg, ids)
+        out = OL.moe_layer(a, ids, w, self.experts, self.sh_host, r.astype(np.float64))
+        return a, ids, w, out
+
+
+class _Stack:
+    """Weights of the eight layers, the oracle's chain over sampled tokens
+    (computed layer by layer on demand) and the GPU's own chain."""
+
+    def __init__(self, dev, T, toks):
+        self.dev, self.T, self.toks = dev, T, toks
+        self.layers = [_Layer(l, dev) for l in range(LAYERS)]
+        x = synth.activations(T, H, "bf16", STACK_ROOT)
+        self.r0 = x.float()                                     # fp32, exact
+        self.o_r = [self.r0.numpy()[toks].astype(np.float32)]   # oracle residual rows
+        self.o_out = []
+        self.o_route = []
+        r = self.r0.to(dev)
+        self.g_r = [r]
+        for L in self.layers:
+            r = L.gpu(dev, r)[3]
+            self.g_r.append(r)
+        torch.cuda.synchronize()
+
+    def oracle_upto(self, l):
+        while len(self.o_out) <= l:
+            j = len(self.o_out)
+            a, ids, w, out = self.layers[j].oracle(self.o_r[j])
+            self.o_out.append(out)
+            self.o_route.append((a, ids, w))
+            self.o_r.append(OF.round_to_format(out, OF.FP32).astype(np.float32))
+            self.layers[j].experts = FX.experts_fn_int4(self.layers[j].host)  # drop the cache
+
+
+_STACKS = {}
+
+
+def _stack(dev, T):
+    if T not in _STACKS:
+        _STACKS.clear()                                         # one weight set at a time
+        toks = [0, 13, 31] if T == 32 else [0, 2049, 4095]
+        _STACKS[T] = _Stack(dev, T, toks)
+    return _STACKS[T]
+
+
+@pytest.mark.parametrize("T,layer", [(T, l) for T in (32, 4096) for l in range(LAYERS)])
+def test_stack_layer(dev, T, layer):
+    st = _stack(dev, T)
+    st.oracle_upto(layer)
+    L, toks = st.layers[layer], st.toks
+    # the GPU layer on its own chain's residual with the oracle's rows spliced in
+    r = st.g_r[layer].clone()
+    r[toks] = torch.from_numpy(st.o_r[layer]).to(dev)
+    a, ids, w, out = L.gpu(dev, r)
+    oa, oids, ow = st.o_route[layer]
+    a16 = a.view(torch.int16).cpu().numpy().view(np.uint16)[toks]
+    assert np.array_equal(a16, OF.bf16_bits(oa))
+    assert np.array_equal(ids.cpu().numpy()[toks], oids)
+    assert np.allclose(w.cpu().numpy()[toks], ow, rtol=1e-5, atol=1e-7)
+    ok, ratio = FX.within_tolerance(out.cpu().numpy()[toks], st.o_out[layer])
+    assert ok, ratio
+    if layer == LAYERS - 1:
+        g = st.g_r[LAYERS].cpu().numpy()[toks].astype(np.float64)
+        o = st.o_r[LAYERS].astype(np.float64)
+        rms = np.sqrt(np.mean(o * o))
+        print("stack T=%d: GPU chain vs oracle chain after %d layers: max |diff| / rms = %.3e"
+              % (T, LAYERS, np.max(np.abs(g - o)) / rms))
