@@ -303,6 +303,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain streaming kernel over MIB MiB (read once, written "
+                         "once), the reference for scaling hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer has no multi-GPU path in this build "
@@ -311,6 +314,15 @@ def main():
     dev = torch.device("cuda:0")
     hip = Hip()
     B.lib()
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)                    # reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     int4 = int4_banks(2, dev, 500)
     jobs = []
