@@ -308,7 +308,7 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     const FwdPlan p = plan_forward(*experts, T, K, E, H, F, Fs);
     if (perm->tile_m != p.tile_m) return MOE_ERR_INVALID_ARG;
     if (ws_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    if (!p.mfma && p.max_tiles > 65535) return MOE_ERR_UNSUPPORTED;
+    if (!p.mfma && p.max_tiles > 65535) return MOE_ERR_UNSUPPORTED;     // grid.y
     if (p.mfma && p.max_tiles * ((H > F ? H : F) / 128 + 1) > (int64_t)1 << 30)
         return MOE_ERR_UNSUPPORTED;
 

@@ -60,6 +60,16 @@ __device__ __forceinline__ void int4_biased_pairs_masked(uint32_t w, uint32_t m,
     out[3] = ((w >> 12) & m) ^ K;
 }
 
+// A value the compiler cannot see through, held in a VGPR. gfx950 VOP3
+// instructions take no literal and at most one scalar operand, so a
+// three-operand bit operation with two constant operands only issues as one
+// instruction when one constant already sits in a vector register.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
+    return r;
+}
+
 // ---- NVFP4 ------------------------------------------------------------------
 // E4M3FN byte -> float32 (exact): exponent bias 7, subnormals m * 2^-9.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {

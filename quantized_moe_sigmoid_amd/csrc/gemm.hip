@@ -29,6 +29,7 @@
 #include <functional>
 
 #include "decode.h"
+#include "stream.h"
 
 namespace moe {
 
@@ -37,8 +38,6 @@ constexpr int kGemmTM = 64;          // rows per tile
 constexpr int kGemmBN = 128;         // output columns per block
 constexpr int kGemmKS = 256;         // inputs per pipeline step (two int4 groups)
 constexpr int kGemmRowBytes = kGemmKS * 2;
-constexpr int kGemmChunks = kGemmKS / 8;                    // 16-byte chunks per row
-constexpr int kGemmStage = kGemmTM * kGemmChunks / kGemmThreads;   // chunks per thread
 
 struct GemmMat {
     const uint8_t *q, *s;
@@ -96,14 +95,6 @@ __device__ __forceinline__ int xcd_remap(int b, int nwg) {
     return xcd * q + min(xcd, r) + b / 8;
 }
 
-// Buffer resource over one expert's matrix: 32-bit offsets, and any offset
-// past `bytes` reads zero instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0,
-                                             (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
-                                             0x00020000);
-}
-
 // Weights of one pipeline step for one lane: four 16-byte loads per matrix
 // (inputs 64i + 32h .. +31 of the step) and the step's scales.
 template <int FMT>
@@ -149,8 +140,6 @@ __device__ __forceinline__ int a_offset(int row, int chunk) {
 // of a row read 64 contiguous bytes per group and a wave writes 1 KB of LDS
 // contiguously. Thread t < 64 also carries row t's two (-BIAS * group sum)
 // values (int4).
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
 template <int FMT>
 struct Stager {
     u32x4_t v[8];      // a native vector type: HIP's uint4 struct copies become
@@ -178,14 +167,6 @@ struct Stager {
         }
     }
 };
-
-// Workgroup barrier that orders LDS only: outstanding global loads (the
-// next step's weights) stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int ACT, int FMT, bool GATEUP>
 struct GemmCtx {
@@ -319,10 +300,10 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
     const int col_a = nb * BN + wave * (GATEUP ? 32 : 64) + cx.l32;
     const int col_b = GATEUP ? col_a : col_a + 32;
     const bool ok_a = col_a < n_rows, ok_b = col_b < n_rows;
-    const __amdgpu_buffer_rsrc_t rqa = make_rsrc(A.q + e * A.qe, (int64_t)n_rows * A.qr);
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(A.s + e * A.se, (int64_t)n_rows * A.sr);
-    const __amdgpu_buffer_rsrc_t rqb = make_rsrc(Bm.q + e * Bm.qe, (int64_t)n_rows * Bm.qr);
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(Bm.s + e * Bm.se, (int64_t)n_rows * Bm.sr);
+    const __amdgpu_buffer_rsrc_t rqa = buffer_rsrc(A.q + e * A.qe, (int64_t)n_rows * A.qr);
+    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(A.s + e * A.se, (int64_t)n_rows * A.sr);
+    const __amdgpu_buffer_rsrc_t rqb = buffer_rsrc(Bm.q + e * Bm.qe, (int64_t)n_rows * Bm.qr);
+    const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(Bm.s + e * Bm.se, (int64_t)n_rows * Bm.sr);
     const int qoff_a = (ok_a ? col_a : 0) * (int)A.qr, soff_a = (ok_a ? col_a : 0) * (int)A.sr;
     const int qoff_b = (ok_b ? col_b : 0) * (int)Bm.qr, soff_b = (ok_b ? col_b : 0) * (int)Bm.sr;
 

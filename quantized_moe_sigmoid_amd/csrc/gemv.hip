@@ -22,6 +22,7 @@
 #include <functional>
 
 #include "decode.h"
+#include "stream.h"
 
 namespace moe {
 
@@ -47,50 +48,6 @@ __host__ __device__ __forceinline__ int xs_units_pad(int kin) {
     return (kin / 32 + LPR - 1) / LPR * LPR * 4;
 }
 
-// Stage the m activation rows of the tile into LDS as 16-bit pairs in the
-// order the decoders produce weights, plus (int4) per-chunk sums of x.
-template <int FMT, int LPR, int TM>
-__device__ __forceinline__ void stage_x(const uint16_t *const *rows, int m, int kin,
-                                        uint4 *xs, float *xsum, bool f16) {
-    const int units = kin / 8;                   // 8 inputs per unit
-    const int upad = xs_units_pad<LPR>(kin);
-    for (int idx = threadIdx.x; idx < TM * units; idx += kGemvThreads) {
-        const int t = idx / units, g8 = idx - t * units;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < m) v = *(const uint4 *)(rows[t] + 8 * g8);
-        uint4 p;
-        if (FMT == MOE_W_INT4_G128) {            // pairs (i, i+4) of the 8 inputs
-            p.x = (v.x & 0xFFFFu) | (v.z << 16);
-            p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
-            p.z = (v.y & 0xFFFFu) | (v.w << 16);
-            p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-        } else {                                 // pairs (2i, 2i+1): natural order
-            p = v;
-        }
-        xs[t * upad + xs_unit<LPR>(g8 >> 2, g8 & 3)] = p;
-    }
-    if (FMT == MOE_W_INT4_G128) {
-        __syncthreads();
-        const int nch = kin / 32;
-        for (int idx = threadIdx.x; idx < TM * nch; idx += kGemvThreads) {
-            const int t = idx / nch, c = idx - t * nch;
-            float s = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint4 p = xs[t * upad + xs_unit<LPR>(c, j)];
-                const uint32_t d[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    s += f16 ? f16_bits_to_f32(d[i] & 0xFFFF) : bf16_bits_to_f32(d[i] & 0xFFFF);
-                    s += f16 ? f16_bits_to_f32(d[i] >> 16) : bf16_bits_to_f32(d[i] >> 16);
-                }
-            }
-            xsum[t * nch + c] = s;
-        }
-    }
-    __syncthreads();
-}
-
 // Partial dot products of one 16-byte weight chunk against token t's x.
 template <int ACT, int FMT>
 struct ChunkDot;
@@ -98,11 +55,17 @@ struct ChunkDot;
 template <int ACT>
 struct ChunkDot<ACT, MOE_W_INT4_G128> {
     uint32_t p[16];
-    __device__ __forceinline__ void decode(uint4 w) {
-        int4_biased_pairs<ACT>(w.x, p + 0);
-        int4_biased_pairs<ACT>(w.y, p + 4);
-        int4_biased_pairs<ACT>(w.z, p + 8);
-        int4_biased_pairs<ACT>(w.w, p + 12);
+    // kv = Int4Bias<ACT>::kMagic | 0x00080008 in a VGPR: each pair is then
+    // one shift and one v_bitop3 ((w >> 4i) & 0x000F000F) ^ kv
+    __device__ __forceinline__ void decode(uint4 w, uint32_t kv) {
+        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            p[4 * q + 0] = (d[q] & 0x000F000Fu) ^ kv;
+            p[4 * q + 1] = ((d[q] >> 4) & 0x000F000Fu) ^ kv;
+            p[4 * q + 2] = ((d[q] >> 8) & 0x000F000Fu) ^ kv;
+            p[4 * q + 3] = ((d[q] >> 12) & 0x000F000Fu) ^ kv;
+        }
     }
     // s2 = the chunk's scale(s): int4 uses one bf16 scale (as float).
     __device__ __forceinline__ float apply(const uint4 *xu, int stride_j, float xs_sum,
@@ -123,7 +86,7 @@ struct ChunkDot<ACT, MOE_W_INT4_G128> {
 template <int ACT>
 struct ChunkDot<ACT, MOE_W_NVFP4_G16> {
     uint32_t p[16];
-    __device__ __forceinline__ void decode(uint4 w) {
+    __device__ __forceinline__ void decode(uint4 w, uint32_t) {
         const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -149,23 +112,44 @@ struct ChunkDot<ACT, MOE_W_NVFP4_G16> {
     }
 };
 
+// The two scale bytes of chunk c (32 inputs) of a row: int4, the bf16
+// scale of its 128-input group (one per 4 chunks); NVFP4, its two E4M3
+// block scales.
 template <int FMT>
-__device__ __forceinline__ void chunk_scales(const uint8_t *srow, int c, float &a, float &b) {
+__device__ __forceinline__ void chunk_scales(uint32_t two, float &a, float &b) {
     if (FMT == MOE_W_INT4_G128) {
-        a = bf16_bits_to_f32(*(const uint16_t *)(srow + 2 * (c >> 2)));
+        a = bf16_bits_to_f32(two);
         b = 0.0f;
     } else {
-        const uint16_t two = *(const uint16_t *)(srow + 2 * c);
         a = e4m3_to_f32(two & 0xFF);
         b = e4m3_to_f32(two >> 8);
     }
 }
+template <int FMT>
+__device__ __forceinline__ int scale_offset(int c) {
+    return FMT == MOE_W_INT4_G128 ? 2 * (c >> 2) : 2 * c;
+}
+
+
+// Chunks in flight per lane and matrix.
+constexpr int kGemvRing = 4;
+// Activation loads per thread issued together while staging.
+constexpr int kGemvStage = 8;
 
 // GATEUP: mats a = gate, b = up, output h (16-bit). Otherwise a = down,
 // output y (float32).
-template <int ACT, int FMT, int LPR, int TM, bool GATEUP>
+//
+// Per work group: the tile's slots, then up to kGemvStage 16-byte loads of
+// activations per thread, then the first kGemvRing weight chunks of every
+// lane (issued before the activations are needed, so the staging latency
+// overlaps the weight stream), then the activations are written to LDS in
+// the decoders' pair order together with (int4) each 32-input chunk's sum,
+// reduced across the four lanes that hold its four 8-input units. The main
+// loop consumes ring slot j and immediately refills it with the chunk
+// kGemvRing iterations ahead.
+template <int ACT, int FMT, int LPR, int TM, bool GATEUP, int NIT, int RPW>
 __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
-    GemvMat A, GemvMat B, int n_rows, int kin, const uint16_t *__restrict__ xin,
+    GemvMat A, GemvMat B, int n_rows, int kin, const uint16_t *xin,
     int x_from_slots, int topk, const int32_t *__restrict__ sorted_slots,
     const int32_t *__restrict__ tile_expert, const int32_t *__restrict__ num_tiles,
     uint16_t *__restrict__ hout, float *__restrict__ yout) {
@@ -174,84 +158,201 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
     if (tile >= num_tiles[0]) return;
     const int e = tile_expert[tile];
 
-    __shared__ const uint16_t *rows[TM];
-    __shared__ int m_sh;
-    if (threadIdx.x == 0) {
-        int m = 0;
-        for (int t = 0; t < TM; ++t) {
-            const int s = sorted_slots[tile * TM + t];
-            if (s >= 0) m = t + 1;
-            rows[t] = x_from_slots ? xin + (size_t)(s >= 0 ? s / topk : 0) * kin
-                                   : xin + (size_t)(tile * TM + t) * kin;
-        }
-        m_sh = m;
-    }
-    __syncthreads();
-    const int m = m_sh;
-    uint4 *xs = smem;
-    float *xsum = (float *)(smem + TM * xs_units_pad<LPR>(kin));
-    stage_x<FMT, LPR, TM>(rows, m, kin, xs, xsum, ACT == MOE_F16);
-
+    static_assert(TM == kGemvWaves, "wave w stages the activation row of slot w");
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    // the tile's number of real rows (slots are -1 past them)
+    int m = 0;
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+        if (sorted_slots[tile * TM + t] >= 0) m = t + 1;
+
+    // activation staging, first batch: loads only. Wave w stages the row of
+    // the tile's slot w (a padding slot reads token 0; it is never used).
+    const int units = kin / 8;                   // 8 inputs per unit
+    const uint16_t *xrow;
+    {
+        const int sl = sorted_slots[tile * TM + wave];
+        xrow = x_from_slots ? xin + (size_t)(sl >= 0 ? sl / topk : 0) * kin
+                            : xin + (size_t)(tile * TM + wave) * kin;
+    }
+    u32x4_t xv[kGemvStage];
+#pragma unroll
+    for (int i = 0; i < kGemvStage; ++i) {
+        const int g = lane + i * kWave;
+        xv[i] = *(const u32x4_t *)(xrow + 8 * (g < units ? g : 0));  // past the end: unused
+    }
+
+    // weight ring: chunk c = sub + LPR * i of the lane's row
+    // RPW passes of 32 rows per work group (a wave owns LPR-lane groups of
+    // 8 rows per pass); the staged activations serve every pass
+    static_assert(NIT > 0 || RPW == 1, "row passes need the unrolled kernel");
     const int sub = lane % LPR;
-    const int row = (blockIdx.x * kGemvWaves + wave) * (kWave / LPR) + lane / LPR;
-    const bool live = row < n_rows;
-    const uint8_t *qa = A.q + e * A.qe + (int64_t)row * A.qr;
-    const uint8_t *sa = A.s + e * A.se + (int64_t)row * A.sr;
-    const uint8_t *qb = GATEUP ? B.q + e * B.qe + (int64_t)row * B.qr : nullptr;
-    const uint8_t *sb = GATEUP ? B.s + e * B.se + (int64_t)row * B.sr : nullptr;
+    auto row_of = [&](int pass) {
+        return ((blockIdx.x * RPW + pass) * kGemvWaves + wave) * (kWave / LPR) + lane / LPR;
+    };
+    // chunks per row and iterations per lane and pass: NIT when the shape is
+    // known at compile time (kin == 32 * LPR * NIT; the main loop then
+    // unrolls completely and every load offset is a constant), else computed
+    const int nch = NIT > 0 ? NIT * LPR : kin / 32;
+    const int nit = NIT > 0 ? NIT : (nch + LPR - 1) / LPR;
+    const __amdgpu_buffer_rsrc_t rqa = buffer_rsrc(A.q + e * A.qe, (int64_t)n_rows * A.qr);
+    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(A.s + e * A.se, (int64_t)n_rows * A.sr);
+    const __amdgpu_buffer_rsrc_t rqb = buffer_rsrc(B.q + e * B.qe, (int64_t)n_rows * B.qr);
+    const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(B.s + e * B.se, (int64_t)n_rows * B.sr);
+    // per pass: byte offsets of the lane's row (rows past the matrix, never
+    // stored, read its last row)
+    int qra[RPW], sra[RPW], qrb[RPW], srb[RPW];
+#pragma unroll
+    for (int ps = 0; ps < RPW; ++ps) {
+        const int r = row_of(ps) < n_rows ? row_of(ps) : n_rows - 1;
+        qra[ps] = r * (int)A.qr;
+        sra[ps] = r * (int)A.sr;
+        qrb[ps] = r * (int)B.qr;
+        srb[ps] = r * (int)B.sr;
+    }
+    const uint32_t kv = in_vgpr(FMT == MOE_W_INT4_G128 ? (Int4Bias<ACT>::kMagic | 0x00080008u) : 0u);
+    u32x4_t wa[kGemvRing], wb[kGemvRing];
+    uint16_t sa[kGemvRing], sb[kGemvRing];
+    // iteration I = pass * nit + i streams chunk c = sub + LPR * i of the pass's row
+    auto load = [&](int j, int I) {
+        const int ps = NIT > 0 ? I / NIT : 0, i = NIT > 0 ? I % NIT : I;
+        const int c = sub + LPR * i;
+        const bool ok = NIT > 0 ? ps < RPW : c < nch;   // past the work: read nothing
+        const int pq = ok ? ps : 0;
+        wa[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rqa, ok ? qra[pq] + 16 * c : kOutOfRange, 0, 0));
+        sa[j] = __builtin_amdgcn_raw_buffer_load_b16(
+            rsa, ok ? sra[pq] + scale_offset<FMT>(c) : kOutOfRange, 0, 0);
+        if (GATEUP) {
+            wb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rqb, ok ? qrb[pq] + 16 * c : kOutOfRange, 0, 0));
+            sb[j] = __builtin_amdgcn_raw_buffer_load_b16(
+                rsb, ok ? srb[pq] + scale_offset<FMT>(c) : kOutOfRange, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < kGemvRing; ++j) load(j, j);
+    // keep every load above in flight before the staging arithmetic starts
+    __builtin_amdgcn_sched_barrier(0);
+
+    // activations into LDS (pair order of the decoders) and chunk sums
+    uint4 *xs = smem;
+    const int upad = xs_units_pad<LPR>(kin);
+    float *xsum = (float *)(smem + TM * upad);
+    // lanes past the end of the row write to a dummy area instead of
+    // branching (a branch would let the compiler sink the staging loads
+    // below the weight loads and wait for those too)
+    uint4 *xdummy = xs + TM * upad + (TM * nch + 3) / 4;
+    float *sdummy = (float *)(xdummy + kWave);
+    auto stage = [&](const u32x4_t &v, int g) {
+        const bool valid = g < units;            // the 4 lanes of a chunk agree (units % 4 == 0)
+        uint4 p;
+        if (FMT == MOE_W_INT4_G128) {            // pairs (i, i+4) of the 8 inputs
+            p.x = (v.x & 0xFFFFu) | (v.z << 16);
+            p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+            p.z = (v.y & 0xFFFFu) | (v.w << 16);
+            p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+        } else {                                 // pairs (2i, 2i+1): natural order
+            p = make_uint4(v.x, v.y, v.z, v.w);
+        }
+        *(valid ? xs + wave * upad + xs_unit<LPR>(g >> 2, g & 3) : xdummy + lane) = p;
+        if (FMT == MOE_W_INT4_G128) {
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+            float sum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sum += act_to_f32<ACT>(d[q] & 0xFFFF) + act_to_f32<ACT>(d[q] >> 16);
+            // the 4 units of a chunk sit in 4 consecutive lanes
+            sum += shfl_xor_f(sum, 1);
+            sum += shfl_xor_f(sum, 2);
+            *(valid && (g & 3) == 0 ? xsum + wave * nch + (g >> 2) : sdummy + lane) = sum;
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < kGemvStage; ++i) stage(xv[i], lane + i * kWave);
+    for (int g0 = kGemvStage * kWave; g0 < units; g0 += kWave) {   // rows over 4096 inputs
+        const int g = g0 + lane;
+        stage(*(const u32x4_t *)(xrow + 8 * (g < units ? g : 0)), g);
+    }
+    lds_barrier();
 
     float acc_a[TM], acc_b[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc_a[t] = acc_b[t] = 0.0f;
-
-    const int nch = kin / 32;
-    const int units = xs_units_pad<LPR>(kin);
-    for (int c0 = 0; c0 < nch; c0 += LPR) {
-        const int c = c0 + sub;
-        if (!live || c >= nch) continue;
-        ChunkDot<ACT, FMT> da, db;
-        da.decode(*(const uint4 *)(qa + 16 * (int64_t)c));
-        float a0, a1, b0 = 0.0f, b1 = 0.0f;
-        chunk_scales<FMT>(sa, c, a0, a1);
-        if (GATEUP) {
-            db.decode(*(const uint4 *)(qb + 16 * (int64_t)c));
-            chunk_scales<FMT>(sb, c, b0, b1);
-        }
-        const int u0 = xs_unit<LPR>(c, 0);
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            if (t < m) {
-                const uint4 *xu = xs + t * units + u0;
-                const float xsm = FMT == MOE_W_INT4_G128 ? xsum[t * nch + c] : 0.0f;
-                acc_a[t] = da.apply(xu, LPR, xsm, a0, a1, acc_a[t]);
-                if (GATEUP) acc_b[t] = db.apply(xu, LPR, xsm, b0, b1, acc_b[t]);
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-#pragma unroll
-        for (int msk = LPR / 2; msk >= 1; msk >>= 1) {
-            acc_a[t] += shfl_xor_f(acc_a[t], msk);
-            if (GATEUP) acc_b[t] += shfl_xor_f(acc_b[t], msk);
-        }
-    }
-    if (!live || sub != 0) return;
     float ga = 1.0f, gb = 1.0f;
     if (FMT == MOE_W_NVFP4_G16) {
         ga = A.gs[e];
         if (GATEUP) gb = B.gs[e];
     }
+    // end of a pass: reduce the LPR partial sums of each row, store, reset
+    auto finish = [&](int ps) {
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-        if (t < m) {
-            const size_t r = (size_t)tile * TM + t;
-            if (GATEUP)
-                hout[r * n_rows + row] = f32_to_act<ACT>(silu_mul(acc_a[t] * ga, acc_b[t] * gb));
-            else
-                yout[r * n_rows + row] = acc_a[t] * ga;
+        for (int t = 0; t < TM; ++t) {
+#pragma unroll
+            for (int msk = LPR / 2; msk >= 1; msk >>= 1) {
+                acc_a[t] += shfl_xor_f(acc_a[t], msk);
+                if (GATEUP) acc_b[t] += shfl_xor_f(acc_b[t], msk);
+            }
         }
+        const int row = row_of(ps);
+        if (row < n_rows && sub == 0) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                if (t < m) {
+                    const size_t r = (size_t)tile * TM + t;
+                    if (GATEUP)
+                        hout[r * n_rows + row] =
+                            f32_to_act<ACT>(silu_mul(acc_a[t] * ga, acc_b[t] * gb));
+                    else
+                        yout[r * n_rows + row] = acc_a[t] * ga;
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t) acc_a[t] = acc_b[t] = 0.0f;
+    };
+    const int total_it = RPW * nit;
+    // every trip runs all kGemvRing slots (slots past the last iteration hold
+    // zeros and are not computed)
+    auto trip = [&](int I0) {
+#pragma unroll
+        for (int j = 0; j < kGemvRing; ++j) {
+            const int I = I0 + j;
+            const int i = NIT > 0 ? I % NIT : I;
+            const int c = sub + LPR * i;
+            ChunkDot<ACT, FMT> da, db;
+            da.decode(make_uint4(wa[j].x, wa[j].y, wa[j].z, wa[j].w), kv);
+            float a0, a1, b0 = 0.0f, b1 = 0.0f;
+            chunk_scales<FMT>(sa[j], a0, a1);
+            if (GATEUP) {
+                db.decode(make_uint4(wb[j].x, wb[j].y, wb[j].z, wb[j].w), kv);
+                chunk_scales<FMT>(sb[j], b0, b1);
+            }
+            // slot j is consumed: refill it in place (the barrier keeps the
+            // refill below the last use, so it reuses the same registers)
+            __builtin_amdgcn_sched_barrier(0);
+            load(j, I + kGemvRing);
+            if (I < total_it && c < nch) {
+                const int u0 = xs_unit<LPR>(c, 0);
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    if (t < m) {
+                        const uint4 *xu = xs + t * upad + u0;
+                        const float xsm = FMT == MOE_W_INT4_G128 ? xsum[t * nch + c] : 0.0f;
+                        acc_a[t] = da.apply(xu, LPR, xsm, a0, a1, acc_a[t]);
+                        if (GATEUP) acc_b[t] = db.apply(xu, LPR, xsm, b0, b1, acc_b[t]);
+                    }
+                }
+            }
+            if (NIT > 0 && I < total_it && i == NIT - 1) finish(I / NIT);
+        }
+    };
+    if constexpr (NIT > 0) {
+#pragma unroll
+        for (int I0 = 0; I0 < RPW * NIT; I0 += kGemvRing) trip(I0);
+    } else {
+        for (int I0 = 0; I0 < nit; I0 += kGemvRing) trip(I0);
+        finish(0);
     }
 }
 
@@ -264,9 +365,12 @@ inline GemvMat gemv_mat(const moe_weight_desc_t &d) {
                    d.scale_row_stride};
 }
 
+// Activation units, chunk sums (rounded up to 16 bytes) and the staging
+// dummy area (64 units + 64 floats).
 template <int LPR, int TM>
 inline size_t gemv_lds_bytes(int kin) {
-    return (size_t)TM * xs_units_pad<LPR>(kin) * 16 + (size_t)TM * (kin / 32) * 4;
+    return (size_t)TM * xs_units_pad<LPR>(kin) * 16 + ((size_t)TM * (kin / 32) + 3) / 4 * 16 +
+           (size_t)kWave * 16 + (size_t)kWave * 4;
 }
 
 template <typename Kern>
@@ -283,23 +387,35 @@ moe_status_t gemv_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
     constexpr int LPR = kGemvLPR, TM = kGemvTM;
     const int F = ex.gate.n, H = ex.gate.k;
     const int rows_per_block = kGemvWaves * (kWave / LPR);
+    // the layer's own shapes get fully unrolled kernels: 4096 inputs -> 16
+    // iterations per lane, 1536 -> 6; other shapes run the generic loop
     {
         const size_t lds = gemv_lds_bytes<LPR, TM>(H);
-        dim3 grid((F + rows_per_block - 1) / rows_per_block, max_tiles);
-        allow_lds(gemv_kernel<ACT, FMT, LPR, TM, true>, lds);
-        hipLaunchKernelGGL((gemv_kernel<ACT, FMT, LPR, TM, true>), grid, dim3(kGemvThreads), lds, s,
-                           gemv_mat(ex.gate), gemv_mat(ex.up), F, H, x, 1, K, p.sorted_slots,
-                           p.tile_expert, p.num_tiles, h, nullptr);
+        constexpr int RP = 1;                   // row passes per work group (more cost VGPRs)
+        const bool fast = H == 32 * LPR * 16 && F % (RP * rows_per_block) == 0;
+        auto k = fast ? gemv_kernel<ACT, FMT, LPR, TM, true, 16, RP>
+                      : gemv_kernel<ACT, FMT, LPR, TM, true, 0, 1>;
+        dim3 grid(fast ? F / (RP * rows_per_block) : (F + rows_per_block - 1) / rows_per_block,
+                  max_tiles);
+        allow_lds(k, lds);
+        hipLaunchKernelGGL(k, grid, dim3(kGemvThreads), lds, s, gemv_mat(ex.gate),
+                           gemv_mat(ex.up), F, H, x, 1, K, p.sorted_slots, p.tile_expert,
+                           p.num_tiles, h, nullptr);
         MOE_LAUNCH_CHECK();
     }
     if (mark && mark(1) != MOE_OK) return MOE_ERR_HIP;
     {
         const size_t lds = gemv_lds_bytes<LPR, TM>(F);
-        dim3 grid((H + rows_per_block - 1) / rows_per_block, max_tiles);
-        allow_lds(gemv_kernel<ACT, FMT, LPR, TM, false>, lds);
-        hipLaunchKernelGGL((gemv_kernel<ACT, FMT, LPR, TM, false>), grid, dim3(kGemvThreads), lds,
-                           s, gemv_mat(ex.down), gemv_mat(ex.down), H, F, h, 0, K,
-                           p.sorted_slots, p.tile_expert, p.num_tiles, nullptr, y);
+        constexpr int RP = 4;
+        const bool fast = F == 32 * LPR * 6 && H % (RP * rows_per_block) == 0;
+        auto k = fast ? gemv_kernel<ACT, FMT, LPR, TM, false, 6, RP>
+                      : gemv_kernel<ACT, FMT, LPR, TM, false, 0, 1>;
+        dim3 grid(fast ? H / (RP * rows_per_block) : (H + rows_per_block - 1) / rows_per_block,
+                  max_tiles);
+        allow_lds(k, lds);
+        hipLaunchKernelGGL(k, grid, dim3(kGemvThreads), lds, s, gemv_mat(ex.down),
+                           gemv_mat(ex.down), H, F, h, 0, K, p.sorted_slots, p.tile_expert,
+                           p.num_tiles, nullptr, y);
         MOE_LAUNCH_CHECK();
     }
     if (mark && mark(2) != MOE_OK) return MOE_ERR_HIP;

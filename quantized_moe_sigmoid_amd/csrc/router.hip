@@ -20,7 +20,6 @@
 namespace moe {
 
 constexpr int kMaxE = 512;
-constexpr int kMaxK = 16;
 
 __device__ __forceinline__ uint64_t topk_key(float f, int e) {
     uint32_t u = __float_as_uint(f + 0.0f);          // -0 -> +0
