@@ -87,12 +87,15 @@ __device__ __forceinline__ uint4 decode_b(uint32_t w, float bs, uint32_t qmask) 
     }
 }
 
-__device__ __forceinline__ int xcd_remap(int b, int nwg) {
+__device__ __forceinline__ int xcd_remap(int b, int nreal) {
     // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
     // contiguous range of logical blocks so blocks sharing a tile (and its
-    // activation rows) share that XCD's L2.
-    const int q = nwg / 8, r = nwg % 8, xcd = b % 8;
-    return xcd * q + min(xcd, r) + b / 8;
+    // activation rows) share that XCD's L2. The grid is sized for the most
+    // tiles the routing can produce, so the ranges split only the blocks
+    // with real work (nreal): each XCD gets its share among the first
+    // blocks it is sent, and the rest (-1) exit.
+    const int q = nreal / 8, r = nreal % 8, xcd = b % 8, j = b / 8;
+    return j < q + (xcd < r ? 1 : 0) ? xcd * q + min(xcd, r) + j : -1;
 }
 
 // Weights of one pipeline step for one lane: four 16-byte loads per matrix
@@ -265,9 +268,9 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
     __shared__ __attribute__((aligned(16))) float xsum1[2 * kGemmTM];
     __shared__ int m_sh;
 
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int lid = xcd_remap(blockIdx.x, num_tiles[0] * n_blocks);
+    if (lid < 0) return;
     const int tile = lid / n_blocks, nb = lid - tile * n_blocks;
-    if (tile >= num_tiles[0]) return;
     const int e = tile_expert[tile];
     const int groups = kin / 128;
 
