@@ -231,8 +231,13 @@ moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts,
  *   events[2] | shared expert (empty without one) | events[3] | combine |
  *   events[4]
  * events: host array of n_events == MOE_FORWARD_STAGES + 1 hipEvent_t
- * handles (passed as void*), created by the caller. Same results, same
- * kernels, same validation as moe_w4a16_forward.
+ * handles (passed as void*), created by the caller; an entry may be NULL,
+ * and then nothing is recorded at that boundary. Each recorded event makes
+ * the stream drain the previous kernel before the next one starts (a few
+ * microseconds), so a caller timing one stage records only its two
+ * boundaries. Same results, same kernels, same validation as
+ * moe_w4a16_forward; MOE_ERR_INVALID_ARG if events is NULL or n_events is
+ * not MOE_FORWARD_STAGES + 1.
  */
 moe_status_t moe_w4a16_forward_profiled(const moe_ffn_desc_t *experts,
                                         const moe_ffn_desc_t *shared,

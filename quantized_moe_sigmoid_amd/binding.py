@@ -241,7 +241,8 @@ def moe_forward_plan(experts, T, K, act_dtype, shared=None):
 def moe_w4a16_forward(experts, x, topk_w, perm, residual=None, out_dtype=torch.float32,
                       shared=None, out=None, ws=None, events=None):
     """events: None, or a sequence of MOE_FORWARD_STAGES + 1 hipEvent_t
-    handles (ints) recorded at the stage boundaries (the profiled entry)."""
+    handles (ints, or None for a boundary that records nothing) recorded at
+    the stage boundaries (the profiled entry)."""
     T, H = x.shape
     K = topk_w.shape[1]
     dev = x.device

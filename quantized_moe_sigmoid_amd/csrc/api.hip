@@ -314,7 +314,8 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
 
     hipStream_t s = (hipStream_t)stream;
     auto mark = [&](int i) -> moe_status_t {
-        if (events && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess) return MOE_ERR_HIP;
+        if (events && events[i] && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess)
+            return MOE_ERR_HIP;
         return MOE_OK;
     };
     char *w = (char *)ws;
@@ -355,8 +356,6 @@ moe_status_t moe_w4a16_forward_profiled(const moe_ffn_desc_t *experts,
                                         void *out, int out_dtype, void *ws, size_t ws_bytes,
                                         void *stream, void *const *events, int n_events) {
     if (!events) return MOE_ERR_INVALID_ARG;
-    for (int i = 0; i < n_events; ++i)
-        if (!events[i]) return MOE_ERR_INVALID_ARG;
     return forward_impl(experts, shared, x, act_dtype, T, K, topk_w, perm, residual, out,
                         out_dtype, ws, ws_bytes, stream, events, n_events);
 }

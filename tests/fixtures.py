@@ -115,3 +115,31 @@ def shared_bf16(Fs, H, root, layer, dev):
             synth.expert_weight_bf16(H, Fs, root, layer, synth.T_SH_DOWN, 0))
     desc = B.ffn(*[B.bank_bf16(W.to(dev)) for W in mats])
     return desc, tuple(W.float().numpy().astype(np.float64) for W in mats)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (ctypes), for the profiled
+    forward entry point."""
+
+    def __init__(self):
+        import ctypes
+        self.c = ctypes
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = self.c.c_void_p()
+        assert self.L.hipEventCreate(self.c.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = self.c.c_float()
+        assert self.L.hipEventElapsedTime(self.c.byref(ms), self.c.c_void_p(a),
+                                          self.c.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(self.c.c_void_p(e))

@@ -177,6 +177,28 @@ def test_forward_validation_before_launch(L):
              B.MOE_F32, None, 0, None) == B.MOE_OK
 
 
+def test_forward_profiled_validation(L):
+    """The profiled entry: events must be an array of MOE_FORWARD_STAGES + 1
+    entries; NULL entries are boundaries that record nothing."""
+    f = _ffn()
+    st, tm, ws = _plan(f, T=8)
+    p = B.PermDesc(*([FAKE] * 9), tm)
+    F = L.moe_w4a16_forward_profiled
+    x = ctypes.c_void_p(FAKE)
+    n = B.MOE_FORWARD_STAGES + 1
+    none = (ctypes.c_void_p * n)()
+    args = (ctypes.byref(f), None, x, B.MOE_F16, 8, 8, x, ctypes.byref(p), None, x, B.MOE_F32,
+            x, ws, None)
+    assert F(*args, None, n) == B.MOE_ERR_INVALID_ARG
+    assert F(*args, none, n - 1) == B.MOE_ERR_INVALID_ARG
+    # the usual validation still runs first
+    bad = args[:12] + (ws - 1, None)
+    assert F(*bad, none, n) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # T == 0 with only NULL entries: a no-op that touches no device
+    assert F(ctypes.byref(f), None, None, B.MOE_F16, 0, 8, None, ctypes.byref(p), None, None,
+             B.MOE_F32, None, 0, None, none, n) == B.MOE_OK
+
+
 def test_dequant_validation(L):
     b = _bank(B.MOE_W_INT4_G128, 4, 64, 256)
     out = ctypes.c_void_p(FAKE)

@@ -229,6 +229,35 @@ def test_forward_decode_full_shape(dev, T):
     assert ok, ratio
 
 
+@pytest.mark.parametrize("T", [8, 256])
+def test_forward_profiled_matches_plain(dev, T):
+    """The profiled entry point runs the same kernels: bitwise the same output
+    as the plain forward, with every boundary recorded and with only the
+    gate/up boundaries (NULL entries elsewhere); the recorded stages have
+    positive durations. T = 8 runs the decode kernels, T = 256 the GEMMs."""
+    ffn, _ = _int4_ffn_random(E, H, F, 300 + T, dev)
+    x = synth.activations(T, H, "bf16", 4).to(dev)
+    lg = synth.router_logits(T, E, 4)
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    tm, _ = B.moe_forward_plan(ffn, T, K, x.dtype)
+    perm = B.moe_permute(ids, E, tm)
+    plain = B.moe_w4a16_forward(ffn, x, w, perm).cpu().numpy()
+    hip = FX.HipEvents()
+    n = B.MOE_FORWARD_STAGES + 1
+    full = [hip.create() for _ in range(n)]
+    gu = [hip.create(), hip.create()]
+    try:
+        a = B.moe_w4a16_forward(ffn, x, w, perm, events=full).cpu().numpy()
+        b = B.moe_w4a16_forward(ffn, x, w, perm, events=gu + [None] * (n - 2)).cpu().numpy()
+        torch.cuda.synchronize()
+        assert _bits_equal(a, plain) and _bits_equal(b, plain)
+        assert hip.elapsed_ms(full[0], full[1]) > 0 and hip.elapsed_ms(full[1], full[2]) > 0
+        assert hip.elapsed_ms(gu[0], gu[1]) > 0
+    finally:
+        for e in full + gu:
+            hip.destroy(e)
+
+
 def test_forward_nvfp4_small(dev):
     Ee, Hh, Ff, T, Kk = 6, 512, 256, 5, 3
     banks, host = [], []
