@@ -93,20 +93,24 @@ __global__ void __launch_bounds__(256) route_given_kernel(
 }
 
 // Logits computed: a plain fp32 SIMT GEMM, logits[t][e] = x[t] . wT[:, e],
-// in which every output is one fma chain over k in ascending order. Block
-// tile: 64 experts (one per lane) x 32 tokens (8 per wave); k advances in
-// chunks of 64 staged in LDS (double buffered): the 64 x 64 slice of wT
-// read by all four waves, and x widened to float32, token-minor, so a wave
-// reads its 8 tokens' inputs with two broadcast 16-byte LDS reads.
-constexpr int kRtExp = 64, kRtTok = 32, kRtKC = 64;
+// in which every output is one fma chain over k in ascending order (so the
+// input range cannot be split across threads). Block tile: 64 experts (one
+// per lane) x 16 tokens (4 per wave): at T = 2048 and E = 352 that is 768
+// work groups, three per CU in one round, and each wave's serial chain
+// work stays short. k advances in chunks of 64 staged in LDS (double
+// buffered): the 64 x 64 slice of wT read by all four waves, and x widened
+// to float32, token-minor, so a wave reads its 4 tokens' inputs with one
+// broadcast 16-byte LDS read per k.
+constexpr int kRtExp = 64, kRtTok = 16, kRtKC = 64;
 
 template <int ACT>
 __global__ void __launch_bounds__(256) router_logits_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wT,
     const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
-    // xs rows padded to 36 floats: the transposing stores of two k rows 8
-    // apart then fall on different bank halves; 36 * 4 bytes keeps every
-    // 8-token group 16-byte aligned for the broadcast reads
+    // xs rows padded to 20 floats: the transposing stores of the four k rows
+    // a wave writes (4 apart) then fall on four different 16-bank groups;
+    // 20 * 4 bytes keeps every 4-token group 16-byte aligned for the
+    // broadcast reads
     __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
     __shared__ __attribute__((aligned(16))) float xs[2][kRtKC][kRtTok + 4];
     const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp;
@@ -114,11 +118,11 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
 
     // staging roles: wT float4 column tid%16 of rows tid/16 + 16 i (each
     // store instruction writes 4 whole 256-byte rows: no bank conflicts);
-    // x: token tid%32, 8 consecutive k starting at 8 * (tid/32)
+    // x: token tid%16, 4 consecutive k starting at 4 * (tid/16)
     const int wk = threadIdx.x >> 4, we = (threadIdx.x & 15) * 4;
-    const int xt = threadIdx.x & 31, xk = (threadIdx.x >> 5) * 8;
+    const int xt = threadIdx.x & 15, xk = (threadIdx.x >> 4) * 4;
     float4 wreg[4];
-    uint4 xreg;
+    uint2 xreg;
     auto load = [&](int k0) {
         const int e = e0 + we;
 #pragma unroll
@@ -129,22 +133,22 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
                                               e + 2 < E ? wp[2] : 0.f, 0.f);
         }
         const int t = t0 + xt;
-        xreg = t < T ? *(const uint4 *)(x + (size_t)t * H + k0 + xk) : make_uint4(0, 0, 0, 0);
+        xreg = t < T ? *(const uint2 *)(x + (size_t)t * H + k0 + xk) : make_uint2(0, 0);
     };
     auto store = [&](int b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) *(float4 *)&ws[b][wk + 16 * i][we] = wreg[i];
-        const uint32_t d[4] = {xreg.x, xreg.y, xreg.z, xreg.w};
+        const uint32_t d[2] = {xreg.x, xreg.y};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             xs[b][xk + 2 * i][xt] = act_to_f32<ACT>(d[i] & 0xFFFF);
             xs[b][xk + 2 * i + 1][xt] = act_to_f32<ACT>(d[i] >> 16);
         }
     };
 
-    float acc[8];
+    float acc[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) acc[i] = 0.0f;
     const int nch = H / kRtKC;
     load(0);
     store(0);
@@ -155,16 +159,11 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
 #pragma unroll 16
         for (int k = 0; k < kRtKC; ++k) {
             const float w = ws[b][k][lane];
-            const float4 xa = *(const float4 *)&xs[b][k][8 * wave];
-            const float4 xb = *(const float4 *)&xs[b][k][8 * wave + 4];
+            const float4 xa = *(const float4 *)&xs[b][k][4 * wave];
             acc[0] = __builtin_fmaf(xa.x, w, acc[0]);
             acc[1] = __builtin_fmaf(xa.y, w, acc[1]);
             acc[2] = __builtin_fmaf(xa.z, w, acc[2]);
             acc[3] = __builtin_fmaf(xa.w, w, acc[3]);
-            acc[4] = __builtin_fmaf(xb.x, w, acc[4]);
-            acc[5] = __builtin_fmaf(xb.y, w, acc[5]);
-            acc[6] = __builtin_fmaf(xb.z, w, acc[6]);
-            acc[7] = __builtin_fmaf(xb.w, w, acc[7]);
         }
         if (c + 1 < nch) store(b ^ 1);
         __syncthreads();
@@ -173,8 +172,92 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
     if (e >= E) return;
     const float bv = bias ? bias[e] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = t0 + 8 * wave + i;
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * wave + i;
+        if (t < T) logits[(size_t)t * E + e] = bias ? acc[i] + bv : acc[i];
+    }
+}
+
+// bf16 activations: the wave's 4 token rows are wave-uniform, so they are
+// read with scalar loads straight into SGPRs and widened there (bf16 -> f32
+// is a shift), and every FMA takes its x operand from an SGPR. Only wT goes
+// through LDS (one lane-varying 4-byte read per k), which removes the
+// broadcast x reads that bound the LDS return path above. Same tiles, same
+// per-(t, e) chain order.
+__global__ void __launch_bounds__(256) router_logits_bf16_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ wT,
+    const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
+    const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the wave's token rows as 32-bit pairs (rows past T read row t0; their
+    // logits are not stored)
+    const uint32_t *xr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * wave + i;
+        xr[i] = (const uint32_t *)(x + (size_t)(t < T ? t : t0) * H);
+    }
+    // E % 4 == 0: a float4 column group is either inside the matrix or past
+    // it; groups past it read the last group and store zeros (no branch)
+    const int wk = threadIdx.x >> 4, we = (threadIdx.x & 15) * 4;
+    const bool w_in = e0 + we < E;
+    const int w_col = w_in ? e0 + we : E - 4;
+    float4 wreg[4];
+    // the next chunk's x bytes of the wave's rows (4 rows x 128 B) are also
+    // touched with vector loads one chunk ahead, so the scalar loads that
+    // consume them hit L2 instead of waiting for HBM; the loaded words only
+    // feed `sink`
+    uint32_t sink = 0, xtouch = 0;
+    const int tpf = t0 + 4 * wave + ((lane >> 3) & 3);
+    const uint16_t *xpf = x + (size_t)(tpf < T ? tpf : t0) * H + (lane & 7) * 8;
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            wreg[i] = *(const float4 *)(wT + (size_t)(k0 + wk + 16 * i) * E + w_col);
+        xtouch = *(const uint32_t *)(xpf + k0);
+    };
+    auto store = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(float4 *)&ws[b][wk + 16 * i][we] = w_in ? wreg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        sink ^= xtouch;
+    };
+
+    float acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = 0.0f;
+    const int nch = H / kRtKC;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        if (c + 1 < nch) load((c + 1) * kRtKC);
+        const int p0 = c * (kRtKC / 2);
+#pragma unroll 8
+        for (int k2 = 0; k2 < kRtKC / 2; ++k2) {
+            uint32_t xp[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xp[i] = xr[i][p0 + k2];
+            const float w0 = ws[b][2 * k2][lane], w1 = ws[b][2 * k2 + 1][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(__uint_as_float(xp[i] << 16), w0, acc[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = __builtin_fmaf(__uint_as_float(xp[i] & 0xFFFF0000u), w1, acc[i]);
+        }
+        if (c + 1 < nch) store(b ^ 1);
+        __syncthreads();
+    }
+    const int e = e0 + lane;
+    if (sink == 0x9E3779B9u && H == 0) logits[0] = 0.0f;    // never true: keeps the prefetch
+    if (e >= E) return;
+    const float bv = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * wave + i;
         if (t < T) logits[(size_t)t * E + e] = bias ? acc[i] + bv : acc[i];
     }
 }
@@ -184,7 +267,7 @@ moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, c
     if (T == 0) return MOE_OK;
     const dim3 grid((T + kRtTok - 1) / kRtTok, (E + kRtExp - 1) / kRtExp);
     if (x_dtype == MOE_BF16)
-        hipLaunchKernelGGL(router_logits_kernel<MOE_BF16>, grid, dim3(256), 0, s,
+        hipLaunchKernelGGL(router_logits_bf16_kernel, grid, dim3(256), 0, s,
                            (const uint16_t *)x, wT, bias, T, H, E, logits);
     else
         hipLaunchKernelGGL(router_logits_kernel<MOE_F16>, grid, dim3(256), 0, s,
