@@ -21,6 +21,8 @@ router    canonical float32 router logits (C), top-K selection, sigmoid
 permute   expert histogram, stable expert-sorted permutation, padded tiles.
 layer     SwiGLU expert FFN, weighted combine, shared expert, residual.
 norm      the zero-centred-gain RMSNorm that feeds each layer of the stack.
+csf       the compressed scale format of the NVFP4 block scales (row base +
+          4-bit code, exceptions grouped by expert): encoder and decoder.
 
 Every function with no independent pin says "parity unpinned" in its
 docstring.
