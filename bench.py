@@ -16,7 +16,8 @@ steps HIP events are recorded only around the gate/up kernel (every recorded
 event drains the stream); the other stages' durations come from a separate,
 untimed pass over the same inputs with every stage boundary recorded.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|nvfp4]
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+                  [--workload decode|prefill|nvfp4|nvfp4-csf|stack]
                   [--tokens T] [--no-sweep] [--no-cpu-baseline]
 """
 import argparse
@@ -57,11 +58,16 @@ class Hip:
         self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                ctypes.c_void_p]
         self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def event(self):
         e = ctypes.c_void_p()
         assert self.L.hipEventCreate(ctypes.byref(e)) == 0
         return e.value
+
+    def record(self, e, stream=None):
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        assert self.L.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(s)) == 0
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -84,6 +90,25 @@ def int4_banks(copies, dev, seed0):
     return out
 
 
+def csf_inputs(banks, dev, seed0):
+    """Per bank copy and matrix: random CSF tensors whose expansion becomes
+    that matrix's scale bytes, and the scale buffer to expand into."""
+    out = []
+    for c, bank in enumerate(banks):
+        mats = []
+        for i, scale in enumerate(bank.scale_tensors):
+            R, C = scale.shape[1], scale.shape[2]
+            mats.append((synth.csf_random(E, R, C, seed0 + 10 * c + i, dev), R, C, scale))
+        out.append(mats)
+    return out
+
+
+def csf_bytes(R, C):
+    """Algorithmic bytes of expanding one expert's scale matrix: the fixed
+    codes and bases read, the bytes written (exceptions are ~0.2 % extra)."""
+    return R * (1 + C // 2) + R * C
+
+
 def nvfp4_banks(copies, dev, seed0):
     out = []
     for c in range(copies):
@@ -91,7 +116,9 @@ def nvfp4_banks(copies, dev, seed0):
         for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
             q, s, g = synth.packed_nvfp4_random(E, n, k, seed0 + 10 * c + i, dev)
             mats.append(B.bank_nvfp4(q, s, g))
-        out.append(B.ffn(*mats))
+        f = B.ffn(*mats)
+        f.scale_tensors = [m._keep[1] for m in mats]     # gate, up, down scale bytes
+        out.append(f)
     return out
 
 
@@ -99,9 +126,11 @@ def touched_experts(logits_cpu):
     return int(torch.unique(torch.topk(logits_cpu, K, dim=1).indices).numel())
 
 
-def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt):
+def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf=None):
     """Times `steps` layer passes. route_mode: 'logits' (fresh N(0,1) logits
-    per step) or 'weights' (router weight + fixed batch). Returns a dict."""
+    per step) or 'weights' (router weight + fixed batch). csf: per bank copy,
+    CSF tensors of its three scale matrices; each step then expands the
+    routed experts' scales before the forward pass. Returns a dict."""
     n_in = steps + warmup
     x = synth.activations(T, H, act, 3 if route_mode == "weights" else 2).to(dev)
     if route_mode == "logits":
@@ -126,12 +155,22 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt):
     nb = min(steps, 10)
     ev_b = [[hip.event() for _ in range(NS + 1)] for _ in range(nb)]
 
-    def step(i, events=None):
+    ev_c = [[hip.event(), hip.event()] for _ in range(nb)] if csf else None
+
+    def step(i, events=None, csf_events=None):
         if route_mode == "logits":
             B.moe_route_topk(K, logits=logits[i], ids=ids, w=w)
         else:
             B.moe_route_topk(K, x=x, router_wT=wT, ids=ids, w=w, ws=rws)
         B.moe_permute(ids, E, tm, perm=perm)
+        if csf:
+            if csf_events:
+                hip.record(csf_events[0])
+            for (fx, ex, st), R, C, scale in csf[i % len(csf)]:
+                B.moe_csf_expand(fx, ex, st, R, C, out=scale, expert_offsets=perm.expert_offsets,
+                                 max_routed=min(E, T * K))
+            if csf_events:
+                hip.record(csf_events[1])
         B.moe_w4a16_forward(banks[i % len(banks)], x, w, perm, out=out, ws=ws, events=events)
 
     for i in range(warmup):
@@ -145,10 +184,11 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt):
     gu_ms = np.array([hip.elapsed_ms(e[0], e[1]) for e in ev_t])
     # stage breakdown: the first nb steps again, every boundary recorded
     for i in range(nb):
-        step(i, ev_b[i])
+        step(i, ev_b[i], ev_c[i] if csf else None)
     torch.cuda.synchronize()
     stage_ms = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(NS)] for e in ev_b])
-    for e in ev_t + ev_b:
+    csf_ms = np.array([hip.elapsed_ms(e[0], e[1]) for e in ev_c]) if csf else None
+    for e in ev_t + ev_b + (ev_c or []):
         for h in e:
             hip.destroy(h)
     if route_mode == "logits":
@@ -167,6 +207,10 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt):
              down_GBps=float(np.mean(U[:nb] * dn_bytes / (stage_ms[:, 1] * 1e-3)) / 1e9),
              layer_TFLOPs=float(T * K * FLOP_PER_SLOT / (ms * 1e-3) / 1e12))
     r["gateup_frac_hbm"] = r["gateup_GBps"] * 1e9 / HBM_PEAK
+    if csf:
+        cb = 2 * csf_bytes(F, H // 16) + csf_bytes(H, F // 16)
+        r["csf_ms"] = float(csf_ms.mean())
+        r["csf_GBps"] = float(np.mean(U[:nb] * cb / (csf_ms * 1e-3)) / 1e9)
     return r
 
 
@@ -324,7 +368,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "nvfp4", "stack"])
+                    choices=["decode", "prefill", "nvfp4", "nvfp4-csf", "stack"])
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -351,17 +395,20 @@ def main():
 
     int4 = int4_banks(2, dev, 500)
     jobs = []
-    main_T = args.tokens or {"decode": 64, "prefill": 2048, "nvfp4": 256,
+    main_T = args.tokens or {"decode": 64, "prefill": 2048, "nvfp4": 256, "nvfp4-csf": 64,
                              "stack": 4096}[args.workload]
     spec = {"decode": ("f16", "logits", "int4"), "prefill": ("bf16", "weights", "int4"),
-            "nvfp4": ("bf16", "logits", "nvfp4"), "stack": ("bf16", "weights", "int4")}
+            "nvfp4": ("bf16", "logits", "nvfp4"), "nvfp4-csf": ("bf16", "logits", "nvfp4"),
+            "stack": ("bf16", "weights", "int4")}
     jobs.append((args.workload, main_T))
     if not args.no_sweep:
         for wl, T in (("decode", 1), ("decode", 8), ("decode", 64), ("prefill", 2048),
-                      ("nvfp4", 1), ("nvfp4", 256), ("stack", 32), ("stack", 4096)):
+                      ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("stack", 32),
+                      ("stack", 4096)):
             if (wl, T) != (args.workload, main_T):
                 jobs.append((wl, T))
     nv = None
+    nv_csf = None
     stack = None
     results = []
     for wl, T in jobs:
@@ -376,8 +423,13 @@ def main():
             if fmt == "nvfp4" and nv is None:
                 nv = nvfp4_banks(2, dev, 900)
             banks = int4 if fmt == "int4" else nv
+            csf = None
+            if wl == "nvfp4-csf":
+                if nv_csf is None:
+                    nv_csf = csf_inputs(nv, dev, 1900)
+                csf = nv_csf
             results.append(run_layer("%s T=%d" % (wl, T), banks, T, act, rmode, steps,
-                                     args.warmup, hip, dev, fmt))
+                                     args.warmup, hip, dev, fmt, csf))
         print("# %s" % json.dumps(results[-1]), file=sys.stderr, flush=True)
 
     head = results[0]

@@ -283,6 +283,43 @@ moe_status_t moe_rmsnorm(const float *x, const float *weight, float eps, int T, 
 moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out,
                          void *stream);
 
+/*
+ * moe_csf_expand -- the E4M3 block-scale bytes of an NVFP4 bank from their
+ * compressed scale format (page "Step-5-Preview-NVFP4-Local", "Format" and
+ * "Modifications" item 1): a scale byte is its row's base plus its 4-bit
+ * code, unless an exception at that position replaces it with the stored
+ * byte. The expanded bytes are the `scale` array of an NVFP4
+ * moe_weight_desc_t with scale_row_stride C and scale_expert_stride R*C
+ * (the page's loader expands one layer's scales into scratch before the
+ * layer runs).
+ *   fixed          U8  [E][R/16][16*(1 + C/2)], 8-byte aligned: per slab of
+ *                  16 rows, the 16 row bases, then each row's C codes, two
+ *                  per byte, low nibble first;
+ *   exceptions     U32 [n_exceptions], 4-byte aligned (NULL if none):
+ *                  (row*C + col) | byte << 24, grouped by expert, row and
+ *                  col counted within the expert, positions distinct within
+ *                  an expert; entries past R*C are ignored;
+ *   starts         I64 [E+1], 8-byte aligned: expert e owns exceptions
+ *                  [starts[e], starts[e+1]) (clamped to [0, n_exceptions]);
+ *   expert_offsets I32 [E+1] or NULL: the moe_permute expert offsets; experts
+ *                  with no routed slot are skipped (their bytes in `out` are
+ *                  left unchanged);
+ *   max_routed_experts  with expert_offsets: an upper bound on the number of
+ *                  experts with routed slots (min(E, T*K) for a batch of T
+ *                  tokens and K choices), which sizes the grid to the routed
+ *                  experts only; 0 = E. A bound below the true count leaves
+ *                  the experts past it unexpanded;
+ *   out            U8  [E][R][C], 16-byte aligned, caller-owned.
+ * All arrays are device memory; the call enqueues two kernels on `stream`.
+ * Limits: R and C positive multiples of 16, E <= 512, max_routed_experts >= 0
+ * (MOE_ERR_INVALID_ARG), R*C < 2^24 (MOE_ERR_UNSUPPORTED): positions are
+ * 24-bit.
+ */
+moe_status_t moe_csf_expand(const uint8_t *fixed, const uint32_t *exceptions,
+                            int64_t n_exceptions, const int64_t *starts, int E, int R, int C,
+                            const int32_t *expert_offsets, int max_routed_experts,
+                            uint8_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16 = 1, 2, 3
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_route_workspace",
            "moe_route_topk", "moe_permute_sizes",
            "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_w4a16_forward_profiled",
-           "moe_round_activations", "moe_rmsnorm", "moe_dequant")
+           "moe_round_activations", "moe_rmsnorm", "moe_dequant", "moe_csf_expand")
 MOE_FORWARD_STAGES = 4
 
 _DT = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
@@ -82,10 +82,12 @@ def lib():
         L.moe_round_activations.argtypes = [vp, i64, i32, vp, vp]
         L.moe_rmsnorm.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, vp]
         L.moe_dequant.argtypes = [P(WeightDesc), i32, vp, vp]
+        L.moe_csf_expand.argtypes = [vp, vp, i64, vp, i32, i32, i32, vp, i32, vp, vp]
         for name in ("moe_router_logits", "moe_route_workspace", "moe_route_topk",
                      "moe_permute_sizes", "moe_permute", "moe_forward_plan",
                      "moe_w4a16_forward", "moe_w4a16_forward_profiled",
-                     "moe_round_activations", "moe_rmsnorm", "moe_dequant"):
+                     "moe_round_activations", "moe_rmsnorm", "moe_dequant",
+                     "moe_csf_expand"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -288,4 +290,22 @@ def moe_dequant(desc, expert, out=None, device=None):
         out = torch.empty((desc.n, desc.k), dtype=torch.float32, device=device or "cuda")
     _check(lib().moe_dequant(ctypes.byref(desc), expert, _ptr(out), _stream(out.device)),
            "moe_dequant")
+    return out
+
+
+def moe_csf_expand(fixed, exceptions, starts, R, C, out=None, expert_offsets=None,
+                   max_routed=0):
+    """NVFP4 block-scale bytes [E][R][C] (uint8) from the CSF tensors: fixed
+    uint8 [E][R/16][16*(1+C/2)], exceptions int32/uint32 [n], starts int64
+    [E+1]; expert_offsets (int32 [E+1], the permute output) limits the
+    expansion to routed experts, max_routed (e.g. min(E, T*K)) bounds their
+    number so the grid covers only them."""
+    E = fixed.shape[0]
+    if out is None:
+        out = torch.empty((E, R, C), dtype=torch.uint8, device=fixed.device)
+    n = exceptions.numel() if exceptions is not None else 0
+    _check(lib().moe_csf_expand(_ptr(fixed), _ptr(exceptions) if n else None, n, _ptr(starts), E,
+                                R, C, _ptr(expert_offsets), int(max_routed), _ptr(out),
+                                _stream(out.device)),
+           "moe_csf_expand")
     return out

@@ -15,6 +15,10 @@ moe_status_t launch_topk(const float *logits, const float *bias, int T, int E, i
 moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_perm_t &p,
                             hipStream_t s);
 moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out, hipStream_t s);
+moe_status_t launch_csf_expand(const uint8_t *fixed, const uint32_t *exceptions, int64_t n,
+                               const int64_t *starts, int E, int R, int C,
+                               const int32_t *expert_offsets, int max_routed, uint8_t *out,
+                               hipStream_t s);
 moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
                                  hipStream_t s, const std::function<moe_status_t(int)> &mark);
@@ -386,6 +390,23 @@ moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out, voi
     if (st != MOE_OK) return st;
     if (!aligned(out, 16)) return MOE_ERR_INVALID_ARG;
     return launch_dequant(*w, expert, out, (hipStream_t)stream);
+}
+
+moe_status_t moe_csf_expand(const uint8_t *fixed, const uint32_t *exceptions,
+                            int64_t n_exceptions, const int64_t *starts, int E, int R, int C,
+                            const int32_t *expert_offsets, int max_routed_experts,
+                            uint8_t *out, void *stream) {
+    if (!fixed || !starts || !out || n_exceptions < 0 || (n_exceptions > 0 && !exceptions))
+        return MOE_ERR_INVALID_ARG;
+    if (E < 1 || E > kMaxExperts || R < 16 || R % 16 || C < 16 || C % 16)
+        return MOE_ERR_INVALID_ARG;
+    if ((int64_t)R * C >= ((int64_t)1 << 24)) return MOE_ERR_UNSUPPORTED;   // 24-bit positions
+    if (max_routed_experts < 0) return MOE_ERR_INVALID_ARG;
+    if (!aligned(fixed, 8) || !aligned(out, 16) || !aligned(starts, 8) ||
+        (exceptions && !aligned(exceptions, 4)) || (expert_offsets && !aligned(expert_offsets, 4)))
+        return MOE_ERR_INVALID_ARG;
+    return launch_csf_expand(fixed, exceptions, n_exceptions, starts, E, R, C, expert_offsets,
+                             max_routed_experts, out, (hipStream_t)stream);
 }
 
 }  // extern "C"

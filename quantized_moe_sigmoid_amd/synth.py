@@ -118,6 +118,31 @@ def packed_int4_random(E, n, k, seed, device, scale_mean=0.0043):
     return q, s.to(torch.bfloat16)
 
 
+def csf_random(E, R, C, seed, device, rate=0.002):
+    """Random CSF tensors of an NVFP4 scale tensor [E, R, C]: row bases
+    uniform in [0x60, 0x6F], uniform 4-bit codes, and per expert about
+    rate * R * C exceptions at distinct random positions (row-major order)
+    holding bytes uniform in [0x30, 0x7E]. Every byte they stand for is a
+    finite non-negative E4M3 value. Returns (fixed uint8 [E, R/16,
+    16 * (1 + C/2)], exceptions int32 [n], starts int64 [E + 1])."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    fixed = torch.randint(0, 256, (E, R // 16, 16 * (1 + C // 2)), generator=g, device=device,
+                          dtype=torch.uint8)
+    fixed[:, :, :16] = torch.randint(0x60, 0x70, (E, R // 16, 16), generator=g, device=device,
+                                     dtype=torch.uint8)
+    m = max(0, int(round(rate * R * C)))
+    exc, starts = [], [0]
+    for e in range(E):
+        pos = torch.unique(torch.randint(0, R * C, (m,), generator=g, device=device))
+        byte = torch.randint(0x30, 0x7F, (pos.numel(),), generator=g, device=device)
+        exc.append((pos | (byte << 24)).to(torch.int32))
+        starts.append(starts[-1] + pos.numel())
+    exceptions = torch.cat(exc) if exc else torch.zeros(0, dtype=torch.int32, device=device)
+    return fixed, exceptions, torch.tensor(starts, dtype=torch.int64, device=device)
+
+
 def packed_nvfp4_random(E, n, k, seed, device, gs_mean=2.0e-5):
     """Random NVFP4 bank in packed form: uniform bytes (two uniform E2M1
     codes each), E4M3 block-scale bytes uniform in [0x70, 0x7E] (128 .. 448)

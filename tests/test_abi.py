@@ -268,3 +268,26 @@ def test_rmsnorm_validation(L):
         B.MOE_ERR_INVALID_ARG                                                      # alignment
     assert N(None, None, 1e-5, 4, 4096, B.MOE_BF16, p, None) == B.MOE_ERR_INVALID_ARG
     assert N(None, None, 1e-5, 0, 4096, B.MOE_BF16, None, None) == B.MOE_OK
+
+
+def test_csf_expand_validation(L):
+    """Argument errors of moe_csf_expand are found before any launch."""
+    F = L.moe_csf_expand
+    p = ctypes.c_void_p(FAKE)
+    ok = (p, p, 4, p, 2, 32, 16, None, 0, p, None)
+    bad = [
+        ((None,) + ok[1:], B.MOE_ERR_INVALID_ARG),                     # fixed
+        (ok[:1] + (None,) + ok[2:], B.MOE_ERR_INVALID_ARG),            # exceptions with n > 0
+        (ok[:2] + (-1,) + ok[3:], B.MOE_ERR_INVALID_ARG),              # n < 0
+        (ok[:3] + (None,) + ok[4:], B.MOE_ERR_INVALID_ARG),            # starts
+        (ok[:4] + (0,) + ok[5:], B.MOE_ERR_INVALID_ARG),               # E
+        (ok[:5] + (24,) + ok[6:], B.MOE_ERR_INVALID_ARG),              # R % 16
+        (ok[:6] + (8,) + ok[7:], B.MOE_ERR_INVALID_ARG),               # C % 16
+        (ok[:5] + (4096, 4096) + ok[7:], B.MOE_ERR_UNSUPPORTED),       # R*C >= 2^24
+        (ok[:8] + (-1,) + ok[9:], B.MOE_ERR_INVALID_ARG),              # max_routed_experts
+        (ok[:9] + (None,) + ok[10:], B.MOE_ERR_INVALID_ARG),           # out
+        (ok[:9] + (ctypes.c_void_p(FAKE + 8),) + ok[10:], B.MOE_ERR_INVALID_ARG),  # out alignment
+        ((ctypes.c_void_p(FAKE + 4),) + ok[1:], B.MOE_ERR_INVALID_ARG),            # fixed alignment
+    ]
+    for args, want in bad:
+        assert F(*args) == want, args

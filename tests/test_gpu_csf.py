@@ -1,0 +1,112 @@
+"""GPU parity of the CSF scale expansion (moe_csf_expand) against the oracle's
+CSF codec: the expanded bytes are bitwise the bytes the tensors encode, at
+small and at the layer's own shapes, with and without the routed-experts
+restriction; an NVFP4 forward pass on expanded scales is bitwise the one on
+the raw scales."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import csf as OC
+from oracle import router as OR
+from quantized_moe_sigmoid_amd import binding as B
+from quantized_moe_sigmoid_amd import synth
+from tests import fixtures as FX
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    return torch.device("cuda:0")
+
+
+def _scales(E, R, C, seed, outlier_rate):
+    """E4M3 scale bytes with the structure CSF targets: each row clustered in
+    a window (its base drawn per row), a fraction of outliers anywhere in the
+    finite non-negative range 0x00..0x7E."""
+    rng = np.random.default_rng(seed)
+    base = rng.integers(0x20, 0x6F, (E, R, 1))
+    s = base + rng.integers(0, 16, (E, R, C))
+    out = rng.random((E, R, C)) < outlier_rate
+    s[out] = rng.integers(0, 0x7F, int(out.sum()))
+    return np.minimum(s, 0x7E).astype(np.uint8)
+
+
+def _to_dev(fixed, exc, starts, dev):
+    return (torch.from_numpy(fixed).to(dev),
+            torch.from_numpy(exc.view(np.int32)).to(dev),
+            torch.from_numpy(starts).to(dev))
+
+
+@pytest.mark.parametrize("E,R,C,rate", [(3, 32, 16, 0.05), (5, 48, 96, 0.2), (2, 16, 256, 0.0),
+                                        (4, 64, 32, 1.0)])
+def test_csf_expand_small(dev, E, R, C, rate):
+    s = _scales(E, R, C, 10 + E, rate)
+    fixed, exc, starts = OC.encode(s)
+    want = OC.decode(fixed, exc, starts, R, C)
+    assert np.array_equal(want, s)
+    got = B.moe_csf_expand(*_to_dev(fixed, exc, starts, dev), R, C).cpu().numpy()
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("R,C", [(1536, 256), (4096, 96)])
+def test_csf_expand_layer_shapes(dev, R, C):
+    """The gate/up and down scale tensors of one layer (352 experts), with
+    0.2 % exceptions (the page's CSF totals imply about that rate)."""
+    s = _scales(352, R, C, R + C, 0.002)
+    fixed, exc, starts = OC.encode(s)
+    assert exc.size > 0
+    got = B.moe_csf_expand(*_to_dev(fixed, exc, starts, dev), R, C).cpu().numpy()
+    assert np.array_equal(got, s)
+
+
+def test_csf_expand_routed_experts_only(dev):
+    """With the permutation's expert offsets, experts with no routed slot are
+    left untouched and every routed expert is expanded exactly."""
+    E, R, C, T, K = 16, 32, 32, 3, 2
+    s = _scales(E, R, C, 7, 0.1)
+    fixed, exc, starts = OC.encode(s)
+    lg = synth.router_logits(T, E, 7)
+    ids, _ = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    perm = B.moe_permute(ids, E, 4)
+    routed = set(OR.topk_ids(lg, K).ravel().tolist())
+    assert 0 < len(routed) < E
+    # full grid with skipped experts, and the compact grid sized by T*K
+    for max_routed in (0, min(E, T * K)):
+        out = torch.full((E, R, C), 0xAB, dtype=torch.uint8, device=dev)
+        B.moe_csf_expand(*_to_dev(fixed, exc, starts, dev), R, C, out=out,
+                         expert_offsets=perm.expert_offsets, max_routed=max_routed)
+        got = out.cpu().numpy()
+        for e in range(E):
+            if e in routed:
+                assert np.array_equal(got[e], s[e]), (max_routed, e)
+            else:
+                assert np.all(got[e] == 0xAB), (max_routed, e)
+
+
+def test_nvfp4_forward_on_expanded_scales(dev):
+    """NVFP4 experts whose block scales come from moe_csf_expand give
+    bitwise the output of the same experts on their raw scale bytes."""
+    Ee, Hh, Ff, T, Kk = 6, 512, 256, 5, 3
+    raw, csf = [], []
+    for which, (n, k) in (("gate", (Ff, Hh)), ("up", (Ff, Hh)), ("down", (Hh, Ff))):
+        q, s, gs = FX.nvfp4_bank_oracle(Ee, n, k, 4, 0, which)
+        qd, gsd = torch.from_numpy(q).to(dev), torch.from_numpy(gs).to(dev)
+        raw.append(B.bank_nvfp4(qd, torch.from_numpy(s).to(dev), gsd))
+        fixed, exc, starts = OC.encode(s)
+        sx = B.moe_csf_expand(*_to_dev(fixed, exc, starts, dev), n, k // 16)
+        csf.append(B.bank_nvfp4(qd, sx, gsd))
+    x = synth.activations(T, Hh, "bf16", 4).to(dev)
+    lg = synth.router_logits(T, Ee, 4)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    outs = []
+    for banks in (raw, csf):
+        ffn = B.ffn(*banks)
+        tm, _ = B.moe_forward_plan(ffn, T, Kk, x.dtype)
+        perm = B.moe_permute(ids, Ee, tm)
+        outs.append(B.moe_w4a16_forward(ffn, x, w, perm).cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
