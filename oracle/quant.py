@@ -25,6 +25,14 @@ Readings where the pages are silent (each also listed in the design notes):
   the first minimum in ratio order wins (ties go to the larger ratio).
 * nibble j of int32 word w along K holds input 8w+j (low nibble first, as the
   NVFP4 page's scale codes are stored), as a two's-complement 4-bit integer.
+* int4 g32 (the page's "g32 with the same clip search"): the same quantizer
+  with one scale per 32 inputs.
+* asymmetric int4 (the page's "int4 g128, asymmetric"): min-max range
+  widened to contain 0, scale bf16((hi - lo) / 15), zero point
+  clamp(rne(-lo / s), 0, 15) stored as one byte per group, unsigned nibbles
+  q in [0, 15], w = (q - z) * s; no clip search. This reading gives 10.04 %
+  on Gaussian weights and inputs against the page's 10.05 % (a clip search
+  would give 9.5 %).
 * NVFP4 global scale = fp32(max|W| / (6 * 448)) per expert matrix (1 for an
   all-zero matrix); block scale = E4M3(max|block| / (6 * gs)), saturating,
   ties to even; element code = E2M1(w / (bs * gs)), saturating, ties to
@@ -109,6 +117,50 @@ def rel_error(W, Wq, X):
     """||(Wq - W) X|| / ||W X|| (Frobenius norm over the columns of X), the
     error measure of the int4 page's table."""
     return np.linalg.norm((Wq - W) @ X) / np.linalg.norm(W @ X)
+
+
+# ------------------------------------------------------- int4 asymmetric ---
+def quantize_int4_asym(W, group=INT4_GROUP):
+    """Asymmetric int4 with one bf16 scale and one zero point per group (the
+    int4 page's error table, "int4 g128, asymmetric"). Min-max range that
+    always contains 0: lo = min(min w, 0), hi = max(max w, 0);
+    s = bf16((hi - lo) / 15); z = clamp(rne(-lo / s), 0, 15);
+    q = clamp(rne(w / s) + z, 0, 15); w ~ (q - z) * s. An all-zero group
+    gets s = 0, z = 0, q = 0. Returns q [n, k] uint8, s [n, k/group] float64
+    (bf16 values), z [n, k/group] uint8."""
+    W = np.asarray(W, dtype=np.float64)
+    n, k = W.shape
+    assert k % group == 0
+    Wg = W.reshape(n, k // group, group)
+    lo = np.minimum(Wg.min(axis=-1), 0.0)
+    hi = np.maximum(Wg.max(axis=-1), 0.0)
+    s = to_bf16((hi - lo) / 15.0)
+    safe = np.where(s > 0, s, 1.0)
+    z = np.where(s > 0, np.clip(np.rint(-lo / safe), 0, 15), 0.0)
+    q = np.where(s[..., None] > 0, np.clip(np.rint(Wg / safe[..., None]) + z[..., None], 0, 15),
+                 0.0)
+    return q.reshape(n, k).astype(np.uint8), s, z.astype(np.uint8)
+
+
+def pack_uint4(q):
+    """q [n, k] in [0, 15] -> int32 words [n, k/8]; nibble j of word w is input 8w+j."""
+    q = np.asarray(q, dtype=np.int64)
+    assert q.min(initial=0) >= 0 and q.max(initial=0) <= 15
+    return pack_int4(q - 16 * (q >= 8))      # the same nibble bits, read as unsigned
+
+
+def unpack_uint4(words):
+    """int32 words [n, k/8] -> q [n, k] uint8 in [0, 15]."""
+    return (unpack_int4(words).astype(np.int64) & 0xF).astype(np.uint8)
+
+
+def dequant_int4_asym(words, scales_bf16_bits, zeros, group=INT4_GROUP):
+    """Exact (q - z) * s (float64) from packed unsigned nibbles [n, k/8], bf16
+    scale bit patterns [n, k/group] and zero points uint8 [n, k/group]."""
+    q = unpack_uint4(words).astype(np.float64)
+    z = np.repeat(np.asarray(zeros, dtype=np.float64), group, axis=1)
+    s = np.repeat(bf16_from_bits(scales_bf16_bits), group, axis=1)
+    return (q - z) * s
 
 
 # ----------------------------------------------------------------- NVFP4 ---

@@ -218,3 +218,89 @@ def test_int4_exact_mse_tie_goes_to_larger_ratio(a_hex, b_hex):
     assert winners[:2] == [0, 1] and exact[0][1] != exact[1][1]
     q, s = Q.quantize_int4(W)
     assert s[0, 0] == exact[0][1]
+
+
+# ------------------------------------------- asymmetric int4, int4 g32 ---
+def test_int4_asym_error_matches_page():
+    """The page's 'int4 g128, asymmetric' error on Gaussian weights and
+    inputs (min-max range containing 0; a clip search would give ~9.5 %)."""
+    g = GOLD["int4_g128_relative_error"]
+    W = _gauss_bf16(512, 4096, 0)
+    X = synth.rng(7, 0, 0).standard_normal((4096, 64))
+    q, s, z = Q.quantize_int4_asym(W)
+    Wq = (q.astype(np.float64) - np.repeat(z, 128, 1)) * np.repeat(s, 128, 1)
+    e = Q.rel_error(W, Wq, X)
+    assert abs(e - g["asymmetric"]) < 0.003, e
+
+
+def test_int4_asym_grid_covers_the_group_and_rounds_to_nearest():
+    W = _gauss_bf16(32, 512, 3)
+    q, s, z8 = Q.quantize_int4_asym(W)
+    assert q.max() <= 15 and z8.max() <= 15
+    z = z8.astype(np.float64)
+    Wg = W.reshape(32, 4, 128)
+    lo = np.minimum(Wg.min(-1), 0.0)
+    hi = np.maximum(Wg.max(-1), 0.0)
+    assert np.all(s == F.to_bf16((hi - lo) / 15.0))
+    # the grid (j - z) s, j = 0..15, reaches both ends of the range to within s/2
+    assert np.all(-z * s <= lo + s / 2 + 1e-18) and np.all((15.0 - z) * s >= hi - s / 2 - 1e-18)
+    # every weight maps to the nearest grid value (brute force over the 16)
+    grid = (np.arange(16)[None, None, :] - z[..., None]) * s[..., None]
+    deq = (q.reshape(32, 4, 128).astype(np.float64) - z[..., None]) * s[..., None]
+    best = np.min(np.abs(grid[..., None, :] - Wg[..., None]), axis=-1)
+    assert np.all(np.abs(deq - Wg) <= best + 1e-18)
+
+
+def test_int4_asym_special_groups():
+    W = np.zeros((3, 128))
+    W[1] = 0.5                     # constant positive group: lo = 0
+    W[2, :64] = -0.25              # two values with zero inside the range
+    W[2, 64:] = 0.75
+    q, s, z = Q.quantize_int4_asym(W)
+    assert s[0, 0] == 0 and z[0, 0] == 0 and np.all(q[0] == 0)
+    assert z[1, 0] == 0 and s[1, 0] == F.to_bf16(0.5 / 15) and np.all(q[1] == 15)
+    # zero is always representable exactly: q == z dequantizes to 0
+    assert np.all((q[2].astype(int) - int(z[2, 0])) * s[2, 0] != 0)   # no zero weights here
+    deq = (q.astype(np.float64) - z.astype(np.float64)) * s
+    assert abs(deq[2, 0] + 0.25) <= s[2, 0] / 2 and abs(deq[2, 100] - 0.75) <= s[2, 0] / 2
+
+
+def test_uint4_pack_exhaustive_and_dequant():
+    for pos in range(8):
+        for v in range(16):
+            q = np.zeros((1, 8), dtype=np.uint8)
+            q[0, pos] = v
+            w = Q.pack_uint4(q)
+            assert int(w.view(np.uint32)[0, 0]) == (v << (4 * pos))
+            assert np.array_equal(Q.unpack_uint4(w), q)
+    q = np.arange(256, dtype=np.int64).reshape(2, 128) % 16
+    z = np.array([[3], [15]], dtype=np.uint8)
+    sb = F.bf16_bits(np.array([[0.125], [2.0 ** -20]]))
+    d = Q.dequant_int4_asym(Q.pack_uint4(q), sb, z)
+    assert np.array_equal(d, (q - z.astype(np.int64)) * np.array([[0.125], [2.0 ** -20]]))
+
+
+def test_int4_g32_clip_search_invariants():
+    """g32 uses the same clip search per 32 inputs: never worse than g128 on
+    the same weights, and each group keeps the first best of the 17 bf16
+    candidates (checked by brute force). The page's g32 figure (10.12 %) is
+    for its real expert weights; on Gaussian weights g32 gives ~8.6 %, so
+    that figure is not a pin here."""
+    W = _gauss_bf16(16, 512, 4)
+    q32, s32 = Q.quantize_int4(W, group=32)
+    q128, s128 = Q.quantize_int4(W, group=128)
+    e32 = np.linalg.norm(q32 * np.repeat(s32, 32, 1) - W)
+    e128 = np.linalg.norm(q128 * np.repeat(s128, 128, 1) - W)
+    assert e32 < e128
+    Wg = W.reshape(16, 16, 32)
+    for r in range(16):
+        for g in range(16):
+            a = np.max(np.abs(Wg[r, g]))
+            best, best_s = None, None
+            for i in range(17):
+                sc = float(F.to_bf16(np.float64((40 - i) * a / 280.0)))
+                qq = np.clip(np.rint(Wg[r, g] / sc), -8, 7) if sc > 0 else np.zeros(32)
+                mse = float(np.sum((qq * sc - Wg[r, g]) ** 2))
+                if best is None or mse < best:
+                    best, best_s = mse, sc
+            assert s32[r, g] == best_s
