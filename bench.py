@@ -17,7 +17,7 @@ event drains the stream); the other stages' durations come from a separate,
 untimed pass over the same inputs with every stage boundary recorded.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--workload decode|prefill|nvfp4|nvfp4-csf|stack]
+                  [--workload decode|prefill|nvfp4|nvfp4-csf|int4-g32|int4-asym|stack]
                   [--tokens T] [--no-sweep] [--no-cpu-baseline]
 """
 import argparse
@@ -46,6 +46,14 @@ INT4_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 128) * 2)
 INT4_DOWN_BYTES = H * F // 2 + H * (F // 128) * 2
 NVFP4_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 16))
 NVFP4_DOWN_BYTES = H * F // 2 + H * (F // 16) + 4
+INT4_G32_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 32) * 2)
+INT4_G32_DOWN_BYTES = H * F // 2 + H * (F // 32) * 2
+INT4_ASYM_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 128) * 3)      # + one zero-point byte
+INT4_ASYM_DOWN_BYTES = H * F // 2 + H * (F // 128) * 3
+EXPERT_BYTES = {"int4": (INT4_GATEUP_BYTES, INT4_DOWN_BYTES),
+                "nvfp4": (NVFP4_GATEUP_BYTES, NVFP4_DOWN_BYTES),
+                "int4-g32": (INT4_G32_GATEUP_BYTES, INT4_G32_DOWN_BYTES),
+                "int4-asym": (INT4_ASYM_GATEUP_BYTES, INT4_ASYM_DOWN_BYTES)}
 FLOP_PER_SLOT = 3 * 2 * H * F
 
 
@@ -86,6 +94,19 @@ def int4_banks(copies, dev, seed0):
         for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
             q, s = synth.packed_int4_random(E, n, k, seed0 + 10 * c + i, dev)
             mats.append(B.bank_int4(q, s))
+        out.append(B.ffn(*mats))
+    return out
+
+
+def int4_variant_banks(copies, dev, seed0, fmt):
+    out = []
+    for c in range(copies):
+        mats = []
+        for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
+            q, s, z = synth.packed_int4_variant_random(E, n, k, seed0 + 10 * c + i, dev,
+                                                       group=32 if fmt == "int4-g32" else 128,
+                                                       asym=fmt == "int4-asym")
+            mats.append(B.bank_int4(q, s, z))
         out.append(B.ffn(*mats))
     return out
 
@@ -195,8 +216,7 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
         U = np.array([touched_experts(lg_cpu[i]) for i in range(steps)], dtype=np.float64)
     else:
         U = np.full(steps, float(torch.unique(ids).numel()))
-    gu_bytes, dn_bytes = ((INT4_GATEUP_BYTES, INT4_DOWN_BYTES) if fmt == "int4"
-                          else (NVFP4_GATEUP_BYTES, NVFP4_DOWN_BYTES))
+    gu_bytes, dn_bytes = EXPERT_BYTES[fmt]
     ms = wall / steps * 1e3
     r = dict(workload=name, tokens=T, ms_per_step=ms, tok_s=T / (ms * 1e-3),
              touched_experts=float(U.mean()),
@@ -368,7 +388,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "nvfp4", "nvfp4-csf", "stack"])
+                    choices=["decode", "prefill", "nvfp4", "nvfp4-csf", "int4-g32",
+                             "int4-asym", "stack"])
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -396,19 +417,21 @@ def main():
     int4 = int4_banks(2, dev, 500)
     jobs = []
     main_T = args.tokens or {"decode": 64, "prefill": 2048, "nvfp4": 256, "nvfp4-csf": 64,
-                             "stack": 4096}[args.workload]
+                             "int4-g32": 64, "int4-asym": 64, "stack": 4096}[args.workload]
     spec = {"decode": ("f16", "logits", "int4"), "prefill": ("bf16", "weights", "int4"),
             "nvfp4": ("bf16", "logits", "nvfp4"), "nvfp4-csf": ("bf16", "logits", "nvfp4"),
+            "int4-g32": ("f16", "logits", "int4-g32"), "int4-asym": ("f16", "logits", "int4-asym"),
             "stack": ("bf16", "weights", "int4")}
     jobs.append((args.workload, main_T))
     if not args.no_sweep:
         for wl, T in (("decode", 1), ("decode", 8), ("decode", 64), ("prefill", 2048),
-                      ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("stack", 32),
-                      ("stack", 4096)):
+                      ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("int4-g32", 64),
+                      ("int4-asym", 64), ("stack", 32), ("stack", 4096)):
             if (wl, T) != (args.workload, main_T):
                 jobs.append((wl, T))
     nv = None
     nv_csf = None
+    variants = {}
     stack = None
     results = []
     for wl, T in jobs:
@@ -422,7 +445,9 @@ def main():
         else:
             if fmt == "nvfp4" and nv is None:
                 nv = nvfp4_banks(2, dev, 900)
-            banks = int4 if fmt == "int4" else nv
+            if fmt in ("int4-g32", "int4-asym") and fmt not in variants:
+                variants[fmt] = int4_variant_banks(2, dev, 2000 if fmt == "int4-g32" else 2100, fmt)
+            banks = int4 if fmt == "int4" else (nv if fmt == "nvfp4" else variants.get(fmt))
             csf = None
             if wl == "nvfp4-csf":
                 if nv_csf is None:
@@ -443,8 +468,7 @@ def main():
                 peak=HBM_PEAK / 1e9, unit="GB/s", frac=round(head["gateup_frac_hbm"], 4),
                 traffic=traffic,
                 algorithmic_bytes_per_launch=round(head["touched_experts"] *
-                                                   (INT4_GATEUP_BYTES if fmt == "int4"
-                                                    else NVFP4_GATEUP_BYTES)))
+                                                   EXPERT_BYTES[fmt][0]))
     cpu = None if args.no_cpu_baseline else cpu_baseline(int4)
     line = {
         "metric": "W4A16 MoE layer tok/s; decode HBM GB/s %peak; prefill TFLOP/s %peak",

@@ -65,8 +65,25 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  * MOE_W_BF16 -- an unquantized bank (the shared expert stays BF16: page
  *   "NeuroSenko/Step-5-Preview-Int4-g128", "What stays in BF16").
  *   qweight: bf16 [E][n][k]; scale and global_scale NULL.
+ *
+ * MOE_W_INT4_G32 -- the same page, "Recipe" ("g32 with the same clip
+ *   search"): as MOE_W_INT4_G128 with one bf16 scale per 32 inputs.
+ *   scale:   bf16 [E][n][k/32].   weight = q * scale.
+ *
+ * MOE_W_INT4_G128_ASYM -- the same page, "Recipe" ("int4 g128,
+ *   asymmetric"): unsigned nibbles q in [0, 15] (nibble j of word w =
+ *   input 8w+j), one bf16 scale and one zero point per 128 inputs.
+ *   scale:   bf16 [E][n][k/128];  zero_point: uint8 [E][n][k/128], values
+ *   0..15.   weight = (q - zero_point) * scale.
+ *
+ * The decode kernels (the GEMV) serve every format; the prefill GEMM serves
+ * MOE_W_INT4_G128 and MOE_W_NVFP4_G16, and the other two formats run the
+ * GEMV at every batch size.
  */
-typedef enum { MOE_W_INT4_G128 = 1, MOE_W_NVFP4_G16 = 2, MOE_W_BF16 = 3 } moe_wfmt_t;
+typedef enum {
+    MOE_W_INT4_G128 = 1, MOE_W_NVFP4_G16 = 2, MOE_W_BF16 = 3,
+    MOE_W_INT4_G32 = 4, MOE_W_INT4_G128_ASYM = 5
+} moe_wfmt_t;
 
 /* One bank of E matrices, each [n out][k in]. Strides are in bytes; the
  * row strides must be multiples of 16 and the base pointers 16-byte
@@ -81,6 +98,8 @@ typedef struct {
     const float *global_scale;   /* NVFP4 only, else NULL                        */
     int64_t qweight_expert_stride, qweight_row_stride;
     int64_t scale_expert_stride, scale_row_stride;
+    const uint8_t *zero_point;   /* MOE_W_INT4_G128_ASYM only, else NULL          */
+    int64_t zero_point_expert_stride, zero_point_row_stride;
 } moe_weight_desc_t;
 
 /* The three projections of a SwiGLU bank: gate and up are [F][H], down is
@@ -113,7 +132,7 @@ typedef struct {
 /* Human-readable name of a status code (host, static storage). */
 const char *moe_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int moe_abi_version(void);
 
 /*
@@ -310,7 +329,7 @@ moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out,
  *                  experts only; 0 = E. A bound below the true count leaves
  *                  the experts past it unexpanded;
  *   out            U8  [E][R][C], 16-byte aligned, caller-owned.
- * All arrays are device memory; the call enqueues two kernels on `stream`.
+ * All arrays are device memory; the call enqueues one kernel on `stream`.
  * Limits: R and C positive multiples of 16, E <= 512, max_routed_experts >= 0
  * (MOE_ERR_INVALID_ARG), R*C < 2^24 (MOE_ERR_UNSUPPORTED): positions are
  * 24-bit.

@@ -15,7 +15,7 @@ _lib = None
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F16, MOE_BF16, MOE_F32 = 1, 2, 3
-MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16 = 1, 2, 3
+MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16, MOE_W_INT4_G32, MOE_W_INT4_G128_ASYM = 1, 2, 3, 4, 5
 
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_route_workspace",
            "moe_route_topk", "moe_permute_sizes",
@@ -39,7 +39,9 @@ class WeightDesc(ctypes.Structure):
                 ("qweight", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("global_scale", ctypes.c_void_p),
                 ("qweight_expert_stride", ctypes.c_int64), ("qweight_row_stride", ctypes.c_int64),
-                ("scale_expert_stride", ctypes.c_int64), ("scale_row_stride", ctypes.c_int64)]
+                ("scale_expert_stride", ctypes.c_int64), ("scale_row_stride", ctypes.c_int64),
+                ("zero_point", ctypes.c_void_p),
+                ("zero_point_expert_stride", ctypes.c_int64), ("zero_point_row_stride", ctypes.c_int64)]
 
 
 class FfnDesc(ctypes.Structure):
@@ -111,13 +113,25 @@ def _stream(device=None):
 
 
 # ------------------------------------------------------------ descriptors ---
-def bank_int4(qweight, scale):
-    """qweight int32 [E, n, k/8], scale bf16 [E, n, k/128] (device)."""
+def bank_int4(qweight, scale, zero_point=None):
+    """qweight int32 [E, n, k/8], scale bf16 [E, n, k/G] (device). G = 128 is
+    MOE_W_INT4_G128, G = 32 MOE_W_INT4_G32; with zero_point (uint8 [E, n,
+    k/128]) the nibbles are unsigned: MOE_W_INT4_G128_ASYM."""
     E, n, kw = qweight.shape
-    d = WeightDesc(MOE_W_INT4_G128, E, n, kw * 8, qweight.data_ptr(), scale.data_ptr(), None,
+    k = kw * 8
+    groups = scale.shape[2]
+    if zero_point is not None:
+        assert groups * 128 == k and zero_point.shape == (E, n, k // 128)
+        fmt = MOE_W_INT4_G128_ASYM
+    else:
+        assert groups * 128 == k or groups * 32 == k
+        fmt = MOE_W_INT4_G128 if groups * 128 == k else MOE_W_INT4_G32
+    zp = zero_point.data_ptr() if zero_point is not None else None
+    zs = (zero_point.stride(0), zero_point.stride(1)) if zero_point is not None else (0, 0)
+    d = WeightDesc(fmt, E, n, k, qweight.data_ptr(), scale.data_ptr(), None,
                    qweight.stride(0) * 4, qweight.stride(1) * 4,
-                   scale.stride(0) * 2, scale.stride(1) * 2)
-    d._keep = (qweight, scale)
+                   scale.stride(0) * 2, scale.stride(1) * 2, zp, zs[0], zs[1])
+    d._keep = (qweight, scale, zero_point)
     return d
 
 

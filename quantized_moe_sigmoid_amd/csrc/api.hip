@@ -67,9 +67,16 @@ moe_status_t check_bank(const moe_weight_desc_t &d, int E, int n, int k) {
         return MOE_ERR_INVALID_ARG;
     if (!aligned(d.scale, 2) || d.scale_row_stride % 2 || d.scale_expert_stride % 2)
         return MOE_ERR_INVALID_ARG;
-    if (d.fmt == MOE_W_INT4_G128) {
+    if (d.fmt == MOE_W_INT4_G128 || d.fmt == MOE_W_INT4_G128_ASYM) {
         if (k % 128) return MOE_ERR_INVALID_ARG;
         if (d.qweight_row_stride < k / 2 || d.scale_row_stride < (k / 128) * 2)
+            return MOE_ERR_INVALID_ARG;
+        if (d.fmt == MOE_W_INT4_G128_ASYM &&
+            (!d.zero_point || d.zero_point_row_stride < k / 128 || d.zero_point_expert_stride < 0))
+            return MOE_ERR_INVALID_ARG;
+    } else if (d.fmt == MOE_W_INT4_G32) {
+        if (k % 32) return MOE_ERR_INVALID_ARG;
+        if (d.qweight_row_stride < k / 2 || d.scale_row_stride < (k / 32) * 2)
             return MOE_ERR_INVALID_ARG;
     } else if (d.fmt == MOE_W_NVFP4_G16) {
         if (k % 16) return MOE_ERR_INVALID_ARG;
@@ -151,6 +158,8 @@ bool mfma_layout_ok(const moe_weight_desc_t &d) {
 
 bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
     const int E = ex.gate.num_experts, H = ex.gate.k, F = ex.gate.n;
+    // the GEMM decodes int4-g128 and NVFP4; the other formats run the GEMV
+    if (ex.gate.fmt != MOE_W_INT4_G128 && ex.gate.fmt != MOE_W_NVFP4_G16) return false;
     // 32-bit buffer offsets must reach every row of an expert matrix
     const bool fits = (int64_t)F * ex.gate.qweight_row_stride < INT32_MAX &&
                       (int64_t)F * ex.up.qweight_row_stride < INT32_MAX &&
@@ -200,7 +209,7 @@ const char *moe_status_string(int status) {
     }
 }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 static moe_status_t check_router(const void *x, int x_dtype, const float *wT, int T, int H,
                                  int E) {

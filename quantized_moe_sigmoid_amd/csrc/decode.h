@@ -5,6 +5,11 @@
 // layout"): int32 words along K, nibble j of a word = input 8w+j, a
 // two's-complement value in [-8, 7]; one bf16 scale per 128 inputs.
 //
+// int4-g32 and asymmetric int4-g128 (the same page, "Recipe": the error
+// table's variants): g32 has one bf16 scale per 32 inputs; the asymmetric
+// form holds unsigned nibbles q in [0, 15] with a zero point z per 128
+// inputs, weight = (q - z) * scale.
+//
 // NVFP4 (page "Step-5-Preview-NVFP4-Local", "Modifications" item 2,
 // "Format"): bytes of two E2M1 codes (low nibble = even input), one E4M3
 // block scale per 16 inputs, one float32 global scale per expert; value =
@@ -26,16 +31,33 @@ __device__ __forceinline__ int int4_q(uint32_t w, int j) {
 // or 128 (bf16, ulp 1) gives 1032 + q or 136 + q without any rounding.
 template <int ACT>
 struct Int4Bias;
+// kMagicValue: the bias of the unsigned form (no XOR), MAGIC + q.
 template <>
 struct Int4Bias<MOE_F16> {
     static constexpr uint32_t kMagic = 0x64006400u;   // fp16 1024.0 in each half
     static constexpr float kBias = 1032.0f;
+    static constexpr float kMagicValue = 1024.0f;
 };
 template <>
 struct Int4Bias<MOE_BF16> {
     static constexpr uint32_t kMagic = 0x43004300u;   // bf16 128.0 in each half
     static constexpr float kBias = 136.0f;
+    static constexpr float kMagicValue = 128.0f;
 };
+
+// The int4 family: nibble weights with bf16 scales.
+__host__ __device__ constexpr bool is_int4(int fmt) {
+    return fmt == MOE_W_INT4_G128 || fmt == MOE_W_INT4_G32 || fmt == MOE_W_INT4_G128_ASYM;
+}
+__host__ __device__ constexpr int int4_group(int fmt) { return fmt == MOE_W_INT4_G32 ? 32 : 128; }
+__host__ __device__ constexpr bool int4_asym(int fmt) { return fmt == MOE_W_INT4_G128_ASYM; }
+// The XOR key of the one-op pair decode ((w >> 4i) & 0x000F000F) ^ key: the
+// signed forms fold the XOR with 8 into the magic, the unsigned form takes
+// the nibble as it is (MAGIC + q).
+template <int ACT, int FMT>
+__host__ __device__ constexpr uint32_t int4_key() {
+    return int4_asym(FMT) ? Int4Bias<ACT>::kMagic : (Int4Bias<ACT>::kMagic | 0x00080008u);
+}
 
 template <int ACT>
 __device__ __forceinline__ void int4_biased_pairs(uint32_t w, uint32_t out[4]) {

@@ -1,31 +1,43 @@
 // Export of one expert's dequantized matrix as float32 [n][k].
 //
 // It runs the forward kernels' own decoders: int4 words go through the
-// biased fp16 pairs (1032 + q, then the bias is removed exactly) and the
-// scale is applied as one exact float32 product; NVFP4 bytes go through the
+// biased fp16 pairs (1032 + q for the signed forms, 1024 + q for the
+// unsigned one, then the bias, with the zero point, is removed exactly) and
+// the scale is applied as one exact float32 product; NVFP4 bytes go through the
 // hardware E2M1 pair conversion, the E4M3 scale multiplies exactly, and the
 // global scale is the single float32 rounding.
 #include "decode.h"
 
 namespace moe {
 
+// GS inputs per scale; ASYM: unsigned nibbles (1024 + q) and a zero point
+// per 128 inputs, subtracted with the bias: (1024 + q) - (1024 + z) = q - z.
+template <int GS, bool ASYM>
 __global__ void __launch_bounds__(256) dequant_int4_kernel(
     const uint8_t *__restrict__ qw, int64_t qrow, const uint8_t *__restrict__ sc, int64_t srow,
-    int n, int k, float *__restrict__ out) {
+    const uint8_t *__restrict__ zp, int64_t zrow, int n, int k, float *__restrict__ out) {
     const int words = k / 8;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)n * words) return;
     const int r = (int)(idx / words), j = (int)(idx % words);
     const uint32_t w = *(const uint32_t *)(qw + r * qrow + 4 * (int64_t)j);
-    const uint16_t sb = *(const uint16_t *)(sc + r * srow + 2 * (int64_t)((8 * j) / 128));
+    const uint16_t sb = *(const uint16_t *)(sc + r * srow + 2 * (int64_t)((8 * j) / GS));
     const float s = bf16_bits_to_f32(sb);
     uint32_t p[4];
-    int4_biased_pairs<MOE_F16>(w, p);
+    float bias;
+    if (ASYM) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = ((w >> (4 * i)) & 0x000F000Fu) | Int4Bias<MOE_F16>::kMagic;
+        bias = Int4Bias<MOE_F16>::kMagicValue + (float)zp[r * zrow + (8 * j) / 128];
+    } else {
+        int4_biased_pairs<MOE_F16>(w, p);
+        bias = Int4Bias<MOE_F16>::kBias;
+    }
     float v[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        v[i] = (f16_bits_to_f32(p[i] & 0xFFFF) - Int4Bias<MOE_F16>::kBias) * s;
-        v[i + 4] = (f16_bits_to_f32(p[i] >> 16) - Int4Bias<MOE_F16>::kBias) * s;
+        v[i] = (f16_bits_to_f32(p[i] & 0xFFFF) - bias) * s;
+        v[i + 4] = (f16_bits_to_f32(p[i] >> 16) - bias) * s;
     }
     float4 *o = (float4 *)(out + (int64_t)r * k + 8 * (int64_t)j);
     o[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -61,9 +73,18 @@ moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out,
     const uint8_t *sc = (const uint8_t *)d.scale + (int64_t)e * d.scale_expert_stride;
     const int64_t items = (int64_t)d.n * (d.k / 8);
     const dim3 grid((unsigned)((items + 255) / 256));
+    const uint8_t *zp = d.zero_point ? d.zero_point + (int64_t)e * d.zero_point_expert_stride
+                                     : nullptr;
     if (d.fmt == MOE_W_INT4_G128)
-        hipLaunchKernelGGL(dequant_int4_kernel, grid, dim3(256), 0, s, qw, d.qweight_row_stride,
-                           sc, d.scale_row_stride, d.n, d.k, out);
+        hipLaunchKernelGGL((dequant_int4_kernel<128, false>), grid, dim3(256), 0, s, qw,
+                           d.qweight_row_stride, sc, d.scale_row_stride, nullptr, 0, d.n, d.k, out);
+    else if (d.fmt == MOE_W_INT4_G32)
+        hipLaunchKernelGGL((dequant_int4_kernel<32, false>), grid, dim3(256), 0, s, qw,
+                           d.qweight_row_stride, sc, d.scale_row_stride, nullptr, 0, d.n, d.k, out);
+    else if (d.fmt == MOE_W_INT4_G128_ASYM)
+        hipLaunchKernelGGL((dequant_int4_kernel<128, true>), grid, dim3(256), 0, s, qw,
+                           d.qweight_row_stride, sc, d.scale_row_stride, zp,
+                           d.zero_point_row_stride, d.n, d.k, out);
     else
         hipLaunchKernelGGL(dequant_nvfp4_kernel, grid, dim3(256), 0, s, qw, d.qweight_row_stride,
                            sc, d.scale_row_stride, d.global_scale + e, d.n, d.k, out);

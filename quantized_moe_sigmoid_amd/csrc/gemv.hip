@@ -15,7 +15,9 @@
 //   dot2 accumulates sum (BIAS + q) x over a 32-input chunk, and the chunk's
 //   sum(x) (kept next to x in LDS) removes BIAS exactly in algebra:
 //   acc += s_g * (dot - BIAS * sum x). The bf16 scale s_g applies per chunk
-//   in float32 (every chunk lies inside one 128-input group).
+//   in float32 (every chunk lies inside one group: 128 inputs, or 32 for
+//   g32). The asymmetric form decodes MAGIC + q and removes MAGIC + z, its
+//   group's zero point: acc += s_g * (dot - (MAGIC + z) * sum x).
 // NVFP4: the hardware pair conversion gives exact E2M1 values; the E4M3
 //   block scale applies per 16 inputs in float32, the global scale once at
 //   the end.
@@ -33,6 +35,8 @@ struct GemvMat {                 // one projection bank, byte addressed
     const uint8_t *q, *s;
     const float *gs;             // NVFP4 global scale [E] or null
     int64_t qe, qr, se, sr;      // expert / row strides (bytes)
+    const uint8_t *z;            // asymmetric int4 zero points or null
+    int64_t ze, zr;
 };
 
 // LDS unit (16 bytes = 4 pair dwords) of input chunk c (32 inputs), word j.
@@ -49,14 +53,15 @@ __host__ __device__ __forceinline__ int xs_units_pad(int kin) {
 }
 
 // Partial dot products of one 16-byte weight chunk against token t's x.
-template <int ACT, int FMT>
+template <int ACT, int FMT, bool INT4 = is_int4(FMT)>
 struct ChunkDot;
 
-template <int ACT>
-struct ChunkDot<ACT, MOE_W_INT4_G128> {
+// The int4 family. kv = int4_key<ACT, FMT>() in a VGPR: each pair is then
+// one shift and one v_bitop3 ((w >> 4i) & 0x000F000F) ^ kv, the exact
+// 16-bit value BIAS + q (signed forms) or MAGIC + q (unsigned form).
+template <int ACT, int FMT>
+struct ChunkDot<ACT, FMT, true> {
     uint32_t p[16];
-    // kv = Int4Bias<ACT>::kMagic | 0x00080008 in a VGPR: each pair is then
-    // one shift and one v_bitop3 ((w >> 4i) & 0x000F000F) ^ kv
     __device__ __forceinline__ void decode(uint4 w, uint32_t kv) {
         const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -67,9 +72,10 @@ struct ChunkDot<ACT, MOE_W_INT4_G128> {
             p[4 * q + 3] = ((d[q] >> 12) & 0x000F000Fu) ^ kv;
         }
     }
-    // s2 = the chunk's scale(s): int4 uses one bf16 scale (as float).
+    // scale: the chunk's bf16 scale; bias: the 16-bit values' offset from
+    // q (signed forms), or from q - z (asymmetric: MAGIC + z).
     __device__ __forceinline__ float apply(const uint4 *xu, int stride_j, float xs_sum,
-                                           float scale, float, float acc) const {
+                                           float scale, float bias, float acc) const {
         float d = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -79,12 +85,12 @@ struct ChunkDot<ACT, MOE_W_INT4_G128> {
             d = dot2<ACT>(p[4 * j + 2], x.z, d);
             d = dot2<ACT>(p[4 * j + 3], x.w, d);
         }
-        return __builtin_fmaf(scale, d - Int4Bias<ACT>::kBias * xs_sum, acc);
+        return __builtin_fmaf(scale, d - bias * xs_sum, acc);
     }
 };
 
-template <int ACT>
-struct ChunkDot<ACT, MOE_W_NVFP4_G16> {
+template <int ACT, int FMT>
+struct ChunkDot<ACT, FMT, false> {
     uint32_t p[16];
     __device__ __forceinline__ void decode(uint4 w, uint32_t) {
         const uint32_t d[4] = {w.x, w.y, w.z, w.w};
@@ -113,21 +119,23 @@ struct ChunkDot<ACT, MOE_W_NVFP4_G16> {
 };
 
 // The two scale bytes of chunk c (32 inputs) of a row: int4, the bf16
-// scale of its 128-input group (one per 4 chunks); NVFP4, its two E4M3
-// block scales.
-template <int FMT>
-__device__ __forceinline__ void chunk_scales(uint32_t two, float &a, float &b) {
-    if (FMT == MOE_W_INT4_G128) {
+// scale of its group (one per 4 chunks at g128, one per chunk at g32) and
+// (asymmetric) its zero point z; NVFP4, its two E4M3 block scales.
+// For int4 the second output is the bias apply() removes.
+template <int ACT, int FMT>
+__device__ __forceinline__ void chunk_scales(uint32_t two, uint32_t z, float &a, float &b) {
+    if constexpr (is_int4(FMT)) {
         a = bf16_bits_to_f32(two);
-        b = 0.0f;
+        b = int4_asym(FMT) ? Int4Bias<ACT>::kMagicValue + (float)z : Int4Bias<ACT>::kBias;
     } else {
+        (void)z;
         a = e4m3_to_f32(two & 0xFF);
         b = e4m3_to_f32(two >> 8);
     }
 }
 template <int FMT>
 __device__ __forceinline__ int scale_offset(int c) {
-    return FMT == MOE_W_INT4_G128 ? 2 * (c >> 2) : 2 * c;
+    return is_int4(FMT) ? 2 * (c / (int4_group(FMT) / 32)) : 2 * c;
 }
 
 
@@ -201,7 +209,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
     const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(B.s + e * B.se, (int64_t)n_rows * B.sr);
     // per pass: byte offsets of the lane's row (rows past the matrix, never
     // stored, read its last row)
-    int qra[RPW], sra[RPW], qrb[RPW], srb[RPW];
+    int qra[RPW], sra[RPW], qrb[RPW], srb[RPW], zra[RPW], zrb[RPW];
 #pragma unroll
     for (int ps = 0; ps < RPW; ++ps) {
         const int r = row_of(ps) < n_rows ? row_of(ps) : n_rows - 1;
@@ -209,10 +217,17 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
         sra[ps] = r * (int)A.sr;
         qrb[ps] = r * (int)B.qr;
         srb[ps] = r * (int)B.sr;
+        zra[ps] = r * (int)A.zr;
+        zrb[ps] = r * (int)B.zr;
     }
-    const uint32_t kv = in_vgpr(FMT == MOE_W_INT4_G128 ? (Int4Bias<ACT>::kMagic | 0x00080008u) : 0u);
+    // asymmetric int4: one zero-point byte per 128 inputs, streamed with the scales
+    constexpr bool kZ = int4_asym(FMT);
+    const __amdgpu_buffer_rsrc_t rza = buffer_rsrc(kZ ? A.z + e * A.ze : A.q, (int64_t)n_rows * A.zr);
+    const __amdgpu_buffer_rsrc_t rzb = buffer_rsrc(kZ ? B.z + e * B.ze : B.q, (int64_t)n_rows * B.zr);
+    const uint32_t kv = in_vgpr(is_int4(FMT) ? int4_key<ACT, FMT>() : 0u);
     u32x4_t wa[kGemvRing], wb[kGemvRing];
     uint16_t sa[kGemvRing], sb[kGemvRing];
+    uint8_t za[kGemvRing], zb[kGemvRing];
     // iteration I = pass * nit + i streams chunk c = sub + LPR * i of the pass's row
     auto load = [&](int j, int I) {
         const int ps = NIT > 0 ? I / NIT : 0, i = NIT > 0 ? I % NIT : I;
@@ -223,11 +238,17 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
                                                    rqa, ok ? qra[pq] + 16 * c : kOutOfRange, 0, 0));
         sa[j] = __builtin_amdgcn_raw_buffer_load_b16(
             rsa, ok ? sra[pq] + scale_offset<FMT>(c) : kOutOfRange, 0, 0);
+        if constexpr (kZ)
+            za[j] = __builtin_amdgcn_raw_buffer_load_b8(rza, ok ? zra[pq] + (c >> 2) : kOutOfRange,
+                                                        0, 0);
         if (GATEUP) {
             wb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                        rqb, ok ? qrb[pq] + 16 * c : kOutOfRange, 0, 0));
             sb[j] = __builtin_amdgcn_raw_buffer_load_b16(
                 rsb, ok ? srb[pq] + scale_offset<FMT>(c) : kOutOfRange, 0, 0);
+            if constexpr (kZ)
+                zb[j] = __builtin_amdgcn_raw_buffer_load_b8(
+                    rzb, ok ? zrb[pq] + (c >> 2) : kOutOfRange, 0, 0);
         }
     };
 #pragma unroll
@@ -247,7 +268,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
     auto stage = [&](const u32x4_t &v, int g) {
         const bool valid = g < units;            // the 4 lanes of a chunk agree (units % 4 == 0)
         uint4 p;
-        if (FMT == MOE_W_INT4_G128) {            // pairs (i, i+4) of the 8 inputs
+        if (is_int4(FMT)) {                      // pairs (i, i+4) of the 8 inputs
             p.x = (v.x & 0xFFFFu) | (v.z << 16);
             p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
             p.z = (v.y & 0xFFFFu) | (v.w << 16);
@@ -256,7 +277,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
             p = make_uint4(v.x, v.y, v.z, v.w);
         }
         *(valid ? xs + wave * upad + xs_unit<LPR>(g >> 2, g & 3) : xdummy + lane) = p;
-        if (FMT == MOE_W_INT4_G128) {
+        if (is_int4(FMT)) {
             const uint32_t d[4] = {v.x, v.y, v.z, v.w};
             float sum = 0.0f;
 #pragma unroll
@@ -323,10 +344,10 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
             ChunkDot<ACT, FMT> da, db;
             da.decode(make_uint4(wa[j].x, wa[j].y, wa[j].z, wa[j].w), kv);
             float a0, a1, b0 = 0.0f, b1 = 0.0f;
-            chunk_scales<FMT>(sa[j], a0, a1);
+            chunk_scales<ACT, FMT>(sa[j], kZ ? za[j] : 0u, a0, a1);
             if (GATEUP) {
                 db.decode(make_uint4(wb[j].x, wb[j].y, wb[j].z, wb[j].w), kv);
-                chunk_scales<FMT>(sb[j], b0, b1);
+                chunk_scales<ACT, FMT>(sb[j], kZ ? zb[j] : 0u, b0, b1);
             }
             // slot j is consumed: refill it in place (the barrier keeps the
             // refill below the last use, so it reuses the same registers)
@@ -338,7 +359,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
                 for (int t = 0; t < TM; ++t) {
                     if (t < m) {
                         const uint4 *xu = xs + t * upad + u0;
-                        const float xsm = FMT == MOE_W_INT4_G128 ? xsum[t * nch + c] : 0.0f;
+                        const float xsm = is_int4(FMT) ? xsum[t * nch + c] : 0.0f;
                         acc_a[t] = da.apply(xu, LPR, xsm, a0, a1, acc_a[t]);
                         if (GATEUP) acc_b[t] = db.apply(xu, LPR, xsm, b0, b1, acc_b[t]);
                     }
@@ -362,7 +383,8 @@ constexpr int kGemvTM = 4;
 inline GemvMat gemv_mat(const moe_weight_desc_t &d) {
     return GemvMat{(const uint8_t *)d.qweight, (const uint8_t *)d.scale, d.global_scale,
                    d.qweight_expert_stride, d.qweight_row_stride, d.scale_expert_stride,
-                   d.scale_row_stride};
+                   d.scale_row_stride, d.zero_point, d.zero_point_expert_stride,
+                   d.zero_point_row_stride};
 }
 
 // Activation units, chunk sums (rounded up to 16 bytes) and the staging
@@ -429,12 +451,25 @@ moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int ac
                                  hipStream_t s, const std::function<moe_status_t(int)> &mark) {
     const uint16_t *xx = (const uint16_t *)x;
     uint16_t *hh = (uint16_t *)h;
-    const bool nv = ex.gate.fmt == MOE_W_NVFP4_G16;
-    if (act == MOE_BF16)
-        return nv ? gemv_forward_t<MOE_BF16, MOE_W_NVFP4_G16>(ex, xx, K, p, max_tiles, hh, y, s, mark)
-                  : gemv_forward_t<MOE_BF16, MOE_W_INT4_G128>(ex, xx, K, p, max_tiles, hh, y, s, mark);
-    return nv ? gemv_forward_t<MOE_F16, MOE_W_NVFP4_G16>(ex, xx, K, p, max_tiles, hh, y, s, mark)
-              : gemv_forward_t<MOE_F16, MOE_W_INT4_G128>(ex, xx, K, p, max_tiles, hh, y, s, mark);
+#define MOE_GEMV_FMT(A, F)                                                               \
+    case F: return gemv_forward_t<A, F>(ex, xx, K, p, max_tiles, hh, y, s, mark)
+    if (act == MOE_BF16) {
+        switch (ex.gate.fmt) {
+            MOE_GEMV_FMT(MOE_BF16, MOE_W_INT4_G128);
+            MOE_GEMV_FMT(MOE_BF16, MOE_W_NVFP4_G16);
+            MOE_GEMV_FMT(MOE_BF16, MOE_W_INT4_G32);
+            MOE_GEMV_FMT(MOE_BF16, MOE_W_INT4_G128_ASYM);
+        }
+    } else {
+        switch (ex.gate.fmt) {
+            MOE_GEMV_FMT(MOE_F16, MOE_W_INT4_G128);
+            MOE_GEMV_FMT(MOE_F16, MOE_W_NVFP4_G16);
+            MOE_GEMV_FMT(MOE_F16, MOE_W_INT4_G32);
+            MOE_GEMV_FMT(MOE_F16, MOE_W_INT4_G128_ASYM);
+        }
+    }
+#undef MOE_GEMV_FMT
+    return MOE_ERR_UNSUPPORTED;
 }
 
 }  // namespace moe

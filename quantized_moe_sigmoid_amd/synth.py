@@ -118,6 +118,23 @@ def packed_int4_random(E, n, k, seed, device, scale_mean=0.0043):
     return q, s.to(torch.bfloat16)
 
 
+def packed_int4_variant_random(E, n, k, seed, device, group=128, asym=False, scale_mean=0.0043):
+    """Random int4-g32 (group=32) or asymmetric int4-g128 (asym=True) bank
+    in packed form: uniform 32-bit words, bf16 scales scale_mean * (1 + 0.1
+    N(0, 1)) per group and, for the asymmetric form, zero points uniform in
+    [0, 15] (uint8 [E, n, k/128]). Returns (words, scales, zero points or
+    None)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    q = torch.randint(-2 ** 31, 2 ** 31 - 1, (E, n, k // 8), generator=g, device=device,
+                      dtype=torch.int32)
+    s = (torch.randn((E, n, k // group), generator=g, device=device) * 0.1 + 1.0) * scale_mean
+    z = (torch.randint(0, 16, (E, n, k // 128), generator=g, device=device, dtype=torch.uint8)
+         if asym else None)
+    return q, s.to(torch.bfloat16), z
+
+
 def csf_random(E, R, C, seed, device, rate=0.002):
     """Random CSF tensors of an NVFP4 scale tensor [E, R, C]: row bases
     uniform in [0x60, 0x6F], uniform 4-bit codes, and per expert about

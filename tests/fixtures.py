@@ -143,3 +143,46 @@ class HipEvents:
 
     def destroy(self, e):
         self.L.hipEventDestroy(self.c.c_void_p(e))
+
+
+def int4_variant_bank_oracle(E, n, k, root, layer, which, fmt):
+    """Gaussian bf16 weights quantized by the oracle as int4-g32 or asymmetric
+    int4-g128 and packed. Returns (words int32 [E, n, k/8], bf16 scale bits
+    uint16 [E, n, k/G], zero points uint8 [E, n, k/128] or None)."""
+    g = 32 if fmt == B.MOE_W_INT4_G32 else 128
+    q = np.empty((E, n, k // 8), dtype=np.int32)
+    s = np.empty((E, n, k // g), dtype=np.uint16)
+    z = np.empty((E, n, k // 128), dtype=np.uint8) if fmt == B.MOE_W_INT4_G128_ASYM else None
+    for e in range(E):
+        W = synth.expert_weight_bf16(n, k, root, layer, TENSOR_OF[which], e)
+        W = W.float().numpy().astype(np.float64)
+        if z is None:
+            qq, ss = OQ.quantize_int4(W, group=32)
+            q[e] = OQ.pack_int4(qq)
+        else:
+            qq, ss, zz = OQ.quantize_int4_asym(W)
+            q[e] = OQ.pack_uint4(qq)
+            z[e] = zz
+        s[e] = OF.bf16_bits(ss)
+    return q, s, z
+
+
+def int4_variant_to_device(q, s_bits, z, device="cuda"):
+    qt, st = int4_to_device(q, s_bits, device)
+    zt = torch.from_numpy(np.ascontiguousarray(z)).to(device) if z is not None else None
+    return qt, st, zt
+
+
+def oracle_int4_variant_expert(q, s_bits, z, e):
+    """Exact float64 dequantized expert e of an int4-g32 or asymmetric bank
+    (host arrays or device tensors)."""
+    if isinstance(q, torch.Tensor):
+        q = q[e].cpu().numpy()
+        s_bits = s_bits[e].view(torch.int16).cpu().numpy().view(np.uint16)
+        z = z[e].cpu().numpy() if z is not None else None
+    else:
+        q, s_bits = q[e], s_bits[e]
+        z = z[e] if z is not None else None
+    if z is not None:
+        return OQ.dequant_int4_asym(q, s_bits, z)
+    return OQ.dequant_int4(q, s_bits, group=32)

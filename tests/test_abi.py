@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert B.status_string(0) == "MOE_OK"
     assert B.status_string(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
     assert B.status_string(99) == "MOE_ERR_UNKNOWN"
@@ -291,3 +291,45 @@ def test_csf_expand_validation(L):
     ]
     for args, want in bad:
         assert F(*args) == want, args
+
+
+def _bank_v(fmt, E, n, k, srow=None, zrow=None, zp=True):
+    """An int4-g32 or asymmetric int4-g128 bank descriptor (fake pointers)."""
+    g = 32 if fmt == B.MOE_W_INT4_G32 else 128
+    qr, sr = k // 2, srow if srow is not None else (k // g) * 2
+    zr = zrow if zrow is not None else k // 128
+    z = FAKE if (fmt == B.MOE_W_INT4_G128_ASYM and zp) else None
+    return B.WeightDesc(fmt, E, n, k, FAKE, FAKE, None, qr * n, qr, sr * n, sr,
+                        z, zr * n if z else 0, zr if z else 0)
+
+
+@pytest.mark.parametrize("fmt", [B.MOE_W_INT4_G32, B.MOE_W_INT4_G128_ASYM])
+def test_int4_variant_banks_plan_the_decode_kernels(L, fmt):
+    """Both variants are accepted and, even at prefill size, planned on the
+    GEMV tile (the GEMM decodes int4-g128 and NVFP4 only)."""
+    f = B.FfnDesc(_bank_v(fmt, 352, 1536, 4096), _bank_v(fmt, 352, 1536, 4096),
+                  _bank_v(fmt, 352, 4096, 1536))
+    st, tm_small, _ = _plan(f, T=8)
+    assert st == B.MOE_OK
+    st, tm_big, _ = _plan(f, T=2048)
+    assert st == B.MOE_OK and tm_big == tm_small
+    st, tm_g128, _ = _plan(_ffn(), T=2048)
+    assert tm_g128 != tm_big
+
+
+def test_int4_variant_bank_errors(L):
+    G32, ASYM = B.MOE_W_INT4_G32, B.MOE_W_INT4_G128_ASYM
+    bad = [
+        _bank_v(ASYM, 352, 1536, 4096, zp=False),            # no zero points
+        _bank_v(ASYM, 352, 1536, 4096, zrow=31),             # zero-point rows too short
+        _bank_v(G32, 352, 1536, 4096, srow=(4096 // 128) * 2),   # g128-sized scale rows
+    ]
+    for g in bad:
+        f = B.FfnDesc(g, _bank_v(g.fmt, 352, 1536, 4096), _bank_v(g.fmt, 352, 4096, 1536))
+        assert _plan(f)[0] == B.MOE_ERR_INVALID_ARG
+    # g32 needs k % 32; the variant formats mixed with another format are refused
+    f = B.FfnDesc(_bank_v(G32, 4, 64, 48), _bank_v(G32, 4, 64, 48), _bank_v(G32, 4, 48, 64))
+    assert _plan(f)[0] == B.MOE_ERR_INVALID_ARG
+    f = B.FfnDesc(_bank_v(G32, 352, 1536, 4096), _bank(B.MOE_W_INT4_G128, 352, 1536, 4096),
+                  _bank_v(G32, 352, 4096, 1536))
+    assert _plan(f)[0] == B.MOE_ERR_INVALID_ARG
