@@ -117,6 +117,7 @@ def test_route_from_router_weight_tiny(dev, act):
 
 
 @pytest.mark.parametrize("T,Hh,Ee,act", [(37, 4096, 352, "bf16"), (2048, 4096, 352, "bf16"),
+                                         (4099, 4096, 352, "bf16"),
                                          (8, 256, 16, "f16"), (70, 192, 20, "f16")])
 def test_router_logits_bitwise(dev, T, Hh, Ee, act):
     """The canonical float32 fma chain, bit for bit against the C oracle

@@ -1,5 +1,6 @@
 """Pins of the oracle's int4 (g128, g32, asymmetric), int8 and NVFP4 quantizers,
 packing and dequant.
+
 Pinned against the pages' printed figures (tests/golden/page_figures.json),
 exhaustive enumeration, exactly-representable special cases and invariants.
 """
