@@ -17,7 +17,7 @@ event drains the stream); the other stages' durations come from a separate,
 untimed pass over the same inputs with every stage boundary recorded.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--workload decode|prefill|nvfp4|nvfp4-csf|int4-g32|int4-asym|stack]
+                  [--workload decode|prefill|nvfp4|nvfp4-csf|int4-g32|int4-asym|int8|stack]
                   [--tokens T] [--no-sweep] [--no-cpu-baseline]
 """
 import argparse
@@ -50,10 +50,13 @@ INT4_G32_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 32) * 2)
 INT4_G32_DOWN_BYTES = H * F // 2 + H * (F // 32) * 2
 INT4_ASYM_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 128) * 3)      # + one zero-point byte
 INT4_ASYM_DOWN_BYTES = H * F // 2 + H * (F // 128) * 3
+INT8_GATEUP_BYTES = 2 * (F * H + F * (H // 128) * 2)
+INT8_DOWN_BYTES = H * F + H * (F // 128) * 2
 EXPERT_BYTES = {"int4": (INT4_GATEUP_BYTES, INT4_DOWN_BYTES),
                 "nvfp4": (NVFP4_GATEUP_BYTES, NVFP4_DOWN_BYTES),
                 "int4-g32": (INT4_G32_GATEUP_BYTES, INT4_G32_DOWN_BYTES),
-                "int4-asym": (INT4_ASYM_GATEUP_BYTES, INT4_ASYM_DOWN_BYTES)}
+                "int4-asym": (INT4_ASYM_GATEUP_BYTES, INT4_ASYM_DOWN_BYTES),
+                "int8": (INT8_GATEUP_BYTES, INT8_DOWN_BYTES)}
 FLOP_PER_SLOT = 3 * 2 * H * F
 
 
@@ -98,11 +101,14 @@ def int4_banks(copies, dev, seed0):
     return out
 
 
-def int4_variant_banks(copies, dev, seed0, fmt):
+def variant_banks(copies, dev, seed0, fmt):
     out = []
     for c in range(copies):
         mats = []
         for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
+            if fmt == "int8":
+                mats.append(B.bank_int8(*synth.int8_random(E, n, k, seed0 + 10 * c + i, dev)))
+                continue
             q, s, z = synth.packed_int4_variant_random(E, n, k, seed0 + 10 * c + i, dev,
                                                        group=32 if fmt == "int4-g32" else 128,
                                                        asym=fmt == "int4-asym")
@@ -389,7 +395,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "nvfp4", "nvfp4-csf", "int4-g32",
-                             "int4-asym", "stack"])
+                             "int4-asym", "int8", "stack"])
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -417,16 +423,18 @@ def main():
     int4 = int4_banks(2, dev, 500)
     jobs = []
     main_T = args.tokens or {"decode": 64, "prefill": 2048, "nvfp4": 256, "nvfp4-csf": 64,
-                             "int4-g32": 64, "int4-asym": 64, "stack": 4096}[args.workload]
+                             "int4-g32": 64, "int4-asym": 64, "int8": 64,
+                             "stack": 4096}[args.workload]
     spec = {"decode": ("f16", "logits", "int4"), "prefill": ("bf16", "weights", "int4"),
             "nvfp4": ("bf16", "logits", "nvfp4"), "nvfp4-csf": ("bf16", "logits", "nvfp4"),
             "int4-g32": ("f16", "logits", "int4-g32"), "int4-asym": ("f16", "logits", "int4-asym"),
+            "int8": ("f16", "logits", "int8"),
             "stack": ("bf16", "weights", "int4")}
     jobs.append((args.workload, main_T))
     if not args.no_sweep:
         for wl, T in (("decode", 1), ("decode", 8), ("decode", 64), ("prefill", 2048),
                       ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("int4-g32", 64),
-                      ("int4-asym", 64), ("stack", 32), ("stack", 4096)):
+                      ("int4-asym", 64), ("int8", 64), ("stack", 32), ("stack", 4096)):
             if (wl, T) != (args.workload, main_T):
                 jobs.append((wl, T))
     nv = None
@@ -445,8 +453,9 @@ def main():
         else:
             if fmt == "nvfp4" and nv is None:
                 nv = nvfp4_banks(2, dev, 900)
-            if fmt in ("int4-g32", "int4-asym") and fmt not in variants:
-                variants[fmt] = int4_variant_banks(2, dev, 2000 if fmt == "int4-g32" else 2100, fmt)
+            if fmt in ("int4-g32", "int4-asym", "int8") and fmt not in variants:
+                variants[fmt] = variant_banks(
+                    2, dev, {"int4-g32": 2000, "int4-asym": 2100, "int8": 2200}[fmt], fmt)
             banks = int4 if fmt == "int4" else (nv if fmt == "nvfp4" else variants.get(fmt))
             csf = None
             if wl == "nvfp4-csf":

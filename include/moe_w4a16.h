@@ -76,13 +76,18 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  *   scale:   bf16 [E][n][k/128];  zero_point: uint8 [E][n][k/128], values
  *   0..15.   weight = (q - zero_point) * scale.
  *
+ * MOE_W_INT8_G128 -- the same page, "Recipe" (the "int8 experts" it
+ *   compares against): symmetric int8 with one bf16 scale per 128 inputs.
+ *   qweight: int8 [E][n][k], two's complement, input j at byte j.
+ *   scale:   bf16 [E][n][k/128].   weight = q * scale.
+ *
  * The decode kernels (the GEMV) serve every format; the prefill GEMM serves
- * MOE_W_INT4_G128 and MOE_W_NVFP4_G16, and the other two formats run the
- * GEMV at every batch size.
+ * MOE_W_INT4_G128 and MOE_W_NVFP4_G16, and the other formats run the GEMV
+ * at every batch size.
  */
 typedef enum {
     MOE_W_INT4_G128 = 1, MOE_W_NVFP4_G16 = 2, MOE_W_BF16 = 3,
-    MOE_W_INT4_G32 = 4, MOE_W_INT4_G128_ASYM = 5
+    MOE_W_INT4_G32 = 4, MOE_W_INT4_G128_ASYM = 5, MOE_W_INT8_G128 = 6
 } moe_wfmt_t;
 
 /* One bank of E matrices, each [n out][k in]. Strides are in bytes; the

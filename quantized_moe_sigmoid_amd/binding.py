@@ -16,6 +16,7 @@ _lib = None
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F16, MOE_BF16, MOE_F32 = 1, 2, 3
 MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16, MOE_W_INT4_G32, MOE_W_INT4_G128_ASYM = 1, 2, 3, 4, 5
+MOE_W_INT8_G128 = 6
 
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_route_workspace",
            "moe_route_topk", "moe_permute_sizes",
@@ -132,6 +133,16 @@ def bank_int4(qweight, scale, zero_point=None):
                    qweight.stride(0) * 4, qweight.stride(1) * 4,
                    scale.stride(0) * 2, scale.stride(1) * 2, zp, zs[0], zs[1])
     d._keep = (qweight, scale, zero_point)
+    return d
+
+
+def bank_int8(qweight, scale):
+    """qweight int8 [E, n, k], scale bf16 [E, n, k/128] (device): MOE_W_INT8_G128."""
+    E, n, k = qweight.shape
+    assert qweight.dtype == torch.int8 and scale.shape == (E, n, k // 128)
+    d = WeightDesc(MOE_W_INT8_G128, E, n, k, qweight.data_ptr(), scale.data_ptr(), None,
+                   qweight.stride(0), qweight.stride(1), scale.stride(0) * 2, scale.stride(1) * 2)
+    d._keep = (qweight, scale)
     return d
 
 

@@ -74,6 +74,10 @@ moe_status_t check_bank(const moe_weight_desc_t &d, int E, int n, int k) {
         if (d.fmt == MOE_W_INT4_G128_ASYM &&
             (!d.zero_point || d.zero_point_row_stride < k / 128 || d.zero_point_expert_stride < 0))
             return MOE_ERR_INVALID_ARG;
+    } else if (d.fmt == MOE_W_INT8_G128) {
+        if (k % 128) return MOE_ERR_INVALID_ARG;
+        if (d.qweight_row_stride < k || d.scale_row_stride < (k / 128) * 2)
+            return MOE_ERR_INVALID_ARG;
     } else if (d.fmt == MOE_W_INT4_G32) {
         if (k % 32) return MOE_ERR_INVALID_ARG;
         if (d.qweight_row_stride < k / 2 || d.scale_row_stride < (k / 32) * 2)

@@ -10,6 +10,9 @@
 // form holds unsigned nibbles q in [0, 15] with a zero point z per 128
 // inputs, weight = (q - z) * scale.
 //
+// int8-g128 (the same page, "Recipe": its "int8 experts" comparison):
+// two's-complement bytes, input j at byte j, one bf16 scale per 128 inputs.
+//
 // NVFP4 (page "Step-5-Preview-NVFP4-Local", "Modifications" item 2,
 // "Format"): bytes of two E2M1 codes (low nibble = even input), one E4M3
 // block scale per 16 inputs, one float32 global scale per expert; value =
@@ -80,6 +83,41 @@ __device__ __forceinline__ void int4_biased_pairs_masked(uint32_t w, uint32_t m,
     out[1] = ((w >> 4) & m) ^ K;
     out[2] = ((w >> 8) & m) ^ K;
     out[3] = ((w >> 12) & m) ^ K;
+}
+
+// ---- int8 -------------------------------------------------------------------
+__host__ __device__ constexpr bool is_int8(int fmt) { return fmt == MOE_W_INT8_G128; }
+// Inputs per 16-byte weight chunk: 32 for the 4-bit formats, 16 for int8.
+__host__ __device__ constexpr int chunk_inputs(int fmt) { return is_int8(fmt) ? 16 : 32; }
+
+// The bias of the decoded int8 pairs: u = q + 128 (the byte XOR 0x80) sits
+// in the low mantissa byte of fp16 1024.0 (ulp 1 on [1024, 2048)), so the
+// fp16 value is 1152 + q; bf16 has no binade with 8 mantissa bits of ulp 1,
+// so there the pair holds u itself (128 + q), converted through float32.
+template <int ACT>
+struct Int8Bias;
+template <>
+struct Int8Bias<MOE_F16> {
+    static constexpr float kBias = 1152.0f;
+};
+template <>
+struct Int8Bias<MOE_BF16> {
+    static constexpr float kBias = 128.0f;
+};
+
+// Inputs (2 SEL, 2 SEL + 1) of a word whose bytes are already XOR 0x80 as
+// an exact 16-bit pair (element 0 = the even input). fp16: one byte
+// permute with the constant 0x64 bytes. bf16: u has at most 8 significant
+// bits, so the upper half of its float32 is exactly its bf16.
+template <int ACT, int SEL>
+__device__ __forceinline__ uint32_t int8_pair(uint32_t u) {
+    if constexpr (ACT == MOE_F16) {
+        return __builtin_amdgcn_perm(0x64646464u, u, SEL ? 0x04030402u : 0x04010400u);
+    } else {
+        const float lo = (float)((u >> (16 * SEL)) & 0xFFu);
+        const float hi = (float)((u >> (16 * SEL + 8)) & 0xFFu);
+        return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+    }
 }
 
 // A value the compiler cannot see through, held in a VGPR. gfx950 VOP3

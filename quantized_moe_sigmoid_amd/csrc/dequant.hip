@@ -3,7 +3,8 @@
 // It runs the forward kernels' own decoders: int4 words go through the
 // biased fp16 pairs (1032 + q for the signed forms, 1024 + q for the
 // unsigned one, then the bias, with the zero point, is removed exactly) and
-// the scale is applied as one exact float32 product; NVFP4 bytes go through the
+// the scale is applied as one exact float32 product; int8 bytes go through
+// the fp16 pairs 1152 + q the same way; NVFP4 bytes go through the
 // hardware E2M1 pair conversion, the E4M3 scale multiplies exactly, and the
 // global scale is the single float32 rounding.
 #include "decode.h"
@@ -38,6 +39,32 @@ __global__ void __launch_bounds__(256) dequant_int4_kernel(
     for (int i = 0; i < 4; ++i) {
         v[i] = (f16_bits_to_f32(p[i] & 0xFFFF) - bias) * s;
         v[i + 4] = (f16_bits_to_f32(p[i] >> 16) - bias) * s;
+    }
+    float4 *o = (float4 *)(out + (int64_t)r * k + 8 * (int64_t)j);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// 8 inputs per thread: (1152 + q) - 1152 = q exactly, times the bf16 scale
+// (at most 8 + 8 significant bits: exact in float32).
+__global__ void __launch_bounds__(256) dequant_int8_kernel(
+    const uint8_t *__restrict__ qw, int64_t qrow, const uint8_t *__restrict__ sc, int64_t srow,
+    int n, int k, float *__restrict__ out) {
+    const int items = k / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)n * items) return;
+    const int r = (int)(idx / items), j = (int)(idx % items);
+    const uint2 w = *(const uint2 *)(qw + r * qrow + 8 * (int64_t)j);
+    const float s = bf16_bits_to_f32(*(const uint16_t *)(sc + r * srow + 2 * (int64_t)(j / 16)));
+    const uint32_t d[2] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u};
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const uint32_t p0 = int8_pair<MOE_F16, 0>(d[q]), p1 = int8_pair<MOE_F16, 1>(d[q]);
+        v[4 * q + 0] = (f16_bits_to_f32(p0 & 0xFFFF) - Int8Bias<MOE_F16>::kBias) * s;
+        v[4 * q + 1] = (f16_bits_to_f32(p0 >> 16) - Int8Bias<MOE_F16>::kBias) * s;
+        v[4 * q + 2] = (f16_bits_to_f32(p1 & 0xFFFF) - Int8Bias<MOE_F16>::kBias) * s;
+        v[4 * q + 3] = (f16_bits_to_f32(p1 >> 16) - Int8Bias<MOE_F16>::kBias) * s;
     }
     float4 *o = (float4 *)(out + (int64_t)r * k + 8 * (int64_t)j);
     o[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -85,6 +112,9 @@ moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out,
         hipLaunchKernelGGL((dequant_int4_kernel<128, true>), grid, dim3(256), 0, s, qw,
                            d.qweight_row_stride, sc, d.scale_row_stride, zp,
                            d.zero_point_row_stride, d.n, d.k, out);
+    else if (d.fmt == MOE_W_INT8_G128)
+        hipLaunchKernelGGL(dequant_int8_kernel, grid, dim3(256), 0, s, qw, d.qweight_row_stride,
+                           sc, d.scale_row_stride, d.n, d.k, out);
     else
         hipLaunchKernelGGL(dequant_nvfp4_kernel, grid, dim3(256), 0, s, qw, d.qweight_row_stride,
                            sc, d.scale_row_stride, d.global_scale + e, d.n, d.k, out);

@@ -18,6 +18,9 @@
 //   in float32 (every chunk lies inside one group: 128 inputs, or 32 for
 //   g32). The asymmetric form decodes MAGIC + q and removes MAGIC + z, its
 //   group's zero point: acc += s_g * (dot - (MAGIC + z) * sum x).
+// int8: a 16-byte chunk holds 16 inputs; each byte pair becomes the exact
+//   16-bit pair BIAS + q (decode.h) and the chunk's sum(x) removes BIAS the
+//   same way: acc += s_g * (dot - BIAS * sum x).
 // NVFP4: the hardware pair conversion gives exact E2M1 values; the E4M3
 //   block scale applies per 16 inputs in float32, the global scale once at
 //   the end.
@@ -39,28 +42,30 @@ struct GemvMat {                 // one projection bank, byte addressed
     int64_t ze, zr;
 };
 
-// LDS unit (16 bytes = 4 pair dwords) of input chunk c (32 inputs), word j.
-// For a fixed j the LPR chunks read together by one row's lanes are 16-byte
-// neighbours, so one wave-wide 16-byte read touches all banks once.
-template <int LPR>
+// LDS unit (16 bytes = 4 pair dwords = 8 inputs) j of input chunk c (UPC
+// units: 4 for 32-input chunks, 2 for int8's 16). For a fixed j the LPR
+// chunks read together by one row's lanes are 16-byte neighbours, so one
+// wave-wide 16-byte read touches all banks once.
+template <int LPR, int UPC>
 __device__ __forceinline__ int xs_unit(int c, int j) {
-    return ((c / LPR) * 4 + j) * LPR + (c % LPR);
+    return ((c / LPR) * UPC + j) * LPR + (c % LPR);
 }
 // LDS units per token row: chunks rounded up to a multiple of LPR.
-template <int LPR>
+template <int LPR, int CI>
 __host__ __device__ __forceinline__ int xs_units_pad(int kin) {
-    return (kin / 32 + LPR - 1) / LPR * LPR * 4;
+    return (kin / CI + LPR - 1) / LPR * LPR * (CI / 8);
 }
 
 // Partial dot products of one 16-byte weight chunk against token t's x.
-template <int ACT, int FMT, bool INT4 = is_int4(FMT)>
+// KIND: 0 NVFP4, 1 the int4 family, 2 int8.
+template <int ACT, int FMT, int KIND = is_int4(FMT) ? 1 : is_int8(FMT) ? 2 : 0>
 struct ChunkDot;
 
 // The int4 family. kv = int4_key<ACT, FMT>() in a VGPR: each pair is then
 // one shift and one v_bitop3 ((w >> 4i) & 0x000F000F) ^ kv, the exact
 // 16-bit value BIAS + q (signed forms) or MAGIC + q (unsigned form).
 template <int ACT, int FMT>
-struct ChunkDot<ACT, FMT, true> {
+struct ChunkDot<ACT, FMT, 1> {
     uint32_t p[16];
     __device__ __forceinline__ void decode(uint4 w, uint32_t kv) {
         const uint32_t d[4] = {w.x, w.y, w.z, w.w};
@@ -89,8 +94,36 @@ struct ChunkDot<ACT, FMT, true> {
     }
 };
 
+// int8: 16 inputs, natural pair order (2i, 2i+1), two LDS units.
 template <int ACT, int FMT>
-struct ChunkDot<ACT, FMT, false> {
+struct ChunkDot<ACT, FMT, 2> {
+    uint32_t p[8];
+    __device__ __forceinline__ void decode(uint4 w, uint32_t) {
+        const uint32_t d[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u,
+                               w.w ^ 0x80808080u};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            p[2 * q + 0] = int8_pair<ACT, 0>(d[q]);
+            p[2 * q + 1] = int8_pair<ACT, 1>(d[q]);
+        }
+    }
+    __device__ __forceinline__ float apply(const uint4 *xu, int stride_j, float xs_sum,
+                                           float scale, float bias, float acc) const {
+        float d = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint4 x = xu[j * stride_j];
+            d = dot2<ACT>(p[4 * j + 0], x.x, d);
+            d = dot2<ACT>(p[4 * j + 1], x.y, d);
+            d = dot2<ACT>(p[4 * j + 2], x.z, d);
+            d = dot2<ACT>(p[4 * j + 3], x.w, d);
+        }
+        return __builtin_fmaf(scale, d - bias * xs_sum, acc);
+    }
+};
+
+template <int ACT, int FMT>
+struct ChunkDot<ACT, FMT, 0> {
     uint32_t p[16];
     __device__ __forceinline__ void decode(uint4 w, uint32_t) {
         const uint32_t d[4] = {w.x, w.y, w.z, w.w};
@@ -118,15 +151,20 @@ struct ChunkDot<ACT, FMT, false> {
     }
 };
 
-// The two scale bytes of chunk c (32 inputs) of a row: int4, the bf16
-// scale of its group (one per 4 chunks at g128, one per chunk at g32) and
-// (asymmetric) its zero point z; NVFP4, its two E4M3 block scales.
-// For int4 the second output is the bias apply() removes.
+// The two scale bytes of chunk c of a row: int4, the bf16 scale of its
+// group (one per 4 chunks at g128, one per chunk at g32) and (asymmetric)
+// its zero point z; int8, the bf16 scale of its group (one per 8 chunks);
+// NVFP4, its two E4M3 block scales. For the integer formats the second
+// output is the bias apply() removes.
 template <int ACT, int FMT>
 __device__ __forceinline__ void chunk_scales(uint32_t two, uint32_t z, float &a, float &b) {
     if constexpr (is_int4(FMT)) {
         a = bf16_bits_to_f32(two);
         b = int4_asym(FMT) ? Int4Bias<ACT>::kMagicValue + (float)z : Int4Bias<ACT>::kBias;
+    } else if constexpr (is_int8(FMT)) {
+        (void)z;
+        a = bf16_bits_to_f32(two);
+        b = Int8Bias<ACT>::kBias;
     } else {
         (void)z;
         a = e4m3_to_f32(two & 0xFF);
@@ -135,8 +173,10 @@ __device__ __forceinline__ void chunk_scales(uint32_t two, uint32_t z, float &a,
 }
 template <int FMT>
 __device__ __forceinline__ int scale_offset(int c) {
-    return is_int4(FMT) ? 2 * (c / (int4_group(FMT) / 32)) : 2 * c;
+    return is_int4(FMT) ? 2 * (c / (int4_group(FMT) / 32)) : is_int8(FMT) ? 2 * (c / 8) : 2 * c;
 }
+// Formats whose chunks carry the sum of their inputs (the integer ones).
+__host__ __device__ constexpr bool needs_xsum(int fmt) { return is_int4(fmt) || is_int8(fmt); }
 
 
 // Chunks in flight per lane and matrix.
@@ -167,6 +207,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
     const int e = tile_expert[tile];
 
     static_assert(TM == kGemvWaves, "wave w stages the activation row of slot w");
+    constexpr int CI = chunk_inputs(FMT), UPC = CI / 8, UPC_LOG = UPC == 4 ? 2 : 1;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
     // the tile's number of real rows (slots are -1 past them)
     int m = 0;
@@ -199,9 +240,9 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
         return ((blockIdx.x * RPW + pass) * kGemvWaves + wave) * (kWave / LPR) + lane / LPR;
     };
     // chunks per row and iterations per lane and pass: NIT when the shape is
-    // known at compile time (kin == 32 * LPR * NIT; the main loop then
+    // known at compile time (kin == CI * LPR * NIT; the main loop then
     // unrolls completely and every load offset is a constant), else computed
-    const int nch = NIT > 0 ? NIT * LPR : kin / 32;
+    const int nch = NIT > 0 ? NIT * LPR : kin / CI;
     const int nit = NIT > 0 ? NIT : (nch + LPR - 1) / LPR;
     const __amdgpu_buffer_rsrc_t rqa = buffer_rsrc(A.q + e * A.qe, (int64_t)n_rows * A.qr);
     const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(A.s + e * A.se, (int64_t)n_rows * A.sr);
@@ -258,7 +299,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
 
     // activations into LDS (pair order of the decoders) and chunk sums
     uint4 *xs = smem;
-    const int upad = xs_units_pad<LPR>(kin);
+    const int upad = xs_units_pad<LPR, CI>(kin);
     float *xsum = (float *)(smem + TM * upad);
     // lanes past the end of the row write to a dummy area instead of
     // branching (a branch would let the compiler sink the staging loads
@@ -266,7 +307,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
     uint4 *xdummy = xs + TM * upad + (TM * nch + 3) / 4;
     float *sdummy = (float *)(xdummy + kWave);
     auto stage = [&](const u32x4_t &v, int g) {
-        const bool valid = g < units;            // the 4 lanes of a chunk agree (units % 4 == 0)
+        const bool valid = g < units;            // the UPC lanes of a chunk agree (units % UPC == 0)
         uint4 p;
         if (is_int4(FMT)) {                      // pairs (i, i+4) of the 8 inputs
             p.x = (v.x & 0xFFFFu) | (v.z << 16);
@@ -276,17 +317,17 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
         } else {                                 // pairs (2i, 2i+1): natural order
             p = make_uint4(v.x, v.y, v.z, v.w);
         }
-        *(valid ? xs + wave * upad + xs_unit<LPR>(g >> 2, g & 3) : xdummy + lane) = p;
-        if (is_int4(FMT)) {
+        *(valid ? xs + wave * upad + xs_unit<LPR, UPC>(g >> UPC_LOG, g & (UPC - 1)) : xdummy + lane) = p;
+        if (needs_xsum(FMT)) {
             const uint32_t d[4] = {v.x, v.y, v.z, v.w};
             float sum = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 sum += act_to_f32<ACT>(d[q] & 0xFFFF) + act_to_f32<ACT>(d[q] >> 16);
-            // the 4 units of a chunk sit in 4 consecutive lanes
+            // the UPC units of a chunk sit in UPC consecutive lanes
             sum += shfl_xor_f(sum, 1);
-            sum += shfl_xor_f(sum, 2);
-            *(valid && (g & 3) == 0 ? xsum + wave * nch + (g >> 2) : sdummy + lane) = sum;
+            if (UPC == 4) sum += shfl_xor_f(sum, 2);
+            *(valid && (g & (UPC - 1)) == 0 ? xsum + wave * nch + (g >> UPC_LOG) : sdummy + lane) = sum;
         }
     };
 #pragma unroll
@@ -354,12 +395,12 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
             __builtin_amdgcn_sched_barrier(0);
             load(j, I + kGemvRing);
             if (I < total_it && c < nch) {
-                const int u0 = xs_unit<LPR>(c, 0);
+                const int u0 = xs_unit<LPR, UPC>(c, 0);
 #pragma unroll
                 for (int t = 0; t < TM; ++t) {
                     if (t < m) {
                         const uint4 *xu = xs + t * upad + u0;
-                        const float xsm = is_int4(FMT) ? xsum[t * nch + c] : 0.0f;
+                        const float xsm = needs_xsum(FMT) ? xsum[t * nch + c] : 0.0f;
                         acc_a[t] = da.apply(xu, LPR, xsm, a0, a1, acc_a[t]);
                         if (GATEUP) acc_b[t] = db.apply(xu, LPR, xsm, b0, b1, acc_b[t]);
                     }
@@ -389,9 +430,9 @@ inline GemvMat gemv_mat(const moe_weight_desc_t &d) {
 
 // Activation units, chunk sums (rounded up to 16 bytes) and the staging
 // dummy area (64 units + 64 floats).
-template <int LPR, int TM>
+template <int LPR, int TM, int CI>
 inline size_t gemv_lds_bytes(int kin) {
-    return (size_t)TM * xs_units_pad<LPR>(kin) * 16 + ((size_t)TM * (kin / 32) + 3) / 4 * 16 +
+    return (size_t)TM * xs_units_pad<LPR, CI>(kin) * 16 + ((size_t)TM * (kin / CI) + 3) / 4 * 16 +
            (size_t)kWave * 16 + (size_t)kWave * 4;
 }
 
@@ -406,16 +447,18 @@ template <int ACT, int FMT>
 moe_status_t gemv_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
                             const moe_perm_t &p, int max_tiles, uint16_t *h, float *y,
                             hipStream_t s, const std::function<moe_status_t(int)> &mark) {
-    constexpr int LPR = kGemvLPR, TM = kGemvTM;
+    constexpr int LPR = kGemvLPR, TM = kGemvTM, CI = chunk_inputs(FMT);
     const int F = ex.gate.n, H = ex.gate.k;
     const int rows_per_block = kGemvWaves * (kWave / LPR);
     // the layer's own shapes get fully unrolled kernels: 4096 inputs -> 16
-    // iterations per lane, 1536 -> 6; other shapes run the generic loop
+    // iterations per lane (32 for int8), 1536 -> 6 (12); other shapes run
+    // the generic loop
+    constexpr int NIT_H = 4096 / (CI * LPR), NIT_F = 1536 / (CI * LPR);
     {
-        const size_t lds = gemv_lds_bytes<LPR, TM>(H);
+        const size_t lds = gemv_lds_bytes<LPR, TM, CI>(H);
         constexpr int RP = 1;                   // row passes per work group (more cost VGPRs)
-        const bool fast = H == 32 * LPR * 16 && F % (RP * rows_per_block) == 0;
-        auto k = fast ? gemv_kernel<ACT, FMT, LPR, TM, true, 16, RP>
+        const bool fast = H == CI * LPR * NIT_H && F % (RP * rows_per_block) == 0;
+        auto k = fast ? gemv_kernel<ACT, FMT, LPR, TM, true, NIT_H, RP>
                       : gemv_kernel<ACT, FMT, LPR, TM, true, 0, 1>;
         dim3 grid(fast ? F / (RP * rows_per_block) : (F + rows_per_block - 1) / rows_per_block,
                   max_tiles);
@@ -427,10 +470,11 @@ moe_status_t gemv_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
     }
     if (mark && mark(1) != MOE_OK) return MOE_ERR_HIP;
     {
-        const size_t lds = gemv_lds_bytes<LPR, TM>(F);
-        constexpr int RP = 4;
-        const bool fast = F == 32 * LPR * 6 && H % (RP * rows_per_block) == 0;
-        auto k = fast ? gemv_kernel<ACT, FMT, LPR, TM, false, 6, RP>
+        const size_t lds = gemv_lds_bytes<LPR, TM, CI>(F);
+        // row passes: the staged h rows serve RP * 32 output rows
+        constexpr int RP = is_int8(FMT) ? 2 : 4;
+        const bool fast = F == CI * LPR * NIT_F && H % (RP * rows_per_block) == 0;
+        auto k = fast ? gemv_kernel<ACT, FMT, LPR, TM, false, NIT_F, RP>
                       : gemv_kernel<ACT, FMT, LPR, TM, false, 0, 1>;
         dim3 grid(fast ? H / (RP * rows_per_block) : (H + rows_per_block - 1) / rows_per_block,
                   max_tiles);
@@ -459,6 +503,7 @@ moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int ac
             MOE_GEMV_FMT(MOE_BF16, MOE_W_NVFP4_G16);
             MOE_GEMV_FMT(MOE_BF16, MOE_W_INT4_G32);
             MOE_GEMV_FMT(MOE_BF16, MOE_W_INT4_G128_ASYM);
+            MOE_GEMV_FMT(MOE_BF16, MOE_W_INT8_G128);
         }
     } else {
         switch (ex.gate.fmt) {
@@ -466,6 +511,7 @@ moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int ac
             MOE_GEMV_FMT(MOE_F16, MOE_W_NVFP4_G16);
             MOE_GEMV_FMT(MOE_F16, MOE_W_INT4_G32);
             MOE_GEMV_FMT(MOE_F16, MOE_W_INT4_G128_ASYM);
+            MOE_GEMV_FMT(MOE_F16, MOE_W_INT8_G128);
         }
     }
 #undef MOE_GEMV_FMT

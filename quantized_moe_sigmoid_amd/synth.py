@@ -135,6 +135,18 @@ def packed_int4_variant_random(E, n, k, seed, device, group=128, asym=False, sca
     return q, s.to(torch.bfloat16), z
 
 
+def int8_random(E, n, k, seed, device, scale_mean=0.00027):
+    """Random int8-g128 bank: uniform bytes (q uniform on [-128, 127]) and
+    bf16 scales scale_mean * (1 + 0.1 N(0, 1)) per 128 inputs (a weight std
+    of about 0.02). Returns (q int8 [E, n, k], scales bf16 [E, n, k/128])."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    q = torch.randint(-128, 128, (E, n, k), generator=g, device=device, dtype=torch.int8)
+    s = (torch.randn((E, n, k // 128), generator=g, device=device) * 0.1 + 1.0) * scale_mean
+    return q, s.to(torch.bfloat16)
+
+
 def csf_random(E, R, C, seed, device, rate=0.002):
     """Random CSF tensors of an NVFP4 scale tensor [E, R, C]: row bases
     uniform in [0x60, 0x6F], uniform 4-bit codes, and per expert about

@@ -145,18 +145,22 @@ class HipEvents:
         self.L.hipEventDestroy(self.c.c_void_p(e))
 
 
-def int4_variant_bank_oracle(E, n, k, root, layer, which, fmt):
-    """Gaussian bf16 weights quantized by the oracle as int4-g32 or asymmetric
-    int4-g128 and packed. Returns (words int32 [E, n, k/8], bf16 scale bits
-    uint16 [E, n, k/G], zero points uint8 [E, n, k/128] or None)."""
+def variant_bank_oracle(E, n, k, root, layer, which, fmt):
+    """Gaussian bf16 weights quantized by the oracle as int4-g32, asymmetric
+    int4-g128 or int8-g128. Returns (weights: int32 words [E, n, k/8], or
+    int8 [E, n, k]; bf16 scale bits uint16 [E, n, k/G]; zero points uint8
+    [E, n, k/128] or None)."""
     g = 32 if fmt == B.MOE_W_INT4_G32 else 128
-    q = np.empty((E, n, k // 8), dtype=np.int32)
+    i8 = fmt == B.MOE_W_INT8_G128
+    q = np.empty((E, n, k) if i8 else (E, n, k // 8), dtype=np.int8 if i8 else np.int32)
     s = np.empty((E, n, k // g), dtype=np.uint16)
     z = np.empty((E, n, k // 128), dtype=np.uint8) if fmt == B.MOE_W_INT4_G128_ASYM else None
     for e in range(E):
         W = synth.expert_weight_bf16(n, k, root, layer, TENSOR_OF[which], e)
         W = W.float().numpy().astype(np.float64)
-        if z is None:
+        if i8:
+            q[e], ss = OQ.quantize_int8(W)
+        elif z is None:
             qq, ss = OQ.quantize_int4(W, group=32)
             q[e] = OQ.pack_int4(qq)
         else:
@@ -167,15 +171,15 @@ def int4_variant_bank_oracle(E, n, k, root, layer, which, fmt):
     return q, s, z
 
 
-def int4_variant_to_device(q, s_bits, z, device="cuda"):
+def variant_to_device(q, s_bits, z, device="cuda"):
     qt, st = int4_to_device(q, s_bits, device)
     zt = torch.from_numpy(np.ascontiguousarray(z)).to(device) if z is not None else None
     return qt, st, zt
 
 
-def oracle_int4_variant_expert(q, s_bits, z, e):
-    """Exact float64 dequantized expert e of an int4-g32 or asymmetric bank
-    (host arrays or device tensors)."""
+def oracle_variant_expert(q, s_bits, z, e):
+    """Exact float64 dequantized expert e of an int4-g32, asymmetric or int8
+    bank (host arrays or device tensors; int8 weights mark the int8 bank)."""
     if isinstance(q, torch.Tensor):
         q = q[e].cpu().numpy()
         s_bits = s_bits[e].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -183,6 +187,8 @@ def oracle_int4_variant_expert(q, s_bits, z, e):
     else:
         q, s_bits = q[e], s_bits[e]
         z = z[e] if z is not None else None
+    if q.dtype == np.int8:
+        return OQ.dequant_int8(q, s_bits)
     if z is not None:
         return OQ.dequant_int4_asym(q, s_bits, z)
     return OQ.dequant_int4(q, s_bits, group=32)

@@ -293,19 +293,21 @@ def test_csf_expand_validation(L):
         assert F(*args) == want, args
 
 
-def _bank_v(fmt, E, n, k, srow=None, zrow=None, zp=True):
-    """An int4-g32 or asymmetric int4-g128 bank descriptor (fake pointers)."""
+def _bank_v(fmt, E, n, k, srow=None, zrow=None, zp=True, qrow=None):
+    """An int4-g32, asymmetric int4-g128 or int8-g128 bank descriptor (fake
+    pointers)."""
     g = 32 if fmt == B.MOE_W_INT4_G32 else 128
-    qr, sr = k // 2, srow if srow is not None else (k // g) * 2
+    qr = qrow if qrow is not None else (k if fmt == B.MOE_W_INT8_G128 else k // 2)
+    sr = srow if srow is not None else (k // g) * 2
     zr = zrow if zrow is not None else k // 128
     z = FAKE if (fmt == B.MOE_W_INT4_G128_ASYM and zp) else None
     return B.WeightDesc(fmt, E, n, k, FAKE, FAKE, None, qr * n, qr, sr * n, sr,
                         z, zr * n if z else 0, zr if z else 0)
 
 
-@pytest.mark.parametrize("fmt", [B.MOE_W_INT4_G32, B.MOE_W_INT4_G128_ASYM])
+@pytest.mark.parametrize("fmt", [B.MOE_W_INT4_G32, B.MOE_W_INT4_G128_ASYM, B.MOE_W_INT8_G128])
 def test_int4_variant_banks_plan_the_decode_kernels(L, fmt):
-    """Both variants are accepted and, even at prefill size, planned on the
+    """The variants are accepted and, even at prefill size, planned on the
     GEMV tile (the GEMM decodes int4-g128 and NVFP4 only)."""
     f = B.FfnDesc(_bank_v(fmt, 352, 1536, 4096), _bank_v(fmt, 352, 1536, 4096),
                   _bank_v(fmt, 352, 4096, 1536))
@@ -323,12 +325,17 @@ def test_int4_variant_bank_errors(L):
         _bank_v(ASYM, 352, 1536, 4096, zp=False),            # no zero points
         _bank_v(ASYM, 352, 1536, 4096, zrow=31),             # zero-point rows too short
         _bank_v(G32, 352, 1536, 4096, srow=(4096 // 128) * 2),   # g128-sized scale rows
+        _bank_v(B.MOE_W_INT8_G128, 352, 1536, 4096, qrow=2048),  # int4-sized weight rows
+        _bank_v(B.MOE_W_INT8_G128, 352, 1536, 4096, srow=62),     # scale rows too short
     ]
     for g in bad:
         f = B.FfnDesc(g, _bank_v(g.fmt, 352, 1536, 4096), _bank_v(g.fmt, 352, 4096, 1536))
         assert _plan(f)[0] == B.MOE_ERR_INVALID_ARG
     # g32 needs k % 32; the variant formats mixed with another format are refused
     f = B.FfnDesc(_bank_v(G32, 4, 64, 48), _bank_v(G32, 4, 64, 48), _bank_v(G32, 4, 48, 64))
+    assert _plan(f)[0] == B.MOE_ERR_INVALID_ARG
+    I8 = B.MOE_W_INT8_G128        # int8 groups are 128 inputs: k % 128
+    f = B.FfnDesc(_bank_v(I8, 4, 64, 192), _bank_v(I8, 4, 64, 192), _bank_v(I8, 4, 192, 64))
     assert _plan(f)[0] == B.MOE_ERR_INVALID_ARG
     f = B.FfnDesc(_bank_v(G32, 352, 1536, 4096), _bank(B.MOE_W_INT4_G128, 352, 1536, 4096),
                   _bank_v(G32, 352, 4096, 1536))

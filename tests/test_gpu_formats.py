@@ -1,5 +1,5 @@
-"""GPU parity of the int4 format variants (int4-g32 and asymmetric
-int4-g128, the int4 page's error-table rows) against the oracle: dequant
+"""GPU parity of the weight-format variants of the int4 page's error table
+(int4-g32, asymmetric int4-g128, int8-g128) against the oracle: dequant
 bit for bit, the layer within |gpu - oracle| <= 1e-2 (|oracle| +
 rms(oracle)) at small, decode and prefill sizes."""
 import numpy as np
@@ -14,7 +14,11 @@ from tests import fixtures as FX
 pytestmark = pytest.mark.gpu
 
 H, F, E, K = 4096, 1536, 352, 8
-FORMATS = [B.MOE_W_INT4_G32, B.MOE_W_INT4_G128_ASYM]
+FORMATS = [B.MOE_W_INT4_G32, B.MOE_W_INT4_G128_ASYM, B.MOE_W_INT8_G128]
+
+
+def _bank(q, s, z):
+    return B.bank_int8(q, s) if q.dtype == torch.int8 else B.bank_int4(q, s, z)
 
 
 @pytest.fixture(scope="module")
@@ -28,8 +32,8 @@ def dev():
 def _oracle_ffn(fmt, Ee, Hh, Ff, root, dev):
     banks, host = [], []
     for which, (n, k) in (("gate", (Ff, Hh)), ("up", (Ff, Hh)), ("down", (Hh, Ff))):
-        q, s, z = FX.int4_variant_bank_oracle(Ee, n, k, root, 0, which, fmt)
-        banks.append(B.bank_int4(*FX.int4_variant_to_device(q, s, z, dev)))
+        q, s, z = FX.variant_bank_oracle(Ee, n, k, root, 0, which, fmt)
+        banks.append(_bank(*FX.variant_to_device(q, s, z, dev)))
         host.append((q, s, z))
     assert banks[0].fmt == fmt
     return B.ffn(*banks), host
@@ -38,10 +42,13 @@ def _oracle_ffn(fmt, Ee, Hh, Ff, root, dev):
 def _random_ffn(fmt, seed, dev):
     banks, host = [], []
     for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
-        q, s, z = synth.packed_int4_variant_random(
-            E, n, k, seed + i, dev, group=32 if fmt == B.MOE_W_INT4_G32 else 128,
-            asym=fmt == B.MOE_W_INT4_G128_ASYM)
-        banks.append(B.bank_int4(q, s, z))
+        if fmt == B.MOE_W_INT8_G128:
+            (q, s), z = synth.int8_random(E, n, k, seed + i, dev), None
+        else:
+            q, s, z = synth.packed_int4_variant_random(
+                E, n, k, seed + i, dev, group=32 if fmt == B.MOE_W_INT4_G32 else 128,
+                asym=fmt == B.MOE_W_INT4_G128_ASYM)
+        banks.append(_bank(q, s, z))
         host.append((q, s, z))
     assert banks[0].fmt == fmt
     return B.ffn(*banks), host
@@ -52,7 +59,7 @@ def _experts_fn(host):
 
     def fn(e):
         if e not in cache:
-            cache[e] = tuple(FX.oracle_int4_variant_expert(q, s, z, e) for (q, s, z) in host)
+            cache[e] = tuple(FX.oracle_variant_expert(q, s, z, e) for (q, s, z) in host)
         return cache[e]
     return fn
 
@@ -66,11 +73,11 @@ def _layer(ffn, x, lg, Ee, Kk, dev):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_dequant_bitwise(dev, fmt):
-    q, s, z = FX.int4_variant_bank_oracle(3, 64, 256, 21, 0, "gate", fmt)
-    bank = B.bank_int4(*FX.int4_variant_to_device(q, s, z, dev))
+    q, s, z = FX.variant_bank_oracle(3, 64, 256, 21, 0, "gate", fmt)
+    bank = _bank(*FX.variant_to_device(q, s, z, dev))
     for e in range(3):
         got = B.moe_dequant(bank, e, device=dev).cpu().numpy()
-        want = FX.oracle_int4_variant_expert(q, s, z, e).astype(np.float32)
+        want = FX.oracle_variant_expert(q, s, z, e).astype(np.float32)
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), e
 
 
