@@ -58,6 +58,11 @@ EXPERT_BYTES = {"int4": (INT4_GATEUP_BYTES, INT4_DOWN_BYTES),
                 "int4-asym": (INT4_ASYM_GATEUP_BYTES, INT4_ASYM_DOWN_BYTES),
                 "int8": (INT8_GATEUP_BYTES, INT8_DOWN_BYTES)}
 FLOP_PER_SLOT = 3 * 2 * H * F
+# Timed steps that record the gate/up kernel's events: every recorded HIP
+# event drains the stream for a few microseconds, so only every
+# EVENT_EVERY-th timed step carries them (the kernel's duration is still
+# measured inside the timed region).
+EVENT_EVERY = 4
 
 
 class Hip:
@@ -176,9 +181,9 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
     rws = torch.empty(max(B.moe_route_workspace(T, E, route_mode == "weights"), 256),
                       dtype=torch.uint8, device=dev)
     NS = B.MOE_FORWARD_STAGES
-    # timed loop: events only at the gate/up boundaries (each recorded event
-    # drains the stream); the other stages are timed in a separate pass
-    ev_t = [[hip.event(), hip.event()] for _ in range(steps)]
+    # timed loop: events only at the gate/up boundaries of every
+    # EVENT_EVERY-th step; the other stages are timed in a separate pass
+    ev_t = {i: [hip.event(), hip.event()] for i in range(0, steps, EVENT_EVERY)}
     nb = min(steps, 10)
     ev_b = [[hip.event() for _ in range(NS + 1)] for _ in range(nb)]
 
@@ -205,17 +210,18 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, ev_t[i] + [None] * (NS - 1))
+        step(i, ev_t[i] + [None] * (NS - 1) if i in ev_t else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gu_ms = np.array([hip.elapsed_ms(e[0], e[1]) for e in ev_t])
+    gu_idx = sorted(ev_t)
+    gu_ms = np.array([hip.elapsed_ms(*ev_t[i]) for i in gu_idx])
     # stage breakdown: the first nb steps again, every boundary recorded
     for i in range(nb):
         step(i, ev_b[i], ev_c[i] if csf else None)
     torch.cuda.synchronize()
     stage_ms = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(NS)] for e in ev_b])
     csf_ms = np.array([hip.elapsed_ms(e[0], e[1]) for e in ev_c]) if csf else None
-    for e in ev_t + ev_b + (ev_c or []):
+    for e in list(ev_t.values()) + ev_b + (ev_c or []):
         for h in e:
             hip.destroy(h)
     if route_mode == "logits":
@@ -229,7 +235,7 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
              layer_GBps=float((U * (gu_bytes + dn_bytes)).mean() / (ms * 1e-3) / 1e9),
              gateup_ms=float(gu_ms.mean()), down_ms=float(stage_ms[:, 1].mean()),
              combine_ms=float(stage_ms[:, 3].mean()),
-             gateup_GBps=float(np.mean(U * gu_bytes / (gu_ms * 1e-3)) / 1e9),
+             gateup_GBps=float(np.mean(U[gu_idx] * gu_bytes / (gu_ms * 1e-3)) / 1e9),
              down_GBps=float(np.mean(U[:nb] * dn_bytes / (stage_ms[:, 1] * 1e-3)) / 1e9),
              layer_TFLOPs=float(T * K * FLOP_PER_SLOT / (ms * 1e-3) / 1e12))
     r["gateup_frac_hbm"] = r["gateup_GBps"] * 1e9 / HBM_PEAK
@@ -272,9 +278,10 @@ def run_stack(layers, T, steps, warmup, hip, dev):
     perm = B.Perm(T, K, E, tm, dev)
     rws = torch.empty(B.moe_route_workspace(T, E, True), dtype=torch.uint8, device=dev)
     NS = B.MOE_FORWARD_STAGES
-    # timed loop: events at each layer's gate/up boundaries only; the other
-    # stages come from a separate pass with every boundary recorded
-    ev_t = [[[hip.event(), hip.event()] for _ in layers] for _ in range(steps)]
+    # timed loop: events at each layer's gate/up boundaries of every
+    # EVENT_EVERY-th step only; the other stages come from a separate pass
+    # with every boundary recorded
+    ev_t = {i: [[hip.event(), hip.event()] for _ in layers] for i in range(0, steps, EVENT_EVERY)}
     nb = min(steps, 3)
     ev_b = [[[hip.event() for _ in range(NS + 1)] for _ in layers] for _ in range(nb)]
 
@@ -295,16 +302,16 @@ def run_stack(layers, T, steps, warmup, hip, dev):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step([e + [None] * (NS - 1) for e in ev_t[i]])
+        step([e + [None] * (NS - 1) for e in ev_t[i]] if i in ev_t else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gu = np.array([[hip.elapsed_ms(e[0], e[1]) for e in le] for le in ev_t])   # [step, layer]
+    gu = np.array([[hip.elapsed_ms(e[0], e[1]) for e in ev_t[i]] for i in sorted(ev_t)])  # [step, layer]
     for i in range(nb):
         step(ev_b[i])
     torch.cuda.synchronize()
     st = np.array([[[hip.elapsed_ms(e[j], e[j + 1]) for j in range(NS)] for e in le]
                    for le in ev_b])                        # [step, layer, stage]
-    for le in ev_t + ev_b:
+    for le in list(ev_t.values()) + ev_b:
         for e in le:
             for h in e:
                 hip.destroy(h)

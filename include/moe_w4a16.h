@@ -197,8 +197,12 @@ moe_status_t moe_permute_sizes(int T, int K, int E, int tile_m,
  * exists so that each touched expert's weights stream from HBM once
  * (routed experts are 96.7 % of the weight bytes: page
  * "NeuroSenko/Step-5-Preview-Int4-g128", "Recipe").
- * topk_ids [T][K] int32 with values in [0, E). tile_m in [1, 256].
- * Deterministic: no atomics decide any order.
+ * topk_ids [T][K] int32, normally in [0, E) (a slot whose id lies outside
+ * is routed nowhere and its slot_to_row entry is left as it was); ids may
+ * repeat within a token. tile_m in [1, 256].
+ * Deterministic: no atomics decide any order (up to 1024 slots, one work
+ * group combines per-expert slot masks with LDS ORs, whose result does not
+ * depend on arrival order).
  */
 moe_status_t moe_permute(const int32_t *topk_ids, int T, int K, int E,
                          const moe_perm_t *perm, void *stream);

@@ -131,12 +131,14 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
 }
 
 // ---- NVFP4 ------------------------------------------------------------------
-// E4M3FN byte -> float32 (exact): exponent bias 7, subnormals m * 2^-9.
+// E4M3FN byte -> float32 (exact): exponent bias 7, so a normal value is
+// (8 + m) 2^(e - 10) and a subnormal (e = 0) m 2^-9 = m 2^(1 - 10); written
+// with selects and one ldexp so that it never branches.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
     const uint32_t e = (b >> 3) & 0xF, m = b & 7;
-    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
-                        : (float)m * 0.001953125f;
-    return (b & 0x80) ? -mag : mag;
+    const float mant = (float)(m | (e ? 8u : 0u));
+    const float mag = __builtin_amdgcn_ldexpf(mant, (int)(e ? e : 1u) - 10);
+    return __uint_as_float(__float_as_uint(mag) | ((b & 0x80u) << 24));
 }
 
 // E2M1 code -> float32 (exact): {0, .5, 1, 1.5, 2, 3, 4, 6}, sign bit 3.

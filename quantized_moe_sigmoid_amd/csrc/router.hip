@@ -9,10 +9,11 @@
 // a different summation order inside the MoE flips near-tied expert choices
 // ("Step-5-Preview-Spark", "Quality", noise-floor paragraph).
 //
-// Selection: the K largest logits by (logit desc, expert asc), as 64-bit
-// keys (order-preserving float bits << 32 | ~expert) reduced across a wave;
-// -0 is folded to +0 first. Weights: sigmoid of the selected logits,
-// renormalised to sum to one when asked.
+// Selection: the K largest logits by (logit desc, expert asc): per round a
+// wave maximum of the logits' order-preserving 32-bit images, ties resolved
+// to the lowest expert index by ballots; -0 is folded to +0 first.
+// Weights: sigmoid of the selected logits, renormalised to sum to one when
+// asked.
 #include "common.h"
 
 #pragma clang fp contract(off)
@@ -21,57 +22,75 @@ namespace moe {
 
 constexpr int kMaxE = 512;
 
-__device__ __forceinline__ uint64_t topk_key(float f, int e) {
-    uint32_t u = __float_as_uint(f + 0.0f);          // -0 -> +0
-    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)e);
+// Order-preserving image of a float in uint32 (a larger float maps to a
+// larger value; -0 is folded to +0 first); 0 lies below every image.
+__device__ __forceinline__ uint32_t ord32(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float key_value(uint64_t key) {
-    uint32_t ord = (uint32_t)(key >> 32);
-    uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
-    return __uint_as_float(u);
+__device__ __forceinline__ float ord32_value(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+
+// Maximum over the wave: four DPP butterflies inside each 16-lane row
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror;
+// every lane then holds its row's maximum), then the four rows through
+// scalar registers.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return v > o ? v : o;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max<0xB1>(v);
+    v = dpp_max<0x4E>(v);
+    v = dpp_max<0x141>(v);
+    v = dpp_max<0x140>(v);
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+    return a > b ? a : b;
 }
 
 // One wave selects the top K of E logits held in `lg` (LDS or global).
-// Lane l owns experts l, l+64, ... Writes ids / weights for one token.
+// Lane l owns experts l, l+64, ... Each round takes the wave maximum of the
+// logits' order images, then the lowest expert holding it: experts of slot
+// j are 64 j + lane, so the first slot whose ballot hits, at its lowest
+// lane (ties go to the lower index). Writes ids / weights for one token.
 template <typename LoadFn>
 __device__ __forceinline__ void wave_topk(LoadFn load, int E, int K, int renorm,
                                           int32_t *ids, float *wts) {
+    constexpr int NJ = kMaxE / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    uint64_t keys[kMaxE / kWave];
+    uint32_t o[NJ];
 #pragma unroll
-    for (int j = 0; j < kMaxE / kWave; ++j) {
-        int e = lane + j * kWave;
-        keys[j] = e < E ? topk_key(load(e), e) : 0ull;    // 0 = below any real key
+    for (int j = 0; j < NJ; ++j) {
+        const int e = lane + j * kWave;
+        o[j] = e < E ? ord32(load(e)) : 0u;
     }
     float my_logit = 0.0f;
     int my_id = 0;
     for (int r = 0; r < K; ++r) {
-        uint64_t best = 0;
+        uint32_t m = o[0];
 #pragma unroll
-        for (int j = 0; j < kMaxE / kWave; ++j) best = keys[j] > best ? keys[j] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(~(uint32_t)best);
+        for (int j = 1; j < NJ; ++j) m = o[j] > m ? o[j] : m;
+        const uint32_t best = wave_max_u32(m);
+        int win = -1;
 #pragma unroll
-        for (int j = 0; j < kMaxE / kWave; ++j)
-            if (keys[j] == best) keys[j] = 0;
-        if (lane == r) { my_id = e; my_logit = key_value(best); }
+        for (int j = 0; j < NJ; ++j) {
+            const uint64_t b = __ballot(o[j] == best);
+            if (win < 0 && b) win = j * kWave + __ffsll((unsigned long long)b) - 1;
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            if (j * kWave + lane == win) o[j] = 0u;
+        if (lane == r) { my_id = win; my_logit = ord32_value(best); }
     }
     float p = 1.0f / (1.0f + expf(-my_logit));
     if (renorm) {
         // sum over lanes 0..K-1 in ascending order (deterministic)
         float s = 0.0f;
-        for (int r = 0; r < K; ++r) s += __shfl(p, r, kWave);
+        for (int r = 0; r < K; ++r) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), r));
         p = p / s;
     }
     if (lane < K) { ids[lane] = my_id; wts[lane] = p; }

@@ -147,8 +147,12 @@ def test_route_from_router_weight_full(dev, T, zipf):
 @pytest.mark.parametrize("T,Kk,Ee,tm,skew", [(1, 8, 352, 4, False), (64, 8, 352, 4, False),
                                              (2048, 8, 352, 64, False), (2048, 8, 352, 64, True),
                                              (4096, 8, 352, 128, True), (8, 2, 16, 4, False),
-                                             (3, 3, 5, 1, False), (0, 8, 352, 4, False)])
+                                             (3, 3, 5, 1, False), (0, 8, 352, 4, False),
+                                             (128, 8, 352, 4, True), (129, 8, 352, 4, False),
+                                             (128, 8, 512, 4, True), (5, 16, 512, 16, False)])
 def test_permute_bitwise(dev, T, Kk, Ee, tm, skew):
+    """Batches of up to 1024 slots take the one-work-group kernel, larger
+    ones the two-launch form; both must match the oracle bit for bit."""
     r = np.random.default_rng(T * 7 + Kk)
     if skew:
         p = 1.0 / np.arange(1, Ee + 1) ** 1.1
@@ -174,6 +178,27 @@ def test_permute_bitwise(dev, T, Kk, Ee, tm, skew):
     na = want["num_active"]
     assert int(perm.num_active.cpu()[0]) == na
     assert np.array_equal(perm.active_experts.cpu().numpy()[:na], want["active_experts"])
+
+
+@pytest.mark.parametrize("T,Kk,Ee,tm", [(40, 8, 16, 4), (300, 8, 16, 8)])
+def test_permute_repeated_and_foreign_ids(dev, T, Kk, Ee, tm):
+    """Ids need not be distinct within a token, and ids outside [0, E) are
+    routed nowhere; slots keep their order inside an expert either way."""
+    r = np.random.default_rng(T + 11)
+    ids = r.integers(-2, Ee + 2, (T, Kk)).astype(np.int32)
+    perm = B.moe_permute(torch.from_numpy(ids).to(dev), Ee, tm)
+    torch.cuda.synchronize()
+    ok = (ids >= 0) & (ids < Ee)
+    # the oracle with the foreign slots sent to an extra, last expert: the
+    # first Ee experts' rows are then exactly the expected ones
+    want = OP.permute(np.where(ok, ids, Ee), Ee + 1, tm)
+    tot = int(want["padded_offsets"][Ee])
+    assert np.array_equal(perm.counts.cpu().numpy(), want["counts"][:Ee])
+    assert np.array_equal(perm.padded_offsets.cpu().numpy(), want["padded_offsets"][:Ee + 1])
+    assert np.array_equal(perm.sorted_slots.cpu().numpy()[:tot], want["sorted_slots"][:tot])
+    assert int(perm.num_tiles.cpu()[0]) == tot // tm
+    s2r = perm.slot_to_row.cpu().numpy()
+    assert np.array_equal(s2r[ok.ravel()], want["slot_to_row"][ok.ravel()])
 
 
 # ------------------------------------------------------------------ forward ---
