@@ -227,8 +227,8 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts,
  *   out_t = sum_{k ascending} topk_w[t][k] * y_(t,k)
  *           [+ Wd_sh (silu(Wg_sh x_t) * (Wu_sh x_t))]  [+ residual_t]
  *
- * x [T][H] in act_dtype (MOE_F16 or MOE_BF16); experts: int4-g128 or NVFP4
- * bank with gate/up [F][H] and down [H][F]; shared: NULL or a MOE_W_BF16
+ * x [T][H] in act_dtype (MOE_F16 or MOE_BF16); experts: a bank of any
+ * quantized moe_wfmt_t with gate/up [F][H] and down [H][F]; shared: NULL or a MOE_W_BF16
  * bank with num_experts == 1, gate/up [Fs][H], down [H][Fs] (act_dtype must
  * then be MOE_BF16; Fs % 128 == 0 and H % 256 == 0, else
  * MOE_ERR_UNSUPPORTED); the shared expert's h is rounded to bf16 like the
@@ -238,8 +238,9 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts,
  * out [T][H] in out_dtype (MOE_F32, MOE_F16 or MOE_BF16); ws: device
  * workspace of at least moe_forward_plan's ws_bytes, 256-byte aligned.
  * Accumulation is float32; h is rounded to act_dtype before the down
- * projection. Limits: H % 128 == 0, F % 128 == 0 (int4) or % 16 (NVFP4),
- * H and F <= 16384, E <= 512.
+ * projection. Limits: 1 <= K <= min(E, 16); H and F multiples of the
+ * format's group (128; 32 for MOE_W_INT4_G32 and NVFP4), at most 16384;
+ * E <= 512.
  */
 moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts,
                                const moe_ffn_desc_t *shared,

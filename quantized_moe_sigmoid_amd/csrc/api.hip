@@ -292,7 +292,7 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts, const moe_ffn_desc_
     int E, H, F;
     moe_status_t st = check_experts(experts, &E, &H, &F);
     if (st != MOE_OK) return st;
-    if (T < 0 || K < 1 || K > E || !is_act(act_dtype) || !tile_m || !ws_bytes)
+    if (T < 0 || K < 1 || K > E || K > kMaxTopK || !is_act(act_dtype) || !tile_m || !ws_bytes)
         return MOE_ERR_INVALID_ARG;
     int Fs;
     if ((st = check_shared(shared, H, act_dtype, &Fs)) != MOE_OK) return st;
@@ -311,7 +311,7 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     int E, H, F;
     moe_status_t st = check_experts(experts, &E, &H, &F);
     if (st != MOE_OK) return st;
-    if (T < 0 || K < 1 || K > E || !is_act(act_dtype)) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || K < 1 || K > E || K > kMaxTopK || !is_act(act_dtype)) return MOE_ERR_INVALID_ARG;
     if (out_dtype != MOE_F32 && !is_act(out_dtype)) return MOE_ERR_INVALID_ARG;
     if ((st = check_perm(perm)) != MOE_OK) return st;
     int Fs;

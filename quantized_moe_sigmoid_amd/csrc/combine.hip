@@ -12,6 +12,9 @@
 
 namespace moe {
 
+// The largest K the library accepts (the host rejects more).
+constexpr int kCombineMaxK = 16;
+
 template <int OUT>
 __global__ void __launch_bounds__(256) combine_kernel(
     const float *__restrict__ y, const int32_t *__restrict__ slot_to_row,
@@ -20,14 +23,30 @@ __global__ void __launch_bounds__(256) combine_kernel(
     const int t = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (n >= H) return;
+    // all K rows and weights first (uniform: scalar loads), then all K row
+    // loads in flight together, then the sum in ascending k
+    int rows[kCombineMaxK];
+    float wk[kCombineMaxK];
+    float4 v[kCombineMaxK];
+#pragma unroll
+    for (int k = 0; k < kCombineMaxK; ++k) {
+        if (k < K) {
+            rows[k] = slot_to_row[(size_t)t * K + k];
+            wk[k] = w[(size_t)t * K + k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineMaxK; ++k)
+        if (k < K) v[k] = *(const float4 *)(y + (size_t)rows[k] * H + n);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-        const float wk = w[(size_t)t * K + k];
-        const float4 v = *(const float4 *)(y + (size_t)slot_to_row[(size_t)t * K + k] * H + n);
-        acc.x = __builtin_fmaf(wk, v.x, acc.x);
-        acc.y = __builtin_fmaf(wk, v.y, acc.y);
-        acc.z = __builtin_fmaf(wk, v.z, acc.z);
-        acc.w = __builtin_fmaf(wk, v.w, acc.w);
+#pragma unroll
+    for (int k = 0; k < kCombineMaxK; ++k) {
+        if (k < K) {
+            acc.x = __builtin_fmaf(wk[k], v[k].x, acc.x);
+            acc.y = __builtin_fmaf(wk[k], v[k].y, acc.y);
+            acc.z = __builtin_fmaf(wk[k], v[k].z, acc.z);
+            acc.w = __builtin_fmaf(wk[k], v[k].w, acc.w);
+        }
     }
     if (shared) {
         const float4 v = *(const float4 *)(shared + (size_t)t * H + n);

@@ -62,6 +62,12 @@ def _plan(ex, T=8, K=8, act=B.MOE_F16, shared=None):
     return st, tm.value, ws.value
 
 
+def test_forward_plan_rejects_k_over_16(L):
+    """The combine sums at most 16 routed slots per token."""
+    assert _plan(_ffn(), T=8, K=16)[0] == B.MOE_OK
+    assert _plan(_ffn(), T=8, K=17)[0] == B.MOE_ERR_INVALID_ARG
+
+
 def test_forward_plan_sizes(L):
     st, tm, ws = _plan(_ffn(), T=64)
     assert st == B.MOE_OK and tm >= 1
