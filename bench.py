@@ -264,7 +264,7 @@ class StackLayer:
         self.norm_w = torch.from_numpy(synth.norm_weight(H, 5, l)).to(dev)
 
 
-def run_stack(layers, T, steps, warmup, hip, dev):
+def run_stack(layers, T, steps, warmup, hip, dev, use_graph=True):
     """Times `steps` passes of the 8-layer stack: per layer, the RMSNorm of
     the fp32 residual rounded to bf16, routing from the router weight plus Zipf bias,
     permutation, routed + shared experts and the combine with the residual."""
@@ -279,9 +279,11 @@ def run_stack(layers, T, steps, warmup, hip, dev):
     rws = torch.empty(B.moe_route_workspace(T, E, True), dtype=torch.uint8, device=dev)
     NS = B.MOE_FORWARD_STAGES
     # timed loop: events at each layer's gate/up boundaries of every
-    # EVENT_EVERY-th step only; the other stages come from a separate pass
-    # with every boundary recorded
-    ev_t = {i: [[hip.event(), hip.event()] for _ in layers] for i in range(0, steps, EVENT_EVERY)}
+    # EVENT_EVERY-th step only (none when the step is a graph replay); the
+    # other stages come from a separate eager pass with every boundary
+    # recorded
+    ev_t = ({} if use_graph else
+            {i: [[hip.event(), hip.event()] for _ in layers] for i in range(0, steps, EVENT_EVERY)})
     nb = min(steps, 3)
     ev_b = [[[hip.event() for _ in range(NS + 1)] for _ in layers] for _ in range(nb)]
 
@@ -300,12 +302,26 @@ def run_stack(layers, T, steps, warmup, hip, dev):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        # the whole 8-layer step as one HIP graph (the step launches ~10
+        # kernels per layer; replaying them as a graph removes the host's
+        # launch gaps); captured after the warm-up, replayed once untimed
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step([e + [None] * (NS - 1) for e in ev_t[i]] if i in ev_t else None)
+        if graph is not None:
+            graph.replay()
+        else:
+            step([e + [None] * (NS - 1) for e in ev_t[i]] if i in ev_t else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gu = np.array([[hip.elapsed_ms(e[0], e[1]) for e in ev_t[i]] for i in sorted(ev_t)])  # [step, layer]
+    gu = (np.array([[hip.elapsed_ms(e[0], e[1]) for e in ev_t[i]] for i in sorted(ev_t)])
+          if graph is None else None)                   # [step, layer]
     for i in range(nb):
         step(ev_b[i])
     torch.cuda.synchronize()
@@ -320,10 +336,12 @@ def run_stack(layers, T, steps, warmup, hip, dev):
     torch.cuda.synchronize()
     ms = wall / steps * 1e3
     per = st.sum(axis=1).mean(axis=0)                      # stage ms per step, all layers
-    per[0] = gu.sum(axis=1).mean()                         # gate/up from the timed loop
+    if gu is not None:
+        per[0] = gu.sum(axis=1).mean()                     # gate/up from the timed loop
     flop = len(layers) * T * (K + 1) * FLOP_PER_SLOT
     gu_flop = len(layers) * T * K * 2 * 2 * H * F
-    return dict(workload="stack T=%d" % T, tokens=T, layers=len(layers), ms_per_step=ms,
+    return dict(workload="stack T=%d" % T, tokens=T, layers=len(layers), graph=use_graph,
+                ms_per_step=ms,
                 tok_s=T / (ms * 1e-3), ms_per_layer=ms / len(layers),
                 touched_experts=float(np.mean(U)),
                 layer_GBps=float(np.sum(U) * (INT4_GATEUP_BYTES + INT4_DOWN_BYTES) /
@@ -406,6 +424,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="run the stack's timed steps eagerly instead of as a HIP graph replay")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain streaming kernel over MIB MiB (read once, written "
                          "once), the reference for scaling hardware byte counters")
@@ -456,7 +476,7 @@ def main():
             if stack is None:
                 stack = [StackLayer(l, dev) for l in range(8)]
             results.append(run_stack(stack, T, max(5, steps // 4), max(2, args.warmup // 4),
-                                     hip, dev))
+                                     hip, dev, use_graph=not args.no_graph))
         else:
             if fmt == "nvfp4" and nv is None:
                 nv = nvfp4_banks(2, dev, 900)

@@ -203,19 +203,26 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
 // through LDS (one lane-varying 4-byte read per k), which removes the
 // broadcast x reads that bound the LDS return path above. Same tiles, same
 // per-(t, e) chain order.
+//
+// TPW tokens per wave: 4 for large batches; 1 for small ones, where the
+// tiled grid would otherwise be a handful of work groups whose waves each
+// run four 4096-step chains back to back (T = 32: 12 groups, 116 us); with
+// one token per wave the grid has four times the waves and each wave a
+// quarter of the serial work.
+template <int TPW>
 __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wT,
     const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
     __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
-    const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp;
+    const int t0 = blockIdx.x * (4 * TPW), e0 = blockIdx.y * kRtExp;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // the wave's token rows as 32-bit pairs (rows past T read row t0; their
     // logits are not stored)
-    const uint32_t *xr[4];
+    const uint32_t *xr[TPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * wave + i;
+    for (int i = 0; i < TPW; ++i) {
+        const int t = t0 + TPW * wave + i;
         xr[i] = (const uint32_t *)(x + (size_t)(t < T ? t : t0) * H);
     }
     // E % 4 == 0: a float4 column group is either inside the matrix or past
@@ -224,12 +231,12 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
     const bool w_in = e0 + we < E;
     const int w_col = w_in ? e0 + we : E - 4;
     float4 wreg[4];
-    // the next chunk's x bytes of the wave's rows (4 rows x 128 B) are also
+    // the next chunk's x bytes of the wave's rows (TPW rows x 128 B) are also
     // touched with vector loads one chunk ahead, so the scalar loads that
     // consume them hit L2 instead of waiting for HBM; the loaded words only
     // feed `sink`
     uint32_t sink = 0, xtouch = 0;
-    const int tpf = t0 + 4 * wave + ((lane >> 3) & 3);
+    const int tpf = t0 + TPW * wave + ((lane >> 3) % TPW);
     const uint16_t *xpf = x + (size_t)(tpf < T ? tpf : t0) * H + (lane & 7) * 8;
     auto load = [&](int k0) {
 #pragma unroll
@@ -244,9 +251,9 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
         sink ^= xtouch;
     };
 
-    float acc[4];
+    float acc[TPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < TPW; ++i) acc[i] = 0.0f;
     const int nch = H / kRtKC;
     load(0);
     store(0);
@@ -255,16 +262,21 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
         const int b = c & 1;
         if (c + 1 < nch) load((c + 1) * kRtKC);
         const int p0 = c * (kRtKC / 2);
-#pragma unroll 8
+        // one token per wave: the whole chunk unrolled, so its LDS and
+        // scalar reads are issued ahead of the FMA chain instead of
+        // between its pieces
+        constexpr int kUnroll = TPW == 1 ? kRtKC / 2 : 8;
+#pragma unroll kUnroll
         for (int k2 = 0; k2 < kRtKC / 2; ++k2) {
-            uint32_t xp[4];
+            uint32_t xp[TPW];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xp[i] = xr[i][p0 + k2];
+            for (int i = 0; i < TPW; ++i) xp[i] = xr[i][p0 + k2];
             const float w0 = ws[b][2 * k2][lane], w1 = ws[b][2 * k2 + 1][lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(__uint_as_float(xp[i] << 16), w0, acc[i]);
+            for (int i = 0; i < TPW; ++i)
+                acc[i] = __builtin_fmaf(__uint_as_float(xp[i] << 16), w0, acc[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < TPW; ++i)
                 acc[i] = __builtin_fmaf(__uint_as_float(xp[i] & 0xFFFF0000u), w1, acc[i]);
         }
         if (c + 1 < nch) store(b ^ 1);
@@ -275,18 +287,24 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
     if (e >= E) return;
     const float bv = bias ? bias[e] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * wave + i;
+    for (int i = 0; i < TPW; ++i) {
+        const int t = t0 + TPW * wave + i;
         if (t < T) logits[(size_t)t * E + e] = bias ? acc[i] + bv : acc[i];
     }
 }
+
+// bf16 batches up to this many tokens run one token per wave.
+constexpr int kRtSmallT = 512;
 
 moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, const float *bias,
                                   int T, int H, int E, float *logits, hipStream_t s) {
     if (T == 0) return MOE_OK;
     const dim3 grid((T + kRtTok - 1) / kRtTok, (E + kRtExp - 1) / kRtExp);
-    if (x_dtype == MOE_BF16)
-        hipLaunchKernelGGL(router_logits_bf16_kernel, grid, dim3(256), 0, s,
+    if (x_dtype == MOE_BF16 && T <= kRtSmallT)
+        hipLaunchKernelGGL(router_logits_bf16_kernel<1>, dim3((T + 3) / 4, grid.y), dim3(256), 0,
+                           s, (const uint16_t *)x, wT, bias, T, H, E, logits);
+    else if (x_dtype == MOE_BF16)
+        hipLaunchKernelGGL(router_logits_bf16_kernel<4>, grid, dim3(256), 0, s,
                            (const uint16_t *)x, wT, bias, T, H, E, logits);
     else
         hipLaunchKernelGGL(router_logits_kernel<MOE_F16>, grid, dim3(256), 0, s,
