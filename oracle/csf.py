@@ -94,6 +94,22 @@ def decode(fixed, exceptions, starts, R, C):
     return out
 
 
+def row_starts(exceptions, starts, E, R, C):
+    """int32 [E, R+1]: entry [e, r] is the index of expert e's first
+    exception at a position >= r * C (the expert's exceptions in stored
+    order, which is ascending position), so row r's exceptions are
+    [entry[e, r], entry[e, r+1]). A reader that keeps scales compressed
+    uses it to find a row's exceptions without scanning the expert's list."""
+    exceptions = np.asarray(exceptions, dtype=np.uint32)
+    out = np.empty((E, R + 1), dtype=np.int32)
+    for e in range(E):
+        lo, hi = int(starts[e]), int(starts[e + 1])
+        pos = (exceptions[lo:hi] & 0xFFFFFF).astype(np.int64)
+        assert np.all(np.diff(pos) > 0), "exceptions of an expert must be in ascending position"
+        out[e] = lo + np.searchsorted(pos, np.arange(R + 1, dtype=np.int64) * C, side="left")
+    return out
+
+
 def fixed_bytes(E, R, C):
     """Bytes of the fixed tensor: E * R/16 slabs of 16 * (1 + C/2)."""
     return E * (R // 16) * 16 * (1 + C // 2)

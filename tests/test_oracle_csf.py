@@ -90,3 +90,34 @@ def test_sizes_reproduce_the_page_table():
     raw = g["layers_3_87"] * (2 * E * sz["gate_up_R"] * sz["gate_up_C"] + E * sz["down_R"] * sz["down_C"])
     assert raw == g["layers_3_87_raw_scales"]
     assert round(100 * g["layers_3_87_csf_scales"] / raw, 2) == g["csf_percent"]
+
+
+def test_row_starts_by_brute_force_and_partition():
+    """Every row's range holds exactly the exceptions whose position falls
+    in that row (brute force over all positions), the ranges tile each
+    expert's list in order, and decoding a row from its range alone
+    reproduces the row."""
+    rng = np.random.default_rng(5)
+    E, R, C = 3, 32, 48
+    base = rng.integers(0x30, 0x60, (E, R, 1))
+    s = (base + rng.integers(0, 16, (E, R, C))).astype(np.uint8)
+    out = rng.random((E, R, C)) < 0.15
+    s[out] = rng.integers(0, 0x7F, int(out.sum()))
+    s[1, 7, :] = 0x7E                     # a row made only of one value
+    s[2] = s[2, :, :1]                    # an expert without exceptions
+    fixed, exc, starts = OC.encode(s)
+    rs = OC.row_starts(exc, starts, E, R, C)
+    assert rs.shape == (E, R + 1) and rs.dtype == np.int32
+    for e in range(E):
+        assert rs[e, 0] == starts[e] and rs[e, R] == starts[e + 1]
+        assert np.all(np.diff(rs[e]) >= 0)
+        for r in range(R):
+            mine = [x for x in range(int(starts[e]), int(starts[e + 1]))
+                    if r * C <= (int(exc[x]) & 0xFFFFFF) < (r + 1) * C]
+            assert list(range(rs[e, r], rs[e, r + 1])) == mine, (e, r)
+            row = (fixed[e, r // 16, r % 16] + np.concatenate(
+                [[b & 15, b >> 4] for b in fixed[e, r // 16, 16 + (r % 16) * (C // 2):
+                                                 16 + (r % 16 + 1) * (C // 2)]])).astype(np.uint8)
+            for x in range(rs[e, r], rs[e, r + 1]):
+                row[(int(exc[x]) & 0xFFFFFF) - r * C] = int(exc[x]) >> 24
+            assert np.array_equal(row, s[e, r]), (e, r)
