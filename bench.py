@@ -17,7 +17,8 @@ event drains the stream); the other stages' durations come from a separate,
 untimed pass over the same inputs with every stage boundary recorded.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--workload decode|prefill|nvfp4|nvfp4-csf|int4-g32|int4-asym|int8|stack]
+                  [--workload decode|prefill|nvfp4|nvfp4-csf|nvfp4-csf-expand|int4-g32|
+                              int4-asym|int8|stack]
                   [--tokens T] [--no-sweep] [--no-cpu-baseline]
 """
 import argparse
@@ -50,13 +51,18 @@ INT4_G32_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 32) * 2)
 INT4_G32_DOWN_BYTES = H * F // 2 + H * (F // 32) * 2
 INT4_ASYM_GATEUP_BYTES = 2 * (F * H // 2 + F * (H // 128) * 3)      # + one zero-point byte
 INT4_ASYM_DOWN_BYTES = H * F // 2 + H * (F // 128) * 3
+# NVFP4 with compressed scales read in place: codes, the CSF fixed bytes
+# (a base per row and a 4-bit code per scale) and the global scale
+NVFP4_CSF_GATEUP_BYTES = 2 * (F * H // 2 + F * (1 + H // 32))
+NVFP4_CSF_DOWN_BYTES = H * F // 2 + H * (1 + F // 32) + 4
 INT8_GATEUP_BYTES = 2 * (F * H + F * (H // 128) * 2)
 INT8_DOWN_BYTES = H * F + H * (F // 128) * 2
 EXPERT_BYTES = {"int4": (INT4_GATEUP_BYTES, INT4_DOWN_BYTES),
                 "nvfp4": (NVFP4_GATEUP_BYTES, NVFP4_DOWN_BYTES),
                 "int4-g32": (INT4_G32_GATEUP_BYTES, INT4_G32_DOWN_BYTES),
                 "int4-asym": (INT4_ASYM_GATEUP_BYTES, INT4_ASYM_DOWN_BYTES),
-                "int8": (INT8_GATEUP_BYTES, INT8_DOWN_BYTES)}
+                "int8": (INT8_GATEUP_BYTES, INT8_DOWN_BYTES),
+                "nvfp4-csf": (NVFP4_CSF_GATEUP_BYTES, NVFP4_CSF_DOWN_BYTES)}
 FLOP_PER_SLOT = 3 * 2 * H * F
 # Timed steps that record the gate/up kernel's events: every recorded HIP
 # event drains the stream for a few microseconds, so only every
@@ -150,19 +156,42 @@ def nvfp4_banks(copies, dev, seed0):
             mats.append(B.bank_nvfp4(q, s, g))
         f = B.ffn(*mats)
         f.scale_tensors = [m._keep[1] for m in mats]     # gate, up, down scale bytes
+        f.code_tensors = [m._keep[0] for m in mats]
+        f.gs_tensors = [m._keep[2] for m in mats]
         out.append(f)
     return out
+
+
+def csf_banks(nv, dev, seed0):
+    """NVFP4 banks with random compressed scales read in place (the codes and
+    global scales of `nv`): per copy the bank, and per matrix the inputs of
+    its per-step row index (exceptions, starts, R, C, row index buffer)."""
+    banks, idx = [], []
+    for c, bank in enumerate(nv):
+        mats, ins = [], []
+        for i, scale in enumerate(bank.scale_tensors):
+            R, C = scale.shape[1], scale.shape[2]
+            fx, ex, st = synth.csf_random(E, R, C, seed0 + 10 * c + i, dev)
+            ri = torch.zeros((E, R + 1), dtype=torch.int32, device=dev)
+            mats.append(B.bank_nvfp4_csf(bank.code_tensors[i], fx, ex, ri, bank.gs_tensors[i]))
+            ins.append((ex, st, R, C, ri))
+        banks.append(B.ffn(*mats))
+        idx.append(ins)
+    return banks, idx
 
 
 def touched_experts(logits_cpu):
     return int(torch.unique(torch.topk(logits_cpu, K, dim=1).indices).numel())
 
 
-def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf=None):
+def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf=None,
+              csf_mode="expand"):
     """Times `steps` layer passes. route_mode: 'logits' (fresh N(0,1) logits
     per step) or 'weights' (router weight + fixed batch). csf: per bank copy,
-    CSF tensors of its three scale matrices; each step then expands the
-    routed experts' scales before the forward pass. Returns a dict."""
+    the compressed scales of its three matrices; each step then either
+    expands the routed experts' scales before the forward pass (csf_mode
+    'expand') or builds their row index for the kernels that read them in
+    place ('index'). Returns a dict."""
     n_in = steps + warmup
     x = synth.activations(T, H, act, 3 if route_mode == "weights" else 2).to(dev)
     if route_mode == "logits":
@@ -198,9 +227,14 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
         if csf:
             if csf_events:
                 hip.record(csf_events[0])
-            for (fx, ex, st), R, C, scale in csf[i % len(csf)]:
-                B.moe_csf_expand(fx, ex, st, R, C, out=scale, expert_offsets=perm.expert_offsets,
-                                 max_routed=min(E, T * K))
+            if csf_mode == "expand":
+                for (fx, ex, st), R, C, scale in csf[i % len(csf)]:
+                    B.moe_csf_expand(fx, ex, st, R, C, out=scale,
+                                     expert_offsets=perm.expert_offsets, max_routed=min(E, T * K))
+            else:
+                for ex, st, R, C, ri in csf[i % len(csf)]:
+                    B.moe_csf_row_index(ex, st, R, C, out=ri, expert_offsets=perm.expert_offsets,
+                                        max_routed=min(E, T * K))
             if csf_events:
                 hip.record(csf_events[1])
         B.moe_w4a16_forward(banks[i % len(banks)], x, w, perm, out=out, ws=ws, events=events)
@@ -240,9 +274,10 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
              layer_TFLOPs=float(T * K * FLOP_PER_SLOT / (ms * 1e-3) / 1e12))
     r["gateup_frac_hbm"] = r["gateup_GBps"] * 1e9 / HBM_PEAK
     if csf:
-        cb = 2 * csf_bytes(F, H // 16) + csf_bytes(H, F // 16)
         r["csf_ms"] = float(csf_ms.mean())
-        r["csf_GBps"] = float(np.mean(U[:nb] * cb / (csf_ms * 1e-3)) / 1e9)
+        if csf_mode == "expand":
+            cb = 2 * csf_bytes(F, H // 16) + csf_bytes(H, F // 16)
+            r["csf_GBps"] = float(np.mean(U[:nb] * cb / (csf_ms * 1e-3)) / 1e9)
     return r
 
 
@@ -419,7 +454,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "nvfp4", "nvfp4-csf", "int4-g32",
+                    choices=["decode", "prefill", "nvfp4", "nvfp4-csf", "nvfp4-csf-expand", "int4-g32",
                              "int4-asym", "int8", "stack"])
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
@@ -450,22 +485,26 @@ def main():
     int4 = int4_banks(2, dev, 500)
     jobs = []
     main_T = args.tokens or {"decode": 64, "prefill": 2048, "nvfp4": 256, "nvfp4-csf": 64,
+                             "nvfp4-csf-expand": 64,
                              "int4-g32": 64, "int4-asym": 64, "int8": 64,
                              "stack": 4096}[args.workload]
     spec = {"decode": ("f16", "logits", "int4"), "prefill": ("bf16", "weights", "int4"),
-            "nvfp4": ("bf16", "logits", "nvfp4"), "nvfp4-csf": ("bf16", "logits", "nvfp4"),
+            "nvfp4": ("bf16", "logits", "nvfp4"), "nvfp4-csf": ("bf16", "logits", "nvfp4-csf"),
+            "nvfp4-csf-expand": ("bf16", "logits", "nvfp4"),
             "int4-g32": ("f16", "logits", "int4-g32"), "int4-asym": ("f16", "logits", "int4-asym"),
             "int8": ("f16", "logits", "int8"),
             "stack": ("bf16", "weights", "int4")}
     jobs.append((args.workload, main_T))
     if not args.no_sweep:
         for wl, T in (("decode", 1), ("decode", 8), ("decode", 64), ("prefill", 2048),
-                      ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("int4-g32", 64),
+                      ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("nvfp4-csf-expand", 64),
+                      ("int4-g32", 64),
                       ("int4-asym", 64), ("int8", 64), ("stack", 32), ("stack", 4096)):
             if (wl, T) != (args.workload, main_T):
                 jobs.append((wl, T))
     nv = None
     nv_csf = None
+    nv_csf_in = None
     variants = {}
     stack = None
     results = []
@@ -478,19 +517,23 @@ def main():
             results.append(run_stack(stack, T, max(5, steps // 4), max(2, args.warmup // 4),
                                      hip, dev, use_graph=not args.no_graph))
         else:
-            if fmt == "nvfp4" and nv is None:
+            if fmt in ("nvfp4", "nvfp4-csf") and nv is None:
                 nv = nvfp4_banks(2, dev, 900)
             if fmt in ("int4-g32", "int4-asym", "int8") and fmt not in variants:
                 variants[fmt] = variant_banks(
                     2, dev, {"int4-g32": 2000, "int4-asym": 2100, "int8": 2200}[fmt], fmt)
             banks = int4 if fmt == "int4" else (nv if fmt == "nvfp4" else variants.get(fmt))
-            csf = None
-            if wl == "nvfp4-csf":
+            csf, csf_mode = None, "expand"
+            if wl == "nvfp4-csf-expand":
                 if nv_csf is None:
                     nv_csf = csf_inputs(nv, dev, 1900)
                 csf = nv_csf
+            if wl == "nvfp4-csf":
+                if nv_csf_in is None:
+                    nv_csf_in = csf_banks(nv, dev, 1900)
+                banks, csf, csf_mode = nv_csf_in[0], nv_csf_in[1], "index"
             results.append(run_layer("%s T=%d" % (wl, T), banks, T, act, rmode, steps,
-                                     args.warmup, hip, dev, fmt, csf))
+                                     args.warmup, hip, dev, fmt, csf, csf_mode))
         print("# %s" % json.dumps(results[-1]), file=sys.stderr, flush=True)
 
     head = results[0]

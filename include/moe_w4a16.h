@@ -81,13 +81,27 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  *   qweight: int8 [E][n][k], two's complement, input j at byte j.
  *   scale:   bf16 [E][n][k/128].   weight = q * scale.
  *
+ * MOE_W_NVFP4_CSF -- MOE_W_NVFP4_G16 with the block scales left in the
+ *   compressed scale format of page "Step-5-Preview-NVFP4-Local" ("Format",
+ *   "Modifications" item 1; see moe_csf_expand), read directly by the
+ *   kernels instead of being expanded first.
+ *   qweight, global_scale: as MOE_W_NVFP4_G16;
+ *   scale: the CSF `fixed` tensor U8 [E][n/16][16*(1 + C/2)], C = k/16,
+ *            scale_expert_stride its expert stride in bytes (>= n*(1 + C/2)),
+ *            scale_row_stride unused (0); n % 16 == 0;
+ *   csf_exceptions: the exceptions U32 (row*C + col) | byte << 24, grouped
+ *            by expert and sorted by position within it (NULL if none);
+ *   csf_row_index: I32 [E][n+1] from moe_csf_row_index (the exceptions of
+ *            row r of expert e are [row_index[e][r], row_index[e][r+1])).
+ *
  * The decode kernels (the GEMV) serve every format; the prefill GEMM serves
  * MOE_W_INT4_G128 and MOE_W_NVFP4_G16, and the other formats run the GEMV
  * at every batch size.
  */
 typedef enum {
     MOE_W_INT4_G128 = 1, MOE_W_NVFP4_G16 = 2, MOE_W_BF16 = 3,
-    MOE_W_INT4_G32 = 4, MOE_W_INT4_G128_ASYM = 5, MOE_W_INT8_G128 = 6
+    MOE_W_INT4_G32 = 4, MOE_W_INT4_G128_ASYM = 5, MOE_W_INT8_G128 = 6,
+    MOE_W_NVFP4_CSF = 7
 } moe_wfmt_t;
 
 /* One bank of E matrices, each [n out][k in]. Strides are in bytes; the
@@ -105,6 +119,8 @@ typedef struct {
     int64_t scale_expert_stride, scale_row_stride;
     const uint8_t *zero_point;   /* MOE_W_INT4_G128_ASYM only, else NULL          */
     int64_t zero_point_expert_stride, zero_point_row_stride;
+    const uint32_t *csf_exceptions;  /* MOE_W_NVFP4_CSF only, else NULL          */
+    const int32_t *csf_row_index;    /* MOE_W_NVFP4_CSF only, else NULL          */
 } moe_weight_desc_t;
 
 /* The three projections of a SwiGLU bank: gate and up are [F][H], down is
@@ -348,6 +364,25 @@ moe_status_t moe_csf_expand(const uint8_t *fixed, const uint32_t *exceptions,
                             int64_t n_exceptions, const int64_t *starts, int E, int R, int C,
                             const int32_t *expert_offsets, int max_routed_experts,
                             uint8_t *out, void *stream);
+
+/*
+ * moe_csf_row_index -- the per-row exception ranges of a compressed scale
+ * tensor (same tensors as moe_csf_expand), which let the kernels read a
+ * MOE_W_NVFP4_CSF bank's scales without expanding them:
+ *   row_index[e][r] = the first x in [starts[e], starts[e+1]) whose
+ *   position (low 24 bits) is >= r*C, for r = 0..R,
+ * so the exceptions of row r are [row_index[e][r], row_index[e][r+1]).
+ * Each expert's exceptions must be sorted by position (the order the
+ * format's exceptions are stored in). exceptions, n_exceptions, starts, E,
+ * R, C, expert_offsets, max_routed_experts: as in moe_csf_expand (only
+ * routed experts are indexed when expert_offsets is given; the rows of the
+ * others are left unchanged); row_index I32 [E][R+1], 4-byte aligned,
+ * caller-owned. Enqueues one kernel. Errors as moe_csf_expand.
+ */
+moe_status_t moe_csf_row_index(const uint32_t *exceptions, int64_t n_exceptions,
+                               const int64_t *starts, int E, int R, int C,
+                               const int32_t *expert_offsets, int max_routed_experts,
+                               int32_t *row_index, void *stream);
 
 #ifdef __cplusplus
 }

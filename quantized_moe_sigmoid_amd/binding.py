@@ -16,12 +16,13 @@ _lib = None
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F16, MOE_BF16, MOE_F32 = 1, 2, 3
 MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16, MOE_W_INT4_G32, MOE_W_INT4_G128_ASYM = 1, 2, 3, 4, 5
-MOE_W_INT8_G128 = 6
+MOE_W_INT8_G128, MOE_W_NVFP4_CSF = 6, 7
 
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_route_workspace",
            "moe_route_topk", "moe_permute_sizes",
            "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_w4a16_forward_profiled",
-           "moe_round_activations", "moe_rmsnorm", "moe_dequant", "moe_csf_expand")
+           "moe_round_activations", "moe_rmsnorm", "moe_dequant", "moe_csf_expand",
+           "moe_csf_row_index")
 MOE_FORWARD_STAGES = 4
 
 _DT = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
@@ -42,7 +43,8 @@ class WeightDesc(ctypes.Structure):
                 ("qweight_expert_stride", ctypes.c_int64), ("qweight_row_stride", ctypes.c_int64),
                 ("scale_expert_stride", ctypes.c_int64), ("scale_row_stride", ctypes.c_int64),
                 ("zero_point", ctypes.c_void_p),
-                ("zero_point_expert_stride", ctypes.c_int64), ("zero_point_row_stride", ctypes.c_int64)]
+                ("zero_point_expert_stride", ctypes.c_int64), ("zero_point_row_stride", ctypes.c_int64),
+                ("csf_exceptions", ctypes.c_void_p), ("csf_row_index", ctypes.c_void_p)]
 
 
 class FfnDesc(ctypes.Structure):
@@ -86,11 +88,12 @@ def lib():
         L.moe_rmsnorm.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, vp]
         L.moe_dequant.argtypes = [P(WeightDesc), i32, vp, vp]
         L.moe_csf_expand.argtypes = [vp, vp, i64, vp, i32, i32, i32, vp, i32, vp, vp]
+        L.moe_csf_row_index.argtypes = [vp, i64, vp, i32, i32, i32, vp, i32, vp, vp]
         for name in ("moe_router_logits", "moe_route_workspace", "moe_route_topk",
                      "moe_permute_sizes", "moe_permute", "moe_forward_plan",
                      "moe_w4a16_forward", "moe_w4a16_forward_profiled",
                      "moe_round_activations", "moe_rmsnorm", "moe_dequant",
-                     "moe_csf_expand"):
+                     "moe_csf_expand", "moe_csf_row_index"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -153,6 +156,20 @@ def bank_nvfp4(qweight, scale, global_scale):
                    global_scale.data_ptr(), qweight.stride(0), qweight.stride(1),
                    scale.stride(0), scale.stride(1))
     d._keep = (qweight, scale, global_scale)
+    return d
+
+
+def bank_nvfp4_csf(qweight, fixed, exceptions, row_index, global_scale):
+    """MOE_W_NVFP4_CSF: qweight uint8 [E, n, k/2], the CSF fixed tensor uint8
+    [E, n/16, 16*(1+k/32)], exceptions int32/uint32 [m] (or None), the row
+    index int32 [E, n+1] from moe_csf_row_index, global_scale float [E]."""
+    E, n, kh = qweight.shape
+    m = exceptions.numel() if exceptions is not None else 0
+    d = WeightDesc(MOE_W_NVFP4_CSF, E, n, kh * 2, qweight.data_ptr(), fixed.data_ptr(),
+                   global_scale.data_ptr(), qweight.stride(0), qweight.stride(1),
+                   fixed.stride(0), 0, None, 0, 0,
+                   exceptions.data_ptr() if m else None, row_index.data_ptr())
+    d._keep = (qweight, fixed, exceptions, row_index, global_scale)
     return d
 
 
@@ -315,6 +332,20 @@ def moe_dequant(desc, expert, out=None, device=None):
         out = torch.empty((desc.n, desc.k), dtype=torch.float32, device=device or "cuda")
     _check(lib().moe_dequant(ctypes.byref(desc), expert, _ptr(out), _stream(out.device)),
            "moe_dequant")
+    return out
+
+
+def moe_csf_row_index(exceptions, starts, R, C, out=None, expert_offsets=None, max_routed=0):
+    """Per-row exception ranges int32 [E, R+1] of a CSF scale tensor (see
+    moe_csf_expand for the arguments)."""
+    E = starts.numel() - 1
+    if out is None:
+        out = torch.zeros((E, R + 1), dtype=torch.int32, device=starts.device)
+    n = exceptions.numel() if exceptions is not None else 0
+    _check(lib().moe_csf_row_index(_ptr(exceptions) if n else None, n, _ptr(starts), E, R, C,
+                                   _ptr(expert_offsets), int(max_routed), _ptr(out),
+                                   _stream(out.device)),
+           "moe_csf_row_index")
     return out
 
 

@@ -19,6 +19,9 @@ moe_status_t launch_csf_expand(const uint8_t *fixed, const uint32_t *exceptions,
                                const int64_t *starts, int E, int R, int C,
                                const int32_t *expert_offsets, int max_routed, uint8_t *out,
                                hipStream_t s);
+moe_status_t launch_csf_row_index(const uint32_t *exceptions, int64_t n, const int64_t *starts,
+                                  int E, int R, int C, const int32_t *expert_offsets,
+                                  int max_routed, int32_t *row_index, hipStream_t s);
 moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
                                  hipStream_t s, const std::function<moe_status_t(int)> &mark);
@@ -81,6 +84,17 @@ moe_status_t check_bank(const moe_weight_desc_t &d, int E, int n, int k) {
     } else if (d.fmt == MOE_W_INT4_G32) {
         if (k % 32) return MOE_ERR_INVALID_ARG;
         if (d.qweight_row_stride < k / 2 || d.scale_row_stride < (k / 32) * 2)
+            return MOE_ERR_INVALID_ARG;
+    } else if (d.fmt == MOE_W_NVFP4_CSF) {
+        // codes as NVFP4; scales: the CSF fixed tensor, 16-row slabs
+        if (k % 16 || n % 16) return MOE_ERR_INVALID_ARG;
+        if (k % 32) return MOE_ERR_UNSUPPORTED;
+        if ((int64_t)n * (k / 16) >= ((int64_t)1 << 24)) return MOE_ERR_UNSUPPORTED;
+        if (!d.global_scale || !aligned(d.global_scale, 4) || !d.csf_row_index ||
+            !aligned(d.csf_row_index, 4) || (d.csf_exceptions && !aligned(d.csf_exceptions, 4)))
+            return MOE_ERR_INVALID_ARG;
+        if (d.qweight_row_stride < k / 2 ||
+            d.scale_expert_stride < (int64_t)n * (1 + k / 32))
             return MOE_ERR_INVALID_ARG;
     } else if (d.fmt == MOE_W_NVFP4_G16) {
         if (k % 16) return MOE_ERR_INVALID_ARG;
@@ -213,7 +227,7 @@ const char *moe_status_string(int status) {
     }
 }
 
-int moe_abi_version(void) { return 2; }
+int moe_abi_version(void) { return 3; }
 
 static moe_status_t check_router(const void *x, int x_dtype, const float *wT, int T, int H,
                                  int E) {
@@ -420,6 +434,23 @@ moe_status_t moe_csf_expand(const uint8_t *fixed, const uint32_t *exceptions,
         return MOE_ERR_INVALID_ARG;
     return launch_csf_expand(fixed, exceptions, n_exceptions, starts, E, R, C, expert_offsets,
                              max_routed_experts, out, (hipStream_t)stream);
+}
+
+moe_status_t moe_csf_row_index(const uint32_t *exceptions, int64_t n_exceptions,
+                               const int64_t *starts, int E, int R, int C,
+                               const int32_t *expert_offsets, int max_routed_experts,
+                               int32_t *row_index, void *stream) {
+    if (!starts || !row_index || n_exceptions < 0 || (n_exceptions > 0 && !exceptions))
+        return MOE_ERR_INVALID_ARG;
+    if (E < 1 || E > kMaxExperts || R < 16 || R % 16 || C < 16 || C % 16)
+        return MOE_ERR_INVALID_ARG;
+    if ((int64_t)R * C >= ((int64_t)1 << 24)) return MOE_ERR_UNSUPPORTED;   // 24-bit positions
+    if (max_routed_experts < 0) return MOE_ERR_INVALID_ARG;
+    if (!aligned(row_index, 4) || !aligned(starts, 8) || (exceptions && !aligned(exceptions, 4)) ||
+        (expert_offsets && !aligned(expert_offsets, 4)))
+        return MOE_ERR_INVALID_ARG;
+    return launch_csf_row_index(exceptions, n_exceptions, starts, E, R, C, expert_offsets,
+                                max_routed_experts, row_index, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -100,6 +100,40 @@ __global__ void __launch_bounds__(256) csf_expand_kernel(
     }
 }
 
+// Row ranges of the exceptions: thread (e, r) finds by binary search the
+// first exception of expert e at or past position r * C (each expert's
+// exceptions are sorted by position), r = 0..R.
+__global__ void __launch_bounds__(256) csf_row_index_kernel(
+    const uint32_t *__restrict__ exceptions, int64_t n, const int64_t *__restrict__ starts, int E,
+    int R, int C, const int32_t *__restrict__ expert_offsets, int compact,
+    int32_t *__restrict__ row_index) {
+    const int e = compact ? csf_routed_expert(expert_offsets, E, blockIdx.y) : (int)blockIdx.y;
+    if (e < 0 || csf_expert_skipped(expert_offsets, e)) return;
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r > R) return;
+    int64_t lo = starts[e], hi = starts[e + 1];
+    lo = lo < 0 ? 0 : (lo > n ? n : lo);
+    hi = hi < lo ? lo : (hi > n ? n : hi);
+    const uint32_t target = (uint32_t)r * (uint32_t)C;
+    while (lo < hi) {                            // first x with pos(x) >= target
+        const int64_t mid = lo + (hi - lo) / 2;
+        if ((exceptions[mid] & 0xFFFFFFu) < target) lo = mid + 1;
+        else hi = mid;
+    }
+    row_index[(size_t)e * (R + 1) + r] = (int32_t)lo;
+}
+
+moe_status_t launch_csf_row_index(const uint32_t *exceptions, int64_t n, const int64_t *starts,
+                                  int E, int R, int C, const int32_t *expert_offsets,
+                                  int max_routed, int32_t *row_index, hipStream_t s) {
+    const bool compact = expert_offsets && max_routed > 0 && max_routed < E;
+    const dim3 grid((R + 1 + 255) / 256, compact ? max_routed : E);
+    hipLaunchKernelGGL(csf_row_index_kernel, grid, dim3(256), 0, s, exceptions, n, starts, E, R,
+                       C, expert_offsets, compact ? 1 : 0, row_index);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
 moe_status_t launch_csf_expand(const uint8_t *fixed, const uint32_t *exceptions, int64_t n,
                                const int64_t *starts, int E, int R, int C,
                                const int32_t *expert_offsets, int max_routed, uint8_t *out,

@@ -85,6 +85,14 @@ __device__ __forceinline__ void int4_biased_pairs_masked(uint32_t w, uint32_t m,
     out[3] = ((w >> 12) & m) ^ K;
 }
 
+// ---- NVFP4 family ------------------------------------------------------------
+// NVFP4_CSF: the same codes with the block scales in the compressed scale
+// format (base + 4-bit code per scale, exceptions), read in place.
+__host__ __device__ constexpr bool is_csf(int fmt) { return fmt == MOE_W_NVFP4_CSF; }
+__host__ __device__ constexpr bool is_nvfp4(int fmt) {
+    return fmt == MOE_W_NVFP4_G16 || fmt == MOE_W_NVFP4_CSF;
+}
+
 // ---- int8 -------------------------------------------------------------------
 __host__ __device__ constexpr bool is_int8(int fmt) { return fmt == MOE_W_INT8_G128; }
 // Inputs per 16-byte weight chunk: 32 for the 4-bit formats, 16 for int8.

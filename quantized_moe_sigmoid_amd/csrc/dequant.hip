@@ -3,7 +3,8 @@
 // It runs the forward kernels' own decoders: int4 words go through the
 // biased fp16 pairs (1032 + q for the signed forms, 1024 + q for the
 // unsigned one, then the bias, with the zero point, is removed exactly) and
-// the scale is applied as one exact float32 product; int8 bytes go through
+// the scale is applied as one exact float32 product (compressed NVFP4 scales
+// are decoded from base, code and exceptions first); int8 bytes go through
 // the fp16 pairs 1152 + q the same way; NVFP4 bytes go through the
 // hardware E2M1 pair conversion, the E4M3 scale multiplies exactly, and the
 // global scale is the single float32 rounding.
@@ -94,6 +95,40 @@ __global__ void __launch_bounds__(256) dequant_nvfp4_kernel(
     o[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// NVFP4 with compressed scales: the block's scale byte is the row's base
+// plus its 4-bit code (low nibble = even block), unless one of the row's
+// exceptions holds the position; then as dequant_nvfp4_kernel.
+__global__ void __launch_bounds__(256) dequant_nvfp4_csf_kernel(
+    const uint8_t *__restrict__ qw, int64_t qrow, const uint8_t *__restrict__ fixed,
+    const uint32_t *__restrict__ xc, const int32_t *__restrict__ ri,
+    const float *__restrict__ gsp, int n, int k, float *__restrict__ out) {
+    const float gs = *gsp;
+    const int dwords = k / 8, C = k / 16;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)n * dwords) return;
+    const int r = (int)(idx / dwords), j = (int)(idx % dwords);
+    const int b = (8 * j) / 16;                              // block of these 8 inputs
+    const uint8_t *slab = fixed + (size_t)(r >> 4) * 16 * (1 + C / 2);
+    const uint32_t code = slab[16 + (r & 15) * (C / 2) + b / 2];
+    uint32_t sb = slab[r & 15] + ((b & 1) ? code >> 4 : code & 15u);
+    const uint32_t pos = (uint32_t)r * (uint32_t)C + (uint32_t)b;
+    for (int x = ri[r]; x < ri[r + 1]; ++x)
+        if ((xc[x] & 0xFFFFFFu) == pos) sb = xc[x] >> 24;
+    const float bs = e4m3_to_f32(sb);
+    const uint32_t w = *(const uint32_t *)(qw + r * qrow + 4 * (int64_t)j);
+    const uint32_t p[4] = {fp4_pair<MOE_BF16, 0>(w), fp4_pair<MOE_BF16, 1>(w),
+                           fp4_pair<MOE_BF16, 2>(w), fp4_pair<MOE_BF16, 3>(w)};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = (bf16_bits_to_f32(p[i] & 0xFFFF) * bs) * gs;
+        v[2 * i + 1] = (bf16_bits_to_f32(p[i] >> 16) * bs) * gs;
+    }
+    float4 *o = (float4 *)(out + (int64_t)r * k + 8 * (int64_t)j);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out,
                             hipStream_t s) {
     const uint8_t *qw = (const uint8_t *)d.qweight + (int64_t)e * d.qweight_expert_stride;
@@ -115,6 +150,11 @@ moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out,
     else if (d.fmt == MOE_W_INT8_G128)
         hipLaunchKernelGGL(dequant_int8_kernel, grid, dim3(256), 0, s, qw, d.qweight_row_stride,
                            sc, d.scale_row_stride, d.n, d.k, out);
+    else if (d.fmt == MOE_W_NVFP4_CSF)
+        hipLaunchKernelGGL(dequant_nvfp4_csf_kernel, grid, dim3(256), 0, s, qw,
+                           d.qweight_row_stride, sc, d.csf_exceptions,
+                           d.csf_row_index + (int64_t)e * (d.n + 1), d.global_scale + e, d.n,
+                           d.k, out);
     else
         hipLaunchKernelGGL(dequant_nvfp4_kernel, grid, dim3(256), 0, s, qw, d.qweight_row_stride,
                            sc, d.scale_row_stride, d.global_scale + e, d.n, d.k, out);

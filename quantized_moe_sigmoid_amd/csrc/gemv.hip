@@ -23,7 +23,10 @@
 //   same way: acc += s_g * (dot - BIAS * sum x).
 // NVFP4: the hardware pair conversion gives exact E2M1 values; the E4M3
 //   block scale applies per 16 inputs in float32, the global scale once at
-//   the end.
+//   the end. With compressed scales (NVFP4_CSF) a chunk's two scale bytes
+//   are its row's base plus the two 4-bit codes of one byte, unless one of
+//   the row's exceptions holds that position (the first two are kept in
+//   registers per row; rows with more walk the rest of their list).
 #include <functional>
 
 #include "decode.h"
@@ -40,7 +43,30 @@ struct GemvMat {                 // one projection bank, byte addressed
     int64_t qe, qr, se, sr;      // expert / row strides (bytes)
     const uint8_t *z;            // asymmetric int4 zero points or null
     int64_t ze, zr;
+    const uint32_t *xc;          // NVFP4_CSF: exceptions and their row index
+    const int32_t *ri;
 };
+
+// NVFP4_CSF: the two scale bytes of chunk c (blocks p0 = r*C + 2c, p0 + 1
+// of its row): base + code, or an exception's byte. ex0 / ex1: the row's
+// first two exceptions (0xFFFFFFFF: none; a 24-bit position never reaches
+// 0xFFFFFF), [x2, xe): the rest of the row's exceptions.
+__device__ __forceinline__ uint32_t csf_scale_pair(uint32_t code, uint32_t base, uint32_t ex0,
+                                                   uint32_t ex1, int x2, int xe,
+                                                   const uint32_t *xc, uint32_t p0) {
+    uint32_t b0 = base + (code & 15u), b1 = base + (code >> 4);
+    const uint32_t q0 = ex0 & 0xFFFFFFu, q1 = ex1 & 0xFFFFFFu;
+    b0 = q0 == p0 ? ex0 >> 24 : b0;
+    b1 = q0 == p0 + 1 ? ex0 >> 24 : b1;
+    b0 = q1 == p0 ? ex1 >> 24 : b0;
+    b1 = q1 == p0 + 1 ? ex1 >> 24 : b1;
+    for (int x = x2; x < xe; ++x) {              // rows with more than two: rare
+        const uint32_t v = xc[x], q = v & 0xFFFFFFu;
+        b0 = q == p0 ? v >> 24 : b0;
+        b1 = q == p0 + 1 ? v >> 24 : b1;
+    }
+    return b0 | (b1 << 8);
+}
 
 // LDS unit (16 bytes = 4 pair dwords = 8 inputs) j of input chunk c (UPC
 // units: 4 for 32-input chunks, 2 for int8's 16). For a fixed j the LPR
@@ -275,9 +301,14 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
     const int nch = NIT > 0 ? NIT * LPR : kin / CI;
     const int nit = NIT > 0 ? NIT : (nch + LPR - 1) / LPR;
     const __amdgpu_buffer_rsrc_t rqa = buffer_rsrc(A.q + e * A.qe, (int64_t)n_rows * A.qr);
-    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(A.s + e * A.se, (int64_t)n_rows * A.sr);
+    constexpr bool kCsf = is_csf(FMT);
+    // NVFP4_CSF: an expert's fixed tensor is n_rows * (1 + C/2) bytes, C = kin/16
+    const int64_t csf_row_bytes = 1 + kin / 32;
+    const __amdgpu_buffer_rsrc_t rsa =
+        buffer_rsrc(A.s + e * A.se, (int64_t)n_rows * (kCsf ? csf_row_bytes : A.sr));
     const __amdgpu_buffer_rsrc_t rqb = buffer_rsrc(B.q + e * B.qe, (int64_t)n_rows * B.qr);
-    const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(B.s + e * B.se, (int64_t)n_rows * B.sr);
+    const __amdgpu_buffer_rsrc_t rsb =
+        buffer_rsrc(B.s + e * B.se, (int64_t)n_rows * (kCsf ? csf_row_bytes : B.sr));
     // per pass: byte offsets of the lane's row (rows past the matrix, never
     // stored, read its last row)
     int qra[RPW], sra[RPW], qrb[RPW], srb[RPW], zra[RPW], zrb[RPW];
@@ -285,11 +316,39 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
     for (int ps = 0; ps < RPW; ++ps) {
         const int r = row_of(ps) < n_rows ? row_of(ps) : n_rows - 1;
         qra[ps] = r * (int)A.qr;
-        sra[ps] = r * (int)A.sr;
         qrb[ps] = r * (int)B.qr;
-        srb[ps] = r * (int)B.sr;
+        if (kCsf) {                              // the row's codes in its 16-row slab
+            sra[ps] = srb[ps] = (r >> 4) * 16 * (int)csf_row_bytes + 16 + (r & 15) * (kin / 32);
+        } else {
+            sra[ps] = r * (int)A.sr;
+            srb[ps] = r * (int)B.sr;
+        }
         zra[ps] = r * (int)A.zr;
         zrb[ps] = r * (int)B.zr;
+    }
+    // NVFP4_CSF: per pass and matrix the row's base byte, its first two
+    // exceptions and the range of the others
+    uint32_t bsa[kCsf ? RPW : 1], bsb[kCsf ? RPW : 1], e0a[kCsf ? RPW : 1], e1a[kCsf ? RPW : 1],
+        e0b[kCsf ? RPW : 1], e1b[kCsf ? RPW : 1];
+    int x2a[kCsf ? RPW : 1], xea[kCsf ? RPW : 1], x2b[kCsf ? RPW : 1], xeb[kCsf ? RPW : 1];
+    if constexpr (kCsf) {
+        auto row_state = [&](const GemvMat &M, int r, uint32_t &bs, uint32_t &e0, uint32_t &e1,
+                             int &x2, int &xe) {
+            const uint8_t *fx = M.s + e * M.se;
+            bs = fx[(size_t)(r >> 4) * 16 * csf_row_bytes + (r & 15)];
+            const int32_t *ri = M.ri + (size_t)e * (n_rows + 1) + r;
+            const int xl = ri[0], xh = ri[1];
+            e0 = xl < xh ? M.xc[xl] : 0xFFFFFFFFu;
+            e1 = xl + 1 < xh ? M.xc[xl + 1] : 0xFFFFFFFFu;
+            x2 = xl + 2;
+            xe = xh;
+        };
+#pragma unroll
+        for (int ps = 0; ps < RPW; ++ps) {
+            const int r = row_of(ps) < n_rows ? row_of(ps) : n_rows - 1;
+            row_state(A, r, bsa[ps], e0a[ps], e1a[ps], x2a[ps], xea[ps]);
+            if (GATEUP) row_state(B, r, bsb[ps], e0b[ps], e1b[ps], x2b[ps], xeb[ps]);
+        }
     }
     // asymmetric int4: one zero-point byte per 128 inputs, streamed with the scales
     constexpr bool kZ = int4_asym(FMT);
@@ -309,16 +368,23 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
         const int pq = ok ? ps : 0;
         wa[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                    rqa, ok ? qra[pq] + 16 * c : kOutOfRange, 0, 0));
-        sa[j] = __builtin_amdgcn_raw_buffer_load_b16(
-            rsa, ok ? sra[pq] + scale_offset<FMT>(c) : kOutOfRange, 0, 0);
+        if constexpr (kCsf)                      // one code byte: the chunk's two blocks
+            sa[j] = __builtin_amdgcn_raw_buffer_load_b8(rsa, ok ? sra[pq] + c : kOutOfRange, 0, 0);
+        else
+            sa[j] = __builtin_amdgcn_raw_buffer_load_b16(
+                rsa, ok ? sra[pq] + scale_offset<FMT>(c) : kOutOfRange, 0, 0);
         if constexpr (kZ)
             za[j] = __builtin_amdgcn_raw_buffer_load_b8(rza, ok ? zra[pq] + (c >> 2) : kOutOfRange,
                                                         0, 0);
         if (GATEUP) {
             wb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                        rqb, ok ? qrb[pq] + 16 * c : kOutOfRange, 0, 0));
-            sb[j] = __builtin_amdgcn_raw_buffer_load_b16(
-                rsb, ok ? srb[pq] + scale_offset<FMT>(c) : kOutOfRange, 0, 0);
+            if constexpr (kCsf)
+                sb[j] = __builtin_amdgcn_raw_buffer_load_b8(rsb, ok ? srb[pq] + c : kOutOfRange, 0,
+                                                            0);
+            else
+                sb[j] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rsb, ok ? srb[pq] + scale_offset<FMT>(c) : kOutOfRange, 0, 0);
             if constexpr (kZ)
                 zb[j] = __builtin_amdgcn_raw_buffer_load_b8(
                     rzb, ok ? zrb[pq] + (c >> 2) : kOutOfRange, 0, 0);
@@ -389,7 +455,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc_a[t] = acc_b[t] = 0.0f;
     float ga = 1.0f, gb = 1.0f;
-    if (FMT == MOE_W_NVFP4_G16) {
+    if (is_nvfp4(FMT)) {
         ga = A.gs[e];
         if (GATEUP) gb = B.gs[e];
     }
@@ -432,10 +498,21 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
             ChunkDot<ACT, FMT> da, db;
             da.template decode<X16>(make_uint4(wa[j].x, wa[j].y, wa[j].z, wa[j].w), kv, kv1);
             float a0, a1, b0 = 0.0f, b1 = 0.0f;
-            chunk_scales<ACT, FMT, X16>(sa[j], kZ ? za[j] : 0u, a0, a1);
+            uint32_t two_a = sa[j], two_b = sb[j];
+            if constexpr (kCsf) {
+                const int ps = NIT > 0 ? I / NIT : 0;
+                const int pp = ps < RPW ? ps : 0;
+                const int r = row_of(pp) < n_rows ? row_of(pp) : n_rows - 1;
+                const uint32_t p0 = (uint32_t)r * (uint32_t)(kin / 16) + 2u * (uint32_t)c;
+                two_a = csf_scale_pair(sa[j], bsa[pp], e0a[pp], e1a[pp], x2a[pp], xea[pp], A.xc, p0);
+                if (GATEUP)
+                    two_b = csf_scale_pair(sb[j], bsb[pp], e0b[pp], e1b[pp], x2b[pp], xeb[pp], B.xc,
+                                           p0);
+            }
+            chunk_scales<ACT, FMT, X16>(two_a, kZ ? za[j] : 0u, a0, a1);
             if (GATEUP) {
                 db.template decode<X16>(make_uint4(wb[j].x, wb[j].y, wb[j].z, wb[j].w), kv, kv1);
-                chunk_scales<ACT, FMT, X16>(sb[j], kZ ? zb[j] : 0u, b0, b1);
+                chunk_scales<ACT, FMT, X16>(two_b, kZ ? zb[j] : 0u, b0, b1);
             }
             // slot j is consumed: refill it in place (the barrier keeps the
             // refill below the last use, so it reuses the same registers)
@@ -472,7 +549,7 @@ inline GemvMat gemv_mat(const moe_weight_desc_t &d) {
     return GemvMat{(const uint8_t *)d.qweight, (const uint8_t *)d.scale, d.global_scale,
                    d.qweight_expert_stride, d.qweight_row_stride, d.scale_expert_stride,
                    d.scale_row_stride, d.zero_point, d.zero_point_expert_stride,
-                   d.zero_point_row_stride};
+                   d.zero_point_row_stride, d.csf_exceptions, d.csf_row_index};
 }
 
 // Activation units, chunk sums (rounded up to 16 bytes) and the staging
@@ -551,6 +628,7 @@ moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int ac
             MOE_GEMV_FMT(MOE_BF16, MOE_W_INT4_G32);
             MOE_GEMV_FMT(MOE_BF16, MOE_W_INT4_G128_ASYM);
             MOE_GEMV_FMT(MOE_BF16, MOE_W_INT8_G128);
+            MOE_GEMV_FMT(MOE_BF16, MOE_W_NVFP4_CSF);
         }
     } else {
         switch (ex.gate.fmt) {
@@ -559,6 +637,7 @@ moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int ac
             MOE_GEMV_FMT(MOE_F16, MOE_W_INT4_G32);
             MOE_GEMV_FMT(MOE_F16, MOE_W_INT4_G128_ASYM);
             MOE_GEMV_FMT(MOE_F16, MOE_W_INT8_G128);
+            MOE_GEMV_FMT(MOE_F16, MOE_W_NVFP4_CSF);
         }
     }
 #undef MOE_GEMV_FMT

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert B.status_string(0) == "MOE_OK"
     assert B.status_string(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
     assert B.status_string(99) == "MOE_ERR_UNKNOWN"
@@ -297,6 +297,53 @@ def test_csf_expand_validation(L):
     ]
     for args, want in bad:
         assert F(*args) == want, args
+
+
+def test_csf_row_index_validation(L):
+    """Argument errors of moe_csf_row_index are found before any launch."""
+    F = L.moe_csf_row_index
+    p = ctypes.c_void_p(FAKE)
+    ok = (p, 4, p, 2, 32, 16, None, 0, p, None)
+    bad = [
+        ((None,) + ok[1:], B.MOE_ERR_INVALID_ARG),                     # exceptions with n > 0
+        (ok[:1] + (-1,) + ok[2:], B.MOE_ERR_INVALID_ARG),              # n < 0
+        (ok[:2] + (None,) + ok[3:], B.MOE_ERR_INVALID_ARG),            # starts
+        (ok[:3] + (0,) + ok[4:], B.MOE_ERR_INVALID_ARG),               # E
+        (ok[:4] + (24,) + ok[5:], B.MOE_ERR_INVALID_ARG),              # R % 16
+        (ok[:5] + (8,) + ok[6:], B.MOE_ERR_INVALID_ARG),               # C % 16
+        (ok[:4] + (4096, 4096) + ok[6:], B.MOE_ERR_UNSUPPORTED),       # R*C >= 2^24
+        (ok[:7] + (-1,) + ok[8:], B.MOE_ERR_INVALID_ARG),              # max_routed_experts
+        (ok[:8] + (None,) + ok[9:], B.MOE_ERR_INVALID_ARG),            # row_index
+        (ok[:8] + (ctypes.c_void_p(FAKE + 2),) + ok[9:], B.MOE_ERR_INVALID_ARG),  # alignment
+    ]
+    for args, want in bad:
+        assert F(*args) == want, args
+
+
+def _bank_csf(E, n, k, fstride=None, ri=True, gs=True):
+    """A MOE_W_NVFP4_CSF bank descriptor (fake pointers; code rows padded to
+    16 bytes)."""
+    fs = fstride if fstride is not None else n * (1 + k // 32)
+    qr = (k // 2 + 15) // 16 * 16
+    return B.WeightDesc(B.MOE_W_NVFP4_CSF, E, n, k, FAKE, FAKE, FAKE if gs else None,
+                        n * qr, qr, fs, 0, None, 0, 0, FAKE, FAKE if ri else None)
+
+
+def test_nvfp4_csf_banks_plan_the_decode_kernels_and_errors(L):
+    f = B.FfnDesc(_bank_csf(352, 1536, 4096), _bank_csf(352, 1536, 4096),
+                  _bank_csf(352, 4096, 1536))
+    st, tm_small, _ = _plan(f, T=8, act=B.MOE_BF16)
+    assert st == B.MOE_OK
+    st, tm_big, _ = _plan(f, T=2048, act=B.MOE_BF16)
+    assert st == B.MOE_OK and tm_big == tm_small          # the GEMV at every size
+    for g in (_bank_csf(352, 1536, 4096, ri=False),         # no row index
+              _bank_csf(352, 1536, 4096, gs=False),         # no global scale
+              _bank_csf(352, 1536, 4096, fstride=1536 * 100),   # fixed tensor too small
+              _bank_csf(352, 1528, 4096)):                  # rows not in 16-row slabs
+        f = B.FfnDesc(g, _bank_csf(352, 1536, 4096), _bank_csf(352, 4096, 1536))
+        assert _plan(f, act=B.MOE_BF16)[0] == B.MOE_ERR_INVALID_ARG, g.n
+    f = B.FfnDesc(_bank_csf(4, 64, 48), _bank_csf(4, 64, 48), _bank_csf(4, 48, 64))
+    assert _plan(f, act=B.MOE_BF16)[0] == B.MOE_ERR_UNSUPPORTED   # k % 32
 
 
 def _bank_v(fmt, E, n, k, srow=None, zrow=None, zp=True, qrow=None):

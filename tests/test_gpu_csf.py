@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from oracle import csf as OC
+from oracle import quant as OQ
 from oracle import router as OR
 from quantized_moe_sigmoid_amd import binding as B
 from quantized_moe_sigmoid_amd import synth
@@ -102,6 +103,90 @@ def test_nvfp4_forward_on_expanded_scales(dev):
         csf.append(B.bank_nvfp4(qd, sx, gsd))
     x = synth.activations(T, Hh, "bf16", 4).to(dev)
     lg = synth.router_logits(T, Ee, 4)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    outs = []
+    for banks in (raw, csf):
+        ffn = B.ffn(*banks)
+        tm, _ = B.moe_forward_plan(ffn, T, Kk, x.dtype)
+        perm = B.moe_permute(ids, Ee, tm)
+        outs.append(B.moe_w4a16_forward(ffn, x, w, perm).cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+# ------------------------------------- compressed scales read in place ---
+def _row_index(exc, starts, R, C, dev, offsets=None, max_routed=0):
+    ex, st = (torch.from_numpy(exc.view(np.int32)).to(dev), torch.from_numpy(starts).to(dev))
+    return B.moe_csf_row_index(ex, st, R, C, expert_offsets=offsets, max_routed=max_routed)
+
+
+@pytest.mark.parametrize("E,R,C,rate", [(3, 32, 16, 0.05), (5, 48, 96, 0.3), (2, 16, 256, 0.0),
+                                        (352, 1536, 256, 0.002), (352, 4096, 96, 0.002)])
+def test_csf_row_index_bitwise(dev, E, R, C, rate):
+    s = _scales(E, R, C, 30 + R + C, rate)
+    fixed, exc, starts = OC.encode(s)
+    got = _row_index(exc, starts, R, C, dev).cpu().numpy()
+    assert np.array_equal(got, OC.row_starts(exc, starts, E, R, C))
+
+
+def test_csf_row_index_routed_experts_only(dev):
+    E, R, C, T, K = 16, 32, 32, 3, 2
+    s = _scales(E, R, C, 8, 0.2)
+    fixed, exc, starts = OC.encode(s)
+    lg = synth.router_logits(T, E, 8)
+    ids, _ = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    perm = B.moe_permute(ids, E, 4)
+    routed = set(OR.topk_ids(lg, K).ravel().tolist())
+    want = OC.row_starts(exc, starts, E, R, C)
+    for max_routed in (0, min(E, T * K)):
+        out = torch.full((E, R + 1), -7, dtype=torch.int32, device=dev)
+        ex, st = torch.from_numpy(exc.view(np.int32)).to(dev), torch.from_numpy(starts).to(dev)
+        B.moe_csf_row_index(ex, st, R, C, out=out, expert_offsets=perm.expert_offsets,
+                            max_routed=max_routed)
+        got = out.cpu().numpy()
+        for e in range(E):
+            if e in routed:
+                assert np.array_equal(got[e], want[e]), (max_routed, e)
+            else:
+                assert np.all(got[e] == -7), (max_routed, e)
+
+
+def _csf_bank(q, s, gs, dev):
+    """An NVFP4_CSF bank of codes q, scale bytes s (host uint8 [E, n, k/16],
+    encoded by the oracle) and global scales gs (device)."""
+    E, n, C = s.shape
+    fixed, exc, starts = OC.encode(s)
+    ri = _row_index(exc, starts, n, C, dev)
+    ex = torch.from_numpy(exc.view(np.int32)).to(dev) if exc.size else None
+    return B.bank_nvfp4_csf(q, torch.from_numpy(fixed).to(dev), ex, ri, gs)
+
+
+def test_nvfp4_csf_dequant_bitwise(dev):
+    E, n, k = 3, 64, 512
+    q, _, gs = synth.packed_nvfp4_random(E, n, k, 31, dev)
+    s = _scales(E, n, k // 16, 31, 0.25)
+    bank = _csf_bank(q, s, gs, dev)
+    qh, gh = q.cpu().numpy(), gs.cpu().numpy()
+    for e in range(E):
+        got = B.moe_dequant(bank, e, device=dev).cpu().numpy()
+        want = OQ.dequant_nvfp4_fp32(qh[e], s[e], gh[e]).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), e
+
+
+@pytest.mark.parametrize("Ee,Hh,Ff,T,Kk,rate,act", [(6, 512, 256, 5, 3, 0.3, "bf16"),
+                                                    (6, 512, 256, 7, 2, 0.0, "f16"),
+                                                    (352, 4096, 1536, 64, 8, 0.002, "bf16")])
+def test_nvfp4_csf_forward_equals_raw_scales(dev, Ee, Hh, Ff, T, Kk, rate, act):
+    """The layer on compressed scales read in place is bitwise the layer on
+    the same scale bytes stored plainly (whose parity with the oracle the
+    NVFP4 tests establish)."""
+    raw, csf = [], []
+    for i, (n, k) in enumerate(((Ff, Hh), (Ff, Hh), (Hh, Ff))):
+        q, _, gs = synth.packed_nvfp4_random(Ee, n, k, 40 + i, dev)
+        s = _scales(Ee, n, k // 16, 40 + i, rate)
+        raw.append(B.bank_nvfp4(q, torch.from_numpy(s).to(dev), gs))
+        csf.append(_csf_bank(q, s, gs, dev))
+    x = synth.activations(T, Hh, act, 41).to(dev)
+    lg = synth.router_logits(T, Ee, 41)
     ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
     outs = []
     for banks in (raw, csf):
