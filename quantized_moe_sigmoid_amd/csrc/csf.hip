@@ -100,34 +100,39 @@ __global__ void __launch_bounds__(256) csf_expand_kernel(
     }
 }
 
-// Row ranges of the exceptions: thread (e, r) finds by binary search the
-// first exception of expert e at or past position r * C (each expert's
-// exceptions are sorted by position), r = 0..R.
+// Row ranges of the exceptions: one work group per expert walks its
+// exceptions (stored in ascending position); exception x, in row r_x, is
+// the first exception of every row after the previous exception's row up
+// to r_x, so it fills those entries; the rows after the last exception get
+// the expert's end. Every entry is written exactly once.
 __global__ void __launch_bounds__(256) csf_row_index_kernel(
     const uint32_t *__restrict__ exceptions, int64_t n, const int64_t *__restrict__ starts, int E,
     int R, int C, const int32_t *__restrict__ expert_offsets, int compact,
     int32_t *__restrict__ row_index) {
     const int e = compact ? csf_routed_expert(expert_offsets, E, blockIdx.y) : (int)blockIdx.y;
     if (e < 0 || csf_expert_skipped(expert_offsets, e)) return;
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r > R) return;
     int64_t lo = starts[e], hi = starts[e + 1];
     lo = lo < 0 ? 0 : (lo > n ? n : lo);
     hi = hi < lo ? lo : (hi > n ? n : hi);
-    const uint32_t target = (uint32_t)r * (uint32_t)C;
-    while (lo < hi) {                            // first x with pos(x) >= target
-        const int64_t mid = lo + (hi - lo) / 2;
-        if ((exceptions[mid] & 0xFFFFFFu) < target) lo = mid + 1;
-        else hi = mid;
+    int32_t *ri = row_index + (size_t)e * (R + 1);
+    // positions past the matrix belong to no row (row R stands for them all)
+    auto row = [&](int64_t x) {
+        const uint32_t q = (exceptions[x] & 0xFFFFFFu) / (uint32_t)C;
+        return q < (uint32_t)R ? (int)q : R;
+    };
+    for (int64_t x = lo + threadIdx.x; x < hi; x += 256) {
+        const int rx = row(x), rp = x > lo ? row(x - 1) : -1;
+        for (int r = rp + 1; r <= rx; ++r) ri[r] = (int32_t)x;
     }
-    row_index[(size_t)e * (R + 1) + r] = (int32_t)lo;
+    const int rl = hi > lo ? row(hi - 1) : -1;           // after the last row with one
+    for (int r = rl + 1 + threadIdx.x; r <= R; r += 256) ri[r] = (int32_t)hi;
 }
 
 moe_status_t launch_csf_row_index(const uint32_t *exceptions, int64_t n, const int64_t *starts,
                                   int E, int R, int C, const int32_t *expert_offsets,
                                   int max_routed, int32_t *row_index, hipStream_t s) {
     const bool compact = expert_offsets && max_routed > 0 && max_routed < E;
-    const dim3 grid((R + 1 + 255) / 256, compact ? max_routed : E);
+    const dim3 grid(1, compact ? max_routed : E);
     hipLaunchKernelGGL(csf_row_index_kernel, grid, dim3(256), 0, s, exceptions, n, starts, E, R,
                        C, expert_offsets, compact ? 1 : 0, row_index);
     MOE_LAUNCH_CHECK();

@@ -25,8 +25,11 @@
 //   block scale applies per 16 inputs in float32, the global scale once at
 //   the end. With compressed scales (NVFP4_CSF) a chunk's two scale bytes
 //   are its row's base plus the two 4-bit codes of one byte, unless one of
-//   the row's exceptions holds that position (the first two are kept in
-//   registers per row; rows with more walk the rest of their list).
+//   the row's exceptions holds that position: each lane keeps the (at most
+//   two) exceptions that fall in its own chunks in registers; a lane with
+//   more recomputes its partial sums at the end of the pass through the
+//   exact per-chunk lookup, in the same order, so every result is the one
+//   the expanded scales give.
 #include <functional>
 
 #include "decode.h"
@@ -48,19 +51,24 @@ struct GemvMat {                 // one projection bank, byte addressed
 };
 
 // NVFP4_CSF: the two scale bytes of chunk c (blocks p0 = r*C + 2c, p0 + 1
-// of its row): base + code, or an exception's byte. ex0 / ex1: the row's
-// first two exceptions (0xFFFFFFFF: none; a 24-bit position never reaches
-// 0xFFFFFF), [x2, xe): the rest of the row's exceptions.
+// of its row): base + code, or an exception's byte. ex0 / ex1: exceptions
+// held in registers (0xFFFFFFFF: none; a 24-bit position never reaches
+// 0xFFFFFF).
 __device__ __forceinline__ uint32_t csf_scale_pair(uint32_t code, uint32_t base, uint32_t ex0,
-                                                   uint32_t ex1, int x2, int xe,
-                                                   const uint32_t *xc, uint32_t p0) {
+                                                   uint32_t ex1, uint32_t p0) {
     uint32_t b0 = base + (code & 15u), b1 = base + (code >> 4);
     const uint32_t q0 = ex0 & 0xFFFFFFu, q1 = ex1 & 0xFFFFFFu;
     b0 = q0 == p0 ? ex0 >> 24 : b0;
     b1 = q0 == p0 + 1 ? ex0 >> 24 : b1;
     b0 = q1 == p0 ? ex1 >> 24 : b0;
     b1 = q1 == p0 + 1 ? ex1 >> 24 : b1;
-    for (int x = x2; x < xe; ++x) {              // rows with more than two: rare
+    return b0 | (b1 << 8);
+}
+// The same pair by walking all of the row's exceptions [xl, xh).
+__device__ __forceinline__ uint32_t csf_scale_pair_walk(uint32_t code, uint32_t base, int xl,
+                                                        int xh, const uint32_t *xc, uint32_t p0) {
+    uint32_t b0 = base + (code & 15u), b1 = base + (code >> 4);
+    for (int x = xl; x < xh; ++x) {
         const uint32_t v = xc[x], q = v & 0xFFFFFFu;
         b0 = q == p0 ? v >> 24 : b0;
         b1 = q == p0 + 1 ? v >> 24 : b1;
@@ -326,28 +334,46 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
         zra[ps] = r * (int)A.zr;
         zrb[ps] = r * (int)B.zr;
     }
-    // NVFP4_CSF: per pass and matrix the row's base byte, its first two
-    // exceptions and the range of the others
+    // NVFP4_CSF: per pass and matrix the row's base byte (bit 31: the lane
+    // has more than two exceptions in its chunks), the lane's first two
+    // exceptions and the row's exception range
     uint32_t bsa[kCsf ? RPW : 1], bsb[kCsf ? RPW : 1], e0a[kCsf ? RPW : 1], e1a[kCsf ? RPW : 1],
         e0b[kCsf ? RPW : 1], e1b[kCsf ? RPW : 1];
-    int x2a[kCsf ? RPW : 1], xea[kCsf ? RPW : 1], x2b[kCsf ? RPW : 1], xeb[kCsf ? RPW : 1];
+    int xla[kCsf ? RPW : 1], xha[kCsf ? RPW : 1], xlb[kCsf ? RPW : 1], xhb[kCsf ? RPW : 1];
     if constexpr (kCsf) {
         auto row_state = [&](const GemvMat &M, int r, uint32_t &bs, uint32_t &e0, uint32_t &e1,
-                             int &x2, int &xe) {
+                             int &xl, int &xh) {
             const uint8_t *fx = M.s + e * M.se;
             bs = fx[(size_t)(r >> 4) * 16 * csf_row_bytes + (r & 15)];
             const int32_t *ri = M.ri + (size_t)e * (n_rows + 1) + r;
-            const int xl = ri[0], xh = ri[1];
-            e0 = xl < xh ? M.xc[xl] : 0xFFFFFFFFu;
-            e1 = xl + 1 < xh ? M.xc[xl + 1] : 0xFFFFFFFFu;
-            x2 = xl + 2;
-            xe = xh;
+            xl = ri[0];
+            xh = ri[1];
+            e0 = e1 = 0xFFFFFFFFu;
+            int cnt = 0;
+            const uint32_t rC = (uint32_t)r * (uint32_t)(kin / 16);
+            auto take = [&](uint32_t v) {
+                if ((int)((((v & 0xFFFFFFu) - rC) >> 1) % LPR) == sub) {   // one of my chunks
+                    e0 = cnt == 0 ? v : e0;
+                    e1 = cnt == 1 ? v : e1;
+                    ++cnt;
+                }
+            };
+            // the row's first four exceptions loaded together, the rest (rows
+            // with more: rare) one by one
+            uint32_t v4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v4[q] = xl + q < xh ? M.xc[xl + q] : 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (xl + q < xh) take(v4[q]);
+            for (int x = xl + 4; x < xh; ++x) take(M.xc[x]);
+            bs |= cnt > 2 ? 0x80000000u : 0u;
         };
 #pragma unroll
         for (int ps = 0; ps < RPW; ++ps) {
             const int r = row_of(ps) < n_rows ? row_of(ps) : n_rows - 1;
-            row_state(A, r, bsa[ps], e0a[ps], e1a[ps], x2a[ps], xea[ps]);
-            if (GATEUP) row_state(B, r, bsb[ps], e0b[ps], e1b[ps], x2b[ps], xeb[ps]);
+            row_state(A, r, bsa[ps], e0a[ps], e1a[ps], xla[ps], xha[ps]);
+            if (GATEUP) row_state(B, r, bsb[ps], e0b[ps], e1b[ps], xlb[ps], xhb[ps]);
         }
     }
     // asymmetric int4: one zero-point byte per 128 inputs, streamed with the scales
@@ -486,6 +512,53 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
 #pragma unroll
         for (int t = 0; t < TM; ++t) acc_a[t] = acc_b[t] = 0.0f;
     };
+    // NVFP4_CSF: a lane with more than two exceptions in its chunks redoes
+    // its pass with the full per-chunk lookup (the same operations in the
+    // same order, so its sums equal those of the expanded scales)
+    auto repair = [&](int ps) {
+        if constexpr (kCsf) {
+            if (((bsa[ps] | (GATEUP ? bsb[ps] : 0u)) >> 31) != 0) {
+                const int r = row_of(ps) < n_rows ? row_of(ps) : n_rows - 1;
+                const uint32_t rC = (uint32_t)r * (uint32_t)(kin / 16);
+#pragma unroll
+                for (int t = 0; t < TM; ++t) acc_a[t] = acc_b[t] = 0.0f;
+                for (int i = 0; i < nit; ++i) {
+                    const int c = sub + LPR * i;
+                    if (c >= nch) break;
+                    const uint32_t p0 = rC + 2u * (uint32_t)c;
+                    ChunkDot<ACT, FMT> da, db;
+                    float a0, a1, b0 = 0.0f, b1 = 0.0f;
+                    const u32x4_t w = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rqa, qra[ps] + 16 * c, 0, 0));
+                    const uint32_t code = __builtin_amdgcn_raw_buffer_load_b8(rsa, sra[ps] + c, 0, 0);
+                    da.template decode<X16>(make_uint4(w.x, w.y, w.z, w.w), kv, kv1);
+                    chunk_scales<ACT, FMT, X16>(
+                        csf_scale_pair_walk(code, bsa[ps] & 0xFFu, xla[ps], xha[ps], A.xc, p0), 0u,
+                        a0, a1);
+                    if (GATEUP) {
+                        const u32x4_t wv = __builtin_bit_cast(
+                            u32x4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(rqb, qrb[ps] + 16 * c, 0, 0));
+                        const uint32_t cb =
+                            __builtin_amdgcn_raw_buffer_load_b8(rsb, srb[ps] + c, 0, 0);
+                        db.template decode<X16>(make_uint4(wv.x, wv.y, wv.z, wv.w), kv, kv1);
+                        chunk_scales<ACT, FMT, X16>(
+                            csf_scale_pair_walk(cb, bsb[ps] & 0xFFu, xlb[ps], xhb[ps], B.xc, p0), 0u,
+                            b0, b1);
+                    }
+                    const int u0 = xs_unit<LPR, UPC>(c, 0);
+#pragma unroll
+                    for (int t = 0; t < TM; ++t) {
+                        if (t < m) {
+                            const uint4 *xu = xs + t * upad + u0;
+                            acc_a[t] = da.apply(xu, LPR, 0.0f, a0, a1, acc_a[t]);
+                            if (GATEUP) acc_b[t] = db.apply(xu, LPR, 0.0f, b0, b1, acc_b[t]);
+                        }
+                    }
+                }
+            }
+        }
+    };
     const int total_it = RPW * nit;
     // every trip runs all kGemvRing slots (slots past the last iteration hold
     // zeros and are not computed)
@@ -504,10 +577,8 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
                 const int pp = ps < RPW ? ps : 0;
                 const int r = row_of(pp) < n_rows ? row_of(pp) : n_rows - 1;
                 const uint32_t p0 = (uint32_t)r * (uint32_t)(kin / 16) + 2u * (uint32_t)c;
-                two_a = csf_scale_pair(sa[j], bsa[pp], e0a[pp], e1a[pp], x2a[pp], xea[pp], A.xc, p0);
-                if (GATEUP)
-                    two_b = csf_scale_pair(sb[j], bsb[pp], e0b[pp], e1b[pp], x2b[pp], xeb[pp], B.xc,
-                                           p0);
+                two_a = csf_scale_pair(sa[j], bsa[pp] & 0xFFu, e0a[pp], e1a[pp], p0);
+                if (GATEUP) two_b = csf_scale_pair(sb[j], bsb[pp] & 0xFFu, e0b[pp], e1b[pp], p0);
             }
             chunk_scales<ACT, FMT, X16>(two_a, kZ ? za[j] : 0u, a0, a1);
             if (GATEUP) {
@@ -530,7 +601,10 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
                     }
                 }
             }
-            if (NIT > 0 && I < total_it && i == NIT - 1) finish(I / NIT);
+            if (NIT > 0 && I < total_it && i == NIT - 1) {
+                repair(I / NIT);
+                finish(I / NIT);
+            }
         }
     };
     if constexpr (NIT > 0) {
@@ -538,6 +612,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
         for (int I0 = 0; I0 < RPW * NIT; I0 += kGemvRing) trip(I0);
     } else {
         for (int I0 = 0; I0 < nit; I0 += kGemvRing) trip(I0);
+        repair(0);
         finish(0);
     }
 }
