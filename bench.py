@@ -301,8 +301,9 @@ class StackLayer:
 
 def run_stack(layers, T, steps, warmup, hip, dev, use_graph=True):
     """Times `steps` passes of the 8-layer stack: per layer, the RMSNorm of
-    the fp32 residual rounded to bf16, routing from the router weight plus Zipf bias,
-    permutation, routed + shared experts and the combine with the residual."""
+    the fp32 residual rounded to bf16 and the routing from the router weight
+    plus Zipf bias (one fused call), permutation, routed + shared experts and
+    the combine with the residual."""
     r0 = synth.activations(T, H, "bf16", 5).float().to(dev)
     res = [r0.clone(), torch.empty_like(r0)]
     a = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -326,8 +327,8 @@ def run_stack(layers, T, steps, warmup, hip, dev, use_graph=True):
         res[0].copy_(r0)
         for l, L in enumerate(layers):
             src, dst = res[l % 2], res[(l + 1) % 2]
-            B.moe_rmsnorm(src, L.norm_w, 1e-5, out=a)
-            B.moe_route_topk(K, x=a, router_wT=L.wT, bias=L.bias, ids=ids, w=w, ws=rws)
+            B.moe_norm_route(src, L.wT, K, norm_w=L.norm_w, eps=1e-5, bias=L.bias, a=a, ids=ids,
+                             w=w, ws=rws)
             B.moe_permute(ids, E, tm, perm=perm)
             B.moe_w4a16_forward(L.ffn, a, w, perm, residual=src, out=dst, ws=ws,
                                 shared=L.shared, events=None if events is None else events[l])

@@ -208,6 +208,34 @@ moe_status_t moe_permute_sizes(int T, int K, int E, int tile_m,
                                int64_t *max_rows, int64_t *max_tiles);
 
 /*
+ * moe_norm_route -- the step before the routed experts, fused (the norm and
+ * the router decide which experts a token reaches; page
+ * "Step-5-Preview-Spark", "Quality": rounding the router input to bf16
+ * flips about a third of the top-8 sets, so where it is rounded matters):
+ *   a = bf16(residual / rms(residual) * (1 + norm_w))   (as moe_rmsnorm)
+ *   topk_ids, topk_w = top-K routing of a from router_wT (+ bias)
+ *                                                        (as moe_route_topk)
+ * For batches of up to 512 tokens with H <= 4096 the norm, the cast and the
+ * router chains run as one kernel (each router work group normalizes its
+ * token rows into LDS; the first expert block writes them to a_out), then
+ * the top-K; otherwise the kernels of the separate calls run. Either way the
+ * results are bitwise those of moe_rmsnorm followed by moe_route_topk.
+ *   residual [T][H] float; norm_w [H] float or NULL (gain 1); eps in [0, 1];
+ *   router_wT [H][E], bias [E] or NULL, K, renormalize: as moe_route_topk;
+ *   a_out [T][H] bf16 (the layer input the experts read);
+ *   topk_ids [T][K] int32, topk_w [T][K] float;
+ *   ws: device workspace of moe_route_workspace(T, E, 1) bytes (the
+ *   logits), 16-byte aligned.
+ * All pointers device memory, 16-byte aligned (ids and weights 4). Limits:
+ * H % 64 == 0 and E % 4 == 0 (else MOE_ERR_UNSUPPORTED), H <= 16384,
+ * 1 <= K <= min(E, 16), E <= 512. T == 0 is a no-op.
+ */
+moe_status_t moe_norm_route(const float *residual, const float *norm_w, float eps, int T, int H,
+                            const float *router_wT, const float *bias, int E, int K,
+                            int renormalize, void *a_out, int32_t *topk_ids, float *topk_w,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
  * moe_permute -- expert histogram and stable expert-sorted permutation of
  * the T*K slots (see moe_perm_t). The pages do not describe this step; it
  * exists so that each touched expert's weights stream from HBM once

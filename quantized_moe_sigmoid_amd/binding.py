@@ -22,7 +22,7 @@ EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_rou
            "moe_route_topk", "moe_permute_sizes",
            "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_w4a16_forward_profiled",
            "moe_round_activations", "moe_rmsnorm", "moe_dequant", "moe_csf_expand",
-           "moe_csf_row_index")
+           "moe_csf_row_index", "moe_norm_route")
 MOE_FORWARD_STAGES = 4
 
 _DT = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
@@ -89,11 +89,13 @@ def lib():
         L.moe_dequant.argtypes = [P(WeightDesc), i32, vp, vp]
         L.moe_csf_expand.argtypes = [vp, vp, i64, vp, i32, i32, i32, vp, i32, vp, vp]
         L.moe_csf_row_index.argtypes = [vp, i64, vp, i32, i32, i32, vp, i32, vp, vp]
+        L.moe_norm_route.argtypes = [vp, vp, ctypes.c_float, i32, i32, vp, vp, i32, i32, i32, vp,
+                                     vp, vp, vp, ctypes.c_size_t, vp]
         for name in ("moe_router_logits", "moe_route_workspace", "moe_route_topk",
                      "moe_permute_sizes", "moe_permute", "moe_forward_plan",
                      "moe_w4a16_forward", "moe_w4a16_forward_profiled",
                      "moe_round_activations", "moe_rmsnorm", "moe_dequant",
-                     "moe_csf_expand", "moe_csf_row_index"):
+                     "moe_csf_expand", "moe_csf_row_index", "moe_norm_route"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -325,6 +327,28 @@ def moe_rmsnorm(x, weight=None, eps=1e-5, dtype=torch.bfloat16, out=None):
     _check(lib().moe_rmsnorm(_ptr(x), _ptr(weight), float(eps), T, H, _DT[out.dtype], _ptr(out),
                              _stream(x.device)), "moe_rmsnorm")
     return out
+
+
+def moe_norm_route(residual, router_wT, K, norm_w=None, eps=1e-5, bias=None, renormalize=True,
+                   a=None, ids=None, w=None, ws=None):
+    """Fused RMSNorm + bf16 cast + router + top-K of a float32 residual [T, H]:
+    returns (a bf16 [T, H], ids int32 [T, K], weights float [T, K])."""
+    T, H = residual.shape
+    E = router_wT.shape[1]
+    dev = residual.device
+    if a is None:
+        a = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if ids is None:
+        ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(T * E * 4, 16), dtype=torch.uint8, device=dev)
+    _check(lib().moe_norm_route(_ptr(residual), _ptr(norm_w), float(eps), T, H, _ptr(router_wT),
+                                _ptr(bias), E, K, 1 if renormalize else 0, _ptr(a), _ptr(ids),
+                                _ptr(w), _ptr(ws), ws.numel(), _stream(dev)),
+           "moe_norm_route")
+    return a, ids, w
 
 
 def moe_dequant(desc, expert, out=None, device=None):

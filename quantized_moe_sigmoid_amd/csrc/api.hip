@@ -35,6 +35,10 @@ moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int ac
 moe_status_t launch_dense_swiglu(const moe_ffn_desc_t &sh, const void *x, int T, void *h,
                                  float *y, float *part, hipStream_t s);
 moe_status_t launch_round(const float *in, size_t n, int dtype, void *out, hipStream_t s);
+bool norm_route_fused(int T, int H, int E);
+moe_status_t launch_norm_router_logits(const float *res, const float *gain, float eps, int T,
+                                       int H, const float *wT, const float *bias, int E,
+                                       void *a_out, float *logits, hipStream_t s);
 moe_status_t launch_rmsnorm(const float *x, const float *w, float eps, int T, int H, int dtype,
                             void *out, hipStream_t s);
 DenseSplit dense_plan(int T, int H, int F);
@@ -407,6 +411,36 @@ moe_status_t moe_rmsnorm(const float *x, const float *weight, float eps, int T, 
     if (!x || !out || !aligned(x, 16) || !aligned(out, 16) || (weight && !aligned(weight, 16)))
         return MOE_ERR_INVALID_ARG;
     return launch_rmsnorm(x, weight, eps, T, H, out_dtype, out, (hipStream_t)stream);
+}
+
+moe_status_t moe_norm_route(const float *residual, const float *norm_w, float eps, int T, int H,
+                            const float *router_wT, const float *bias, int E, int K,
+                            int renormalize, void *a_out, int32_t *topk_ids, float *topk_w,
+                            void *ws, size_t ws_bytes, void *stream) {
+    if (T < 0 || H < 4 || H > kMaxDim || E < 1 || E > kMaxExperts || K < 1 || K > E ||
+        K > kMaxTopK)
+        return MOE_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f) || eps > 1.0f || !router_wT) return MOE_ERR_INVALID_ARG;
+    if (H % 64 || E % 4) return MOE_ERR_UNSUPPORTED;
+    if (ws_bytes < (size_t)T * E * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (T == 0) return MOE_OK;
+    if (!residual || !a_out || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+    if (!aligned(residual, 16) || !aligned(a_out, 16) || !aligned(router_wT, 16) ||
+        !aligned(ws, 16) || (norm_w && !aligned(norm_w, 16)))
+        return MOE_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    float *lg = (float *)ws;
+    moe_status_t st;
+    if (norm_route_fused(T, H, E)) {
+        st = launch_norm_router_logits(residual, norm_w, eps, T, H, router_wT, bias, E, a_out, lg,
+                                       s);
+    } else {
+        if ((st = launch_rmsnorm(residual, norm_w, eps, T, H, MOE_BF16, a_out, s)) != MOE_OK)
+            return st;
+        st = launch_router_logits(a_out, MOE_BF16, router_wT, bias, T, H, E, lg, s);
+    }
+    if (st != MOE_OK) return st;
+    return launch_topk(lg, nullptr, T, E, K, renormalize, topk_ids, topk_w, s);
 }
 
 moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out, void *stream) {

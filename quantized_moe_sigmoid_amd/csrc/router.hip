@@ -15,6 +15,7 @@
 // Weights: sigmoid of the selected logits, renormalised to sum to one when
 // asked.
 #include "common.h"
+#include "norm.h"
 
 #pragma clang fp contract(off)
 
@@ -197,6 +198,84 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
     }
 }
 
+// The 64-expert column block of wT streamed through a two-stage LDS buffer
+// in chunks of KC rows, NP chunks ahead in registers. Chunk m sits in
+// register slot m % NP; step c stores chunk c + 1 into the stage that step
+// c - 1 finished reading, reloads the freed slot with chunk c + 1 + NP, then
+// runs the chain over chunk c. A load thus has NP steps of chain work to
+// arrive. Every step issues the same loads (chunk indices past the end are
+// clamped to the last chunk, steps past the end only store and
+// synchronize), so the compiler's wait before a store counts exactly the
+// NP - 1 younger chunks instead of draining every load in flight.
+// Staging roles (NT threads): float4 column tid % 16 of rows tid / 16 +
+// (NT / 16) i, so each store instruction writes NT / 16 whole 256-byte rows.
+// E % 4 == 0: a column
+// group past E stages a copy of the last group; the lanes that read it
+// compute logits that are never stored.
+// XT = kXTouch: one 4-byte word of `xt` per chunk (KC 16-bit inputs apart)
+// is loaded with the chunk and folded into `sink`, which touches the
+// activation rows ahead of the scalar loads that consume them.
+constexpr int kXNone = 0, kXTouch = 1;
+
+template <int KC, int NP, int XT, int NT = 256>
+struct RouterWeightPipe {
+    static constexpr int kStride = NT / 16;      // rows apart of a thread's loads
+    static constexpr int kRows = KC / kStride;   // float4 loads per thread and chunk
+    f32x4_t r[NP][kRows];
+    uint32_t xw[NP];
+    const float *src;                            // wT + (tid / 16) * E + column
+    const uint16_t *xt;
+    size_t row;                                  // one row of wT, in floats (E)
+    int wk, we, nch;
+    uint32_t sink;
+
+    __device__ __forceinline__ RouterWeightPipe(const float *wT, int E, int e0, int H, int tid,
+                                                const uint16_t *xtouch = nullptr) {
+        wk = tid >> 4;
+        we = (tid & 15) * 4;
+        src = wT + (size_t)wk * E + (e0 + we < E ? e0 + we : E - 4);
+        row = (size_t)E;
+        nch = H / KC;
+        xt = xtouch;
+        sink = 0;
+    }
+    __device__ __forceinline__ void load(int slot, int chunk) {
+        chunk = chunk < nch ? chunk : nch - 1;
+        const float *p = src + (size_t)chunk * KC * row;
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) r[slot][i] = *(const f32x4_t *)(p + i * kStride * row);
+        if (XT == kXTouch) xw[slot] = *(const uint32_t *)(xt + (size_t)chunk * KC);
+    }
+    __device__ __forceinline__ void store(float (*st)[kRtExp], int slot) {
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) *(f32x4_t *)&st[wk + kStride * i][we] = r[slot][i];
+        if (XT == kXTouch) sink ^= xw[slot];
+    }
+    // chunks 0 .. NP-1 in flight
+    __device__ __forceinline__ void prime() {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) load(j, j);
+    }
+    // after prime(): chunk 0 into stage 0, then every step; chunk(c, stage)
+    // runs the chain over chunk c. Ends with a barrier.
+    template <typename Chunk>
+    __device__ __forceinline__ void run(float (*ws)[KC][kRtExp], Chunk &&chunk) {
+        store(ws[0], 0);
+        load(0, NP);
+        __syncthreads();
+        for (int c0 = 0; c0 < nch; c0 += NP) {
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                const int c = c0 + j;
+                store(ws[(c + 1) & 1], (j + 1) % NP);
+                load((j + 1) % NP, c + 1 + NP);
+                if (c < nch) chunk(c, ws[c & 1]);  // uniform over the block
+                __syncthreads();
+            }
+        }
+    }
+};
+
 // bf16 activations: the wave's 4 token rows are wave-uniform, so they are
 // read with scalar loads straight into SGPRs and widened there (bf16 -> f32
 // is a shift), and every FMA takes its x operand from an SGPR. Only wT goes
@@ -204,12 +283,9 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
 // broadcast x reads that bound the LDS return path above. Same tiles, same
 // per-(t, e) chain order.
 //
-// TPW tokens per wave: 4 for large batches; 1 for small ones, where the
-// tiled grid would otherwise be a handful of work groups whose waves each
-// run four 4096-step chains back to back (T = 32: 12 groups, 116 us); with
-// one token per wave the grid has four times the waves and each wave a
-// quarter of the serial work.
-template <int TPW>
+// TPW tokens per wave (4) for large batches; small ones run
+// router_rows_kernel below, one token per wave.
+template <int TPW, int NP>
 __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wT,
     const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
@@ -225,53 +301,25 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
         const int t = t0 + TPW * wave + i;
         xr[i] = (const uint32_t *)(x + (size_t)(t < T ? t : t0) * H);
     }
-    // E % 4 == 0: a float4 column group is either inside the matrix or past
-    // it; groups past it read the last group and store zeros (no branch)
-    const int wk = threadIdx.x >> 4, we = (threadIdx.x & 15) * 4;
-    const bool w_in = e0 + we < E;
-    const int w_col = w_in ? e0 + we : E - 4;
-    float4 wreg[4];
-    // the next chunk's x bytes of the wave's rows (TPW rows x 128 B) are also
-    // touched with vector loads one chunk ahead, so the scalar loads that
-    // consume them hit L2 instead of waiting for HBM; the loaded words only
-    // feed `sink`
-    uint32_t sink = 0, xtouch = 0;
+    // the x bytes of the wave's rows (TPW rows x 128 B per chunk) are also
+    // touched with vector loads NP chunks ahead, so the scalar loads that
+    // consume them hit L2 instead of waiting for HBM
     const int tpf = t0 + TPW * wave + ((lane >> 3) % TPW);
     const uint16_t *xpf = x + (size_t)(tpf < T ? tpf : t0) * H + (lane & 7) * 8;
-    auto load = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            wreg[i] = *(const float4 *)(wT + (size_t)(k0 + wk + 16 * i) * E + w_col);
-        xtouch = *(const uint32_t *)(xpf + k0);
-    };
-    auto store = [&](int b) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *(float4 *)&ws[b][wk + 16 * i][we] = w_in ? wreg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        sink ^= xtouch;
-    };
+    RouterWeightPipe<kRtKC, NP, kXTouch> pipe(wT, E, e0, H, threadIdx.x, xpf);
+    pipe.prime();
 
     float acc[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) acc[i] = 0.0f;
-    const int nch = H / kRtKC;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-        const int b = c & 1;
-        if (c + 1 < nch) load((c + 1) * kRtKC);
+    pipe.run(ws, [&](int c, float (*st)[kRtExp]) {
         const int p0 = c * (kRtKC / 2);
-        // one token per wave: the whole chunk unrolled, so its LDS and
-        // scalar reads are issued ahead of the FMA chain instead of
-        // between its pieces
-        constexpr int kUnroll = TPW == 1 ? kRtKC / 2 : 8;
-#pragma unroll kUnroll
+#pragma unroll 8
         for (int k2 = 0; k2 < kRtKC / 2; ++k2) {
             uint32_t xp[TPW];
 #pragma unroll
             for (int i = 0; i < TPW; ++i) xp[i] = xr[i][p0 + k2];
-            const float w0 = ws[b][2 * k2][lane], w1 = ws[b][2 * k2 + 1][lane];
+            const float w0 = st[2 * k2][lane], w1 = st[2 * k2 + 1][lane];
 #pragma unroll
             for (int i = 0; i < TPW; ++i)
                 acc[i] = __builtin_fmaf(__uint_as_float(xp[i] << 16), w0, acc[i]);
@@ -279,11 +327,9 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
             for (int i = 0; i < TPW; ++i)
                 acc[i] = __builtin_fmaf(__uint_as_float(xp[i] & 0xFFFF0000u), w1, acc[i]);
         }
-        if (c + 1 < nch) store(b ^ 1);
-        __syncthreads();
-    }
+    });
     const int e = e0 + lane;
-    if (sink == 0x9E3779B9u && H == 0) logits[0] = 0.0f;    // never true: keeps the prefetch
+    if (pipe.sink == 0x9E3779B9u && H == 0) logits[0] = 0.0f;  // never true: keeps the prefetch
     if (e >= E) return;
     const float bv = bias ? bias[e] : 0.0f;
 #pragma unroll
@@ -293,18 +339,228 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
     }
 }
 
-// bf16 batches up to this many tokens run one token per wave.
-constexpr int kRtSmallT = 512;
+// Top-K of logits that are already final (bias, if any, folded in by the
+// caller) or given plus an optional bias.
+moe_status_t launch_topk(const float *logits, const float *bias, int T, int E, int K, int renorm,
+                         int32_t *ids, float *wts, hipStream_t s) {
+    if (T == 0) return MOE_OK;
+    hipLaunchKernelGGL(route_given_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, bias, T, E,
+                       K, renorm, ids, wts);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+// acc = fma(x_j, w[j], acc) for j = 0 .. 15 in this order, where x_j is the
+// value of lane j of the lane's 16-lane row in xq, delivered to the FMA by
+// DPP row_newbcast:j. With the same 16 inputs in every row this broadcasts
+// input j to the whole wave inside the FMA: one instruction per input and
+// no LDS or scalar traffic for x. The FMA is the same single-rounding fp32
+// fma the compiler emits for __builtin_fmaf. The leading s_nop covers the
+// two wait states a DPP read needs after a VALU write of its source. The
+// memory clobber keeps the caller's loads on their side of the block, so
+// the reads of the next 16 inputs overlap these FMAs.
+__device__ __forceinline__ void fma16_row_bcast(float &acc, float xq, const float (&w)[16]) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %10 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %11 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %12 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %13 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %14 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %15 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(xq), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]), "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15])
+        : "memory");
+}
+
+// ---- small batches: rows staged in LDS, one token per wave ------------------
+// W tokens x 64 experts a work group of W waves (W = 2 or 4), one token per
+// wave: a batch of a few tokens has too few waves for the tiled kernels
+// above, and each wave runs one 4096-step chain. The group first stages its W rows in LDS
+// as float32: the bf16 activations widened (NORM = false) or, fused, the
+// RMSNorm of W fp32 residual rows (NORM = true), whose float64 sums of
+// squares follow rmsnorm_kernel's 256-thread order exactly (each thread
+// stands in for 4 / W of those threads: same columns, same wave shuffles,
+// same block sum), so the 16-bit rows are bitwise the ones moe_rmsnorm
+// writes; the groups of the first expert block also write them to a_out for
+// the experts. In the chain each input costs one FMA (x broadcast by DPP
+// from one 4-byte LDS read per 16 inputs) and half a 4-byte-pair LDS read
+// of weights; what bounds it is that instruction stream of one wave (about
+// 19 cycles per input measured, against the 6.5-cycle latency of the FMA
+// chain), not LDS bandwidth or the weight loads: prefetch depth and chunk
+// size change nothing, and neither does W, apart from the number of groups.
+// Same chain, same order as the other router kernels.
+constexpr int kRowsMaxT = 512;                   // batches up to this size
+constexpr int kRowsMaxH = 4096;                  // W float32 rows in LDS
+
+template <bool NORM, int W>
+__global__ void __launch_bounds__(64 * W) router_rows_kernel(
+    const void *__restrict__ xin, const float *__restrict__ gain, double eps,
+    const float *__restrict__ wT, const float *__restrict__ bias, int T, int H, int E,
+    uint16_t *__restrict__ a_out, float *__restrict__ logits) {
+    constexpr int NT = 64 * W, KC = 64, NP = 2;
+    static_assert(W == 1 || W == 2 || W == 4, "norm threads must split evenly");
+    constexpr int kVT = 4 / W;                   // 256-thread norm threads per thread
+    constexpr int kCols = kRowsMaxH / 1024;      // float4 groups of a row per norm thread
+    __shared__ __attribute__((aligned(16))) float ws[2][KC][kRtExp];
+    __shared__ __attribute__((aligned(16))) float as[W][kRowsMaxH];
+    __shared__ double red[W][4];
+    const int t0 = blockIdx.x * W, e0 = blockIdx.y * kRtExp;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // the router weight's first chunks are in flight while the rows stage
+    RouterWeightPipe<KC, NP, kXNone, NT> pipe(wT, E, e0, H, tid);
+    pipe.prime();
+
+    if (!NORM) {
+        // bf16 rows widened (rows past T repeat row t0; never stored)
+        const uint16_t *x = (const uint16_t *)xin;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            const int t = t0 + i < T ? t0 + i : t0;
+            for (int c = tid * 4; c < H; c += 4 * NT) {
+                const uint2 v = *(const uint2 *)(x + (size_t)t * H + c);
+                *(f32x4_t *)&as[i][c] = f32x4_t{__uint_as_float(v.x << 16),
+                                                __uint_as_float(v.x & 0xFFFF0000u),
+                                                __uint_as_float(v.y << 16),
+                                                __uint_as_float(v.y & 0xFFFF0000u)};
+            }
+        }
+    } else {
+        // RMSNorm of the W rows (rows past T repeat row t0; not stored).
+        // Norm thread tid + NT u of rmsnorm_kernel's 256 (its wave: wave +
+        // W u, its lane: lane) owns columns 4 (tid + NT u) + 1024 j. All of a
+        // thread's values are loaded at once.
+        const float *res = (const float *)xin;
+        f32x4_t v[W][kVT][kCols], g[kVT][kCols];
+#pragma unroll
+        for (int u = 0; u < kVT; ++u)
+#pragma unroll
+            for (int j = 0; j < kCols; ++j) {
+                const int c = (tid + NT * u) * 4 + 1024 * j;
+                g[u][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if (c < H) {
+                    if (gain) g[u][j] = *(const f32x4_t *)(gain + c);
+#pragma unroll
+                    for (int i = 0; i < W; ++i) {
+                        const int t = t0 + i < T ? t0 + i : t0;
+                        v[i][u][j] = *(const f32x4_t *)(res + (size_t)t * H + c);
+                    }
+                }
+            }
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+#pragma unroll
+            for (int u = 0; u < kVT; ++u) {
+                double ss = 0.0;
+#pragma unroll
+                for (int j = 0; j < kCols; ++j) {
+                    if ((tid + NT * u) * 4 + 1024 * j < H) {
+                        const f32x4_t q = v[i][u][j];
+                        ss += (double)q.x * q.x + (double)q.y * q.y + (double)q.z * q.z +
+                              (double)q.w * q.w;
+                    }
+                }
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, kWave);
+                if (lane == 0) red[i][wave + W * u] = ss;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            double tot = 0.0;
+            for (int w = 0; w < 4; ++w) tot += red[i][w];
+            const double inv = 1.0 / __builtin_sqrt(tot / H + eps);
+#pragma unroll
+            for (int u = 0; u < kVT; ++u)
+#pragma unroll
+                for (int j = 0; j < kCols; ++j) {
+                    const int c = (tid + NT * u) * 4 + 1024 * j;
+                    if (c < H) {
+                        const f32x4_t q = v[i][u][j], gg = g[u][j];
+                        const uint32_t lo =
+                            f64_to_act<MOE_BF16>((double)q.x * inv * (1.0 + (double)gg.x)) |
+                            ((uint32_t)f64_to_act<MOE_BF16>((double)q.y * inv *
+                                                            (1.0 + (double)gg.y))
+                             << 16);
+                        const uint32_t hi =
+                            f64_to_act<MOE_BF16>((double)q.z * inv * (1.0 + (double)gg.z)) |
+                            ((uint32_t)f64_to_act<MOE_BF16>((double)q.w * inv *
+                                                            (1.0 + (double)gg.w))
+                             << 16);
+                        *(f32x4_t *)&as[i][c] = f32x4_t{__uint_as_float(lo << 16),
+                                                        __uint_as_float(lo & 0xFFFF0000u),
+                                                        __uint_as_float(hi << 16),
+                                                        __uint_as_float(hi & 0xFFFF0000u)};
+                        if (blockIdx.y == 0 && t0 + i < T)
+                            *(uint2 *)(a_out + (size_t)(t0 + i) * H + c) = make_uint2(lo, hi);
+                    }
+                }
+        }
+    }
+    // the rows reach LDS before the chains read them: run() stores the first
+    // chunk and synchronizes before its first step
+
+    // lane j of every 16-lane row reads inputs 16 m + j of the chunk
+    const float *xr = &as[wave][lane & 15];
+    float acc = 0.0f;
+    pipe.run(ws, [&](int c, float (*st)[kRtExp]) {
+        // 16 inputs at a time, the reads of the next 16 issued before the
+        // FMAs of these (double-buffered in registers)
+        float xq[2], w[2][16];
+        auto read = [&](int m, int b) {
+            xq[b] = xr[c * KC + 16 * m];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) w[b][j] = st[16 * m + j][lane];
+        };
+        read(0, 0);
+#pragma unroll
+        for (int m = 0; m < KC / 16; ++m) {
+            if (m + 1 < KC / 16) read(m + 1, (m + 1) & 1);
+            fma16_row_bcast(acc, xq[m & 1], w[m & 1]);
+        }
+    });
+    const int e = e0 + lane, t = t0 + wave;
+    if (e < E && t < T) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
+}
+
+// tokens per work group, measured at H = 4096, E = 352: W = 2 up to 64
+// tokens (T = 32: 36 us against 39 us at W = 4 and 41 us at W = 1, whose
+// single wave per group gains no LDS bandwidth worth its lost sharing),
+// W = 4 beyond (T = 256: 68 us against 79 us at W = 2)
+constexpr int kRowsW2MaxT = 64;
+
+template <bool NORM>
+static void launch_rows(const void *xin, const float *gain, float eps, int T, int H,
+                        const float *wT, const float *bias, int E, void *a_out, float *logits,
+                        hipStream_t s) {
+    const int eb = (E + kRtExp - 1) / kRtExp;
+    if (T <= kRowsW2MaxT)
+        hipLaunchKernelGGL((router_rows_kernel<NORM, 2>), dim3((T + 1) / 2, eb), dim3(128), 0, s,
+                           xin, gain, (double)eps, wT, bias, T, H, E, (uint16_t *)a_out, logits);
+    else
+        hipLaunchKernelGGL((router_rows_kernel<NORM, 4>), dim3((T + 3) / 4, eb), dim3(256), 0, s,
+                           xin, gain, (double)eps, wT, bias, T, H, E, (uint16_t *)a_out, logits);
+}
 
 moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, const float *bias,
                                   int T, int H, int E, float *logits, hipStream_t s) {
     if (T == 0) return MOE_OK;
     const dim3 grid((T + kRtTok - 1) / kRtTok, (E + kRtExp - 1) / kRtExp);
-    if (x_dtype == MOE_BF16 && T <= kRtSmallT)
-        hipLaunchKernelGGL(router_logits_bf16_kernel<1>, dim3((T + 3) / 4, grid.y), dim3(256), 0,
-                           s, (const uint16_t *)x, wT, bias, T, H, E, logits);
+    if (x_dtype == MOE_BF16 && T <= kRowsMaxT && H <= kRowsMaxH)
+        launch_rows<false>(x, nullptr, 0.f, T, H, wT, bias, E, nullptr, logits, s);
     else if (x_dtype == MOE_BF16)
-        hipLaunchKernelGGL(router_logits_bf16_kernel<4>, grid, dim3(256), 0, s,
+        hipLaunchKernelGGL((router_logits_bf16_kernel<4, 2>), grid, dim3(256), 0, s,
                            (const uint16_t *)x, wT, bias, T, H, E, logits);
     else
         hipLaunchKernelGGL(router_logits_kernel<MOE_F16>, grid, dim3(256), 0, s,
@@ -313,13 +569,13 @@ moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, c
     return MOE_OK;
 }
 
-// Top-K of logits that are already final (bias, if any, folded in by the
-// caller) or given plus an optional bias.
-moe_status_t launch_topk(const float *logits, const float *bias, int T, int E, int K, int renorm,
-                         int32_t *ids, float *wts, hipStream_t s) {
+bool norm_route_fused(int T, int H, int E) { return T <= kRowsMaxT && H <= kRowsMaxH; }
+
+moe_status_t launch_norm_router_logits(const float *res, const float *gain, float eps, int T,
+                                       int H, const float *wT, const float *bias, int E,
+                                       void *a_out, float *logits, hipStream_t s) {
     if (T == 0) return MOE_OK;
-    hipLaunchKernelGGL(route_given_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, bias, T, E,
-                       K, renorm, ids, wts);
+    launch_rows<true>(res, gain, eps, T, H, wT, bias, E, a_out, logits, s);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -23,6 +23,5 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 }  // namespace moe

@@ -299,6 +299,29 @@ def test_csf_expand_validation(L):
         assert F(*args) == want, args
 
 
+def test_norm_route_validation(L):
+    """Argument errors of moe_norm_route are found before any launch."""
+    F = L.moe_norm_route
+    p = ctypes.c_void_p(FAKE)
+    ok = (p, None, 1e-5, 8, 4096, p, None, 352, 8, 1, p, p, p, p, 8 * 352 * 4, None)
+    bad = [
+        ((None,) + ok[1:], B.MOE_ERR_INVALID_ARG),                     # residual
+        (ok[:2] + (-1.0,) + ok[3:], B.MOE_ERR_INVALID_ARG),            # eps
+        (ok[:3] + (-1,) + ok[4:], B.MOE_ERR_INVALID_ARG),              # T
+        (ok[:4] + (4032 + 32,) + ok[5:], B.MOE_ERR_UNSUPPORTED),       # H % 64
+        (ok[:5] + (None,) + ok[6:], B.MOE_ERR_INVALID_ARG),            # router weight
+        (ok[:7] + (350,) + ok[8:], B.MOE_ERR_UNSUPPORTED),             # E % 4
+        (ok[:8] + (17,) + ok[9:], B.MOE_ERR_INVALID_ARG),              # K > 16
+        (ok[:10] + (None,) + ok[11:], B.MOE_ERR_INVALID_ARG),          # a_out
+        (ok[:13] + (None,) + ok[14:], B.MOE_ERR_INVALID_ARG),          # ws
+        (ok[:14] + (8 * 352 * 4 - 4,) + ok[15:], B.MOE_ERR_WORKSPACE_TOO_SMALL),
+        (ok[:10] + (ctypes.c_void_p(FAKE + 8),) + ok[11:], B.MOE_ERR_INVALID_ARG),  # alignment
+    ]
+    for args, want in bad:
+        assert F(*args) == want, args
+    assert F(*(ok[:3] + (0,) + ok[4:])) == B.MOE_OK                   # T == 0: a no-op
+
+
 def test_csf_row_index_validation(L):
     """Argument errors of moe_csf_row_index are found before any launch."""
     F = L.moe_csf_row_index

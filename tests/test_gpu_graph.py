@@ -50,8 +50,12 @@ def test_stack_step_graph_replays_match_eager(dev):
         res[0].copy_(r0)
         for l, (ffn, sh, wT, bias, nw) in enumerate(layers):
             src, dst = res[l % 2], res[(l + 1) % 2]
-            B.moe_rmsnorm(src, nw, 1e-5, out=a)
-            B.moe_route_topk(K, x=a, router_wT=wT, bias=bias, ids=ids, w=w, ws=rws)
+            if l % 2 == 0:                      # the fused call and the separate ones
+                B.moe_norm_route(src, wT, K, norm_w=nw, eps=1e-5, bias=bias, a=a, ids=ids, w=w,
+                                 ws=rws)
+            else:
+                B.moe_rmsnorm(src, nw, 1e-5, out=a)
+                B.moe_route_topk(K, x=a, router_wT=wT, bias=bias, ids=ids, w=w, ws=rws)
             B.moe_permute(ids, E, tm, perm=perm)
             B.moe_w4a16_forward(ffn, a, w, perm, residual=src, out=dst, ws=ws, shared=sh)
 

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import layer as OL
 from oracle import permute as OP
 from oracle import quant as OQ
 from oracle import router as OR
@@ -117,11 +118,13 @@ def test_route_from_router_weight_tiny(dev, act):
 
 
 @pytest.mark.parametrize("T,Hh,Ee,act", [(37, 4096, 352, "bf16"), (2048, 4096, 352, "bf16"),
-                                         (4099, 4096, 352, "bf16"),
+                                         (4099, 4096, 352, "bf16"), (9, 576, 20, "bf16"),
+                                         (3, 64, 8, "bf16"), (600, 320, 24, "bf16"),
                                          (8, 256, 16, "f16"), (70, 192, 20, "f16")])
 def test_router_logits_bitwise(dev, T, Hh, Ee, act):
     """The canonical float32 fma chain, bit for bit against the C oracle
-    (partial token and expert tiles included)."""
+    (partial token and expert tiles included; bf16 inputs whose 64-input
+    chunk count is below or not a multiple of the weight prefetch depth)."""
     x = synth.activations(T, Hh, act, 5)
     wT = synth.router_weight_T(Hh, Ee, 5)
     b = synth.zipf_bias(Ee, 5)
@@ -331,6 +334,39 @@ def test_forward_nvfp4_decode_full_shape(dev):
 
 
 # --------------------------------------------------------------- properties ---
+@pytest.mark.parametrize("T", [1, 3, 37])
+def test_forward_single_expert(dev, T):
+    """E = K = 1: every token goes to the one expert with weight exactly 1,
+    so the layer is one SwiGLU FFN (T = 37 takes the MFMA path)."""
+    Ee, Kk, Hh, Ff = 1, 1, 512, 256
+    ffn, host = _int4_ffn_from_oracle(Ee, Hh, Ff, 12, dev)
+    x = synth.activations(T, Hh, "bf16", 12)
+    lg = synth.router_logits(T, Ee, 12)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    assert torch.all(ids == 0) and torch.all(w == 1.0)
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, Ee).cpu().numpy()
+    ref = OL.swiglu_ffn(x.float().numpy().astype(np.float64), *_experts_fn_int4(host)(0))
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
+def test_forward_empty_batch(dev):
+    """T = 0: plan, permutation and forward pass all succeed and write
+    nothing."""
+    Ee, Kk, Hh, Ff = 8, 2, 512, 256
+    ffn, _ = _int4_ffn_from_oracle(Ee, Hh, Ff, 13, dev)
+    ids = torch.empty((0, Kk), dtype=torch.int32, device=dev)
+    w = torch.empty((0, Kk), dtype=torch.float32, device=dev)
+    tm, _ = B.moe_forward_plan(ffn, 0, Kk, torch.bfloat16)
+    perm = B.moe_permute(ids, Ee, tm)
+    torch.cuda.synchronize()
+    assert int(perm.num_tiles.cpu()[0]) == 0
+    x = torch.empty((0, Hh), dtype=torch.bfloat16, device=dev)
+    out = B.moe_w4a16_forward(ffn, x, w, perm)
+    torch.cuda.synchronize()
+    assert out.shape == (0, Hh)
+
+
 def test_forward_properties(dev):
     """Determinism, zero input, residual pass-through, and exact doubling of
     the output when every down-projection scale doubles."""
@@ -455,3 +491,26 @@ def test_forward_nvfp4_prefill_full_shape(dev):
                           _efn_nvfp4(host))
     ok, ratio = FX.within_tolerance(out[toks], ref)
     assert ok, ratio
+
+
+# -------------------------------------------- fused norm + router + top-K ---
+@pytest.mark.parametrize("T,Hh,Ee,Kk,with_bias,with_gain", [
+    (1, 4096, 352, 8, True, True), (5, 4096, 352, 8, False, True), (32, 4096, 352, 8, True, True),
+    (256, 4096, 352, 8, True, False), (513, 4096, 352, 8, True, True),
+    (9, 256, 16, 2, True, True), (4, 1024, 512, 16, False, False), (3, 192, 20, 3, True, True),
+    (6, 8192, 64, 4, True, True)])
+def test_norm_route_matches_separate_calls(dev, T, Hh, Ee, Kk, with_bias, with_gain):
+    """moe_norm_route (norm fused into the router up to 512 tokens and H = 4096,
+    separate kernels beyond: T = 513, H = 8192) is bitwise
+    moe_rmsnorm + moe_route_topk, which the tests above pin to the oracle."""
+    r = torch.from_numpy(synth.normal((T, Hh), 1.0, 14, 0, synth.T_X, T)).to(dev)
+    gain = torch.from_numpy(synth.norm_weight(Hh, 14, 0)).to(dev) if with_gain else None
+    wT = torch.from_numpy(synth.router_weight_T(Hh, Ee, 14)).to(dev)
+    bias = torch.from_numpy(synth.zipf_bias(Ee, 14, 0)).to(dev) if with_bias else None
+    a, ids, w = B.moe_norm_route(r, wT, Kk, norm_w=gain, eps=1e-5, bias=bias)
+    a2 = B.moe_rmsnorm(r, gain, 1e-5, torch.bfloat16)
+    ids2, w2 = B.moe_route_topk(Kk, x=a2, router_wT=wT, bias=bias)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), a2.view(torch.int16))
+    assert torch.equal(ids, ids2)
+    assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
