@@ -215,7 +215,7 @@ moe_status_t moe_permute_sizes(int T, int K, int E, int tile_m,
  *   a = bf16(residual / rms(residual) * (1 + norm_w))   (as moe_rmsnorm)
  *   topk_ids, topk_w = top-K routing of a from router_wT (+ bias)
  *                                                        (as moe_route_topk)
- * For batches of up to 512 tokens with H <= 4096 the norm, the cast and the
+ * For batches of up to 192 tokens with H <= 4096 the norm, the cast and the
  * router chains run as one kernel (each router work group normalizes its
  * token rows into LDS; the first expert block writes them to a_out), then
  * the top-K; otherwise the kernels of the separate calls run. Either way the

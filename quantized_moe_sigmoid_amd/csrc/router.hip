@@ -212,44 +212,50 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
 // E % 4 == 0: a column
 // group past E stages a copy of the last group; the lanes that read it
 // compute logits that are never stored.
-// XT = kXTouch: one 4-byte word of `xt` per chunk (KC 16-bit inputs apart)
-// is loaded with the chunk and folded into `sink`, which touches the
-// activation rows ahead of the scalar loads that consume them.
-constexpr int kXNone = 0, kXTouch = 1;
+// XT = kXStage (NT = 256, KC = 64): the chunk's inputs of 16 tokens ride
+// along with the weights, 4 bf16 per thread (token tid / 16, inputs 4 (tid %
+// 16) .. + 3 of the chunk), and are stored widened to float32 into `xs`
+// [stage][16][KC] with the weights.
+constexpr int kXNone = 0, kXStage = 1;
 
 template <int KC, int NP, int XT, int NT = 256>
 struct RouterWeightPipe {
     static constexpr int kStride = NT / 16;      // rows apart of a thread's loads
     static constexpr int kRows = KC / kStride;   // float4 loads per thread and chunk
     f32x4_t r[NP][kRows];
-    uint32_t xw[NP];
+    uint2 xw[NP];
     const float *src;                            // wT + (tid / 16) * E + column
-    const uint16_t *xt;
+    const uint16_t *xt;                          // kXStage: this thread's 4 inputs
+    float *xs;                                   // kXStage: [2][16][KC] in LDS
     size_t row;                                  // one row of wT, in floats (E)
     int wk, we, nch;
-    uint32_t sink;
 
     __device__ __forceinline__ RouterWeightPipe(const float *wT, int E, int e0, int H, int tid,
-                                                const uint16_t *xtouch = nullptr) {
+                                                const uint16_t *xsrc = nullptr,
+                                                float *xstage = nullptr) {
         wk = tid >> 4;
         we = (tid & 15) * 4;
         src = wT + (size_t)wk * E + (e0 + we < E ? e0 + we : E - 4);
         row = (size_t)E;
         nch = H / KC;
-        xt = xtouch;
-        sink = 0;
+        xt = xsrc;
+        xs = xstage;
     }
     __device__ __forceinline__ void load(int slot, int chunk) {
         chunk = chunk < nch ? chunk : nch - 1;
         const float *p = src + (size_t)chunk * KC * row;
 #pragma unroll
         for (int i = 0; i < kRows; ++i) r[slot][i] = *(const f32x4_t *)(p + i * kStride * row);
-        if (XT == kXTouch) xw[slot] = *(const uint32_t *)(xt + (size_t)chunk * KC);
+        if (XT == kXStage) xw[slot] = *(const uint2 *)(xt + (size_t)chunk * KC);
     }
-    __device__ __forceinline__ void store(float (*st)[kRtExp], int slot) {
+    __device__ __forceinline__ void store(float (*ws)[KC][kRtExp], int stage, int slot) {
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) *(f32x4_t *)&st[wk + kStride * i][we] = r[slot][i];
-        if (XT == kXTouch) sink ^= xw[slot];
+        for (int i = 0; i < kRows; ++i)
+            *(f32x4_t *)&ws[stage][wk + kStride * i][we] = r[slot][i];
+        if (XT == kXStage)
+            *(f32x4_t *)&xs[(stage * 16 + wk) * KC + we] =
+                f32x4_t{__uint_as_float(xw[slot].x << 16), __uint_as_float(xw[slot].x & 0xFFFF0000u),
+                        __uint_as_float(xw[slot].y << 16), __uint_as_float(xw[slot].y & 0xFFFF0000u)};
     }
     // chunks 0 .. NP-1 in flight
     __device__ __forceinline__ void prime() {
@@ -260,14 +266,14 @@ struct RouterWeightPipe {
     // runs the chain over chunk c. Ends with a barrier.
     template <typename Chunk>
     __device__ __forceinline__ void run(float (*ws)[KC][kRtExp], Chunk &&chunk) {
-        store(ws[0], 0);
+        store(ws, 0, 0);
         load(0, NP);
         __syncthreads();
         for (int c0 = 0; c0 < nch; c0 += NP) {
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
                 const int c = c0 + j;
-                store(ws[(c + 1) & 1], (j + 1) % NP);
+                store(ws, (c + 1) & 1, (j + 1) % NP);
                 load((j + 1) % NP, c + 1 + NP);
                 if (c < nch) chunk(c, ws[c & 1]);  // uniform over the block
                 __syncthreads();
@@ -276,65 +282,167 @@ struct RouterWeightPipe {
     }
 };
 
-// bf16 activations: the wave's 4 token rows are wave-uniform, so they are
-// read with scalar loads straight into SGPRs and widened there (bf16 -> f32
-// is a shift), and every FMA takes its x operand from an SGPR. Only wT goes
-// through LDS (one lane-varying 4-byte read per k), which removes the
-// broadcast x reads that bound the LDS return path above. Same tiles, same
-// per-(t, e) chain order.
+// Larger bf16 batches: 64 experts x 16 tokens a work group, 4 tokens per
+// wave. Each 64-input chunk stages the weight tile and the 16 tokens'
+// inputs (widened to float32) in LDS; a wave reads, per 16 inputs, 16
+// weights (8 pair reads, shared by its 4 tokens) and one 4-byte input word
+// per token (lane j of every 16-lane row: input j), and runs the 4 tokens'
+// chains interleaved, each FMA taking its input by DPP row_newbcast: about
+// 4.75 instructions per input position for 4 FMAs, where scalar loads of x
+// cost 8.5 (an unpacking SALU op per FMA). Same per-(t, e) chain order.
 //
-// TPW tokens per wave (4) for large batches; small ones run
-// router_rows_kernel below, one token per wave.
-template <int TPW, int NP>
-__global__ void __launch_bounds__(256) router_logits_bf16_kernel(
+// acc[i] = fma(x_i,j, w[j - J], acc[i]) for j = J .. J+3 in this order, i =
+// 0 .. 3 interleaved (independent chains), x_i,j = lane j of xq[i]'s 16-lane
+// row; as fma16_row_bcast.
+template <int J>
+__device__ __forceinline__ void fma4x4_row_bcast(float (&acc)[4], const float (&xq)[4],
+                                                 const float *w);
+template <>
+__device__ __forceinline__ void fma4x4_row_bcast<0>(float (&acc)[4], const float (&xq)[4],
+                                                    const float *w) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(xq[0]), "v"(xq[1]), "v"(xq[2]), "v"(xq[3]), "v"(w[0]), "v"(w[1]), "v"(w[2]),
+          "v"(w[3])
+        : "memory");
+}
+
+template <>
+__device__ __forceinline__ void fma4x4_row_bcast<4>(float (&acc)[4], const float (&xq)[4],
+                                                    const float *w) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(xq[0]), "v"(xq[1]), "v"(xq[2]), "v"(xq[3]), "v"(w[0]), "v"(w[1]), "v"(w[2]),
+          "v"(w[3])
+        : "memory");
+}
+
+template <>
+__device__ __forceinline__ void fma4x4_row_bcast<8>(float (&acc)[4], const float (&xq)[4],
+                                                    const float *w) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(xq[0]), "v"(xq[1]), "v"(xq[2]), "v"(xq[3]), "v"(w[0]), "v"(w[1]), "v"(w[2]),
+          "v"(w[3])
+        : "memory");
+}
+
+template <>
+__device__ __forceinline__ void fma4x4_row_bcast<12>(float (&acc)[4], const float (&xq)[4],
+                                                    const float *w) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %9 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %9 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %9 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %9 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %10 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %10 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %10 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %11 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %11 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %11 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %11 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(xq[0]), "v"(xq[1]), "v"(xq[2]), "v"(xq[3]), "v"(w[0]), "v"(w[1]), "v"(w[2]),
+          "v"(w[3])
+        : "memory");
+}
+
+template <int NP>
+__global__ void __launch_bounds__(256) router_tiled_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wT,
     const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
     __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
-    const int t0 = blockIdx.x * (4 * TPW), e0 = blockIdx.y * kRtExp;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // the wave's token rows as 32-bit pairs (rows past T read row t0; their
+    __shared__ __attribute__((aligned(16))) float xs[2][16][kRtKC];
+    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * kRtExp;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // this thread's staging share of x (rows past T read row t0; their
     // logits are not stored)
-    const uint32_t *xr[TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int t = t0 + TPW * wave + i;
-        xr[i] = (const uint32_t *)(x + (size_t)(t < T ? t : t0) * H);
-    }
-    // the x bytes of the wave's rows (TPW rows x 128 B per chunk) are also
-    // touched with vector loads NP chunks ahead, so the scalar loads that
-    // consume them hit L2 instead of waiting for HBM
-    const int tpf = t0 + TPW * wave + ((lane >> 3) % TPW);
-    const uint16_t *xpf = x + (size_t)(tpf < T ? tpf : t0) * H + (lane & 7) * 8;
-    RouterWeightPipe<kRtKC, NP, kXTouch> pipe(wT, E, e0, H, threadIdx.x, xpf);
+    const int ts = t0 + (tid >> 4);
+    const uint16_t *xsrc = x + (size_t)(ts < T ? ts : t0) * H + 4 * (tid & 15);
+    RouterWeightPipe<kRtKC, NP, kXStage> pipe(wT, E, e0, H, tid, xsrc, &xs[0][0][0]);
     pipe.prime();
 
-    float acc[TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) acc[i] = 0.0f;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     pipe.run(ws, [&](int c, float (*st)[kRtExp]) {
-        const int p0 = c * (kRtKC / 2);
-#pragma unroll 8
-        for (int k2 = 0; k2 < kRtKC / 2; ++k2) {
-            uint32_t xp[TPW];
+        const float *xw = &xs[c & 1][4 * wave][lane & 15];
+        float xq[2][4], w[2][16];
+        auto read = [&](int m, int b) {
 #pragma unroll
-            for (int i = 0; i < TPW; ++i) xp[i] = xr[i][p0 + k2];
-            const float w0 = st[2 * k2][lane], w1 = st[2 * k2 + 1][lane];
+            for (int i = 0; i < 4; ++i) xq[b][i] = xw[i * kRtKC + 16 * m];
 #pragma unroll
-            for (int i = 0; i < TPW; ++i)
-                acc[i] = __builtin_fmaf(__uint_as_float(xp[i] << 16), w0, acc[i]);
+            for (int j = 0; j < 16; ++j) w[b][j] = st[16 * m + j][lane];
+        };
+        read(0, 0);
 #pragma unroll
-            for (int i = 0; i < TPW; ++i)
-                acc[i] = __builtin_fmaf(__uint_as_float(xp[i] & 0xFFFF0000u), w1, acc[i]);
+        for (int m = 0; m < kRtKC / 16; ++m) {
+            if (m + 1 < kRtKC / 16) read(m + 1, (m + 1) & 1);
+            fma4x4_row_bcast<0>(acc, xq[m & 1], &w[m & 1][0]);
+            fma4x4_row_bcast<4>(acc, xq[m & 1], &w[m & 1][4]);
+            fma4x4_row_bcast<8>(acc, xq[m & 1], &w[m & 1][8]);
+            fma4x4_row_bcast<12>(acc, xq[m & 1], &w[m & 1][12]);
         }
     });
     const int e = e0 + lane;
-    if (pipe.sink == 0x9E3779B9u && H == 0) logits[0] = 0.0f;  // never true: keeps the prefetch
     if (e >= E) return;
     const float bv = bias ? bias[e] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int t = t0 + TPW * wave + i;
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * wave + i;
         if (t < T) logits[(size_t)t * E + e] = bias ? acc[i] + bv : acc[i];
     }
 }
@@ -399,7 +507,9 @@ __device__ __forceinline__ void fma16_row_bcast(float &acc, float xq, const floa
 // chain), not LDS bandwidth or the weight loads: prefetch depth and chunk
 // size change nothing, and neither does W, apart from the number of groups.
 // Same chain, same order as the other router kernels.
-constexpr int kRowsMaxT = 512;                   // batches up to this size
+constexpr int kRowsMaxT = 192;                   // batches up to this size (beyond it
+                                                 // router_tiled_kernel is faster: T = 256,
+                                                 // 64 us against 69)
 constexpr int kRowsMaxH = 4096;                  // W float32 rows in LDS
 
 template <bool NORM, int W>
@@ -560,7 +670,7 @@ moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, c
     if (x_dtype == MOE_BF16 && T <= kRowsMaxT && H <= kRowsMaxH)
         launch_rows<false>(x, nullptr, 0.f, T, H, wT, bias, E, nullptr, logits, s);
     else if (x_dtype == MOE_BF16)
-        hipLaunchKernelGGL((router_logits_bf16_kernel<4, 2>), grid, dim3(256), 0, s,
+        hipLaunchKernelGGL((router_tiled_kernel<2>), grid, dim3(256), 0, s,
                            (const uint16_t *)x, wT, bias, T, H, E, logits);
     else
         hipLaunchKernelGGL(router_logits_kernel<MOE_F16>, grid, dim3(256), 0, s,

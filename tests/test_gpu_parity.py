@@ -118,7 +118,8 @@ def test_route_from_router_weight_tiny(dev, act):
 
 
 @pytest.mark.parametrize("T,Hh,Ee,act", [(37, 4096, 352, "bf16"), (2048, 4096, 352, "bf16"),
-                                         (4099, 4096, 352, "bf16"), (9, 576, 20, "bf16"),
+                                         (4099, 4096, 352, "bf16"), (200, 4096, 352, "bf16"),
+                                         (9, 576, 20, "bf16"),
                                          (3, 64, 8, "bf16"), (600, 320, 24, "bf16"),
                                          (8, 256, 16, "f16"), (70, 192, 20, "f16")])
 def test_router_logits_bitwise(dev, T, Hh, Ee, act):
@@ -496,12 +497,13 @@ def test_forward_nvfp4_prefill_full_shape(dev):
 # -------------------------------------------- fused norm + router + top-K ---
 @pytest.mark.parametrize("T,Hh,Ee,Kk,with_bias,with_gain", [
     (1, 4096, 352, 8, True, True), (5, 4096, 352, 8, False, True), (32, 4096, 352, 8, True, True),
-    (256, 4096, 352, 8, True, False), (513, 4096, 352, 8, True, True),
+    (65, 4096, 352, 8, True, True), (192, 4096, 352, 8, True, False), (193, 4096, 352, 8, True, True),
     (9, 256, 16, 2, True, True), (4, 1024, 512, 16, False, False), (3, 192, 20, 3, True, True),
     (6, 8192, 64, 4, True, True)])
 def test_norm_route_matches_separate_calls(dev, T, Hh, Ee, Kk, with_bias, with_gain):
-    """moe_norm_route (norm fused into the router up to 512 tokens and H = 4096,
-    separate kernels beyond: T = 513, H = 8192) is bitwise
+    """moe_norm_route (norm fused into the router up to 192 tokens and H = 4096,
+    two tokens per work group up to 64, four beyond; separate kernels past
+    that: T = 193, H = 8192) is bitwise
     moe_rmsnorm + moe_route_topk, which the tests above pin to the oracle."""
     r = torch.from_numpy(synth.normal((T, Hh), 1.0, 14, 0, synth.T_X, T)).to(dev)
     gain = torch.from_numpy(synth.norm_weight(Hh, 14, 0)).to(dev) if with_gain else None
