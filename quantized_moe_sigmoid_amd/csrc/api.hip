@@ -173,15 +173,24 @@ struct FwdPlan {
 // grouped GEMM, which reads each weight once per tile of 64 slots, takes
 // over. One code path per shape class.
 bool mfma_layout_ok(const moe_weight_desc_t &d) {
-    // the GEMM loads a step's scales as one 4-byte (int4) or 16-byte (NVFP4) word
-    const int64_t a = d.fmt == MOE_W_INT4_G128 ? 4 : 16;
-    return aligned(d.scale, a) && d.scale_row_stride % a == 0 && d.scale_expert_stride % a == 0;
+    // the GEMM loads a step's scales as one 4-byte (int4) or 16-byte (NVFP4)
+    // word, and an asymmetric bank's two zero points as one 2-byte word
+    const bool i4 = d.fmt == MOE_W_INT4_G128 || d.fmt == MOE_W_INT4_G128_ASYM;
+    const int64_t a = i4 ? 4 : 16;
+    const bool zp = d.fmt != MOE_W_INT4_G128_ASYM ||
+                    (aligned(d.zero_point, 2) && d.zero_point_row_stride % 2 == 0 &&
+                     d.zero_point_expert_stride % 2 == 0 &&
+                     (int64_t)d.n * d.zero_point_row_stride < INT32_MAX);
+    return aligned(d.scale, a) && d.scale_row_stride % a == 0 && d.scale_expert_stride % a == 0 &&
+           zp;
 }
 
 bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
     const int E = ex.gate.num_experts, H = ex.gate.k, F = ex.gate.n;
-    // the GEMM decodes int4-g128 and NVFP4; the other formats run the GEMV
-    if (ex.gate.fmt != MOE_W_INT4_G128 && ex.gate.fmt != MOE_W_NVFP4_G16) return false;
+    // the GEMM decodes int4-g128 (signed or asymmetric) and NVFP4; the other
+    // formats run the GEMV
+    const int f = ex.gate.fmt;
+    if (f != MOE_W_INT4_G128 && f != MOE_W_INT4_G128_ASYM && f != MOE_W_NVFP4_G16) return false;
     // 32-bit buffer offsets must reach every row of an expert matrix
     const bool fits = (int64_t)F * ex.gate.qweight_row_stride < INT32_MAX &&
                       (int64_t)F * ex.up.qweight_row_stride < INT32_MAX &&
@@ -201,9 +210,10 @@ FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F
     p.max_tiles = p.max_rows / p.tile_m;
     p.off_h = 0;
     p.off_y = align256((size_t)p.max_rows * F * 2);
-    // MFMA path, int4: x in the decoder's pair order, and per-row sums of
-    // each 128-input group of x and of h
-    const bool sums = p.mfma && ex.gate.fmt == MOE_W_INT4_G128;
+    // MFMA path, int4 (signed or asymmetric): x in the decoder's pair order,
+    // and per-row sums of each 128-input group of x and of h
+    const bool sums = p.mfma && (ex.gate.fmt == MOE_W_INT4_G128 ||
+                                 ex.gate.fmt == MOE_W_INT4_G128_ASYM);
     p.off_xperm = p.off_y + align256((size_t)p.max_rows * H * 4);
     p.off_xsum = p.off_xperm + (sums ? align256((size_t)T * H * 2) : 0);
     p.off_hsum = p.off_xsum + (sums ? align256((size_t)T * (H / 128) * 4) : 0);

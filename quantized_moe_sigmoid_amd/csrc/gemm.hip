@@ -19,7 +19,9 @@
 //   partial sum P = sum (BIAS + q) x is turned into s_g (P - BIAS sum x) and
 //   accumulated in float32, with sum x over the group's 128 inputs of each
 //   row computed while staging the activations. The bf16 scale is applied
-//   exactly once per group in float32.
+//   exactly once per group in float32. Asymmetric int4 (uint4 codes, zero
+//   point z per group and column): B holds MAGIC + q and the group's term is
+//   s_g (P - (MAGIC + z) sum x).
 // NVFP4: B holds e2m1 * e4m3 exactly in 16 bits (<= 6 significant bits);
 //   the float32 global scale multiplies the accumulators in the epilogue.
 //
@@ -39,10 +41,26 @@ constexpr int kGemmBN = 128;         // output columns per block
 constexpr int kGemmKS = 256;         // inputs per pipeline step (two int4 groups)
 constexpr int kGemmRowBytes = kGemmKS * 2;
 
+// The int4 group path: signed int4-g128, or asymmetric (uint4 codes and a
+// 4-bit zero point per group) int4-g128.
+__host__ __device__ constexpr bool int4_g128(int fmt) {
+    return fmt == MOE_W_INT4_G128 || fmt == MOE_W_INT4_G128_ASYM;
+}
+
+// The bias of the decoded 16-bit values: signed codes BIAS + q (decode.h),
+// asymmetric codes MAGIC + q, whose zero point is added per group and
+// column (see GemmCtx::step).
+template <int ACT, int FMT>
+__device__ __forceinline__ constexpr float g128_bias() {
+    return FMT == MOE_W_INT4_G128_ASYM ? Int4Bias<ACT>::kMagicValue : Int4Bias<ACT>::kBias;
+}
+
 struct GemmMat {
     const uint8_t *q, *s;
     const float *gs;
     int64_t qe, qr, se, sr;
+    const uint8_t *z;                            // asymmetric int4: zero points [E][n][k/128]
+    int64_t ze, zr;
 };
 
 template <int ACT>
@@ -72,6 +90,12 @@ __device__ __forceinline__ uint4 decode_b(uint32_t w, float bs, uint32_t qmask) 
         int4_biased_pairs_masked<ACT>(w, qmask, p);
         (void)bs;
         return make_uint4(p[0], p[1], p[2], p[3]);
+    } else if constexpr (FMT == MOE_W_INT4_G128_ASYM) {
+        // unsigned codes: MAGIC + q, the same pair order as the signed form
+        (void)bs;
+        return make_uint4((w & qmask) | Int4Bias<ACT>::kMagic, ((w >> 4) & qmask) | Int4Bias<ACT>::kMagic,
+                          ((w >> 8) & qmask) | Int4Bias<ACT>::kMagic,
+                          ((w >> 12) & qmask) | Int4Bias<ACT>::kMagic);
     } else {
         (void)qmask;
         uint32_t d[4];
@@ -105,13 +129,17 @@ struct StepW {
     uint4 w[4];
     uint32_t s32;      // int4: the step's two bf16 group scales
     uint4 s128;        // NVFP4: the step's sixteen E4M3 block scales
+    uint32_t z16;      // asymmetric int4: the step's two zero points (bytes)
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t q, __amdgpu_buffer_rsrc_t s,
-                                         int qoff, int soff, int step, int half) {
+                                         __amdgpu_buffer_rsrc_t z, int qoff, int soff, int zoff,
+                                         int step, int half) {
+        if (FMT == MOE_W_INT4_G128_ASYM)
+            z16 = __builtin_amdgcn_raw_buffer_load_b16(z, zoff + step * 2, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 q, qoff + step * (kGemmKS / 2) + i * 32 + half * 16, 0, 0));
-        if (FMT == MOE_W_INT4_G128)
+        if (int4_g128(FMT))
             s32 = __builtin_amdgcn_raw_buffer_load_b32(s, soff + step * 4, 0, 0);
         else
             s128 = __builtin_bit_cast(uint4,
@@ -154,7 +182,7 @@ struct Stager {
 #pragma unroll
         for (int g = 0; g < 8; ++g)
             v[g] = *(const u32x4_t *)(src_row + step * kGemmKS + (g * 4 + kc) * 8);
-        if (FMT == MOE_W_INT4_G128 && threadIdx.x < kGemmTM) {
+        if (int4_g128(FMT) && threadIdx.x < kGemmTM) {
             rs0 = sum_row[2 * step];
             rs1 = sum_row[2 * step + 1];
         }
@@ -164,7 +192,7 @@ struct Stager {
 #pragma unroll
         for (int g = 0; g < 8; ++g)
             *(u32x4_t *)(buf + (g * kGemmTM + row) * 64 + ((threadIdx.x & 3) << 4)) = v[g];
-        if (FMT == MOE_W_INT4_G128 && threadIdx.x < kGemmTM) {
+        if (int4_g128(FMT) && threadIdx.x < kGemmTM) {
             xs[threadIdx.x] = rs0;
             xs[kGemmTM + threadIdx.x] = rs1;
         }
@@ -186,7 +214,7 @@ struct GemmCtx {
             const uint4 wa0 = wa_s.w[2 * gi], wa1 = wa_s.w[2 * gi + 1];
             const uint4 wb0 = wb_s.w[2 * gi], wb1 = wb_s.w[2 * gi + 1];
             uint32_t ma = 0, mbk = 0;
-            if (FMT == MOE_W_INT4_G128) {
+            if (int4_g128(FMT)) {
                 float sa_g = bf16_bits_to_f32(gi ? wa_s.s32 >> 16 : wa_s.s32 & 0xFFFF);
                 float sb_g = bf16_bits_to_f32(gi ? wb_s.s32 >> 16 : wb_s.s32 & 0xFFFF);
                 // a zero scale drops the group: its nibbles decode as q = 0
@@ -196,6 +224,15 @@ struct GemmCtx {
                 sb_g = sb_g == 0.0f ? 1.0f : sb_g;
                 const float ra = sprev_a * __builtin_amdgcn_rcpf(sa_g);
                 const float rb = sprev_b * __builtin_amdgcn_rcpf(sb_g);
+                // asymmetric: the group's correction is -(MAGIC + z) sum x, the
+                // staged -MAGIC sum x times (MAGIC + z) / MAGIC (exact: MAGIC is
+                // a power of two); a dropped group keeps q = 0 and factor 1
+                float za = 1.0f, zb = 1.0f;
+                if (FMT == MOE_W_INT4_G128_ASYM) {
+                    constexpr float kM = Int4Bias<ACT>::kMagicValue;
+                    if (ma) za = (kM + (float)((wa_s.z16 >> (8 * gi)) & 0xFFu)) * (1.0f / kM);
+                    if (mbk) zb = (kM + (float)((wb_s.z16 >> (8 * gi)) & 0xFFu)) * (1.0f / kM);
+                }
                 sprev_a = sa_g;
                 sprev_b = sb_g;
 #pragma unroll
@@ -207,8 +244,10 @@ struct GemmCtx {
                         const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            da[mb][4 * b4 + r] = __builtin_fmaf(da[mb][4 * b4 + r], ra, xv[r]);
-                            db[mb][4 * b4 + r] = __builtin_fmaf(db[mb][4 * b4 + r], rb, xv[r]);
+                            const float xa = FMT == MOE_W_INT4_G128_ASYM ? xv[r] * za : xv[r];
+                            const float xb = FMT == MOE_W_INT4_G128_ASYM ? xv[r] * zb : xv[r];
+                            da[mb][4 * b4 + r] = __builtin_fmaf(da[mb][4 * b4 + r], ra, xa);
+                            db[mb][4 * b4 + r] = __builtin_fmaf(db[mb][4 * b4 + r], rb, xb);
                         }
                     }
                 }
@@ -248,8 +287,13 @@ struct GemmCtx {
 // writes h = silu(gate) * up. Otherwise A and B are the same down matrix at
 // columns c and c + 32, so a wave owns 64 output columns and every
 // activation fragment read from LDS feeds two MFMAs in both passes.
+// The asymmetric form needs a few registers more than the 256 that keep two
+// waves per SIMD; held to two waves it spills 1 - 2 registers, which costs
+// less than running one wave per SIMD (T = 2048 gate/up: 824 against 1028
+// us). The other formats fit without the bound, and get none.
 template <int ACT, int FMT, bool GATEUP>
-__global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
+__global__ void __launch_bounds__(kGemmThreads)
+    __attribute__((amdgpu_waves_per_eu(FMT == MOE_W_INT4_G128_ASYM ? 2 : 1))) gemm_kernel(
     GemmMat A, GemmMat Bm, int n_rows, int kin,
     // xin and rowsum_in are not __restrict__: as restrict read-only kernel
     // arguments their loads count as invariant and get sunk below the MFMAs
@@ -292,7 +336,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
         const uint64_t live = __ballot(sl >= 0);
         if (threadIdx.x == 0) m_sh = __popcll(live);
         if (sl < 0) { sl = sorted_slots[tile * kGemmTM]; prow = 0; }
-        if (FMT == MOE_W_INT4_G128)
+        if (int4_g128(FMT))
             sum_row = rowsum_in +
                       (x_from_slots ? (size_t)(sl / topk) : (size_t)tile * kGemmTM + prow) * groups;
     }
@@ -309,6 +353,11 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
     const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(Bm.s + e * Bm.se, (int64_t)n_rows * Bm.sr);
     const int qoff_a = (ok_a ? col_a : 0) * (int)A.qr, soff_a = (ok_a ? col_a : 0) * (int)A.sr;
     const int qoff_b = (ok_b ? col_b : 0) * (int)Bm.qr, soff_b = (ok_b ? col_b : 0) * (int)Bm.sr;
+    const bool asym = FMT == MOE_W_INT4_G128_ASYM;
+    const __amdgpu_buffer_rsrc_t rza = buffer_rsrc(asym ? A.z + e * A.ze : A.q, asym ? (int64_t)n_rows * A.zr : 0);
+    const __amdgpu_buffer_rsrc_t rzb = buffer_rsrc(asym ? Bm.z + e * Bm.ze : Bm.q, asym ? (int64_t)n_rows * Bm.zr : 0);
+    const int zoff_a = asym ? (ok_a ? col_a : 0) * (int)A.zr : 0;
+    const int zoff_b = asym ? (ok_b ? col_b : 0) * (int)Bm.zr : 0;
 
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -324,8 +373,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
     Stager<FMT> st;
     StepW<FMT> wa0, wb0, wa1, wb1;
     st.load(src_row, sum_row, 0);
-    wa0.load(rqa, rsa, qoff_a, soff_a, 0, cx.half);
-    wb0.load(rqb, rsb, qoff_b, soff_b, 0, cx.half);
+    wa0.load(rqa, rsa, rza, qoff_a, soff_a, zoff_a, 0, cx.half);
+    wb0.load(rqb, rsb, rzb, qoff_b, soff_b, zoff_b, 0, cx.half);
     st.store(abuf0, xsum0);
     __syncthreads();
     cx.two_mb = m_sh > 32;
@@ -339,8 +388,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
         /* would merge with the old register values and force early waits */         \
         const int sn = more ? s_ + 1 : s_;                                             \
         st.load(src_row, sum_row, sn);                                                 \
-        NWA.load(rqa, rsa, qoff_a, soff_a, sn, cx.half);                               \
-        NWB.load(rqb, rsb, qoff_b, soff_b, sn, cx.half);                               \
+        NWA.load(rqa, rsa, rza, qoff_a, soff_a, zoff_a, sn, cx.half);                  \
+        NWB.load(rqb, rsb, rzb, qoff_b, soff_b, zoff_b, sn, cx.half);                  \
         /* keep the compiler from sinking the prefetch below the MFMAs */             \
         /* (no memory clobber: it would pin the staging registers to memory) */       \
         __builtin_amdgcn_sched_barrier(0);                                             \
@@ -358,12 +407,12 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
 
     const int m_valid = m_sh;
     const int half = cx.half;
-    const float ga = FMT == MOE_W_INT4_G128 ? cx.sprev_a : A.gs[e];
-    const float gb = FMT == MOE_W_INT4_G128 ? cx.sprev_b : Bm.gs[e];
+    const float ga = int4_g128(FMT) ? cx.sprev_a : A.gs[e];
+    const float gb = int4_g128(FMT) ? cx.sprev_b : Bm.gs[e];
     float *hs = (float *)abuf0;                    // [64 rows][128 cols] for the row sums
     // position of column c inside the pair-permuted layout of its 8-group
     // (int4 MFMA path only): (c0 c4 c1 c5 c2 c6 c3 c7)
-    const int hcol = FMT == MOE_W_INT4_G128 ? (col_a & ~7) | ((col_a & 3) << 1) | ((col_a >> 2) & 1)
+    const int hcol = int4_g128(FMT) ? (col_a & ~7) | ((col_a & 3) << 1) | ((col_a >> 2) & 1)
                                             : col_a;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -374,7 +423,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
             if (GATEUP) {
                 const uint16_t hb = f32_to_act<ACT>(silu_mul(cx.da[mb][v] * ga, cx.db[mb][v] * gb));
                 if (m < m_valid && ok_a) hout[r * n_rows + hcol] = hb;
-                if (FMT == MOE_W_INT4_G128)
+                if (int4_g128(FMT))
                     hs[m * kGemmBN + wave * 32 + cx.l32] = m < m_valid ? act_to_f32<ACT>(hb) : 0.0f;
             } else if (m < m_valid) {
                 if (ok_a) yout[r * n_rows + col_a] = cx.da[mb][v] * ga;
@@ -382,7 +431,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
             }
         }
     }
-    if (GATEUP && FMT == MOE_W_INT4_G128) {
+    if (GATEUP && int4_g128(FMT)) {
         // -BIAS * sum of the rounded h over this block's 128 columns: the
         // down projection's 128-input group nb of row m
         __syncthreads();
@@ -393,14 +442,14 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(
         t += shfl_xor_f(t, 1);
         t += shfl_xor_f(t, 2);
         if (qtr == 0 && row < m_valid)
-            hsum_out[((size_t)tile * kGemmTM + row) * n_blocks + nb] = -Int4Bias<ACT>::kBias * t;
+            hsum_out[((size_t)tile * kGemmTM + row) * n_blocks + nb] = -g128_bias<ACT, FMT>() * t;
     }
 }
 
 // int4 MFMA path, once per token: x with the inputs of every 8-group in
 // the decoder's pair order (x0 x4 x1 x5 x2 x6 x3 x7), and -BIAS times the
 // sum of each 128-input group (float32).
-template <int ACT>
+template <int ACT, int FMT>
 __global__ void __launch_bounds__(256) prep_x_kernel(const uint16_t *__restrict__ x, int H,
                                                      uint16_t *__restrict__ xp,
                                                      float *__restrict__ sums) {
@@ -425,14 +474,15 @@ __global__ void __launch_bounds__(256) prep_x_kernel(const uint16_t *__restrict_
         }
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) s += shfl_xor_f(s, m);
-        if (g < groups && sub == 0) sums[(size_t)t * groups + g] = -Int4Bias<ACT>::kBias * s;
+        if (g < groups && sub == 0) sums[(size_t)t * groups + g] = -g128_bias<ACT, FMT>() * s;
     }
 }
 
 inline GemmMat gemm_mat(const moe_weight_desc_t &d) {
     return GemmMat{(const uint8_t *)d.qweight, (const uint8_t *)d.scale, d.global_scale,
                    d.qweight_expert_stride, d.qweight_row_stride, d.scale_expert_stride,
-                   d.scale_row_stride};
+                   d.scale_row_stride, d.zero_point, d.zero_point_expert_stride,
+                   d.zero_point_row_stride};
 }
 
 template <int ACT, int FMT>
@@ -442,8 +492,8 @@ moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int T, 
                             const std::function<moe_status_t(int)> &mark) {
     const int F = ex.gate.n, H = ex.gate.k;
     const uint16_t *xa = x;
-    if (FMT == MOE_W_INT4_G128) {
-        hipLaunchKernelGGL(prep_x_kernel<ACT>, dim3(T), dim3(256), 0, s, x, H, xperm, xsum);
+    if (int4_g128(FMT)) {
+        hipLaunchKernelGGL((prep_x_kernel<ACT, FMT>), dim3(T), dim3(256), 0, s, x, H, xperm, xsum);
         MOE_LAUNCH_CHECK();
         xa = xperm;
     }
@@ -479,12 +529,17 @@ moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int ac
                                  const std::function<moe_status_t(int)> &mark) {
     const uint16_t *xx = (const uint16_t *)x;
     uint16_t *hh = (uint16_t *)h;
-    const bool nv = ex.gate.fmt == MOE_W_NVFP4_G16;
+#define MOE_GEMM_FWD(A, F)                                                                    \
+    gemm_forward_t<A, F>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark)
+    const int f = ex.gate.fmt;
     if (act == MOE_BF16)
-        return nv ? gemm_forward_t<MOE_BF16, MOE_W_NVFP4_G16>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark)
-                  : gemm_forward_t<MOE_BF16, MOE_W_INT4_G128>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark);
-    return nv ? gemm_forward_t<MOE_F16, MOE_W_NVFP4_G16>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark)
-              : gemm_forward_t<MOE_F16, MOE_W_INT4_G128>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark);
+        return f == MOE_W_NVFP4_G16        ? MOE_GEMM_FWD(MOE_BF16, MOE_W_NVFP4_G16)
+               : f == MOE_W_INT4_G128_ASYM ? MOE_GEMM_FWD(MOE_BF16, MOE_W_INT4_G128_ASYM)
+                                           : MOE_GEMM_FWD(MOE_BF16, MOE_W_INT4_G128);
+    return f == MOE_W_NVFP4_G16        ? MOE_GEMM_FWD(MOE_F16, MOE_W_NVFP4_G16)
+           : f == MOE_W_INT4_G128_ASYM ? MOE_GEMM_FWD(MOE_F16, MOE_W_INT4_G128_ASYM)
+                                       : MOE_GEMM_FWD(MOE_F16, MOE_W_INT4_G128);
+#undef MOE_GEMM_FWD
 }
 
 }  // namespace moe

@@ -95,12 +95,41 @@ def test_forward_small(dev, fmt, act):
     assert ok, ratio
 
 
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("zero_groups", [False, True])
+def test_forward_small_grouped_gemm(dev, act, zero_groups):
+    """Asymmetric int4-g128 on the grouped MFMA GEMM (T*K >= 4E): 4 experts,
+    hidden 512, width 256, 40 tokens, top-2, several tiles per expert; with
+    zero_groups, some groups of every matrix get a zero scale (the GEMM
+    drops such a group), which the oracle dequantizes to zeros."""
+    fmt = B.MOE_W_INT4_G128_ASYM
+    Ee, Hh, Ff, T, Kk = 4, 512, 256, 40, 2
+    banks, host = [], []
+    for which, (n, k) in (("gate", (Ff, Hh)), ("up", (Ff, Hh)), ("down", (Hh, Ff))):
+        q, s, z = FX.variant_bank_oracle(Ee, n, k, 24, 0, which, fmt)
+        if zero_groups:
+            s = s.copy()
+            s[:, ::7, 1] = 0
+            s[1, 3, :] = 0
+        banks.append(_bank(*FX.variant_to_device(q, s, z, dev)))
+        host.append((q, s, z))
+    ffn = B.ffn(*banks)
+    x = synth.activations(T, Hh, act, 24)
+    lg = synth.router_logits(T, Ee, 24)
+    out = _layer(ffn, x.to(dev), lg, Ee, Kk, dev)
+    oids = OR.topk_ids(lg, Kk)
+    ref = FX.oracle_layer(x, oids, OR.routing_weights(lg, oids), _experts_fn(host))
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("T,act,toks", [(8, "f16", list(range(8))), (64, "f16", [0, 17, 40, 63]),
-                                        (256, "bf16", [0, 101, 255])])
+                                        (256, "bf16", [0, 101, 255]), (2048, "f16", [0, 1000, 2047])])
 def test_forward_layer_shape(dev, fmt, T, act, toks):
-    """352 experts, hidden 4096, width 1536: decode batches and a
-    prefill-sized one (which these formats also run on the decode kernels)."""
+    """352 experts, hidden 4096, width 1536: decode batches and prefill-sized
+    ones (asymmetric int4 runs the grouped MFMA GEMM there, int4-g32 and
+    int8 the decode kernels)."""
     ffn, host = _random_ffn(fmt, 600 + T, dev)
     x = synth.activations(T, H, act, 23)
     lg = synth.router_logits(T, E, 23)
