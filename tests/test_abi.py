@@ -382,17 +382,32 @@ def _bank_v(fmt, E, n, k, srow=None, zrow=None, zp=True, qrow=None):
 
 
 @pytest.mark.parametrize("fmt", [B.MOE_W_INT4_G32, B.MOE_W_INT4_G128_ASYM, B.MOE_W_INT8_G128])
-def test_int4_variant_banks_plan_the_decode_kernels(L, fmt):
-    """The variants are accepted and, even at prefill size, planned on the
-    GEMV tile (the GEMM decodes int4-g128 and NVFP4 only)."""
+def test_variant_banks_plan_kernels(L, fmt):
+    """The variants are accepted; at prefill size asymmetric int4 is planned
+    on the grouped GEMM's tile like int4-g128, while int4-g32 and int8 stay
+    on the GEMV tile (the GEMM does not decode them)."""
     f = B.FfnDesc(_bank_v(fmt, 352, 1536, 4096), _bank_v(fmt, 352, 1536, 4096),
                   _bank_v(fmt, 352, 4096, 1536))
     st, tm_small, _ = _plan(f, T=8)
     assert st == B.MOE_OK
     st, tm_big, _ = _plan(f, T=2048)
-    assert st == B.MOE_OK and tm_big == tm_small
+    assert st == B.MOE_OK
     st, tm_g128, _ = _plan(_ffn(), T=2048)
-    assert tm_g128 != tm_big
+    assert tm_g128 != tm_small
+    assert tm_big == (tm_g128 if fmt == B.MOE_W_INT4_G128_ASYM else tm_small)
+
+
+def test_asym_bank_with_odd_zero_point_stride_plans_the_gemv(L):
+    """The GEMM loads a step's two zero points as one 2-byte word; a bank
+    whose zero-point rows are an odd number of bytes apart runs the GEMV at
+    every size."""
+    A = B.MOE_W_INT4_G128_ASYM
+    f = B.FfnDesc(_bank_v(A, 352, 1536, 4096, zrow=33), _bank_v(A, 352, 1536, 4096, zrow=33),
+                  _bank_v(A, 352, 4096, 1536, zrow=13))
+    st, tm_small, _ = _plan(f, T=8)
+    assert st == B.MOE_OK
+    st, tm_big, _ = _plan(f, T=2048)
+    assert st == B.MOE_OK and tm_big == tm_small
 
 
 def test_int4_variant_bank_errors(L):
