@@ -22,6 +22,9 @@
 //   exactly once per group in float32. Asymmetric int4 (uint4 codes, zero
 //   point z per group and column): B holds MAGIC + q and the group's term is
 //   s_g (P - (MAGIC + z) sum x).
+// int4-g32: one 32x32x16 MFMA takes inputs from two 32-input groups (its
+//   two lane halves), so the scale cannot be applied between MFMAs; B holds
+//   q s_g instead (exact in fp16, rounded once in bf16), as for NVFP4.
 // NVFP4: B holds e2m1 * e4m3 exactly in 16 bits (<= 6 significant bits);
 //   the float32 global scale multiplies the accumulators in the epilogue.
 //
@@ -45,6 +48,12 @@ constexpr int kGemmRowBytes = kGemmKS * 2;
 // 4-bit zero point per group) int4-g128.
 __host__ __device__ constexpr bool int4_g128(int fmt) {
     return fmt == MOE_W_INT4_G128 || fmt == MOE_W_INT4_G128_ASYM;
+}
+
+// Every int4 form: nibble pairs (i, i + 4) of a word, so x and h are
+// staged in that pair order.
+__host__ __device__ constexpr bool int4_pairs(int fmt) {
+    return int4_g128(fmt) || fmt == MOE_W_INT4_G32;
 }
 
 // The bias of the decoded 16-bit values: signed codes BIAS + q (decode.h),
@@ -90,6 +99,33 @@ __device__ __forceinline__ uint4 decode_b(uint32_t w, float bs, uint32_t qmask) 
         int4_biased_pairs_masked<ACT>(w, qmask, p);
         (void)bs;
         return make_uint4(p[0], p[1], p[2], p[3]);
+    } else if constexpr (FMT == MOE_W_INT4_G32) {
+        // the 32-input group's scale goes into the operand: q s in 16 bits.
+        // fp16: |q| <= 8 has at most 3 significant bits and the bf16 scale
+        // 8, so q s is exact (for scales in fp16's normal range), formed by
+        // an exact packed subtraction of the bias and an exact product.
+        // bf16: q s is exact in float32 and rounded once to bf16.
+        (void)qmask;
+        uint32_t p[4];
+        int4_biased_pairs<ACT>(w, p);
+        uint32_t d[4];
+        if constexpr (ACT == MOE_F16) {
+            const _Float16 sh = (_Float16)bs;
+            const half2_t s2 = {sh, sh};
+            const half2_t nb = {(_Float16)(-Int4Bias<MOE_F16>::kBias),
+                                (_Float16)(-Int4Bias<MOE_F16>::kBias)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                d[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, p[i]) + nb) * s2);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = (__uint_as_float(p[i] << 16) - Int4Bias<MOE_BF16>::kBias) * bs;
+                const float hi = (__uint_as_float(p[i] & 0xFFFF0000u) - Int4Bias<MOE_BF16>::kBias) * bs;
+                d[i] = (uint32_t)f32_to_act<MOE_BF16>(lo) | ((uint32_t)f32_to_act<MOE_BF16>(hi) << 16);
+            }
+        }
+        return make_uint4(d[0], d[1], d[2], d[3]);
     } else if constexpr (FMT == MOE_W_INT4_G128_ASYM) {
         // unsigned codes: MAGIC + q, the same pair order as the signed form
         (void)bs;
@@ -146,6 +182,11 @@ struct StepW {
                                       __builtin_amdgcn_raw_buffer_load_b128(s, soff + step * 16, 0, 0));
     }
 };
+
+__device__ __forceinline__ uint32_t half_of(uint4 v, int i) {
+    const uint32_t d = i < 4 ? (i < 2 ? v.x : v.y) : (i < 6 ? v.z : v.w);
+    return (d >> (16 * (i & 1))) & 0xFFFF;
+}
 
 __device__ __forceinline__ uint32_t byte_of(uint4 v, int i) {
     const uint32_t d = i < 8 ? (i < 4 ? v.x : v.y) : (i < 12 ? v.z : v.w);
@@ -265,6 +306,11 @@ struct GemmCtx {
                         const int blk = i * 4 + half * 2 + (j >> 1);
                         bsa = e4m3_to_f32(byte_of(wa_s.s128, blk));
                         bsb = e4m3_to_f32(byte_of(wb_s.s128, blk));
+                    }
+                    if (FMT == MOE_W_INT4_G32) {
+                        // this lane's 32 inputs of the chunk: group 2 i + half
+                        bsa = bf16_bits_to_f32(half_of(wa_s.s128, 2 * i + half));
+                        bsb = bf16_bits_to_f32(half_of(wb_s.s128, 2 * i + half));
                     }
                     const uint4 ob = decode_b<ACT, FMT>(wav[j], bsa, ma);
                     const uint4 obb = decode_b<ACT, FMT>(wbv[j], bsb, mbk);
@@ -407,12 +453,14 @@ __global__ void __launch_bounds__(kGemmThreads)
 
     const int m_valid = m_sh;
     const int half = cx.half;
-    const float ga = int4_g128(FMT) ? cx.sprev_a : A.gs[e];
-    const float gb = int4_g128(FMT) ? cx.sprev_b : Bm.gs[e];
+    // NVFP4: the global scale; int4-g128: the last group's scale (the
+    // accumulators are kept in its units); int4-g32: 1 (scales in the operands)
+    const float ga = FMT == MOE_W_NVFP4_G16 ? A.gs[e] : cx.sprev_a;
+    const float gb = FMT == MOE_W_NVFP4_G16 ? Bm.gs[e] : cx.sprev_b;
     float *hs = (float *)abuf0;                    // [64 rows][128 cols] for the row sums
     // position of column c inside the pair-permuted layout of its 8-group
     // (int4 MFMA path only): (c0 c4 c1 c5 c2 c6 c3 c7)
-    const int hcol = int4_g128(FMT) ? (col_a & ~7) | ((col_a & 3) << 1) | ((col_a >> 2) & 1)
+    const int hcol = int4_pairs(FMT) ? (col_a & ~7) | ((col_a & 3) << 1) | ((col_a >> 2) & 1)
                                             : col_a;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -492,7 +540,7 @@ moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int T, 
                             const std::function<moe_status_t(int)> &mark) {
     const int F = ex.gate.n, H = ex.gate.k;
     const uint16_t *xa = x;
-    if (int4_g128(FMT)) {
+    if (int4_pairs(FMT)) {
         hipLaunchKernelGGL((prep_x_kernel<ACT, FMT>), dim3(T), dim3(256), 0, s, x, H, xperm, xsum);
         MOE_LAUNCH_CHECK();
         xa = xperm;
@@ -535,9 +583,11 @@ moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int ac
     if (act == MOE_BF16)
         return f == MOE_W_NVFP4_G16        ? MOE_GEMM_FWD(MOE_BF16, MOE_W_NVFP4_G16)
                : f == MOE_W_INT4_G128_ASYM ? MOE_GEMM_FWD(MOE_BF16, MOE_W_INT4_G128_ASYM)
+               : f == MOE_W_INT4_G32       ? MOE_GEMM_FWD(MOE_BF16, MOE_W_INT4_G32)
                                            : MOE_GEMM_FWD(MOE_BF16, MOE_W_INT4_G128);
     return f == MOE_W_NVFP4_G16        ? MOE_GEMM_FWD(MOE_F16, MOE_W_NVFP4_G16)
            : f == MOE_W_INT4_G128_ASYM ? MOE_GEMM_FWD(MOE_F16, MOE_W_INT4_G128_ASYM)
+           : f == MOE_W_INT4_G32       ? MOE_GEMM_FWD(MOE_F16, MOE_W_INT4_G32)
                                        : MOE_GEMM_FWD(MOE_F16, MOE_W_INT4_G128);
 #undef MOE_GEMM_FWD
 }

@@ -383,9 +383,9 @@ def _bank_v(fmt, E, n, k, srow=None, zrow=None, zp=True, qrow=None):
 
 @pytest.mark.parametrize("fmt", [B.MOE_W_INT4_G32, B.MOE_W_INT4_G128_ASYM, B.MOE_W_INT8_G128])
 def test_variant_banks_plan_kernels(L, fmt):
-    """The variants are accepted; at prefill size asymmetric int4 is planned
-    on the grouped GEMM's tile like int4-g128, while int4-g32 and int8 stay
-    on the GEMV tile (the GEMM does not decode them)."""
+    """The variants are accepted; at prefill size the int4 forms are planned
+    on the grouped GEMM's tile like int4-g128, while int8 stays on the GEMV
+    tile (the GEMM does not decode it)."""
     f = B.FfnDesc(_bank_v(fmt, 352, 1536, 4096), _bank_v(fmt, 352, 1536, 4096),
                   _bank_v(fmt, 352, 4096, 1536))
     st, tm_small, _ = _plan(f, T=8)
@@ -394,7 +394,7 @@ def test_variant_banks_plan_kernels(L, fmt):
     assert st == B.MOE_OK
     st, tm_g128, _ = _plan(_ffn(), T=2048)
     assert tm_g128 != tm_small
-    assert tm_big == (tm_g128 if fmt == B.MOE_W_INT4_G128_ASYM else tm_small)
+    assert tm_big == (tm_small if fmt == B.MOE_W_INT8_G128 else tm_g128)
 
 
 def test_asym_bank_with_odd_zero_point_stride_plans_the_gemv(L):
@@ -404,6 +404,19 @@ def test_asym_bank_with_odd_zero_point_stride_plans_the_gemv(L):
     A = B.MOE_W_INT4_G128_ASYM
     f = B.FfnDesc(_bank_v(A, 352, 1536, 4096, zrow=33), _bank_v(A, 352, 1536, 4096, zrow=33),
                   _bank_v(A, 352, 4096, 1536, zrow=13))
+    st, tm_small, _ = _plan(f, T=8)
+    assert st == B.MOE_OK
+    st, tm_big, _ = _plan(f, T=2048)
+    assert st == B.MOE_OK and tm_big == tm_small
+
+
+def test_g32_bank_with_unaligned_scale_rows_plans_the_gemv(L):
+    """The GEMM loads a step's eight int4-g32 scales as one 16-byte word; a
+    bank whose scale rows are not a multiple of 16 bytes apart runs the GEMV
+    at every size."""
+    G = B.MOE_W_INT4_G32
+    f = B.FfnDesc(_bank_v(G, 352, 1536, 4096, srow=264), _bank_v(G, 352, 1536, 4096, srow=264),
+                  _bank_v(G, 352, 4096, 1536, srow=104))
     st, tm_small, _ = _plan(f, T=8)
     assert st == B.MOE_OK
     st, tm_big, _ = _plan(f, T=2048)
