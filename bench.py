@@ -500,7 +500,8 @@ def main():
         for wl, T in (("decode", 1), ("decode", 8), ("decode", 64), ("prefill", 2048),
                       ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("nvfp4-csf-expand", 64),
                       ("int4-g32", 64), ("int4-g32", 2048),
-                      ("int4-asym", 64), ("int4-asym", 2048), ("int8", 64), ("stack", 32),
+                      ("int4-asym", 64), ("int4-asym", 2048), ("int8", 64), ("int8", 2048),
+                      ("stack", 32),
                       ("stack", 4096)):
             if (wl, T) != (args.workload, main_T):
                 jobs.append((wl, T))

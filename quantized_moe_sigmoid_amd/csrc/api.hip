@@ -176,7 +176,8 @@ bool mfma_layout_ok(const moe_weight_desc_t &d) {
     // the GEMM loads a step's scales as one 4-byte (int4) or 16-byte (NVFP4)
     // word, and an asymmetric bank's two zero points as one 2-byte word
     // (int4-g32: the step's eight bf16 scales, 16 bytes)
-    const bool i4 = d.fmt == MOE_W_INT4_G128 || d.fmt == MOE_W_INT4_G128_ASYM;
+    const bool i4 = d.fmt == MOE_W_INT4_G128 || d.fmt == MOE_W_INT4_G128_ASYM ||
+                    d.fmt == MOE_W_INT8_G128;
     const int64_t a = i4 ? 4 : 16;
     const bool zp = d.fmt != MOE_W_INT4_G128_ASYM ||
                     (aligned(d.zero_point, 2) && d.zero_point_row_stride % 2 == 0 &&
@@ -188,11 +189,11 @@ bool mfma_layout_ok(const moe_weight_desc_t &d) {
 
 bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
     const int E = ex.gate.num_experts, H = ex.gate.k, F = ex.gate.n;
-    // the GEMM decodes int4-g128 (signed or asymmetric), int4-g32 and NVFP4;
-    // int8 (and compressed NVFP4 scales) run the GEMV
+    // the GEMM decodes int4-g128 (signed or asymmetric), int4-g32, int8-g128
+    // and NVFP4; compressed NVFP4 scales run the GEMV
     const int f = ex.gate.fmt;
     if (f != MOE_W_INT4_G128 && f != MOE_W_INT4_G128_ASYM && f != MOE_W_INT4_G32 &&
-        f != MOE_W_NVFP4_G16)
+        f != MOE_W_INT8_G128 && f != MOE_W_NVFP4_G16)
         return false;
     // 32-bit buffer offsets must reach every row of an expert matrix
     const bool fits = (int64_t)F * ex.gate.qweight_row_stride < INT32_MAX &&
@@ -213,11 +214,10 @@ FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F
     p.max_tiles = p.max_rows / p.tile_m;
     p.off_h = 0;
     p.off_y = align256((size_t)p.max_rows * F * 2);
-    // MFMA path, int4 (every form): x in the decoder's pair order, and per-row
-    // sums of each 128-input group of x and of h (unused by int4-g32)
-    const bool sums = p.mfma && (ex.gate.fmt == MOE_W_INT4_G128 ||
-                                 ex.gate.fmt == MOE_W_INT4_G128_ASYM ||
-                                 ex.gate.fmt == MOE_W_INT4_G32);
+    // MFMA path, int4 (every form) and int8: x in the decoder's pair order,
+    // and per-row sums of each 128-input group of x and of h (unused by
+    // int4-g32)
+    const bool sums = p.mfma && ex.gate.fmt != MOE_W_NVFP4_G16;
     p.off_xperm = p.off_y + align256((size_t)p.max_rows * H * 4);
     p.off_xsum = p.off_xperm + (sums ? align256((size_t)T * H * 2) : 0);
     p.off_hsum = p.off_xsum + (sums ? align256((size_t)T * (H / 128) * 4) : 0);

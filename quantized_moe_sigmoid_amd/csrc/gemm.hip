@@ -22,6 +22,9 @@
 //   exactly once per group in float32. Asymmetric int4 (uint4 codes, zero
 //   point z per group and column): B holds MAGIC + q and the group's term is
 //   s_g (P - (MAGIC + z) sum x).
+// int8-g128: as int4-g128 with BIAS + q = 1152 + q (fp16) / 128 + q (bf16),
+//   the bytes re-paired into the same (i, i + 4) order; twice the weight
+//   registers, so that instantiation runs one wave per SIMD.
 // int4-g32: one 32x32x16 MFMA takes inputs from two 32-input groups (its
 //   two lane halves), so the scale cannot be applied between MFMAs; B holds
 //   q s_g instead (exact in fp16, rounded once in bf16), as for NVFP4.
@@ -50,18 +53,42 @@ __host__ __device__ constexpr bool int4_g128(int fmt) {
     return fmt == MOE_W_INT4_G128 || fmt == MOE_W_INT4_G128_ASYM;
 }
 
-// Every int4 form: nibble pairs (i, i + 4) of a word, so x and h are
-// staged in that pair order.
-__host__ __device__ constexpr bool int4_pairs(int fmt) {
-    return int4_g128(fmt) || fmt == MOE_W_INT4_G32;
+// Group-rescaled forms: 128-input groups, exact BIAS + q operands, the
+// per-group correction -BIAS sum x (int4 as above; int8-g128 as 1152 + q in
+// fp16 and 128 + q in bf16, decode.h).
+__host__ __device__ constexpr bool g128_rescaled(int fmt) {
+    return int4_g128(fmt) || fmt == MOE_W_INT8_G128;
 }
+
+// Every int4 form and int8: the operand pairs hold inputs (i, i + 4) of an
+// 8-input group, so x and h are staged in that pair order.
+__host__ __device__ constexpr bool int4_pairs(int fmt) {
+    return g128_rescaled(fmt) || fmt == MOE_W_INT4_G32;
+}
+
+// 16-byte weight loads per matrix and step: 32 inputs of a lane are 16 bytes
+// of int4 or 32 of int8.
+constexpr int gemm_wloads(int fmt) { return fmt == MOE_W_INT8_G128 ? 8 : 4; }
 
 // The bias of the decoded 16-bit values: signed codes BIAS + q (decode.h),
 // asymmetric codes MAGIC + q, whose zero point is added per group and
 // column (see GemmCtx::step).
 template <int ACT, int FMT>
 __device__ __forceinline__ constexpr float g128_bias() {
-    return FMT == MOE_W_INT4_G128_ASYM ? Int4Bias<ACT>::kMagicValue : Int4Bias<ACT>::kBias;
+    return FMT == MOE_W_INT8_G128        ? Int8Bias<ACT>::kBias
+           : FMT == MOE_W_INT4_G128_ASYM ? Int4Bias<ACT>::kMagicValue
+                                         : Int4Bias<ACT>::kBias;
+}
+
+// int8: inputs 0..3 in word lo, 4..7 in word hi, bytes masked (a dropped
+// group decodes as q = 0) and re-paired as (0, 4) (1, 5) (2, 6) (3, 7).
+template <int ACT>
+__device__ __forceinline__ uint4 decode_int8_b(uint32_t lo, uint32_t hi, uint32_t bmask) {
+    const uint32_t l = (lo & bmask) ^ 0x80808080u, h = (hi & bmask) ^ 0x80808080u;
+    const uint32_t t01 = __builtin_amdgcn_perm(h, l, 0x05010400u);   // l0 h0 l1 h1
+    const uint32_t t23 = __builtin_amdgcn_perm(h, l, 0x07030602u);   // l2 h2 l3 h3
+    return make_uint4(int8_pair<ACT, 0>(t01), int8_pair<ACT, 1>(t01), int8_pair<ACT, 0>(t23),
+                      int8_pair<ACT, 1>(t23));
 }
 
 struct GemmMat {
@@ -162,8 +189,8 @@ __device__ __forceinline__ int xcd_remap(int b, int nreal) {
 // (inputs 64i + 32h .. +31 of the step) and the step's scales.
 template <int FMT>
 struct StepW {
-    uint4 w[4];
-    uint32_t s32;      // int4: the step's two bf16 group scales
+    uint4 w[gemm_wloads(FMT)];
+    uint32_t s32;      // g128 forms: the step's two bf16 group scales
     uint4 s128;        // NVFP4: the step's sixteen E4M3 block scales
     uint32_t z16;      // asymmetric int4: the step's two zero points (bytes)
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t q, __amdgpu_buffer_rsrc_t s,
@@ -171,11 +198,18 @@ struct StepW {
                                          int step, int half) {
         if (FMT == MOE_W_INT4_G128_ASYM)
             z16 = __builtin_amdgcn_raw_buffer_load_b16(z, zoff + step * 2, 0, 0);
+        if (FMT == MOE_W_INT8_G128) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                q, qoff + step * (kGemmKS / 2) + i * 32 + half * 16, 0, 0));
-        if (int4_g128(FMT))
+            for (int i = 0; i < 8; ++i)
+                w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    q, qoff + step * kGemmKS + (i >> 1) * 64 + half * 32 + (i & 1) * 16, 0, 0));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    q, qoff + step * (kGemmKS / 2) + i * 32 + half * 16, 0, 0));
+        }
+        if (g128_rescaled(FMT))
             s32 = __builtin_amdgcn_raw_buffer_load_b32(s, soff + step * 4, 0, 0);
         else
             s128 = __builtin_bit_cast(uint4,
@@ -223,7 +257,7 @@ struct Stager {
 #pragma unroll
         for (int g = 0; g < 8; ++g)
             v[g] = *(const u32x4_t *)(src_row + step * kGemmKS + (g * 4 + kc) * 8);
-        if (int4_g128(FMT) && threadIdx.x < kGemmTM) {
+        if (g128_rescaled(FMT) && threadIdx.x < kGemmTM) {
             rs0 = sum_row[2 * step];
             rs1 = sum_row[2 * step + 1];
         }
@@ -233,7 +267,7 @@ struct Stager {
 #pragma unroll
         for (int g = 0; g < 8; ++g)
             *(u32x4_t *)(buf + (g * kGemmTM + row) * 64 + ((threadIdx.x & 3) << 4)) = v[g];
-        if (int4_g128(FMT) && threadIdx.x < kGemmTM) {
+        if (g128_rescaled(FMT) && threadIdx.x < kGemmTM) {
             xs[threadIdx.x] = rs0;
             xs[kGemmTM + threadIdx.x] = rs1;
         }
@@ -252,17 +286,20 @@ struct GemmCtx {
                                          const StepW<FMT> &wa_s, const StepW<FMT> &wb_s) {
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {            // two 128-input groups per step
-            const uint4 wa0 = wa_s.w[2 * gi], wa1 = wa_s.w[2 * gi + 1];
-            const uint4 wb0 = wb_s.w[2 * gi], wb1 = wb_s.w[2 * gi + 1];
             uint32_t ma = 0, mbk = 0;
-            if (int4_g128(FMT)) {
+            if (g128_rescaled(FMT)) {
                 float sa_g = bf16_bits_to_f32(gi ? wa_s.s32 >> 16 : wa_s.s32 & 0xFFFF);
                 float sb_g = bf16_bits_to_f32(gi ? wb_s.s32 >> 16 : wb_s.s32 & 0xFFFF);
-                // a zero scale drops the group: its nibbles decode as q = 0
-                ma = sa_g == 0.0f ? 0u : 0x000F000Fu;
-                mbk = sb_g == 0.0f ? 0u : 0x000F000Fu;
-                sa_g = sa_g == 0.0f ? 1.0f : sa_g;
-                sb_g = sb_g == 0.0f ? 1.0f : sb_g;
+                // a zero scale drops the group: its codes decode as q = 0
+                constexpr uint32_t kKeep = FMT == MOE_W_INT8_G128 ? 0xFFFFFFFFu : 0x000F000Fu;
+                ma = sa_g == 0.0f ? 0u : kKeep;
+                mbk = sb_g == 0.0f ? 0u : kKeep;
+                // and runs with the scale 2^-24 instead: its codes are zeroed,
+                // but P - BIAS sum x cancels only up to float32 rounding
+                // (~1e-2 of the group's sum), which this scale makes
+                // negligible; a power of two keeps every rescale exact
+                sa_g = sa_g == 0.0f ? 0x1p-24f : sa_g;
+                sb_g = sb_g == 0.0f ? 0x1p-24f : sb_g;
                 const float ra = sprev_a * __builtin_amdgcn_rcpf(sa_g);
                 const float rb = sprev_b * __builtin_amdgcn_rcpf(sb_g);
                 // asymmetric: the group's correction is -(MAGIC + z) sum x, the
@@ -295,10 +332,14 @@ struct GemmCtx {
             }
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2) {
-                const uint4 wa = i2 ? wa1 : wa0, wb = i2 ? wb1 : wb0;
-                const uint32_t wav[4] = {wa.x, wa.y, wa.z, wa.w};
-                const uint32_t wbv[4] = {wb.x, wb.y, wb.z, wb.w};
                 const int i = 2 * gi + i2;
+                // the lane's 32 inputs of 64-input chunk i: one 16-byte word
+                // of int4 (8 inputs per dword) or two of int8 (4 per dword)
+                constexpr int kW = gemm_wloads(FMT) / 4;
+                const uint4 wa = wa_s.w[kW * i], wb = wb_s.w[kW * i];
+                const uint4 wa2 = wa_s.w[kW * i + kW - 1], wb2 = wb_s.w[kW * i + kW - 1];
+                const uint32_t wav[8] = {wa.x, wa.y, wa.z, wa.w, wa2.x, wa2.y, wa2.z, wa2.w};
+                const uint32_t wbv[8] = {wb.x, wb.y, wb.z, wb.w, wb2.x, wb2.y, wb2.z, wb2.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     float bsa = 0.0f, bsb = 0.0f;
@@ -312,8 +353,14 @@ struct GemmCtx {
                         bsa = bf16_bits_to_f32(half_of(wa_s.s128, 2 * i + half));
                         bsb = bf16_bits_to_f32(half_of(wb_s.s128, 2 * i + half));
                     }
-                    const uint4 ob = decode_b<ACT, FMT>(wav[j], bsa, ma);
-                    const uint4 obb = decode_b<ACT, FMT>(wbv[j], bsb, mbk);
+                    uint4 ob, obb;
+                    if constexpr (FMT == MOE_W_INT8_G128) {
+                        ob = decode_int8_b<ACT>(wav[2 * j], wav[2 * j + 1], ma);
+                        obb = decode_int8_b<ACT>(wbv[2 * j], wbv[2 * j + 1], mbk);
+                    } else {
+                        ob = decode_b<ACT, FMT>(wav[j], bsa, ma);
+                        obb = decode_b<ACT, FMT>(wbv[j], bsb, mbk);
+                    }
                     const int chunk = i * 8 + half * 4 + j;
 #pragma unroll
                     for (int mb = 0; mb < 2; ++mb) {
@@ -382,7 +429,7 @@ __global__ void __launch_bounds__(kGemmThreads)
         const uint64_t live = __ballot(sl >= 0);
         if (threadIdx.x == 0) m_sh = __popcll(live);
         if (sl < 0) { sl = sorted_slots[tile * kGemmTM]; prow = 0; }
-        if (int4_g128(FMT))
+        if (g128_rescaled(FMT))
             sum_row = rowsum_in +
                       (x_from_slots ? (size_t)(sl / topk) : (size_t)tile * kGemmTM + prow) * groups;
     }
@@ -471,7 +518,7 @@ __global__ void __launch_bounds__(kGemmThreads)
             if (GATEUP) {
                 const uint16_t hb = f32_to_act<ACT>(silu_mul(cx.da[mb][v] * ga, cx.db[mb][v] * gb));
                 if (m < m_valid && ok_a) hout[r * n_rows + hcol] = hb;
-                if (int4_g128(FMT))
+                if (g128_rescaled(FMT))
                     hs[m * kGemmBN + wave * 32 + cx.l32] = m < m_valid ? act_to_f32<ACT>(hb) : 0.0f;
             } else if (m < m_valid) {
                 if (ok_a) yout[r * n_rows + col_a] = cx.da[mb][v] * ga;
@@ -479,7 +526,7 @@ __global__ void __launch_bounds__(kGemmThreads)
             }
         }
     }
-    if (GATEUP && int4_g128(FMT)) {
+    if (GATEUP && g128_rescaled(FMT)) {
         // -BIAS * sum of the rounded h over this block's 128 columns: the
         // down projection's 128-input group nb of row m
         __syncthreads();
@@ -584,10 +631,12 @@ moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int ac
         return f == MOE_W_NVFP4_G16        ? MOE_GEMM_FWD(MOE_BF16, MOE_W_NVFP4_G16)
                : f == MOE_W_INT4_G128_ASYM ? MOE_GEMM_FWD(MOE_BF16, MOE_W_INT4_G128_ASYM)
                : f == MOE_W_INT4_G32       ? MOE_GEMM_FWD(MOE_BF16, MOE_W_INT4_G32)
+               : f == MOE_W_INT8_G128      ? MOE_GEMM_FWD(MOE_BF16, MOE_W_INT8_G128)
                                            : MOE_GEMM_FWD(MOE_BF16, MOE_W_INT4_G128);
     return f == MOE_W_NVFP4_G16        ? MOE_GEMM_FWD(MOE_F16, MOE_W_NVFP4_G16)
            : f == MOE_W_INT4_G128_ASYM ? MOE_GEMM_FWD(MOE_F16, MOE_W_INT4_G128_ASYM)
            : f == MOE_W_INT4_G32       ? MOE_GEMM_FWD(MOE_F16, MOE_W_INT4_G32)
+           : f == MOE_W_INT8_G128      ? MOE_GEMM_FWD(MOE_F16, MOE_W_INT8_G128)
                                        : MOE_GEMM_FWD(MOE_F16, MOE_W_INT4_G128);
 #undef MOE_GEMM_FWD
 }

@@ -383,9 +383,8 @@ def _bank_v(fmt, E, n, k, srow=None, zrow=None, zp=True, qrow=None):
 
 @pytest.mark.parametrize("fmt", [B.MOE_W_INT4_G32, B.MOE_W_INT4_G128_ASYM, B.MOE_W_INT8_G128])
 def test_variant_banks_plan_kernels(L, fmt):
-    """The variants are accepted; at prefill size the int4 forms are planned
-    on the grouped GEMM's tile like int4-g128, while int8 stays on the GEMV
-    tile (the GEMM does not decode it)."""
+    """The variants are accepted, planned on the GEMV tile at decode size and
+    on the grouped GEMM's tile at prefill size, like int4-g128."""
     f = B.FfnDesc(_bank_v(fmt, 352, 1536, 4096), _bank_v(fmt, 352, 1536, 4096),
                   _bank_v(fmt, 352, 4096, 1536))
     st, tm_small, _ = _plan(f, T=8)
@@ -394,7 +393,7 @@ def test_variant_banks_plan_kernels(L, fmt):
     assert st == B.MOE_OK
     st, tm_g128, _ = _plan(_ffn(), T=2048)
     assert tm_g128 != tm_small
-    assert tm_big == (tm_small if fmt == B.MOE_W_INT8_G128 else tm_g128)
+    assert tm_big == tm_g128
 
 
 def test_asym_bank_with_odd_zero_point_stride_plans_the_gemv(L):

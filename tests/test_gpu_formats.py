@@ -95,15 +95,14 @@ def test_forward_small(dev, fmt, act):
     assert ok, ratio
 
 
-@pytest.mark.parametrize("fmt", [B.MOE_W_INT4_G128_ASYM, B.MOE_W_INT4_G32])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("zero_groups", [False, True])
 def test_forward_small_grouped_gemm(dev, fmt, act, zero_groups):
-    """Asymmetric int4-g128 and int4-g32 on the grouped MFMA GEMM (T*K >=
-    4E): 4 experts, hidden 512, width 256, 40 tokens, top-2, several tiles
-    per expert; with zero_groups, some groups of every matrix get a zero
-    scale (the g128 GEMM drops such a group), which the oracle dequantizes
-    to zeros."""
+    """The variants on the grouped MFMA GEMM (T*K >= 4E): 4 experts, hidden
+    512, width 256, 40 tokens, top-2, several tiles per expert; with
+    zero_groups, some groups of every matrix get a zero scale (the g128
+    forms drop such a group), which the oracle dequantizes to zeros."""
     Ee, Hh, Ff, T, Kk = 4, 512, 256, 40, 2
     banks, host = [], []
     for which, (n, k) in (("gate", (Ff, Hh)), ("up", (Ff, Hh)), ("down", (Hh, Ff))):
@@ -128,9 +127,8 @@ def test_forward_small_grouped_gemm(dev, fmt, act, zero_groups):
 @pytest.mark.parametrize("T,act,toks", [(8, "f16", list(range(8))), (64, "f16", [0, 17, 40, 63]),
                                         (256, "bf16", [0, 101, 255]), (2048, "f16", [0, 1000, 2047])])
 def test_forward_layer_shape(dev, fmt, T, act, toks):
-    """352 experts, hidden 4096, width 1536: decode batches and prefill-sized
-    ones (the int4 forms run the grouped MFMA GEMM there, int8 the decode
-    kernels)."""
+    """352 experts, hidden 4096, width 1536: decode batches (decode GEMV) and
+    prefill-sized ones (grouped MFMA GEMM)."""
     ffn, host = _random_ffn(fmt, 600 + T, dev)
     x = synth.activations(T, H, act, 23)
     lg = synth.router_logits(T, E, 23)
