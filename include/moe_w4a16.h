@@ -95,8 +95,12 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  *            row r of expert e are [row_index[e][r], row_index[e][r+1])).
  *
  * The decode kernels (the GEMV) serve every format; the prefill GEMM serves
- * MOE_W_INT4_G128 and MOE_W_NVFP4_G16, and the other formats run the GEMV
- * at every batch size.
+ * every format but MOE_W_NVFP4_CSF, which runs the GEMV at every batch size.
+ * The GEMM needs 4-byte-aligned scale rows (int4-g128 forms, int8), 16-byte
+ * aligned ones (int4-g32, NVFP4) and 2-byte-aligned zero-point rows
+ * (asymmetric int4); a bank without them runs the GEMV at every size. At
+ * prefill sizes int4-g32 with bf16 activations rounds q * s to bf16 before
+ * the MFMA (relative 2^-9 per weight); every other path decodes exactly.
  */
 typedef enum {
     MOE_W_INT4_G128 = 1, MOE_W_NVFP4_G16 = 2, MOE_W_BF16 = 3,
