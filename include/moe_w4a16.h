@@ -94,11 +94,14 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  *   csf_row_index: I32 [E][n+1] from moe_csf_row_index (the exceptions of
  *            row r of expert e are [row_index[e][r], row_index[e][r+1])).
  *
- * The decode kernels (the GEMV) serve every format; the prefill GEMM serves
- * every format but MOE_W_NVFP4_CSF, which runs the GEMV at every batch size.
- * The GEMM needs 4-byte-aligned scale rows (int4-g128 forms, int8), 16-byte
- * aligned ones (int4-g32, NVFP4) and 2-byte-aligned zero-point rows
- * (asymmetric int4); a bank without them runs the GEMV at every size. At
+ * The decode kernels (the GEMV) serve every format, and so does the prefill
+ * GEMM (batches with T*K >= 4E); for MOE_W_NVFP4_CSF banks the forward pass
+ * first expands the routed experts' scales into its workspace (which
+ * moe_forward_plan sizes for all E experts of the three matrices). The GEMM
+ * needs 4-byte-aligned scale rows (int4-g128 forms, int8), 16-byte aligned
+ * ones (int4-g32, NVFP4), 2-byte-aligned zero-point rows (asymmetric int4)
+ * and an 8-byte-aligned CSF fixed tensor; a bank without them runs the GEMV
+ * at every size. At
  * prefill sizes int4-g32 with bf16 activations rounds q * s to bf16 before
  * the MFMA (relative 2^-9 per weight); every other path decodes exactly.
  */

@@ -36,6 +36,8 @@ moe_status_t launch_dense_swiglu(const moe_ffn_desc_t &sh, const void *x, int T,
                                  float *y, float *part, hipStream_t s);
 moe_status_t launch_round(const float *in, size_t n, int dtype, void *out, hipStream_t s);
 bool norm_route_fused(int T, int H, int E);
+moe_status_t launch_csf_expand_rows(const moe_weight_desc_t &d, const int32_t *expert_offsets,
+                                    uint8_t *out, hipStream_t s);
 moe_status_t launch_norm_router_logits(const float *res, const float *gain, float eps, int T,
                                        int H, const float *wT, const float *bias, int E,
                                        void *a_out, float *logits, hipStream_t s);
@@ -164,7 +166,7 @@ struct FwdPlan {
     int tile_m;
     int64_t max_rows, max_tiles;
     size_t off_h, off_y, off_xperm, off_xsum, off_hsum;
-    size_t off_sh_h, off_sh_y, off_sh_part, total;
+    size_t off_sh_h, off_sh_y, off_sh_part, off_csf, total;
 };
 
 // Kernel choice by batch shape: with few slots per expert the dequantizing
@@ -173,6 +175,10 @@ struct FwdPlan {
 // grouped GEMM, which reads each weight once per tile of 64 slots, takes
 // over. One code path per shape class.
 bool mfma_layout_ok(const moe_weight_desc_t &d) {
+    // compressed scales reach the GEMM expanded into the workspace (aligned
+    // there); the expansion reads 8 code bytes at a time
+    if (d.fmt == MOE_W_NVFP4_CSF)
+        return aligned(d.scale, 8) && d.scale_expert_stride % 8 == 0;
     // the GEMM loads a step's scales as one 4-byte (int4) or 16-byte (NVFP4)
     // word, and an asymmetric bank's two zero points as one 2-byte word
     // (int4-g32: the step's eight bf16 scales, 16 bytes)
@@ -189,11 +195,11 @@ bool mfma_layout_ok(const moe_weight_desc_t &d) {
 
 bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
     const int E = ex.gate.num_experts, H = ex.gate.k, F = ex.gate.n;
-    // the GEMM decodes int4-g128 (signed or asymmetric), int4-g32, int8-g128
-    // and NVFP4; compressed NVFP4 scales run the GEMV
+    // the GEMM decodes every format (compressed NVFP4 scales after their
+    // expansion into the workspace)
     const int f = ex.gate.fmt;
     if (f != MOE_W_INT4_G128 && f != MOE_W_INT4_G128_ASYM && f != MOE_W_INT4_G32 &&
-        f != MOE_W_INT8_G128 && f != MOE_W_NVFP4_G16)
+        f != MOE_W_INT8_G128 && f != MOE_W_NVFP4_G16 && f != MOE_W_NVFP4_CSF)
         return false;
     // 32-bit buffer offsets must reach every row of an expert matrix
     const bool fits = (int64_t)F * ex.gate.qweight_row_stride < INT32_MAX &&
@@ -204,6 +210,10 @@ bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
     return (int64_t)T * K >= 4 * (int64_t)E && H % gemm_group() == 0 &&
            F % gemm_group() == 0 && F % gemm_bn() == 0 && H % (2 * gemm_bn()) == 0 && fits &&
            mfma_layout_ok(ex.gate) && mfma_layout_ok(ex.up) && mfma_layout_ok(ex.down);
+}
+
+size_t csf_bytes(const moe_weight_desc_t &d) {
+    return align256((size_t)d.num_experts * d.n * (d.k / 16));
 }
 
 FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F, int Fs) {
@@ -217,7 +227,7 @@ FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F
     // MFMA path, int4 (every form) and int8: x in the decoder's pair order,
     // and per-row sums of each 128-input group of x and of h (unused by
     // int4-g32)
-    const bool sums = p.mfma && ex.gate.fmt != MOE_W_NVFP4_G16;
+    const bool sums = p.mfma && ex.gate.fmt != MOE_W_NVFP4_G16 && ex.gate.fmt != MOE_W_NVFP4_CSF;
     p.off_xperm = p.off_y + align256((size_t)p.max_rows * H * 4);
     p.off_xsum = p.off_xperm + (sums ? align256((size_t)T * H * 2) : 0);
     p.off_hsum = p.off_xsum + (sums ? align256((size_t)T * (H / 128) * 4) : 0);
@@ -226,7 +236,11 @@ FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F
     const size_t part = Fs ? dense_plan(T, H, Fs).part_floats : 0;
     p.off_sh_y = p.off_sh_h + (Fs ? align256((size_t)T * Fs * 2) : 0);
     p.off_sh_part = p.off_sh_y + (Fs ? align256((size_t)T * H * 4) : 0);
-    p.total = p.off_sh_part + align256(part * 4);
+    p.off_csf = p.off_sh_part + align256(part * 4);
+    // MFMA path, compressed NVFP4 scales: every routed expert's E4M3 block
+    // scales of gate, up and down, expanded ([E][n][k/16] each)
+    const bool csf = p.mfma && ex.gate.fmt == MOE_W_NVFP4_CSF;
+    p.total = p.off_csf + (csf ? csf_bytes(ex.gate) + csf_bytes(ex.up) + csf_bytes(ex.down) : 0);
     return p;
 }
 
@@ -373,7 +387,26 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     if ((st = mark(0)) != MOE_OK) return st;
     const std::function<moe_status_t(int)> mk =
         events ? std::function<moe_status_t(int)>(mark) : std::function<moe_status_t(int)>();
-    st = p.mfma ? launch_gemm_forward(*experts, x, act_dtype, T, K, *perm, (int)p.max_tiles, h, y,
+    moe_ffn_desc_t ex = *experts;
+    if (p.mfma && ex.gate.fmt == MOE_W_NVFP4_CSF) {
+        // prefill sizes: the routed experts' compressed scales expanded into
+        // the workspace, then the NVFP4 GEMM (the in-place GEMV rereads each
+        // expert once per 4-slot tile)
+        uint8_t *sc = (uint8_t *)(w + p.off_csf);
+        moe_weight_desc_t *mats[3] = {&ex.gate, &ex.up, &ex.down};
+        for (moe_weight_desc_t *d : mats) {
+            st = launch_csf_expand_rows(*d, perm->expert_offsets, sc, s);
+            if (st != MOE_OK) return st;
+            d->fmt = MOE_W_NVFP4_G16;
+            d->scale = sc;
+            d->scale_row_stride = d->k / 16;
+            d->scale_expert_stride = (int64_t)d->n * (d->k / 16);
+            d->csf_exceptions = nullptr;
+            d->csf_row_index = nullptr;
+            sc += csf_bytes(*d);
+        }
+    }
+    st = p.mfma ? launch_gemm_forward(ex, x, act_dtype, T, K, *perm, (int)p.max_tiles, h, y,
                                       w + p.off_xperm, (float *)(w + p.off_xsum),
                                       (float *)(w + p.off_hsum), s, mk)
                 : launch_gemv_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s, mk);

@@ -139,6 +139,51 @@ moe_status_t launch_csf_row_index(const uint32_t *exceptions, int64_t n, const i
     return MOE_OK;
 }
 
+// Expansion from the per-row exception ranges (the row index the in-place
+// kernels read), for the forward pass at prefill sizes: one thread per
+// (row, 16 scale bytes), so no barrier is needed; the thread applies the
+// row's exceptions whose column falls in its 16 bytes. Experts with no
+// routed slot exit at once.
+__global__ void __launch_bounds__(256) csf_expand_rows_kernel(
+    const uint8_t *__restrict__ fixed, int64_t fixed_expert_stride,
+    const uint32_t *__restrict__ xc, const int32_t *__restrict__ ri,
+    const int32_t *__restrict__ expert_offsets, int R, int C, uint8_t *__restrict__ out) {
+    const int e = blockIdx.y;
+    if (expert_offsets[e + 1] == expert_offsets[e]) return;
+    const int chunks = C / 16;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)R * chunks) return;
+    const int r = (int)(idx / chunks), j = (int)(idx % chunks);
+    const uint8_t *slab =
+        fixed + e * fixed_expert_stride + (size_t)(r >> 4) * 16 * (1 + C / 2);
+    const uint2 codes = *(const uint2 *)(slab + 16 + (r & 15) * (C / 2) + 8 * j);
+    uint4 o = csf_expand16(codes, slab[r & 15]);
+    const int32_t *rix = ri + (size_t)e * (R + 1);
+    const uint32_t p0 = (uint32_t)r * (uint32_t)C + 16u * (uint32_t)j;
+    for (int x = rix[r]; x < rix[r + 1]; ++x) {
+        const uint32_t v = xc[x], d = (v & 0xFFFFFFu) - p0;
+        if (d < 16) {
+            const uint32_t sh = 8 * (d & 3), m = ~(0xFFu << sh), b = (v >> 24) << sh;
+            if (d < 4) o.x = (o.x & m) | b;
+            else if (d < 8) o.y = (o.y & m) | b;
+            else if (d < 12) o.z = (o.z & m) | b;
+            else o.w = (o.w & m) | b;
+        }
+    }
+    *(uint4 *)(out + ((size_t)e * R + r) * C + 16 * j) = o;
+}
+
+moe_status_t launch_csf_expand_rows(const moe_weight_desc_t &d, const int32_t *expert_offsets,
+                                    uint8_t *out, hipStream_t s) {
+    const int R = d.n, C = d.k / 16;
+    const dim3 grid((unsigned)(((int64_t)R * (C / 16) + 255) / 256), d.num_experts);
+    hipLaunchKernelGGL(csf_expand_rows_kernel, grid, dim3(256), 0, s, (const uint8_t *)d.scale,
+                       d.scale_expert_stride, d.csf_exceptions, d.csf_row_index, expert_offsets, R,
+                       C, out);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
 moe_status_t launch_csf_expand(const uint8_t *fixed, const uint32_t *exceptions, int64_t n,
                                const int64_t *starts, int E, int R, int C,
                                const int32_t *expert_offsets, int max_routed, uint8_t *out,

@@ -352,13 +352,25 @@ def _bank_csf(E, n, k, fstride=None, ri=True, gs=True):
                         n * qr, qr, fs, 0, None, 0, 0, FAKE, FAKE if ri else None)
 
 
-def test_nvfp4_csf_banks_plan_the_decode_kernels_and_errors(L):
+def test_nvfp4_csf_banks_plan_kernels_and_errors(L):
+    """Decode sizes read the compressed scales in place (GEMV tile); prefill
+    sizes expand them into the workspace for the grouped GEMM (its tile,
+    and room for every expert's expanded scales); a fixed tensor whose
+    experts are not 8 bytes apart cannot be expanded with 8-byte reads and
+    keeps the GEMV."""
     f = B.FfnDesc(_bank_csf(352, 1536, 4096), _bank_csf(352, 1536, 4096),
                   _bank_csf(352, 4096, 1536))
     st, tm_small, _ = _plan(f, T=8, act=B.MOE_BF16)
     assert st == B.MOE_OK
-    st, tm_big, _ = _plan(f, T=2048, act=B.MOE_BF16)
-    assert st == B.MOE_OK and tm_big == tm_small          # the GEMV at every size
+    st, tm_big, ws_big = _plan(f, T=2048, act=B.MOE_BF16)
+    st_g, tm_g128, _ = _plan(_ffn(), T=2048)
+    assert st == B.MOE_OK and tm_big == tm_g128 != tm_small
+    assert ws_big >= 352 * (2 * 1536 * 256 + 4096 * 96)
+    odd = 1536 * (1 + 4096 // 32) + 4
+    f = B.FfnDesc(_bank_csf(352, 1536, 4096, fstride=odd), _bank_csf(352, 1536, 4096),
+                  _bank_csf(352, 4096, 1536))
+    st, tm_odd, _ = _plan(f, T=2048, act=B.MOE_BF16)
+    assert st == B.MOE_OK and tm_odd == tm_small
     for g in (_bank_csf(352, 1536, 4096, ri=False),         # no row index
               _bank_csf(352, 1536, 4096, gs=False),         # no global scale
               _bank_csf(352, 1536, 4096, fstride=1536 * 100),   # fixed tensor too small

@@ -174,11 +174,14 @@ def test_nvfp4_csf_dequant_bitwise(dev):
 
 @pytest.mark.parametrize("Ee,Hh,Ff,T,Kk,rate,act", [(6, 512, 256, 5, 3, 0.3, "bf16"),
                                                     (6, 512, 256, 7, 2, 0.0, "f16"),
-                                                    (352, 4096, 1536, 64, 8, 0.002, "bf16")])
+                                                    (352, 4096, 1536, 64, 8, 0.002, "bf16"),
+                                                    (6, 512, 256, 40, 3, 0.3, "f16"),
+                                                    (352, 4096, 1536, 256, 8, 0.002, "bf16")])
 def test_nvfp4_csf_forward_equals_raw_scales(dev, Ee, Hh, Ff, T, Kk, rate, act):
-    """The layer on compressed scales read in place is bitwise the layer on
-    the same scale bytes stored plainly (whose parity with the oracle the
-    NVFP4 tests establish)."""
+    """The layer on compressed scales, read in place by the decode kernels
+    (small batches) or expanded into the workspace for the grouped GEMM
+    (T*K >= 4E), is bitwise the layer on the same scale bytes stored plainly
+    (whose parity with the oracle the NVFP4 tests establish)."""
     raw, csf = [], []
     for i, (n, k) in enumerate(((Ff, Hh), (Ff, Hh), (Hh, Ff))):
         q, _, gs = synth.packed_nvfp4_random(Ee, n, k, 40 + i, dev)
