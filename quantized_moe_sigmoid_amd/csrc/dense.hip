@@ -172,6 +172,10 @@ __global__ void __launch_bounds__(256) swiglu_reduce_kernel(const float *__restr
     if (i >= (size_t)T * F) return;
     const size_t t = i / F, c = i % F;
     float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+    // unrolled so the loads of several slices are in flight together (the
+    // sums keep ascending z): one slice at a time, the few work groups of a
+    // small batch waited out a cache round trip per slice
+#pragma unroll 8
     for (int z = 0; z < S; ++z) {
         const float *p = part + ((size_t)z * T + t) * 2 * F + c;
         const float4 a = *(const float4 *)p, b = *(const float4 *)(p + F);
@@ -191,6 +195,7 @@ __global__ void __launch_bounds__(256) sum_reduce_kernel(const float *__restrict
     const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= n) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int z = 0; z < S; ++z) {
         const float4 a = *(const float4 *)(part + (size_t)z * n + i);
         acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
