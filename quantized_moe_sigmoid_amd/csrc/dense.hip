@@ -204,13 +204,15 @@ __global__ void __launch_bounds__(256) sum_reduce_kernel(const float *__restrict
 }
 
 // Input-range split for a grid of `units` work units over `steps` steps:
-// double S while the grid is under one work unit per CU, S divides the
-// steps, every slice keeps at least 2 steps and S stays at most `max_split`
-// (which bounds the partial-sum traffic).
+// the largest S that divides the steps, leaves every slice at least 2
+// steps, keeps the grid within one work unit per CU and stays at most
+// `max_split` (which bounds the partial-sum traffic). Any divisor, not only
+// powers of two: the down projection's 24 steps at H = 4096, F = 1536 split
+// 12 ways (192 work groups) where doubling stopped at 4 (64).
 int dense_split(int64_t units, int steps, int max_split) {
     int S = 1;
-    while (units * S < 256 && 2 * S <= max_split && steps % (2 * S) == 0 && steps / (2 * S) >= 2)
-        S *= 2;
+    for (int c = 2; c <= max_split; ++c)
+        if (steps % c == 0 && steps / c >= 2 && units * c <= 256) S = c;
     return S;
 }
 
@@ -218,7 +220,7 @@ DenseSplit dense_plan(int T, int H, int F) {
     const int64_t tiles = (T + kDnTM - 1) / kDnTM;
     DenseSplit d;
     d.s_gateup = dense_split(tiles * (F / kDnBN), H / kDnKS, 16);
-    d.s_down = dense_split(tiles * (H / (2 * kDnBN)), F / kDnKS, 8);
+    d.s_down = dense_split(tiles * (H / (2 * kDnBN)), F / kDnKS, 12);
     d.part_floats = 0;
     if (d.s_gateup > 1) d.part_floats = (size_t)d.s_gateup * T * 2 * F;
     if (d.s_down > 1 && (size_t)d.s_down * T * H > d.part_floats)
