@@ -499,6 +499,7 @@ def main():
     if not args.no_sweep:
         for wl, T in (("decode", 1), ("decode", 8), ("decode", 64), ("prefill", 2048),
                       ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("nvfp4-csf-expand", 64),
+                      ("nvfp4-csf-expand", 256),
                       ("int4-g32", 64), ("int4-g32", 2048),
                       ("int4-asym", 64), ("int4-asym", 2048), ("int8", 64), ("int8", 2048),
                       ("stack", 32),
