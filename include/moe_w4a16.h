@@ -66,17 +66,17 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  *   "NeuroSenko/Step-5-Preview-Int4-g128", "What stays in BF16").
  *   qweight: bf16 [E][n][k]; scale and global_scale NULL.
  *
- * MOE_W_INT4_G32 -- the same page, "Recipe" ("g32 with the same clip
- *   search"): as MOE_W_INT4_G128 with one bf16 scale per 32 inputs.
+ * MOE_W_INT4_G32 -- the same page, "Recipe" (its int4-g32 row, same clip
+ *   search): as MOE_W_INT4_G128 with one bf16 scale per 32 inputs.
  *   scale:   bf16 [E][n][k/32].   weight = q * scale.
  *
- * MOE_W_INT4_G128_ASYM -- the same page, "Recipe" ("int4 g128,
- *   asymmetric"): unsigned nibbles q in [0, 15] (nibble j of word w =
+ * MOE_W_INT4_G128_ASYM -- the same page, "Recipe" (its asymmetric
+ *   int4-g128 row): unsigned nibbles q in [0, 15] (nibble j of word w =
  *   input 8w+j), one bf16 scale and one zero point per 128 inputs.
  *   scale:   bf16 [E][n][k/128];  zero_point: uint8 [E][n][k/128], values
  *   0..15.   weight = (q - zero_point) * scale.
  *
- * MOE_W_INT8_G128 -- the same page, "Recipe" (the "int8 experts" it
+ * MOE_W_INT8_G128 -- the same page, "Recipe" (the 8-bit experts it
  *   compares against): symmetric int8 with one bf16 scale per 128 inputs.
  *   qweight: int8 [E][n][k], two's complement, input j at byte j.
  *   scale:   bf16 [E][n][k/128].   weight = q * scale.
@@ -89,8 +89,8 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  *   scale: the CSF `fixed` tensor U8 [E][n/16][16*(1 + C/2)], C = k/16,
  *            scale_expert_stride its expert stride in bytes (>= n*(1 + C/2)),
  *            scale_row_stride unused (0); n % 16 == 0;
- *   csf_exceptions: the exceptions U32 (row*C + col) | byte << 24, grouped
- *            by expert and sorted by position within it (NULL if none);
+ *   csf_exceptions: the exceptions U32 (row*C + col) | byte << 24, each
+ *            expert's contiguous and in position order (NULL if none);
  *   csf_row_index: I32 [E][n+1] from moe_csf_row_index (the exceptions of
  *            row r of expert e are [row_index[e][r], row_index[e][r+1])).
  *
@@ -102,8 +102,11 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  * ones (int4-g32, NVFP4), 2-byte-aligned zero-point rows (asymmetric int4)
  * and an 8-byte-aligned CSF fixed tensor; a bank without them runs the GEMV
  * at every size. At
- * prefill sizes int4-g32 with bf16 activations rounds q * s to bf16 before
- * the MFMA (relative 2^-9 per weight); every other path decodes exactly.
+ * prefill sizes int4-g32 puts the group scale into the MFMA operand: with
+ * bf16 activations q * s is rounded to bf16 (relative 2^-9 per weight);
+ * with fp16 activations the scale is converted to fp16 and q * s formed in
+ * fp16, which is exact while the scale lies in fp16's normal range
+ * (2^-14 .. 65504) and rounds otherwise. Every other path decodes exactly.
  */
 typedef enum {
     MOE_W_INT4_G128 = 1, MOE_W_NVFP4_G16 = 2, MOE_W_BF16 = 3,
@@ -160,7 +163,7 @@ typedef struct {
 /* Human-readable name of a status code (host, static storage). */
 const char *moe_status_string(int status);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 4 (moe_abi_version returns it). */
 int moe_abi_version(void);
 
 /*
@@ -246,11 +249,12 @@ moe_status_t moe_norm_route(const float *residual, const float *norm_w, float ep
  * moe_permute -- expert histogram and stable expert-sorted permutation of
  * the T*K slots (see moe_perm_t). The pages do not describe this step; it
  * exists so that each touched expert's weights stream from HBM once
- * (routed experts are 96.7 % of the weight bytes: page
- * "NeuroSenko/Step-5-Preview-Int4-g128", "Recipe").
- * topk_ids [T][K] int32, normally in [0, E) (a slot whose id lies outside
- * is routed nowhere and its slot_to_row entry is left as it was); ids may
- * repeat within a token. tile_m in [1, 256].
+ * (on page "NeuroSenko/Step-5-Preview-Int4-g128", "Recipe", the routed
+ * experts hold nearly all of the model's bytes).
+ * topk_ids [T][K] int32, normally in [0, E); a slot whose id lies outside
+ * is routed nowhere: it gets no row and slot_to_row[s] = -1, and the
+ * forward pass adds nothing for it. Ids may repeat within a token.
+ * tile_m in [1, 256].
  * Deterministic: no atomics decide any order (up to 1024 slots, one work
  * group combines per-expert slot masks with LDS ORs, whose result does not
  * depend on arrival order).
@@ -261,7 +265,13 @@ moe_status_t moe_permute(const int32_t *topk_ids, int T, int K, int E,
 /* The tile_m the forward pass needs for T tokens (host output), and the
  * workspace bytes it needs (host output), with or without the shared expert
  * (same argument rules as moe_w4a16_forward). Pass that tile_m to
- * moe_permute. */
+ * moe_permute. The workspace holds h [max_rows][F] in the activation dtype
+ * and y [max_rows][H] float32 (max_rows from moe_permute_sizes), plus, on
+ * the prefill GEMM path, per-group sums of x and h; with a shared expert its
+ * h, y and split partial sums; and for a MOE_W_NVFP4_CSF bank on the GEMM
+ * path the expanded E4M3 scales of all E experts of gate, up and down (E *
+ * (2 F H + H F) / 16 bytes, 415 MB at E = 352, H = 4096, F = 1536: the GEMM
+ * path needs T*K >= 4E, so every expert may be routed). */
 moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts,
                               const moe_ffn_desc_t *shared, int T, int K,
                               int act_dtype, int *tile_m, size_t *ws_bytes);
@@ -269,8 +279,8 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts,
 /*
  * moe_w4a16_forward -- the routed experts, the optional shared expert and
  * the weighted combine (page "Step 5 Preview: ...", "The shape: narrow and
- * deep": 8 routed experts per token plus one shared expert, each a SwiGLU of
- * width 1536; the residual stream is fp32 per the same page's paragraph on
+ * deep": each token reaches its 8 chosen routed experts and the one shared
+ * expert, all SwiGLUs of width 1536; the residual stream is fp32 per the same page's paragraph on
  * fp32_residual_connection):
  *
  *   for each slot s = (t, k) routed to expert e:
@@ -343,10 +353,16 @@ moe_status_t moe_round_activations(const float *in, int64_t n, int out_dtype, vo
  * residual stream (page "Step 5 Preview: ...", the paragraph on training the
  * deep stack: Step5RMSNorm scales x / rms(x) by the zero-centred gain
  * (1 + w), computed in fp32; the gain is stored in FP32):
- *   out[t][h] = x[t][h] / sqrt(mean_h x[t][h]^2 + eps) * (1 + weight[h])
- * evaluated in float64 and rounded once to out_dtype (MOE_F16 or MOE_BF16),
- * to nearest, ties to even. x [T][H] float and weight [H] float (NULL = all
- * zero, a gain of 1) 16-byte aligned; out [T][H] 16-byte aligned.
+ *   out[t][h] = (x[t][h] / sqrt(mean_h x[t][h]^2 + eps)) * (1 + weight[h])
+ * with every operation in float32, rounded to nearest even (IEEE division
+ * and square root, no fused multiply-adds), then rounded to out_dtype
+ * (MOE_F16 or MOE_BF16), ties to even. The pages do not fix the order of
+ * the sum of squares; it is this one: partial p (p = 0..255) adds the
+ * squares of columns 4p..4p+3, 1024+4p..1024+4p+3, ... in ascending column
+ * order; each run of 64 consecutive partials is folded in halves (partial i
+ * gets partial i + m added, m = 32, 16, .., 1); the four run sums are added
+ * left to right. x [T][H] float and weight [H] float (NULL = all zero, a
+ * gain of 1) 16-byte aligned; out [T][H] 16-byte aligned.
  * Limits: H % 4 == 0, 4 <= H <= 16384, 0 <= eps <= 1. T == 0 is a no-op.
  */
 moe_status_t moe_rmsnorm(const float *x, const float *weight, float eps, int T, int H,
@@ -354,11 +370,17 @@ moe_status_t moe_rmsnorm(const float *x, const float *weight, float eps, int T, 
 
 /*
  * moe_dequant -- the exact dequantized matrix of one expert, as float32
- * [n][k] (int4: q * scale; NVFP4: (e2m1 * e4m3) * global_scale with one
- * float32 rounding). It runs the forward kernels' own nibble decoders
- * (int4: the biased 16-bit pair decode; NVFP4: the hardware E2M1 pair
- * conversion), so a bit-exact export checks the format interpretation the
- * forward pass relies on.
+ * [n][k]. int4 forms and int8 (page "NeuroSenko/Step-5-Preview-Int4-g128",
+ * "Recipe" and "Tensor layout"): q * scale, or (q - zero_point) * scale for
+ * the asymmetric form, exact in float32. NVFP4 (page
+ * "Step-5-Preview-NVFP4-Local", "Format" and "Modifications" item 2): the
+ * E2M1 value times its E4M3 block scale (exact), times the expert's float32
+ * global scale with one float32 rounding; MOE_W_NVFP4_CSF banks decode their
+ * compressed scales first. The export has decoders of its own (the biased
+ * 16-bit int4 pair decode, the hardware E2M1 pair conversion); it checks the
+ * format interpretation, not the forward kernels' decoders, which are
+ * checked through the layer's outputs. w: a quantized bank (not
+ * MOE_W_BF16); expert in [0, E); out [n][k] float, 16-byte aligned.
  */
 moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out,
                          void *stream);
@@ -366,21 +388,23 @@ moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out,
 /*
  * moe_csf_expand -- the E4M3 block-scale bytes of an NVFP4 bank from their
  * compressed scale format (page "Step-5-Preview-NVFP4-Local", "Format" and
- * "Modifications" item 1): a scale byte is its row's base plus its 4-bit
- * code, unless an exception at that position replaces it with the stored
- * byte. The expanded bytes are the `scale` array of an NVFP4
+ * "Modifications" item 1): each byte is rebuilt as its row's base plus the
+ * 4-bit code at its position, except at the positions its expert's
+ * exception list names, which take the byte stored there. The expanded bytes are the `scale` array of an NVFP4
  * moe_weight_desc_t with scale_row_stride C and scale_expert_stride R*C
  * (the page's loader expands one layer's scales into scratch before the
  * layer runs).
- *   fixed          U8  [E][R/16][16*(1 + C/2)], 8-byte aligned: per slab of
- *                  16 rows, the 16 row bases, then each row's C codes, two
- *                  per byte, low nibble first;
+ *   fixed          U8  [E][R/16][16*(1 + C/2)], 8-byte aligned: rows in
+ *                  slabs of 16, each slab its 16 bases followed by the C
+ *                  4-bit codes of each of its rows, packed in pairs with
+ *                  the even column in the low bits;
  *   exceptions     U32 [n_exceptions], 4-byte aligned (NULL if none):
- *                  (row*C + col) | byte << 24, grouped by expert, row and
+ *                  (row*C + col) | byte << 24, contiguous per expert, row and
  *                  col counted within the expert, positions distinct within
  *                  an expert; entries past R*C are ignored;
- *   starts         I64 [E+1], 8-byte aligned: expert e owns exceptions
- *                  [starts[e], starts[e+1]) (clamped to [0, n_exceptions]);
+ *   starts         I64 [E+1], 8-byte aligned: the exceptions of expert e are
+ *                  entries starts[e] .. starts[e+1]-1 (clamped to
+ *                  [0, n_exceptions]);
  *   expert_offsets I32 [E+1] or NULL: the moe_permute expert offsets; experts
  *                  with no routed slot are skipped (their bytes in `out` are
  *                  left unchanged);

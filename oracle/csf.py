@@ -3,20 +3,26 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Page "Step-5-Preview-NVFP4-Local", sections "Modifications" (item 1) and
-"Format": a routed-expert scale tensor [E, R, C] of E4M3 bytes (one byte per
-16 weights; gate and up R = 1536, C = 256; down R = 4096, C = 96) is stored
-as three tensors:
+"Format". The E4M3 block scales of a routed-expert matrix form a tensor
+[E, R, C] (one byte per 16 weights; R = 1536, C = 256 for gate and up,
+R = 4096, C = 96 for down). The page keeps them in three tensors, restated
+here as this module uses them:
 
-* fixed      U8  [E, R/16, 16 * (1 + C/2)]: per slab of 16 rows, the 16 row
-  bases, then each row's 4-bit codes, two per byte, low nibble first;
-* exceptions U32 [n]: (row * C + col) | byte << 24, grouped by expert,
-  row-major within an expert;
-* starts     I64 [E + 1]: expert e owns exceptions[starts[e]:starts[e+1]].
+* `fixed`, bytes [E, R/16, 16 * (1 + C/2)]. Rows come in slabs of 16; a
+  slab holds its 16 per-row bases first, then, row after row, that row's C
+  4-bit codes packed in pairs (the even column in bits 0..3).
+* `exceptions`, 32-bit words: the low 24 bits give a position row * C + col
+  inside one expert, the top 8 bits the byte stored there; the words of an
+  expert are contiguous and in position order.
+* `starts`, int64 [E + 1]: the words of expert e are those from starts[e] up
+  to, not including, starts[e + 1].
 
-A scale byte is its row's base plus its 4-bit code, unless an exception at
-that position replaces it with the stored byte. A row's base is the lowest
-value (0 to 240) whose 16-value window [base, base + 15] covers the most of
-the row's bytes.
+Decoding: the byte at a position listed among its expert's exceptions is
+the byte stored with it; every other byte equals its row's base plus its
+code (at most base + 15). Encoding chooses, per row, the smallest base in
+0 .. 240 for which the 16 consecutive values from the base on contain as
+many of the row's bytes as any other choice; bytes outside that range
+become exceptions.
 
 Reading where the page is silent: a position held by an exception keeps
 code 0 in the fixed tensor (the decoder never uses it). Rows and columns of

@@ -4,16 +4,18 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 int4-g128 (page "NeuroSenko/Step-5-Preview-Int4-g128", sections "Recipe" and
 "Tensor layout"): symmetric int4, one scale per 128 input channels, the scale
-stored in bf16 and chosen per group among 17 clip ratios in [0.60, 1.00] to
-minimise the rounding MSE, the search done in the scale's own precision so
+stored in bf16; each group tries 17 clipping ratios between 0.60 and 1.00
+and keeps the one with the smallest squared rounding error, the search done in the scale's own precision so
 that quantizing and dequantizing agree exactly. Routed experts only; the
 fused source tensors are [experts, out, in].
 
 NVFP4 (page "Step-5-Preview-NVFP4-Local", "Modifications" item 2 and
-"Format"): weight U8 [E, R, K/2] holding E2M1 pairs, one F8_E4M3 block scale
-per 16 weights [E, R, K/16], one F32 weight_scale_2 per expert [E]; a weight
-dequantizes as E2M1 value x E4M3 block scale x weight_scale_2. Layers that
-were BF16 at the source were "quantized here the same way".
+"Format"): bytes [E, R, K/2], each holding two E2M1 codes; an E4M3 block
+scale for every 16 weights [E, R, K/16]; one float32 global scale
+(weight_scale_2) per expert [E]. A weight's value is the product of its E2M1
+value, its block scale and its expert's global scale. The page's last three
+layers were BF16 at the source and were brought to NVFP4 by the page's
+author with the same recipe as the others.
 
 Readings where the pages are silent (each also listed in the design notes):
 * int4 scale = clip_ratio * max|w| / 7 (divisor 7), q = clamp(rne(w/s), -8, 7).
@@ -25,15 +27,15 @@ Readings where the pages are silent (each also listed in the design notes):
   the first minimum in ratio order wins (ties go to the larger ratio).
 * nibble j of int32 word w along K holds input 8w+j (low nibble first, as the
   NVFP4 page's scale codes are stored), as a two's-complement 4-bit integer.
-* int4 g32 (the page's "g32 with the same clip search"): the same quantizer
+* int4 g32 (the error table's int4-g32 row, searched like g128): the same quantizer
   with one scale per 32 inputs.
-* asymmetric int4 (the page's "int4 g128, asymmetric"): min-max range
+* asymmetric int4 (the error table's asymmetric int4-g128 row): min-max range
   widened to contain 0, scale bf16((hi - lo) / 15), zero point
   clamp(rne(-lo / s), 0, 15) stored as one byte per group, unsigned nibbles
   q in [0, 15], w = (q - z) * s; no clip search. This reading gives 10.04 %
   on Gaussian weights and inputs against the page's 10.05 % (a clip search
   would give 9.5 %).
-* int8 (the page's "int8 experts", no format given): the int4-g128 recipe
+* int8 (the page compares against 8-bit experts but gives no format): the int4-g128 recipe
   on the 8-bit grid: candidate scale bf16(ratio * max|w| / 127) over the
   same 17 ratios, q = clamp(rne(w / s), -128, 127), one byte per weight
   [n, k] (two's complement), bf16 scales [n, k/128]. On Gaussian weights
@@ -47,8 +49,8 @@ Readings where the pages are silent (each also listed in the design notes):
 """
 import numpy as np
 
-from .formats import (E2M1, E4M3, bf16_from_bits, round_to_format, to_bf16,
-                      to_fp32, e2m1_decode, e2m1_encode, e4m3_decode,
+from .formats import (E2M1, E2M1_TABLE, E4M3, E4M3_TABLE, bf16_from_bits, round_to_format,
+                      to_bf16, to_fp32, e2m1_decode, e2m1_encode, e4m3_decode,
                       e4m3_encode_nonneg)
 
 INT4_GROUP = 128
@@ -114,28 +116,31 @@ def pack_int4(q):
 
 
 def unpack_int4(words):
-    """int32 words [n, k/8] -> q [n, k] int8."""
-    w = np.asarray(words).view(np.uint32).astype(np.int64)
+    """int32 words [n, k/8] -> q [n, k] int8: nibble j of a word, read as a
+    4-bit two's-complement number (8..15 stand for -8..-1)."""
+    w = np.asarray(words).view(np.uint32)
     n, kw = w.shape
-    nib = (w[..., None] >> (4 * np.arange(8))) & 0xF
-    q = nib - 16 * (nib >= 8)
-    return q.reshape(n, kw * 8).astype(np.int8)
+    nib = ((w[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF).astype(np.int8)
+    q = nib - np.int8(16) * (nib >= 8)
+    return q.reshape(n, kw * 8)
+
+
+def _group_scale(q, s, group):
+    """q [n, k] times the scale of its group, s [n, k/group] (float64)."""
+    n, k = q.shape
+    return (q.reshape(n, k // group, group) * s[..., None]).reshape(n, k)
 
 
 def dequant_int4(words, scales_bf16_bits, group=INT4_GROUP):
     """Exact dequantized values q * s (float64) from packed words [n, k/8]
     and bf16 scale bit patterns [n, k/group] (uint16)."""
-    q = unpack_int4(words).astype(np.float64)
-    s = bf16_from_bits(scales_bf16_bits)
-    return q * np.repeat(s, group, axis=1)
+    return _group_scale(unpack_int4(words), bf16_from_bits(scales_bf16_bits), group)
 
 
 def dequant_int8(q, scales_bf16_bits, group=INT4_GROUP):
     """Exact q * s (float64) from int8 weights [n, k] and bf16 scale bit
     patterns [n, k/group]."""
-    q = np.asarray(q, dtype=np.int8).astype(np.float64)
-    s = bf16_from_bits(scales_bf16_bits)
-    return q * np.repeat(s, group, axis=1)
+    return _group_scale(np.asarray(q, dtype=np.int8), bf16_from_bits(scales_bf16_bits), group)
 
 
 def rel_error(W, Wq, X):
@@ -147,7 +152,7 @@ def rel_error(W, Wq, X):
 # ------------------------------------------------------- int4 asymmetric ---
 def quantize_int4_asym(W, group=INT4_GROUP):
     """Asymmetric int4 with one bf16 scale and one zero point per group (the
-    int4 page's error table, "int4 g128, asymmetric"). Min-max range that
+    int4 page's error table, its asymmetric g128 row). Min-max range that
     always contains 0: lo = min(min w, 0), hi = max(max w, 0);
     s = bf16((hi - lo) / 15); z = clamp(rne(-lo / s), 0, 15);
     q = clamp(rne(w / s) + z, 0, 15); w ~ (q - z) * s. An all-zero group
@@ -183,9 +188,9 @@ def dequant_int4_asym(words, scales_bf16_bits, zeros, group=INT4_GROUP):
     """Exact (q - z) * s (float64) from packed unsigned nibbles [n, k/8], bf16
     scale bit patterns [n, k/group] and zero points uint8 [n, k/group]."""
     q = unpack_uint4(words).astype(np.float64)
-    z = np.repeat(np.asarray(zeros, dtype=np.float64), group, axis=1)
-    s = np.repeat(bf16_from_bits(scales_bf16_bits), group, axis=1)
-    return (q - z) * s
+    n, k = q.shape
+    d = q.reshape(n, k // group, group) - np.asarray(zeros, dtype=np.float64)[..., None]
+    return _group_scale(d.reshape(n, k), bf16_from_bits(scales_bf16_bits), group)
 
 
 # ----------------------------------------------------------------- NVFP4 ---
@@ -238,10 +243,11 @@ def e4m3_bytes(bs):
 
 
 def dequant_nvfp4(packed, scale_bytes, gs, group=NVFP4_GROUP):
-    """E2M1 value x E4M3 block scale x global scale, exact in float64."""
-    v = e2m1_decode(unpack_nvfp4(packed))
-    b = e4m3_decode(scale_bytes)
-    return v * np.repeat(b, group, axis=1) * float(gs)
+    """The product of the E2M1 value, its E4M3 block scale and the expert's
+    global scale, exact in float64."""
+    v = E2M1_TABLE[unpack_nvfp4(packed)]          # value of every code
+    b = E4M3_TABLE[np.asarray(scale_bytes, dtype=np.uint8)]
+    return _group_scale(v, b, group) * float(gs)
 
 
 def dequant_nvfp4_fp32(packed, scale_bytes, gs, group=NVFP4_GROUP):

@@ -6,7 +6,7 @@
  *
  * The router scores every expert by the dot product of the token's hidden
  * state with that expert's router row (pages "Step-5-Preview-Spark",
- * "At a glance": 352 routed experts, top-8, sigmoid router). The pages fix no
+ * "At a glance": a sigmoid router picks 8 of the 352 routed experts). The pages fix no
  * summation order, but they show that routing flips under a changed
  * summation order ("Step-5-Preview-Spark", "Quality", the noise-floor
  * paragraph). Bit-exact routing therefore needs one order; this file is its

@@ -259,7 +259,7 @@ const char *moe_status_string(int status) {
     }
 }
 
-int moe_abi_version(void) { return 3; }
+int moe_abi_version(void) { return 4; }
 
 static moe_status_t check_router(const void *x, int x_dtype, const float *wT, int T, int H,
                                  int E) {

@@ -7,7 +7,8 @@
 //               (+ shared[t][n]) (+ residual[t][n])
 //
 // float32 throughout, one fixed order, no atomics: the result does not
-// depend on scheduling.
+// depend on scheduling. A slot whose row is -1 (its id lay outside the
+// expert range, so the permutation routed it nowhere) adds nothing.
 #include "common.h"
 
 namespace moe {
@@ -37,11 +38,11 @@ __global__ void __launch_bounds__(256) combine_kernel(
     }
 #pragma unroll
     for (int k = 0; k < kCombineMaxK; ++k)
-        if (k < K) v[k] = *(const float4 *)(y + (size_t)rows[k] * H + n);
+        if (k < K && rows[k] >= 0) v[k] = *(const float4 *)(y + (size_t)rows[k] * H + n);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int k = 0; k < kCombineMaxK; ++k) {
-        if (k < K) {
+        if (k < K && rows[k] >= 0) {
             acc.x = __builtin_fmaf(wk[k], v[k].x, acc.x);
             acc.y = __builtin_fmaf(wk[k], v[k].y, acc.y);
             acc.z = __builtin_fmaf(wk[k], v[k].z, acc.z);

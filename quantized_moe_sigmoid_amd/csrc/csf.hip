@@ -1,6 +1,7 @@
 // Expansion of CSF-compressed NVFP4 block scales (page
-// "Step-5-Preview-NVFP4-Local", "Format"): a scale byte is its row's base
-// plus its 4-bit code, unless an exception at that position replaces it.
+// "Step-5-Preview-NVFP4-Local", "Format"): every byte is rebuilt as the row
+// base plus the 4-bit code at its position, and the positions the expert's
+// exception list names are then overwritten with the bytes stored there.
 //
 // One kernel per scale tensor; work group = (expert, range of kCsfRows
 // rows). The group first writes its rows from the fixed tensor (each

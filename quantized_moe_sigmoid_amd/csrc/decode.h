@@ -10,7 +10,7 @@
 // form holds unsigned nibbles q in [0, 15] with a zero point z per 128
 // inputs, weight = (q - z) * scale.
 //
-// int8-g128 (the same page, "Recipe": its "int8 experts" comparison):
+// int8-g128 (the same page, "Recipe": its comparison with 8-bit experts):
 // two's-complement bytes, input j at byte j, one bf16 scale per 128 inputs.
 //
 // NVFP4 (page "Step-5-Preview-NVFP4-Local", "Modifications" item 2,

@@ -95,9 +95,10 @@ __global__ void __launch_bounds__(256) dequant_nvfp4_kernel(
     o[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// NVFP4 with compressed scales: the block's scale byte is the row's base
-// plus its 4-bit code (low nibble = even block), unless one of the row's
-// exceptions holds the position; then as dequant_nvfp4_kernel.
+// NVFP4 with compressed scales: a block's scale byte comes from the row's
+// exception list when it names the block's position, else it is the row
+// base plus the block's 4-bit code (even blocks in the low nibble); the
+// rest as dequant_nvfp4_kernel.
 __global__ void __launch_bounds__(256) dequant_nvfp4_csf_kernel(
     const uint8_t *__restrict__ qw, int64_t qrow, const uint8_t *__restrict__ fixed,
     const uint32_t *__restrict__ xc, const int32_t *__restrict__ ri,

@@ -21,7 +21,8 @@
 //            an expert is the slot order. It also pads its segment with -1,
 //            writes its tile map entries and its place among active experts;
 //            the last block writes the totals.
-// Ids outside [0, E) are not routed anywhere in either form.
+// Ids outside [0, E) are not routed anywhere in either form: such a slot
+// gets slot_to_row -1 and no row, and the combine adds nothing for it.
 #include "common.h"
 
 namespace moe {
@@ -43,9 +44,15 @@ __device__ __forceinline__ int block_sum(int v, int *red) {
 }
 
 __global__ void __launch_bounds__(kPermThreads) perm_count_kernel(
-    const int32_t *__restrict__ ids, int n, int32_t *__restrict__ counts) {
+    const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ counts,
+    int32_t *__restrict__ slot_to_row) {
     __shared__ int red[kPermWaves];
     const int e = blockIdx.x;
+    // slots with a foreign id, spread over the blocks: no row
+    for (int i = blockIdx.x * kPermThreads + threadIdx.x; i < n; i += E * kPermThreads) {
+        const int id = ids[i];
+        if (id < 0 || id >= E) slot_to_row[i] = -1;
+    }
     int c = 0;
     for (int i = threadIdx.x; i < n; i += kPermThreads) c += (ids[i] == e);
     c = block_sum(c, red);
@@ -191,7 +198,10 @@ __global__ void __launch_bounds__(kPermSmallThreads) perm_small_kernel(
     // a slot's rank among its expert's slots: that expert's bits below it
     for (int s = tid; s < n; s += kPermSmallThreads) {
         const int ee = ids[s];
-        if (ee < 0 || ee >= E) continue;
+        if (ee < 0 || ee >= E) {
+            slot_to_row[s] = -1;
+            continue;
+        }
         const uint64_t *m = mask + (size_t)ee * W;
         int r = __popcll(m[s >> 6] & ((1ull << (s & 63)) - 1ull));
         for (int w = 0; w < (s >> 6); ++w) r += __popcll(m[w]);
@@ -218,7 +228,8 @@ moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_p
         MOE_LAUNCH_CHECK();
         return MOE_OK;
     }
-    hipLaunchKernelGGL(perm_count_kernel, dim3(E), dim3(kPermThreads), 0, s, ids, n, p.counts);
+    hipLaunchKernelGGL(perm_count_kernel, dim3(E), dim3(kPermThreads), 0, s, ids, n, E, p.counts,
+                       p.slot_to_row);
     MOE_LAUNCH_CHECK();
     hipLaunchKernelGGL(perm_scatter_kernel, dim3(E), dim3(kPermThreads), 0, s, ids, n, E,
                        p.tile_m, p.counts, p.expert_offsets, p.padded_offsets, p.sorted_slots,

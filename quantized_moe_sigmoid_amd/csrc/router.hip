@@ -15,7 +15,6 @@
 // Weights: sigmoid of the selected logits, renormalised to sum to one when
 // asked.
 #include "common.h"
-#include "norm.h"
 
 #pragma clang fp contract(off)
 
@@ -495,7 +494,7 @@ __device__ __forceinline__ void fma16_row_bcast(float &acc, float xq, const floa
 // wave: a batch of a few tokens has too few waves for the tiled kernels
 // above, and each wave runs one 4096-step chain. The group first stages its W rows in LDS
 // as float32: the bf16 activations widened (NORM = false) or, fused, the
-// RMSNorm of W fp32 residual rows (NORM = true), whose float64 sums of
+// RMSNorm of W fp32 residual rows (NORM = true), whose float32 sums of
 // squares follow rmsnorm_kernel's 256-thread order exactly (each thread
 // stands in for 4 / W of those threads: same columns, same wave shuffles,
 // same block sum), so the 16-bit rows are bitwise the ones moe_rmsnorm
@@ -514,7 +513,7 @@ constexpr int kRowsMaxH = 4096;                  // W float32 rows in LDS
 
 template <bool NORM, int W>
 __global__ void __launch_bounds__(64 * W) router_rows_kernel(
-    const void *__restrict__ xin, const float *__restrict__ gain, double eps,
+    const void *__restrict__ xin, const float *__restrict__ gain, float eps,
     const float *__restrict__ wT, const float *__restrict__ bias, int T, int H, int E,
     uint16_t *__restrict__ a_out, float *__restrict__ logits) {
     constexpr int NT = 64 * W, KC = 64, NP = 2;
@@ -523,7 +522,7 @@ __global__ void __launch_bounds__(64 * W) router_rows_kernel(
     constexpr int kCols = kRowsMaxH / 1024;      // float4 groups of a row per norm thread
     __shared__ __attribute__((aligned(16))) float ws[2][KC][kRtExp];
     __shared__ __attribute__((aligned(16))) float as[W][kRowsMaxH];
-    __shared__ double red[W][4];
+    __shared__ float red[W][4];
     const int t0 = blockIdx.x * W, e0 = blockIdx.y * kRtExp;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -572,25 +571,26 @@ __global__ void __launch_bounds__(64 * W) router_rows_kernel(
         for (int i = 0; i < W; ++i)
 #pragma unroll
             for (int u = 0; u < kVT; ++u) {
-                double ss = 0.0;
+                float ss = 0.0f;
 #pragma unroll
                 for (int j = 0; j < kCols; ++j) {
                     if ((tid + NT * u) * 4 + 1024 * j < H) {
                         const f32x4_t q = v[i][u][j];
-                        ss += (double)q.x * q.x + (double)q.y * q.y + (double)q.z * q.z +
-                              (double)q.w * q.w;
+                        ss = ss + q.x * q.x;
+                        ss = ss + q.y * q.y;
+                        ss = ss + q.z * q.z;
+                        ss = ss + q.w * q.w;
                     }
                 }
 #pragma unroll
-                for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, kWave);
+                for (int m = 32; m >= 1; m >>= 1) ss = ss + __shfl_xor(ss, m, kWave);
                 if (lane == 0) red[i][wave + W * u] = ss;
             }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < W; ++i) {
-            double tot = 0.0;
-            for (int w = 0; w < 4; ++w) tot += red[i][w];
-            const double inv = 1.0 / __builtin_sqrt(tot / H + eps);
+            const float tot = ((red[i][0] + red[i][1]) + red[i][2]) + red[i][3];
+            const float r = __builtin_sqrtf(tot / (float)H + eps);
 #pragma unroll
             for (int u = 0; u < kVT; ++u)
 #pragma unroll
@@ -599,15 +599,11 @@ __global__ void __launch_bounds__(64 * W) router_rows_kernel(
                     if (c < H) {
                         const f32x4_t q = v[i][u][j], gg = g[u][j];
                         const uint32_t lo =
-                            f64_to_act<MOE_BF16>((double)q.x * inv * (1.0 + (double)gg.x)) |
-                            ((uint32_t)f64_to_act<MOE_BF16>((double)q.y * inv *
-                                                            (1.0 + (double)gg.y))
-                             << 16);
+                            f32_to_bf16_bits((q.x / r) * (1.0f + gg.x)) |
+                            ((uint32_t)f32_to_bf16_bits((q.y / r) * (1.0f + gg.y)) << 16);
                         const uint32_t hi =
-                            f64_to_act<MOE_BF16>((double)q.z * inv * (1.0 + (double)gg.z)) |
-                            ((uint32_t)f64_to_act<MOE_BF16>((double)q.w * inv *
-                                                            (1.0 + (double)gg.w))
-                             << 16);
+                            f32_to_bf16_bits((q.z / r) * (1.0f + gg.z)) |
+                            ((uint32_t)f32_to_bf16_bits((q.w / r) * (1.0f + gg.w)) << 16);
                         *(f32x4_t *)&as[i][c] = f32x4_t{__uint_as_float(lo << 16),
                                                         __uint_as_float(lo & 0xFFFF0000u),
                                                         __uint_as_float(hi << 16),
@@ -657,10 +653,10 @@ static void launch_rows(const void *xin, const float *gain, float eps, int T, in
     const int eb = (E + kRtExp - 1) / kRtExp;
     if (T <= kRowsW2MaxT)
         hipLaunchKernelGGL((router_rows_kernel<NORM, 2>), dim3((T + 1) / 2, eb), dim3(128), 0, s,
-                           xin, gain, (double)eps, wT, bias, T, H, E, (uint16_t *)a_out, logits);
+                           xin, gain, eps, wT, bias, T, H, E, (uint16_t *)a_out, logits);
     else
         hipLaunchKernelGGL((router_rows_kernel<NORM, 4>), dim3((T + 3) / 4, eb), dim3(256), 0, s,
-                           xin, gain, (double)eps, wT, bias, T, H, E, (uint16_t *)a_out, logits);
+                           xin, gain, eps, wT, bias, T, H, E, (uint16_t *)a_out, logits);
 }
 
 moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, const float *bias,

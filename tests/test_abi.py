@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     assert B.status_string(0) == "MOE_OK"
     assert B.status_string(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
     assert B.status_string(99) == "MOE_ERR_UNKNOWN"
