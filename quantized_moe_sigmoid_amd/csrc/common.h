@@ -42,6 +42,14 @@ template <int ACT>
 __device__ __forceinline__ uint16_t f32_to_act(float f) {
     return ACT == MOE_BF16 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f);
 }
+// A float32 value the compiler must materialise as such: without it, a
+// product converted to fp16 is folded into one mixed-precision FMA that
+// rounds the exact product to fp16 once (v_fma_mixlo_f16), which is not the
+// float32 product rounded to fp16.
+__device__ __forceinline__ float as_f32(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
 
 // ---- cross-lane helpers ----------------------------------------------------
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {

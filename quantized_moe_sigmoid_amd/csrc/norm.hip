@@ -44,10 +44,10 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ 
         const float4 v = *(const float4 *)(row + i);
         float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
         if (w) g = *(const float4 *)(w + i);
-        const uint32_t lo = f32_to_act<OUT>((v.x / r) * (1.0f + g.x)) |
-                            ((uint32_t)f32_to_act<OUT>((v.y / r) * (1.0f + g.y)) << 16);
-        const uint32_t hi = f32_to_act<OUT>((v.z / r) * (1.0f + g.z)) |
-                            ((uint32_t)f32_to_act<OUT>((v.w / r) * (1.0f + g.w)) << 16);
+        const uint32_t lo = f32_to_act<OUT>(as_f32((v.x / r) * (1.0f + g.x))) |
+                            ((uint32_t)f32_to_act<OUT>(as_f32((v.y / r) * (1.0f + g.y))) << 16);
+        const uint32_t hi = f32_to_act<OUT>(as_f32((v.z / r) * (1.0f + g.z))) |
+                            ((uint32_t)f32_to_act<OUT>(as_f32((v.w / r) * (1.0f + g.w))) << 16);
         *(uint2 *)(o + i) = make_uint2(lo, hi);
     }
 }

@@ -172,14 +172,28 @@ def csf_random(E, R, C, seed, device, rate=0.002):
     return fixed, exceptions, torch.tensor(starts, dtype=torch.int64, device=device)
 
 
-def packed_nvfp4_random(E, n, k, seed, device, gs_mean=2.0e-5):
+def packed_nvfp4_random(E, n, k, seed, device, gs_mean=2.0e-5, scale_window=None):
     """Random NVFP4 bank in packed form: uniform bytes (two uniform E2M1
     codes each), E4M3 block-scale bytes uniform in [0x70, 0x7E] (128 .. 448)
-    and float32 global scales gs_mean * (1 + 0.1 N(0, 1))."""
+    and float32 global scales gs_mean * (1 + 0.1 N(0, 1)).
+
+    With scale_window = w, the scale bytes of expert e are instead uniform
+    in [b_e, b_e + w - 1] with b_e uniform in [0, 0x7F - w], so that over a
+    layer the block scales reach every finite non-negative E4M3 byte
+    (0x00 .. 0x7E: zero, subnormals and normals); the caller then picks
+    global scales that bring each expert back to a common magnitude."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     q = torch.randint(0, 256, (E, n, k // 2), generator=g, device=device, dtype=torch.uint8)
-    s = torch.randint(0x70, 0x7F, (E, n, k // 16), generator=g, device=device, dtype=torch.uint8)
+    if scale_window is None:
+        s = torch.randint(0x70, 0x7F, (E, n, k // 16), generator=g, device=device,
+                          dtype=torch.uint8)
+    else:
+        w = int(scale_window)
+        base = torch.randint(0, 0x80 - w, (E, 1, 1), generator=g, device=device,
+                             dtype=torch.int32)
+        off = torch.randint(0, w, (E, n, k // 16), generator=g, device=device, dtype=torch.int32)
+        s = (base + off).to(torch.uint8)
     gs = (torch.randn((E,), generator=g, device=device) * 0.1 + 1.0) * gs_mean
     return q, s, gs.float()

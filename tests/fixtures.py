@@ -192,3 +192,92 @@ def oracle_variant_expert(q, s_bits, z, e):
     if z is not None:
         return OQ.dequant_int4_asym(q, s_bits, z)
     return OQ.dequant_int4(q, s_bits, group=32)
+
+
+# ------------------------------------------------ streamed oracle layer ---
+def host_bank(q, s, z=None, gs=None):
+    """Host (numpy) copies of a bank's device tensors: codes, scale bits or
+    bytes, zero points, global scales (None passes through)."""
+    def h(t):
+        if t is None or not isinstance(t, torch.Tensor):
+            return t
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+    return h(q), h(s), h(z), h(gs)
+
+
+def dequant_fn(host, fmt="int4"):
+    """expert -> float64 (Wg, Wu, Wd) from host banks (see host_bank), no
+    cache: each call dequantizes afresh."""
+    def fn(e):
+        mats = []
+        for (q, s, z, gs) in host:
+            if fmt == "int4":
+                mats.append(OQ.dequant_int4(q[e], s[e]))
+            elif fmt == "nvfp4":
+                mats.append(OQ.dequant_nvfp4(q[e], s[e], float(gs[e])))
+            else:
+                raise ValueError(fmt)
+        return tuple(mats)
+    return fn
+
+
+def oracle_layer_streamed(x16, ids, w, expert_fn, shared=None, residual=None, threads=16):
+    """The oracle's layer (oracle.layer) on rows x16 [n, H] with routing ids
+    [n, K] and weights w [n, K]: every expert the rows reach is dequantized
+    once by expert_fn, its slots evaluated and its weights dropped, so the
+    memory held stays a few experts'. Experts run on a thread pool (numpy
+    releases the GIL in its array operations); each slot's value depends
+    only on its own token and expert, so the order of the experts does not
+    change any result."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    x = x16.float().cpu().numpy().astype(np.float64) if isinstance(x16, torch.Tensor) \
+        else np.asarray(x16, dtype=np.float64)
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    y = np.zeros((T, K, x.shape[1]))
+
+    def work(e):
+        t_idx, k_idx = np.nonzero(ids == e)
+        Wg, Wu, Wd = expert_fn(int(e))
+        return t_idx, k_idx, OL.swiglu_ffn(x[t_idx], Wg, Wu, Wd)
+
+    with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+        for t_idx, k_idx, out in ex.map(work, np.unique(ids)):
+            y[t_idx, k_idx] = out
+    sh = OL.swiglu_ffn(x, *shared) if shared is not None else None
+    return OL.combine(y, np.asarray(w, dtype=np.float64), sh, residual)
+
+
+def tile_probe_tokens(ids, E, tile_m, min_tokens=64, max_tokens=96):
+    """Tokens whose slots land on chosen rows of the expert-sorted tiles
+    (the oracle's permutation): rows 0, 31, 32 and 63 of full tiles and the
+    last filled row of partial tiles, over experts with several tiles first,
+    then experts with one partial tile; topped up with evenly spaced tokens
+    (the first and last included) to at least min_tokens. Sorted, at most
+    max_tokens."""
+    from oracle import permute as OP
+    ids = np.asarray(ids)
+    K = ids.shape[1]
+    p = OP.permute(ids, E, tile_m)
+    counts, po, ss = p["counts"], p["padded_offsets"], p["sorted_slots"]
+    order = list(np.argsort(-counts, kind="stable"))
+    big = [e for e in order if counts[e] > tile_m][:16]
+    small = [e for e in order[::-1] if 0 < counts[e] < tile_m][:16]
+    picks = []
+    for e in big + small:
+        c = int(counts[e])
+        for t0 in range(0, c, tile_m):
+            for r in (0, 31, 32, 63, min(c - t0, tile_m) - 1):
+                if r < tile_m and t0 + r < c:
+                    picks.append(int(ss[po[e] + t0 + r]) // K)
+    T = ids.shape[0]
+    toks = list(dict.fromkeys(picks + [0, T - 1]))[:max_tokens]
+    for t in np.linspace(0, T - 1, min_tokens).astype(int):
+        if len(toks) >= min_tokens:
+            break
+        if int(t) not in toks:
+            toks.append(int(t))
+    return sorted(toks)

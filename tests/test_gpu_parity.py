@@ -5,7 +5,9 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import formats as OF
 from oracle import layer as OL
+from oracle import norm as ON
 from oracle import permute as OP
 from oracle import quant as OQ
 from oracle import router as OR
@@ -242,20 +244,24 @@ def test_forward_tiny_end_to_end(dev):
     assert ok, ratio
 
 
+def _host_int4(host):
+    return [FX.host_bank(q, s) for (q, s) in host]
+
+
 @pytest.mark.parametrize("T", [1, 8, 64])
 def test_forward_decode_full_shape(dev, T):
     """Decode shape: 352 int4 experts, hidden 4096, width 1536, fp16 x,
-    given logits. Every token for T <= 8, four sampled tokens for T = 64."""
+    given logits. Every token against the oracle (streamed per expert)."""
     ffn, host = _int4_ffn_random(E, H, F, 100 + T, dev)
     x = synth.activations(T, H, "f16", 2)
     lg = synth.router_logits(T, E, 2)
     ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
     out = _run_layer(dev, ffn, x.to(dev), ids, w, E).cpu().numpy()
-    toks = list(range(T)) if T <= 8 else [0, 17, 40, 63]
     oids = OR.topk_ids(lg, K)
+    assert np.array_equal(ids.cpu().numpy(), oids)
     ow = OR.routing_weights(lg, oids)
-    ref = FX.oracle_layer(x[toks], oids[toks], ow[toks], _experts_fn_int4(host))
-    ok, ratio = FX.within_tolerance(out[toks], ref)
+    ref = FX.oracle_layer_streamed(x, oids, ow, FX.dequant_fn(_host_int4(host)))
+    ok, ratio = FX.within_tolerance(out, ref)
     assert ok, ratio
 
 
@@ -467,9 +473,13 @@ def test_forward_prefill_full_shape(dev, zipf):
     lg = OR.router_logits(x.float().numpy(), wT, b)
     oids = OR.topk_ids(lg, K)
     assert np.array_equal(ids.cpu().numpy(), oids)
-    toks = [0, 1, 1023, 2047]
+    # tokens on rows 0, 31, 32, 63 of full tiles and the last rows of
+    # partial ones (tile_m 64), and evenly spaced ones
+    toks = FX.tile_probe_tokens(oids, E, 64)
+    assert len(toks) >= 64
     ow = OR.routing_weights(lg, oids)
-    ref = FX.oracle_layer(x[toks], oids[toks], ow[toks], _experts_fn_int4(host))
+    ref = FX.oracle_layer_streamed(x[toks], oids[toks], ow[toks],
+                                   FX.dequant_fn(_host_int4(host)))
     ok, ratio = FX.within_tolerance(out[toks], ref)
     assert ok, ratio
 
@@ -487,9 +497,42 @@ def test_forward_nvfp4_prefill_full_shape(dev):
     ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
     out = _run_layer(dev, ffn, x.to(dev), ids, w, E).cpu().numpy()
     oids = OR.topk_ids(lg, K)
-    toks = [0, 100, 255]
-    ref = FX.oracle_layer(x[toks], oids[toks], OR.routing_weights(lg, oids)[toks],
-                          _efn_nvfp4(host))
+    toks = FX.tile_probe_tokens(oids, E, 64)
+    assert len(toks) >= 64
+    hb = [FX.host_bank(q, s, gs=g) for (q, s, g) in host]
+    ref = FX.oracle_layer_streamed(x[toks], oids[toks], OR.routing_weights(lg, oids)[toks],
+                                   FX.dequant_fn(hb, "nvfp4"))
+    ok, ratio = FX.within_tolerance(out[toks], ref)
+    assert ok, ratio
+
+
+@pytest.mark.parametrize("T", [64, 256])
+def test_forward_nvfp4_every_scale_byte(dev, T):
+    """NVFP4 at the layer shape with block-scale bytes spanning every finite
+    non-negative E4M3 value: each expert draws its bytes from its own window
+    of 8 (zero and subnormal scales included) and its global scale brings
+    its weights back to a common magnitude, so a mis-decoded scale byte
+    shows in the outputs. T = 64 runs the decode kernels, T = 256 the
+    grouped GEMM; every token (T = 64) or tile-probing tokens."""
+    banks, hb = [], []
+    for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
+        qt, st, _ = synth.packed_nvfp4_random(E, n, k, 80 + i, dev, scale_window=8)
+        mid = st.amin(dim=(1, 2)).cpu().numpy().astype(np.int64) + 4
+        gs = (2.0e-5 * 320.0 / OF.E4M3_TABLE[mid]).astype(np.float32)
+        gt = torch.from_numpy(gs).to(dev)
+        banks.append(B.bank_nvfp4(qt, st, gt))
+        hb.append(FX.host_bank(qt, st, gs=gs))
+    bytes_seen = np.unique(np.concatenate([np.unique(h[1]) for h in hb]))
+    assert bytes_seen.min() == 0 and bytes_seen.max() == 0x7E
+    ffn = B.ffn(*banks)
+    x = synth.activations(T, H, "bf16", 8)
+    lg = synth.router_logits(T, E, 8)
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, E).cpu().numpy()
+    oids = OR.topk_ids(lg, K)
+    toks = list(range(T)) if T <= 64 else FX.tile_probe_tokens(oids, E, 64)
+    ref = FX.oracle_layer_streamed(x[toks], oids[toks], OR.routing_weights(lg, oids)[toks],
+                                   FX.dequant_fn(hb, "nvfp4"))
     ok, ratio = FX.within_tolerance(out[toks], ref)
     assert ok, ratio
 
@@ -516,3 +559,87 @@ def test_norm_route_matches_separate_calls(dev, T, Hh, Ee, Kk, with_bias, with_g
     assert torch.equal(a.view(torch.int16), a2.view(torch.int16))
     assert torch.equal(ids, ids2)
     assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
+
+
+@pytest.mark.parametrize("T,Hh,Ee,Kk,with_bias,with_gain", [
+    (1, 4096, 352, 8, True, True), (32, 4096, 352, 8, True, True),
+    (192, 4096, 352, 8, True, True), (193, 4096, 352, 8, True, True),
+    (6, 8192, 64, 4, True, False)])
+def test_norm_route_against_oracle(dev, T, Hh, Ee, Kk, with_bias, with_gain):
+    """moe_norm_route against the oracle directly: the layer input a is the
+    oracle's float32 RMSNorm rounded to bf16, bit for bit; the expert ids are
+    the oracle's top-K of its router chain on that a, bit for bit; weights
+    within 1e-5. T <= 192 runs the fused kernel (one and two token groups
+    per wave count), T = 193 and H = 8192 the separate kernels."""
+    r = synth.normal((T, Hh), 1.0, 15, 0, synth.T_X, T)
+    r[0] *= 300.0                                          # rows of other scales
+    if T > 2:
+        r[2] *= 1e-3
+    gain = synth.norm_weight(Hh, 15, 0) if with_gain else None
+    wT = synth.router_weight_T(Hh, Ee, 15)
+    bias = synth.zipf_bias(Ee, 15, 0) if with_bias else None
+    a, ids, w = B.moe_norm_route(torch.from_numpy(r).to(dev), torch.from_numpy(wT).to(dev), Kk,
+                                 norm_w=None if gain is None else torch.from_numpy(gain).to(dev),
+                                 eps=1e-5,
+                                 bias=None if bias is None else torch.from_numpy(bias).to(dev))
+    oa = OF.round_to_format(ON.rmsnorm(r, gain, 1e-5), OF.BF16)
+    a16 = a.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.argwhere(a16 != OF.bf16_bits(oa))
+    assert bad.size == 0, bad[:5]
+    lg = OR.router_logits(oa.astype(np.float32), wT, bias)
+    oids = OR.topk_ids(lg, Kk)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    np.testing.assert_allclose(w.cpu().numpy(), OR.routing_weights(lg, oids), rtol=1e-5, atol=0)
+
+
+@pytest.mark.parametrize("T,Kk,Ee", [(9, 4, 16), (300, 4, 16)])
+def test_forward_foreign_ids(dev, T, Kk, Ee):
+    """Slots whose expert id lies outside [0, E) are routed nowhere: the
+    layer equals the oracle's layer with those slots dropped (their weight
+    set to zero). T = 9 runs the decode kernels and the one-group
+    permutation, T = 300 the GEMM and the two-launch permutation."""
+    Hh, Ff = 512, 256
+    ffn, host = FX.int4_ffn_random(Ee, Hh, Ff, 90 + T, dev)
+    r = np.random.default_rng(T)
+    ids = np.stack([r.choice(Ee, Kk, replace=False) for _ in range(T)]).astype(np.int32)
+    foreign = r.random((T, Kk)) < 0.2
+    ids[foreign] = r.choice([-3, -1, Ee, Ee + 5], int(foreign.sum()))
+    w = r.random((T, Kk)).astype(np.float32)
+    x = synth.activations(T, Hh, "bf16", 16)
+    tm, _ = B.moe_forward_plan(ffn, T, Kk, x.dtype)
+    perm = B.moe_permute(torch.from_numpy(ids).to(dev), Ee, tm)
+    out = B.moe_w4a16_forward(ffn, x.to(dev), torch.from_numpy(w).to(dev), perm).cpu().numpy()
+    s2r = perm.slot_to_row.cpu().numpy().reshape(T, Kk)
+    assert np.all(s2r[foreign] == -1) and np.all(s2r[~foreign] >= 0)
+    ref = FX.oracle_layer(x, np.where(foreign, 0, ids), np.where(foreign, 0.0, w),
+                          FX.experts_fn_int4(host))
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
+@pytest.mark.parametrize("T,fmt", [(1, "int4"), (8, "int4"), (64, "int4"), (300, "int4"),
+                                   (5, "nvfp4"), (300, "nvfp4")])
+def test_forward_workspace_nan_canary(dev, T, fmt):
+    """Workspace contents never reach the output: the forward pass run on a
+    workspace filled with NaN gives bitwise the output it gives on a
+    zero-filled one (padded tile rows stage uninitialised h and y rows; the
+    kernels must keep them out of every result). Decode (T <= 64, E = 16,
+    K = 4) and GEMM (T = 300) paths, with the shared expert at T = 300."""
+    Ee, Kk, Hh, Ff = 16, 4, 512, 256
+    if fmt == "int4":
+        ffn, _ = FX.int4_ffn_random(Ee, Hh, Ff, 95, dev)
+    else:
+        ffn, _ = _nvfp4_ffn_from_oracle(Ee, Hh, Ff, 9, dev)
+    sh = FX.shared_bf16(256, Hh, 4, 0, dev)[0] if T == 300 else None
+    x = synth.activations(T, Hh, "bf16", 17).to(dev)
+    lg = synth.router_logits(T, Ee, 17)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    tm, need = B.moe_forward_plan(ffn, T, Kk, x.dtype, sh)
+    perm = B.moe_permute(ids, Ee, tm)
+    outs = []
+    for fill in (0.0, float("nan")):
+        ws = torch.full(((need + 3) // 4,), fill, dtype=torch.float32, device=dev)
+        o = B.moe_w4a16_forward(ffn, x, w, perm, shared=sh, ws=ws.view(torch.uint8))
+        outs.append(o.cpu().numpy())
+    assert not np.isnan(outs[1]).any()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))

@@ -10,7 +10,8 @@ a_l = bf16(rmsnorm_l(r_l)), route a_l with the layer's router weight and
 Zipf expert bias, r_{l+1} = fp32(r_l + MoE_l(a_l)). Without the norm the
 chain diverges: the SwiGLU is quadratic in its input, so the residual's rms
 roughly squares from layer to layer. Tokens never mix inside an MoE layer, so
-the oracle follows a few sampled tokens through all eight layers on its own;
+the oracle follows sampled tokens (all 32 of the decode batch, 34 of the
+prefill batch) through all eight layers on its own;
 each GPU layer is then fed the oracle's r_l in those rows and checked against
 the oracle's r_{l+1} there (routing bit for bit, outputs within the
 tolerance). The GPU's own eight-layer chain is run too, and its drift from
@@ -24,6 +25,7 @@ import torch
 from oracle import formats as OF
 from oracle import layer as OL
 from oracle import norm as ON
+from oracle import quant as OQ
 from oracle import router as OR
 from quantized_moe_sigmoid_amd import binding as B
 from quantized_moe_sigmoid_amd import synth
@@ -83,11 +85,12 @@ def test_round_activations_bitwise(dev, dtype, fmt):
 
 # ------------------------------------------------------------- rmsnorm ---
 @pytest.mark.parametrize("dtype,fmt", [(torch.bfloat16, OF.BF16), (torch.float16, OF.FP16)])
-@pytest.mark.parametrize("T,Hh", [(37, 4096), (5, 256), (3, 12)])
+@pytest.mark.parametrize("T,Hh", [(37, 4096), (5, 256), (3, 12), (4, 16384), (600, 4096)])
 def test_rmsnorm_bitwise(dev, dtype, fmt, T, Hh):
-    """moe_rmsnorm against the oracle's float64 RMSNorm rounded once: Gaussian
-    rows of several scales, a zero row (eps keeps it finite), and a row with
-    one large entry so that the others land in the fp16 subnormal range."""
+    """moe_rmsnorm against the oracle's float32 RMSNorm (fixed summation
+    order) rounded to the 16-bit format: Gaussian rows of several scales, a
+    zero row (eps keeps it finite), and a row with one large entry so that
+    the others land in the fp16 subnormal range."""
     g = synth.rng(10, 0, synth.T_X)
     x = g.standard_normal((T, Hh)) * np.exp(g.uniform(-8, 8, size=(T, 1)))
     x[1] = 0.0
@@ -188,12 +191,18 @@ class _Layer:
         self.norm_w_d = torch.from_numpy(self.norm_w).to(dev)
         self.wT_d = torch.from_numpy(self.wT).to(dev)
         self.bias_d = torch.from_numpy(self.bias).to(dev)
-        self.experts = FX.experts_fn_int4(self.host)
+
+    def experts(self, e):
+        """Expert e's float64 (Wg, Wu, Wd), fetched from the device and
+        dequantized by the oracle (no cache)."""
+        return tuple(OQ.dequant_int4(*FX.host_bank(q[e], s[e])[:2]) for (q, s) in self.host)
 
     def gpu(self, dev, r):
-        """One GPU layer on the float32 residual r [T, H] (device)."""
-        a = B.moe_rmsnorm(r, self.norm_w_d, EPS, torch.bfloat16)
-        ids, w = B.moe_route_topk(K, x=a, router_wT=self.wT_d, bias=self.bias_d)
+        """One GPU layer on the float32 residual r [T, H] (device), through
+        the calls the stack benchmark makes: moe_norm_route (the norm fused
+        into the router kernel up to 192 tokens), permute, forward."""
+        a, ids, w = B.moe_norm_route(r, self.wT_d, K, norm_w=self.norm_w_d, eps=EPS,
+                                     bias=self.bias_d)
         out = _forward(dev, self.ffn, a, ids, w, E, shared=self.sh, residual=r)
         return a, ids, w, out
 
@@ -203,7 +212,8 @@ class _Layer:
         lg = OR.router_logits(a.astype(np.float32), self.wT, self.bias)
         ids = OR.topk_ids(lg, K)
         w = OR.routing_weights(lg, ids)
-        out = OL.moe_layer(a, ids, w, self.experts, self.sh_host, r.astype(np.float64))
+        out = FX.oracle_layer_streamed(a, ids, w, self.experts, self.sh_host,
+                                       r.astype(np.float64))
         return a, ids, w, out
 
 
@@ -233,7 +243,6 @@ class _Stack:
             self.o_out.append(out)
             self.o_route.append((a, ids, w))
             self.o_r.append(OF.round_to_format(out, OF.FP32).astype(np.float32))
-            self.layers[j].experts = FX.experts_fn_int4(self.layers[j].host)  # drop the cache
 
 
 _STACKS = {}
@@ -242,7 +251,10 @@ _STACKS = {}
 def _stack(dev, T):
     if T not in _STACKS:
         _STACKS.clear()                                         # one weight set at a time
-        toks = [0, 13, 31] if T == 32 else [0, 2049, 4095]
+        # every token of the decode batch; 32 tokens spread over the prefill
+        # batch (first and last included)
+        toks = list(range(32)) if T == 32 else \
+            sorted(set(np.linspace(0, T - 1, 32).astype(int).tolist()) | {1, 2049})
         _STACKS[T] = _Stack(dev, T, toks)
     return _STACKS[T]
 
