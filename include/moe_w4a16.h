@@ -14,7 +14,9 @@
  * --------------------------------
  * - Every pointer argument is a DEVICE pointer unless its comment says
  *   "host". The caller owns all memory, workspaces included; the library
- *   allocates nothing and keeps no mutable global state.
+ *   allocates nothing and keeps no mutable global state, apart from the
+ *   static device buffer of moe_w4a16_forward_scratch and the per-device
+ *   address of it that the first call on a device looks up.
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   Every call only enqueues work on it and returns; nothing synchronises.
  * - Arguments are validated on the host before anything is launched; an
@@ -309,6 +311,38 @@ moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts,
                                const float *topk_w, const moe_perm_t *perm,
                                const float *residual, void *out, int out_dtype,
                                void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of the library-owned device buffer of moe_w4a16_forward_scratch. */
+#define MOE_FORWARD_SCRATCH_BYTES (64u << 20)
+
+/*
+ * moe_w4a16_forward_scratch -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): moe_w4a16_forward with its workspace replaced by one
+ * library-owned device buffer of MOE_FORWARD_SCRATCH_BYTES (64 MiB), a
+ * static device array of which each GPU the library runs on holds its own
+ * copy until the process ends. Same arguments (minus ws, ws_bytes), same
+ * kernels, same results. The device is the current HIP device of the
+ * calling thread, which must own `stream`; the first call on a device looks
+ * the buffer's address up (hipGetSymbolAddress, no allocation), later calls
+ * reuse it. Nothing here allocates: no hipMalloc, hipFree or allocating
+ * library routine. The buffer keeps the last call's contents; no step of
+ * the forward pass reads workspace memory it has not written in the same
+ * call, so nothing needs clearing. Calls that overlap on one GPU (other
+ * streams, other threads) share the buffer and race: serialise them.
+ * Errors: as moe_w4a16_forward, plus MOE_ERR_WORKSPACE_TOO_SMALL when
+ * moe_forward_plan's ws_bytes for the call exceeds the buffer (at the
+ * Step-5 shape every batch the decode kernels serve fits, T*K < 4E, i.e. up
+ * to 175 tokens at K = 8 and E = 352, with or without the shared expert;
+ * the prefill GEMM path's workspace does not), MOE_ERR_HIP if the device or
+ * the buffer's address cannot be had.
+ */
+moe_status_t moe_w4a16_forward_scratch(const moe_ffn_desc_t *experts,
+                                       const moe_ffn_desc_t *shared,
+                                       const void *x, int act_dtype, int T, int K,
+                                       const float *topk_w, const moe_perm_t *perm,
+                                       const float *residual, void *out, int out_dtype,
+                                       void *stream);
 
 /* Number of timed stages of moe_w4a16_forward_profiled. */
 #define MOE_FORWARD_STAGES 4

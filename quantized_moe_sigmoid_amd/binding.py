@@ -22,8 +22,9 @@ EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_rou
            "moe_route_topk", "moe_permute_sizes",
            "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_w4a16_forward_profiled",
            "moe_round_activations", "moe_rmsnorm", "moe_dequant", "moe_csf_expand",
-           "moe_csf_row_index", "moe_norm_route")
+           "moe_csf_row_index", "moe_norm_route", "moe_w4a16_forward_scratch")
 MOE_FORWARD_STAGES = 4
+MOE_FORWARD_SCRATCH_BYTES = 64 << 20
 
 _DT = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
 _TD = {v: k for k, v in _DT.items()}
@@ -84,6 +85,8 @@ def lib():
         L.moe_w4a16_forward.argtypes = [P(FfnDesc), P(FfnDesc), vp, i32, i32, i32, vp,
                                         P(PermDesc), vp, vp, i32, vp, sz, vp]
         L.moe_w4a16_forward_profiled.argtypes = L.moe_w4a16_forward.argtypes + [P(vp), i32]
+        L.moe_w4a16_forward_scratch.argtypes = [P(FfnDesc), P(FfnDesc), vp, i32, i32, i32, vp,
+                                                P(PermDesc), vp, vp, i32, vp]
         L.moe_round_activations.argtypes = [vp, i64, i32, vp, vp]
         L.moe_rmsnorm.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, vp]
         L.moe_dequant.argtypes = [P(WeightDesc), i32, vp, vp]
@@ -95,7 +98,8 @@ def lib():
                      "moe_permute_sizes", "moe_permute", "moe_forward_plan",
                      "moe_w4a16_forward", "moe_w4a16_forward_profiled",
                      "moe_round_activations", "moe_rmsnorm", "moe_dequant",
-                     "moe_csf_expand", "moe_csf_row_index", "moe_norm_route"):
+                     "moe_csf_expand", "moe_csf_row_index", "moe_norm_route",
+                     "moe_w4a16_forward_scratch"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -307,6 +311,24 @@ def moe_w4a16_forward(experts, x, topk_w, perm, residual=None, out_dtype=torch.f
         arr = (ctypes.c_void_p * len(events))(*events)
         _check(lib().moe_w4a16_forward_profiled(*args, arr, len(events)),
                "moe_w4a16_forward_profiled")
+    return out
+
+
+def moe_w4a16_forward_scratch(experts, x, topk_w, perm, residual=None, out_dtype=torch.float32,
+                              shared=None, out=None):
+    """moe_w4a16_forward on the library's own device buffer (no workspace
+    argument; the library allocates nothing). `out` is allocated here by
+    torch unless given."""
+    T, H = x.shape
+    K = topk_w.shape[1]
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    pd = perm.desc()
+    _check(lib().moe_w4a16_forward_scratch(
+        ctypes.byref(experts), ctypes.byref(shared) if shared is not None else None, _ptr(x),
+        _DT[x.dtype], T, K, _ptr(topk_w), ctypes.byref(pd), _ptr(residual), _ptr(out),
+        _DT[out.dtype], _stream(dev)), "moe_w4a16_forward_scratch")
     return out
 
 

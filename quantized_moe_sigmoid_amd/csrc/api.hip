@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <functional>
+#include <mutex>
 
 #include "common.h"
 
@@ -440,6 +441,53 @@ moe_status_t moe_w4a16_forward_profiled(const moe_ffn_desc_t *experts,
     if (!events) return MOE_ERR_INVALID_ARG;
     return forward_impl(experts, shared, x, act_dtype, T, K, topk_w, perm, residual, out,
                         out_dtype, ws, ws_bytes, stream, events, n_events);
+}
+
+}  // extern "C"
+
+// ---- the forward pass on library-owned device memory ----------------------
+// For callers that cannot allocate device memory: one static device array,
+// of which every GPU the library runs on holds its own copy until the
+// process ends. Its device address is looked up once per device (host code
+// must never pass the array's own name to a kernel: on the host that name
+// is a stand-in, not a device address).
+static __device__ __align__(256) uint8_t scratch[MOE_FORWARD_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+moe_status_t scratch_of_current_device(void **p) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = q;
+    }
+    *p = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_w4a16_forward_scratch(const moe_ffn_desc_t *experts,
+                                       const moe_ffn_desc_t *shared, const void *x,
+                                       int act_dtype, int T, int K, const float *topk_w,
+                                       const moe_perm_t *perm, const float *residual,
+                                       void *out, int out_dtype, void *stream) {
+    int tile_m = 0;
+    size_t need = 0;
+    moe_status_t st = moe_forward_plan(experts, shared, T, K, act_dtype, &tile_m, &need);
+    if (st != MOE_OK) return st;
+    if (need > (size_t)MOE_FORWARD_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+    return forward_impl(experts, shared, x, act_dtype, T, K, topk_w, perm, residual, out,
+                        out_dtype, ws, (size_t)MOE_FORWARD_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
 moe_status_t moe_round_activations(const float *in, int64_t n, int out_dtype, void *out,

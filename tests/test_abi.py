@@ -205,6 +205,35 @@ def test_forward_profiled_validation(L):
              B.MOE_F32, None, 0, None, none, n) == B.MOE_OK
 
 
+def test_forward_scratch_validation(L):
+    """The entry on the library's own buffer: argument errors as
+    moe_w4a16_forward, and a call whose workspace would exceed the buffer is
+    refused before any HIP call. Every decode-kernel batch of the Step-5
+    shape fits (T*K < 4E: up to 175 tokens, with the shared expert too);
+    the prefill GEMM's workspace does not."""
+    F = L.moe_w4a16_forward_scratch
+    x = ctypes.c_void_p(FAKE)
+    f = _ffn()
+    for T in (1, 64, 175):
+        st, tm, ws = _plan(f, T=T, act=B.MOE_BF16)
+        assert st == B.MOE_OK and tm == 4 and ws <= B.MOE_FORWARD_SCRATCH_BYTES, (T, ws)
+        sh = _shared()
+        st, tm, ws = _plan(f, T=T, act=B.MOE_BF16, shared=ctypes.byref(sh))
+        assert st == B.MOE_OK and ws <= B.MOE_FORWARD_SCRATCH_BYTES, (T, ws)
+    st, tm, ws = _plan(f, T=176, act=B.MOE_BF16)
+    assert tm == 64 and ws > B.MOE_FORWARD_SCRATCH_BYTES
+    p = B.PermDesc(*([FAKE] * 9), tm)
+    assert F(ctypes.byref(f), None, x, B.MOE_BF16, 176, 8, x, ctypes.byref(p), None, x,
+             B.MOE_F32, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # invalid arguments are reported before the buffer is looked up
+    assert F(None, None, x, B.MOE_BF16, 8, 8, x, ctypes.byref(p), None, x, B.MOE_F32,
+             None) == B.MOE_ERR_INVALID_ARG
+    assert F(ctypes.byref(f), None, x, 9, 8, 8, x, ctypes.byref(p), None, x, B.MOE_F32,
+             None) == B.MOE_ERR_INVALID_ARG
+    assert F(ctypes.byref(f), None, x, B.MOE_BF16, 8, 17, x, ctypes.byref(p), None, x,
+             B.MOE_F32, None) == B.MOE_ERR_INVALID_ARG
+
+
 def test_dequant_validation(L):
     b = _bank(B.MOE_W_INT4_G128, 4, 64, 256)
     out = ctypes.c_void_p(FAKE)
