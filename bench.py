@@ -185,15 +185,19 @@ def touched_experts(logits_cpu):
 
 
 def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf=None,
-              csf_mode="expand"):
+              csf_mode="expand", use_graph=False):
     """Times `steps` layer passes. route_mode: 'logits' (fresh N(0,1) logits
-    per step) or 'weights' (router weight + fixed batch). csf: per bank copy,
-    the compressed scales of its three matrices; each step then either
-    expands the routed experts' scales before the forward pass (csf_mode
-    'expand') or builds their row index for the kernels that read them in
-    place ('index'). Returns a dict."""
+    per step), 'weights' (router weight + fixed batch) or 'zipf' (router
+    weight + Zipf(1.1) expert biases, fixed batch). csf: per bank copy, the
+    compressed scales of its three matrices; each step then either expands
+    the routed experts' scales before the forward pass (csf_mode 'expand')
+    or builds their row index for the kernels that read them in place
+    ('index'). use_graph: the timed steps are captured once as one HIP graph
+    (each step its own logits and weight copy, as eagerly) and replayed.
+    Returns a dict."""
     n_in = steps + warmup
-    x = synth.activations(T, H, act, 3 if route_mode == "weights" else 2).to(dev)
+    x = synth.activations(T, H, act, 2 if route_mode == "logits" else 3).to(dev)
+    bias = None
     if route_mode == "logits":
         lg_cpu = [torch.from_numpy(synth.router_logits(T, E, 1000 + i)) for i in range(n_in)]
         logits = [t.to(dev) for t in lg_cpu]
@@ -201,13 +205,15 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
     else:
         lg_cpu = None
         wT = torch.from_numpy(synth.router_weight_T(H, E, 3)).to(dev)
+        if route_mode == "zipf":
+            bias = torch.from_numpy(synth.zipf_bias(E, 3)).to(dev)
     tm, ws_bytes = B.moe_forward_plan(banks[0], T, K, x.dtype)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ids = torch.empty((T, K), dtype=torch.int32, device=dev)
     w = torch.empty((T, K), dtype=torch.float32, device=dev)
     perm = B.Perm(T, K, E, tm, dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
-    rws = torch.empty(max(B.moe_route_workspace(T, E, route_mode == "weights"), 256),
+    rws = torch.empty(max(B.moe_route_workspace(T, E, route_mode != "logits"), 256),
                       dtype=torch.uint8, device=dev)
     NS = B.MOE_FORWARD_STAGES
     # timed loop: events only at the gate/up boundaries of every
@@ -222,7 +228,7 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
         if route_mode == "logits":
             B.moe_route_topk(K, logits=logits[i], ids=ids, w=w)
         else:
-            B.moe_route_topk(K, x=x, router_wT=wT, ids=ids, w=w, ws=rws)
+            B.moe_route_topk(K, x=x, router_wT=wT, bias=bias, ids=ids, w=w, ws=rws)
         B.moe_permute(ids, E, tm, perm=perm)
         if csf:
             if csf_events:
@@ -242,11 +248,41 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
     for i in range(warmup):
         step(steps + i)
     torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        # the timed steps as one HIP graph, replayed once untimed first
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(i, ev_t[i] + [None] * (NS - 1) if i in ev_t else None)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(steps):
+            step(i, ev_t[i] + [None] * (NS - 1) if i in ev_t else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # per-step durations (events at step boundaries only), for the median
+    ev_s = [hip.event() for _ in range(min(steps, 20) + 1)]
+    hip.record(ev_s[0])
+    for i in range(len(ev_s) - 1):
+        step(i)
+        hip.record(ev_s[i + 1])
+    torch.cuda.synchronize()
+    step_ms = np.array([hip.elapsed_ms(ev_s[i], ev_s[i + 1]) for i in range(len(ev_s) - 1)])
+    for e in ev_s:
+        hip.destroy(e)
+    if graph is not None:
+        # gate/up events from an eager pass over every step in order (a
+        # graph replay records none; running only the evented steps would
+        # leave the previous step's weight copy in the Infinity Cache)
+        for i in range(steps):
+            step(i, ev_t[i] + [None] * (NS - 1) if i in ev_t else None)
+        torch.cuda.synchronize()
+        del graph
     gu_idx = sorted(ev_t)
     gu_ms = np.array([hip.elapsed_ms(*ev_t[i]) for i in gu_idx])
     # stage breakdown: the first nb steps again, every boundary recorded
@@ -264,7 +300,8 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
         U = np.full(steps, float(torch.unique(ids).numel()))
     gu_bytes, dn_bytes = EXPERT_BYTES[fmt]
     ms = wall / steps * 1e3
-    r = dict(workload=name, tokens=T, ms_per_step=ms, tok_s=T / (ms * 1e-3),
+    r = dict(workload=name, tokens=T, graph=use_graph, ms_per_step=ms, tok_s=T / (ms * 1e-3),
+             ms_per_step_median=float(np.median(step_ms)),
              touched_experts=float(U.mean()),
              layer_GBps=float((U * (gu_bytes + dn_bytes)).mean() / (ms * 1e-3) / 1e9),
              gateup_ms=float(gu_ms.mean()), down_ms=float(stage_ms[:, 1].mean()),
@@ -273,12 +310,63 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
              down_GBps=float(np.mean(U[:nb] * dn_bytes / (stage_ms[:, 1] * 1e-3)) / 1e9),
              layer_TFLOPs=float(T * K * FLOP_PER_SLOT / (ms * 1e-3) / 1e12))
     r["gateup_frac_hbm"] = r["gateup_GBps"] * 1e9 / HBM_PEAK
+    r["gateup_TFLOPs"] = float(T * K * 2 * 2 * H * F / (gu_ms.mean() * 1e-3) / 1e12)
+    r["down_TFLOPs"] = float(T * K * 2 * H * F / (stage_ms[:, 1].mean() * 1e-3) / 1e12)
     if csf:
         r["csf_ms"] = float(csf_ms.mean())
         if csf_mode == "expand":
             cb = 2 * csf_bytes(F, H // 16) + csf_bytes(H, F // 16)
             r["csf_GBps"] = float(np.mean(U[:nb] * cb / (csf_ms * 1e-3)) / 1e9)
     return r
+
+
+def run_tiny(steps, warmup, dev):
+    """The tiny layer (8 tokens, hidden 256, 16 experts, top-2, SwiGLU width
+    128, int4-g128, fp16 x, router from a N(0, 0.02) weight): a step is
+    route + permute + forward. Launch-bound, so it is reported as latency,
+    eager and as a HIP graph replay."""
+    cfg = synth.CONFIGS["tiny"]
+    T, h, e, k, f = cfg["T"][0], cfg["H"], cfg["E"], cfg["K"], cfg["F"]
+    mats = []
+    for i, (n, kk) in enumerate(((f, h), (f, h), (h, f))):
+        mats.append(B.bank_int4(*synth.packed_int4_random(e, n, kk, 50 + i, dev)))
+    ffn = B.ffn(*mats)
+    x = synth.activations(T, h, "f16", 0).to(dev)
+    wT = torch.from_numpy(synth.router_weight_T(h, e, 0)).to(dev)
+    tm, ws_bytes = B.moe_forward_plan(ffn, T, k, x.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    rws = torch.empty(max(B.moe_route_workspace(T, e, True), 256), dtype=torch.uint8, device=dev)
+    perm = B.Perm(T, k, e, tm, dev)
+    out = torch.empty((T, h), dtype=torch.float32, device=dev)
+
+    def step():
+        B.moe_route_topk(k, x=x, router_wT=wT, ids=ids, w=w, ws=rws)
+        B.moe_permute(ids, e, tm, perm=perm)
+        B.moe_w4a16_forward(ffn, x, w, perm, out=out, ws=ws)
+
+    res = dict(workload="tiny T=8", tokens=T)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    res["us_per_step_eager"] = (time.perf_counter() - t0) / steps * 1e6
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            step()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    res["us_per_step_graph"] = (time.perf_counter() - t0) / steps * 1e6
+    res["tok_s"] = T / (res["us_per_step_graph"] * 1e-6)
+    return res
 
 
 class StackLayer:
@@ -388,40 +476,93 @@ def run_stack(layers, T, steps, warmup, hip, dev, use_graph=True):
                 layer_TFLOPs=float(flop / (ms * 1e-3) / 1e12))
 
 
-def cpu_baseline(dev_banks, n_tok=2):
-    """The oracle, as it stands, on a bounded sample of the decode workload:
-    n_tok tokens of a T=64 batch with their 8 experts each, dequantized from
-    the same packed int4 bytes in float64."""
+def _oracle_tokens(x, lg, wT, bias, n_tok, efn, router=True):
+    """The oracle on the first n_tok tokens: routing (the C router chain from
+    the router weight, or the given logits), the 8 experts of each token
+    dequantized by efn, SwiGLU and combine. Returns seconds."""
+    from oracle import layer as OL
+    from oracle import router as OR
+    t0 = time.perf_counter()
+    if router:
+        _, ids, w = OR.route(x=x[:n_tok].float().numpy(), wT=wT, bias=bias, K=K)
+    else:
+        _, ids, w = OR.route(logits=lg[:n_tok], K=K)
+    OL.moe_layer(x[:n_tok].float().numpy().astype(np.float64), ids, w, efn)
+    return time.perf_counter() - t0
+
+
+def _efn(mats, fmt):
+    from oracle import quant as OQ
+
+    def fn(e):
+        if fmt == "int4":
+            return tuple(OQ.dequant_int4(m._keep[0][e].cpu().numpy(),
+                                         m._keep[1][e].view(torch.int16).cpu().numpy()
+                                         .view(np.uint16)) for m in mats)
+        return tuple(OQ.dequant_nvfp4(m._keep[0][e].cpu().numpy(), m._keep[1][e].cpu().numpy(),
+                                      float(m._keep[2][e].cpu())) for m in mats)
+    return fn
+
+
+def cpu_baseline(int4, nv, n_tok=4):
+    """The oracle, as it stands, on bounded samples: n_tok tokens of the
+    decode T=64 batch (the headline), and n_tok tokens of the prefill batch
+    (routing by the C router chain), of the NVFP4 batch, and the whole tiny
+    layer. Each token's 8 experts are dequantized from the same packed bytes
+    the GPU streams, in float64; threads as numpy's BLAS uses them."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    lg = synth.router_logits(64, E, 1000)
+    x = synth.activations(64, H, "f16", 2)
+    dt = _oracle_tokens(x, lg, None, None, n_tok, _efn(int4[0]._keep, "int4"), router=False)
+    per = []
+    xp = synth.activations(n_tok, H, "bf16", 3)
+    wT = synth.router_weight_T(H, E, 3)
+    t = _oracle_tokens(xp, None, wT, None, n_tok, _efn(int4[0]._keep, "int4"))
+    per.append(dict(workload="prefill T=2048", tokens=n_tok, seconds=round(t, 2),
+                    tok_s=n_tok / t))
+    if nv is not None:
+        lgn = synth.router_logits(n_tok, E, 1000)
+        xn = synth.activations(n_tok, H, "bf16", 2)
+        t = _oracle_tokens(xn, lgn, None, None, n_tok, _efn(nv[0]._keep, "nvfp4"), router=False)
+        per.append(dict(workload="nvfp4 T=256", tokens=n_tok, seconds=round(t, 2),
+                        tok_s=n_tok / t))
+    from tests import fixtures as FX       # the tiny layer's oracle-quantized experts
+    cfg = synth.CONFIGS["tiny"]
+    host = []
+    for which, (n, k) in (("gate", (cfg["F"], cfg["H"])), ("up", (cfg["F"], cfg["H"])),
+                          ("down", (cfg["H"], cfg["F"]))):
+        host.append(FX.int4_bank_oracle(cfg["E"], n, k, 0, 0, which))
     from oracle import layer as OL
     from oracle import quant as OQ
     from oracle import router as OR
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    mats = dev_banks[0]._keep              # the gate, up, down descriptors
-    lg = synth.router_logits(64, E, 1000)[:n_tok]
-    x = synth.activations(64, H, "f16", 2)[:n_tok]
+    xt = synth.activations(8, cfg["H"], "f16", 0)
+    wTt = synth.router_weight_T(cfg["H"], cfg["E"], 0)
     t0 = time.perf_counter()
-    _, ids, w = OR.route(logits=lg, K=K)
-    cache = {}
-
-    def efn(e):
-        if e not in cache:
-            cache[e] = tuple(OQ.dequant_int4(m._keep[0][e].cpu().numpy(),
-                                             m._keep[1][e].view(torch.int16).cpu().numpy()
-                                             .view(np.uint16)) for m in mats)
-        return cache[e]
-    OL.moe_layer(x.float().numpy().astype(np.float64), ids, w, efn)
-    dt = time.perf_counter() - t0
-    return dict(value=n_tok / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+    _, ids, w = OR.route(x=xt.float().numpy(), wT=wTt, K=cfg["K"])
+    OL.moe_layer(xt.float().numpy().astype(np.float64), ids, w,
+                 lambda e: tuple(OQ.dequant_int4(q[e], sc[e]) for (q, sc) in host))
+    t = time.perf_counter() - t0
+    per.append(dict(workload="tiny T=8", tokens=8, seconds=round(t, 4), tok_s=8 / t))
+    return dict(value=n_tok / dt, unit="tokens/s", cores=cores, blas_threads=int(blas),
+                kind="oracle",
                 sample="%d tokens of the decode T=64 batch (route on given logits, 8 int4 "
                        "experts per token dequantized to float64, SwiGLU, combine); %.1f s"
-                       % (n_tok, dt))
+                       % (n_tok, dt),
+                per_config=per)
 
 
-def traffic_for(kernel):
+# Sources a kernel is built from: its counters stay valid while these are
+# unchanged.
+GEMV_SOURCES = ("gemv.hip", "decode.h", "stream.h", "common.h")
+GEMM_SOURCES = ("gemm.hip", "decode.h", "stream.h", "common.h")
+
+
+def traffic_for(kernel, files=GEMV_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -431,14 +572,9 @@ def traffic_for(kernel):
         rec = json.load(open(path)).get(kernel)
     except Exception:
         return None
-    if not rec or rec.get("source_sha") != source_sha():
+    if not rec or rec.get("source_sha") != source_sha(files):
         return None
     return rec.get("bytes_per_launch")
-
-
-# Sources the decode GEMV kernel is built from: its counters stay valid
-# while these are unchanged.
-GEMV_SOURCES = ("gemv.hip", "decode.h", "stream.h", "common.h")
 
 
 def source_sha(files=GEMV_SOURCES):
@@ -455,8 +591,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "nvfp4", "nvfp4-csf", "nvfp4-csf-expand", "int4-g32",
-                             "int4-asym", "int8", "stack"])
+                    choices=["decode", "decode-graph", "prefill", "prefill-zipf", "nvfp4",
+                             "nvfp4-csf", "nvfp4-csf-expand", "int4-g32", "int4-asym", "int8",
+                             "stack"])
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -485,11 +622,13 @@ def main():
 
     int4 = int4_banks(2, dev, 500)
     jobs = []
-    main_T = args.tokens or {"decode": 64, "prefill": 2048, "nvfp4": 256, "nvfp4-csf": 64,
+    main_T = args.tokens or {"decode": 64, "decode-graph": 64, "prefill": 2048,
+                             "prefill-zipf": 2048, "nvfp4": 256, "nvfp4-csf": 64,
                              "nvfp4-csf-expand": 64,
                              "int4-g32": 64, "int4-asym": 64, "int8": 64,
                              "stack": 4096}[args.workload]
-    spec = {"decode": ("f16", "logits", "int4"), "prefill": ("bf16", "weights", "int4"),
+    spec = {"decode": ("f16", "logits", "int4"), "decode-graph": ("f16", "logits", "int4"),
+            "prefill": ("bf16", "weights", "int4"), "prefill-zipf": ("bf16", "zipf", "int4"),
             "nvfp4": ("bf16", "logits", "nvfp4"), "nvfp4-csf": ("bf16", "logits", "nvfp4-csf"),
             "nvfp4-csf-expand": ("bf16", "logits", "nvfp4"),
             "int4-g32": ("f16", "logits", "int4-g32"), "int4-asym": ("f16", "logits", "int4-asym"),
@@ -497,7 +636,9 @@ def main():
             "stack": ("bf16", "weights", "int4")}
     jobs.append((args.workload, main_T))
     if not args.no_sweep:
-        for wl, T in (("decode", 1), ("decode", 8), ("decode", 64), ("prefill", 2048),
+        for wl, T in (("tiny", 8), ("decode", 1), ("decode", 8), ("decode", 64),
+                      ("decode-graph", 1), ("decode-graph", 8), ("decode-graph", 64),
+                      ("prefill", 2048), ("prefill-zipf", 2048),
                       ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("nvfp4-csf-expand", 64),
                       ("nvfp4-csf-expand", 256),
                       ("int4-g32", 64), ("int4-g32", 2048),
@@ -513,8 +654,12 @@ def main():
     stack = None
     results = []
     for wl, T in jobs:
-        act, rmode, fmt = spec[wl]
         steps = args.steps if (wl, T) == jobs[0] else max(10, args.steps // 2)
+        if wl == "tiny":
+            results.append(run_tiny(100, 10, dev))
+            print("# %s" % json.dumps(results[-1]), file=sys.stderr, flush=True)
+            continue
+        act, rmode, fmt = spec[wl]
         if wl == "stack":
             if stack is None:
                 stack = [StackLayer(l, dev) for l in range(8)]
@@ -537,7 +682,8 @@ def main():
                     nv_csf_in = csf_banks(nv, dev, 1900)
                 banks, csf, csf_mode = nv_csf_in[0], nv_csf_in[1], "index"
             results.append(run_layer("%s T=%d" % (wl, T), banks, T, act, rmode, steps,
-                                     args.warmup, hip, dev, fmt, csf, csf_mode))
+                                     args.warmup, hip, dev, fmt, csf, csf_mode,
+                                     use_graph=wl == "decode-graph"))
         print("# %s" % json.dumps(results[-1]), file=sys.stderr, flush=True)
 
     head = results[0]
@@ -552,7 +698,22 @@ def main():
                 traffic=traffic,
                 algorithmic_bytes_per_launch=round(head["touched_experts"] *
                                                    EXPERT_BYTES[fmt][0]))
-    cpu = None if args.no_cpu_baseline else cpu_baseline(int4)
+    # the prefill grouped GEMM (gate/up at T = 2048, uniform routing):
+    # MFMA fraction (the bound the pages' prefill figures are about) and the
+    # HBM fraction of the same launch
+    pre = next((r for r in results if r["workload"] == "prefill T=2048"), None)
+    roof_pre = None
+    if pre is not None:
+        gu_b = EXPERT_BYTES["int4"][0]
+        roof_pre = dict(bound="mfma", kernel="gemm_gateup_int4_bf16", unit="TFLOP/s",
+                        achieved=round(pre["gateup_TFLOPs"], 1), peak=MFMA_BF16_PEAK / 1e12,
+                        frac=round(pre["gateup_TFLOPs"] * 1e12 / MFMA_BF16_PEAK, 4),
+                        hbm_GBps=round(pre["gateup_GBps"], 1),
+                        hbm_frac=round(pre["gateup_frac_hbm"], 4),
+                        traffic=traffic_for("gemm_gateup_int4_bf16", GEMM_SOURCES),
+                        flop_per_launch=2048 * K * 2 * 2 * H * F,
+                        algorithmic_bytes_per_launch=round(pre["touched_experts"] * gu_b))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(int4, nv)
     line = {
         "metric": "W4A16 MoE layer tok/s; decode HBM GB/s %peak; prefill TFLOP/s %peak",
         "value": round(head["tok_s"], 2), "unit": "tokens/s", "n_gpus": 1,
@@ -564,6 +725,7 @@ def main():
                                                                       fmt, act),
                    "tokens": main_T, "experts": E, "top_k": K, "hidden": H, "width": F},
         "roofline": roof,
+        "roofline_prefill": roof_pre,
         "cpu_baseline": cpu,
         "sweep": results,
     }
