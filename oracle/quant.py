@@ -223,6 +223,42 @@ def quantize_nvfp4(W, group=NVFP4_GROUP):
     return codes, bs, gs
 
 
+def quantize_nvfp4_act(x, g, group=NVFP4_GROUP):
+    """NVFP4 quantization of activations (rows of x [..., k], 16-bit values
+    widened to float32) with the tensor's float32 global scale g > 0.
+
+    The pages give no rule for activations; the reading taken is the
+    weights' two-level rule (page "Step-5-Preview-NVFP4-Local", "Format":
+    E2M1 value x E4M3 block scale per 16 x a float32 scale, here the input
+    scale of the quantized layers, "Modifications" items 2-3), with every
+    decision taken in float32, the precision of the kernels:
+        D = 6 g;  per 16-block t = max|x| / D;  bs = E4M3(t), nearest,
+        ties to even, saturating at 448;  den = bs g;  v = x / den;
+        code = E2M1(v), nearest, ties to even, saturating at 6 (a zero
+        block scale gives code 0, a magnitude rounding to 0 gives +0),
+    each arithmetic step one float32 operation rounded to nearest even.
+    Returns (codes uint8 [..., k], bs float64 [..., k/16] E4M3 values,
+    xhat float64 [..., k] = e2m1 x bs, exact); the quantized activation is
+    xhat * g.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    g32 = np.float32(g)
+    k = x32.shape[-1]
+    assert k % group == 0 and g32 > 0
+    xb = x32.reshape(x32.shape[:-1] + (k // group, group))
+    D = np.float32(6.0) * g32
+    with np.errstate(over="ignore", under="ignore"):
+        t = np.max(np.abs(xb), axis=-1) / D                       # float32
+        bs = round_to_format(t.astype(np.float64), E4M3, saturate=True)
+        den = bs.astype(np.float32) * g32                         # float32
+        safe = np.where(den > 0, den, np.float32(1.0))
+        v = np.where(den[..., None] > 0, xb / safe[..., None], np.float32(0.0))
+    vq = round_to_format(v.astype(np.float64), E2M1, saturate=True)
+    codes = e2m1_encode(vq).reshape(x32.shape)
+    xhat = (vq * bs[..., None]).reshape(x32.shape) + 0.0       # -0 -> +0
+    return codes, bs, xhat
+
+
 def pack_nvfp4(codes):
     """codes [n, k] -> bytes [n, k/2]; the low nibble is the even input."""
     c = np.asarray(codes, dtype=np.uint8)
