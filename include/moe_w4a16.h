@@ -133,6 +133,9 @@ typedef struct {
     int64_t zero_point_expert_stride, zero_point_row_stride;
     const uint32_t *csf_exceptions;  /* MOE_W_NVFP4_CSF only, else NULL          */
     const int32_t *csf_row_index;    /* MOE_W_NVFP4_CSF only, else NULL          */
+    float input_scale;           /* NVFP4 forms: 0 = 16-bit inputs (W4A16); > 0 =
+                                    the inputs are NVFP4-quantized with this
+                                    float32 global scale (see moe_w4a16_forward) */
 } moe_weight_desc_t;
 
 /* The three projections of a SwiGLU bank: gate and up are [F][H], down is
@@ -165,7 +168,7 @@ typedef struct {
 /* Human-readable name of a status code (host, static storage). */
 const char *moe_status_string(int status);
 
-/* ABI version of this header: 4 (moe_abi_version returns it). */
+/* ABI version of this header: 5 (moe_abi_version returns it). */
 int moe_abi_version(void);
 
 /*
@@ -301,7 +304,19 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts,
  * out [T][H] in out_dtype (MOE_F32, MOE_F16 or MOE_BF16); ws: device
  * workspace of at least moe_forward_plan's ws_bytes, 256-byte aligned.
  * Accumulation is float32; h is rounded to act_dtype before the down
- * projection. Limits: 1 <= K <= min(E, 16); H and F multiples of the
+ * projection.
+ *
+ * Quantized inputs (page "Step-5-Preview-NVFP4-Local", "Modifications"
+ * items 2-3: the NVFP4 layers that keep an input scale quantize their
+ * activations, the W4A16 ones keep 16-bit inputs): when the experts are an
+ * NVFP4 bank (plain or CSF scales) whose input_scale is > 0, x is quantized
+ * with gate.input_scale (which must equal up.input_scale) as
+ * moe_quantize_nvfp4_act does, and h, after its rounding to act_dtype,
+ * with down.input_scale (which must then be > 0 too); each projection's
+ * accumulators are multiplied by its input scale with the global scale.
+ * The shared expert reads x unquantized (it stays BF16). Input scales are
+ * 0 or in [2^-100, 2^100]; any other combination is MOE_ERR_INVALID_ARG.
+ * Limits: 1 <= K <= min(E, 16); H and F multiples of the
  * format's group (128; 32 for MOE_W_INT4_G32 and NVFP4), at most 16384;
  * E <= 512.
  */
@@ -418,6 +433,26 @@ moe_status_t moe_rmsnorm(const float *x, const float *weight, float eps, int T, 
  */
 moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out,
                          void *stream);
+
+/*
+ * moe_quantize_nvfp4_act -- NVFP4 quantization of 16-bit activations with a
+ * per-tensor float32 global scale g = input_scale, as the quantized-input
+ * layers apply it (page "Step-5-Preview-NVFP4-Local", "Modifications" items
+ * 2-3; the rule for activations is not on the pages: it is the weights'
+ * two-level rule of the page's "Format" section, with every decision in
+ * float32). For each block of 16 consecutive elements of a row:
+ *   t  = max|x| / (6 g)                  (float32; 6 g rounded to float32)
+ *   bs = E4M3(t): nearest, ties to even, saturating at 448
+ *   code_i = E2M1(x_i / (bs g)): nearest, ties to even, saturating at 6;
+ *            0 when bs = 0; a magnitude that rounds to 0 gives +0
+ *   out_i  = e2m1(code_i) * bs           (exact in both 16-bit formats)
+ * so the quantized value of x_i is out_i * g.
+ * x [rows][k] and out [rows][k] in dtype (MOE_F16 or MOE_BF16), 16-byte
+ * aligned (out may equal x); k % 16 == 0, 16 <= k <= 16384; input_scale in
+ * [2^-100, 2^100]. rows == 0 is a no-op. Enqueues one kernel.
+ */
+moe_status_t moe_quantize_nvfp4_act(const void *x, int dtype, int64_t rows, int k,
+                                    float input_scale, void *out, void *stream);
 
 /*
  * moe_csf_expand -- the E4M3 block-scale bytes of an NVFP4 bank from their

@@ -22,7 +22,8 @@ EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_rou
            "moe_route_topk", "moe_permute_sizes",
            "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_w4a16_forward_profiled",
            "moe_round_activations", "moe_rmsnorm", "moe_dequant", "moe_csf_expand",
-           "moe_csf_row_index", "moe_norm_route", "moe_w4a16_forward_scratch")
+           "moe_csf_row_index", "moe_norm_route", "moe_w4a16_forward_scratch",
+           "moe_quantize_nvfp4_act")
 MOE_FORWARD_STAGES = 4
 MOE_FORWARD_SCRATCH_BYTES = 64 << 20
 
@@ -45,7 +46,8 @@ class WeightDesc(ctypes.Structure):
                 ("scale_expert_stride", ctypes.c_int64), ("scale_row_stride", ctypes.c_int64),
                 ("zero_point", ctypes.c_void_p),
                 ("zero_point_expert_stride", ctypes.c_int64), ("zero_point_row_stride", ctypes.c_int64),
-                ("csf_exceptions", ctypes.c_void_p), ("csf_row_index", ctypes.c_void_p)]
+                ("csf_exceptions", ctypes.c_void_p), ("csf_row_index", ctypes.c_void_p),
+                ("input_scale", ctypes.c_float)]
 
 
 class FfnDesc(ctypes.Structure):
@@ -87,6 +89,7 @@ def lib():
         L.moe_w4a16_forward_profiled.argtypes = L.moe_w4a16_forward.argtypes + [P(vp), i32]
         L.moe_w4a16_forward_scratch.argtypes = [P(FfnDesc), P(FfnDesc), vp, i32, i32, i32, vp,
                                                 P(PermDesc), vp, vp, i32, vp]
+        L.moe_quantize_nvfp4_act.argtypes = [vp, i32, i64, i32, ctypes.c_float, vp, vp]
         L.moe_round_activations.argtypes = [vp, i64, i32, vp, vp]
         L.moe_rmsnorm.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, vp]
         L.moe_dequant.argtypes = [P(WeightDesc), i32, vp, vp]
@@ -99,7 +102,7 @@ def lib():
                      "moe_w4a16_forward", "moe_w4a16_forward_profiled",
                      "moe_round_activations", "moe_rmsnorm", "moe_dequant",
                      "moe_csf_expand", "moe_csf_row_index", "moe_norm_route",
-                     "moe_w4a16_forward_scratch"):
+                     "moe_w4a16_forward_scratch", "moe_quantize_nvfp4_act"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -155,17 +158,19 @@ def bank_int8(qweight, scale):
     return d
 
 
-def bank_nvfp4(qweight, scale, global_scale):
-    """qweight uint8 [E, n, k/2], scale uint8 (E4M3) [E, n, k/16], global_scale float [E]."""
+def bank_nvfp4(qweight, scale, global_scale, input_scale=0.0):
+    """qweight uint8 [E, n, k/2], scale uint8 (E4M3) [E, n, k/16], global_scale
+    float [E]; input_scale > 0 quantizes the bank's inputs (NVFP4)."""
     E, n, kh = qweight.shape
     d = WeightDesc(MOE_W_NVFP4_G16, E, n, kh * 2, qweight.data_ptr(), scale.data_ptr(),
                    global_scale.data_ptr(), qweight.stride(0), qweight.stride(1),
                    scale.stride(0), scale.stride(1))
+    d.input_scale = float(input_scale)
     d._keep = (qweight, scale, global_scale)
     return d
 
 
-def bank_nvfp4_csf(qweight, fixed, exceptions, row_index, global_scale):
+def bank_nvfp4_csf(qweight, fixed, exceptions, row_index, global_scale, input_scale=0.0):
     """MOE_W_NVFP4_CSF: qweight uint8 [E, n, k/2], the CSF fixed tensor uint8
     [E, n/16, 16*(1+k/32)], exceptions int32/uint32 [m] (or None), the row
     index int32 [E, n+1] from moe_csf_row_index, global_scale float [E]."""
@@ -175,6 +180,7 @@ def bank_nvfp4_csf(qweight, fixed, exceptions, row_index, global_scale):
                    global_scale.data_ptr(), qweight.stride(0), qweight.stride(1),
                    fixed.stride(0), 0, None, 0, 0,
                    exceptions.data_ptr() if m else None, row_index.data_ptr())
+    d.input_scale = float(input_scale)
     d._keep = (qweight, fixed, exceptions, row_index, global_scale)
     return d
 
@@ -329,6 +335,17 @@ def moe_w4a16_forward_scratch(experts, x, topk_w, perm, residual=None, out_dtype
         ctypes.byref(experts), ctypes.byref(shared) if shared is not None else None, _ptr(x),
         _DT[x.dtype], T, K, _ptr(topk_w), ctypes.byref(pd), _ptr(residual), _ptr(out),
         _DT[out.dtype], _stream(dev)), "moe_w4a16_forward_scratch")
+    return out
+
+
+def moe_quantize_nvfp4_act(x, input_scale, out=None):
+    """x [rows, k] float16 / bfloat16 -> e2m1 x bs values [rows, k], same dtype
+    (the quantized activation is that times input_scale)."""
+    rows, k = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().moe_quantize_nvfp4_act(_ptr(x), _DT[x.dtype], rows, k, float(input_scale),
+                                        _ptr(out), _stream(x.device)), "moe_quantize_nvfp4_act")
     return out
 
 

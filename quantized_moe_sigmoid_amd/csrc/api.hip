@@ -44,6 +44,8 @@ moe_status_t launch_norm_router_logits(const float *res, const float *gain, floa
                                        void *a_out, float *logits, hipStream_t s);
 moe_status_t launch_rmsnorm(const float *x, const float *w, float eps, int T, int H, int dtype,
                             void *out, hipStream_t s);
+moe_status_t launch_act_quant(const void *in, int dtype, int64_t rows, int k, float g,
+                              void *out, const int32_t *row_slot, hipStream_t s);
 DenseSplit dense_plan(int T, int H, int F);
 bool dense_shape_ok(int H, int F);
 int gemv_tile_m();
@@ -68,9 +70,16 @@ int64_t perm_max_rows(int T, int K, int E, int tile_m) {
     return n + (n < E ? n : E) * (int64_t)(tile_m - 1);
 }
 
+// An input scale of the NVFP4-activation forms: 0 (16-bit inputs) or a
+// finite float32 in [2^-100, 2^100] (so 6 g and every bs g stay normal).
+bool input_scale_ok(float g) { return g == 0.0f || (g >= 0x1p-100f && g <= 0x1p100f); }
+
 // A quantized bank of E matrices [n][k]: format rules and alignment.
 moe_status_t check_bank(const moe_weight_desc_t &d, int E, int n, int k) {
     if (d.num_experts != E || d.n != n || d.k != k) return MOE_ERR_INVALID_ARG;
+    if (!input_scale_ok(d.input_scale)) return MOE_ERR_INVALID_ARG;
+    if (d.input_scale != 0.0f && d.fmt != MOE_W_NVFP4_G16 && d.fmt != MOE_W_NVFP4_CSF)
+        return MOE_ERR_INVALID_ARG;
     if (!d.qweight || !d.scale) return MOE_ERR_INVALID_ARG;
     if (n <= 0 || k <= 0 || n > kMaxDim || k > kMaxDim) return MOE_ERR_INVALID_ARG;
     if (!aligned(d.qweight, 16) || d.qweight_row_stride % 16 || d.qweight_expert_stride % 16)
@@ -124,6 +133,11 @@ moe_status_t check_experts(const moe_ffn_desc_t *ex, int *E, int *H, int *F) {
     if ((st = check_bank(ex->gate, e, f, h)) != MOE_OK) return st;
     if ((st = check_bank(ex->up, e, f, h)) != MOE_OK) return st;
     if ((st = check_bank(ex->down, e, h, f)) != MOE_OK) return st;
+    // quantized inputs: gate and up read the same x (one input scale), and
+    // the down projection's input is quantized too
+    if (ex->gate.input_scale != ex->up.input_scale ||
+        (ex->gate.input_scale > 0.0f) != (ex->down.input_scale > 0.0f))
+        return MOE_ERR_INVALID_ARG;
     *E = e; *H = h; *F = f;
     return MOE_OK;
 }
@@ -167,7 +181,7 @@ struct FwdPlan {
     int tile_m;
     int64_t max_rows, max_tiles;
     size_t off_h, off_y, off_xperm, off_xsum, off_hsum;
-    size_t off_sh_h, off_sh_y, off_sh_part, off_csf, total;
+    size_t off_sh_h, off_sh_y, off_sh_part, off_csf, off_xq, total;
 };
 
 // Kernel choice by batch shape: with few slots per expert the dequantizing
@@ -241,7 +255,10 @@ FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F
     // MFMA path, compressed NVFP4 scales: every routed expert's E4M3 block
     // scales of gate, up and down, expanded ([E][n][k/16] each)
     const bool csf = p.mfma && ex.gate.fmt == MOE_W_NVFP4_CSF;
-    p.total = p.off_csf + (csf ? csf_bytes(ex.gate) + csf_bytes(ex.up) + csf_bytes(ex.down) : 0);
+    p.off_xq = p.off_csf + (csf ? csf_bytes(ex.gate) + csf_bytes(ex.up) + csf_bytes(ex.down) : 0);
+    // quantized inputs: the quantized x [T][H] (16-bit values e2m1 x bs)
+    const bool a4 = ex.gate.input_scale > 0.0f;
+    p.total = p.off_xq + (a4 ? align256((size_t)T * H * 2) : 0);
     return p;
 }
 
@@ -260,7 +277,7 @@ const char *moe_status_string(int status) {
     }
 }
 
-int moe_abi_version(void) { return 4; }
+int moe_abi_version(void) { return 5; }
 
 static moe_status_t check_router(const void *x, int x_dtype, const float *wT, int T, int H,
                                  int E) {
@@ -386,8 +403,28 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     void *h = w + p.off_h;
     float *y = (float *)(w + p.off_y);
     if ((st = mark(0)) != MOE_OK) return st;
+    // quantized inputs (NVFP4 banks with input scales): x is quantized with
+    // the gate/up input scale before the experts run, and h in place with
+    // the down input scale between the two projections; the kernels
+    // multiply their accumulators by the input scale with the global scale
+    const bool a4 = experts->gate.input_scale > 0.0f;
+    const void *xin = x;
+    if (a4) {
+        void *xq = w + p.off_xq;
+        st = launch_act_quant(x, act_dtype, T, H, experts->gate.input_scale, xq, nullptr, s);
+        if (st != MOE_OK) return st;
+        xin = xq;
+    }
+    auto between = [&](int i) -> moe_status_t {
+        moe_status_t r = mark(i);
+        if (r == MOE_OK && i == 1 && a4)
+            r = launch_act_quant(h, act_dtype, p.max_rows, F, experts->down.input_scale, h,
+                                 perm->sorted_slots, s);
+        return r;
+    };
     const std::function<moe_status_t(int)> mk =
-        events ? std::function<moe_status_t(int)>(mark) : std::function<moe_status_t(int)>();
+        events || a4 ? std::function<moe_status_t(int)>(between)
+                     : std::function<moe_status_t(int)>();
     moe_ffn_desc_t ex = *experts;
     if (p.mfma && ex.gate.fmt == MOE_W_NVFP4_CSF) {
         // prefill sizes: the routed experts' compressed scales expanded into
@@ -407,10 +444,11 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
             sc += csf_bytes(*d);
         }
     }
-    st = p.mfma ? launch_gemm_forward(ex, x, act_dtype, T, K, *perm, (int)p.max_tiles, h, y,
+    st = p.mfma ? launch_gemm_forward(ex, xin, act_dtype, T, K, *perm, (int)p.max_tiles, h, y,
                                       w + p.off_xperm, (float *)(w + p.off_xsum),
                                       (float *)(w + p.off_hsum), s, mk)
-                : launch_gemv_forward(*experts, x, act_dtype, K, *perm, (int)p.max_tiles, h, y, s, mk);
+                : launch_gemv_forward(*experts, xin, act_dtype, K, *perm, (int)p.max_tiles, h, y,
+                                      s, mk);
     if (st != MOE_OK) return st;
     float *ysh = shared ? (float *)(w + p.off_sh_y) : nullptr;
     if (shared) {
@@ -546,6 +584,15 @@ moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out, voi
     if (st != MOE_OK) return st;
     if (!aligned(out, 16)) return MOE_ERR_INVALID_ARG;
     return launch_dequant(*w, expert, out, (hipStream_t)stream);
+}
+
+moe_status_t moe_quantize_nvfp4_act(const void *x, int dtype, int64_t rows, int k,
+                                    float input_scale, void *out, void *stream) {
+    if (rows < 0 || k < 16 || k % 16 || k > kMaxDim || !is_act(dtype)) return MOE_ERR_INVALID_ARG;
+    if (!(input_scale > 0.0f) || !input_scale_ok(input_scale)) return MOE_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_OK;
+    if (!x || !out || !aligned(x, 16) || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+    return launch_act_quant(x, dtype, rows, k, input_scale, out, nullptr, (hipStream_t)stream);
 }
 
 moe_status_t moe_csf_expand(const uint8_t *fixed, const uint32_t *exceptions,

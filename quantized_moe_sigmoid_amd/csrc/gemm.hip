@@ -97,6 +97,8 @@ struct GemmMat {
     int64_t qe, qr, se, sr;
     const uint8_t *z;                            // asymmetric int4: zero points [E][n][k/128]
     int64_t ze, zr;
+    float xs;                                    // NVFP4 with quantized inputs: the input
+                                                 // scale (else 1), with the global scale
 };
 
 template <int ACT>
@@ -502,8 +504,8 @@ __global__ void __launch_bounds__(kGemmThreads)
     const int half = cx.half;
     // NVFP4: the global scale; int4-g128: the last group's scale (the
     // accumulators are kept in its units); int4-g32: 1 (scales in the operands)
-    const float ga = FMT == MOE_W_NVFP4_G16 ? A.gs[e] : cx.sprev_a;
-    const float gb = FMT == MOE_W_NVFP4_G16 ? Bm.gs[e] : cx.sprev_b;
+    const float ga = FMT == MOE_W_NVFP4_G16 ? A.gs[e] * A.xs : cx.sprev_a;
+    const float gb = FMT == MOE_W_NVFP4_G16 ? Bm.gs[e] * Bm.xs : cx.sprev_b;
     float *hs = (float *)abuf0;                    // [64 rows][128 cols] for the row sums
     // position of column c inside the pair-permuted layout of its 8-group
     // (int4 MFMA path only): (c0 c4 c1 c5 c2 c6 c3 c7)
@@ -577,7 +579,7 @@ inline GemmMat gemm_mat(const moe_weight_desc_t &d) {
     return GemmMat{(const uint8_t *)d.qweight, (const uint8_t *)d.scale, d.global_scale,
                    d.qweight_expert_stride, d.qweight_row_stride, d.scale_expert_stride,
                    d.scale_row_stride, d.zero_point, d.zero_point_expert_stride,
-                   d.zero_point_row_stride};
+                   d.zero_point_row_stride, d.input_scale > 0.0f ? d.input_scale : 1.0f};
 }
 
 template <int ACT, int FMT>

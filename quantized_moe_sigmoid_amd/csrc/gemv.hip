@@ -48,6 +48,7 @@ struct GemvMat {                 // one projection bank, byte addressed
     int64_t ze, zr;
     const uint32_t *xc;          // NVFP4_CSF: exceptions and their row index
     const int32_t *ri;
+    float xs;                    // NVFP4 with quantized inputs: the input scale (else 1)
 };
 
 // NVFP4_CSF: the two scale bytes of chunk c (blocks p0 = r*C + 2c, p0 + 1
@@ -482,8 +483,8 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
     for (int t = 0; t < TM; ++t) acc_a[t] = acc_b[t] = 0.0f;
     float ga = 1.0f, gb = 1.0f;
     if (is_nvfp4(FMT)) {
-        ga = A.gs[e];
-        if (GATEUP) gb = B.gs[e];
+        ga = A.gs[e] * A.xs;
+        if (GATEUP) gb = B.gs[e] * B.xs;
     }
     // end of a pass: reduce the LPR partial sums of each row, store, reset
     auto finish = [&](int ps) {
@@ -624,7 +625,8 @@ inline GemvMat gemv_mat(const moe_weight_desc_t &d) {
     return GemvMat{(const uint8_t *)d.qweight, (const uint8_t *)d.scale, d.global_scale,
                    d.qweight_expert_stride, d.qweight_row_stride, d.scale_expert_stride,
                    d.scale_row_stride, d.zero_point, d.zero_point_expert_stride,
-                   d.zero_point_row_stride, d.csf_exceptions, d.csf_row_index};
+                   d.zero_point_row_stride, d.csf_exceptions, d.csf_row_index,
+                   d.input_scale > 0.0f ? d.input_scale : 1.0f};
 }
 
 // Activation units, chunk sums (rounded up to 16 bytes) and the staging

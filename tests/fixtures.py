@@ -223,12 +223,14 @@ def dequant_fn(host, fmt="int4"):
     return fn
 
 
-def oracle_layer_streamed(x16, ids, w, expert_fn, shared=None, residual=None, threads=16):
+def oracle_layer_streamed(x16, ids, w, expert_fn, shared=None, residual=None, threads=16,
+                          h_fn=None):
     """The oracle's layer (oracle.layer) on rows x16 [n, H] with routing ids
     [n, K] and weights w [n, K]: every expert the rows reach is dequantized
     once by expert_fn, its slots evaluated and its weights dropped, so the
     memory held stays a few experts'. Experts run on a thread pool (numpy
-    releases the GIL in its array operations); each slot's value depends
+    releases the GIL in its array operations); h_fn as in oracle.layer.
+    Each slot's value depends
     only on its own token and expert, so the order of the experts does not
     change any result."""
     from concurrent.futures import ThreadPoolExecutor
@@ -242,7 +244,7 @@ def oracle_layer_streamed(x16, ids, w, expert_fn, shared=None, residual=None, th
     def work(e):
         t_idx, k_idx = np.nonzero(ids == e)
         Wg, Wu, Wd = expert_fn(int(e))
-        return t_idx, k_idx, OL.swiglu_ffn(x[t_idx], Wg, Wu, Wd)
+        return t_idx, k_idx, OL.swiglu_ffn(x[t_idx], Wg, Wu, Wd, h_fn)
 
     with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
         for t_idx, k_idx, out in ex.map(work, np.unique(ids)):

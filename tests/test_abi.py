@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
     assert B.status_string(0) == "MOE_OK"
     assert B.status_string(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
     assert B.status_string(99) == "MOE_ERR_UNKNOWN"
@@ -484,3 +484,40 @@ def test_int4_variant_bank_errors(L):
     f = B.FfnDesc(_bank_v(G32, 352, 1536, 4096), _bank(B.MOE_W_INT4_G128, 352, 1536, 4096),
                   _bank_v(G32, 352, 4096, 1536))
     assert _plan(f)[0] == B.MOE_ERR_INVALID_ARG
+
+
+def test_input_scale_rules(L):
+    """Quantized inputs: NVFP4 banks only, gate and up with one input scale,
+    the down projection quantized too; scales 0 or in [2^-100, 2^100]; the
+    plan holds the quantized x."""
+    f = _ffn(B.MOE_W_NVFP4_G16)
+    st, tm, ws0 = _plan(f, T=8, act=B.MOE_BF16)
+    assert st == B.MOE_OK
+    for b in (f.gate, f.up, f.down):
+        b.input_scale = 0.01
+    st, tm, ws1 = _plan(f, T=8, act=B.MOE_BF16)
+    assert st == B.MOE_OK and ws1 >= ws0 + 8 * 4096 * 2
+    f.up.input_scale = 0.02                                   # gate and up differ
+    assert _plan(f, T=8, act=B.MOE_BF16)[0] == B.MOE_ERR_INVALID_ARG
+    f.up.input_scale = 0.01
+    f.down.input_scale = 0.0                                  # h left unquantized
+    assert _plan(f, T=8, act=B.MOE_BF16)[0] == B.MOE_ERR_INVALID_ARG
+    for bad in (-1.0, 2.0 ** -101, 2.0 ** 101, float("inf"), float("nan")):
+        for b in (f.gate, f.up, f.down):
+            b.input_scale = bad
+        assert _plan(f, T=8, act=B.MOE_BF16)[0] == B.MOE_ERR_INVALID_ARG, bad
+    g = _ffn(B.MOE_W_INT4_G128)                               # not an NVFP4 bank
+    for b in (g.gate, g.up, g.down):
+        b.input_scale = 0.01
+    assert _plan(g, T=8)[0] == B.MOE_ERR_INVALID_ARG
+
+
+def test_quantize_nvfp4_act_validation(L):
+    Q = L.moe_quantize_nvfp4_act
+    x = ctypes.c_void_p(FAKE)
+    assert Q(x, B.MOE_BF16, 4, 24, 0.1, x, None) == B.MOE_ERR_INVALID_ARG     # k % 16
+    assert Q(x, B.MOE_BF16, 4, 32, 0.0, x, None) == B.MOE_ERR_INVALID_ARG     # scale 0
+    assert Q(x, B.MOE_BF16, 4, 32, 2.0 ** 101, x, None) == B.MOE_ERR_INVALID_ARG
+    assert Q(x, B.MOE_F32, 4, 32, 0.1, x, None) == B.MOE_ERR_INVALID_ARG      # dtype
+    assert Q(ctypes.c_void_p(FAKE + 8), B.MOE_BF16, 4, 32, 0.1, x, None) == B.MOE_ERR_INVALID_ARG
+    assert Q(None, B.MOE_BF16, 0, 32, 0.1, None, None) == B.MOE_OK            # no-op
