@@ -17,8 +17,8 @@ event drains the stream); the other stages' durations come from a separate,
 untimed pass over the same inputs with every stage boundary recorded.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--workload decode|prefill|nvfp4|nvfp4-csf|nvfp4-csf-expand|int4-g32|
-                              int4-asym|int8|stack]
+                  [--workload decode|decode-graph|prefill|prefill-zipf|nvfp4|nvfp4-csf|
+                              nvfp4-csf-expand|nvfp4-a4|int4-g32|int4-asym|int8|stack]
                   [--tokens T] [--no-sweep] [--no-cpu-baseline]
 """
 import argparse
@@ -62,7 +62,8 @@ EXPERT_BYTES = {"int4": (INT4_GATEUP_BYTES, INT4_DOWN_BYTES),
                 "int4-g32": (INT4_G32_GATEUP_BYTES, INT4_G32_DOWN_BYTES),
                 "int4-asym": (INT4_ASYM_GATEUP_BYTES, INT4_ASYM_DOWN_BYTES),
                 "int8": (INT8_GATEUP_BYTES, INT8_DOWN_BYTES),
-                "nvfp4-csf": (NVFP4_CSF_GATEUP_BYTES, NVFP4_CSF_DOWN_BYTES)}
+                "nvfp4-csf": (NVFP4_CSF_GATEUP_BYTES, NVFP4_CSF_DOWN_BYTES),
+                "nvfp4-a4": (NVFP4_GATEUP_BYTES, NVFP4_DOWN_BYTES)}
 FLOP_PER_SLOT = 3 * 2 * H * F
 # Timed steps that record the gate/up kernel's events: every recorded HIP
 # event drains the stream for a few microseconds, so only every
@@ -159,6 +160,18 @@ def nvfp4_banks(copies, dev, seed0):
         f.code_tensors = [m._keep[0] for m in mats]
         f.gs_tensors = [m._keep[2] for m in mats]
         out.append(f)
+    return out
+
+
+def a4_banks(nv, g_x, g_h):
+    """The NVFP4 banks `nv` with quantized inputs: input scale g_x for gate
+    and up, g_h for down."""
+    out = []
+    for bank in nv:
+        mats = [B.bank_nvfp4(q, s, g, input_scale=(g_h if i == 2 else g_x))
+                for i, (q, s, g) in enumerate(zip(bank.code_tensors, bank.scale_tensors,
+                                                   bank.gs_tensors))]
+        out.append(B.ffn(*mats))
     return out
 
 
@@ -592,8 +605,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "decode-graph", "prefill", "prefill-zipf", "nvfp4",
-                             "nvfp4-csf", "nvfp4-csf-expand", "int4-g32", "int4-asym", "int8",
-                             "stack"])
+                             "nvfp4-csf", "nvfp4-csf-expand", "nvfp4-a4", "int4-g32",
+                             "int4-asym", "int8", "stack"])
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -622,7 +635,7 @@ def main():
 
     int4 = int4_banks(2, dev, 500)
     jobs = []
-    main_T = args.tokens or {"decode": 64, "decode-graph": 64, "prefill": 2048,
+    main_T = args.tokens or {"decode": 64, "decode-graph": 64, "prefill": 2048, "nvfp4-a4": 256,
                              "prefill-zipf": 2048, "nvfp4": 256, "nvfp4-csf": 64,
                              "nvfp4-csf-expand": 64,
                              "int4-g32": 64, "int4-asym": 64, "int8": 64,
@@ -630,6 +643,7 @@ def main():
     spec = {"decode": ("f16", "logits", "int4"), "decode-graph": ("f16", "logits", "int4"),
             "prefill": ("bf16", "weights", "int4"), "prefill-zipf": ("bf16", "zipf", "int4"),
             "nvfp4": ("bf16", "logits", "nvfp4"), "nvfp4-csf": ("bf16", "logits", "nvfp4-csf"),
+            "nvfp4-a4": ("bf16", "logits", "nvfp4-a4"),
             "nvfp4-csf-expand": ("bf16", "logits", "nvfp4"),
             "int4-g32": ("f16", "logits", "int4-g32"), "int4-asym": ("f16", "logits", "int4-asym"),
             "int8": ("f16", "logits", "int8"),
@@ -640,7 +654,7 @@ def main():
                       ("decode-graph", 1), ("decode-graph", 8), ("decode-graph", 64),
                       ("prefill", 2048), ("prefill-zipf", 2048),
                       ("nvfp4", 1), ("nvfp4", 256), ("nvfp4-csf", 64), ("nvfp4-csf-expand", 64),
-                      ("nvfp4-csf-expand", 256),
+                      ("nvfp4-csf-expand", 256), ("nvfp4-a4", 1), ("nvfp4-a4", 256),
                       ("int4-g32", 64), ("int4-g32", 2048),
                       ("int4-asym", 64), ("int4-asym", 2048), ("int8", 64), ("int8", 2048),
                       ("stack", 32),
@@ -666,12 +680,18 @@ def main():
             results.append(run_stack(stack, T, max(5, steps // 4), max(2, args.warmup // 4),
                                      hip, dev, use_graph=not args.no_graph))
         else:
-            if fmt in ("nvfp4", "nvfp4-csf") and nv is None:
+            if fmt in ("nvfp4", "nvfp4-csf", "nvfp4-a4") and nv is None:
                 nv = nvfp4_banks(2, dev, 900)
             if fmt in ("int4-g32", "int4-asym", "int8") and fmt not in variants:
                 variants[fmt] = variant_banks(
                     2, dev, {"int4-g32": 2000, "int4-asym": 2100, "int8": 2200}[fmt], fmt)
             banks = int4 if fmt == "int4" else (nv if fmt == "nvfp4" else variants.get(fmt))
+            if fmt == "nvfp4-a4":
+                # input scales: x's from the largest activation of the decode
+                # batches (N(0, 1) in bf16), h's 2^-7 (the h of these weights
+                # stays below 6 x 448 x 2^-7 = 21)
+                g_x = float(np.float32(5.5 / (6 * 448)))
+                banks = a4_banks(nv, g_x, 2.0 ** -7)
             csf, csf_mode = None, "expand"
             if wl == "nvfp4-csf-expand":
                 if nv_csf is None:
