@@ -26,6 +26,10 @@ moe_status_t launch_csf_row_index(const uint32_t *exceptions, int64_t n, const i
 moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
                                  hipStream_t s, const std::function<moe_status_t(int)> &mark);
+bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act);
+moe_status_t launch_gemv_mx_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
+                                    const moe_perm_t &p, int max_tiles, void *h, float *y,
+                                    hipStream_t s, const std::function<moe_status_t(int)> &mark);
 moe_status_t launch_combine(const float *y, const int32_t *slot_to_row, const float *w, int T,
                             int K, int H, const float *shared, const float *residual, void *out,
                             int out_dtype, hipStream_t s);
@@ -447,8 +451,11 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     st = p.mfma ? launch_gemm_forward(ex, xin, act_dtype, T, K, *perm, (int)p.max_tiles, h, y,
                                       w + p.off_xperm, (float *)(w + p.off_xsum),
                                       (float *)(w + p.off_hsum), s, mk)
-                : launch_gemv_forward(*experts, xin, act_dtype, K, *perm, (int)p.max_tiles, h, y,
-                                      s, mk);
+         : gemv_mx_supported(*experts, act_dtype)
+             ? launch_gemv_mx_forward(*experts, xin, act_dtype, K, *perm, (int)p.max_tiles, h, y,
+                                      s, mk)
+             : launch_gemv_forward(*experts, xin, act_dtype, K, *perm, (int)p.max_tiles, h, y, s,
+                                   mk);
     if (st != MOE_OK) return st;
     float *ysh = shared ? (float *)(w + p.off_sh_y) : nullptr;
     if (shared) {

@@ -40,17 +40,6 @@ namespace moe {
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 
-struct GemvMat {                 // one projection bank, byte addressed
-    const uint8_t *q, *s;
-    const float *gs;             // NVFP4 global scale [E] or null
-    int64_t qe, qr, se, sr;      // expert / row strides (bytes)
-    const uint8_t *z;            // asymmetric int4 zero points or null
-    int64_t ze, zr;
-    const uint32_t *xc;          // NVFP4_CSF: exceptions and their row index
-    const int32_t *ri;
-    float xs;                    // NVFP4 with quantized inputs: the input scale (else 1)
-};
-
 // NVFP4_CSF: the two scale bytes of chunk c (blocks p0 = r*C + 2c, p0 + 1
 // of its row): base + code, or an exception's byte. ex0 / ex1: exceptions
 // held in registers (0xFFFFFFFF: none; a 24-bit position never reaches
@@ -621,27 +610,12 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
 constexpr int kGemvLPR = 8;
 constexpr int kGemvTM = 4;
 
-inline GemvMat gemv_mat(const moe_weight_desc_t &d) {
-    return GemvMat{(const uint8_t *)d.qweight, (const uint8_t *)d.scale, d.global_scale,
-                   d.qweight_expert_stride, d.qweight_row_stride, d.scale_expert_stride,
-                   d.scale_row_stride, d.zero_point, d.zero_point_expert_stride,
-                   d.zero_point_row_stride, d.csf_exceptions, d.csf_row_index,
-                   d.input_scale > 0.0f ? d.input_scale : 1.0f};
-}
-
 // Activation units, chunk sums (rounded up to 16 bytes) and the staging
 // dummy area (64 units + 64 floats).
 template <int LPR, int TM, int CI>
 inline size_t gemv_lds_bytes(int kin) {
     return (size_t)TM * xs_units_pad<LPR, CI>(kin) * 16 + ((size_t)TM * (kin / CI) + 3) / 4 * 16 +
            (size_t)kWave * 16 + (size_t)kWave * 4;
-}
-
-template <typename Kern>
-inline void allow_lds(Kern k, size_t lds) {
-    if (lds > 65536)
-        (void)hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)lds);
 }
 
 template <int ACT, int FMT>

@@ -23,5 +23,31 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+struct GemvMat {                 // one projection bank, byte addressed
+    const uint8_t *q, *s;
+    const float *gs;             // NVFP4 global scale [E] or null
+    int64_t qe, qr, se, sr;      // expert / row strides (bytes)
+    const uint8_t *z;            // asymmetric int4 zero points or null
+    int64_t ze, zr;
+    const uint32_t *xc;          // NVFP4_CSF: exceptions and their row index
+    const int32_t *ri;
+    float xs;                    // NVFP4 with quantized inputs: the input scale (else 1)
+};
+
+inline GemvMat gemv_mat(const moe_weight_desc_t &d) {
+    return GemvMat{(const uint8_t *)d.qweight, (const uint8_t *)d.scale, d.global_scale,
+                   d.qweight_expert_stride, d.qweight_row_stride, d.scale_expert_stride,
+                   d.scale_row_stride, d.zero_point, d.zero_point_expert_stride,
+                   d.zero_point_row_stride, d.csf_exceptions, d.csf_row_index,
+                   d.input_scale > 0.0f ? d.input_scale : 1.0f};
+}
+
+// Work groups that need more than 64 KB of LDS must say so before launch.
+template <typename Kern>
+inline void allow_lds(Kern k, size_t lds) {
+    if (lds > 65536)
+        (void)hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+}
 
 }  // namespace moe
