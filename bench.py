@@ -572,7 +572,19 @@ def cpu_baseline(int4, nv, n_tok=4):
 # Sources a kernel is built from: its counters stay valid while these are
 # unchanged.
 GEMV_SOURCES = ("gemv.hip", "decode.h", "stream.h", "common.h")
+GEMV_MFMA_SOURCES = ("gemv_mfma.hip", "decode.h", "stream.h", "common.h")
 GEMM_SOURCES = ("gemm.hip", "decode.h", "stream.h", "common.h")
+
+
+def decode_kernel(fmt, act, T):
+    """The gate/up kernel a batch of T tokens runs at the layer's shape: the
+    grouped GEMM from T * top-k >= 4 * experts slots on, below that the MFMA
+    GEMV for int4-g128 (both forms) and the dot2 GEMV for the others."""
+    if T * K >= 4 * E:
+        return "gemm_gateup_%s_%s" % (fmt, act), GEMM_SOURCES
+    if fmt in ("int4", "int4-asym"):
+        return "gemv_mfma_gateup_%s_%s" % (fmt, act), GEMV_MFMA_SOURCES
+    return "gemv_gateup_%s_%s" % (fmt, act), GEMV_SOURCES
 
 
 def traffic_for(kernel, files=GEMV_SOURCES):
@@ -711,8 +723,8 @@ def main():
         print(json.dumps({"workload": "stack", "result": head}))
         return
     act, rmode, fmt = spec[args.workload]
-    kern = "gemv_gateup_%s_%s" % (fmt, act)
-    traffic = traffic_for(kern)
+    kern, kern_src = decode_kernel(fmt, act, main_T)
+    traffic = traffic_for(kern, kern_src)
     roof = dict(bound="hbm", kernel=kern, achieved=round(head["gateup_GBps"], 1),
                 peak=HBM_PEAK / 1e9, unit="GB/s", frac=round(head["gateup_frac_hbm"], 4),
                 traffic=traffic,
