@@ -164,6 +164,151 @@ __global__ void __launch_bounds__(kDnThreads) dense_kernel(
     }
 }
 
+// Small batches (T <= 32) at the layer's shape: v_mfma_f32_16x16x32_bf16
+// with the tokens as the A operand (two 16-token blocks) and 16 weight rows
+// as B. A work group owns BPW = 4 / KS blocks of 16 rows and one slice of
+// KS * NSW * 32 inputs (blockIdx.y); the KS waves of a row block take NSW
+// consecutive 32-input steps each and meet in LDS at the end (added in
+// input order). A step's 16 rows x 64 bytes are loaded four lanes per row
+// (lane 4 r + c: row r, bytes 16 c) and pass through a per-wave LDS tile
+// into the MFMA layout (lane 16 c + r: row r, bytes 16 c; loaded that way
+// directly, every 16 lanes of a load would touch 16 cache lines); R steps
+// are in flight per lane and matrix. The slice's inputs of the T tokens are
+// staged in LDS once. Output: float32 sums [slice][T][ncols] (gate at column
+// c, up at n_rows + c), added and SwiGLU'd by swiglu_reduce_kernel, or the
+// down projection's y when there is one slice.
+constexpr int kDxWaves = 4, kDxThreads = kDxWaves * 64;
+
+__host__ __device__ constexpr int dx_upad(int kz) { return kz / 8 + 1; }
+
+inline size_t dense_small_lds(int kz, int nm, int ks) {
+    return (size_t)32 * dx_upad(kz) * 16 + (size_t)kDxWaves * 1024 +
+           (ks > 1 ? (size_t)kDxWaves * nm * 2 * 64 * 16 : 0);
+}
+
+template <bool GATEUP, int KS, int NSW, int R>
+__global__ void __launch_bounds__(kDxThreads) dense_small_kernel(
+    const uint8_t *__restrict__ wa, int64_t ra, const uint8_t *__restrict__ wb, int64_t rb,
+    int n_rows, int kin, const uint16_t *__restrict__ xin, int T, float *__restrict__ out) {
+    constexpr int NM = GATEUP ? 2 : 1, BPW = kDxWaves / KS, KZ = KS * NSW * 32;
+    constexpr int UPAD = dx_upad(KZ), UNITS = KZ / 8;
+    static_assert(kDxWaves % KS == 0 && NSW % R == 0 && (32 * UNITS) % kDxThreads == 0,
+                  "whole wave parts, ring trips and staging rounds");
+    extern __shared__ u32x4_t dxs[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kp = wave % KS, rbk = blockIdx.x * BPW + wave / KS;   // input part, row block
+    const int z = blockIdx.y, k0 = z * KZ;
+    const int r16 = lane & 15, g = lane >> 4, lr = lane >> 2, lc = lane & 3;
+    u32x4_t *xs = dxs;                                    // [32 tokens][UPAD] units
+    u32x4_t *wt = dxs + 32 * UPAD + wave * 64;            // this wave's 16 x 64-byte tile
+    f32x4_t *red = (f32x4_t *)(dxs + 32 * UPAD + kDxWaves * 64);
+
+    // weight ring (first: every thread's staging loads, then the ring's)
+    constexpr int SR = 32 * UNITS / kDxThreads;           // staged units per thread
+    u32x4_t xv[SR];
+#pragma unroll
+    for (int i = 0; i < SR; ++i) {
+        const int idx = threadIdx.x + kDxThreads * i, t = idx / UNITS, u = idx % UNITS;
+        xv[i] = *(const u32x4_t *)(xin + (size_t)(t < T ? t : 0) * kin + k0 + 8 * u);
+    }
+    const uint8_t *mats[2] = {wa, wb};
+    const int64_t strides[2] = {ra, rb};
+    int qo[NM];
+#pragma unroll
+    for (int k = 0; k < NM; ++k)
+        qo[k] = (rbk * 16 + lr) * (int)strides[k] + 2 * k0 + 16 * lc;
+    __amdgpu_buffer_rsrc_t rq[NM];
+#pragma unroll
+    for (int k = 0; k < NM; ++k)
+        rq[k] = __builtin_amdgcn_make_buffer_rsrc((void *)mats[k], (short)0,
+                                                  (int)min((int64_t)n_rows * strides[k],
+                                                           (int64_t)0x7FFFFFFF),
+                                                  0x00020000);
+    u32x4_t w[R][NM];
+    const int j_lo = kp * NSW;
+    auto load = [&](int slot, int j) {
+#pragma unroll
+        for (int k = 0; k < NM; ++k)
+            w[slot][k] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq[k], qo[k] + 64 * j, 0, 0));
+    };
+#pragma unroll
+    for (int j = 0; j < R; ++j) load(j, j_lo + j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < SR; ++i) {
+        const int idx = threadIdx.x + kDxThreads * i, t = idx / UNITS, u = idx % UNITS;
+        if (t < T) xs[t * UPAD + u] = xv[i];
+    }
+    dn_barrier();
+
+    // tile: chunk c of row r at unit 4 r + (c ^ (r / 4 % 4))
+    u32x4_t *const wt_st = wt + 4 * lr + (lc ^ ((lr >> 2) & 3));
+    const u32x4_t *const wt_ld = wt + 4 * r16 + (g ^ ((r16 >> 2) & 3));
+    f32x4_t acc[NM][2];
+#pragma unroll
+    for (int k = 0; k < NM; ++k) acc[k][0] = acc[k][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto step = [&](int slot, int j, bool refill, int jr) {
+        u32x4_t b[NM];
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            *wt_st = w[slot][k];
+            b[k] = *wt_ld;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (refill) load(slot, jr);
+        const u32x4_t a0 = xs[r16 * UPAD + 4 * j + g], a1 = xs[(16 + r16) * UPAD + 4 * j + g];
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            acc[k][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, a0), __builtin_bit_cast(bf16x8_t, b[k]), acc[k][0], 0, 0, 0);
+            acc[k][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, a1), __builtin_bit_cast(bf16x8_t, b[k]), acc[k][1], 0, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int i0 = 0; i0 < NSW - R; i0 += R) {
+#pragma unroll
+        for (int slot = 0; slot < R; ++slot) step(slot, j_lo + i0 + slot, true, j_lo + i0 + slot + R);
+    }
+#pragma unroll
+    for (int slot = 0; slot < R; ++slot) step(slot, j_lo + NSW - R + slot, false, 0);
+
+    if constexpr (KS > 1) {
+        if (kp != 0) {
+#pragma unroll
+            for (int k = 0; k < NM; ++k)
+#pragma unroll
+                for (int b2 = 0; b2 < 2; ++b2) red[((wave * NM + k) * 2 + b2) * 64 + lane] = acc[k][b2];
+        }
+        dn_barrier();
+        if (kp != 0) return;
+#pragma unroll
+        for (int q = 1; q < KS; ++q)
+#pragma unroll
+            for (int k = 0; k < NM; ++k)
+#pragma unroll
+                for (int b2 = 0; b2 < 2; ++b2) {
+                    const f32x4_t o = red[(((wave + q) * NM + k) * 2 + b2) * 64 + lane];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[k][b2][i] += o[i];
+                }
+    }
+    // lane (r16, g): tokens 16 b2 + 4 g + i of row r16
+    const int ncols = NM * n_rows, col = rbk * 16 + r16;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * b2 + 4 * g + i;
+            if (t < T) {
+                float *o = out + ((size_t)z * T + t) * ncols + col;
+                o[0] = acc[0][b2][i];
+                if constexpr (GATEUP) o[n_rows] = acc[1][b2][i];
+            }
+        }
+}
+
 // h[t][c] = bf16(silu(sum_z gate) * sum_z up), z ascending; 4 columns a thread.
 __global__ void __launch_bounds__(256) swiglu_reduce_kernel(const float *__restrict__ part,
                                                             int S, int T, int F,
@@ -216,12 +361,27 @@ int dense_split(int64_t units, int steps, int max_split) {
     return S;
 }
 
+// The small-batch kernels' shapes: gate/up slices of 512 inputs (two waves
+// of 8 steps per 16 rows), the down pass in one slice (four waves of 12).
+constexpr int kDxGuKS = 2, kDxGuNSW = 8, kDxGuR = 4, kDxDnKS = 4, kDxDnNSW = 12, kDxDnR = 6;
+static bool dense_small_ok(int T, int H, int F) {
+    return T >= 1 && T <= 32 && H % (kDxGuKS * kDxGuNSW * 32) == 0 &&
+           F == kDxDnKS * kDxDnNSW * 32 && F % (16 * (kDxWaves / kDxGuKS)) == 0 &&
+           H % (16 * (kDxWaves / kDxDnKS)) == 0;
+}
+
 DenseSplit dense_plan(int T, int H, int F) {
-    const int64_t tiles = (T + kDnTM - 1) / kDnTM;
     DenseSplit d;
+    d.part_floats = 0;
+    if (dense_small_ok(T, H, F)) {
+        d.s_gateup = H / (kDxGuKS * kDxGuNSW * 32);
+        d.s_down = 1;
+        d.part_floats = (size_t)d.s_gateup * T * 2 * F;
+        return d;
+    }
+    const int64_t tiles = (T + kDnTM - 1) / kDnTM;
     d.s_gateup = dense_split(tiles * (F / kDnBN), H / kDnKS, 16);
     d.s_down = dense_split(tiles * (H / (2 * kDnBN)), F / kDnKS, 12);
-    d.part_floats = 0;
     if (d.s_gateup > 1) d.part_floats = (size_t)d.s_gateup * T * 2 * F;
     if (d.s_down > 1 && (size_t)d.s_down * T * H > d.part_floats)
         d.part_floats = (size_t)d.s_down * T * H;
@@ -236,6 +396,38 @@ moe_status_t launch_dense_swiglu(const moe_ffn_desc_t &sh, const void *x, int T,
                                  float *y, float *part, hipStream_t s) {
     const int F = sh.gate.n, H = sh.gate.k;
     const DenseSplit d = dense_plan(T, H, F);
+    if (dense_small_ok(T, H, F)) {
+        const uint8_t *g = (const uint8_t *)sh.gate.qweight, *u = (const uint8_t *)sh.up.qweight;
+        const uint8_t *dn = (const uint8_t *)sh.down.qweight;
+        {
+            auto k = dense_small_kernel<true, kDxGuKS, kDxGuNSW, kDxGuR>;
+            const size_t lds = dense_small_lds(kDxGuKS * kDxGuNSW * 32, 2, kDxGuKS);
+            if (lds > 65536)
+                (void)hipFuncSetAttribute((const void *)k,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipLaunchKernelGGL(k, dim3(F / (16 * (kDxWaves / kDxGuKS)), d.s_gateup),
+                               dim3(kDxThreads), lds, s, g, sh.gate.qweight_row_stride, u,
+                               sh.up.qweight_row_stride, F, H, (const uint16_t *)x, T, part);
+            MOE_LAUNCH_CHECK();
+            const size_t n4 = ((size_t)T * F) / 4;
+            hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)),
+                               dim3(256), 0, s, (const float *)part, d.s_gateup, T, F,
+                               (uint16_t *)h);
+            MOE_LAUNCH_CHECK();
+        }
+        {
+            auto k = dense_small_kernel<false, kDxDnKS, kDxDnNSW, kDxDnR>;
+            const size_t lds = dense_small_lds(F, 1, kDxDnKS);
+            if (lds > 65536)
+                (void)hipFuncSetAttribute((const void *)k,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipLaunchKernelGGL(k, dim3(H / (16 * (kDxWaves / kDxDnKS)), 1), dim3(kDxThreads), lds,
+                               s, dn, sh.down.qweight_row_stride, dn, sh.down.qweight_row_stride, H,
+                               F, (const uint16_t *)h, T, y);
+            MOE_LAUNCH_CHECK();
+        }
+        return MOE_OK;
+    }
     const unsigned tiles = (unsigned)((T + kDnTM - 1) / kDnTM);
     const uint8_t *g = (const uint8_t *)sh.gate.qweight, *u = (const uint8_t *)sh.up.qweight;
     const uint8_t *dn = (const uint8_t *)sh.down.qweight;
