@@ -261,8 +261,9 @@ moe_status_t moe_norm_route(const float *residual, const float *norm_w, float ep
  * forward pass adds nothing for it. Ids may repeat within a token.
  * tile_m in [1, 256].
  * Deterministic: no atomics decide any order (up to 1024 slots, one work
- * group combines per-expert slot masks with LDS ORs, whose result does not
- * depend on arrival order).
+ * group combines per-expert slot masks with LDS ORs; beyond, each expert's
+ * work group counts all slots with LDS integer adds; neither result depends
+ * on arrival order).
  */
 moe_status_t moe_permute(const int32_t *topk_ids, int T, int K, int E,
                          const moe_perm_t *perm, void *stream);

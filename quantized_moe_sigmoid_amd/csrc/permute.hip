@@ -13,14 +13,14 @@
 // rank inside its expert is the number of its expert's bits below its own,
 // so the order inside an expert is the slot order.
 //
-// Larger batches: two launches, one block per expert in each, no atomics:
-//   count:   block e counts the slots routed to e (compare + ballot).
-//   scatter: block e derives its offsets from all counts, then walks the
-//            slots in ascending order and compacts its own (ballot prefix
-//            inside a wave, wave prefix through LDS), so the order inside
-//            an expert is the slot order. It also pads its segment with -1,
-//            writes its tile map entries and its place among active experts;
-//            the last block writes the totals.
+// Larger batches: one launch, one block per expert.
+// Block e counts every expert's slots in LDS (integer adds: the counts do
+// not depend on the order they arrive in), derives its offsets from the
+// counts below it, then walks the slots in ascending order and compacts
+// its own (ballot prefix inside a wave, wave prefix through LDS), so the
+// order inside an expert is the slot order. It also pads its segment with
+// -1, writes its tile map entries and its place among active experts; the
+// last block writes the totals.
 // Ids outside [0, E) are not routed anywhere in either form: such a slot
 // gets slot_to_row -1 and no row, and the combine adds nothing for it.
 #include "common.h"
@@ -43,38 +43,49 @@ __device__ __forceinline__ int block_sum(int v, int *red) {
     return s;
 }
 
-__global__ void __launch_bounds__(kPermThreads) perm_count_kernel(
-    const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ counts,
-    int32_t *__restrict__ slot_to_row) {
+// Larger batches: one block per expert. Each block builds the histogram of
+// all slots in LDS (integer adds, whose sum does not depend on their
+// order), takes its offsets from the counts of the experts below it, and
+// compacts its own slots in slot order, kPermPass slots per pass: thread t
+// holds slots s0 + 256 j + t (j < 8), ranked by one ballot per j and wave.
+constexpr int kPermPerThread = 8, kPermPass = kPermThreads * kPermPerThread;
+
+__global__ void __launch_bounds__(kPermThreads) perm_large_kernel(
+    const int32_t *__restrict__ ids, int n, int E, int tile_m, int32_t *__restrict__ counts,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ padded_offsets,
+    int32_t *__restrict__ sorted_slots, int32_t *__restrict__ slot_to_row,
+    int32_t *__restrict__ tile_expert, int32_t *__restrict__ num_tiles,
+    int32_t *__restrict__ active_experts, int32_t *__restrict__ num_active) {
+    extern __shared__ int hist[];                              // [E]
     __shared__ int red[kPermWaves];
-    const int e = blockIdx.x;
+    __shared__ int wcnt[2][kPermPerThread][kPermWaves];        // by pass parity
+    const int e = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid >> 6;
+
+    for (int j = tid; j < E; j += kPermThreads) hist[j] = 0;
+    __syncthreads();
+    for (int s0 = 0; s0 < n; s0 += kPermPass) {
+        int v[kPermPerThread];
+#pragma unroll
+        for (int j = 0; j < kPermPerThread; ++j) {
+            const int s = s0 + j * kPermThreads + tid;
+            v[j] = s < n ? ids[s] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kPermPerThread; ++j)
+            if (v[j] >= 0 && v[j] < E) atomicAdd(&hist[v[j]], 1);
+    }
     // slots with a foreign id, spread over the blocks: no row
-    for (int i = blockIdx.x * kPermThreads + threadIdx.x; i < n; i += E * kPermThreads) {
+    for (int i = e * kPermThreads + tid; i < n; i += E * kPermThreads) {
         const int id = ids[i];
         if (id < 0 || id >= E) slot_to_row[i] = -1;
     }
-    int c = 0;
-    for (int i = threadIdx.x; i < n; i += kPermThreads) c += (ids[i] == e);
-    c = block_sum(c, red);
-    if (threadIdx.x == 0) counts[e] = c;
-}
+    __syncthreads();
 
-__global__ void __launch_bounds__(kPermThreads) perm_scatter_kernel(
-    const int32_t *__restrict__ ids, int n, int E, int tile_m,
-    const int32_t *__restrict__ counts, int32_t *__restrict__ expert_offsets,
-    int32_t *__restrict__ padded_offsets, int32_t *__restrict__ sorted_slots,
-    int32_t *__restrict__ slot_to_row, int32_t *__restrict__ tile_expert,
-    int32_t *__restrict__ num_tiles, int32_t *__restrict__ active_experts,
-    int32_t *__restrict__ num_active) {
-    __shared__ int red[kPermWaves];
-    __shared__ int wave_cnt[kPermWaves];
-    const int e = blockIdx.x;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-
-    // Offsets of e from the counts of all experts below it.
+    // Offsets of e from the counts of the experts below it.
     int below = 0, below_pad = 0, below_act = 0;
-    for (int j = threadIdx.x; j < e; j += kPermThreads) {
-        const int c = counts[j];
+    for (int j = tid; j < e; j += kPermThreads) {
+        const int c = hist[j];
         below += c;
         below_pad += (c + tile_m - 1) / tile_m * tile_m;
         below_act += (c > 0);
@@ -82,9 +93,10 @@ __global__ void __launch_bounds__(kPermThreads) perm_scatter_kernel(
     below = block_sum(below, red);
     below_pad = block_sum(below_pad, red);
     below_act = block_sum(below_act, red);
-    const int cnt = counts[e];
+    const int cnt = hist[e];
     const int pad_cnt = (cnt + tile_m - 1) / tile_m * tile_m;
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
+        counts[e] = cnt;
         expert_offsets[e] = below;
         padded_offsets[e] = below_pad;
         if (cnt > 0) active_experts[below_act] = e;
@@ -95,35 +107,47 @@ __global__ void __launch_bounds__(kPermThreads) perm_scatter_kernel(
             num_active[0] = below_act + (cnt > 0);
         }
     }
-    for (int i = threadIdx.x; i < pad_cnt / tile_m; i += kPermThreads)
+    for (int i = tid; i < pad_cnt / tile_m; i += kPermThreads)
         tile_expert[below_pad / tile_m + i] = e;
-    for (int i = cnt + threadIdx.x; i < pad_cnt; i += kPermThreads)
-        sorted_slots[below_pad + i] = -1;
-    if (cnt == 0) return;
+    for (int i = cnt + tid; i < pad_cnt; i += kPermThreads) sorted_slots[below_pad + i] = -1;
 
-    // Stable compaction of the slots routed to e.
-    int base = 0;
-    for (int s0 = 0; s0 < n; s0 += kPermThreads) {
-        const int s = s0 + threadIdx.x;
-        const bool hit = s < n && ids[s] == e;
-        const uint64_t m = __ballot(hit);
-        const int rank = __popcll(m & ((1ull << lane) - 1ull));
-        __syncthreads();
-        if (lane == 0) wave_cnt[wave] = __popcll(m);
-        __syncthreads();
-        int pre = 0;
+    // Stable compaction of the slots routed to e. Pass i writes wave counts
+    // into wcnt[i % 2] and reads them after one barrier; pass i + 2 writes
+    // the same half only after every thread has passed pass i + 1's barrier.
+    const uint64_t below_lane = (1ull << lane) - 1ull;
+    int base = 0, par = 0;
+    for (int s0 = 0; s0 < n && base < cnt; s0 += kPermPass) {   // base: uniform
+        bool hit[kPermPerThread];
+        int rank[kPermPerThread];
 #pragma unroll
-        for (int w = 0; w < kPermWaves; ++w) pre += (w < wave) ? wave_cnt[w] : 0;
-        if (hit) {
-            const int row = below_pad + base + pre + rank;
-            sorted_slots[row] = s;
-            slot_to_row[s] = row;
+        for (int j = 0; j < kPermPerThread; ++j) {
+            const int s = s0 + j * kPermThreads + tid;
+            hit[j] = s < n && ids[s] == e;
+            const uint64_t m = __ballot(hit[j]);
+            rank[j] = __popcll(m & below_lane);
+            if (lane == 0) wcnt[par][j][wave] = __popcll(m);
         }
-        int tot = 0;
+        __syncthreads();
+        int before = 0;                          // slots of e earlier in this pass
 #pragma unroll
-        for (int w = 0; w < kPermWaves; ++w) tot += wave_cnt[w];
-        base += tot;
-        if (base >= cnt) break;          // uniform across the block
+        for (int j = 0; j < kPermPerThread; ++j) {
+            int pre = 0, tot = 0;
+#pragma unroll
+            for (int w = 0; w < kPermWaves; ++w) {
+                const int c = wcnt[par][j][w];
+                pre += w < wave ? c : 0;
+                tot += c;
+            }
+            if (hit[j]) {
+                const int s = s0 + j * kPermThreads + tid;
+                const int row = below_pad + base + before + pre + rank[j];
+                sorted_slots[row] = s;
+                slot_to_row[s] = row;
+            }
+            before += tot;
+        }
+        base += before;
+        par ^= 1;
     }
 }
 
@@ -228,13 +252,10 @@ moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_p
         MOE_LAUNCH_CHECK();
         return MOE_OK;
     }
-    hipLaunchKernelGGL(perm_count_kernel, dim3(E), dim3(kPermThreads), 0, s, ids, n, E, p.counts,
-                       p.slot_to_row);
-    MOE_LAUNCH_CHECK();
-    hipLaunchKernelGGL(perm_scatter_kernel, dim3(E), dim3(kPermThreads), 0, s, ids, n, E,
-                       p.tile_m, p.counts, p.expert_offsets, p.padded_offsets, p.sorted_slots,
-                       p.slot_to_row, p.tile_expert, p.num_tiles, p.active_experts,
-                       p.num_active);
+    hipLaunchKernelGGL(perm_large_kernel, dim3(E), dim3(kPermThreads), (size_t)E * sizeof(int), s,
+                       ids, n, E, p.tile_m, p.counts, p.expert_offsets, p.padded_offsets,
+                       p.sorted_slots, p.slot_to_row, p.tile_expert, p.num_tiles,
+                       p.active_experts, p.num_active);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

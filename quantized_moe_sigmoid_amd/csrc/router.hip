@@ -406,7 +406,14 @@ __global__ void __launch_bounds__(256) router_tiled_kernel(
     const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
     __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
     __shared__ __attribute__((aligned(16))) float xs[2][16][kRtKC];
-    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * kRtExp;
+    // Work groups go round-robin over the 8 XCDs; each XCD takes a
+    // contiguous range of (expert block, token block) pairs, expert block
+    // major, so it reads the weight slices of one or two expert blocks
+    // from its own L2 instead of all of them.
+    const int nb = gridDim.x, b = blockIdx.x, xq = nb / 8, xr = nb % 8, xcd = b % 8;
+    const int lid = xcd * xq + (xcd < xr ? xcd : xr) + b / 8;
+    const int ntb = (T + 15) / 16, eb = lid / ntb;
+    const int t0 = (lid - eb * ntb) * 16, e0 = eb * kRtExp;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // this thread's staging share of x (rows past T read row t0; their
@@ -666,7 +673,7 @@ moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, c
     if (x_dtype == MOE_BF16 && T <= kRowsMaxT && H <= kRowsMaxH)
         launch_rows<false>(x, nullptr, 0.f, T, H, wT, bias, E, nullptr, logits, s);
     else if (x_dtype == MOE_BF16)
-        hipLaunchKernelGGL((router_tiled_kernel<2>), grid, dim3(256), 0, s,
+        hipLaunchKernelGGL((router_tiled_kernel<2>), dim3(grid.x * grid.y), dim3(256), 0, s,
                            (const uint16_t *)x, wT, bias, T, H, E, logits);
     else
         hipLaunchKernelGGL(router_logits_kernel<MOE_F16>, grid, dim3(256), 0, s,

@@ -155,10 +155,12 @@ def test_route_from_router_weight_full(dev, T, zipf):
                                              (4096, 8, 352, 128, True), (8, 2, 16, 4, False),
                                              (3, 3, 5, 1, False), (0, 8, 352, 4, False),
                                              (128, 8, 352, 4, True), (129, 8, 352, 4, False),
-                                             (128, 8, 512, 4, True), (5, 16, 512, 16, False)])
+                                             (128, 8, 512, 4, True), (5, 16, 512, 16, False),
+                                             (1000, 3, 352, 16, True), (700, 8, 512, 32, False)])
 def test_permute_bitwise(dev, T, Kk, Ee, tm, skew):
     """Batches of up to 1024 slots take the one-work-group kernel, larger
-    ones the two-launch form; both must match the oracle bit for bit."""
+    ones the one-work-group-per-expert form (ragged last passes included);
+    both must match the oracle bit for bit."""
     r = np.random.default_rng(T * 7 + Kk)
     if skew:
         p = 1.0 / np.arange(1, Ee + 1) ** 1.1
@@ -186,7 +188,7 @@ def test_permute_bitwise(dev, T, Kk, Ee, tm, skew):
     assert np.array_equal(perm.active_experts.cpu().numpy()[:na], want["active_experts"])
 
 
-@pytest.mark.parametrize("T,Kk,Ee,tm", [(40, 8, 16, 4), (300, 8, 16, 8)])
+@pytest.mark.parametrize("T,Kk,Ee,tm", [(40, 8, 16, 4), (300, 8, 16, 8), (1100, 4, 352, 64)])
 def test_permute_repeated_and_foreign_ids(dev, T, Kk, Ee, tm):
     """Ids need not be distinct within a token, and ids outside [0, E) are
     routed nowhere; slots keep their order inside an expert either way."""
