@@ -15,6 +15,9 @@ bounded sample, and a sweep over the other layer shapes. Inside the timed
 steps HIP events are recorded only around the gate/up kernel (every recorded
 event drains the stream); the other stages' durations come from a separate,
 untimed pass over the same inputs with every stage boundary recorded.
+The default workload, decode T=64, replays its timed steps as one HIP graph
+(the way a serving loop launches a decode step); the sweep also times it
+with every kernel launched from the host.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
                   [--workload decode|decode-graph|prefill|prefill-zipf|nvfp4|nvfp4-csf|
@@ -615,7 +618,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode",
+    ap.add_argument("--workload", default="decode-graph",
                     choices=["decode", "decode-graph", "prefill", "prefill-zipf", "nvfp4",
                              "nvfp4-csf", "nvfp4-csf-expand", "nvfp4-a4", "int4-g32",
                              "int4-asym", "int8", "stack"])

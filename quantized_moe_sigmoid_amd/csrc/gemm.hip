@@ -344,6 +344,20 @@ struct GemmCtx {
                 const uint32_t wbv[8] = {wb.x, wb.y, wb.z, wb.w, wb2.x, wb2.y, wb2.z, wb2.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
+                    const int chunk = i * 8 + half * 4 + j;
+                    // int4-g128: both row blocks' activation words first (the
+                    // second is read even when unused), so their LDS latency
+                    // runs under the decode below (2-3 % at T=2048; the other
+                    // formats measured slower this way)
+                    constexpr bool kEarlyA = int4_g128(FMT);
+                    uint4 avv[2];
+                    if constexpr (kEarlyA) {
+#pragma unroll
+                        for (int mb = 0; mb < 2; ++mb)
+                            avv[mb] = *(const uint4 *)(buf + a_offset(mb * 32 + l32, chunk));
+                        // issued here, not sunk into the branch that uses the second
+                        asm volatile("" ::: "memory");
+                    }
                     float bsa = 0.0f, bsb = 0.0f;
                     if (FMT == MOE_W_NVFP4_G16) {
                         const int blk = i * 4 + half * 2 + (j >> 1);
@@ -363,12 +377,12 @@ struct GemmCtx {
                         ob = decode_b<ACT, FMT>(wav[j], bsa, ma);
                         obb = decode_b<ACT, FMT>(wbv[j], bsb, mbk);
                     }
-                    const int chunk = i * 8 + half * 4 + j;
 #pragma unroll
                     for (int mb = 0; mb < 2; ++mb) {
                         if (mb == 1 && !two_mb) break;
-                        const int row = mb * 32 + l32;
-                        const uint4 av = *(const uint4 *)(buf + a_offset(row, chunk));
+                        const uint4 av =
+                            kEarlyA ? avv[mb]
+                                    : *(const uint4 *)(buf + a_offset(mb * 32 + l32, chunk));
                         da[mb] = mfma32<ACT>(av, ob, da[mb]);
                         db[mb] = mfma32<ACT>(av, obb, db[mb]);
                     }
