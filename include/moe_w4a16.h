@@ -272,7 +272,9 @@ moe_status_t moe_permute(const int32_t *topk_ids, int T, int K, int E,
  * workspace bytes it needs (host output), with or without the shared expert
  * (same argument rules as moe_w4a16_forward). Pass that tile_m to
  * moe_permute. The workspace holds h [max_rows][F] in the activation dtype
- * and y [max_rows][H] float32 (max_rows from moe_permute_sizes), plus, on
+ * and y [max_rows][H] float32 (max_rows from moe_permute_sizes; on the
+ * prefill GEMM path, but for int4-g32, the same bytes hold y in fp16 with a
+ * power-of-two scale per row and 32 columns), plus, on
  * the prefill GEMM path, per-group sums of x and h; with a shared expert its
  * h, y and split partial sums; and for a MOE_W_NVFP4_CSF bank on the GEMM
  * path the expanded E4M3 scales of all E experts of gate, up and down (E *

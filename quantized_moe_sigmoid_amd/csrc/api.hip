@@ -30,13 +30,16 @@ bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act);
 moe_status_t launch_gemv_mx_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
                                     const moe_perm_t &p, int max_tiles, void *h, float *y,
                                     hipStream_t s, const std::function<moe_status_t(int)> &mark);
-moe_status_t launch_combine(const float *y, const int32_t *slot_to_row, const float *w, int T,
-                            int K, int H, const float *shared, const float *residual, void *out,
-                            int out_dtype, hipStream_t s);
+moe_status_t launch_combine(const float *y, const uint16_t *y16, const int8_t *yexp,
+                            const int32_t *slot_to_row, const float *w, int T, int K, int H,
+                            const float *shared, const float *residual, void *out, int out_dtype,
+                            hipStream_t s);
 moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int act, int T, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
-                                 void *xperm, float *xsum, float *hsum, hipStream_t s,
+                                 uint16_t *y16, int8_t *yexp, void *xperm, float *xsum,
+                                 float *hsum, hipStream_t s,
                                  const std::function<moe_status_t(int)> &mark);
+bool gemm_stores_y16(int fmt);
 moe_status_t launch_dense_swiglu(const moe_ffn_desc_t &sh, const void *x, int T, void *h,
                                  float *y, float *part, hipStream_t s);
 moe_status_t launch_round(const float *in, size_t n, int dtype, void *out, hipStream_t s);
@@ -408,6 +411,12 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     char *w = (char *)ws;
     void *h = w + p.off_h;
     float *y = (float *)(w + p.off_y);
+    // the grouped-GEMM path stores y (but for int4-g32) in fp16 with a
+    // power-of-two scale per (row, 32-column group) in the same region:
+    // [max_rows][H] fp16, then [max_rows][H / 32] signed bytes
+    const bool y16_on = p.mfma && gemm_stores_y16(experts->gate.fmt);
+    uint16_t *y16 = y16_on ? (uint16_t *)y : nullptr;
+    int8_t *yexp = y16_on ? (int8_t *)(y16 + (size_t)p.max_rows * H) : nullptr;
     if ((st = mark(0)) != MOE_OK) return st;
     // quantized inputs (NVFP4 banks with input scales): x is quantized with
     // the gate/up input scale before the experts run, and h in place with
@@ -451,7 +460,7 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
         }
     }
     st = p.mfma ? launch_gemm_forward(ex, xin, act_dtype, T, K, *perm, (int)p.max_tiles, h, y,
-                                      w + p.off_xperm, (float *)(w + p.off_xsum),
+                                      y16, yexp, w + p.off_xperm, (float *)(w + p.off_xsum),
                                       (float *)(w + p.off_hsum), s, mk)
          : gemv_mx_supported(*experts, act_dtype)
              ? launch_gemv_mx_forward(*experts, xin, act_dtype, K, *perm, (int)p.max_tiles, h, y,
@@ -466,7 +475,8 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
         if (st != MOE_OK) return st;
     }
     if ((st = mark(3)) != MOE_OK) return st;
-    st = launch_combine(y, perm->slot_to_row, topk_w, T, K, H, ysh, residual, out, out_dtype, s);
+    st = launch_combine(y, y16, yexp, perm->slot_to_row, topk_w, T, K, H, ysh, residual, out,
+                        out_dtype, s);
     if (st != MOE_OK) return st;
     return mark(4);
 }

@@ -7,7 +7,9 @@
 //               (+ shared[t][n]) (+ residual[t][n])
 //
 // float32 throughout, one fixed order, no atomics: the result does not
-// depend on scheduling. A slot whose row is -1 (its id lay outside the
+// depend on scheduling. y is float32, or (Y16, the grouped-GEMM path) fp16
+// with a power-of-two scale per (row, 32-column group): y = v * 2^-s with s
+// one signed byte of yexp [rows][H / 32], widened exactly. A slot whose row is -1 (its id lay outside the
 // expert range, so the permutation routed it nowhere) adds nothing.
 #include "common.h"
 
@@ -16,19 +18,24 @@ namespace moe {
 // The largest K the library accepts (the host rejects more).
 constexpr int kCombineMaxK = 16;
 
-template <int OUT>
+// A thread owns NC consecutive columns of one token: 4 (float32 y, one
+// 16-byte load per row) or 8 (fp16 y, one 16-byte load per row).
+template <int OUT, bool Y16>
 __global__ void __launch_bounds__(256) combine_kernel(
-    const float *__restrict__ y, const int32_t *__restrict__ slot_to_row,
+    const float *__restrict__ y, const uint16_t *__restrict__ y16,
+    const int8_t *__restrict__ yexp, const int32_t *__restrict__ slot_to_row,
     const float *__restrict__ w, int K, int H, const float *__restrict__ shared,
     const float *__restrict__ residual, void *__restrict__ out) {
+    constexpr int NC = Y16 ? 8 : 4;
     const int t = blockIdx.y;
-    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * NC;
     if (n >= H) return;
     // all K rows and weights first (uniform: scalar loads), then all K row
     // loads in flight together, then the sum in ascending k
     int rows[kCombineMaxK];
     float wk[kCombineMaxK];
-    float4 v[kCombineMaxK];
+    uint4 v[kCombineMaxK];
+    int sh[kCombineMaxK];
 #pragma unroll
     for (int k = 0; k < kCombineMaxK; ++k) {
         if (k < K) {
@@ -37,49 +44,75 @@ __global__ void __launch_bounds__(256) combine_kernel(
         }
     }
 #pragma unroll
-    for (int k = 0; k < kCombineMaxK; ++k)
-        if (k < K && rows[k] >= 0) v[k] = *(const float4 *)(y + (size_t)rows[k] * H + n);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < kCombineMaxK; ++k) {
+        if (k < K && rows[k] >= 0) {
+            if constexpr (Y16) {
+                v[k] = *(const uint4 *)(y16 + (size_t)rows[k] * H + n);
+                sh[k] = -(int)yexp[(size_t)rows[k] * (H / 32) + n / 32];
+            } else {
+                v[k] = *(const uint4 *)(y + (size_t)rows[k] * H + n);
+            }
+        }
+    }
+    float acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = 0.0f;
 #pragma unroll
     for (int k = 0; k < kCombineMaxK; ++k) {
         if (k < K && rows[k] >= 0) {
-            acc.x = __builtin_fmaf(wk[k], v[k].x, acc.x);
-            acc.y = __builtin_fmaf(wk[k], v[k].y, acc.y);
-            acc.z = __builtin_fmaf(wk[k], v[k].z, acc.z);
-            acc.w = __builtin_fmaf(wk[k], v[k].w, acc.w);
+            const uint32_t d[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float yv;
+                if constexpr (Y16)
+                    yv = __builtin_ldexpf(
+                        (float)__builtin_bit_cast(_Float16, (uint16_t)(d[c >> 1] >> (16 * (c & 1)))),
+                        sh[k]);
+                else
+                    yv = __uint_as_float(d[c]);
+                acc[c] = __builtin_fmaf(wk[k], yv, acc[c]);
+            }
         }
     }
-    if (shared) {
-        const float4 v = *(const float4 *)(shared + (size_t)t * H + n);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    if (residual) {
-        const float4 v = *(const float4 *)(residual + (size_t)t * H + n);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    const size_t o = (size_t)t * H + n;
-    if (OUT == MOE_F32) {
-        *(float4 *)((float *)out + o) = acc;
-    } else {
-        const uint32_t lo = f32_to_act<OUT>(acc.x) | ((uint32_t)f32_to_act<OUT>(acc.y) << 16);
-        const uint32_t hi = f32_to_act<OUT>(acc.z) | ((uint32_t)f32_to_act<OUT>(acc.w) << 16);
-        *(uint2 *)((uint16_t *)out + o) = make_uint2(lo, hi);
+#pragma unroll
+    for (int c0 = 0; c0 < NC; c0 += 4) {
+        if (shared) {
+            const float4 u = *(const float4 *)(shared + (size_t)t * H + n + c0);
+            acc[c0] += u.x; acc[c0 + 1] += u.y; acc[c0 + 2] += u.z; acc[c0 + 3] += u.w;
+        }
+        if (residual) {
+            const float4 u = *(const float4 *)(residual + (size_t)t * H + n + c0);
+            acc[c0] += u.x; acc[c0 + 1] += u.y; acc[c0 + 2] += u.z; acc[c0 + 3] += u.w;
+        }
+        const size_t o = (size_t)t * H + n + c0;
+        if (OUT == MOE_F32) {
+            *(float4 *)((float *)out + o) = make_float4(acc[c0], acc[c0 + 1], acc[c0 + 2], acc[c0 + 3]);
+        } else {
+            const uint32_t lo = f32_to_act<OUT>(acc[c0]) | ((uint32_t)f32_to_act<OUT>(acc[c0 + 1]) << 16);
+            const uint32_t hi = f32_to_act<OUT>(acc[c0 + 2]) | ((uint32_t)f32_to_act<OUT>(acc[c0 + 3]) << 16);
+            *(uint2 *)((uint16_t *)out + o) = make_uint2(lo, hi);
+        }
     }
 }
 
-moe_status_t launch_combine(const float *y, const int32_t *slot_to_row, const float *w, int T,
-                            int K, int H, const float *shared, const float *residual, void *out,
-                            int out_dtype, hipStream_t s) {
-    const dim3 grid((H / 4 + 255) / 256, T);
-    if (out_dtype == MOE_F32)
-        hipLaunchKernelGGL(combine_kernel<MOE_F32>, grid, dim3(256), 0, s, y, slot_to_row, w, K,
-                           H, shared, residual, out);
-    else if (out_dtype == MOE_BF16)
-        hipLaunchKernelGGL(combine_kernel<MOE_BF16>, grid, dim3(256), 0, s, y, slot_to_row, w, K,
-                           H, shared, residual, out);
-    else
-        hipLaunchKernelGGL(combine_kernel<MOE_F16>, grid, dim3(256), 0, s, y, slot_to_row, w, K,
-                           H, shared, residual, out);
+moe_status_t launch_combine(const float *y, const uint16_t *y16, const int8_t *yexp,
+                            const int32_t *slot_to_row, const float *w, int T, int K, int H,
+                            const float *shared, const float *residual, void *out, int out_dtype,
+                            hipStream_t s) {
+    const int nc = y16 ? 8 : 4;
+    const dim3 grid((H / nc + 255) / 256, T);
+#define MOE_COMBINE(O, Y)                                                                      \
+    hipLaunchKernelGGL((combine_kernel<O, Y>), grid, dim3(256), 0, s, y, y16, yexp, slot_to_row, \
+                       w, K, H, shared, residual, out)
+    const bool h16 = y16 != nullptr;
+    if (out_dtype == MOE_F32) {
+        if (h16) MOE_COMBINE(MOE_F32, true); else MOE_COMBINE(MOE_F32, false);
+    } else if (out_dtype == MOE_BF16) {
+        if (h16) MOE_COMBINE(MOE_BF16, true); else MOE_COMBINE(MOE_BF16, false);
+    } else {
+        if (h16) MOE_COMBINE(MOE_F16, true); else MOE_COMBINE(MOE_F16, false);
+    }
+#undef MOE_COMBINE
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -33,7 +33,8 @@
 //
 //   gate/up pass: h = silu(gate) * up for the wave's 32 columns (both
 //                 projections of a column in the same lane: SwiGLU fused);
-//   down pass:    y rows in float32 for the combine.
+//   down pass:    y rows for the combine: fp16 with a power-of-two scale
+//                 per (row, 32-column group), float32 for int4-g32.
 #include <functional>
 
 #include "decode.h"
@@ -65,6 +66,12 @@ __host__ __device__ constexpr bool g128_rescaled(int fmt) {
 __host__ __device__ constexpr bool int4_pairs(int fmt) {
     return g128_rescaled(fmt) || fmt == MOE_W_INT4_G32;
 }
+
+// The down pass stores y in fp16 with a power-of-two scale per (row,
+// 32-column group) for the formats whose operands are exact; int4-g32 in
+// bf16 already rounds q s into its operands, which uses most of the layer's
+// error bound, so its y stays float32.
+__host__ __device__ constexpr bool gemm_y16(int fmt) { return fmt != MOE_W_INT4_G32; }
 
 // 16-byte weight loads per matrix and step: 32 inputs of a lane are 16 bytes
 // of int4 or 32 of int8.
@@ -410,7 +417,8 @@ __global__ void __launch_bounds__(kGemmThreads)
     const uint16_t *xin, int x_from_slots, int topk, const float *rowsum_in,
     const int32_t *__restrict__ sorted_slots, const int32_t *__restrict__ tile_expert,
     const int32_t *__restrict__ num_tiles, int n_blocks, uint16_t *__restrict__ hout,
-    float *__restrict__ hsum_out, float *__restrict__ yout) {
+    float *__restrict__ hsum_out, float *__restrict__ yout, uint16_t *__restrict__ y16,
+    int8_t *__restrict__ yexp) {
     constexpr int BN = GATEUP ? kGemmBN : 2 * kGemmBN;      // output columns per block
     // two separate LDS objects per double buffer: the compiler then knows a
     // DMA into one does not alias reads of the other, and does not make the
@@ -536,9 +544,61 @@ __global__ void __launch_bounds__(kGemmThreads)
                 if (m < m_valid && ok_a) hout[r * n_rows + hcol] = hb;
                 if (g128_rescaled(FMT))
                     hs[m * kGemmBN + wave * 32 + cx.l32] = m < m_valid ? act_to_f32<ACT>(hb) : 0.0f;
-            } else if (m < m_valid) {
+            } else if (!gemm_y16(FMT) && m < m_valid) {
                 if (ok_a) yout[r * n_rows + col_a] = cx.da[mb][v] * ga;
                 if (ok_b) yout[r * n_rows + col_b] = cx.db[mb][v] * gb;
+            }
+        }
+    }
+    if (!GATEUP && gemm_y16(FMT)) {
+        // y rows in fp16 with a power-of-two scale per (row, 32-column
+        // group), y = fp16 * 2^-s: 32 rows of the wave's 64 x 64 tile at a
+        // time go through LDS (rows padded to 65 floats, so the column-wise
+        // writes and the row-wise reads each touch every bank once); lane L
+        // then owns row L % 32, columns 32 (L / 32) .. + 31. Their largest
+        // magnitude fixes s (it lands in [2^14, 2^15)), the scaled values
+        // round once to fp16 and go out as 64 contiguous bytes, s as one
+        // signed byte. The ring buffers are free: the loop ended on a barrier.
+        float *tb = (wave < 2 ? (float *)abuf0 : (float *)abuf1) + (wave & 1) * (32 * 65);
+        const int colw = nb * BN + wave * 64;
+        const int rr = cx.l32, g = half;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            if (mb == 1 && m_valid <= 32) break;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 8 * (v >> 2) + 4 * half + (v & 3);
+                tb[r * 65 + cx.l32] = cx.da[mb][v] * ga;
+                tb[r * 65 + 32 + cx.l32] = cx.db[mb][v] * gb;
+            }
+            float vals[32];
+            float mx = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) {
+                vals[c] = tb[rr * 65 + 32 * g + c];
+                mx = fmaxf(mx, fabsf(vals[c]));
+            }
+            int sh = 0;
+            if (mx > 0.0f) {
+                sh = 15 - __builtin_amdgcn_frexp_expf(mx);
+                sh = sh < -127 ? -127 : (sh > 127 ? 127 : sh);
+            }
+            const int m = mb * 32 + rr;
+            if (m < m_valid && colw + 32 * g < n_rows) {
+                const size_t r = (size_t)tile * kGemmTM + m;
+                uint32_t pk[16];
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const _Float16 lo = (_Float16)__builtin_ldexpf(vals[2 * c], sh);
+                    const _Float16 hi = (_Float16)__builtin_ldexpf(vals[2 * c + 1], sh);
+                    pk[c] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                }
+                uint4 *dst = (uint4 *)(y16 + r * n_rows + colw + 32 * g);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    dst[q] = make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
+                yexp[r * (n_rows / 32) + (colw + 32 * g) / 32] = (int8_t)sh;
             }
         }
     }
@@ -599,8 +659,8 @@ inline GemmMat gemm_mat(const moe_weight_desc_t &d) {
 template <int ACT, int FMT>
 moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int T, int K,
                             const moe_perm_t &p, int max_tiles, uint16_t *h, float *y,
-                            uint16_t *xperm, float *xsum, float *hsum, hipStream_t s,
-                            const std::function<moe_status_t(int)> &mark) {
+                            uint16_t *y16, int8_t *yexp, uint16_t *xperm, float *xsum, float *hsum,
+                            hipStream_t s, const std::function<moe_status_t(int)> &mark) {
     const int F = ex.gate.n, H = ex.gate.k;
     const uint16_t *xa = x;
     if (int4_pairs(FMT)) {
@@ -613,7 +673,7 @@ moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int T, 
         hipLaunchKernelGGL((gemm_kernel<ACT, FMT, true>), dim3(max_tiles * nbk),
                            dim3(kGemmThreads), 0, s, gemm_mat(ex.gate), gemm_mat(ex.up), F, H, xa,
                            1, K, xsum, p.sorted_slots, p.tile_expert, p.num_tiles, nbk, h, hsum,
-                           nullptr);
+                           nullptr, nullptr, nullptr);
         MOE_LAUNCH_CHECK();
     }
     if (mark && mark(1) != MOE_OK) return MOE_ERR_HIP;
@@ -623,7 +683,7 @@ moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int T, 
         const GemmMat d = gemm_mat(ex.down);
         hipLaunchKernelGGL((gemm_kernel<ACT, FMT, false>), dim3(max_tiles * nbk),
                            dim3(kGemmThreads), 0, s, d, d, H, F, h, 0, K, hsum, p.sorted_slots,
-                           p.tile_expert, p.num_tiles, nbk, nullptr, nullptr, y);
+                           p.tile_expert, p.num_tiles, nbk, nullptr, nullptr, y, y16, yexp);
         MOE_LAUNCH_CHECK();
     }
     if (mark && mark(2) != MOE_OK) return MOE_ERR_HIP;
@@ -634,14 +694,18 @@ int gemm_tile_m() { return kGemmTM; }
 int gemm_group() { return kGemmKS; }
 int gemm_bn() { return kGemmBN; }
 
+bool gemm_stores_y16(int fmt) { return gemm_y16(fmt); }
+
 moe_status_t launch_gemm_forward(const moe_ffn_desc_t &ex, const void *x, int act, int T, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
-                                 void *xperm, float *xsum, float *hsum, hipStream_t s,
+                                 uint16_t *y16, int8_t *yexp, void *xperm, float *xsum,
+                                 float *hsum, hipStream_t s,
                                  const std::function<moe_status_t(int)> &mark) {
     const uint16_t *xx = (const uint16_t *)x;
     uint16_t *hh = (uint16_t *)h;
 #define MOE_GEMM_FWD(A, F)                                                                    \
-    gemm_forward_t<A, F>(ex, xx, T, K, p, max_tiles, hh, y, (uint16_t *)xperm, xsum, hsum, s, mark)
+    gemm_forward_t<A, F>(ex, xx, T, K, p, max_tiles, hh, y, y16, yexp, (uint16_t *)xperm, xsum, \
+                         hsum, s, mark)
     const int f = ex.gate.fmt;
     if (act == MOE_BF16)
         return f == MOE_W_NVFP4_G16        ? MOE_GEMM_FWD(MOE_BF16, MOE_W_NVFP4_G16)

@@ -13,8 +13,9 @@
 // rank inside its expert is the number of its expert's bits below its own,
 // so the order inside an expert is the slot order.
 //
-// Larger batches: one launch, one block per expert.
-// Block e counts every expert's slots in LDS (integer adds: the counts do
+// Larger batches: one launch, one block per expert. Up to 32768 slots the
+// block first copies the ids into LDS. Block e counts every expert's slots
+// in LDS (integer adds: the counts do
 // not depend on the order they arrive in), derives its offsets from the
 // counts below it, then walks the slots in ascending order and compacts
 // its own (ballot prefix inside a wave, wave prefix through LDS), so the
@@ -49,27 +50,56 @@ __device__ __forceinline__ int block_sum(int v, int *red) {
 // compacts its own slots in slot order, kPermPass slots per pass: thread t
 // holds slots s0 + 256 j + t (j < 8), ranked by one ballot per j and wave.
 constexpr int kPermPerThread = 8, kPermPass = kPermThreads * kPermPerThread;
+constexpr int kPermStageMax = 32768;          // slots whose ids a block stages in LDS (64 KB)
 
+// STAGE: the block first copies all ids into LDS (16-bit; E <= 512, a
+// foreign id becomes 0xFFFF), so its passes read LDS instead of L2.
+template <bool STAGE>
 __global__ void __launch_bounds__(kPermThreads) perm_large_kernel(
     const int32_t *__restrict__ ids, int n, int E, int tile_m, int32_t *__restrict__ counts,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ padded_offsets,
     int32_t *__restrict__ sorted_slots, int32_t *__restrict__ slot_to_row,
     int32_t *__restrict__ tile_expert, int32_t *__restrict__ num_tiles,
     int32_t *__restrict__ active_experts, int32_t *__restrict__ num_active) {
-    extern __shared__ int hist[];                              // [E]
+    extern __shared__ int hist[];                              // [E], then STAGE: ids [n]
+    uint16_t *sid = (uint16_t *)(hist + ((E + 3) & ~3));
     __shared__ int red[kPermWaves];
     __shared__ int wcnt[2][kPermPerThread][kPermWaves];        // by pass parity
     const int e = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid >> 6;
+    auto id_at = [&](int s) -> int {
+        if constexpr (STAGE) {
+            const int v = sid[s];
+            return v == 0xFFFF ? -1 : v;
+        } else {
+            return ids[s];
+        }
+    };
 
     for (int j = tid; j < E; j += kPermThreads) hist[j] = 0;
+    if constexpr (STAGE) {
+        // 16 loads in flight per thread
+        for (int s0 = 0; s0 < n; s0 += 16 * kPermThreads) {
+            int v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int s = s0 + j * kPermThreads + tid;
+                v[j] = s < n ? ids[s] : -1;
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int s = s0 + j * kPermThreads + tid;
+                if (s < n) sid[s] = (uint16_t)(v[j] >= 0 && v[j] < E ? v[j] : 0xFFFF);
+            }
+        }
+    }
     __syncthreads();
     for (int s0 = 0; s0 < n; s0 += kPermPass) {
         int v[kPermPerThread];
 #pragma unroll
         for (int j = 0; j < kPermPerThread; ++j) {
             const int s = s0 + j * kPermThreads + tid;
-            v[j] = s < n ? ids[s] : -1;
+            v[j] = s < n ? id_at(s) : -1;
         }
 #pragma unroll
         for (int j = 0; j < kPermPerThread; ++j)
@@ -122,7 +152,7 @@ __global__ void __launch_bounds__(kPermThreads) perm_large_kernel(
 #pragma unroll
         for (int j = 0; j < kPermPerThread; ++j) {
             const int s = s0 + j * kPermThreads + tid;
-            hit[j] = s < n && ids[s] == e;
+            hit[j] = s < n && id_at(s) == e;
             const uint64_t m = __ballot(hit[j]);
             rank[j] = __popcll(m & below_lane);
             if (lane == 0) wcnt[par][j][wave] = __popcll(m);
@@ -252,10 +282,23 @@ moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_p
         MOE_LAUNCH_CHECK();
         return MOE_OK;
     }
-    hipLaunchKernelGGL(perm_large_kernel, dim3(E), dim3(kPermThreads), (size_t)E * sizeof(int), s,
-                       ids, n, E, p.tile_m, p.counts, p.expert_offsets, p.padded_offsets,
-                       p.sorted_slots, p.slot_to_row, p.tile_expert, p.num_tiles,
-                       p.active_experts, p.num_active);
+    const size_t hist_b = (size_t)((E + 3) & ~3) * sizeof(int);
+    if (n <= kPermStageMax) {
+        const size_t lds = hist_b + (size_t)n * sizeof(uint16_t);
+        if (lds > 65536 &&
+            hipFuncSetAttribute((const void *)perm_large_kernel<true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return MOE_ERR_HIP;
+        hipLaunchKernelGGL(perm_large_kernel<true>, dim3(E), dim3(kPermThreads), lds, s, ids, n, E,
+                           p.tile_m, p.counts, p.expert_offsets, p.padded_offsets, p.sorted_slots,
+                           p.slot_to_row, p.tile_expert, p.num_tiles, p.active_experts,
+                           p.num_active);
+    } else {
+        hipLaunchKernelGGL(perm_large_kernel<false>, dim3(E), dim3(kPermThreads), hist_b, s, ids,
+                           n, E, p.tile_m, p.counts, p.expert_offsets, p.padded_offsets,
+                           p.sorted_slots, p.slot_to_row, p.tile_expert, p.num_tiles,
+                           p.active_experts, p.num_active);
+    }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
