@@ -446,6 +446,36 @@ def test_forward_mfma_int4_small(dev, act, Ee, Kk, T):
     assert ok, ratio
 
 
+@pytest.mark.parametrize("act,shift", [("bf16", 22), ("f16", -20)])
+def test_forward_mfma_y_far_outside_fp16(dev, act, shift):
+    """The grouped-GEMM path hands y to the combine in fp16 with a
+    power-of-two scale per (row, 32 columns): with the down projection's
+    scales multiplied by 2^22 (y far above fp16's largest value) or 2^-20
+    (far below its normal range) the layer still meets the tolerance."""
+    Ee, Hh, Ff, T, Kk = 8, 512, 256, 40, 4
+    banks, host = [], []
+    for which, (n, k) in (("gate", (Ff, Hh)), ("up", (Ff, Hh)), ("down", (Hh, Ff))):
+        q, sbits = FX.int4_bank_oracle(Ee, n, k, 6, 0, which)
+        if which == "down":   # a power of two: add to the bf16 exponent field
+            sbits = (sbits.astype(np.int32) + (shift << 7)).astype(np.uint16)
+        qt, st = FX.int4_to_device(q, sbits, dev)
+        banks.append(B.bank_int4(qt, st))
+        host.append((q, sbits))
+    ffn = B.ffn(*banks)
+    x = synth.activations(T, Hh, act, 6)
+    lg = synth.router_logits(T, Ee, 6)
+    ids, w = B.moe_route_topk(Kk, logits=torch.from_numpy(lg).to(dev))
+    tm, _ = B.moe_forward_plan(ffn, T, Kk, x.dtype)
+    assert tm == 64
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, Ee).cpu().numpy()
+    oids = OR.topk_ids(lg, Kk)
+    ref = FX.oracle_layer(x, oids, OR.routing_weights(lg, oids), _experts_fn_int4(host))
+    big = np.max(np.abs(ref))
+    assert (big > 6.6e4) if shift > 0 else (big < 6.1e-5)
+    ok, ratio = FX.within_tolerance(out, ref)
+    assert ok, ratio
+
+
 def test_forward_mfma_nvfp4_small(dev):
     Ee, Hh, Ff, T, Kk = 6, 512, 256, 64, 3
     ffn, host = _nvfp4_ffn_from_oracle(Ee, Hh, Ff, 8, dev)
