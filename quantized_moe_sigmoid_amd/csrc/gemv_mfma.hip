@@ -432,6 +432,7 @@ bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act) {
 // routing, so the uniform decode case decides.
 constexpr int kMxTM = 4;
 int gemv_mx_tile_m() { return kMxTM; }
+constexpr int kMxDeepTiles = 300;
 
 template <int ACT, int FMT, bool GATEUP, int NS, int RP, int KS, int R>
 moe_status_t launch_mx(const GemvMat &a, const GemvMat &b, int n_rows, const uint16_t *x,
@@ -450,7 +451,12 @@ moe_status_t launch_mx(const GemvMat &a, const GemvMat &b, int n_rows, const uin
 }
 
 // Few tiles (small batches) split each row block's inputs over more waves;
-// the thresholds keep at least ~2 work groups per CU.
+// the thresholds keep at least ~2 work groups per CU. Past kMxDeepTiles
+// tiles (T = 64 at top-8 of 352) a wave keeps 8 gate/up steps and all 12
+// down steps in flight, the down pass one row block per wave: decode T=64
+// 0.470 -> 0.460 ms (down 160 -> 153 us). At 256 tiles (the Zipf-routed
+// stack at T=32) that form measured slower (down 40 -> 44 us per layer),
+// so smaller batches keep the 4-step rings and two row passes.
 template <int ACT, int FMT>
 moe_status_t gemv_mx_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
                                const moe_perm_t &p, int max_tiles, uint16_t *h, float *y,
@@ -462,16 +468,20 @@ moe_status_t gemv_mx_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int 
         st = launch_mx<ACT, FMT, true, 32, 1, 4, 4>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
     else if (max_tiles <= 48)
         st = launch_mx<ACT, FMT, true, 32, 1, 2, 4>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
-    else
+    else if (max_tiles <= kMxDeepTiles)
         st = launch_mx<ACT, FMT, true, 32, 1, 1, 4>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
+    else
+        st = launch_mx<ACT, FMT, true, 32, 1, 1, 8>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
     if (st != MOE_OK) return st;
     if (mark && mark(1) != MOE_OK) return MOE_ERR_HIP;
     if (max_tiles <= 16)
         st = launch_mx<ACT, FMT, false, 12, 1, 2, 3>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
     else if (max_tiles <= 48)
         st = launch_mx<ACT, FMT, false, 12, 1, 1, 4>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
-    else
+    else if (max_tiles <= kMxDeepTiles)
         st = launch_mx<ACT, FMT, false, 12, 2, 1, 4>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
+    else
+        st = launch_mx<ACT, FMT, false, 12, 1, 1, 12>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
     if (st != MOE_OK) return st;
     if (mark && mark(2) != MOE_OK) return MOE_ERR_HIP;
     return MOE_OK;
