@@ -7,7 +7,9 @@ router picks 8 of the 352 routed experts; "Step 5 Preview: 92 narrow layers, and
 sparse indexer that scores blocks of 8", "The shape: narrow and deep"):
 
 1. logits[t, e] = x[t] . Wr[e] in the canonical float32 order of
-   router_ref.c (plus an optional per-expert bias), or given logits;
+   router_ref.c (one fused chain per block of 512 inputs, the blocks' sums
+   added in ascending order; plus an optional per-expert bias), or given
+   logits;
 2. the K experts with the largest logits, ties broken by the lower expert
    index (the same convention the sparse indexer's region top-k uses, page
    "Step 5 Preview: ...", "Sparse GQA, read from the kernels", step 3);

@@ -10,8 +10,9 @@ from quantized_moe_sigmoid_amd import synth
 
 
 def test_logits_within_fp32_error_bound_of_exact_sum():
-    """|chain - exact| <= H * 2^-24 * sum|x w| (sequential summation bound),
-    on the tiny layer; a transposed or mis-indexed weight fails this."""
+    """|chain - exact| <= H * 2^-24 * sum|x w| (the sequential summation
+    bound, which also covers block chains added in order), on the tiny
+    layer; a transposed or mis-indexed weight fails this."""
     cfg = synth.CONFIGS["tiny"]
     T, H, E = cfg["T"][0], cfg["H"], cfg["E"]
     x = synth.activations(T, H, "f16", 0).float().numpy()
@@ -45,6 +46,38 @@ def test_chain_uses_fused_multiply_add_in_ascending_order():
     assert float(lg[0, 0]) == 2.0 ** -11 + 2.0 ** -24
     lg_rev = R.router_logits(x[:, ::-1], wT[::-1])
     assert float(lg_rev[0, 0]) == 2.0 ** -11
+
+
+def _boundary_case(H, k_one, k_minus, k_tiny):
+    """x w = 1 at k_one, -1 at k_minus, 2^-30 at k_tiny (in that order): a
+    chain holding all three returns 2^-30; one whose -1 and 2^-30 start a
+    fresh chain after the 1 returns 0 (-1 + 2^-30 rounds to -1)."""
+    x = np.zeros((1, H), dtype=np.float32)
+    wT = np.zeros((H, 1), dtype=np.float32)
+    x[0, [k_one, k_minus, k_tiny]] = [1.0, -1.0, 1.0]
+    wT[[k_one, k_minus, k_tiny], 0] = [1.0, 1.0, 2.0 ** -30]
+    return float(R.router_logits(x, wT)[0, 0])
+
+
+def test_chain_restarts_at_every_512_input_block():
+    """Blocks of exactly 512: a fresh chain starts at input 512 (the 1 at
+    511 and the -1 at 512 fall in different blocks) but not at 256."""
+    assert _boundary_case(1024, 511, 512, 513) == 0.0
+    assert _boundary_case(1024, 255, 256, 257) == 2.0 ** -30
+    assert _boundary_case(1024, 0, 300, 301) == 2.0 ** -30
+    # a short last block (H = 576): its chain also starts fresh
+    assert _boundary_case(576, 100, 512, 575) == 0.0
+
+
+def test_block_sums_added_in_ascending_order():
+    """Block sums 1, 2^-24, 2^-24: ((1 + 2^-24) + 2^-24) rounds to 1 twice
+    (ties to even); the other grouping would give 1 + 2^-23."""
+    H = 1536
+    x = np.zeros((1, H), dtype=np.float32)
+    wT = np.zeros((H, 1), dtype=np.float32)
+    x[0, [0, 512, 1024]] = 1.0
+    wT[[0, 512, 1024], 0] = [1.0, 2.0 ** -24, 2.0 ** -24]
+    assert float(R.router_logits(x, wT)[0, 0]) == 1.0
 
 
 def test_bias_added_after_the_chain_in_float32():
