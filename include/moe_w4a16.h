@@ -174,12 +174,14 @@ int moe_abi_version(void);
 /*
  * moe_router_logits -- the router scores of every (token, expert) pair
  * (page "Step-5-Preview-Spark", "At a glance": a sigmoid router over 352
- * routed experts), as the float32 chain
- *     acc = +0; for k = 0 .. H-1: acc = fma(float(x[t][k]), router_wT[k][e], acc)
- *     logits[t][e] = acc   (+ bias[e], one float32 addition, if bias != NULL)
- * This fixed order makes routing reproducible bit for bit (page
- * "Step-5-Preview-Spark", "Quality": top-8 choices flip under a changed
- * summation order).
+ * routed experts), as a float32 sum in one fixed order: the inputs in
+ * blocks of 512 (the last may be shorter), each block a fused chain
+ *     s_b = +0; for k in block b ascending: s_b = fma(float(x[t][k]), router_wT[k][e], s_b)
+ *     logits[t][e] = ((s_0 + s_1) + s_2) + ...   (+ bias[e] if bias != NULL)
+ * in float32 additions. This fixed order makes routing reproducible bit for
+ * bit (page "Step-5-Preview-Spark", "Quality": top-8 choices flip under a
+ * changed summation order); the blocks let small batches run a token's
+ * chains side by side.
  * x [T][H] in x_dtype (MOE_F16 or MOE_BF16), router_wT [H][E] float (the
  * router weight transposed, 16-byte aligned), bias [E] float or NULL,
  * logits [T][E] float. Limits: H % 64 == 0, E % 4 == 0, E <= 512.
@@ -188,8 +190,11 @@ moe_status_t moe_router_logits(const void *x, int x_dtype, const float *router_w
                                const float *bias, int T, int H, int E, float *logits,
                                void *stream);
 
-/* Workspace bytes (host output) moe_route_topk needs: T*E*4 when it computes
- * the logits from a router weight (use_router_weight != 0), else 0. */
+/* Workspace bytes (host output) moe_route_topk and moe_norm_route need when
+ * they compute the logits from a router weight (use_router_weight != 0),
+ * else 0: up to 192 tokens one float32 per 512-input block, token and
+ * expert (8*T*E*4, enough for any H <= 4096; larger H then take the
+ * T*E*4 path), beyond that the logits, T*E*4. */
 moe_status_t moe_route_workspace(int T, int E, int use_router_weight, size_t *bytes);
 
 /*
@@ -199,8 +204,10 @@ moe_status_t moe_route_workspace(int T, int E, int use_router_weight, size_t *by
  * Preview: ...", "Sparse GQA, read from the kernels", step 3).
  *
  * Logits come from exactly one of:
- *   router_wT: the moe_router_logits chain of x (x, x_dtype, H as there),
- *     written to the workspace `ws` (moe_route_workspace bytes);
+ *   router_wT: the moe_router_logits sum of x (x, x_dtype, H as there);
+ *     its block sums (bf16 up to 192 tokens and H <= 4096) or the logits
+ *     go to the workspace `ws` (moe_route_workspace bytes) and the top-K
+ *     adds them up in block order;
  *   logits_in [T][E] float: given logits (x, router_wT, ws unused).
  * If bias [E] float is non-NULL, logit = logit + bias[e] in float32.
  * topk_ids [T][K] int32: the K largest logits by (logit descending, expert
@@ -231,8 +238,10 @@ moe_status_t moe_permute_sizes(int T, int K, int E, int tile_m,
  *   topk_ids, topk_w = top-K routing of a from router_wT (+ bias)
  *                                                        (as moe_route_topk)
  * For batches of up to 192 tokens with H <= 4096 the norm, the cast and the
- * router chains run as one kernel (each router work group normalizes its
- * token rows into LDS; the first expert block writes them to a_out), then
+ * router chains run as one kernel (one work group per token pair or quad,
+ * 64-expert block and 512-input block normalizes its token rows into LDS
+ * and stores its chains' block sums; the first expert and input block
+ * writes the rows to a_out), then
  * the top-K; otherwise the kernels of the separate calls run. Either way the
  * results are bitwise those of moe_rmsnorm followed by moe_route_topk.
  *   residual [T][H] float; norm_w [H] float or NULL (gain 1); eps in [0, 1];
@@ -240,7 +249,7 @@ moe_status_t moe_permute_sizes(int T, int K, int E, int tile_m,
  *   a_out [T][H] bf16 (the layer input the experts read);
  *   topk_ids [T][K] int32, topk_w [T][K] float;
  *   ws: device workspace of moe_route_workspace(T, E, 1) bytes (the
- *   logits), 16-byte aligned.
+ *   block sums or the logits), 16-byte aligned.
  * All pointers device memory, 16-byte aligned (ids and weights 4). Limits:
  * H % 64 == 0 and E % 4 == 0 (else MOE_ERR_UNSUPPORTED), H <= 16384,
  * 1 <= K <= min(E, 16), E <= 512. T == 0 is a no-op.

@@ -382,7 +382,7 @@ def moe_norm_route(residual, router_wT, K, norm_w=None, eps=1e-5, bias=None, ren
     if w is None:
         w = torch.empty((T, K), dtype=torch.float32, device=dev)
     if ws is None:
-        ws = torch.empty(max(T * E * 4, 16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(moe_route_workspace(T, E, True), 16), dtype=torch.uint8, device=dev)
     _check(lib().moe_norm_route(_ptr(residual), _ptr(norm_w), float(eps), T, H, _ptr(router_wT),
                                 _ptr(bias), E, K, 1 if renormalize else 0, _ptr(a), _ptr(ids),
                                 _ptr(w), _ptr(ws), ws.numel(), _stream(dev)),

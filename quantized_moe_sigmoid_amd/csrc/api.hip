@@ -12,7 +12,12 @@ namespace moe {
 moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, const float *bias,
                                   int T, int H, int E, float *logits, hipStream_t s);
 moe_status_t launch_topk(const float *logits, const float *bias, int T, int E, int K, int renorm,
-                         int32_t *ids, float *wts, hipStream_t s);
+                         int32_t *ids, float *wts, hipStream_t s, int P = 1);
+moe_status_t launch_router_scores(const void *x, int x_dtype, const float *wT, int T, int H,
+                                  int E, float *part, int *P, hipStream_t s);
+size_t router_ws_floats(int T, int H, int E, int x_dtype);
+size_t router_ws_floats_max(int T, int E);
+int router_blocks(int H);
 moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_perm_t &p,
                             hipStream_t s);
 moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out, hipStream_t s);
@@ -46,9 +51,9 @@ moe_status_t launch_round(const float *in, size_t n, int dtype, void *out, hipSt
 bool norm_route_fused(int T, int H, int E);
 moe_status_t launch_csf_expand_rows(const moe_weight_desc_t &d, const int32_t *expert_offsets,
                                     uint8_t *out, hipStream_t s);
-moe_status_t launch_norm_router_logits(const float *res, const float *gain, float eps, int T,
-                                       int H, const float *wT, const float *bias, int E,
-                                       void *a_out, float *logits, hipStream_t s);
+moe_status_t launch_norm_router_scores(const float *res, const float *gain, float eps, int T,
+                                       int H, const float *wT, int E, void *a_out, float *part,
+                                       hipStream_t s);
 moe_status_t launch_rmsnorm(const float *x, const float *w, float eps, int T, int H, int dtype,
                             void *out, hipStream_t s);
 moe_status_t launch_act_quant(const void *in, int dtype, int64_t rows, int k, float g,
@@ -311,7 +316,7 @@ moe_status_t moe_router_logits(const void *x, int x_dtype, const float *router_w
 
 moe_status_t moe_route_workspace(int T, int E, int use_router_weight, size_t *bytes) {
     if (T < 0 || E < 1 || E > kMaxExperts || !bytes) return MOE_ERR_INVALID_ARG;
-    *bytes = use_router_weight ? (size_t)T * E * 4 : 0;
+    *bytes = use_router_weight ? router_ws_floats_max(T, E) * 4 : 0;
     return MOE_OK;
 }
 
@@ -328,13 +333,14 @@ moe_status_t moe_route_topk(const void *x, int x_dtype, const float *router_wT,
         moe_status_t st = check_router(x, x_dtype, router_wT, T, H, E);
         if (st != MOE_OK) return st;
         if (T > 0 && !ws) return MOE_ERR_INVALID_ARG;
-        if (ws_bytes < (size_t)T * E * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
+        if (ws_bytes < router_ws_floats(T, H, E, x_dtype) * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
         if (ws && !aligned(ws, 16)) return MOE_ERR_INVALID_ARG;
         if (T == 0) return MOE_OK;
-        float *lg = (float *)ws;
-        st = launch_router_logits(x, x_dtype, router_wT, bias, T, H, E, lg, s);
+        float *part = (float *)ws;
+        int P = 1;
+        st = launch_router_scores(x, x_dtype, router_wT, T, H, E, part, &P, s);
         if (st != MOE_OK) return st;
-        return launch_topk(lg, nullptr, T, E, K, renormalize, topk_ids, topk_w, s);
+        return launch_topk(part, bias, T, E, K, renormalize, topk_ids, topk_w, s, P);
     }
     if (T == 0) return MOE_OK;
     return launch_topk(logits_in, bias, T, E, K, renormalize, topk_ids, topk_w, s);
@@ -574,25 +580,26 @@ moe_status_t moe_norm_route(const float *residual, const float *norm_w, float ep
         return MOE_ERR_INVALID_ARG;
     if (!(eps >= 0.0f) || eps > 1.0f || !router_wT) return MOE_ERR_INVALID_ARG;
     if (H % 64 || E % 4) return MOE_ERR_UNSUPPORTED;
-    if (ws_bytes < (size_t)T * E * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (ws_bytes < router_ws_floats(T, H, E, MOE_BF16) * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (T == 0) return MOE_OK;
     if (!residual || !a_out || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
     if (!aligned(residual, 16) || !aligned(a_out, 16) || !aligned(router_wT, 16) ||
         !aligned(ws, 16) || (norm_w && !aligned(norm_w, 16)))
         return MOE_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    float *lg = (float *)ws;
+    float *part = (float *)ws;
     moe_status_t st;
+    int P = 1;
     if (norm_route_fused(T, H, E)) {
-        st = launch_norm_router_logits(residual, norm_w, eps, T, H, router_wT, bias, E, a_out, lg,
-                                       s);
+        P = router_blocks(H);
+        st = launch_norm_router_scores(residual, norm_w, eps, T, H, router_wT, E, a_out, part, s);
     } else {
         if ((st = launch_rmsnorm(residual, norm_w, eps, T, H, MOE_BF16, a_out, s)) != MOE_OK)
             return st;
-        st = launch_router_logits(a_out, MOE_BF16, router_wT, bias, T, H, E, lg, s);
+        st = launch_router_scores(a_out, MOE_BF16, router_wT, T, H, E, part, &P, s);
     }
     if (st != MOE_OK) return st;
-    return launch_topk(lg, nullptr, T, E, K, renormalize, topk_ids, topk_w, s);
+    return launch_topk(part, bias, T, E, K, renormalize, topk_ids, topk_w, s, P);
 }
 
 moe_status_t moe_dequant(const moe_weight_desc_t *w, int expert, float *out, void *stream) {

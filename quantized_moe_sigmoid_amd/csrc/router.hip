@@ -3,9 +3,13 @@
 //
 // Logits are either computed here from the 16-bit activations and the
 // float32 router weight stored transposed ([H][E]), or given. The logit of
-// (t, e) is the float32 chain acc = fma(x[t][k], wT[k][e], acc) over k
-// ascending from +0: one fixed order, so the chosen experts are the same on
-// every run and on the CPU reference. The pages show why the order matters:
+// (t, e) is a sum in one fixed order: the inputs in blocks of 512, each
+// block one float32 chain s = fma(x[t][k], wT[k][e], s) over its k
+// ascending from +0, the block sums added in ascending block order (then
+// the bias, if any). The chosen experts are thus the same on every run and
+// on the CPU reference, and a small batch can run a token's 8 block chains
+// side by side instead of one 4096-step chain. The pages show why the order
+// matters:
 // a different summation order inside the MoE flips near-tied expert choices
 // ("Step-5-Preview-Spark", "Quality", noise-floor paragraph).
 //
@@ -21,6 +25,26 @@
 namespace moe {
 
 constexpr int kMaxE = 512;
+
+// Inputs per block of the canonical logit sum, and the most blocks whose
+// sums the top-K adds up (the block-sum paths take H <= 4096).
+constexpr int kRouterBlock = 512;
+constexpr int kMaxRouterBlocks = 8;
+
+// After the chain over 64-input chunk c (of nch) has run into acc: at the
+// end of a 512-input block, fold the block's sum into tot (the first block
+// sets it) and start a fresh chain.
+template <int N>
+__device__ __forceinline__ void block_end(int c, int nch, float (&acc)[N], float (&tot)[N]) {
+    if (((c + 1) & (kRouterBlock / 64 - 1)) == 0 || c + 1 == nch) {
+        const bool first = c < kRouterBlock / 64;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            tot[i] = first ? acc[i] : tot[i] + acc[i];
+            acc[i] = 0.0f;
+        }
+    }
+}
 
 // Order-preserving image of a float in uint32 (a larger float maps to a
 // larger value; -0 is folded to +0 first); 0 lies below every image.
@@ -57,17 +81,13 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // logits' order images, then the lowest expert holding it: experts of slot
 // j are 64 j + lane, so the first slot whose ballot hits, at its lowest
 // lane (ties go to the lower index). Writes ids / weights for one token.
-template <typename LoadFn>
-__device__ __forceinline__ void wave_topk(LoadFn load, int E, int K, int renorm,
-                                          int32_t *ids, float *wts) {
-    constexpr int NJ = kMaxE / kWave;
+constexpr int kTopkSlots = kMaxE / kWave;
+
+// The selection over the order images o (0 for experts past E).
+__device__ __forceinline__ void wave_topk_keys(uint32_t (&o)[kTopkSlots], int K, int renorm,
+                                               int32_t *ids, float *wts) {
+    constexpr int NJ = kTopkSlots;
     const int lane = threadIdx.x & (kWave - 1);
-    uint32_t o[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int e = lane + j * kWave;
-        o[j] = e < E ? ord32(load(e)) : 0u;
-    }
     float my_logit = 0.0f;
     int my_id = 0;
     for (int r = 0; r < K; ++r) {
@@ -96,19 +116,51 @@ __device__ __forceinline__ void wave_topk(LoadFn load, int E, int K, int renorm,
     if (lane < K) { ids[lane] = my_id; wts[lane] = p; }
 }
 
-// Logits given: one wave per token.
+template <typename LoadFn>
+__device__ __forceinline__ void wave_topk(LoadFn load, int E, int K, int renorm,
+                                          int32_t *ids, float *wts) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t o[kTopkSlots];
+#pragma unroll
+    for (int j = 0; j < kTopkSlots; ++j) {
+        const int e = lane + j * kWave;
+        o[j] = e < E ? ord32(load(e)) : 0u;
+    }
+    wave_topk_keys(o, K, renorm, ids, wts);
+}
+
+// Logits given, or P block sums of them ([P][T][E], added in block
+// order): one wave per token.
 __global__ void __launch_bounds__(256) route_given_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, int E, int K,
-    int renorm, int32_t *__restrict__ ids, float *__restrict__ wts) {
+    int renorm, int P, int32_t *__restrict__ ids, float *__restrict__ wts) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const float *row = logits + (size_t)t * E;
-    auto load = [&](int e) {
-        float v = row[e];
-        if (bias) v = v + bias[e];
-        return v;
-    };
-    wave_topk(load, E, K, renorm, ids + (size_t)t * K, wts + (size_t)t * K);
+    const size_t pstride = (size_t)T * E;
+    const int lane = threadIdx.x & (kWave - 1);
+    // every slot's block values (and bias) loaded before any addition:
+    // unconditional loads at clamped addresses, the extra ones unused
+    float q[kTopkSlots][kMaxRouterBlocks], bv[kTopkSlots];
+#pragma unroll
+    for (int j = 0; j < kTopkSlots; ++j) {
+        const int e = min(lane + j * kWave, E - 1);
+#pragma unroll
+        for (int p = 0; p < kMaxRouterBlocks; ++p)
+            q[j][p] = row[min(p, P - 1) * pstride + e];
+        bv[j] = bias ? bias[e] : 0.0f;
+    }
+    uint32_t o[kTopkSlots];
+#pragma unroll
+    for (int j = 0; j < kTopkSlots; ++j) {
+        float v = q[j][0];
+#pragma unroll
+        for (int p = 1; p < kMaxRouterBlocks; ++p)
+            if (p < P) v = v + q[j][p];
+        if (bias) v = v + bv[j];
+        o[j] = lane + j * kWave < E ? ord32(v) : 0u;
+    }
+    wave_topk_keys(o, K, renorm, ids + (size_t)t * K, wts + (size_t)t * K);
 }
 
 // Logits computed: a plain fp32 SIMT GEMM, logits[t][e] = x[t] . wT[:, e],
@@ -165,9 +217,9 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
         }
     };
 
-    float acc[4];
+    float acc[4], tot[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) acc[i] = tot[i] = 0.0f;
     const int nch = H / kRtKC;
     load(0);
     store(0);
@@ -184,6 +236,7 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
             acc[2] = __builtin_fmaf(xa.z, w, acc[2]);
             acc[3] = __builtin_fmaf(xa.w, w, acc[3]);
         }
+        block_end(c, nch, acc, tot);
         if (c + 1 < nch) store(b ^ 1);
         __syncthreads();
     }
@@ -193,7 +246,7 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = t0 + 4 * wave + i;
-        if (t < T) logits[(size_t)t * E + e] = bias ? acc[i] + bv : acc[i];
+        if (t < T) logits[(size_t)t * E + e] = bias ? tot[i] + bv : tot[i];
     }
 }
 
@@ -423,7 +476,7 @@ __global__ void __launch_bounds__(256) router_tiled_kernel(
     RouterWeightPipe<kRtKC, NP, kXStage> pipe(wT, E, e0, H, tid, xsrc, &xs[0][0][0]);
     pipe.prime();
 
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     pipe.run(ws, [&](int c, float (*st)[kRtExp]) {
         const float *xw = &xs[c & 1][4 * wave][lane & 15];
         float xq[2][4], w[2][16];
@@ -442,6 +495,7 @@ __global__ void __launch_bounds__(256) router_tiled_kernel(
             fma4x4_row_bcast<8>(acc, xq[m & 1], &w[m & 1][8]);
             fma4x4_row_bcast<12>(acc, xq[m & 1], &w[m & 1][12]);
         }
+        block_end(c, pipe.nch, acc, tot);
     });
     const int e = e0 + lane;
     if (e >= E) return;
@@ -449,17 +503,17 @@ __global__ void __launch_bounds__(256) router_tiled_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = t0 + 4 * wave + i;
-        if (t < T) logits[(size_t)t * E + e] = bias ? acc[i] + bv : acc[i];
+        if (t < T) logits[(size_t)t * E + e] = bias ? tot[i] + bv : tot[i];
     }
 }
 
 // Top-K of logits that are already final (bias, if any, folded in by the
 // caller) or given plus an optional bias.
 moe_status_t launch_topk(const float *logits, const float *bias, int T, int E, int K, int renorm,
-                         int32_t *ids, float *wts, hipStream_t s) {
+                         int32_t *ids, float *wts, hipStream_t s, int P) {
     if (T == 0) return MOE_OK;
     hipLaunchKernelGGL(route_given_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, bias, T, E,
-                       K, renorm, ids, wts);
+                       K, renorm, P, ids, wts);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -498,38 +552,26 @@ __device__ __forceinline__ void fma16_row_bcast(float &acc, float xq, const floa
 
 // ---- small batches: rows staged in LDS, one token per wave ------------------
 // W tokens x 64 experts a work group of W waves (W = 2 or 4), one token per
-// wave: a batch of a few tokens has too few waves for the tiled kernels
-// above, and each wave runs one 4096-step chain. The group first stages its W rows in LDS
-// as float32: the bf16 activations widened (NORM = false) or, fused, the
-// RMSNorm of W fp32 residual rows (NORM = true), whose float32 sums of
-// squares follow rmsnorm_kernel's 256-thread order exactly (each thread
-// stands in for 4 / W of those threads: same columns, same wave shuffles,
-// same block sum), so the 16-bit rows are bitwise the ones moe_rmsnorm
-// writes; the groups of the first expert block also write them to a_out for
-// the experts. In the chain each input costs one FMA (x broadcast by DPP
-// from one 4-byte LDS read per 16 inputs) and half a 4-byte-pair LDS read
-// of weights; what bounds it is that instruction stream of one wave (about
-// 19 cycles per input measured, against the 6.5-cycle latency of the FMA
-// chain), not LDS bandwidth or the weight loads: prefetch depth and chunk
-// size change nothing, and neither does W, apart from the number of groups.
-// Same chain, same order as the other router kernels.
+// wave, the logits of moe_router_logits: a batch of a few tokens has too few
+// waves for the tiled kernel above. The group stages its W bf16 rows in LDS
+// widened to float32; each wave runs its token's blocks in turn. In the
+// chain each input costs one FMA (x broadcast by DPP from one 4-byte LDS
+// read per 16 inputs) and half a 4-byte-pair LDS read of weights; what
+// bounds it is that instruction stream of one wave (about 19 cycles per
+// input measured, against 7 for the bare DPP FMA chain). The routing calls
+// run the block sums side by side instead (router_block_kernel below).
 constexpr int kRowsMaxT = 192;                   // batches up to this size (beyond it
                                                  // router_tiled_kernel is faster: T = 256,
                                                  // 64 us against 69)
 constexpr int kRowsMaxH = 4096;                  // W float32 rows in LDS
 
-template <bool NORM, int W>
+template <int W>
 __global__ void __launch_bounds__(64 * W) router_rows_kernel(
-    const void *__restrict__ xin, const float *__restrict__ gain, float eps,
-    const float *__restrict__ wT, const float *__restrict__ bias, int T, int H, int E,
-    uint16_t *__restrict__ a_out, float *__restrict__ logits) {
+    const uint16_t *__restrict__ x, const float *__restrict__ wT,
+    const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
     constexpr int NT = 64 * W, KC = 64, NP = 2;
-    static_assert(W == 1 || W == 2 || W == 4, "norm threads must split evenly");
-    constexpr int kVT = 4 / W;                   // 256-thread norm threads per thread
-    constexpr int kCols = kRowsMaxH / 1024;      // float4 groups of a row per norm thread
     __shared__ __attribute__((aligned(16))) float ws[2][KC][kRtExp];
     __shared__ __attribute__((aligned(16))) float as[W][kRowsMaxH];
-    __shared__ float red[W][4];
     const int t0 = blockIdx.x * W, e0 = blockIdx.y * kRtExp;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -537,88 +579,16 @@ __global__ void __launch_bounds__(64 * W) router_rows_kernel(
     // the router weight's first chunks are in flight while the rows stage
     RouterWeightPipe<KC, NP, kXNone, NT> pipe(wT, E, e0, H, tid);
     pipe.prime();
-
-    if (!NORM) {
-        // bf16 rows widened (rows past T repeat row t0; never stored)
-        const uint16_t *x = (const uint16_t *)xin;
+    // bf16 rows widened (rows past T repeat row t0; never stored)
 #pragma unroll
-        for (int i = 0; i < W; ++i) {
-            const int t = t0 + i < T ? t0 + i : t0;
-            for (int c = tid * 4; c < H; c += 4 * NT) {
-                const uint2 v = *(const uint2 *)(x + (size_t)t * H + c);
-                *(f32x4_t *)&as[i][c] = f32x4_t{__uint_as_float(v.x << 16),
-                                                __uint_as_float(v.x & 0xFFFF0000u),
-                                                __uint_as_float(v.y << 16),
-                                                __uint_as_float(v.y & 0xFFFF0000u)};
-            }
-        }
-    } else {
-        // RMSNorm of the W rows (rows past T repeat row t0; not stored).
-        // Norm thread tid + NT u of rmsnorm_kernel's 256 (its wave: wave +
-        // W u, its lane: lane) owns columns 4 (tid + NT u) + 1024 j. All of a
-        // thread's values are loaded at once.
-        const float *res = (const float *)xin;
-        f32x4_t v[W][kVT][kCols], g[kVT][kCols];
-#pragma unroll
-        for (int u = 0; u < kVT; ++u)
-#pragma unroll
-            for (int j = 0; j < kCols; ++j) {
-                const int c = (tid + NT * u) * 4 + 1024 * j;
-                g[u][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if (c < H) {
-                    if (gain) g[u][j] = *(const f32x4_t *)(gain + c);
-#pragma unroll
-                    for (int i = 0; i < W; ++i) {
-                        const int t = t0 + i < T ? t0 + i : t0;
-                        v[i][u][j] = *(const f32x4_t *)(res + (size_t)t * H + c);
-                    }
-                }
-            }
-#pragma unroll
-        for (int i = 0; i < W; ++i)
-#pragma unroll
-            for (int u = 0; u < kVT; ++u) {
-                float ss = 0.0f;
-#pragma unroll
-                for (int j = 0; j < kCols; ++j) {
-                    if ((tid + NT * u) * 4 + 1024 * j < H) {
-                        const f32x4_t q = v[i][u][j];
-                        ss = ss + q.x * q.x;
-                        ss = ss + q.y * q.y;
-                        ss = ss + q.z * q.z;
-                        ss = ss + q.w * q.w;
-                    }
-                }
-#pragma unroll
-                for (int m = 32; m >= 1; m >>= 1) ss = ss + __shfl_xor(ss, m, kWave);
-                if (lane == 0) red[i][wave + W * u] = ss;
-            }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < W; ++i) {
-            const float tot = ((red[i][0] + red[i][1]) + red[i][2]) + red[i][3];
-            const float r = __builtin_sqrtf(tot / (float)H + eps);
-#pragma unroll
-            for (int u = 0; u < kVT; ++u)
-#pragma unroll
-                for (int j = 0; j < kCols; ++j) {
-                    const int c = (tid + NT * u) * 4 + 1024 * j;
-                    if (c < H) {
-                        const f32x4_t q = v[i][u][j], gg = g[u][j];
-                        const uint32_t lo =
-                            f32_to_bf16_bits((q.x / r) * (1.0f + gg.x)) |
-                            ((uint32_t)f32_to_bf16_bits((q.y / r) * (1.0f + gg.y)) << 16);
-                        const uint32_t hi =
-                            f32_to_bf16_bits((q.z / r) * (1.0f + gg.z)) |
-                            ((uint32_t)f32_to_bf16_bits((q.w / r) * (1.0f + gg.w)) << 16);
-                        *(f32x4_t *)&as[i][c] = f32x4_t{__uint_as_float(lo << 16),
-                                                        __uint_as_float(lo & 0xFFFF0000u),
-                                                        __uint_as_float(hi << 16),
-                                                        __uint_as_float(hi & 0xFFFF0000u)};
-                        if (blockIdx.y == 0 && t0 + i < T)
-                            *(uint2 *)(a_out + (size_t)(t0 + i) * H + c) = make_uint2(lo, hi);
-                    }
-                }
+    for (int i = 0; i < W; ++i) {
+        const int t = t0 + i < T ? t0 + i : t0;
+        for (int c = tid * 4; c < H; c += 4 * NT) {
+            const uint2 v = *(const uint2 *)(x + (size_t)t * H + c);
+            *(f32x4_t *)&as[i][c] = f32x4_t{__uint_as_float(v.x << 16),
+                                            __uint_as_float(v.x & 0xFFFF0000u),
+                                            __uint_as_float(v.y << 16),
+                                            __uint_as_float(v.y & 0xFFFF0000u)};
         }
     }
     // the rows reach LDS before the chains read them: run() stores the first
@@ -626,7 +596,7 @@ __global__ void __launch_bounds__(64 * W) router_rows_kernel(
 
     // lane j of every 16-lane row reads inputs 16 m + j of the chunk
     const float *xr = &as[wave][lane & 15];
-    float acc = 0.0f;
+    float acc[1] = {0.0f}, tot[1] = {0.0f};
     pipe.run(ws, [&](int c, float (*st)[kRtExp]) {
         // 16 inputs at a time, the reads of the next 16 issued before the
         // FMAs of these (double-buffered in registers)
@@ -640,11 +610,12 @@ __global__ void __launch_bounds__(64 * W) router_rows_kernel(
 #pragma unroll
         for (int m = 0; m < KC / 16; ++m) {
             if (m + 1 < KC / 16) read(m + 1, (m + 1) & 1);
-            fma16_row_bcast(acc, xq[m & 1], w[m & 1]);
+            fma16_row_bcast(acc[0], xq[m & 1], w[m & 1]);
         }
+        block_end(c, pipe.nch, acc, tot);
     });
     const int e = e0 + lane, t = t0 + wave;
-    if (e < E && t < T) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
+    if (e < E && t < T) logits[(size_t)t * E + e] = bias ? tot[0] + bias[e] : tot[0];
 }
 
 // tokens per work group, measured at H = 4096, E = 352: W = 2 up to 64
@@ -653,17 +624,191 @@ __global__ void __launch_bounds__(64 * W) router_rows_kernel(
 // W = 4 beyond (T = 256: 68 us against 79 us at W = 2)
 constexpr int kRowsW2MaxT = 64;
 
-template <bool NORM>
-static void launch_rows(const void *xin, const float *gain, float eps, int T, int H,
-                        const float *wT, const float *bias, int E, void *a_out, float *logits,
-                        hipStream_t s) {
+static void launch_rows(const void *x, int T, int H, const float *wT, const float *bias, int E,
+                        float *logits, hipStream_t s) {
     const int eb = (E + kRtExp - 1) / kRtExp;
     if (T <= kRowsW2MaxT)
-        hipLaunchKernelGGL((router_rows_kernel<NORM, 2>), dim3((T + 1) / 2, eb), dim3(128), 0, s,
-                           xin, gain, eps, wT, bias, T, H, E, (uint16_t *)a_out, logits);
+        hipLaunchKernelGGL((router_rows_kernel<2>), dim3((T + 1) / 2, eb), dim3(128), 0, s,
+                           (const uint16_t *)x, wT, bias, T, H, E, logits);
     else
-        hipLaunchKernelGGL((router_rows_kernel<NORM, 4>), dim3((T + 3) / 4, eb), dim3(256), 0, s,
-                           xin, gain, eps, wT, bias, T, H, E, (uint16_t *)a_out, logits);
+        hipLaunchKernelGGL((router_rows_kernel<4>), dim3((T + 3) / 4, eb), dim3(256), 0, s,
+                           (const uint16_t *)x, wT, bias, T, H, E, logits);
+}
+
+// ---- small batches, block sums side by side --------------------------------
+// One work group per (4 TW tokens, 64 experts, 512-input block), TW tokens
+// per wave: the tiled kernel's layout (x by DPP row broadcast, the weight
+// chunk shared through LDS by the group's waves) over one block of the
+// canonical sum, whose chains' values go to part [block][T][E] for the
+// top-K to add up in block order. A token's 8 chains of 512 steps run side
+// by side instead of one chain of 4096. Fewer tokens per wave shorten a
+// wave's instruction stream (TW DPP FMAs per input); more tokens per group
+// read each 128 KB weight slice for more tokens (the batch streams the
+// 5.8 MB router weight once per 4 TW tokens). Groups are ordered (expert
+// block, input block) major in contiguous ranges per XCD, so the groups
+// sharing a weight slice share an L2.
+// The group first stages its rows' block inputs in LDS as float32: the
+// bf16 activations widened (NORM = false), or (NORM = true) the RMSNorm of
+// the float32 residual rows, bf16-rounded and widened. The norm's sums of
+// squares follow rmsnorm_kernel exactly (the group's 256 threads are that
+// kernel's 256 threads, one row after the other), so the rows are bitwise
+// the ones moe_rmsnorm writes; the groups of the first expert block write
+// their block's columns of them to a_out for the experts.
+constexpr int kBlkPitch = kRouterBlock + 4;      // floats per staged row: the 4 pad
+                                                 // floats keep 16-byte alignment
+
+// TW tokens per wave, 4 TW per group; a wave runs its tokens' chains one
+// 16-input DPP broadcast FMA block after the other.
+template <bool NORM, int TW>
+__global__ void __launch_bounds__(256) router_block_kernel(
+    const void *__restrict__ xin, const float *__restrict__ gain, float eps,
+    const float *__restrict__ wT, int T, int H, int E, uint16_t *__restrict__ a_out,
+    float *__restrict__ part) {
+    constexpr int BT = 4 * TW;                   // tokens per group
+    constexpr int TPR = 256 / BT;                // staging threads per row
+    static_assert(TW == 1 || TW == 2, "tokens per wave");
+    __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
+    __shared__ __attribute__((aligned(16))) float xs[BT][kBlkPitch];
+    __shared__ float red[BT][4];
+    const int nb = gridDim.x, b = blockIdx.x, xq8 = nb / 8, xr8 = nb % 8, xcd = b % 8;
+    const int lid = xcd * xq8 + (xcd < xr8 ? xcd : xr8) + b / 8;
+    const int ntb = (T + BT - 1) / BT, P = (H + kRouterBlock - 1) / kRouterBlock;
+    const int tb = lid % ntb, rest = lid / ntb, pb = rest % P, eb = rest / P;
+    const int t0 = tb * BT, e0 = eb * kRtExp;
+    const int k0 = pb * kRouterBlock, kn = min(kRouterBlock, H - k0);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // the block's first weight chunks are in flight while the rows stage
+    RouterWeightPipe<kRtKC, 2, kXNone> pipe(wT + (size_t)k0 * E, E, e0, kn, tid);
+    pipe.prime();
+
+    // staging roles: row tid / TPR, columns 4 (tid % TPR) + 4 TPR i of the
+    // block (rows past T repeat row t0; their logits are not stored)
+    const int sr = tid / TPR, sc = (tid % TPR) * 4;
+    const int st_row = t0 + sr < T ? t0 + sr : t0;
+    if (!NORM) {
+        const uint16_t *x = (const uint16_t *)xin + (size_t)st_row * H + k0;
+        for (int c = sc; c < kn; c += 4 * TPR) {
+            const uint2 v = *(const uint2 *)(x + c);
+            *(f32x4_t *)&xs[sr][c] = f32x4_t{__uint_as_float(v.x << 16),
+                                             __uint_as_float(v.x & 0xFFFF0000u),
+                                             __uint_as_float(v.y << 16),
+                                             __uint_as_float(v.y & 0xFFFF0000u)};
+        }
+    } else {
+        const float *res = (const float *)xin;
+        // sums of squares, row after row: thread p adds columns 4p .. 4p+3,
+        // 1024 + 4p .. in order, the wave folds by xor-shuffles 32 .. 1, the
+        // four wave sums add left to right (after the barrier); four rows'
+        // loads in flight at a time
+        constexpr int kCols = kRowsMaxH / 1024;
+        for (int r0 = 0; r0 < BT; r0 += 4) {
+            f32x4_t v[4][kCols];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + r0 + i < T ? t0 + r0 + i : t0;
+#pragma unroll
+                for (int j = 0; j < kCols; ++j) {
+                    const int c = tid * 4 + 1024 * j;
+                    if (c < H) v[i][j] = *(const f32x4_t *)(res + (size_t)t * H + c);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float ss = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kCols; ++j) {
+                    if (tid * 4 + 1024 * j < H) {
+                        const f32x4_t q = v[i][j];
+                        ss = ss + q.x * q.x;
+                        ss = ss + q.y * q.y;
+                        ss = ss + q.z * q.z;
+                        ss = ss + q.w * q.w;
+                    }
+                }
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) ss = ss + __shfl_xor(ss, m, kWave);
+                if (lane == 0) red[r0 + i][wave] = ss;
+            }
+        }
+        __syncthreads();
+        const float tot = ((red[sr][0] + red[sr][1]) + red[sr][2]) + red[sr][3];
+        const float rr = __builtin_sqrtf(tot / (float)H + eps);
+        const float *rrow = res + (size_t)st_row * H + k0;
+        for (int c = sc; c < kn; c += 4 * TPR) {
+            const f32x4_t q = *(const f32x4_t *)(rrow + c);
+            f32x4_t gg = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (gain) gg = *(const f32x4_t *)(gain + k0 + c);
+            const uint32_t lo = f32_to_bf16_bits((q.x / rr) * (1.0f + gg.x)) |
+                                ((uint32_t)f32_to_bf16_bits((q.y / rr) * (1.0f + gg.y)) << 16);
+            const uint32_t hi = f32_to_bf16_bits((q.z / rr) * (1.0f + gg.z)) |
+                                ((uint32_t)f32_to_bf16_bits((q.w / rr) * (1.0f + gg.w)) << 16);
+            *(f32x4_t *)&xs[sr][c] = f32x4_t{__uint_as_float(lo << 16),
+                                             __uint_as_float(lo & 0xFFFF0000u),
+                                             __uint_as_float(hi << 16),
+                                             __uint_as_float(hi & 0xFFFF0000u)};
+            if (eb == 0 && t0 + sr < T)
+                *(uint2 *)(a_out + (size_t)(t0 + sr) * H + k0 + c) = make_uint2(lo, hi);
+        }
+    }
+    // the rows reach LDS before the chains read them: run() stores the first
+    // chunk and synchronizes before its first step
+
+    float acc[TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) acc[i] = 0.0f;
+    pipe.run(ws, [&](int c, float (*st)[kRtExp]) {
+        // lane j of every 16-lane row reads inputs 16 m + j of the chunk
+        const float *xw = &xs[TW * wave][c * kRtKC + (lane & 15)];
+        float xq[2][TW], w[2][16];
+        auto read = [&](int m, int bb) {
+#pragma unroll
+            for (int i = 0; i < TW; ++i) xq[bb][i] = xw[i * kBlkPitch + 16 * m];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) w[bb][j] = st[16 * m + j][lane];
+        };
+        read(0, 0);
+#pragma unroll
+        for (int m = 0; m < kRtKC / 16; ++m) {
+            if (m + 1 < kRtKC / 16) read(m + 1, (m + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < TW; ++i) fma16_row_bcast(acc[i], xq[m & 1][i], w[m & 1]);
+        }
+    });
+    const int e = e0 + lane;
+    if (e >= E) return;
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const int t = t0 + TW * wave + i;
+        if (t < T) part[((size_t)pb * T + t) * E + e] = acc[i];
+    }
+}
+
+template <bool NORM, int TW>
+static void launch_block_tw(const void *xin, const float *gain, float eps, int T, int H,
+                            const float *wT, int E, void *a_out, float *part, hipStream_t s) {
+    const int n = ((T + 4 * TW - 1) / (4 * TW)) * ((E + kRtExp - 1) / kRtExp) *
+                  ((H + kRouterBlock - 1) / kRouterBlock);
+    hipLaunchKernelGGL((router_block_kernel<NORM, TW>), dim3(n), dim3(256), 0, s, xin, gain, eps,
+                       wT, T, H, E, (uint16_t *)a_out, part);
+}
+
+// Tokens per wave, measured on moe_norm_route (H = 4096, E = 352, graph
+// replay, with the top-K): one up to 64 tokens (T = 1: 14.1 us, T = 32:
+// 18.7 us, against 17.6 and 19.2 with two and 24.9 and 26.5 with four; the
+// kernels with one 4096-step chain per token took 42 and 44 us), two
+// beyond (T = 128: 29.0 us against 36.0 with one and 33.5 with four; T =
+// 192: 41.6 against 49.1 and 50.1).
+constexpr int kBlkTw1MaxT = 64;
+
+template <bool NORM>
+static void launch_block(const void *xin, const float *gain, float eps, int T, int H,
+                         const float *wT, int E, void *a_out, float *part, hipStream_t s) {
+    if (T <= kBlkTw1MaxT)
+        launch_block_tw<NORM, 1>(xin, gain, eps, T, H, wT, E, a_out, part, s);
+    else
+        launch_block_tw<NORM, 2>(xin, gain, eps, T, H, wT, E, a_out, part, s);
 }
 
 moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, const float *bias,
@@ -671,7 +816,7 @@ moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, c
     if (T == 0) return MOE_OK;
     const dim3 grid((T + kRtTok - 1) / kRtTok, (E + kRtExp - 1) / kRtExp);
     if (x_dtype == MOE_BF16 && T <= kRowsMaxT && H <= kRowsMaxH)
-        launch_rows<false>(x, nullptr, 0.f, T, H, wT, bias, E, nullptr, logits, s);
+        launch_rows(x, T, H, wT, bias, E, logits, s);
     else if (x_dtype == MOE_BF16)
         hipLaunchKernelGGL((router_tiled_kernel<2>), dim3(grid.x * grid.y), dim3(256), 0, s,
                            (const uint16_t *)x, wT, bias, T, H, E, logits);
@@ -684,11 +829,47 @@ moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, c
 
 bool norm_route_fused(int T, int H, int E) { return T <= kRowsMaxT && H <= kRowsMaxH; }
 
-moe_status_t launch_norm_router_logits(const float *res, const float *gain, float eps, int T,
-                                       int H, const float *wT, const float *bias, int E,
-                                       void *a_out, float *logits, hipStream_t s) {
+int router_blocks(int H) { return (H + kRouterBlock - 1) / kRouterBlock; }
+
+static_assert(kRowsMaxH / kRouterBlock <= kMaxRouterBlocks, "block sums the top-K adds");
+
+// The block-sum path: small bf16 batches.
+static bool block_path(int T, int H, int x_dtype) {
+    return x_dtype == MOE_BF16 && T <= kRowsMaxT && H <= kRowsMaxH;
+}
+
+// Workspace floats of the routing calls: the block sums on that path,
+// else the logits; and the most any H <= kMaxDim can need.
+size_t router_ws_floats(int T, int H, int E, int x_dtype) {
+    return (size_t)(block_path(T, H, x_dtype) ? router_blocks(H) : 1) * T * E;
+}
+size_t router_ws_floats_max(int T, int E) {
+    return (size_t)(T <= kRowsMaxT ? kRowsMaxH / kRouterBlock : 1) * T * E;
+}
+
+// Block sums per 512-input block side by side for small bf16 batches
+// (T <= 192, H <= 4096): [router_blocks(H)][T][E]
+// into `part`, *P = router_blocks(H); otherwise the logits (no bias) with
+// *P = 1. Either way route_given_kernel adds them up in block order.
+moe_status_t launch_router_scores(const void *x, int x_dtype, const float *wT, int T, int H,
+                                  int E, float *part, int *P, hipStream_t s) {
+    if (block_path(T, H, x_dtype)) {
+        *P = router_blocks(H);
+        if (T == 0) return MOE_OK;
+        launch_block<false>(x, nullptr, 0.f, T, H, wT, E, nullptr, part, s);
+        MOE_LAUNCH_CHECK();
+        return MOE_OK;
+    }
+    *P = 1;
+    return launch_router_logits(x, x_dtype, wT, nullptr, T, H, E, part, s);
+}
+
+// The fused norm and router, block sums [router_blocks(H)][T][E] into part.
+moe_status_t launch_norm_router_scores(const float *res, const float *gain, float eps, int T,
+                                       int H, const float *wT, int E, void *a_out, float *part,
+                                       hipStream_t s) {
     if (T == 0) return MOE_OK;
-    launch_rows<true>(res, gain, eps, T, H, wT, bias, E, a_out, logits, s);
+    launch_block<true>(res, gain, eps, T, H, wT, E, a_out, part, s);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -129,11 +129,18 @@ def test_route_topk_validation(L):
     assert R(p, 1, p, n, n, 4, 64, 16, 2, 1, p, p, n, big, n) == B.MOE_ERR_INVALID_ARG
     assert R(p, 1, p, n, n, 4, 64, 16, 2, 1, p, p, p, 4 * 16 * 4 - 1, n) == \
         B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # bf16 up to 192 tokens: one float per 512-input block, token and expert
+    assert R(p, 2, p, n, n, 4, 1024, 16, 2, 1, p, p, p, 2 * 4 * 16 * 4 - 1, n) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
     assert R(n, 0, n, p, n, 4, 0, 16, 2, 1, n, p, n, 0, n) == B.MOE_ERR_INVALID_ARG
     # T == 0 is a no-op that touches nothing
     assert R(n, 0, n, p, n, 0, 0, 16, 2, 1, p, p, n, 0, n) == B.MOE_OK
     assert B.moe_route_workspace(2048, 352, True) == 2048 * 352 * 4
     assert B.moe_route_workspace(2048, 352, False) == 0
+    # up to 192 tokens the workspace holds one sum per 512-input block
+    # (8 for H <= 4096)
+    assert B.moe_route_workspace(192, 352, True) == 8 * 192 * 352 * 4
+    assert B.moe_route_workspace(193, 352, True) == 193 * 352 * 4
 
 
 def test_router_logits_validation(L):
@@ -332,7 +339,8 @@ def test_norm_route_validation(L):
     """Argument errors of moe_norm_route are found before any launch."""
     F = L.moe_norm_route
     p = ctypes.c_void_p(FAKE)
-    ok = (p, None, 1e-5, 8, 4096, p, None, 352, 8, 1, p, p, p, p, 8 * 352 * 4, None)
+    # the workspace: one float per 512-input block, token and expert
+    ok = (p, None, 1e-5, 8, 4096, p, None, 352, 8, 1, p, p, p, p, 8 * 8 * 352 * 4, None)
     bad = [
         ((None,) + ok[1:], B.MOE_ERR_INVALID_ARG),                     # residual
         (ok[:2] + (-1.0,) + ok[3:], B.MOE_ERR_INVALID_ARG),            # eps
@@ -343,7 +351,7 @@ def test_norm_route_validation(L):
         (ok[:8] + (17,) + ok[9:], B.MOE_ERR_INVALID_ARG),              # K > 16
         (ok[:10] + (None,) + ok[11:], B.MOE_ERR_INVALID_ARG),          # a_out
         (ok[:13] + (None,) + ok[14:], B.MOE_ERR_INVALID_ARG),          # ws
-        (ok[:14] + (8 * 352 * 4 - 4,) + ok[15:], B.MOE_ERR_WORKSPACE_TOO_SMALL),
+        (ok[:14] + (8 * 8 * 352 * 4 - 4,) + ok[15:], B.MOE_ERR_WORKSPACE_TOO_SMALL),
         (ok[:10] + (ctypes.c_void_p(FAKE + 8),) + ok[11:], B.MOE_ERR_INVALID_ARG),  # alignment
     ]
     for args, want in bad:

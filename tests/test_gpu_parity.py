@@ -125,7 +125,7 @@ def test_route_from_router_weight_tiny(dev, act):
                                          (3, 64, 8, "bf16"), (600, 320, 24, "bf16"),
                                          (8, 256, 16, "f16"), (70, 192, 20, "f16")])
 def test_router_logits_bitwise(dev, T, Hh, Ee, act):
-    """The canonical float32 fma chain, bit for bit against the C oracle
+    """The canonical float32 block sum, bit for bit against the C oracle
     (partial token and expert tiles included; bf16 inputs whose 64-input
     chunk count is below or not a multiple of the weight prefetch depth)."""
     x = synth.activations(T, Hh, act, 5)
@@ -136,6 +136,36 @@ def test_router_logits_bitwise(dev, T, Hh, Ee, act):
                                   None if bias is None else torch.from_numpy(bias).to(dev))
         want = OR.router_logits(x.float().numpy(), wT, bias)
         assert _bits_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("T", [3, 200])
+def test_router_block_order_every_path(dev, T):
+    """Inputs whose logit depends on where the canonical sum starts a fresh
+    chain: x w = 1 at input 511, -1 at 512 and 2^-30 at 513 give 2^-30 in
+    one 1024-step chain but 0 in the two 512-input blocks (-1 + 2^-30
+    rounds to -1), against a lone 2^-31 for expert 1. Every router path
+    returns the blocks' answer, so expert 1 is the top-1: the bf16 rows
+    kernel (T = 3: logits in turn, block sums side by side for the top-K),
+    the tiled kernel (T = 200), the f16 kernel, and the fused norm (the
+    +-1 rows normalise to +-16 exactly with eps = 0)."""
+    Hh, Ee = 1024, 8
+    xv = np.zeros((T, Hh), np.float32)
+    xv[:, [511, 512, 513, 700]] = [1.0, -1.0, 1.0, 1.0]
+    wT = np.zeros((Hh, Ee), np.float32)
+    wT[[511, 512, 513], 0] = [1.0, 1.0, 2.0 ** -30]
+    wT[700, 1] = 2.0 ** -31
+    want = OR.router_logits(xv, wT)
+    assert want[0, 0] == 0.0 and want[0, 1] == 2.0 ** -31
+    wd = torch.from_numpy(wT).to(dev)
+    for dt in (torch.bfloat16, torch.float16):
+        x = torch.from_numpy(xv).to(dt).to(dev)
+        got = B.moe_router_logits(x, wd)
+        assert _bits_equal(got.cpu().numpy(), want)
+        ids, w = B.moe_route_topk(1, x=x, router_wT=wd)
+        assert (ids.cpu().numpy() == 1).all()
+    a, ids, w = B.moe_norm_route(torch.from_numpy(xv).to(dev), wd, 1, eps=0.0)
+    assert (a.float().cpu().numpy()[:, [511, 512, 513, 700]] == [16.0, -16.0, 16.0, 16.0]).all()
+    assert (ids.cpu().numpy() == 1).all()
 
 
 @pytest.mark.parametrize("T,zipf", [(37, False), (2048, False), (300, True)])
@@ -576,10 +606,10 @@ def test_forward_nvfp4_every_scale_byte(dev, T):
     (9, 256, 16, 2, True, True), (4, 1024, 512, 16, False, False), (3, 192, 20, 3, True, True),
     (6, 8192, 64, 4, True, True)])
 def test_norm_route_matches_separate_calls(dev, T, Hh, Ee, Kk, with_bias, with_gain):
-    """moe_norm_route (norm fused into the router up to 192 tokens and H = 4096,
-    two tokens per work group up to 64, four beyond; separate kernels past
-    that: T = 193, H = 8192) is bitwise
-    moe_rmsnorm + moe_route_topk, which the tests above pin to the oracle."""
+    """moe_norm_route (norm fused into the block-sum router up to 192 tokens
+    and H = 4096, one token per wave up to 64, two beyond; separate kernels
+    past that: T = 193, H = 8192) is bitwise moe_rmsnorm + moe_route_topk,
+    which the tests above pin to the oracle."""
     r = torch.from_numpy(synth.normal((T, Hh), 1.0, 14, 0, synth.T_X, T)).to(dev)
     gain = torch.from_numpy(synth.norm_weight(Hh, 14, 0)).to(dev) if with_gain else None
     wT = torch.from_numpy(synth.router_weight_T(Hh, Ee, 14)).to(dev)
@@ -601,8 +631,8 @@ def test_norm_route_against_oracle(dev, T, Hh, Ee, Kk, with_bias, with_gain):
     """moe_norm_route against the oracle directly: the layer input a is the
     oracle's float32 RMSNorm rounded to bf16, bit for bit; the expert ids are
     the oracle's top-K of its router chain on that a, bit for bit; weights
-    within 1e-5. T <= 192 runs the fused kernel (one and two token groups
-    per wave count), T = 193 and H = 8192 the separate kernels."""
+    within 1e-5. T <= 192 runs the fused block-sum kernel (one and two
+    tokens per wave), T = 193 and H = 8192 the separate kernels."""
     r = synth.normal((T, Hh), 1.0, 15, 0, synth.T_X, T)
     r[0] *= 300.0                                          # rows of other scales
     if T > 2:
