@@ -61,7 +61,7 @@ moe_status_t launch_act_quant(const void *in, int dtype, int64_t rows, int k, fl
 DenseSplit dense_plan(int T, int H, int F);
 bool dense_shape_ok(int H, int F);
 int gemv_tile_m();
-int gemv_mx_tile_m();
+int gemv_mx_tile_m(int T);
 int gemm_tile_m();
 int gemm_group();
 int gemm_bn();
@@ -248,7 +248,7 @@ FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F
     FwdPlan p;
     p.mfma = use_mfma(ex, T, K);
     p.tile_m = p.mfma ? gemm_tile_m()
-               : gemv_mx_supported(ex, MOE_F16) ? gemv_mx_tile_m() : gemv_tile_m();
+               : gemv_mx_supported(ex, MOE_F16) ? gemv_mx_tile_m(T) : gemv_tile_m();
     p.max_rows = perm_max_rows(T, K, E, p.tile_m);
     p.max_tiles = p.max_rows / p.tile_m;
     p.off_h = 0;

@@ -424,21 +424,22 @@ bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act) {
            mx_layout_ok(ex.gate) && mx_layout_ok(ex.up) && mx_layout_ok(ex.down);
 }
 
-// Slots per tile. Measured (bench, same host): 8-slot tiles took the
-// Zipf-routed stack at T=32 from 1.531 to 1.436 ms per step (a hot expert
-// re-streams its weights once per tile) but decode T=64 with uniform
-// routing from 488 to 508 µs (twice the staged activations halve the work
-// groups per CU); 16 slots were slower for both. The plan cannot see the
-// routing, so the uniform decode case decides.
-constexpr int kMxTM = 4;
-int gemv_mx_tile_m() { return kMxTM; }
+// Slots per tile: 8 for 5 to 32 tokens, else 4. The plan sees the batch
+// size but not the routing. Measured (bench, graph replay, same host):
+// 8-slot tiles took the Zipf-routed 8-layer stack at T=32 from 1.33-1.35
+// to 1.22-1.25 ms per step (a hot expert re-streams its weights once per
+// tile), and uniform decode at T=8, 16 and 32 within 1 % either way; but
+// uniform decode at T=64 from 488 to 508 us (twice the staged activations
+// halve the work groups per CU) and at T=1 from 34.3 to 36.5 us. Up to 4
+// tokens no expert holds more than 4 slots unless a token repeats an id.
+// 16 slots were slower for both.
+int gemv_mx_tile_m(int T) { return T > 4 && T <= 32 ? 8 : 4; }
 constexpr int kMxDeepTiles = 300;
 
-template <int ACT, int FMT, bool GATEUP, int NS, int RP, int KS, int R>
+template <int ACT, int FMT, int TM, bool GATEUP, int NS, int RP, int KS, int R>
 moe_status_t launch_mx(const GemvMat &a, const GemvMat &b, int n_rows, const uint16_t *x,
                        int K, const moe_perm_t &p, int max_tiles, uint16_t *h, float *y,
                        hipStream_t s) {
-    constexpr int TM = kMxTM;
     const size_t lds = gemv_mx_lds_bytes(TM, NS * 128, KS, GATEUP ? 2 : 1);
     auto k = gemv_mx_kernel<ACT, FMT, TM, GATEUP, NS, RP, KS, R>;
     allow_lds(k, lds);
@@ -457,7 +458,7 @@ moe_status_t launch_mx(const GemvMat &a, const GemvMat &b, int n_rows, const uin
 // 0.470 -> 0.460 ms (down 160 -> 153 us). At 256 tiles (the Zipf-routed
 // stack at T=32) that form measured slower (down 40 -> 44 us per layer),
 // so smaller batches keep the 4-step rings and two row passes.
-template <int ACT, int FMT>
+template <int ACT, int FMT, int TM>
 moe_status_t gemv_mx_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int K,
                                const moe_perm_t &p, int max_tiles, uint16_t *h, float *y,
                                hipStream_t s, const std::function<moe_status_t(int)> &mark) {
@@ -465,23 +466,23 @@ moe_status_t gemv_mx_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int 
     const GemvMat g = gemv_mat(ex.gate), u = gemv_mat(ex.up), d = gemv_mat(ex.down);
     moe_status_t st;
     if (max_tiles <= 16)
-        st = launch_mx<ACT, FMT, true, 32, 1, 4, 4>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
+        st = launch_mx<ACT, FMT, TM, true, 32, 1, 4, 4>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
     else if (max_tiles <= 48)
-        st = launch_mx<ACT, FMT, true, 32, 1, 2, 4>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
+        st = launch_mx<ACT, FMT, TM, true, 32, 1, 2, 4>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
     else if (max_tiles <= kMxDeepTiles)
-        st = launch_mx<ACT, FMT, true, 32, 1, 1, 4>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
+        st = launch_mx<ACT, FMT, TM, true, 32, 1, 1, 4>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
     else
-        st = launch_mx<ACT, FMT, true, 32, 1, 1, 8>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
+        st = launch_mx<ACT, FMT, TM, true, 32, 1, 1, 8>(g, u, F, x, K, p, max_tiles, h, nullptr, s);
     if (st != MOE_OK) return st;
     if (mark && mark(1) != MOE_OK) return MOE_ERR_HIP;
     if (max_tiles <= 16)
-        st = launch_mx<ACT, FMT, false, 12, 1, 2, 3>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
+        st = launch_mx<ACT, FMT, TM, false, 12, 1, 2, 3>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
     else if (max_tiles <= 48)
-        st = launch_mx<ACT, FMT, false, 12, 1, 1, 4>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
+        st = launch_mx<ACT, FMT, TM, false, 12, 1, 1, 4>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
     else if (max_tiles <= kMxDeepTiles)
-        st = launch_mx<ACT, FMT, false, 12, 2, 1, 4>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
+        st = launch_mx<ACT, FMT, TM, false, 12, 2, 1, 4>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
     else
-        st = launch_mx<ACT, FMT, false, 12, 1, 1, 12>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
+        st = launch_mx<ACT, FMT, TM, false, 12, 1, 1, 12>(d, d, H, h, K, p, max_tiles, nullptr, y, s);
     if (st != MOE_OK) return st;
     if (mark && mark(2) != MOE_OK) return MOE_ERR_HIP;
     return MOE_OK;
@@ -494,7 +495,8 @@ moe_status_t launch_gemv_mx_forward(const moe_ffn_desc_t &ex, const void *x, int
     uint16_t *hh = (uint16_t *)h;
 #define MOE_MX_FMT(A, F)                                                                   \
     if (act == A && ex.gate.fmt == F)                                                      \
-        return gemv_mx_forward_t<A, F>(ex, xx, K, p, max_tiles, hh, y, s, mark);
+        return p.tile_m == 8 ? gemv_mx_forward_t<A, F, 8>(ex, xx, K, p, max_tiles, hh, y, s, mark) \
+                             : gemv_mx_forward_t<A, F, 4>(ex, xx, K, p, max_tiles, hh, y, s, mark);
     MOE_MX_FMT(MOE_F16, MOE_W_INT4_G128)
     MOE_MX_FMT(MOE_F16, MOE_W_INT4_G128_ASYM)
     MOE_MX_FMT(MOE_BF16, MOE_W_INT4_G128)
