@@ -241,11 +241,11 @@ def run_layer(name, banks, T, act, route_mode, steps, warmup, hip, dev, fmt, csf
     ev_c = [[hip.event(), hip.event()] for _ in range(nb)] if csf else None
 
     def step(i, events=None, csf_events=None):
+        # top-K and permutation in one call (one kernel up to 16 tokens)
         if route_mode == "logits":
-            B.moe_route_topk(K, logits=logits[i], ids=ids, w=w)
+            B.moe_route_permute(K, perm, logits=logits[i], ids=ids, w=w)
         else:
-            B.moe_route_topk(K, x=x, router_wT=wT, bias=bias, ids=ids, w=w, ws=rws)
-        B.moe_permute(ids, E, tm, perm=perm)
+            B.moe_route_permute(K, perm, x=x, router_wT=wT, bias=bias, ids=ids, w=w, ws=rws)
         if csf:
             if csf_events:
                 hip.record(csf_events[0])
@@ -358,8 +358,7 @@ def run_tiny(steps, warmup, dev):
     out = torch.empty((T, h), dtype=torch.float32, device=dev)
 
     def step():
-        B.moe_route_topk(k, x=x, router_wT=wT, ids=ids, w=w, ws=rws)
-        B.moe_permute(ids, e, tm, perm=perm)
+        B.moe_route_permute(k, perm, x=x, router_wT=wT, ids=ids, w=w, ws=rws)
         B.moe_w4a16_forward(ffn, x, w, perm, out=out, ws=ws)
 
     res = dict(workload="tiny T=8", tokens=T)

@@ -168,7 +168,7 @@ typedef struct {
 /* Human-readable name of a status code (host, static storage). */
 const char *moe_status_string(int status);
 
-/* ABI version of this header: 5 (moe_abi_version returns it). */
+/* ABI version of this header: 6 (moe_abi_version returns it). */
 int moe_abi_version(void);
 
 /*
@@ -276,6 +276,24 @@ moe_status_t moe_norm_route(const float *residual, const float *norm_w, float ep
  */
 moe_status_t moe_permute(const int32_t *topk_ids, int T, int K, int E,
                          const moe_perm_t *perm, void *stream);
+
+/*
+ * moe_route_permute -- moe_route_topk followed by moe_permute on its ids,
+ * in one call (the routing of page "Step-5-Preview-Spark", "At a glance",
+ * and the expert-sorted permutation that lets each expert stream once).
+ * Arguments as moe_route_topk (x, x_dtype, router_wT, logits_in, bias, T,
+ * H, E, K, renormalize, topk_ids, topk_w, ws, ws_bytes) plus perm, the
+ * moe_permute outputs (tile_m from moe_forward_plan). For batches of up to
+ * 16 tokens (T*K <= 1024) the top-K and the permutation run as one kernel:
+ * one wave per token selects, then the work group permutes the ids from
+ * LDS; larger batches run the two calls' kernels. Either way every output
+ * is bitwise that of moe_route_topk followed by moe_permute. Errors: as
+ * those two calls (T*K > 2^24: MOE_ERR_UNSUPPORTED).
+ */
+moe_status_t moe_route_permute(const void *x, int x_dtype, const float *router_wT,
+                               const float *logits_in, const float *bias, int T, int H, int E,
+                               int K, int renormalize, int32_t *topk_ids, float *topk_w,
+                               const moe_perm_t *perm, void *ws, size_t ws_bytes, void *stream);
 
 /* The tile_m the forward pass needs for T tokens (host output), and the
  * workspace bytes it needs (host output), with or without the shared expert

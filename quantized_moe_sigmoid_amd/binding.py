@@ -19,7 +19,7 @@ MOE_W_INT4_G128, MOE_W_NVFP4_G16, MOE_W_BF16, MOE_W_INT4_G32, MOE_W_INT4_G128_AS
 MOE_W_INT8_G128, MOE_W_NVFP4_CSF = 6, 7
 
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_router_logits", "moe_route_workspace",
-           "moe_route_topk", "moe_permute_sizes",
+           "moe_route_topk", "moe_route_permute", "moe_permute_sizes",
            "moe_permute", "moe_forward_plan", "moe_w4a16_forward", "moe_w4a16_forward_profiled",
            "moe_round_activations", "moe_rmsnorm", "moe_dequant", "moe_csf_expand",
            "moe_csf_row_index", "moe_norm_route", "moe_w4a16_forward_scratch",
@@ -83,6 +83,8 @@ def lib():
                                      vp]
         L.moe_permute_sizes.argtypes = [i32, i32, i32, i32, P(i64), P(i64)]
         L.moe_permute.argtypes = [vp, i32, i32, i32, P(PermDesc), vp]
+        L.moe_route_permute.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp,
+                                        P(PermDesc), vp, sz, vp]
         L.moe_forward_plan.argtypes = [P(FfnDesc), P(FfnDesc), i32, i32, i32, P(i32), P(sz)]
         L.moe_w4a16_forward.argtypes = [P(FfnDesc), P(FfnDesc), vp, i32, i32, i32, vp,
                                         P(PermDesc), vp, vp, i32, vp, sz, vp]
@@ -98,6 +100,7 @@ def lib():
         L.moe_norm_route.argtypes = [vp, vp, ctypes.c_float, i32, i32, vp, vp, i32, i32, i32, vp,
                                      vp, vp, vp, ctypes.c_size_t, vp]
         for name in ("moe_router_logits", "moe_route_workspace", "moe_route_topk",
+                     "moe_route_permute",
                      "moe_permute_sizes", "moe_permute", "moe_forward_plan",
                      "moe_w4a16_forward", "moe_w4a16_forward_profiled",
                      "moe_round_activations", "moe_rmsnorm", "moe_dequant",
@@ -283,6 +286,31 @@ def moe_permute(topk_ids, E, tile_m, perm=None):
     _check(lib().moe_permute(_ptr(topk_ids), T, K, E, ctypes.byref(d), _stream(topk_ids.device)),
            "moe_permute")
     return perm
+
+
+def moe_route_permute(K, perm, x=None, router_wT=None, logits=None, bias=None, renormalize=True,
+                      ids=None, w=None, ws=None):
+    """moe_route_topk then moe_permute into perm (a Perm of the batch's
+    T, K, E and tile_m), in one call. Returns (topk_ids, topk_w)."""
+    src = logits if logits is not None else x
+    T = src.shape[0]
+    E = logits.shape[1] if logits is not None else router_wT.shape[1]
+    H = x.shape[1] if x is not None else 0
+    dev = src.device
+    if ids is None:
+        ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    need = moe_route_workspace(T, E, router_wT is not None)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    xd = _DT.get(x.dtype, 0) if x is not None else 0
+    d = perm.desc()
+    st = lib().moe_route_permute(_ptr(x), xd, _ptr(router_wT), _ptr(logits), _ptr(bias), T, H, E,
+                                 K, int(bool(renormalize)), _ptr(ids), _ptr(w), ctypes.byref(d),
+                                 _ptr(ws) if need else None, need, _stream(dev))
+    _check(st, "moe_route_permute")
+    return ids, w
 
 
 def moe_forward_plan(experts, T, K, act_dtype, shared=None):

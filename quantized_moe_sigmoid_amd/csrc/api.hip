@@ -20,6 +20,10 @@ size_t router_ws_floats_max(int T, int E);
 int router_blocks(int H);
 moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_perm_t &p,
                             hipStream_t s);
+bool route_perm_fused(int T, int K);
+moe_status_t launch_route_perm_small(const float *scores, const float *bias, int T, int E, int K,
+                                     int renorm, int P, int32_t *ids, float *wts,
+                                     const moe_perm_t &p, hipStream_t s);
 moe_status_t launch_dequant(const moe_weight_desc_t &d, int e, float *out, hipStream_t s);
 moe_status_t launch_csf_expand(const uint8_t *fixed, const uint32_t *exceptions, int64_t n,
                                const int64_t *starts, int E, int R, int C,
@@ -291,7 +295,7 @@ const char *moe_status_string(int status) {
     }
 }
 
-int moe_abi_version(void) { return 5; }
+int moe_abi_version(void) { return 6; }
 
 static moe_status_t check_router(const void *x, int x_dtype, const float *wT, int T, int H,
                                  int E) {
@@ -344,6 +348,40 @@ moe_status_t moe_route_topk(const void *x, int x_dtype, const float *router_wT,
     }
     if (T == 0) return MOE_OK;
     return launch_topk(logits_in, bias, T, E, K, renormalize, topk_ids, topk_w, s);
+}
+
+moe_status_t moe_route_permute(const void *x, int x_dtype, const float *router_wT,
+                               const float *logits_in, const float *bias, int T, int H, int E,
+                               int K, int renormalize, int32_t *topk_ids, float *topk_w,
+                               const moe_perm_t *perm, void *ws, size_t ws_bytes,
+                               void *stream) {
+    if (T < 0 || E < 1 || E > kMaxExperts || K < 1 || K > E || K > kMaxTopK)
+        return MOE_ERR_INVALID_ARG;
+    if (!topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if ((router_wT == nullptr) == (logits_in == nullptr)) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)T * K > (1 << 24)) return MOE_ERR_UNSUPPORTED;
+    moe_status_t st = check_perm(perm);
+    if (st != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const float *scores = logits_in;
+    int P = 1;
+    if (router_wT) {
+        if ((st = check_router(x, x_dtype, router_wT, T, H, E)) != MOE_OK) return st;
+        if (T > 0 && !ws) return MOE_ERR_INVALID_ARG;
+        if (ws_bytes < router_ws_floats(T, H, E, x_dtype) * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
+        if (ws && !aligned(ws, 16)) return MOE_ERR_INVALID_ARG;
+        if (T == 0) return MOE_OK;
+        st = launch_router_scores(x, x_dtype, router_wT, T, H, E, (float *)ws, &P, s);
+        if (st != MOE_OK) return st;
+        scores = (const float *)ws;
+    }
+    if (T == 0) return MOE_OK;
+    if (route_perm_fused(T, K))
+        return launch_route_perm_small(scores, bias, T, E, K, renormalize, P, topk_ids, topk_w,
+                                       *perm, s);
+    if ((st = launch_topk(scores, bias, T, E, K, renormalize, topk_ids, topk_w, s, P)) != MOE_OK)
+        return st;
+    return launch_permute(topk_ids, T, K, E, *perm, s);
 }
 
 moe_status_t moe_permute_sizes(int T, int K, int E, int tile_m, int64_t *max_rows,

@@ -24,7 +24,7 @@
 // last block writes the totals.
 // Ids outside [0, E) are not routed anywhere in either form: such a slot
 // gets slot_to_row -1 and no row, and the combine adds nothing for it.
-#include "common.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -184,15 +184,24 @@ __global__ void __launch_bounds__(kPermThreads) perm_large_kernel(
 constexpr int kPermSmallThreads = 1024;
 constexpr int kPermSmallSlots = 1024;
 
-__global__ void __launch_bounds__(kPermSmallThreads) perm_small_kernel(
-    const int32_t *__restrict__ ids, int n, int E, int tile_m, int32_t *__restrict__ counts,
+// LDS bytes of the one-group permutation of n slots over E experts: the
+// slot masks [E][W], the per-wave scan totals, the padded offsets [E].
+__host__ __device__ inline size_t perm_small_lds(int n, int E) {
+    const int W = n > 0 ? (n + 63) / 64 : 1;
+    return (size_t)E * W * 8 + 3 * (kPermSmallThreads / kWave) * 4 + (size_t)E * 4;
+}
+
+// The one-group permutation (1024 threads) of n slots whose ids id_at(s)
+// returns, LDS at sm (perm_small_lds bytes).
+template <typename IdFn>
+__device__ __forceinline__ void perm_small_body(
+    IdFn id_at, int n, int E, int tile_m, uint64_t *sm, int32_t *__restrict__ counts,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ padded_offsets,
     int32_t *__restrict__ sorted_slots, int32_t *__restrict__ slot_to_row,
     int32_t *__restrict__ tile_expert, int32_t *__restrict__ num_tiles,
     int32_t *__restrict__ active_experts, int32_t *__restrict__ num_active) {
-    extern __shared__ uint64_t sm_masks[];
     const int W = (n + 63) / 64 > 0 ? (n + 63) / 64 : 1;     // mask words per expert
-    uint64_t *mask = sm_masks;                               // [E][W]
+    uint64_t *mask = sm;                                     // [E][W]
     int *wtot = (int *)(mask + (size_t)E * W);               // [waves][3]
     int *poff = wtot + 3 * (kPermSmallThreads / kWave);      // [E] padded offsets
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
@@ -200,7 +209,7 @@ __global__ void __launch_bounds__(kPermSmallThreads) perm_small_kernel(
     for (int i = tid; i < E * W; i += kPermSmallThreads) mask[i] = 0ull;
     __syncthreads();
     for (int s = tid; s < n; s += kPermSmallThreads) {
-        const int e = ids[s];
+        const int e = id_at(s);
         if (e >= 0 && e < E)
             atomicOr((unsigned long long *)&mask[e * W + (s >> 6)], 1ull << (s & 63));
     }
@@ -251,7 +260,7 @@ __global__ void __launch_bounds__(kPermSmallThreads) perm_small_kernel(
 
     // a slot's rank among its expert's slots: that expert's bits below it
     for (int s = tid; s < n; s += kPermSmallThreads) {
-        const int ee = ids[s];
+        const int ee = id_at(s);
         if (ee < 0 || ee >= E) {
             slot_to_row[s] = -1;
             continue;
@@ -265,12 +274,70 @@ __global__ void __launch_bounds__(kPermSmallThreads) perm_small_kernel(
     }
 }
 
+__global__ void __launch_bounds__(kPermSmallThreads) perm_small_kernel(
+    const int32_t *__restrict__ ids, int n, int E, int tile_m, int32_t *__restrict__ counts,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ padded_offsets,
+    int32_t *__restrict__ sorted_slots, int32_t *__restrict__ slot_to_row,
+    int32_t *__restrict__ tile_expert, int32_t *__restrict__ num_tiles,
+    int32_t *__restrict__ active_experts, int32_t *__restrict__ num_active) {
+    extern __shared__ uint64_t sm_masks[];
+    perm_small_body([&](int s) { return ids[s]; }, n, E, tile_m, sm_masks, counts,
+                    expert_offsets, padded_offsets, sorted_slots, slot_to_row, tile_expert,
+                    num_tiles, active_experts, num_active);
+}
+
+// Top-K and permutation of a batch of up to 16 tokens in one launch: wave t
+// selects token t's experts from its scores (the logits, or P block sums
+// [P][T][E] added in block order, then the bias) and keeps the ids in LDS
+// too; after one barrier the group permutes them as perm_small_kernel does.
+// Bitwise the results of route_given_kernel followed by perm_small_kernel.
+constexpr int kRoutePermMaxT = kPermSmallThreads / kWave;
+
+__global__ void __launch_bounds__(kPermSmallThreads) route_perm_small_kernel(
+    const float *__restrict__ scores, const float *__restrict__ bias, int T, int E, int K,
+    int renorm, int P, int32_t *__restrict__ ids, float *__restrict__ wts, int tile_m,
+    int32_t *__restrict__ counts, int32_t *__restrict__ expert_offsets,
+    int32_t *__restrict__ padded_offsets, int32_t *__restrict__ sorted_slots,
+    int32_t *__restrict__ slot_to_row, int32_t *__restrict__ tile_expert,
+    int32_t *__restrict__ num_tiles, int32_t *__restrict__ active_experts,
+    int32_t *__restrict__ num_active) {
+    extern __shared__ uint64_t sm_masks[];
+    const int n = T * K;
+    int32_t *sid = (int32_t *)((char *)sm_masks + perm_small_lds(n, E));   // [n]
+    const int t = threadIdx.x >> 6;
+    if (t < T)
+        token_topk(scores + (size_t)t * E, (size_t)T * E, P, bias, E, K, renorm,
+                   ids + (size_t)t * K, wts + (size_t)t * K, sid + t * K);
+    __syncthreads();
+    perm_small_body([&](int s) { return sid[s]; }, n, E, tile_m, sm_masks, counts,
+                    expert_offsets, padded_offsets, sorted_slots, slot_to_row, tile_expert,
+                    num_tiles, active_experts, num_active);
+}
+
+bool route_perm_fused(int T, int K) { return T <= kRoutePermMaxT && T * K <= kPermSmallSlots; }
+
+moe_status_t launch_route_perm_small(const float *scores, const float *bias, int T, int E, int K,
+                                     int renorm, int P, int32_t *ids, float *wts,
+                                     const moe_perm_t &p, hipStream_t s) {
+    if (T == 0) return MOE_OK;
+    const size_t lds = perm_small_lds(T * K, E) + (size_t)T * K * 4;
+    if (lds > 65536 &&
+        hipFuncSetAttribute((const void *)route_perm_small_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return MOE_ERR_HIP;
+    hipLaunchKernelGGL(route_perm_small_kernel, dim3(1), dim3(kPermSmallThreads), lds, s, scores,
+                       bias, T, E, K, renorm, P, ids, wts, p.tile_m, p.counts, p.expert_offsets,
+                       p.padded_offsets, p.sorted_slots, p.slot_to_row, p.tile_expert,
+                       p.num_tiles, p.active_experts, p.num_active);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
 moe_status_t launch_permute(const int32_t *ids, int T, int K, int E, const moe_perm_t &p,
                             hipStream_t s) {
     const int n = T * K;
     if (n <= kPermSmallSlots && E <= kPermSmallThreads) {
-        const int W = n > 0 ? (n + 63) / 64 : 1;
-        const size_t lds = (size_t)E * W * 8 + 3 * (kPermSmallThreads / kWave) * 4 + (size_t)E * 4;
+        const size_t lds = perm_small_lds(n, E);
         if (lds > 65536 &&
             hipFuncSetAttribute((const void *)perm_small_kernel,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)

@@ -9,27 +9,14 @@
 // the bias, if any). The chosen experts are thus the same on every run and
 // on the CPU reference, and a small batch can run a token's 8 block chains
 // side by side instead of one 4096-step chain. The pages show why the order
-// matters:
-// a different summation order inside the MoE flips near-tied expert choices
-// ("Step-5-Preview-Spark", "Quality", noise-floor paragraph).
-//
-// Selection: the K largest logits by (logit desc, expert asc): per round a
-// wave maximum of the logits' order-preserving 32-bit images, ties resolved
-// to the lowest expert index by ballots; -0 is folded to +0 first.
-// Weights: sigmoid of the selected logits, renormalised to sum to one when
-// asked.
-#include "common.h"
+// matters: a different summation order inside the MoE flips near-tied
+// expert choices ("Step-5-Preview-Spark", "Quality", noise-floor
+// paragraph). The selection and the weights are in topk.h.
+#include "topk.h"
 
 #pragma clang fp contract(off)
 
 namespace moe {
-
-constexpr int kMaxE = 512;
-
-// Inputs per block of the canonical logit sum, and the most blocks whose
-// sums the top-K adds up (the block-sum paths take H <= 4096).
-constexpr int kRouterBlock = 512;
-constexpr int kMaxRouterBlocks = 8;
 
 // After the chain over 64-input chunk c (of nch) has run into acc: at the
 // end of a 512-input block, fold the block's sum into tot (the first block
@@ -46,89 +33,6 @@ __device__ __forceinline__ void block_end(int c, int nch, float (&acc)[N], float
     }
 }
 
-// Order-preserving image of a float in uint32 (a larger float maps to a
-// larger value; -0 is folded to +0 first); 0 lies below every image.
-__device__ __forceinline__ uint32_t ord32(float f) {
-    const uint32_t u = __float_as_uint(f + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float ord32_value(uint32_t o) {
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
-// Maximum over the wave: four DPP butterflies inside each 16-lane row
-// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror;
-// every lane then holds its row's maximum), then the four rows through
-// scalar registers.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-    return v > o ? v : o;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = dpp_max<0xB1>(v);
-    v = dpp_max<0x4E>(v);
-    v = dpp_max<0x141>(v);
-    v = dpp_max<0x140>(v);
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
-    return a > b ? a : b;
-}
-
-// One wave selects the top K of E logits held in `lg` (LDS or global).
-// Lane l owns experts l, l+64, ... Each round takes the wave maximum of the
-// logits' order images, then the lowest expert holding it: experts of slot
-// j are 64 j + lane, so the first slot whose ballot hits, at its lowest
-// lane (ties go to the lower index). Writes ids / weights for one token.
-constexpr int kTopkSlots = kMaxE / kWave;
-
-// The selection over the order images o (0 for experts past E).
-__device__ __forceinline__ void wave_topk_keys(uint32_t (&o)[kTopkSlots], int K, int renorm,
-                                               int32_t *ids, float *wts) {
-    constexpr int NJ = kTopkSlots;
-    const int lane = threadIdx.x & (kWave - 1);
-    float my_logit = 0.0f;
-    int my_id = 0;
-    for (int r = 0; r < K; ++r) {
-        uint32_t m = o[0];
-#pragma unroll
-        for (int j = 1; j < NJ; ++j) m = o[j] > m ? o[j] : m;
-        const uint32_t best = wave_max_u32(m);
-        int win = -1;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const uint64_t b = __ballot(o[j] == best);
-            if (win < 0 && b) win = j * kWave + __ffsll((unsigned long long)b) - 1;
-        }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            if (j * kWave + lane == win) o[j] = 0u;
-        if (lane == r) { my_id = win; my_logit = ord32_value(best); }
-    }
-    float p = 1.0f / (1.0f + expf(-my_logit));
-    if (renorm) {
-        // sum over lanes 0..K-1 in ascending order (deterministic)
-        float s = 0.0f;
-        for (int r = 0; r < K; ++r) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), r));
-        p = p / s;
-    }
-    if (lane < K) { ids[lane] = my_id; wts[lane] = p; }
-}
-
-template <typename LoadFn>
-__device__ __forceinline__ void wave_topk(LoadFn load, int E, int K, int renorm,
-                                          int32_t *ids, float *wts) {
-    const int lane = threadIdx.x & (kWave - 1);
-    uint32_t o[kTopkSlots];
-#pragma unroll
-    for (int j = 0; j < kTopkSlots; ++j) {
-        const int e = lane + j * kWave;
-        o[j] = e < E ? ord32(load(e)) : 0u;
-    }
-    wave_topk_keys(o, K, renorm, ids, wts);
-}
-
 // Logits given, or P block sums of them ([P][T][E], added in block
 // order): one wave per token.
 __global__ void __launch_bounds__(256) route_given_kernel(
@@ -136,36 +40,13 @@ __global__ void __launch_bounds__(256) route_given_kernel(
     int renorm, int P, int32_t *__restrict__ ids, float *__restrict__ wts) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float *row = logits + (size_t)t * E;
-    const size_t pstride = (size_t)T * E;
-    const int lane = threadIdx.x & (kWave - 1);
-    // every slot's block values (and bias) loaded before any addition:
-    // unconditional loads at clamped addresses, the extra ones unused
-    float q[kTopkSlots][kMaxRouterBlocks], bv[kTopkSlots];
-#pragma unroll
-    for (int j = 0; j < kTopkSlots; ++j) {
-        const int e = min(lane + j * kWave, E - 1);
-#pragma unroll
-        for (int p = 0; p < kMaxRouterBlocks; ++p)
-            q[j][p] = row[min(p, P - 1) * pstride + e];
-        bv[j] = bias ? bias[e] : 0.0f;
-    }
-    uint32_t o[kTopkSlots];
-#pragma unroll
-    for (int j = 0; j < kTopkSlots; ++j) {
-        float v = q[j][0];
-#pragma unroll
-        for (int p = 1; p < kMaxRouterBlocks; ++p)
-            if (p < P) v = v + q[j][p];
-        if (bias) v = v + bv[j];
-        o[j] = lane + j * kWave < E ? ord32(v) : 0u;
-    }
-    wave_topk_keys(o, K, renorm, ids + (size_t)t * K, wts + (size_t)t * K);
+    token_topk(logits + (size_t)t * E, (size_t)T * E, P, bias, E, K, renorm, ids + (size_t)t * K,
+               wts + (size_t)t * K, nullptr);
 }
 
 // Logits computed: a plain fp32 SIMT GEMM, logits[t][e] = x[t] . wT[:, e],
-// in which every output is one fma chain over k in ascending order (so the
-// input range cannot be split across threads). Block tile: 64 experts (one
+// every output the canonical sum (fma chains over k ascending, restarted
+// every 512 inputs, the block sums added in order). Block tile: 64 experts (one
 // per lane) x 16 tokens (4 per wave): at T = 2048 and E = 352 that is 768
 // work groups, three per CU in one round, and each wave's serial chain
 // work stays short. k advances in chunks of 64 staged in LDS (double

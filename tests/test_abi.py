@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
     assert B.status_string(0) == "MOE_OK"
     assert B.status_string(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
     assert B.status_string(99) == "MOE_ERR_UNKNOWN"
@@ -162,6 +162,37 @@ def test_permute_validation(L):
     assert L.moe_permute(ctypes.c_void_p(FAKE), 2, 2, 16, ctypes.byref(p), None) == B.MOE_ERR_INVALID_ARG
     p = B.PermDesc(*([FAKE] * 8), None, 4)
     assert L.moe_permute(ctypes.c_void_p(FAKE), 2, 2, 16, ctypes.byref(p), None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_route_permute_validation(L):
+    """moe_route_permute checks moe_route_topk's and moe_permute's argument
+    rules before any launch."""
+    R = L.moe_route_permute
+    p = ctypes.c_void_p(FAKE)
+    n = None
+    big = 1 << 30
+    d = B.PermDesc(*([FAKE] * 9), 4)
+    pd = ctypes.byref(d)
+    # K > E, K > 16, E > 512, both or neither logit source, missing outputs
+    assert R(n, 0, n, p, n, 4, 0, 8, 9, 1, p, p, pd, n, 0, n) == B.MOE_ERR_INVALID_ARG
+    assert R(n, 0, n, p, n, 4, 0, 64, 17, 1, p, p, pd, n, 0, n) == B.MOE_ERR_INVALID_ARG
+    assert R(n, 0, n, p, n, 4, 0, 513, 8, 1, p, p, pd, n, 0, n) == B.MOE_ERR_INVALID_ARG
+    assert R(p, 2, p, p, n, 4, 64, 16, 2, 1, p, p, pd, p, big, n) == B.MOE_ERR_INVALID_ARG
+    assert R(n, 0, n, n, n, 4, 64, 16, 2, 1, p, p, pd, p, big, n) == B.MOE_ERR_INVALID_ARG
+    assert R(n, 0, n, p, n, 4, 0, 16, 2, 1, n, p, pd, n, 0, n) == B.MOE_ERR_INVALID_ARG
+    # the permutation arrays: a missing array, tile_m out of range
+    d2 = B.PermDesc(*([FAKE] * 8), None, 4)
+    assert R(n, 0, n, p, n, 4, 0, 16, 2, 1, p, p, ctypes.byref(d2), n, 0, n) == \
+        B.MOE_ERR_INVALID_ARG
+    d3 = B.PermDesc(*([FAKE] * 9), 0)
+    assert R(n, 0, n, p, n, 4, 0, 16, 2, 1, p, p, ctypes.byref(d3), n, 0, n) == \
+        B.MOE_ERR_INVALID_ARG
+    # router weight: H % 64, workspace (one float per 512-input block)
+    assert R(p, 2, p, n, n, 4, 96, 16, 2, 1, p, p, pd, p, big, n) == B.MOE_ERR_UNSUPPORTED
+    assert R(p, 2, p, n, n, 4, 1024, 16, 2, 1, p, p, pd, p, 2 * 4 * 16 * 4 - 1, n) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # T == 0 is a no-op
+    assert R(n, 0, n, p, n, 0, 0, 16, 2, 1, p, p, pd, n, 0, n) == B.MOE_OK
 
 
 def test_forward_validation_before_launch(L):

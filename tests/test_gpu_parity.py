@@ -179,6 +179,46 @@ def test_route_from_router_weight_full(dev, T, zipf):
     _check_route(ids, w, lg, K)
 
 
+@pytest.mark.parametrize("T,Kk,Ee,src", [(1, 8, 352, "logits"), (5, 8, 352, "bias"),
+                                         (16, 8, 352, "logits"), (17, 8, 352, "bias"),
+                                         (64, 8, 352, "logits"), (16, 16, 512, "bias"),
+                                         (3, 2, 16, "logits"), (3, 8, 352, "weight"),
+                                         (32, 8, 352, "weight"), (2, 4, 64, "weight_f16")])
+def test_route_permute_matches_separate_calls(dev, T, Kk, Ee, src):
+    """moe_route_permute (one kernel up to 16 tokens, the two calls' kernels
+    beyond) is bitwise moe_route_topk followed by moe_permute: ids, weights
+    and every permutation array; given logits with or without a bias, and
+    a router weight (bf16 block sums, f16 logits)."""
+    tm = 8 if 5 <= T <= 32 else 4
+    kw = {}
+    if src in ("logits", "bias"):
+        kw["logits"] = torch.from_numpy(synth.router_logits(T, Ee, 40 + T)).to(dev)
+        if src == "bias":
+            kw["bias"] = torch.from_numpy(synth.zipf_bias(Ee, 40 + T)).to(dev)
+    else:
+        Hh = 1024
+        act = "f16" if src == "weight_f16" else "bf16"
+        kw["x"] = synth.activations(T, Hh, act, 40 + T).to(dev)
+        kw["router_wT"] = torch.from_numpy(synth.router_weight_T(Hh, Ee, 40 + T)).to(dev)
+    perm = B.Perm(T, Kk, Ee, tm, dev)
+    ids, w = B.moe_route_permute(Kk, perm, **kw)
+    ids2, w2 = B.moe_route_topk(Kk, **kw)
+    perm2 = B.moe_permute(ids2, Ee, tm)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2)
+    assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    n_rows = int(perm2.padded_offsets[Ee])
+    n_tiles = int(perm2.num_tiles[0])
+    n_act = int(perm2.num_active[0])
+    for f, m in (("counts", None), ("expert_offsets", None), ("padded_offsets", None),
+                 ("slot_to_row", None), ("num_tiles", None), ("num_active", None),
+                 ("sorted_slots", n_rows), ("tile_expert", n_tiles), ("active_experts", n_act)):
+        a, b = getattr(perm, f), getattr(perm2, f)
+        if m is not None:
+            a, b = a[:m], b[:m]
+        assert torch.equal(a, b), f
+
+
 # -------------------------------------------------------------- permutation ---
 @pytest.mark.parametrize("T,Kk,Ee,tm,skew", [(1, 8, 352, 4, False), (64, 8, 352, 4, False),
                                              (2048, 8, 352, 64, False), (2048, 8, 352, 64, True),
