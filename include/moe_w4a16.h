@@ -333,6 +333,9 @@ moe_status_t moe_forward_plan(const moe_ffn_desc_t *experts,
  * tile_m from moe_forward_plan; residual: NULL or [T][H] float;
  * out [T][H] in out_dtype (MOE_F32, MOE_F16 or MOE_BF16); ws: device
  * workspace of at least moe_forward_plan's ws_bytes, 256-byte aligned.
+ * On the grouped-GEMM path (T*K >= 4*E) x and h are read through 32-bit
+ * byte offsets: T*H*2 and max_rows*F*2 must stay below 2^31 - 2^20 bytes
+ * (else MOE_ERR_UNSUPPORTED; about 85 K tokens at top-8, F = 1536).
  * Accumulation is float32; h is rounded to act_dtype before the down
  * projection.
  *

@@ -78,6 +78,8 @@ namespace {
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxDim = 16384;
+// Bytes a 32-bit buffer offset reaches, with room for a step past a row.
+constexpr int64_t kMaxBufferBytes = ((int64_t)1 << 31) - ((int64_t)1 << 20);
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -444,6 +446,9 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     if (ws_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!p.mfma && p.max_tiles > 65535) return MOE_ERR_UNSUPPORTED;     // grid.y
     if (p.mfma && p.max_tiles * ((H > F ? H : F) / 128 + 1) > (int64_t)1 << 30)
+        return MOE_ERR_UNSUPPORTED;
+    // the grouped GEMM reads x and h through 32-bit buffer offsets
+    if (p.mfma && ((int64_t)T * H * 2 > kMaxBufferBytes || p.max_rows * F * 2 > kMaxBufferBytes))
         return MOE_ERR_UNSUPPORTED;
 
     hipStream_t s = (hipStream_t)stream;

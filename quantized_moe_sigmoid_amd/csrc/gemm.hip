@@ -253,19 +253,26 @@ __device__ __forceinline__ int a_offset(int row, int chunk) {
 // Thread t owns row t/4 and chunk slot t%4 of each of the eight column
 // groups; the slot holds input chunk (t%4) ^ swz(row), so the four threads
 // of a row read 64 contiguous bytes per group and a wave writes 1 KB of LDS
-// contiguously. Thread t < 64 also carries row t's two (-BIAS * group sum)
+// contiguously. The row's bytes come through a buffer resource at byte
+// offset xoff; a padded row's xoff lies past the resource, so its loads
+// return zeros without fetching anything (its output row is never
+// stored). Thread t < 64 also carries row t's two (-BIAS * group sum)
 // values (int4).
 template <int FMT>
 struct Stager {
     u32x4_t v[8];      // a native vector type: HIP's uint4 struct copies become
                        // memcpy through scratch memory
     float rs0, rs1;
-    __device__ __forceinline__ void load(const uint16_t *src_row, const float *sum_row, int step) {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rx, uint32_t xoff,
+                                         const float *sum_row, int step) {
         const int row = threadIdx.x >> 2;
         const int kc = (threadIdx.x & 3) ^ a_swz(row);
 #pragma unroll
         for (int g = 0; g < 8; ++g)
-            v[g] = *(const u32x4_t *)(src_row + step * kGemmKS + (g * 4 + kc) * 8);
+            v[g] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                             rx, (int)(xoff + (uint32_t)(step * kGemmKS + (g * 4 + kc) * 8) * 2u),
+                             0, 0));
         if (g128_rescaled(FMT) && threadIdx.x < kGemmTM) {
             rs0 = sum_row[2 * step];
             rs1 = sum_row[2 * step + 1];
@@ -414,7 +421,7 @@ __global__ void __launch_bounds__(kGemmThreads)
     // xin and rowsum_in are not __restrict__: as restrict read-only kernel
     // arguments their loads count as invariant and get sunk below the MFMAs
     // that should hide their latency
-    const uint16_t *xin, int x_from_slots, int topk, const float *rowsum_in,
+    const uint16_t *xin, int64_t x_bytes, int x_from_slots, int topk, const float *rowsum_in,
     const int32_t *__restrict__ sorted_slots, const int32_t *__restrict__ tile_expert,
     const int32_t *__restrict__ num_tiles, int n_blocks, uint16_t *__restrict__ hout,
     float *__restrict__ hsum_out, float *__restrict__ yout, uint16_t *__restrict__ y16,
@@ -435,16 +442,19 @@ __global__ void __launch_bounds__(kGemmThreads)
     const int e = tile_expert[tile];
     const int groups = kin / 128;
 
-    // this thread's staging row (padded rows repeat the tile's first, real,
-    // row; their output rows are never stored)
+    // this thread's staging row: its byte offset in xin, or past the end
+    // for a padded row (loads of zeros that fetch nothing; the host keeps
+    // x_bytes below 2^31)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint16_t *src_row;
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc((const uint8_t *)xin, x_bytes);
+    uint32_t xoff;
     {
         const int row = threadIdx.x >> 2;
-        int sl = sorted_slots[tile * kGemmTM + row];
-        int prow = row;
-        if (sl < 0) { sl = sorted_slots[tile * kGemmTM]; prow = 0; }
-        src_row = xin + (x_from_slots ? (size_t)(sl / topk) : (size_t)tile * kGemmTM + prow) * kin;
+        const int sl = sorted_slots[tile * kGemmTM + row];
+        xoff = sl < 0 ? (uint32_t)kOutOfRange
+                      : (uint32_t)((x_from_slots ? (size_t)(sl / topk)
+                                                 : (size_t)tile * kGemmTM + row) *
+                                   kin * 2);
     }
     const float *sum_row = nullptr;
     if (threadIdx.x < kGemmTM) {
@@ -489,7 +499,7 @@ __global__ void __launch_bounds__(kGemmThreads)
     const int nsteps = kin / kGemmKS;
     Stager<FMT> st;
     StepW<FMT> wa0, wb0, wa1, wb1;
-    st.load(src_row, sum_row, 0);
+    st.load(rx, xoff, sum_row, 0);
     wa0.load(rqa, rsa, rza, qoff_a, soff_a, zoff_a, 0, cx.half);
     wb0.load(rqb, rsb, rzb, qoff_b, soff_b, zoff_b, 0, cx.half);
     st.store(abuf0, xsum0);
@@ -504,7 +514,7 @@ __global__ void __launch_bounds__(kGemmThreads)
         /* unconditional (the last step reloads itself): conditional loads */         \
         /* would merge with the old register values and force early waits */         \
         const int sn = more ? s_ + 1 : s_;                                             \
-        st.load(src_row, sum_row, sn);                                                 \
+        st.load(rx, xoff, sum_row, sn);                                                \
         NWA.load(rqa, rsa, rza, qoff_a, soff_a, zoff_a, sn, cx.half);                  \
         NWB.load(rqb, rsb, rzb, qoff_b, soff_b, zoff_b, sn, cx.half);                  \
         /* keep the compiler from sinking the prefetch below the MFMAs */             \
@@ -672,8 +682,8 @@ moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int T, 
         const int nbk = F / kGemmBN;
         hipLaunchKernelGGL((gemm_kernel<ACT, FMT, true>), dim3(max_tiles * nbk),
                            dim3(kGemmThreads), 0, s, gemm_mat(ex.gate), gemm_mat(ex.up), F, H, xa,
-                           1, K, xsum, p.sorted_slots, p.tile_expert, p.num_tiles, nbk, h, hsum,
-                           nullptr, nullptr, nullptr);
+                           (int64_t)T * H * 2, 1, K, xsum, p.sorted_slots, p.tile_expert,
+                           p.num_tiles, nbk, h, hsum, nullptr, nullptr, nullptr);
         MOE_LAUNCH_CHECK();
     }
     if (mark && mark(1) != MOE_OK) return MOE_ERR_HIP;
@@ -682,7 +692,8 @@ moe_status_t gemm_forward_t(const moe_ffn_desc_t &ex, const uint16_t *x, int T, 
         // A and B are the same down matrix; the kernel offsets B by 32 columns
         const GemmMat d = gemm_mat(ex.down);
         hipLaunchKernelGGL((gemm_kernel<ACT, FMT, false>), dim3(max_tiles * nbk),
-                           dim3(kGemmThreads), 0, s, d, d, H, F, h, 0, K, hsum, p.sorted_slots,
+                           dim3(kGemmThreads), 0, s, d, d, H, F, h,
+                           (int64_t)max_tiles * kGemmTM * F * 2, 0, K, hsum, p.sorted_slots,
                            p.tile_expert, p.num_tiles, nbk, nullptr, nullptr, y, y16, yexp);
         MOE_LAUNCH_CHECK();
     }

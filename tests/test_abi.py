@@ -221,6 +221,23 @@ def test_forward_validation_before_launch(L):
              B.MOE_F32, None, 0, None) == B.MOE_OK
 
 
+def test_forward_gemm_offsets_limit(L):
+    """The grouped GEMM reads x and h through 32-bit byte offsets: a batch
+    whose h would pass 2^31 - 2^20 bytes (T = 90000, top-8: about 720 K
+    rows of 3 KB) is refused before any launch; T = 80000 passes that
+    check (and stops at the workspace size)."""
+    f = _ffn()
+    F = L.moe_w4a16_forward
+    x = ctypes.c_void_p(FAKE)
+    for T, want in ((90000, B.MOE_ERR_UNSUPPORTED), (80000, B.MOE_ERR_WORKSPACE_TOO_SMALL)):
+        st, tm, ws = _plan(f, T=T)
+        assert st == B.MOE_OK
+        p = B.PermDesc(*([FAKE] * 9), tm)
+        big = ws if want == B.MOE_ERR_UNSUPPORTED else ws - 1
+        assert F(ctypes.byref(f), None, x, B.MOE_F16, T, 8, x, ctypes.byref(p), None, x,
+                 B.MOE_F32, x, big, None) == want
+
+
 def test_forward_profiled_validation(L):
     """The profiled entry: events must be an array of MOE_FORWARD_STAGES + 1
     entries; NULL entries are boundaries that record nothing."""
