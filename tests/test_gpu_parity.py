@@ -168,6 +168,33 @@ def test_router_block_order_every_path(dev, T):
     assert (ids.cpu().numpy() == 1).all()
 
 
+@pytest.mark.parametrize("T,Hh,Ee,Kk", [(5, 576, 20, 3), (70, 576, 24, 4), (3, 1088, 352, 8)])
+def test_block_sum_routing_short_last_block(dev, T, Hh, Ee, Kk):
+    """The block-sum paths with a last block shorter than 512 inputs (H = 576:
+    512 + 64; H = 1088: 2 x 512 + 64): moe_route_topk from a bf16 router
+    input and moe_norm_route (fused) give the oracle's ids bit for bit and
+    its weights within 1e-5; T = 70 runs two tokens per wave."""
+    x = synth.activations(T, Hh, "bf16", 60 + T)
+    wT = synth.router_weight_T(Hh, Ee, 60 + T)
+    b = synth.zipf_bias(Ee, 60 + T)
+    lg = OR.router_logits(x.float().numpy(), wT, b)
+    ids, w = B.moe_route_topk(Kk, x=x.to(dev), router_wT=torch.from_numpy(wT).to(dev),
+                              bias=torch.from_numpy(b).to(dev))
+    oids = OR.topk_ids(lg, Kk)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    np.testing.assert_allclose(w.cpu().numpy(), OR.routing_weights(lg, oids), rtol=1e-5, atol=0)
+    r = synth.normal((T, Hh), 1.0, 61, 0, synth.T_X, T)
+    a, ids2, w2 = B.moe_norm_route(torch.from_numpy(r).to(dev), torch.from_numpy(wT).to(dev), Kk,
+                                   eps=1e-5, bias=torch.from_numpy(b).to(dev))
+    oa = OF.round_to_format(ON.rmsnorm(r, None, 1e-5), OF.BF16)
+    assert np.array_equal(a.view(torch.int16).cpu().numpy().view(np.uint16), OF.bf16_bits(oa))
+    lg2 = OR.router_logits(oa.astype(np.float32), wT, b)
+    oids2 = OR.topk_ids(lg2, Kk)
+    assert np.array_equal(ids2.cpu().numpy(), oids2)
+    np.testing.assert_allclose(w2.cpu().numpy(), OR.routing_weights(lg2, oids2), rtol=1e-5,
+                               atol=0)
+
+
 @pytest.mark.parametrize("T,zipf", [(37, False), (2048, False), (300, True)])
 def test_route_from_router_weight_full(dev, T, zipf):
     x = synth.activations(T, H, "bf16", 3)
