@@ -192,9 +192,9 @@ moe_status_t moe_router_logits(const void *x, int x_dtype, const float *router_w
 
 /* Workspace bytes (host output) moe_route_topk and moe_norm_route need when
  * they compute the logits from a router weight (use_router_weight != 0),
- * else 0: up to 192 tokens one float32 per 512-input block, token and
- * expert (8*T*E*4, enough for any H <= 4096; larger H then take the
- * T*E*4 path), beyond that the logits, T*E*4. */
+ * else 0: one float32 per 512-input block, token and expert, 8*T*E*4
+ * (a bf16 router input with H <= 4096 takes the block sums; f16 inputs and
+ * larger H take the logits, T*E*4). */
 moe_status_t moe_route_workspace(int T, int E, int use_router_weight, size_t *bytes);
 
 /*
@@ -205,7 +205,7 @@ moe_status_t moe_route_workspace(int T, int E, int use_router_weight, size_t *by
  *
  * Logits come from exactly one of:
  *   router_wT: the moe_router_logits sum of x (x, x_dtype, H as there);
- *     its block sums (bf16 up to 192 tokens and H <= 4096) or the logits
+ *     its block sums (bf16 and H <= 4096) or the logits
  *     go to the workspace `ws` (moe_route_workspace bytes) and the top-K
  *     adds them up in block order;
  *   logits_in [T][E] float: given logits (x, router_wT, ws unused).

@@ -334,27 +334,33 @@ __device__ __forceinline__ void fma4x4_row_bcast<12>(float (&acc)[4], const floa
         : "memory");
 }
 
-template <int NP>
+// PART: one 512-input block per work group (the grid spans the blocks
+// too) and the chains' values to logits as block sums [block][T][E] for
+// the top-K; else all blocks in turn and the logits.
+template <int NP, bool PART>
 __global__ void __launch_bounds__(256) router_tiled_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wT,
     const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
     __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
     __shared__ __attribute__((aligned(16))) float xs[2][16][kRtKC];
     // Work groups go round-robin over the 8 XCDs; each XCD takes a
-    // contiguous range of (expert block, token block) pairs, expert block
-    // major, so it reads the weight slices of one or two expert blocks
-    // from its own L2 instead of all of them.
+    // contiguous range of (expert block[, input block], token block)
+    // tuples, expert block major, so it reads the weight slices of one or
+    // two expert blocks from its own L2 instead of all of them.
     const int nb = gridDim.x, b = blockIdx.x, xq = nb / 8, xr = nb % 8, xcd = b % 8;
     const int lid = xcd * xq + (xcd < xr ? xcd : xr) + b / 8;
-    const int ntb = (T + 15) / 16, eb = lid / ntb;
-    const int t0 = (lid - eb * ntb) * 16, e0 = eb * kRtExp;
+    const int ntb = (T + 15) / 16, P = PART ? (H + kRouterBlock - 1) / kRouterBlock : 1;
+    const int rest = lid / ntb, pb = rest % P, eb = rest / P;
+    const int t0 = (lid - rest * ntb) * 16, e0 = eb * kRtExp;
+    const int k0 = pb * kRouterBlock, kn = PART ? min(kRouterBlock, H - k0) : H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // this thread's staging share of x (rows past T read row t0; their
     // logits are not stored)
     const int ts = t0 + (tid >> 4);
-    const uint16_t *xsrc = x + (size_t)(ts < T ? ts : t0) * H + 4 * (tid & 15);
-    RouterWeightPipe<kRtKC, NP, kXStage> pipe(wT, E, e0, H, tid, xsrc, &xs[0][0][0]);
+    const uint16_t *xsrc = x + (size_t)(ts < T ? ts : t0) * H + k0 + 4 * (tid & 15);
+    RouterWeightPipe<kRtKC, NP, kXStage> pipe(wT + (size_t)k0 * E, E, e0, kn, tid, xsrc,
+                                              &xs[0][0][0]);
     pipe.prime();
 
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -376,15 +382,19 @@ __global__ void __launch_bounds__(256) router_tiled_kernel(
             fma4x4_row_bcast<8>(acc, xq[m & 1], &w[m & 1][8]);
             fma4x4_row_bcast<12>(acc, xq[m & 1], &w[m & 1][12]);
         }
-        block_end(c, pipe.nch, acc, tot);
+        if (!PART) block_end(c, pipe.nch, acc, tot);
     });
     const int e = e0 + lane;
     if (e >= E) return;
-    const float bv = bias ? bias[e] : 0.0f;
+    const float bv = bias && !PART ? bias[e] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = t0 + 4 * wave + i;
-        if (t < T) logits[(size_t)t * E + e] = bias ? tot[i] + bv : tot[i];
+        if (t >= T) continue;
+        if (PART)
+            logits[((size_t)pb * T + t) * E + e] = acc[i];
+        else
+            logits[(size_t)t * E + e] = bias ? tot[i] + bv : tot[i];
     }
 }
 
@@ -699,7 +709,7 @@ moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, c
     if (x_dtype == MOE_BF16 && T <= kRowsMaxT && H <= kRowsMaxH)
         launch_rows(x, T, H, wT, bias, E, logits, s);
     else if (x_dtype == MOE_BF16)
-        hipLaunchKernelGGL((router_tiled_kernel<2>), dim3(grid.x * grid.y), dim3(256), 0, s,
+        hipLaunchKernelGGL((router_tiled_kernel<2, false>), dim3(grid.x * grid.y), dim3(256), 0, s,
                            (const uint16_t *)x, wT, bias, T, H, E, logits);
     else
         hipLaunchKernelGGL(router_logits_kernel<MOE_F16>, grid, dim3(256), 0, s,
@@ -718,26 +728,41 @@ static_assert(kRowsMaxH / kRouterBlock <= kMaxRouterBlocks, "block sums the top-
 static bool block_path(int T, int H, int x_dtype) {
     return x_dtype == MOE_BF16 && T <= kRowsMaxT && H <= kRowsMaxH;
 }
+// Block sums (small batches by router_block_kernel, larger ones by the
+// tiled kernel): bf16 and H <= 4096.
+static bool sums_path(int H, int x_dtype) { return x_dtype == MOE_BF16 && H <= kRowsMaxH; }
 
 // Workspace floats of the routing calls: the block sums on that path,
 // else the logits; and the most any H <= kMaxDim can need.
 size_t router_ws_floats(int T, int H, int E, int x_dtype) {
-    return (size_t)(block_path(T, H, x_dtype) ? router_blocks(H) : 1) * T * E;
+    return (size_t)(sums_path(H, x_dtype) ? router_blocks(H) : 1) * T * E;
 }
 size_t router_ws_floats_max(int T, int E) {
-    return (size_t)(T <= kRowsMaxT ? kRowsMaxH / kRouterBlock : 1) * T * E;
+    return (size_t)(kRowsMaxH / kRouterBlock) * T * E;
 }
 
-// Block sums per 512-input block side by side for small bf16 batches
-// (T <= 192, H <= 4096): [router_blocks(H)][T][E]
-// into `part`, *P = router_blocks(H); otherwise the logits (no bias) with
-// *P = 1. Either way route_given_kernel adds them up in block order.
+// Block sums of bf16 inputs with H <= 4096, [router_blocks(H)][T][E] into
+// `part`, *P = router_blocks(H): router_block_kernel up to 192 tokens, the
+// tiled kernel with one 512-input block per work group beyond (8x the work
+// groups of one chain over all inputs: at 256 tokens 28 us against 72, at
+// 4096 tokens 266 against 276, H = 4096, E = 352). Otherwise the logits
+// (no bias) with *P = 1. Either way route_given_kernel adds them up in
+// block order.
 moe_status_t launch_router_scores(const void *x, int x_dtype, const float *wT, int T, int H,
                                   int E, float *part, int *P, hipStream_t s) {
     if (block_path(T, H, x_dtype)) {
         *P = router_blocks(H);
         if (T == 0) return MOE_OK;
         launch_block<false>(x, nullptr, 0.f, T, H, wT, E, nullptr, part, s);
+        MOE_LAUNCH_CHECK();
+        return MOE_OK;
+    }
+    if (x_dtype == MOE_BF16 && H <= kRowsMaxH) {
+        *P = router_blocks(H);
+        if (T == 0) return MOE_OK;
+        const int n = ((T + kRtTok - 1) / kRtTok) * ((E + kRtExp - 1) / kRtExp) * *P;
+        hipLaunchKernelGGL((router_tiled_kernel<2, true>), dim3(n), dim3(256), 0, s,
+                           (const uint16_t *)x, wT, nullptr, T, H, E, part);
         MOE_LAUNCH_CHECK();
         return MOE_OK;
     }

@@ -135,12 +135,18 @@ def test_route_topk_validation(L):
     assert R(n, 0, n, p, n, 4, 0, 16, 2, 1, n, p, n, 0, n) == B.MOE_ERR_INVALID_ARG
     # T == 0 is a no-op that touches nothing
     assert R(n, 0, n, p, n, 0, 0, 16, 2, 1, p, p, n, 0, n) == B.MOE_OK
-    assert B.moe_route_workspace(2048, 352, True) == 2048 * 352 * 4
+    # the workspace holds one sum per 512-input block, token and expert (8
+    # blocks for H <= 4096; wider f16 or bf16 inputs need only the logits)
+    assert B.moe_route_workspace(2048, 352, True) == 8 * 2048 * 352 * 4
     assert B.moe_route_workspace(2048, 352, False) == 0
-    # up to 192 tokens the workspace holds one sum per 512-input block
-    # (8 for H <= 4096)
     assert B.moe_route_workspace(192, 352, True) == 8 * 192 * 352 * 4
-    assert B.moe_route_workspace(193, 352, True) == 193 * 352 * 4
+    assert B.moe_route_workspace(193, 352, True) == 8 * 193 * 352 * 4
+    # bf16 past 192 tokens still takes the block sums
+    assert R(p, 2, p, n, n, 200, 1024, 16, 2, 1, p, p, p, 2 * 200 * 16 * 4 - 1, n) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # f16 takes the logits: one float per token and expert
+    assert R(p, 1, p, n, n, 200, 1024, 16, 2, 1, p, p, p, 200 * 16 * 4 - 1, n) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_router_logits_validation(L):

@@ -146,7 +146,8 @@ def test_router_block_order_every_path(dev, T):
     rounds to -1), against a lone 2^-31 for expert 1. Every router path
     returns the blocks' answer, so expert 1 is the top-1: the bf16 rows
     kernel (T = 3: logits in turn, block sums side by side for the top-K),
-    the tiled kernel (T = 200), the f16 kernel, and the fused norm (the
+    the tiled kernel (T = 200: logits in turn, one block per work group for
+    the top-K), the f16 kernel, and the fused norm (the
     +-1 rows normalise to +-16 exactly with eps = 0)."""
     Hh, Ee = 1024, 8
     xv = np.zeros((T, Hh), np.float32)
@@ -168,12 +169,14 @@ def test_router_block_order_every_path(dev, T):
     assert (ids.cpu().numpy() == 1).all()
 
 
-@pytest.mark.parametrize("T,Hh,Ee,Kk", [(5, 576, 20, 3), (70, 576, 24, 4), (3, 1088, 352, 8)])
+@pytest.mark.parametrize("T,Hh,Ee,Kk", [(5, 576, 20, 3), (70, 576, 24, 4), (3, 1088, 352, 8),
+                                         (300, 1088, 352, 8)])
 def test_block_sum_routing_short_last_block(dev, T, Hh, Ee, Kk):
     """The block-sum paths with a last block shorter than 512 inputs (H = 576:
     512 + 64; H = 1088: 2 x 512 + 64): moe_route_topk from a bf16 router
     input and moe_norm_route (fused) give the oracle's ids bit for bit and
-    its weights within 1e-5; T = 70 runs two tokens per wave."""
+    its weights within 1e-5; T = 70 runs two tokens per wave; T = 300 takes
+    the tiled kernel's block sums (and the unfused norm)."""
     x = synth.activations(T, Hh, "bf16", 60 + T)
     wT = synth.router_weight_T(Hh, Ee, 60 + T)
     b = synth.zipf_bias(Ee, 60 + T)
