@@ -148,30 +148,34 @@ __global__ void __launch_bounds__(256) router_logits_kernel(
 // XT = kXStage (NT = 256, KC = 64): the chunk's inputs of 16 tokens ride
 // along with the weights, 4 bf16 per thread (token tid / 16, inputs 4 (tid %
 // 16) .. + 3 of the chunk), and are stored widened to float32 into `xs`
-// [stage][16][KC] with the weights.
-constexpr int kXNone = 0, kXStage = 1;
+// [stage][16][KC] with the weights. XT = kXStage2: two tokens per thread,
+// tid / 16 from xsrc and tid / 16 + 16 from xsrc2, into [stage][32][KC].
+constexpr int kXNone = 0, kXStage = 1, kXStage2 = 2;
 
 template <int KC, int NP, int XT, int NT = 256>
 struct RouterWeightPipe {
     static constexpr int kStride = NT / 16;      // rows apart of a thread's loads
     static constexpr int kRows = KC / kStride;   // float4 loads per thread and chunk
+    static constexpr int kXR = XT == kXStage2 ? 2 : 1;  // staged token rows per thread
     f32x4_t r[NP][kRows];
-    uint2 xw[NP];
+    uint2 xw[NP][kXR];
     const float *src;                            // wT + (tid / 16) * E + column
-    const uint16_t *xt;                          // kXStage: this thread's 4 inputs
+    const uint16_t *xt[kXR];                     // this thread's 4 inputs of each row
     float *xs;                                   // kXStage: [2][16][KC] in LDS
     size_t row;                                  // one row of wT, in floats (E)
     int wk, we, nch;
 
     __device__ __forceinline__ RouterWeightPipe(const float *wT, int E, int e0, int H, int tid,
                                                 const uint16_t *xsrc = nullptr,
-                                                float *xstage = nullptr) {
+                                                float *xstage = nullptr,
+                                                const uint16_t *xsrc2 = nullptr) {
         wk = tid >> 4;
         we = (tid & 15) * 4;
         src = wT + (size_t)wk * E + (e0 + we < E ? e0 + we : E - 4);
         row = (size_t)E;
         nch = H / KC;
-        xt = xsrc;
+        xt[0] = xsrc;
+        xt[kXR - 1] = XT == kXStage2 ? xsrc2 : xsrc;
         xs = xstage;
     }
     __device__ __forceinline__ void load(int slot, int chunk) {
@@ -179,16 +183,22 @@ struct RouterWeightPipe {
         const float *p = src + (size_t)chunk * KC * row;
 #pragma unroll
         for (int i = 0; i < kRows; ++i) r[slot][i] = *(const f32x4_t *)(p + i * kStride * row);
-        if (XT == kXStage) xw[slot] = *(const uint2 *)(xt + (size_t)chunk * KC);
+        if (XT != kXNone)
+#pragma unroll
+            for (int q = 0; q < kXR; ++q) xw[slot][q] = *(const uint2 *)(xt[q] + (size_t)chunk * KC);
     }
     __device__ __forceinline__ void store(float (*ws)[KC][kRtExp], int stage, int slot) {
 #pragma unroll
         for (int i = 0; i < kRows; ++i)
             *(f32x4_t *)&ws[stage][wk + kStride * i][we] = r[slot][i];
-        if (XT == kXStage)
-            *(f32x4_t *)&xs[(stage * 16 + wk) * KC + we] =
-                f32x4_t{__uint_as_float(xw[slot].x << 16), __uint_as_float(xw[slot].x & 0xFFFF0000u),
-                        __uint_as_float(xw[slot].y << 16), __uint_as_float(xw[slot].y & 0xFFFF0000u)};
+        if (XT != kXNone)
+#pragma unroll
+            for (int q = 0; q < kXR; ++q) {
+                const uint2 v = xw[slot][q];
+                *(f32x4_t *)&xs[(stage * 16 * kXR + wk + 16 * q) * KC + we] =
+                    f32x4_t{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                            __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+            }
     }
     // chunks 0 .. NP-1 in flight
     __device__ __forceinline__ void prime() {
@@ -216,7 +226,7 @@ struct RouterWeightPipe {
 };
 
 // Larger bf16 batches: 64 experts x 16 tokens a work group, 4 tokens per
-// wave. Each 64-input chunk stages the weight tile and the 16 tokens'
+// wave (or 32 tokens, 8 per wave, two 4-token groups per weight read). Each 64-input chunk stages the weight tile and the 16 tokens'
 // inputs (widened to float32) in LDS; a wave reads, per 16 inputs, 16
 // weights (8 pair reads, shared by its 4 tokens) and one 4-byte input word
 // per token (lane j of every 16-lane row: input j), and runs the 4 tokens'
@@ -336,40 +346,45 @@ __device__ __forceinline__ void fma4x4_row_bcast<12>(float (&acc)[4], const floa
 
 // PART: one 512-input block per work group (the grid spans the blocks
 // too) and the chains' values to logits as block sums [block][T][E] for
-// the top-K; else all blocks in turn and the logits.
-template <int NP, bool PART>
+// the top-K; else all blocks in turn and the logits. TPW tokens per wave
+// (4 or 8), 4 TPW per work group.
+template <int NP, bool PART, int TPW>
 __global__ void __launch_bounds__(256) router_tiled_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wT,
     const float *__restrict__ bias, int T, int H, int E, float *__restrict__ logits) {
+    constexpr int BT = 4 * TPW;
     __shared__ __attribute__((aligned(16))) float ws[2][kRtKC][kRtExp];
-    __shared__ __attribute__((aligned(16))) float xs[2][16][kRtKC];
+    __shared__ __attribute__((aligned(16))) float xs[2][BT][kRtKC];
     // Work groups go round-robin over the 8 XCDs; each XCD takes a
     // contiguous range of (expert block[, input block], token block)
     // tuples, expert block major, so it reads the weight slices of one or
     // two expert blocks from its own L2 instead of all of them.
     const int nb = gridDim.x, b = blockIdx.x, xq = nb / 8, xr = nb % 8, xcd = b % 8;
     const int lid = xcd * xq + (xcd < xr ? xcd : xr) + b / 8;
-    const int ntb = (T + 15) / 16, P = PART ? (H + kRouterBlock - 1) / kRouterBlock : 1;
+    const int ntb = (T + BT - 1) / BT, P = PART ? (H + kRouterBlock - 1) / kRouterBlock : 1;
     const int rest = lid / ntb, pb = rest % P, eb = rest / P;
-    const int t0 = (lid - rest * ntb) * 16, e0 = eb * kRtExp;
+    const int t0 = (lid - rest * ntb) * BT, e0 = eb * kRtExp;
     const int k0 = pb * kRouterBlock, kn = PART ? min(kRouterBlock, H - k0) : H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // this thread's staging share of x (rows past T read row t0; their
     // logits are not stored)
-    const int ts = t0 + (tid >> 4);
+    const int ts = t0 + (tid >> 4), ts2 = ts + 16;
     const uint16_t *xsrc = x + (size_t)(ts < T ? ts : t0) * H + k0 + 4 * (tid & 15);
-    RouterWeightPipe<kRtKC, NP, kXStage> pipe(wT + (size_t)k0 * E, E, e0, kn, tid, xsrc,
-                                              &xs[0][0][0]);
+    const uint16_t *xsrc2 = x + (size_t)(ts2 < T ? ts2 : t0) * H + k0 + 4 * (tid & 15);
+    RouterWeightPipe<kRtKC, NP, TPW == 8 ? kXStage2 : kXStage> pipe(
+        wT + (size_t)k0 * E, E, e0, kn, tid, xsrc, &xs[0][0][0], xsrc2);
     pipe.prime();
 
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[TPW], tot[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) acc[i] = tot[i] = 0.0f;
     pipe.run(ws, [&](int c, float (*st)[kRtExp]) {
-        const float *xw = &xs[c & 1][4 * wave][lane & 15];
-        float xq[2][4], w[2][16];
+        const float *xw = &xs[c & 1][TPW * wave][lane & 15];
+        float xq[2][TPW], w[2][16];
         auto read = [&](int m, int b) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xq[b][i] = xw[i * kRtKC + 16 * m];
+            for (int i = 0; i < TPW; ++i) xq[b][i] = xw[i * kRtKC + 16 * m];
 #pragma unroll
             for (int j = 0; j < 16; ++j) w[b][j] = st[16 * m + j][lane];
         };
@@ -377,10 +392,15 @@ __global__ void __launch_bounds__(256) router_tiled_kernel(
 #pragma unroll
         for (int m = 0; m < kRtKC / 16; ++m) {
             if (m + 1 < kRtKC / 16) read(m + 1, (m + 1) & 1);
-            fma4x4_row_bcast<0>(acc, xq[m & 1], &w[m & 1][0]);
-            fma4x4_row_bcast<4>(acc, xq[m & 1], &w[m & 1][4]);
-            fma4x4_row_bcast<8>(acc, xq[m & 1], &w[m & 1][8]);
-            fma4x4_row_bcast<12>(acc, xq[m & 1], &w[m & 1][12]);
+#pragma unroll
+            for (int g = 0; g < TPW / 4; ++g) {
+                float(&a4)[4] = *reinterpret_cast<float(*)[4]>(&acc[4 * g]);
+                const float(&x4)[4] = *reinterpret_cast<const float(*)[4]>(&xq[m & 1][4 * g]);
+                fma4x4_row_bcast<0>(a4, x4, &w[m & 1][0]);
+                fma4x4_row_bcast<4>(a4, x4, &w[m & 1][4]);
+                fma4x4_row_bcast<8>(a4, x4, &w[m & 1][8]);
+                fma4x4_row_bcast<12>(a4, x4, &w[m & 1][12]);
+            }
         }
         if (!PART) block_end(c, pipe.nch, acc, tot);
     });
@@ -388,8 +408,8 @@ __global__ void __launch_bounds__(256) router_tiled_kernel(
     if (e >= E) return;
     const float bv = bias && !PART ? bias[e] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * wave + i;
+    for (int i = 0; i < TPW; ++i) {
+        const int t = t0 + TPW * wave + i;
         if (t >= T) continue;
         if (PART)
             logits[((size_t)pb * T + t) * E + e] = acc[i];
@@ -709,7 +729,7 @@ moe_status_t launch_router_logits(const void *x, int x_dtype, const float *wT, c
     if (x_dtype == MOE_BF16 && T <= kRowsMaxT && H <= kRowsMaxH)
         launch_rows(x, T, H, wT, bias, E, logits, s);
     else if (x_dtype == MOE_BF16)
-        hipLaunchKernelGGL((router_tiled_kernel<2, false>), dim3(grid.x * grid.y), dim3(256), 0, s,
+        hipLaunchKernelGGL((router_tiled_kernel<2, false, 4>), dim3(grid.x * grid.y), dim3(256), 0, s,
                            (const uint16_t *)x, wT, bias, T, H, E, logits);
     else
         hipLaunchKernelGGL(router_logits_kernel<MOE_F16>, grid, dim3(256), 0, s,
@@ -741,11 +761,19 @@ size_t router_ws_floats_max(int T, int E) {
     return (size_t)(kRowsMaxH / kRouterBlock) * T * E;
 }
 
+// Tokens per wave of the tiled kernel's block sums: 8 from this batch size
+// up (twice the independent chains per lane and half the LDS weight reads
+// per FMA, at 3 work groups per CU instead of 4: routing at H = 4096, E =
+// 352 took 41.4 / 70.7 / 130.6 / 240.1 us at 512 / 1024 / 2048 / 4096
+// tokens against 44.2 / 79.0 / 141.4 / 263.3 with 4), else 4 (256 tokens:
+// 28.3 us against 31.5).
+constexpr int kTiled8MinT = 512;
+
 // Block sums of bf16 inputs with H <= 4096, [router_blocks(H)][T][E] into
 // `part`, *P = router_blocks(H): router_block_kernel up to 192 tokens, the
 // tiled kernel with one 512-input block per work group beyond (8x the work
 // groups of one chain over all inputs: at 256 tokens 28 us against 72, at
-// 4096 tokens 266 against 276, H = 4096, E = 352). Otherwise the logits
+// 4096 tokens 263 against 276 with 4 tokens per wave). Otherwise the logits
 // (no bias) with *P = 1. Either way route_given_kernel adds them up in
 // block order.
 moe_status_t launch_router_scores(const void *x, int x_dtype, const float *wT, int T, int H,
@@ -760,9 +788,14 @@ moe_status_t launch_router_scores(const void *x, int x_dtype, const float *wT, i
     if (x_dtype == MOE_BF16 && H <= kRowsMaxH) {
         *P = router_blocks(H);
         if (T == 0) return MOE_OK;
-        const int n = ((T + kRtTok - 1) / kRtTok) * ((E + kRtExp - 1) / kRtExp) * *P;
-        hipLaunchKernelGGL((router_tiled_kernel<2, true>), dim3(n), dim3(256), 0, s,
-                           (const uint16_t *)x, wT, nullptr, T, H, E, part);
+        const int bt = T >= kTiled8MinT ? 32 : 16;
+        const int n = ((T + bt - 1) / bt) * ((E + kRtExp - 1) / kRtExp) * *P;
+        if (bt == 32)
+            hipLaunchKernelGGL((router_tiled_kernel<2, true, 8>), dim3(n), dim3(256), 0, s,
+                               (const uint16_t *)x, wT, nullptr, T, H, E, part);
+        else
+            hipLaunchKernelGGL((router_tiled_kernel<2, true, 4>), dim3(n), dim3(256), 0, s,
+                               (const uint16_t *)x, wT, nullptr, T, H, E, part);
         MOE_LAUNCH_CHECK();
         return MOE_OK;
     }

@@ -170,13 +170,14 @@ def test_router_block_order_every_path(dev, T):
 
 
 @pytest.mark.parametrize("T,Hh,Ee,Kk", [(5, 576, 20, 3), (70, 576, 24, 4), (3, 1088, 352, 8),
-                                         (300, 1088, 352, 8)])
+                                         (300, 1088, 352, 8), (600, 576, 40, 8)])
 def test_block_sum_routing_short_last_block(dev, T, Hh, Ee, Kk):
     """The block-sum paths with a last block shorter than 512 inputs (H = 576:
     512 + 64; H = 1088: 2 x 512 + 64): moe_route_topk from a bf16 router
     input and moe_norm_route (fused) give the oracle's ids bit for bit and
     its weights within 1e-5; T = 70 runs two tokens per wave; T = 300 takes
-    the tiled kernel's block sums (and the unfused norm)."""
+    the tiled kernel's block sums with 4 tokens per wave (and the unfused
+    norm), T = 600 with 8 and a last 32-token tile of 24."""
     x = synth.activations(T, Hh, "bf16", 60 + T)
     wT = synth.router_weight_T(Hh, Ee, 60 + T)
     b = synth.zipf_bias(Ee, 60 + T)
