@@ -35,7 +35,8 @@ moe_status_t launch_csf_row_index(const uint32_t *exceptions, int64_t n, const i
 moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
                                  hipStream_t s, const std::function<moe_status_t(int)> &mark);
-bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act);
+bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act, int T, int K);
+bool nvfp4_mx_band(const moe_ffn_desc_t &ex, int T, int K);
 moe_status_t launch_gemv_mx_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
                                     const moe_perm_t &p, int max_tiles, void *h, float *y,
                                     hipStream_t s, const std::function<moe_status_t(int)> &mark);
@@ -65,7 +66,7 @@ moe_status_t launch_act_quant(const void *in, int dtype, int64_t rows, int k, fl
 DenseSplit dense_plan(int T, int H, int F);
 bool dense_shape_ok(int H, int F);
 int gemv_tile_m();
-int gemv_mx_tile_m(int T);
+int gemv_mx_tile_m(int T, int K, int E);
 int gemm_tile_m();
 int gemm_group();
 int gemm_bn();
@@ -204,10 +205,11 @@ struct FwdPlan {
 };
 
 // Kernel choice by batch shape: with few slots per expert the dequantizing
-// GEMV streams each touched expert once per tile of 4 slots; once the
-// average expert sees several tiles' worth of slots (T*K >= 4*E) the MFMA
-// grouped GEMM, which reads each weight once per tile of 64 slots, takes
-// over. One code path per shape class.
+// GEMV streams each touched expert once per tile of 4 or 8 slots; once the
+// average expert sees several tiles' worth of slots (T*K >= 4*E; NVFP4 at
+// the layer's shape 8*E, with the MFMA GEMV's 8-slot tiles in between) the
+// MFMA grouped GEMM, which reads each weight once per tile of 64 slots,
+// takes over. One code path per shape class.
 bool mfma_layout_ok(const moe_weight_desc_t &d) {
     // compressed scales reach the GEMM expanded into the workspace (aligned
     // there); the expansion reads 8 code bytes at a time
@@ -235,6 +237,8 @@ bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
     if (f != MOE_W_INT4_G128 && f != MOE_W_INT4_G128_ASYM && f != MOE_W_INT4_G32 &&
         f != MOE_W_INT8_G128 && f != MOE_W_NVFP4_G16 && f != MOE_W_NVFP4_CSF)
         return false;
+    // NVFP4 at the layer's shape from 4E to 8E slots: the MFMA GEMV
+    if (f == MOE_W_NVFP4_G16 && gemv_mx_supported(ex, MOE_F16, T, K)) return false;
     // 32-bit buffer offsets must reach every row of an expert matrix
     const bool fits = (int64_t)F * ex.gate.qweight_row_stride < INT32_MAX &&
                       (int64_t)F * ex.up.qweight_row_stride < INT32_MAX &&
@@ -254,7 +258,7 @@ FwdPlan plan_forward(const moe_ffn_desc_t &ex, int T, int K, int E, int H, int F
     FwdPlan p;
     p.mfma = use_mfma(ex, T, K);
     p.tile_m = p.mfma ? gemm_tile_m()
-               : gemv_mx_supported(ex, MOE_F16) ? gemv_mx_tile_m(T) : gemv_tile_m();
+               : gemv_mx_supported(ex, MOE_F16, T, K) ? gemv_mx_tile_m(T, K, E) : gemv_tile_m();
     p.max_rows = perm_max_rows(T, K, E, p.tile_m);
     p.max_tiles = p.max_rows / p.tile_m;
     p.off_h = 0;
@@ -511,7 +515,7 @@ static moe_status_t forward_impl(const moe_ffn_desc_t *experts, const moe_ffn_de
     st = p.mfma ? launch_gemm_forward(ex, xin, act_dtype, T, K, *perm, (int)p.max_tiles, h, y,
                                       y16, yexp, w + p.off_xperm, (float *)(w + p.off_xsum),
                                       (float *)(w + p.off_hsum), s, mk)
-         : gemv_mx_supported(*experts, act_dtype)
+         : gemv_mx_supported(*experts, act_dtype, T, K)
              ? launch_gemv_mx_forward(*experts, xin, act_dtype, K, *perm, (int)p.max_tiles, h, y,
                                       s, mk)
              : launch_gemv_forward(*experts, xin, act_dtype, K, *perm, (int)p.max_tiles, h, y, s,

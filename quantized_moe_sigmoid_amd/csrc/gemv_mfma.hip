@@ -31,6 +31,21 @@
 // 1/16, and the staged group sum carries both biases, 1032 sum(x even) +
 // 72 sum(x odd).
 //
+// NVFP4 (E2M1 codes, one E4M3 scale per 16 inputs, a float32 scale per
+// expert): every MFMA spans four 16-input blocks, so the block scale goes
+// into the operand. The scaled pair conversion gives 256 e2m1 exactly in
+// fp16 (its scale is a power of two), and one packed fp16 multiply by the
+// scale's bits moved into an fp16 (b / 256, subnormal for the smaller
+// scales) leaves e2m1 x E4M3, at most 6 significant bits inside fp16's
+// normal range: exact. The MFMA runs in fp16 for both activation types: bf16
+// inputs are staged as fp16 x 2^-p with p per staged row from its largest
+// magnitude (largest < 2^15 after the shift), exact for every element within
+// 2^29 of that largest, and the epilogue multiplies by the global and input
+// scales, then by 2^p. The rows are staged in input order, the MFMAs add
+// into the accumulators directly (no group rescale), and a step's block
+// scales travel with its weights (two bytes per loading lane, moved to the
+// MFMA lanes by ds_bpermute).
+//
 // A tile's padding slots (t >= m) are neither staged nor stored: the rows
 // of an MFMA result are independent, so whatever their LDS rows hold only
 // reaches outputs that are dropped.
@@ -60,16 +75,38 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 __host__ __device__ constexpr int mx_upad(int kin) { return kin / 8 + 1; }
 
 // Staged rows, the group sums [group][16 slots] (float32), one 16-row x
-// 64-byte weight tile per wave, and with KS > 1 the partial sums [wave]
-// [matrix][lane] (float32 x 4).
-inline size_t gemv_mx_lds_bytes(int tm, int kin, int ks, int nm) {
+// 64-byte weight tile per wave, with KS > 1 the partial sums [wave]
+// [matrix][lane] (float32 x 4), and for NVFP4 the staging exponents (per
+// slot: the waves' largest magnitudes, then p).
+constexpr int kMxF4Bytes = 16 * (kMxWaves + 1) * 4;
+inline size_t gemv_mx_lds_bytes(int tm, int kin, int ks, int nm, bool f4) {
     return (size_t)tm * mx_upad(kin) * 16 + (size_t)(kin / 128) * 16 * sizeof(float) +
-           (size_t)kMxWaves * 1024 + (ks > 1 ? (size_t)kMxWaves * nm * kWave * 16 : 0);
+           (size_t)kMxWaves * 1024 + (ks > 1 ? (size_t)kMxWaves * nm * kWave * 16 : 0) +
+           (f4 ? kMxF4Bytes : 0);
 }
 
 template <int ACT, int FMT>
 __host__ __device__ constexpr bool mx_x16() {
     return ACT == MOE_F16 && FMT == MOE_W_INT4_G128;
+}
+
+// Word d of NVFP4 codes (inputs 0..7 in order) as the fp16 pairs e2m1 x
+// E4M3: sp holds the block scale as fp16 bits of b / 256 in both halves.
+__device__ __forceinline__ uint4 mx_decode_f4(uint32_t d, uint32_t sp) {
+    const half2_t s2 = __builtin_bit_cast(half2_t, sp);
+    auto mul = [&](half2_t v) { return __builtin_bit_cast(uint32_t, v * s2); };
+    return make_uint4(mul(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 256.0f, 0)),
+                      mul(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 256.0f, 1)),
+                      mul(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 256.0f, 2)),
+                      mul(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 256.0f, 3)));
+}
+
+// E4M3 byte b as the fp16 bits of b / 256 (exponent and mantissa fields
+// moved up by 7 bits, which also maps its subnormals onto fp16's), in both
+// halves of a word.
+__device__ __forceinline__ uint32_t e4m3_f16_pair(uint32_t b) {
+    const uint32_t h = ((b & 0x7Fu) << 7) | ((b & 0x80u) << 8);
+    return h | (h << 16);
 }
 
 // The four pairs (inputs i, i + 4 of the word, i < 4) of word d as BIAS + q
@@ -102,6 +139,7 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
     static_assert(UNITS % 16 == 0 && kMxWaves % KS == 0 && NS % KS == 0 && NSW % R == 0,
                   "whole groups, wave parts and ring trips");
     constexpr bool kZ = int4_asym(FMT), X16 = mx_x16<ACT, FMT>();
+    constexpr bool kF4 = FMT == MOE_W_NVFP4_G16;
     constexpr int NM = GATEUP ? 2 : 1;           // matrices streamed side by side
     // one matrix: odd ring slots refill themselves and the slot before, so
     // both halves of a 128-byte row line are asked for together (two
@@ -132,6 +170,11 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
     float *xb = (float *)(smem + TM * UPAD);
     uint4 *wt = smem + TM * UPAD + NS * 4 + wave * 64;   // this wave's 16 x 64-byte tile
     f32x4_t *red = (f32x4_t *)(smem + TM * UPAD + NS * 4 + kMxWaves * 64);
+    // NVFP4: [slot][wave] largest magnitudes, then [slot] staging exponents
+    float *f4m = (float *)(red + (KS > 1 ? kMxWaves * NM * kWave : 0));
+    int *f4e = (int *)(f4m + 16 * kMxWaves);
+    // NVFP4: the expert's global scale with the input scale, per matrix
+    const float ca = kF4 ? A.gs[e] * A.xs : 1.0f, cb = kF4 ? B.gs[e] * B.xs : 1.0f;
 
     // ---- activation staging: every thread, units t + 256 i of each slot ----
     // (the first four slots' loads go out before the weights')
@@ -153,7 +196,7 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
     auto block_of = [&](int p) { return ((blockIdx.x * RP + p) * BPW + wb) * 16; };
     const GemvMat *mats[2] = {&A, &B};
     __amdgpu_buffer_rsrc_t rq[NM], rs[NM], rz[NM];
-    int q0[NM], s0[NM], z0[NM], qp[NM], sp[NM], zp[NM];
+    int q0[NM], s0[NM], z0[NM], qp[NM], sp[NM], zp[NM], f0[NM];
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
         const GemvMat &M = *mats[k];
@@ -167,21 +210,30 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
         qp[k] = 16 * BPW * (int)M.qr;            // the next pass's block
         sp[k] = 16 * BPW * (int)M.sr;
         zp[k] = 16 * BPW * (int)M.zr;
+        // NVFP4: a step's eight block scales of row lr, two bytes per lane
+        // of the row (blocks 2 lc, 2 lc + 1; 4 rows per 16 lanes, as the
+        // weights), passed to the MFMA lanes by ds_bpermute
+        f0[k] = row * (int)M.sr + 2 * lc;
     }
     u32x4_t w[R][NM];
+    uint32_t wsc[R][NM];
     // step j of pass p into ring slot `slot`; every call issues the same
     // loads, so the compiler's waits count exactly the younger steps
     auto load = [&](int slot, int p, int j) {
 #pragma unroll
-        for (int k = 0; k < NM; ++k)
+        for (int k = 0; k < NM; ++k) {
             w[slot][k] = __builtin_bit_cast(
                 u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq[k], q0[k] + p * qp[k] + 64 * j, 0, 0));
+            if constexpr (kF4)
+                wsc[slot][k] = __builtin_amdgcn_raw_buffer_load_b16(rs[k], f0[k] + p * sp[k] + 8 * j, 0, 0);
+        }
     };
     // the block's scales (and zero points) of pass p, as loaded: lane 4 r + c
     // holds bytes 16 i + 4 c .. + 3 of row r, i < SL (ZL); bytes past a
     // row's end are never used (past the matrix they read zero)
     uint32_t sreg[NM][SL], zreg[NM][kZ ? ZL : 1];
     auto load_scales = [&](int p) {
+        if constexpr (kF4) return;               // NVFP4: with the weights
 #pragma unroll
         for (int k = 0; k < NM; ++k) {
 #pragma unroll
@@ -202,7 +254,30 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- activations into LDS: pair order of the decoder, group sums -------
+    int pe[4] = {0, 0, 0, 0};                    // NVFP4, bf16: the batch's exponents p
     auto xstage = [&](int t, int q) {
+        if constexpr (kF4) {                     // input order; bf16 as fp16 x 2^-p
+#pragma unroll
+            for (int i = 0; i < SPT; ++i) {
+                const u32x4_t v = xv[q][i];
+                const int u = threadIdx.x + kMxThreads * i;
+                uint32_t o[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if constexpr (ACT == MOE_BF16) {
+                        const uint32_t lo = f32_to_f16_bits(
+                            __builtin_amdgcn_ldexpf(bf16_bits_to_f32(v[c] & 0xFFFFu), -pe[q]));
+                        const uint32_t hi = f32_to_f16_bits(
+                            __builtin_amdgcn_ldexpf(bf16_bits_to_f32(v[c] >> 16), -pe[q]));
+                        o[c] = lo | (hi << 16);
+                    } else {
+                        o[c] = v[c];
+                    }
+                }
+                if (u < UNITS) xs[t * UPAD + u] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
             const u32x4_t v = xv[q][i];
@@ -243,6 +318,50 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
             if (valid && r16 == 0) xb[(u >> 4) * 16 + t] = sum;
         }
     };
+    // NVFP4 with bf16 inputs: p of the staged rows t0 .. t0 + 3 (those below
+    // m) from their largest magnitude, so that it stays below 2^15 in fp16
+    // (m is uniform over the work group: every thread takes the barrier)
+    auto f4_exps = [&](int t0) {
+        if constexpr (kF4 && ACT == MOE_BF16) {
+            float mx[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                mx[q] = 0.0f;
+                if (t0 + q < m) {
+#pragma unroll
+                    for (int i = 0; i < SPT; ++i) {
+                        const u32x4_t v = xv[q][i];      // past the row: its unit 0
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            mx[q] = fmaxf(mx[q], fmaxf(fabsf(bf16_bits_to_f32(v[c] & 0xFFFFu)),
+                                                       fabsf(bf16_bits_to_f32(v[c] >> 16))));
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < kWave; o <<= 1) mx[q] = fmaxf(mx[q], shfl_xor_f(mx[q], o));
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (t0 + q < m) f4m[(t0 + q) * kMxWaves + wave] = mx[q];
+            }
+            lds_barrier();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                pe[q] = 0;
+                if (t0 + q < m) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int w2 = 0; w2 < kMxWaves; ++w2) v = fmaxf(v, f4m[(t0 + q) * kMxWaves + w2]);
+                    // largest in [2^E, 2^(E+1)) -> p = E - 14; a zero row keeps p = 0
+                    const int eb = (int)((__float_as_uint(v) >> 23) & 0xFFu);
+                    pe[q] = v > 0.0f ? eb - 127 - 14 : 0;
+                    if (threadIdx.x == 0) f4e[t0 + q] = pe[q];
+                }
+            }
+        }
+    };
+    f4_exps(0);
 #pragma unroll
     for (int q = 0; q < 4 && q < TM; ++q)
         if (q < m) xstage(q, q);
@@ -250,6 +369,7 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (t0 + q < m) xload(t0 + q, q);
+        f4_exps(t0);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (t0 + q < m) xstage(t0 + q, q);
@@ -298,10 +418,19 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
                 const int s = 4 * g + i;
                 if (s < m) {
                     const size_t r = (size_t)tile * TM + s;
+                    float v0 = acc[0][i], v1 = acc[NM - 1][i];
+                    if constexpr (kF4) {
+                        // global and input scales first, then 2^p: a sum of
+                        // staged (< 2^15) inputs may exceed float32 once
+                        // shifted back, the scaled value may not
+                        const int pp = ACT == MOE_BF16 ? f4e[s] : 0;
+                        v0 = __builtin_amdgcn_ldexpf(v0 * ca, pp);
+                        v1 = __builtin_amdgcn_ldexpf(v1 * cb, pp);
+                    }
                     if constexpr (GATEUP)
-                        hout[r * n_rows + row] = f32_to_act<ACT>(silu_mul(acc[0][i], acc[1][i]));
+                        hout[r * n_rows + row] = f32_to_act<ACT>(silu_mul(v0, v1));
                     else
-                        yout[r * n_rows + row] = acc[0][i];
+                        yout[r * n_rows + row] = v0;
                 }
             }
         }
@@ -322,6 +451,18 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
             // through the wave's tile into the MFMA layout: row r16, chunk g
             *wt_st = __builtin_bit_cast(uint4, w[slot][k]);
             const uint4 wv = *wt_ld;
+            if constexpr (kF4) {
+                // words 0, 1: block 2 g of the step; words 2, 3: block 2 g + 1,
+                // loaded by lane 4 r16 + g
+                const uint32_t sb =
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_s + 4 * g, (int)wsc[slot][k]);
+                const uint32_t s0p = e4m3_f16_pair(sb & 0xFFu), s1p = e4m3_f16_pair(sb >> 8);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) d[k][q] = mx_decode_f4((&wv.x)[q], q < 2 ? s0p : s1p);
+                sc[k] = 1.0f;
+                bi[k] = 0.0f;
+                continue;
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) d[k][q] = mx_decode<X16>((&wv.x)[q], kv, kv1);
             // scale of (row r16, group j): bytes 2j of the row, held by lane
@@ -351,6 +492,15 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
             }
         }
         const uint4 *xa = xs + xa0 + 16 * j;
+        if constexpr (kF4) {                     // no group rescale: into the accumulators
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 x = xa[q];
+#pragma unroll
+                for (int k = 0; k < NM; ++k) acc[k] = mfma16<MOE_F16>(x, d[k][q], acc[k]);
+            }
+            return;
+        }
         const f32x4_t xsum = *(const f32x4_t *)(xb + j * 16 + 4 * g);
         f32x4_t t[NM];
 #pragma unroll
@@ -406,6 +556,12 @@ __global__ void __launch_bounds__(kMxThreads) gemv_mx_kernel(
 // kernel's loads); other shapes, formats and layouts run the dot2 GEMV.
 static bool mx_layout_ok(const moe_weight_desc_t &d) {
     auto al = [](const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
+    if (d.fmt == MOE_W_NVFP4_G16)                // 2-byte scale loads, a global scale
+        return al(d.qweight, 16) && d.qweight_row_stride % 16 == 0 &&
+               d.qweight_expert_stride % 16 == 0 && al(d.scale, 2) && d.scale_row_stride % 2 == 0 &&
+               d.scale_expert_stride % 2 == 0 && d.global_scale &&
+               (int64_t)d.n * d.qweight_row_stride < INT32_MAX &&
+               (int64_t)d.n * d.scale_row_stride < INT32_MAX;
     const bool z = d.fmt != MOE_W_INT4_G128_ASYM ||
                    (al(d.zero_point, 4) && d.zero_point_row_stride % 4 == 0 &&
                     d.zero_point_expert_stride % 4 == 0 &&
@@ -416,15 +572,32 @@ static bool mx_layout_ok(const moe_weight_desc_t &d) {
            (int64_t)d.n * d.scale_row_stride < INT32_MAX && z;
 }
 
-bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act) {
+// NVFP4 banks take this kernel only for T*K in [4E, 8E) (176 to 351 tokens
+// at top-8 of 352), with 8-slot tiles. Below, the dot2 GEMV is faster: its
+// decode is one conversion per pair, where exact fp16 operands need a
+// conversion and a multiply, and that makes this kernel's gate/up pass
+// issue-bound (same host: T=1 40.5 against 39.5 us per step, T=8 170 against
+// 142, T=64 617 against 578). From 4E slots the dot2 GEMV's 4-slot tiles
+// re-read experts and the 64-row GEMM tiles run mostly empty: at T=256 this
+// kernel took 0.960 ms per step against the GEMM's 1.125 (16-slot tiles:
+// 1.096), at T=512 1.376 against 1.148.
+bool nvfp4_mx_band(const moe_ffn_desc_t &ex, int T, int K) {
+    const int64_t n = (int64_t)T * K, E = ex.gate.num_experts;
+    return n >= 4 * E && n < 8 * E;
+}
+
+bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act, int T, int K) {
     const int f = ex.gate.fmt;
+    if (f == MOE_W_NVFP4_G16 && !nvfp4_mx_band(ex, T, K)) return false;
     return (act == MOE_F16 || act == MOE_BF16) &&
-           (f == MOE_W_INT4_G128 || f == MOE_W_INT4_G128_ASYM) && ex.gate.k == 4096 &&
+           (f == MOE_W_INT4_G128 || f == MOE_W_INT4_G128_ASYM || f == MOE_W_NVFP4_G16) &&
+           ex.gate.k == 4096 &&
            ex.gate.n == 1536 && ex.down.k == 1536 && ex.down.n == 4096 &&
            mx_layout_ok(ex.gate) && mx_layout_ok(ex.up) && mx_layout_ok(ex.down);
 }
 
-// Slots per tile: 8 for 5 to 32 tokens, else 4. The plan sees the batch
+// Slots per tile: 8 for 5 to 32 tokens and from T*K = 4E (NVFP4 only), else
+// 4. The plan sees the batch
 // size but not the routing. Measured (bench, graph replay, same host):
 // 8-slot tiles took the Zipf-routed 8-layer stack at T=32 from 1.33-1.35
 // to 1.22-1.25 ms per step (a hot expert re-streams its weights once per
@@ -433,14 +606,16 @@ bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act) {
 // halve the work groups per CU) and at T=1 from 34.3 to 36.5 us. Up to 4
 // tokens no expert holds more than 4 slots unless a token repeats an id.
 // 16 slots were slower for both.
-int gemv_mx_tile_m(int T) { return T > 4 && T <= 32 ? 8 : 4; }
+int gemv_mx_tile_m(int T, int K, int E) {
+    return (T > 4 && T <= 32) || (int64_t)T * K >= 4 * (int64_t)E ? 8 : 4;
+}
 constexpr int kMxDeepTiles = 300;
 
 template <int ACT, int FMT, int TM, bool GATEUP, int NS, int RP, int KS, int R>
 moe_status_t launch_mx(const GemvMat &a, const GemvMat &b, int n_rows, const uint16_t *x,
                        int K, const moe_perm_t &p, int max_tiles, uint16_t *h, float *y,
                        hipStream_t s) {
-    const size_t lds = gemv_mx_lds_bytes(TM, NS * 128, KS, GATEUP ? 2 : 1);
+    const size_t lds = gemv_mx_lds_bytes(TM, NS * 128, KS, GATEUP ? 2 : 1, FMT == MOE_W_NVFP4_G16);
     auto k = gemv_mx_kernel<ACT, FMT, TM, GATEUP, NS, RP, KS, R>;
     allow_lds(k, lds);
     const int rows_per_group = 16 * (kMxWaves / KS) * RP;
@@ -501,6 +676,8 @@ moe_status_t launch_gemv_mx_forward(const moe_ffn_desc_t &ex, const void *x, int
     MOE_MX_FMT(MOE_F16, MOE_W_INT4_G128_ASYM)
     MOE_MX_FMT(MOE_BF16, MOE_W_INT4_G128)
     MOE_MX_FMT(MOE_BF16, MOE_W_INT4_G128_ASYM)
+    MOE_MX_FMT(MOE_F16, MOE_W_NVFP4_G16)
+    MOE_MX_FMT(MOE_BF16, MOE_W_NVFP4_G16)
 #undef MOE_MX_FMT
     return MOE_ERR_UNSUPPORTED;
 }

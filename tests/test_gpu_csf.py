@@ -197,9 +197,12 @@ def test_nvfp4_csf_dequant_bitwise(dev):
 def test_nvfp4_csf_forward_equals_raw_scales(dev, Ee, Hh, Ff, T, Kk, rate, act):
     """The layer on compressed scales, read in place by the decode kernels
     (small batches) or expanded into the workspace for the grouped GEMM
-    (T*K >= 4E), is bitwise the layer on the same scale bytes stored plainly,
-    and within tolerance of the oracle, whose scale bytes come from its own
-    CSF decoder (every token up to T = 64, tile-probing tokens beyond)."""
+    (T*K >= 4E), is bitwise the layer on the same scale bytes stored plainly
+    where both run the same kernel, and within tolerance of the oracle, whose
+    scale bytes come from its own CSF decoder (every token up to T = 64,
+    tile-probing tokens beyond). At the layer's shape and T*K in [4E, 8E)
+    the plain bytes take the MFMA GEMV and the compressed ones the grouped
+    GEMM, so there both are held to the oracle."""
     raw, csf, hb = [], [], []
     for i, (n, k) in enumerate(((Ff, Hh), (Ff, Hh), (Hh, Ff))):
         q, _, gs = synth.packed_nvfp4_random(Ee, n, k, 40 + i, dev)
@@ -223,11 +226,14 @@ def test_nvfp4_csf_forward_equals_raw_scales(dev, Ee, Hh, Ff, T, Kk, rate, act):
         tm, _ = B.moe_forward_plan(ffn, T, Kk, x.dtype)
         perm = B.moe_permute(ids, Ee, tm)
         outs.append(B.moe_w4a16_forward(ffn, x, w, perm).cpu().numpy())
-    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    same_kernel = not (Hh == 4096 and Ff == 1536 and 4 * Ee <= T * Kk < 8 * Ee)
+    if same_kernel:
+        assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
     oids = OR.topk_ids(lg, Kk)
     assert np.array_equal(ids.cpu().numpy(), oids)
     toks = list(range(T)) if T <= 64 else FX.tile_probe_tokens(oids, Ee, 64)
     ref = FX.oracle_layer_streamed(x.cpu()[toks], oids[toks],
                                    OR.routing_weights(lg, oids)[toks], FX.dequant_fn(hb, "nvfp4"))
-    ok, ratio = FX.within_tolerance(outs[1][toks], ref)
-    assert ok, ratio
+    for o in (outs if not same_kernel else outs[1:]):
+        ok, ratio = FX.within_tolerance(o[toks], ref)
+        assert ok, ratio

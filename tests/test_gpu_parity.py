@@ -443,6 +443,61 @@ def test_forward_nvfp4_decode_full_shape(dev):
     assert ok, ratio
 
 
+_NV_DECODE = {}
+
+
+def _nvfp4_decode_banks(dev):
+    """One full-shape NVFP4 bank set for the decode-range tests (built once)."""
+    if "ffn" not in _NV_DECODE:
+        banks, host = [], []
+        for i, (n, k) in enumerate(((F, H), (F, H), (H, F))):
+            qt, st, gt = synth.packed_nvfp4_random(E, n, k, 90 + i, dev)
+            banks.append(B.bank_nvfp4(qt, st, gt))
+            host.append(FX.host_bank(qt, st, gs=gt.cpu().numpy()))
+        _NV_DECODE["ffn"], _NV_DECODE["host"] = B.ffn(*banks), host
+    return _NV_DECODE["ffn"], _NV_DECODE["host"]
+
+
+@pytest.mark.parametrize("T,act,shift", [
+    (176, "bf16", 0), (351, "bf16", 0), (200, "f16", 0), (256, "bf16", 60),
+    (256, "bf16", -60), (176, "bf16", "split"), (180, "bf16", "zero")])
+def test_forward_nvfp4_band_activation_range(dev, T, act, shift):
+    """NVFP4 at the layer shape for T*K in [4E, 8E), the batches the MFMA
+    GEMV serves with 8-slot tiles (T = 176 and 351 its ends), against the
+    oracle on tile-probing tokens (the last rows of full and partial 8-slot
+    tiles, and spread tokens): fp16 and bf16 inputs, bf16 inputs far outside
+    fp16's range (whole batches scaled by 2^60 or 2^-60; tokens whose halves
+    differ by 2^40, where the staged fp16 values of the small half lose bits
+    below the tolerance), which the per-row staging exponent has to bring
+    into range, and all-zero tokens among ordinary ones (exactly zero out)."""
+    ffn, hb = _nvfp4_decode_banks(dev)
+    x = synth.activations(T, H, act, 11 + T).float()
+    if shift == "split":
+        x[:, : H // 2] *= 2.0 ** 20
+        x[:, H // 2:] *= 2.0 ** -20
+    elif shift == "zero":
+        x[::3] = 0.0
+    else:
+        x *= 2.0 ** shift
+    x = x.to(torch.bfloat16 if act == "bf16" else torch.float16)
+    assert torch.isfinite(x.float()).all()
+    lg = synth.router_logits(T, E, 11 + T)
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    tm, _ = B.moe_forward_plan(ffn, T, K, x.dtype)
+    assert tm == 8
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, E).cpu().numpy()
+    oids = OR.topk_ids(lg, K)
+    toks = FX.tile_probe_tokens(oids, E, 8, min_tokens=48, max_tokens=64)
+    if shift == "zero":
+        toks = sorted(set(toks) | {0, 3, 6})
+        assert not out[::3].any()
+    ref = FX.oracle_layer_streamed(x[toks], oids[toks], OR.routing_weights(lg, oids)[toks],
+                                   FX.dequant_fn(hb, "nvfp4"))
+    assert np.isfinite(out).all()
+    ok, ratio = FX.within_tolerance(out[toks], ref)
+    assert ok, ratio
+
+
 # --------------------------------------------------------------- properties ---
 @pytest.mark.parametrize("T", [1, 3, 37])
 def test_forward_single_expert(dev, T):
