@@ -97,7 +97,10 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  *            row r of expert e are [row_index[e][r], row_index[e][r+1])).
  *
  * The decode kernels (the GEMV) serve every format, and so does the prefill
- * GEMM (batches with T*K >= 4E); for MOE_W_NVFP4_CSF banks the forward pass
+ * GEMM (batches with T*K >= 4E; MOE_W_NVFP4_G16 banks at H = 4096, F = 1536
+ * from 8E, with the MFMA GEMV's 8-slot tiles from 4E to 8E, where its fp16
+ * arithmetic holds bf16 inputs exactly within 2^29 of each token's largest
+ * magnitude and rounds smaller ones); for MOE_W_NVFP4_CSF banks the forward pass
  * first expands the routed experts' scales into its workspace (which
  * moe_forward_plan sizes for all E experts of the three matrices). The GEMM
  * needs 4-byte-aligned scale rows (int4-g128 forms, int8), 16-byte aligned
@@ -380,9 +383,9 @@ moe_status_t moe_w4a16_forward(const moe_ffn_desc_t *experts,
  * streams, other threads) share the buffer and race: serialise them.
  * Errors: as moe_w4a16_forward, plus MOE_ERR_WORKSPACE_TOO_SMALL when
  * moe_forward_plan's ws_bytes for the call exceeds the buffer (at the
- * Step-5 shape every batch the decode kernels serve fits, T*K < 4E, i.e. up
- * to 175 tokens at K = 8 and E = 352, with or without the shared expert;
- * the prefill GEMM path's workspace does not), MOE_ERR_HIP if the device or
+ * Step-5 shape every batch below T*K = 4E fits, i.e. up to 175 tokens at
+ * K = 8 and E = 352, with or without the shared expert; the workspaces of
+ * the prefill GEMM and of NVFP4 banks from 4E slots do not), MOE_ERR_HIP if the device or
  * the buffer's address cannot be had.
  */
 moe_status_t moe_w4a16_forward_scratch(const moe_ffn_desc_t *experts,
