@@ -191,9 +191,9 @@ __host__ __device__ inline size_t perm_small_lds(int n, int E) {
     return (size_t)E * W * 8 + 3 * (kPermSmallThreads / kWave) * 4 + (size_t)E * 4;
 }
 
-// The one-group permutation (1024 threads) of n slots whose ids id_at(s)
-// returns, LDS at sm (perm_small_lds bytes).
-template <typename IdFn>
+// The one-group permutation (NT threads, at least E) of n slots whose ids
+// id_at(s) returns, LDS at sm (perm_small_lds bytes).
+template <int NT, typename IdFn>
 __device__ __forceinline__ void perm_small_body(
     IdFn id_at, int n, int E, int tile_m, uint64_t *sm, int32_t *__restrict__ counts,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ padded_offsets,
@@ -206,9 +206,9 @@ __device__ __forceinline__ void perm_small_body(
     int *poff = wtot + 3 * (kPermSmallThreads / kWave);      // [E] padded offsets
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
 
-    for (int i = tid; i < E * W; i += kPermSmallThreads) mask[i] = 0ull;
+    for (int i = tid; i < E * W; i += NT) mask[i] = 0ull;
     __syncthreads();
-    for (int s = tid; s < n; s += kPermSmallThreads) {
+    for (int s = tid; s < n; s += NT) {
         const int e = id_at(s);
         if (e >= 0 && e < E)
             atomicOr((unsigned long long *)&mask[e * W + (s >> 6)], 1ull << (s & 63));
@@ -259,7 +259,7 @@ __device__ __forceinline__ void perm_small_body(
     __syncthreads();
 
     // a slot's rank among its expert's slots: that expert's bits below it
-    for (int s = tid; s < n; s += kPermSmallThreads) {
+    for (int s = tid; s < n; s += NT) {
         const int ee = id_at(s);
         if (ee < 0 || ee >= E) {
             slot_to_row[s] = -1;
@@ -281,7 +281,7 @@ __global__ void __launch_bounds__(kPermSmallThreads) perm_small_kernel(
     int32_t *__restrict__ tile_expert, int32_t *__restrict__ num_tiles,
     int32_t *__restrict__ active_experts, int32_t *__restrict__ num_active) {
     extern __shared__ uint64_t sm_masks[];
-    perm_small_body([&](int s) { return ids[s]; }, n, E, tile_m, sm_masks, counts,
+    perm_small_body<kPermSmallThreads>([&](int s) { return ids[s]; }, n, E, tile_m, sm_masks, counts,
                     expert_offsets, padded_offsets, sorted_slots, slot_to_row, tile_expert,
                     num_tiles, active_experts, num_active);
 }
@@ -292,8 +292,12 @@ __global__ void __launch_bounds__(kPermSmallThreads) perm_small_kernel(
 // too; after one barrier the group permutes them as perm_small_kernel does.
 // Bitwise the results of route_given_kernel followed by perm_small_kernel.
 constexpr int kRoutePermMaxT = kPermSmallThreads / kWave;
+// Up to 6 tokens over at most 384 experts: 6 waves instead of 16 (fewer
+// waves to launch and to meet at each barrier; the same results).
+constexpr int kRoutePermFewT = 6, kRoutePermFewThreads = kRoutePermFewT * kWave;
 
-__global__ void __launch_bounds__(kPermSmallThreads) route_perm_small_kernel(
+template <int NT>
+__global__ void __launch_bounds__(NT) route_perm_small_kernel(
     const float *__restrict__ scores, const float *__restrict__ bias, int T, int E, int K,
     int renorm, int P, int32_t *__restrict__ ids, float *__restrict__ wts, int tile_m,
     int32_t *__restrict__ counts, int32_t *__restrict__ expert_offsets,
@@ -309,7 +313,7 @@ __global__ void __launch_bounds__(kPermSmallThreads) route_perm_small_kernel(
         token_topk(scores + (size_t)t * E, (size_t)T * E, P, bias, E, K, renorm,
                    ids + (size_t)t * K, wts + (size_t)t * K, sid + t * K);
     __syncthreads();
-    perm_small_body([&](int s) { return sid[s]; }, n, E, tile_m, sm_masks, counts,
+    perm_small_body<NT>([&](int s) { return sid[s]; }, n, E, tile_m, sm_masks, counts,
                     expert_offsets, padded_offsets, sorted_slots, slot_to_row, tile_expert,
                     num_tiles, active_experts, num_active);
 }
@@ -321,14 +325,22 @@ moe_status_t launch_route_perm_small(const float *scores, const float *bias, int
                                      const moe_perm_t &p, hipStream_t s) {
     if (T == 0) return MOE_OK;
     const size_t lds = perm_small_lds(T * K, E) + (size_t)T * K * 4;
+    const bool few = T <= kRoutePermFewT && E <= kRoutePermFewThreads;
+    const void *k = few ? (const void *)route_perm_small_kernel<kRoutePermFewThreads>
+                        : (const void *)route_perm_small_kernel<kPermSmallThreads>;
     if (lds > 65536 &&
-        hipFuncSetAttribute((const void *)route_perm_small_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return MOE_ERR_HIP;
-    hipLaunchKernelGGL(route_perm_small_kernel, dim3(1), dim3(kPermSmallThreads), lds, s, scores,
-                       bias, T, E, K, renorm, P, ids, wts, p.tile_m, p.counts, p.expert_offsets,
-                       p.padded_offsets, p.sorted_slots, p.slot_to_row, p.tile_expert,
-                       p.num_tiles, p.active_experts, p.num_active);
+#define MOE_ROUTE_PERM(NT)                                                                      \
+    hipLaunchKernelGGL(route_perm_small_kernel<NT>, dim3(1), dim3(NT), lds, s, scores, bias, T, E, \
+                       K, renorm, P, ids, wts, p.tile_m, p.counts, p.expert_offsets,           \
+                       p.padded_offsets, p.sorted_slots, p.slot_to_row, p.tile_expert,          \
+                       p.num_tiles, p.active_experts, p.num_active)
+    if (few)
+        MOE_ROUTE_PERM(kRoutePermFewThreads);
+    else
+        MOE_ROUTE_PERM(kPermSmallThreads);
+#undef MOE_ROUTE_PERM
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
