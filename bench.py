@@ -581,10 +581,12 @@ GEMM_SOURCES = ("gemm.hip", "decode.h", "stream.h", "common.h")
 def decode_kernel(fmt, act, T):
     """The gate/up kernel a batch of T tokens runs at the layer's shape: the
     grouped GEMM from T * top-k >= 4 * experts slots on (NVFP4: 8 * experts,
-    the MFMA GEMV from 4 to 8), below that the MFMA GEMV for int4-g128 (both
-    forms) and the dot2 GEMV for the others."""
+    the MFMA GEMV from 4 to 8; int4-g128, both forms: 7 * experts, the MFMA
+    GEMV below), below that the dot2 GEMV for the other formats."""
     if fmt == "nvfp4" and 4 * E <= T * K < 8 * E:
         return "gemv_mfma_gateup_nvfp4_%s" % act, GEMV_MFMA_SOURCES
+    if fmt in ("int4", "int4-asym") and T * K < 7 * E:
+        return "gemv_mfma_gateup_%s_%s" % (fmt, act), GEMV_MFMA_SOURCES
     if T * K >= 4 * E:
         return "gemm_gateup_%s_%s" % (fmt, act), GEMM_SOURCES
     if fmt in ("int4", "int4-asym"):

@@ -97,8 +97,9 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2, MOE_F32 = 3 } moe_dtype_t;
  *            row r of expert e are [row_index[e][r], row_index[e][r+1])).
  *
  * The decode kernels (the GEMV) serve every format, and so does the prefill
- * GEMM (batches with T*K >= 4E; MOE_W_NVFP4_G16 banks at H = 4096, F = 1536
- * from 8E, with the MFMA GEMV's 8-slot tiles from 4E to 8E, where its fp16
+ * GEMM (batches with T*K >= 4E; at H = 4096, F = 1536 MOE_W_NVFP4_G16 banks
+ * from 8E and int4-g128 banks, both forms, from 7E, with the MFMA GEMV's
+ * 8-slot tiles from 4E up to there; for NVFP4 its fp16
  * arithmetic holds bf16 inputs exactly within 2^29 of each token's largest
  * magnitude and rounds smaller ones); for MOE_W_NVFP4_CSF banks the forward pass
  * first expands the routed experts' scales into its workspace (which

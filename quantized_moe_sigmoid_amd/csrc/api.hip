@@ -36,7 +36,6 @@ moe_status_t launch_gemv_forward(const moe_ffn_desc_t &ex, const void *x, int ac
                                  const moe_perm_t &p, int max_tiles, void *h, float *y,
                                  hipStream_t s, const std::function<moe_status_t(int)> &mark);
 bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act, int T, int K);
-bool nvfp4_mx_band(const moe_ffn_desc_t &ex, int T, int K);
 moe_status_t launch_gemv_mx_forward(const moe_ffn_desc_t &ex, const void *x, int act, int K,
                                     const moe_perm_t &p, int max_tiles, void *h, float *y,
                                     hipStream_t s, const std::function<moe_status_t(int)> &mark);
@@ -206,8 +205,9 @@ struct FwdPlan {
 
 // Kernel choice by batch shape: with few slots per expert the dequantizing
 // GEMV streams each touched expert once per tile of 4 or 8 slots; once the
-// average expert sees several tiles' worth of slots (T*K >= 4*E; NVFP4 at
-// the layer's shape 8*E, with the MFMA GEMV's 8-slot tiles in between) the
+// average expert sees several tiles' worth of slots (T*K >= 4*E; at the
+// layer's shape NVFP4 8*E and int4-g128 7*E, with the MFMA GEMV's 8-slot
+// tiles in between) the
 // MFMA grouped GEMM, which reads each weight once per tile of 64 slots,
 // takes over. One code path per shape class.
 bool mfma_layout_ok(const moe_weight_desc_t &d) {
@@ -237,8 +237,11 @@ bool use_mfma(const moe_ffn_desc_t &ex, int T, int K) {
     if (f != MOE_W_INT4_G128 && f != MOE_W_INT4_G128_ASYM && f != MOE_W_INT4_G32 &&
         f != MOE_W_INT8_G128 && f != MOE_W_NVFP4_G16 && f != MOE_W_NVFP4_CSF)
         return false;
-    // NVFP4 at the layer's shape from 4E to 8E slots: the MFMA GEMV
-    if (f == MOE_W_NVFP4_G16 && gemv_mx_supported(ex, MOE_F16, T, K)) return false;
+    // at the layer's shape from 4E slots to 8E (NVFP4) or 7E (int4-g128,
+    // both forms): the MFMA GEMV with 8-slot tiles
+    if ((f == MOE_W_NVFP4_G16 || f == MOE_W_INT4_G128 || f == MOE_W_INT4_G128_ASYM) &&
+        gemv_mx_supported(ex, MOE_F16, T, K))
+        return false;
     // 32-bit buffer offsets must reach every row of an expert matrix
     const bool fits = (int64_t)F * ex.gate.qweight_row_stride < INT32_MAX &&
                       (int64_t)F * ex.up.qweight_row_stride < INT32_MAX &&

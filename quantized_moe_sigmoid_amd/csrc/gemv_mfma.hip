@@ -581,14 +581,15 @@ static bool mx_layout_ok(const moe_weight_desc_t &d) {
 // re-read experts and the 64-row GEMM tiles run mostly empty: at T=256 this
 // kernel took 0.960 ms per step against the GEMM's 1.125 (16-slot tiles:
 // 1.096), at T=512 1.376 against 1.148.
-bool nvfp4_mx_band(const moe_ffn_desc_t &ex, int T, int K) {
-    const int64_t n = (int64_t)T * K, E = ex.gate.num_experts;
-    return n >= 4 * E && n < 8 * E;
-}
-
+// int4-g128 (both forms) takes it at every batch below T*K = 7E, the band
+// from 4E included: at T=200 / 256 0.741 / 0.795 ms per step against the
+// GEMM's 0.876 / 0.887 (fp16; bf16 T=256 0.826 against 0.898, asymmetric
+// 0.823 against 0.968), at T=336 (7.6E) 0.936 against 0.915.
 bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act, int T, int K) {
     const int f = ex.gate.fmt;
-    if (f == MOE_W_NVFP4_G16 && !nvfp4_mx_band(ex, T, K)) return false;
+    const int64_t n = (int64_t)T * K, E = ex.gate.num_experts;
+    if (f == MOE_W_NVFP4_G16 && n < 4 * E) return false;
+    if (n >= (f == MOE_W_NVFP4_G16 ? 8 : 7) * E) return false;
     return (act == MOE_F16 || act == MOE_BF16) &&
            (f == MOE_W_INT4_G128 || f == MOE_W_INT4_G128_ASYM || f == MOE_W_NVFP4_G16) &&
            ex.gate.k == 4096 &&
@@ -596,7 +597,7 @@ bool gemv_mx_supported(const moe_ffn_desc_t &ex, int act, int T, int K) {
            mx_layout_ok(ex.gate) && mx_layout_ok(ex.up) && mx_layout_ok(ex.down);
 }
 
-// Slots per tile: 8 for 5 to 32 tokens and from T*K = 4E (NVFP4 only), else
+// Slots per tile: 8 for 5 to 32 tokens and from T*K = 4E, else
 // 4. The plan sees the batch
 // size but not the routing. Measured (bench, graph replay, same host):
 // 8-slot tiles took the Zipf-routed 8-layer stack at T=32 from 1.33-1.35

@@ -270,8 +270,8 @@ def test_forward_scratch_validation(L):
     """The entry on the library's own buffer: argument errors as
     moe_w4a16_forward, and a call whose workspace would exceed the buffer is
     refused before any HIP call. Every decode-kernel batch of the Step-5
-    shape fits (T*K < 4E: up to 175 tokens, with the shared expert too);
-    the prefill GEMM's workspace does not."""
+    shape below T*K = 4E fits (up to 175 tokens, with the shared expert
+    too); the larger batches' workspaces do not."""
     F = L.moe_w4a16_forward_scratch
     x = ctypes.c_void_p(FAKE)
     f = _ffn()
@@ -281,8 +281,12 @@ def test_forward_scratch_validation(L):
         sh = _shared()
         st, tm, ws = _plan(f, T=T, act=B.MOE_BF16, shared=ctypes.byref(sh))
         assert st == B.MOE_OK and ws <= B.MOE_FORWARD_SCRATCH_BYTES, (T, ws)
+    # from 4E slots the MFMA GEMV's 8-slot tiles (up to 7E), then the GEMM:
+    # neither workspace fits
+    st, tm, ws = _plan(f, T=308, act=B.MOE_BF16)
+    assert st == B.MOE_OK and tm == 64 and ws > B.MOE_FORWARD_SCRATCH_BYTES
     st, tm, ws = _plan(f, T=176, act=B.MOE_BF16)
-    assert tm == 64 and ws > B.MOE_FORWARD_SCRATCH_BYTES
+    assert tm == 8 and ws > B.MOE_FORWARD_SCRATCH_BYTES
     p = B.PermDesc(*([FAKE] * 9), tm)
     assert F(ctypes.byref(f), None, x, B.MOE_BF16, 176, 8, x, ctypes.byref(p), None, x,
              B.MOE_F32, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL

@@ -498,6 +498,26 @@ def test_forward_nvfp4_band_activation_range(dev, T, act, shift):
     assert ok, ratio
 
 
+@pytest.mark.parametrize("T,act", [(176, "f16"), (256, "bf16"), (307, "f16")])
+def test_forward_int4_band_full_shape(dev, T, act):
+    """int4-g128 at the layer shape for T*K in [4E, 7E) (the MFMA GEMV with
+    8-slot tiles; T = 176 and 307 the band's ends) against the oracle on
+    tile-probing tokens."""
+    ffn, host = _int4_ffn_random(E, H, F, 300 + T, dev)
+    x = synth.activations(T, H, act, 5 + T)
+    lg = synth.router_logits(T, E, 5 + T)
+    ids, w = B.moe_route_topk(K, logits=torch.from_numpy(lg).to(dev))
+    tm, _ = B.moe_forward_plan(ffn, T, K, x.dtype)
+    assert tm == 8
+    out = _run_layer(dev, ffn, x.to(dev), ids, w, E).cpu().numpy()
+    oids = OR.topk_ids(lg, K)
+    toks = FX.tile_probe_tokens(oids, E, 8, min_tokens=48, max_tokens=64)
+    ref = FX.oracle_layer_streamed(x[toks], oids[toks], OR.routing_weights(lg, oids)[toks],
+                                   FX.dequant_fn(_host_int4(host)))
+    ok, ratio = FX.within_tolerance(out[toks], ref)
+    assert ok, ratio
+
+
 # --------------------------------------------------------------- properties ---
 @pytest.mark.parametrize("T", [1, 3, 37])
 def test_forward_single_expert(dev, T):
